@@ -1,0 +1,422 @@
+"""Pins of the CPU oracle against facts the pages and mathematics fix.
+
+Each pin takes a loaded oracle library so that the mutation test can run the
+same pins on copies of the oracle with a planted mistake and show that they
+fail.  No pin reuses the oracle's code: expected values come from exact
+enumeration of the output law, closed forms printed on the pages, numpy's
+argmax, brute-force tree paths, and hand-derived fixtures under tests/golden/.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import oracle
+from workloads import bf16_bits, bf16_to_f32
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def np_softmax(logits, T):
+    """Textbook softmax(l / T) in float64 with numpy (the definition of p and q)."""
+    l = np.asarray(logits, np.float64)
+    m = np.max(l[np.isfinite(l)])
+    e = np.exp((l - m) / T)
+    return e / e.sum()
+
+
+def widen(a):
+    return bf16_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+# ------------------------------------------------------------- exact law
+
+def _boundaries(pred, n, iters=64):
+    """Per-lane boundary of a predicate that is True for u < boundary, on [0, 1)."""
+    lo, hi = np.zeros(n), np.ones(n)
+    at_zero = np.asarray(pred(lo.copy()), bool)
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        r = np.asarray(pred(mid), bool)
+        lo, hi = np.where(r, mid, lo), np.where(r, hi, mid)
+    return np.where(at_zero, hi, 0.0)
+
+
+def exact_law(lib, target, draft, T):
+    """Law of the emitted tokens of one sequence, found by bisecting the
+    oracle's decisions over the uniforms (double-precision entry point).
+
+    Returns (out, reach): out[k][y] = P(position k is emitted and equals y),
+    reach[k] = P(position k is emitted).  The drafted token at position k is
+    weighted by q_k (numpy softmax of draft row k), as a draft sampler would.
+    """
+    K1, V = target.shape
+    K = K1 - 1
+    q = [np_softmax(widen(draft[k]), T) for k in range(K)]
+
+    def call(tok_rows, ua_rows, us):
+        n = len(tok_rows)
+        t, a, _ = oracle.verify_chain(
+            np.repeat(target[None], n, 0), np.repeat(draft[None], n, 0),
+            np.asarray(tok_rows, np.int32).reshape(n, K),
+            np.asarray(ua_rows, np.float64).reshape(n, K),
+            np.asarray(us, np.float64).reshape(n), T, lib=lib)
+        return t, a
+
+    def partition(toks, ua, pos):
+        """Measure of u_s leading to each token at position pos (monotone inverse CDF)."""
+        if V == 1:
+            return np.ones(1)
+
+        def pred(u):
+            t, a = call([toks] * (V - 1), [ua] * (V - 1), u)
+            assert np.all(a == pos)
+            return t[:, pos] < np.arange(1, V)
+        b = np.concatenate([[0.0], _boundaries(pred, V - 1), [1.0]])
+        return np.diff(b)
+
+    out = np.zeros((K + 1, V))
+    reach = np.zeros(K + 1)
+    prefixes = [((), 1.0)]
+    for k in range(K + 1):
+        nxt = []
+        for pre, mass in prefixes:
+            reach[k] += mass
+            pad = [0] * (K - k - 1)
+            if k == K:
+                out[K] += mass * partition(list(pre), [0.0] * K, K)
+                continue
+            xs = [x for x in range(V) if q[k][x] > 0]
+
+            def acc(u, pre=pre, xs=xs, pad=pad):
+                rows = [list(pre) + [x] + pad for x in xs]
+                ua = [[0.0] * k + [u[i]] + [0.0] * len(pad) for i in range(len(xs))]
+                _, a = call(rows, ua, [0.5] * len(xs))
+                return a > k
+            thr = _boundaries(acc, len(xs))
+            for i, x in enumerate(xs):
+                a = thr[i]
+                if a > 0:
+                    nxt.append((pre + (x,), mass * q[k][x] * a))
+                    out[k][x] += mass * q[k][x] * a
+                if a < 1:
+                    ua = [0.0] * k + [0.5 * (1.0 + a)] + [0.0] * len(pad)
+                    out[k] += mass * q[k][x] * (1.0 - a) * partition(list(pre) + [x] + pad, ua, k)
+        prefixes = nxt
+    return out, reach
+
+
+def _law_case(rng, V, K, T, dtype, zeros):
+    """Random target/draft distributions p, q (with some zero entries) as logits T ln p."""
+    def dist():
+        d = rng.dirichlet(np.ones(V))
+        if zeros and V > 2:
+            d[rng.integers(0, V)] = 0.0
+        return d / d.sum()
+    p = [dist() for _ in range(K + 1)]
+    q = [dist() for _ in range(K)]
+    with np.errstate(divide="ignore"):
+        tl = np.array([T * np.log(x) for x in p], np.float32)
+        dl = np.array([T * np.log(x) for x in q], np.float32)
+    if dtype == "bf16":
+        tl, dl = bf16_bits(tl), bf16_bits(dl)
+    return tl, dl, p
+
+
+LAW_CASES = [  # (V, K, T, dtype, zero entries)
+    (2, 1, 1.0, "f32", False),
+    (3, 2, 1.0, "f32", True),
+    (5, 1, 0.7, "f32", True),
+    (8, 1, 1.0, "bf16", True),
+    (8, 2, 1.3, "f32", False),
+    (4, 2, 0.7, "bf16", True),
+]
+
+
+def pin_exact_law(lib, cases=LAW_CASES, seed=5):
+    """The output law equals the target's: at every emitted position k the
+    token is distributed as p_k, and position k+1 is reached with probability
+    sum_i min(p_k,i, q_k,i) (forum post §3, the proof that the output law is p;
+    French lesson, "La règle de l'exactitude")."""
+    rng = np.random.default_rng(seed)
+    for V, K, T, dtype, zeros in cases:
+        tl, dl, p_chosen = _law_case(rng, V, K, T, dtype, zeros)
+        out, reach = exact_law(lib, tl, dl, T)
+        assert abs(reach[0] - 1.0) < 1e-12
+        assert abs(out[0].sum() - 1.0) < 1e-12, f"mass {out[0].sum()}"
+        for k in range(K + 1):
+            p = np_softmax(widen(tl[k]), T)
+            got = out[k] / reach[k]
+            assert np.max(np.abs(got - p)) < 1e-12, (V, K, T, dtype, k, got, p)
+            if dtype == "f32":  # logits T ln p rounded to fp32 only
+                assert np.max(np.abs(got - p_chosen[k])) < 1e-6
+            if k < K:
+                qk = np_softmax(widen(dl[k]), T)
+                alpha = np.minimum(p, qk).sum()
+                assert abs(reach[k + 1] - reach[k] * alpha) < 1e-12, (k, reach, alpha)
+
+
+# ------------------------------------------------------------- expected tokens
+
+def expected_tokens(alpha, K):
+    """Expected tokens per target pass (French lesson, "Accélération attendue";
+    forum post §4): (1 - alpha^(K+1)) / (1 - alpha)."""
+    return (1.0 - alpha ** (K + 1)) / (1.0 - alpha)
+
+
+def pin_expected_tokens(lib, B=100_000, seed=7):
+    """Monte Carlo on constant-alpha pairs (V = 2): mean emitted tokens within
+    1% of the closed form; the French lesson prints 3.36 at alpha=0.8, K=4."""
+    facts = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+    printed = {(f["alpha"], f["K"]): f["printed"] for f in facts["expected_tokens"]}
+    assert round(expected_tokens(0.8, 4), 2) == printed[(0.8, 4)]
+    rng = np.random.default_rng(seed)
+    for p, q, K in [((0.6, 0.4), (0.4, 0.6), 4), ((0.75, 0.25), (0.5, 0.5), 5)]:
+        alpha = float(np.minimum(p, q).sum())
+        tl = np.tile(np.log(np.array(p, np.float32)), (B, K + 1, 1)).astype(np.float32)
+        dl = np.tile(np.log(np.array(q, np.float32)), (B, K, 1)).astype(np.float32)
+        tokens = (rng.random((B, K)) >= q[0]).astype(np.int32)     # token 1 w.p. q[1]
+        ua = rng.random((B, K), dtype=np.float32)
+        us = rng.random((B,), dtype=np.float32)
+        _, acc, _ = oracle.verify_chain(tl, dl, tokens, ua, us, 1.0, lib=lib)
+        mean = float((acc + 1).mean())
+        want = expected_tokens(alpha, K)
+        assert abs(mean - want) / want < 0.01, (p, q, K, mean, want)
+
+
+# ------------------------------------------------------------- page facts
+
+def pin_page_counts(lib):
+    """K+1 tokens when every draft is accepted, one when the first is rejected
+    (French lesson, "Le concept"); five accepted drafts plus the bonus give six
+    tokens (Arabic lesson, end of step 3)."""
+    facts = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+    rng = np.random.default_rng(3)
+    for f in facts["emitted_counts"]:
+        K, V, B = f["K"], 16, 64
+        tl = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+        if f["case"] == "all_accepted":      # draft == target: ratio 1 > u
+            dl = tl[:, :K].copy()
+            tokens = rng.integers(0, V, (B, K)).astype(np.int32)
+        else:                                # first drafted token has p = 0
+            dl = rng.standard_normal((B, K, V)).astype(np.float32)
+            tokens = rng.integers(0, V, (B, K)).astype(np.int32)
+            tl[np.arange(B), 0, tokens[:, 0]] = -np.inf
+        ua = rng.random((B, K), dtype=np.float32)
+        us = rng.random((B,), dtype=np.float32)
+        out, acc, _ = oracle.verify_chain(tl, dl, tokens, ua, us, 1.0, lib=lib)
+        emitted = (out >= 0).sum(axis=1)
+        assert np.all(emitted == f["tokens"]), (f, emitted)
+        assert np.all(emitted == acc + 1)
+
+
+def pin_strict_acceptance(lib):
+    """Both lessons' code accepts on a strict comparison of the uniform with
+    p(x)/q(x) (French lesson, "La règle de l'exactitude"; Arabic lesson,
+    step 1), so u equal to the ratio rejects, and a token the target gives zero
+    mass is rejected even at u = 0 (it can never be emitted, since the output
+    law is p)."""
+    V = 4
+    tl = np.zeros((1, 2, V), np.float32)                      # p = 1/4 each
+    dl = np.array([[[0.0, 0.0, -np.inf, -np.inf]]], np.float32)   # q = (1/2, 1/2, 0, 0)
+    for u, accepted in [(0.5, 0), (np.nextafter(np.float32(0.5), np.float32(0)), 1), (0.0, 1)]:
+        _, acc, d = oracle.verify_chain(tl, dl, [[1]], np.array([[u]], np.float32),
+                                        np.array([0.5], np.float32), 1.0, diag=True, lib=lib)
+        assert d[0, 0, 2] == 0.5 and acc[0] == accepted, (u, acc, d[0, 0])
+    tl[0, 0, 1] = -np.inf                                     # p(1) = 0
+    out, acc, _ = oracle.verify_chain(tl, dl, [[1]], np.array([[0.0]], np.float32),
+                                      np.array([0.0], np.float32), 1.0, lib=lib)
+    assert acc[0] == 0 and out[0, 0] != 1
+
+
+# ------------------------------------------------------------- softmax values
+
+def pin_softmax_values(lib):
+    """A constant row gives p = 1/V exactly; a two-level row has the closed
+    form 1 / (n_a + n_b exp((b - a) / T))."""
+    B, K, V = 1, 1, 7
+    tl = np.full((B, K + 1, V), 0.375, np.float32)
+    dl = np.full((B, K, V), -1.25, np.float32)
+    _, _, d = oracle.verify_chain(tl, dl, [[3]], np.array([[0.5]], np.float32),
+                                  np.array([0.5], np.float32), 0.8, diag=True, lib=lib)
+    assert d[0, 0, 0] == 1.0 / V and d[0, 0, 1] == 1.0 / V and d[0, 0, 2] == 1.0
+    for T in (1.0, 0.7, 2.5):
+        a, b, na, nb = 1.5, -0.5, 3, 9
+        row = np.array([a] * na + [b] * nb, np.float32)
+        tl = np.stack([row, row])[None]
+        dl = np.full((1, 1, na + nb), 0.0, np.float32)
+        _, _, d = oracle.verify_chain(tl, dl, [[1]], np.array([[0.0]], np.float32),
+                                      np.array([0.0], np.float32), T, diag=True, lib=lib)
+        want = 1.0 / (na + nb * np.exp((b - a) / T))
+        assert abs(d[0, 0, 0] - want) <= 1e-14 * want, (T, d[0, 0, 0], want)
+        assert abs(d[0, 0, 1] - 1.0 / (na + nb)) <= 1e-15
+
+
+# ------------------------------------------------------------- inverse CDF
+
+def pin_inverse_cdf(lib):
+    """Sampling is the inverse CDF with a strict comparison: with power-of-two
+    masses u*S lands exactly on a running sum and the next token is taken; a
+    zero-mass token is never drawn; an all-zero residual falls back to p."""
+    V, K = 4, 1
+    tl = np.zeros((1, K + 1, V), np.float32)       # bonus row uniform: C = .25 .5 .75 1
+    dl = tl[:, :K].copy()
+    for us, want in [(0.0, 0), (0.24999999, 0), (0.25, 1), (0.5, 2), (0.75, 3), (0.99999994, 3)]:
+        out, acc, _ = oracle.verify_chain(tl, dl, [[2]], np.array([[0.5]], np.float32),
+                                          np.array([us], np.float32), 1.0, lib=lib)
+        assert acc[0] == 1 and out[0, 1] == want, (us, out)
+    tl[0, 1] = [0.0, -np.inf, 0.0, -np.inf]       # p = (.5, 0, .5, 0)
+    for us, want in [(0.0, 0), (0.5, 2), (0.99999994, 2)]:
+        out, acc, _ = oracle.verify_chain(tl, dl, [[2]], np.array([[0.5]], np.float32),
+                                          np.array([us], np.float32), 1.0, lib=lib)
+        assert out[0, 1] == want, (us, out)
+    p = np.array([0.25, 0.25, 0.5])
+    tok, S = oracle.residual_draw(p, p, 0.3, lib=lib)
+    assert tok == 1 and S == 1.0
+    tok, S = oracle.residual_draw(p, np.array([0.5, 0.25, 0.25]), 0.5, lib=lib)
+    assert tok == 2 and S == 0.25                  # residual (0, 0, .25)
+
+
+# ------------------------------------------------------------- greedy
+
+def _greedy_expect(vals, tokens):
+    amax = np.argmax(vals, axis=-1)                # numpy: first maximum
+    B, K = tokens.shape
+    out = np.full((B, K + 1), -1, np.int64)
+    acc = np.zeros(B, np.int64)
+    for b in range(B):
+        j = next((k for k in range(K) if tokens[b, k] != amax[b, k]), K)
+        acc[b] = j
+        out[b, :j + 1] = amax[b, :j + 1]
+    return out, acc, amax
+
+
+def pin_greedy(lib, seed=11):
+    """Greedy chain (French lesson, "La règle de l'exactitude", greedy case)
+    equals argmax decoding up to the first mismatch, with numpy's argmax
+    (lowest index on ties; -0.0 ties +0.0)."""
+    rng = np.random.default_rng(seed)
+    for dtype in ("f32", "bf16"):
+        B, K, V = 400, 4, 37
+        vals = (rng.integers(-3, 4, size=(B, K + 1, V)) * 0.5).astype(np.float32)
+        vals[rng.random(vals.shape) < 0.05] = -np.inf
+        neg0 = (vals == 0) & (rng.random(vals.shape) < 0.5)
+        vals[neg0] = -0.0
+        logits = bf16_bits(vals) if dtype == "bf16" else vals
+        amax = np.argmax(widen(logits), axis=-1)
+        tokens = np.where(rng.random((B, K)) < 0.7, amax[:, :K],
+                          rng.integers(0, V, (B, K))).astype(np.int32)
+        out, acc = oracle.verify_greedy(logits, tokens, lib=lib)
+        e_out, e_acc, _ = _greedy_expect(widen(logits), tokens)
+        assert np.array_equal(acc, e_acc) and np.array_equal(out, e_out), dtype
+        # all drafts equal to the argmax: plain greedy decoding of K+1 tokens
+        out, acc = oracle.verify_greedy(logits, amax[:, :K].astype(np.int32), lib=lib)
+        assert np.all(acc == K) and np.array_equal(out, amax)
+    zero_rows = np.array([[[-0.0, 0.0, -1.0], [0.0, -0.0, -0.0]]], np.float32)
+    out, acc = oracle.verify_greedy(zero_rows, [[0]], lib=lib)
+    assert acc[0] == 1 and list(out[0]) == [0, 0]
+
+
+# ------------------------------------------------------------- tree
+
+def tree_bruteforce(vals, tokens, parents):
+    """Deepest root path whose every node matches its parent's argmax; lowest
+    node index among equally deep ones.  Enumerates every root path."""
+    N = len(parents)
+    amax = np.argmax(vals, axis=-1)
+    best, best_path = 0, [0]
+    for v in range(N):
+        path = [v]
+        while path[-1] != 0:
+            path.append(parents[path[-1]])
+        path = path[::-1]
+        if all(tokens[c] == amax[u] for u, c in zip(path[:-1], path[1:])):
+            if len(path) > len(best_path):
+                best, best_path = v, path
+    return best_path, [int(tokens[c]) for c in best_path[1:]] + [int(amax[best])]
+
+
+def pin_tree_bruteforce(lib, seed=13):
+    rng = np.random.default_rng(seed)
+    for trial in range(80):
+        N = int(rng.integers(1, 24))
+        parents = [-1] + [int(rng.integers(0, v)) for v in range(1, N)]
+        B, V = 4, 6
+        dtype = "bf16" if trial % 2 else "f32"
+        vals = (rng.integers(-2, 3, size=(B, N, V)) * 0.5).astype(np.float32)
+        logits = bf16_bits(vals) if dtype == "bf16" else vals
+        amax = np.argmax(widen(logits), axis=-1)
+        tokens = np.zeros((B, N), np.int32)
+        for b in range(B):
+            for v in range(1, N):
+                tokens[b, v] = amax[b, parents[v]] if rng.random() < 0.7 else rng.integers(0, V)
+        out_t, out_p, out_d = oracle.verify_tree_greedy(logits, tokens, parents, lib=lib)
+        for b in range(B):
+            path, toks = tree_bruteforce(widen(logits[b]), tokens[b], parents)
+            d = len(path) - 1
+            assert out_d[b] == d, (trial, b, out_d[b], path)
+            assert list(out_p[b, :d + 1]) == path and np.all(out_p[b, d + 1:] == -1)
+            assert list(out_t[b, :d + 1]) == toks and np.all(out_t[b, d + 1:] == -1)
+
+
+def pin_tree_chain(lib, seed=17):
+    """A tree with branching 1,1,...,1 is a chain: its greedy tree verify
+    equals the greedy chain verify."""
+    rng = np.random.default_rng(seed)
+    B, K, V = 200, 4, 29
+    vals = (rng.integers(-3, 4, size=(B, K + 1, V)) * 0.5).astype(np.float32)
+    amax = np.argmax(vals, axis=-1)
+    x = np.where(rng.random((B, K)) < 0.75, amax[:, :K], rng.integers(0, V, (B, K))).astype(np.int32)
+    parents = [-1] + list(range(K))
+    node_tokens = np.concatenate([np.zeros((B, 1), np.int32), x], axis=1)
+    t_t, _, t_d = oracle.verify_tree_greedy(vals, node_tokens, parents, lib=lib)
+    g_t, g_a = oracle.verify_greedy(vals, x, lib=lib)
+    assert np.array_equal(t_d, g_a) and np.array_equal(t_t, g_t)
+
+
+def pin_tree_figure(lib):
+    """Hand-derived cases on the French lesson's root/a/b/c/d/e/f tree."""
+    fx = json.load(open(os.path.join(GOLDEN, "tree_p1_figure.json")))
+    parents = fx["parents"]
+    for case in fx["cases"]:
+        rows = np.array(case["rows"], np.float32)[None]
+        toks = np.array(case["tokens"], np.int32)[None]
+        out_t, out_p, out_d = oracle.verify_tree_greedy(rows, toks, parents, lib=lib)
+        d = case["depth"]
+        assert out_d[0] == d, case["name"]
+        assert list(out_p[0, :d + 1]) == case["path"], case["name"]
+        assert list(out_t[0, :d + 1]) == case["emitted"], case["name"]
+
+
+# ------------------------------------------------------------- chi-square
+
+def pin_chi_square(lib, n=50_000, seed=19):
+    """The emitted token passes a chi-square test against p at the 0.05 level
+    over 50,000 draws (Arabic lesson, exercises), at the first position and at
+    the bonus position."""
+    from scipy.stats import chisquare
+    rng = np.random.default_rng(seed)
+    V, K, T = 8, 1, 1.0
+    p = [rng.dirichlet(np.ones(V) * 2) for _ in range(K + 1)]
+    q = rng.dirichlet(np.ones(V) * 2)
+    tl = np.tile(np.log(np.array(p, np.float32)), (n, 1, 1)).astype(np.float32)
+    dl = np.tile(np.log(q.astype(np.float32)), (n, 1, 1)).astype(np.float32)
+    tokens = rng.choice(V, size=(n, 1), p=q).astype(np.int32)
+    ua = rng.random((n, 1), dtype=np.float32)
+    us = rng.random((n,), dtype=np.float32)
+    out, acc, _ = oracle.verify_chain(tl, dl, tokens, ua, us, T, lib=lib)
+    p0 = np_softmax(np.log(np.array(p[0], np.float32)), 1.0)
+    h0 = np.bincount(out[:, 0], minlength=V)
+    assert chisquare(h0, p0 * n).pvalue > 0.05
+    sel = acc == K
+    p1 = np_softmax(np.log(np.array(p[1], np.float32)), 1.0)
+    h1 = np.bincount(out[sel, 1], minlength=V)
+    assert chisquare(h1, p1 * sel.sum()).pvalue > 0.05
+
+
+ALL_PINS = [pin_exact_law, pin_expected_tokens, pin_page_counts, pin_strict_acceptance,
+            pin_softmax_values,
+            pin_inverse_cdf, pin_greedy, pin_tree_bruteforce, pin_tree_chain,
+            pin_tree_figure, pin_chi_square]
