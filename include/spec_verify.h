@@ -1,0 +1,193 @@
+/*
+ * spec_verify.h - the verify step of speculative sampling on MI355X (gfx950).
+ *
+ * Given the target model's logits at K+1 positions and the draft model's
+ * logits at K positions, the chain verify accepts drafted tokens left to right
+ * while u < p(x)/q(x) with p = softmax(target/T), q = softmax(draft/T); at the
+ * first rejection it draws a replacement from the residual max(0, p-q)
+ * normalised; if every draft is accepted it draws a bonus token from p at
+ * position K+1.  At T = 0 the drafted token is compared with argmax(p), on a
+ * chain or on a static candidate tree.
+ *
+ * Sources: the French lesson "Décodage spéculatif et Eagle" (sections "Le
+ * concept", "La règle de l'exactitude", "Vérifie l'attention des arbres"), the
+ * Arabic lesson "Speculative decoding: draft, verify, repeat" (steps 1 to 3 of
+ * "Build it", with p and q named the other way round), and the forum post
+ * "Speculative Decoding: от идеи до SOTA" (§3 acceptance and resampling rules,
+ * §6 tree verification).
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer except `parents` and `workspace_bytes`-style out-params is
+ *    a DEVICE pointer owned by the caller.  The library allocates nothing.
+ *  - Logit arrays are row-major with the vocabulary innermost and must be
+ *    16-byte aligned at their base; other arrays need natural alignment.
+ *  - Work is enqueued on `stream` and nothing is synchronised: outputs are
+ *    valid once the stream reaches that point.  Argument errors are returned
+ *    synchronously and nothing is enqueued then.  SPEC_ERR_LAUNCH reports a
+ *    launch failure seen right after enqueueing.
+ *  - The workspace (size from spec_verify_workspace_bytes) holds per-call
+ *    scratch; its contents need no initialisation and are garbage afterwards.
+ *    Calls that share a workspace must be ordered on one stream.
+ *  - Inputs that break a documented precondition (a drafted token outside
+ *    [0, V), a uniform outside [0, 1), NaN or +inf logits, a row that is
+ *    entirely -inf) give unspecified outputs but never an out-of-bounds
+ *    access: token ids are clamped before they address memory.
+ *  - Results are bitwise reproducible run to run (fixed reduction orders, no
+ *    floating-point atomics).
+ *  - The library keeps no state between calls and is safe to call from
+ *    several host threads.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPEC_DTYPE_F32 = 0,  /* IEEE float32 logits                      */
+    SPEC_DTYPE_BF16 = 1  /* bfloat16 logits (upper half of a float32) */
+} spec_dtype;
+
+typedef enum {
+    SPEC_MODE_CHAIN = 0,  /* spec_verify_chain (T > 0)           */
+    SPEC_MODE_GREEDY = 1, /* spec_verify_greedy (T = 0, chain)   */
+    SPEC_MODE_TREE = 2    /* spec_verify_tree_greedy (T = 0)     */
+} spec_mode;
+
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_ERR_INVALID_ARG = 1, /* a size, pointer, dtype, temperature or tree is invalid */
+    SPEC_ERR_WORKSPACE = 2,   /* workspace missing or smaller than required            */
+    SPEC_ERR_LAUNCH = 3       /* the HIP runtime reported an error at enqueue          */
+} spec_status;
+
+#define SPEC_VERIFY_MAX_K 64            /* draft length limit of chain and greedy verify */
+#define SPEC_VERIFY_MAX_TREE_NODES 256  /* node limit of the static tree (root included) */
+#define SPEC_VERIFY_MAX_V (1 << 26)     /* vocabulary limit                              */
+
+/*
+ * Workspace size for one call.  K_or_N is K for the chain and greedy modes
+ * and N (nodes, root included) for the tree mode.  Pure host arithmetic.
+ * Returns SPEC_ERR_INVALID_ARG (and leaves *bytes alone) for sizes the entry
+ * point would reject.
+ */
+spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_N, int32_t V,
+                                        spec_dtype dtype, size_t *bytes);
+
+/*
+ * Chain verify at temperature T > 0 (French lesson, "La règle de
+ * l'exactitude"; forum post §3; Arabic lesson, steps 1-3).
+ *
+ *   target_logits [B][K+1][V]  row k < K scores drafted token k; row K is the
+ *                              bonus row.
+ *   draft_logits  [B][K][V]    row k is the distribution x_k was drawn from.
+ *   dtype                      dtype of both logit arrays.
+ *   draft_tokens  [B][K]       int32, 0 <= x < V.
+ *   u_accept      [B][K]       float32 in [0,1): the accept test of position k
+ *                              is u_accept[b][k] < p_k(x_k)/q_k(x_k) (strict;
+ *                              q_k(x_k) = 0 accepts iff p_k(x_k) > 0).
+ *   u_sample      [B]          float32 in [0,1): the one uniform of the draw
+ *                              that ends the step (residual or bonus).  A draw
+ *                              from weights w returns the smallest i with
+ *                              w_0+...+w_i > u * sum(w).
+ *   B >= 0, 0 <= K <= SPEC_VERIFY_MAX_K, 1 <= V <= SPEC_VERIFY_MAX_V, T > 0.
+ *   out_tokens    [B][K+1]     int32: the first out_accepted[b]+1 entries are
+ *                              the emitted tokens, the rest are -1.
+ *   out_accepted  [B]          int32 j in [0, K]: accepted drafts.
+ *   out_diag      nullable [B][K+1][4] float32: for k < K {p_k(x_k), q_k(x_k),
+ *                              ratio, S if k == j else 0}; row K {0, 0, 0, S if
+ *                              j == K else 0}.  S is the mass of the weights
+ *                              the final draw used; ratio is p/q (+inf when
+ *                              q = 0 < p, 0 when both are 0).
+ *   workspace                  at least spec_verify_workspace_bytes(CHAIN, ...).
+ *
+ * The step is spec_verify_chain_stats followed by spec_verify_chain_sample on
+ * the same stream and workspace.
+ */
+spec_status spec_verify_chain(const void *target_logits, const void *draft_logits, spec_dtype dtype,
+                              const int32_t *draft_tokens, const float *u_accept,
+                              const float *u_sample, int32_t B, int32_t K, int32_t V,
+                              float temperature, int32_t *out_tokens, int32_t *out_accepted,
+                              float *out_diag, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * First phase of the chain verify: one streaming pass over every target and
+ * draft logit that leaves each row's softmax statistics (running maximum and
+ * sum of exponentials, per vocabulary chunk) in the workspace.  Same argument
+ * meaning as spec_verify_chain.
+ */
+spec_status spec_verify_chain_stats(const void *target_logits, const void *draft_logits,
+                                    spec_dtype dtype, int32_t B, int32_t K, int32_t V,
+                                    float temperature, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
+ * Second phase of the chain verify: acceptance of each position, the first
+ * rejection j, and the residual or bonus draw, reading the statistics the
+ * first phase left in the same workspace.  Must follow spec_verify_chain_stats
+ * with identical logits, sizes and temperature on the same stream.
+ */
+spec_status spec_verify_chain_sample(const void *target_logits, const void *draft_logits,
+                                     spec_dtype dtype, const int32_t *draft_tokens,
+                                     const float *u_accept, const float *u_sample, int32_t B,
+                                     int32_t K, int32_t V, float temperature, int32_t *out_tokens,
+                                     int32_t *out_accepted, float *out_diag, void *workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Greedy chain verify, T = 0 (French lesson, "La règle de l'exactitude",
+ * greedy case): a_k = argmax of target row k over raw logits (lowest index on
+ * ties; -0.0 ties +0.0).  j = first k < K with x_k != a_k, else K.  Emits
+ * x_0..x_{j-1}, a_j.
+ *
+ *   target_logits [B][K+1][V], draft_tokens [B][K] int32,
+ *   out_tokens [B][K+1] (-1 padded), out_accepted [B].
+ *   B >= 0, 0 <= K <= SPEC_VERIFY_MAX_K, 1 <= V <= SPEC_VERIFY_MAX_V.
+ */
+spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
+                               const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V,
+                               int32_t *out_tokens, int32_t *out_accepted, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Greedy verify on a static candidate tree shared by the batch, T = 0 (French
+ * lesson, "Vérifie l'attention des arbres" and the EAGLE section: one target
+ * pass scores every candidate path and the longest accepted branch wins;
+ * forum post §6).
+ *
+ *   node_logits [B][N][V]  row v is the target's distribution after the path
+ *                          root..v.
+ *   node_tokens [B][N]     int32 token of node v; column 0 (the root) unused.
+ *   parents     [N]        HOST pointer, int32: parents[0] = -1 and
+ *                          0 <= parents[v] < v (nodes in topological order).
+ *   1 <= N <= SPEC_VERIFY_MAX_TREE_NODES.
+ * Node v > 0 matches iff node_tokens[b][v] == argmax(row parents[v]); it is
+ * accepted iff it and all its ancestors match.  The deepest accepted node
+ * wins, the lowest node index among equally deep ones.  With D the tree's
+ * maximum depth:
+ *   out_tokens [B][D+1]    tokens of the accepted path's nodes below the root,
+ *                          then the argmax of the last node's row, then -1.
+ *   out_path   nullable [B][D+1]  node ids root..last, then -1.
+ *   out_depth  [B]         accepted depth d (out_tokens holds d+1 tokens).
+ */
+spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
+                                    const int32_t *node_tokens, const int32_t *parents,
+                                    int32_t B, int32_t N, int32_t V, int32_t *out_tokens,
+                                    int32_t *out_path, int32_t *out_depth, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *spec_verify_status_string(spec_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

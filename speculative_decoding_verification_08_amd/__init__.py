@@ -1,0 +1,235 @@
+"""Speculative-sampling verify step on MI355X (gfx950): Python binding.
+
+Thin ctypes binding of ``libspecverify.so`` (declared in include/spec_verify.h)
+with the same entry-point names.  It only marshals torch tensors into device
+pointers and the current HIP stream; every step of the verify runs in the
+library's HIP kernels.  PyTorch supplies device memory and streams.
+
+The library must be built first (``__graft_entry__.build()``); importing this
+package without it raises ImportError.  There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "spec_verify.h")
+
+SPEC_DTYPE_F32, SPEC_DTYPE_BF16 = 0, 1
+SPEC_MODE_CHAIN, SPEC_MODE_GREEDY, SPEC_MODE_TREE = 0, 1, 2
+SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_LAUNCH = 0, 1, 2, 3
+MAX_K, MAX_TREE_NODES, MAX_V = 64, 256, 1 << 26
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        text = _lib.spec_verify_status_string(status).decode()
+        super().__init__(f"{fn} failed with status {status} ({text})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.spec_verify_status_string.argtypes = [ctypes.c_int]
+    lib.spec_verify_status_string.restype = ctypes.c_char_p
+    lib.spec_verify_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, ctypes.c_int,
+                                                ctypes.POINTER(sz)]
+    lib.spec_verify_chain.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f32,
+                                      vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_chain_stats.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, f32, vp, sz, vp]
+    lib.spec_verify_chain_sample.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i32,
+                                             f32, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.spec_verify_tree_greedy.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, vp, vp, vp,
+                                            vp, sz, vp]
+    for fn in ("spec_verify_workspace_bytes", "spec_verify_chain", "spec_verify_chain_stats",
+               "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy"):
+        getattr(lib, fn).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def header_symbols(path: str = HEADER_PATH) -> list[str]:
+    """Entry points declared in the public header."""
+    text = open(path).read()
+    return sorted(set(re.findall(r"^\S.*?\b(spec_verify_\w+)\s*\(", text, flags=re.M)))
+
+
+def library():
+    return _lib
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SPEC_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return SPEC_DTYPE_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check_dev(name, t, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _call(fn, *args):
+    st = getattr(_lib, fn)(*args)
+    if st != SPEC_OK:
+        raise SpecVerifyError(fn, st)
+
+
+def spec_verify_workspace_bytes(mode: int, B: int, K_or_N: int, V: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    _call("spec_verify_workspace_bytes", mode, B, K_or_N, V, dtype, ctypes.byref(out))
+    return out.value
+
+
+def workspace(mode: int, B: int, K_or_N: int, V: int, dtype: int, device) -> torch.Tensor:
+    """A device byte buffer large enough for one call."""
+    n = spec_verify_workspace_bytes(mode, B, K_or_N, V, dtype)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _chain_check(target, draft, draft_tokens, u_accept, u_sample):
+    _check_dev("target_logits", target)
+    dt = _dtype_code(target)
+    if target.dim() != 3:
+        raise ValueError("target_logits must be [B][K+1][V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    _check_dev("draft_logits", draft, target.dtype, (B, K, V))
+    if draft_tokens is not None:
+        _check_dev("draft_tokens", draft_tokens, torch.int32, (B, K))
+        _check_dev("u_accept", u_accept, torch.float32, (B, K))
+        _check_dev("u_sample", u_sample, torch.float32, (B,))
+    return dt, B, K, V
+
+
+def spec_verify_chain(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
+                      temperature: float, *, out_tokens=None, out_accepted=None, diag=False,
+                      out_diag=None, workspace_buf=None, stream=None):
+    """Chain verify at T > 0.  Returns (tokens [B][K+1], accepted [B], diag [B][K+1][4] or None)."""
+    dt, B, K, V = _chain_check(target_logits, draft_logits, draft_tokens, u_accept, u_sample)
+    dev = target_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if out_accepted is None:
+        out_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_diag is None and diag:
+        out_diag = torch.empty((B, K + 1, 4), dtype=torch.float32, device=dev)
+    if workspace_buf is None:
+        workspace_buf = workspace(SPEC_MODE_CHAIN, B, K, V, dt, dev)
+    _call("spec_verify_chain", _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens),
+          _ptr(u_accept), _ptr(u_sample), B, K, V, float(temperature), _ptr(out_tokens),
+          _ptr(out_accepted), _ptr(out_diag), _ptr(workspace_buf), workspace_buf.numel(),
+          _stream(dev, stream))
+    return out_tokens, out_accepted, out_diag
+
+
+def spec_verify_chain_stats(target_logits, draft_logits, temperature: float, workspace_buf, *,
+                            stream=None):
+    """First phase of the chain verify (softmax statistics of every row into the workspace)."""
+    dt, B, K, V = _chain_check(target_logits, draft_logits, None, None, None)
+    dev = target_logits.device
+    _call("spec_verify_chain_stats", _ptr(target_logits), _ptr(draft_logits), dt, B, K, V,
+          float(temperature), _ptr(workspace_buf), workspace_buf.numel(), _stream(dev, stream))
+
+
+def spec_verify_chain_sample(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
+                             temperature: float, workspace_buf, *, out_tokens=None,
+                             out_accepted=None, out_diag=None, stream=None):
+    """Second phase of the chain verify; follows spec_verify_chain_stats on the same workspace."""
+    dt, B, K, V = _chain_check(target_logits, draft_logits, draft_tokens, u_accept, u_sample)
+    dev = target_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if out_accepted is None:
+        out_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    _call("spec_verify_chain_sample", _ptr(target_logits), _ptr(draft_logits), dt,
+          _ptr(draft_tokens), _ptr(u_accept), _ptr(u_sample), B, K, V, float(temperature),
+          _ptr(out_tokens), _ptr(out_accepted), _ptr(out_diag), _ptr(workspace_buf),
+          workspace_buf.numel(), _stream(dev, stream))
+    return out_tokens, out_accepted, out_diag
+
+
+def spec_verify_greedy(target_logits, draft_tokens, *, out_tokens=None, out_accepted=None,
+                       workspace_buf=None, stream=None):
+    """Greedy chain verify (T = 0).  Returns (tokens [B][K+1], accepted [B])."""
+    _check_dev("target_logits", target_logits)
+    dt = _dtype_code(target_logits)
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    _check_dev("draft_tokens", draft_tokens, torch.int32, (B, K))
+    dev = target_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if out_accepted is None:
+        out_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if workspace_buf is None:
+        workspace_buf = workspace(SPEC_MODE_GREEDY, B, K, V, dt, dev)
+    _call("spec_verify_greedy", _ptr(target_logits), dt, _ptr(draft_tokens), B, K, V,
+          _ptr(out_tokens), _ptr(out_accepted), _ptr(workspace_buf), workspace_buf.numel(),
+          _stream(dev, stream))
+    return out_tokens, out_accepted
+
+
+def tree_max_depth(parents) -> int:
+    depth = [0] * len(parents)
+    for v in range(1, len(parents)):
+        depth[v] = depth[int(parents[v])] + 1
+    return max(depth)
+
+
+def spec_verify_tree_greedy(node_logits, node_tokens, parents, *, with_path=True,
+                            out_tokens=None, out_path=None, out_depth=None, workspace_buf=None,
+                            stream=None):
+    """Greedy static-tree verify (T = 0).  `parents` is a host sequence of N ints.
+    Returns (tokens [B][D+1], path [B][D+1] or None, depth [B])."""
+    _check_dev("node_logits", node_logits)
+    dt = _dtype_code(node_logits)
+    B, N, V = node_logits.shape
+    _check_dev("node_tokens", node_tokens, torch.int32, (B, N))
+    if len(parents) != N:
+        raise ValueError("parents must have N entries")
+    par = (ctypes.c_int32 * N)(*[int(p) for p in parents])
+    D = tree_max_depth(parents) if N > 1 else 0
+    dev = node_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+    if out_path is None and with_path:
+        out_path = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+    if out_depth is None:
+        out_depth = torch.empty((B,), dtype=torch.int32, device=dev)
+    if workspace_buf is None:
+        workspace_buf = workspace(SPEC_MODE_TREE, B, N, V, dt, dev)
+    _call("spec_verify_tree_greedy", _ptr(node_logits), dt, _ptr(node_tokens), par, B, N, V,
+          _ptr(out_tokens), _ptr(out_path), _ptr(out_depth), _ptr(workspace_buf),
+          workspace_buf.numel(), _stream(dev, stream))
+    return out_tokens, out_path, out_depth

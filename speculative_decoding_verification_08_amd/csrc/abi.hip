@@ -1,0 +1,269 @@
+// C ABI of the verify library: argument validation, launch planning and the
+// workspace layout.  Everything here is host code; the kernels live in
+// chain.hip and greedy_tree.hip.
+#include <math.h>
+#include <string.h>
+
+#include "plan.hpp"
+#include "spec_verify.h"
+
+namespace sv {
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Elements per chunk of the streaming pass: the largest power-of-two multiple
+// of 2048 up to 16384 that still gives at least 4096 workgroups (16 per CU on
+// 256 CUs); small problems fall back to 2048.
+int first_pass_chunk(int64_t rows, int V) {
+    int ch = 16384;
+    while (ch > 2048 && rows * ((V + ch - 1) / ch) < 4096) ch >>= 1;
+    return ch;
+}
+
+bool valid_dtype(spec_dtype d) { return d == SPEC_DTYPE_F32 || d == SPEC_DTYPE_BF16; }
+
+bool valid_sizes(spec_mode mode, int32_t B, int32_t KN, int32_t V) {
+    if (B < 0 || V < 1 || V > SPEC_VERIFY_MAX_V) return false;
+    if (mode == SPEC_MODE_TREE) return KN >= 1 && KN <= SPEC_VERIFY_MAX_TREE_NODES;
+    return KN >= 0 && KN <= SPEC_VERIFY_MAX_K;
+}
+
+bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, Plan &p) {
+    if (!valid_sizes(mode, B, KN, V)) return false;
+    int64_t rows;
+    if (mode == SPEC_MODE_CHAIN) rows = static_cast<int64_t>(B) * (2 * KN + 1);
+    else if (mode == SPEC_MODE_GREEDY) rows = static_cast<int64_t>(B) * (KN + 1);
+    else rows = static_cast<int64_t>(B) * KN;
+    p.rows = rows;
+    p.chunk = first_pass_chunk(rows, V);
+    p.nchunk = (V + p.chunk - 1) / p.chunk;
+    if (rows * p.nchunk > 0x7fffffffLL) return false;  // one-dimensional grid
+    size_t off = 0;
+    p.off_partial = off;
+    off += align_up(static_cast<size_t>(rows) * p.nchunk * 8);
+    if (mode == SPEC_MODE_CHAIN) {
+        p.nchunk2 = (V + kChunk2 - 1) / kChunk2;
+        if (static_cast<int64_t>(B) * p.nchunk2 > 0x7fffffffLL) return false;
+        p.off_sums = off;
+        off += align_up(static_cast<size_t>(B) * p.nchunk2 * 4);
+        p.off_counters = off;
+        off += align_up(static_cast<size_t>(B) * 4);
+    }
+    p.bytes = off > 0 ? off : kAlign;
+    return true;
+}
+
+template <class T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+spec_status launch_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH; }
+
+// Shared validation of the chain entry points.
+spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype, int32_t B,
+                        int32_t K, int32_t V, float T, void *ws, size_t ws_bytes, Plan &plan,
+                        ChainArgs &a) {
+    if (!valid_dtype(dtype) || !(T > 0.f) || isinf(T)) return SPEC_ERR_INVALID_ARG;
+    if (!make_plan(SPEC_MODE_CHAIN, B, K, V, plan)) return SPEC_ERR_INVALID_ARG;
+    if (B == 0) return SPEC_OK;
+    if (!target || !aligned(target, 16)) return SPEC_ERR_INVALID_ARG;
+    if (K > 0 && (!draft || !aligned(draft, 16))) return SPEC_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < plan.bytes || !aligned(ws, 16)) return SPEC_ERR_WORKSPACE;
+    memset(&a, 0, sizeof a);
+    a.target = target;
+    a.draft = draft;
+    a.B = B;
+    a.K = K;
+    a.V = V;
+    a.c = static_cast<float>(1.4426950408889634 / static_cast<double>(T));
+    a.chunk = plan.chunk;
+    a.nchunk = plan.nchunk;
+    a.nchunk2 = plan.nchunk2;
+    a.partial = at<float2>(ws, plan.off_partial);
+    a.sums = at<float>(ws, plan.off_sums);
+    a.counters = at<uint32_t>(ws, plan.off_counters);
+    return SPEC_OK;
+}
+
+spec_status chain_sample_args(const int32_t *tokens, const float *ua, const float *us, int32_t B,
+                              int32_t K, int32_t *out_tokens, int32_t *out_accepted,
+                              float *out_diag, ChainArgs &a) {
+    if (B == 0) return SPEC_OK;
+    if (K > 0 && (!tokens || !ua)) return SPEC_ERR_INVALID_ARG;
+    if (!us || !out_tokens || !out_accepted) return SPEC_ERR_INVALID_ARG;
+    if ((tokens && !aligned(tokens, 4)) || (ua && !aligned(ua, 4)) || !aligned(us, 4) ||
+        !aligned(out_tokens, 4) || !aligned(out_accepted, 4) || (out_diag && !aligned(out_diag, 16)))
+        return SPEC_ERR_INVALID_ARG;
+    a.tokens = tokens;
+    a.u_accept = ua;
+    a.u_sample = us;
+    a.out_tokens = out_tokens;
+    a.out_accepted = out_accepted;
+    a.out_diag = out_diag;
+    return SPEC_OK;
+}
+
+}  // namespace
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" {
+
+const char *spec_verify_status_string(spec_status status) {
+    switch (status) {
+        case SPEC_OK: return "ok";
+        case SPEC_ERR_INVALID_ARG: return "invalid argument";
+        case SPEC_ERR_WORKSPACE: return "workspace missing or too small";
+        case SPEC_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_N, int32_t V,
+                                        spec_dtype dtype, size_t *bytes) {
+    if (!bytes || !valid_dtype(dtype)) return SPEC_ERR_INVALID_ARG;
+    if (mode != SPEC_MODE_CHAIN && mode != SPEC_MODE_GREEDY && mode != SPEC_MODE_TREE)
+        return SPEC_ERR_INVALID_ARG;
+    Plan p;
+    if (!make_plan(mode, B, K_or_N, V, p)) return SPEC_ERR_INVALID_ARG;
+    *bytes = p.bytes;
+    return SPEC_OK;
+}
+
+spec_status spec_verify_chain_stats(const void *target_logits, const void *draft_logits,
+                                    spec_dtype dtype, int32_t B, int32_t K, int32_t V,
+                                    float temperature, void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    Plan plan;
+    ChainArgs a;
+    spec_status st = chain_setup(target_logits, draft_logits, dtype, B, K, V, temperature,
+                                 workspace, workspace_bytes, plan, a);
+    if (st != SPEC_OK || B == 0) return st;
+    return launch_status(launch_chain_stats(a, dtype, stream));
+}
+
+spec_status spec_verify_chain_sample(const void *target_logits, const void *draft_logits,
+                                     spec_dtype dtype, const int32_t *draft_tokens,
+                                     const float *u_accept, const float *u_sample, int32_t B,
+                                     int32_t K, int32_t V, float temperature, int32_t *out_tokens,
+                                     int32_t *out_accepted, float *out_diag, void *workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+    Plan plan;
+    ChainArgs a;
+    spec_status st = chain_setup(target_logits, draft_logits, dtype, B, K, V, temperature,
+                                 workspace, workspace_bytes, plan, a);
+    if (st != SPEC_OK || B == 0) return st;
+    st = chain_sample_args(draft_tokens, u_accept, u_sample, B, K, out_tokens, out_accepted,
+                           out_diag, a);
+    if (st != SPEC_OK) return st;
+    return launch_status(launch_chain_sample(a, dtype, stream));
+}
+
+spec_status spec_verify_chain(const void *target_logits, const void *draft_logits,
+                              spec_dtype dtype, const int32_t *draft_tokens,
+                              const float *u_accept, const float *u_sample, int32_t B, int32_t K,
+                              int32_t V, float temperature, int32_t *out_tokens,
+                              int32_t *out_accepted, float *out_diag, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    Plan plan;
+    ChainArgs a;
+    spec_status st = chain_setup(target_logits, draft_logits, dtype, B, K, V, temperature,
+                                 workspace, workspace_bytes, plan, a);
+    if (st != SPEC_OK || B == 0) return st;
+    st = chain_sample_args(draft_tokens, u_accept, u_sample, B, K, out_tokens, out_accepted,
+                           out_diag, a);
+    if (st != SPEC_OK) return st;
+    st = launch_status(launch_chain_stats(a, dtype, stream));
+    if (st != SPEC_OK) return st;
+    return launch_status(launch_chain_sample(a, dtype, stream));
+}
+
+spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
+                               const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V,
+                               int32_t *out_tokens, int32_t *out_accepted, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return SPEC_ERR_INVALID_ARG;
+    Plan plan;
+    if (!make_plan(SPEC_MODE_GREEDY, B, K, V, plan)) return SPEC_ERR_INVALID_ARG;
+    if (B == 0) return SPEC_OK;
+    if (!target_logits || !aligned(target_logits, 16)) return SPEC_ERR_INVALID_ARG;
+    if ((K > 0 && (!draft_tokens || !aligned(draft_tokens, 4))) || !out_tokens ||
+        !out_accepted || !aligned(out_tokens, 4) || !aligned(out_accepted, 4))
+        return SPEC_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 16))
+        return SPEC_ERR_WORKSPACE;
+    ArgmaxArgs am;
+    am.logits = target_logits;
+    am.rows = plan.rows;
+    am.V = V;
+    am.chunk = plan.chunk;
+    am.nchunk = plan.nchunk;
+    am.partial = at<int2>(workspace, plan.off_partial);
+    spec_status st = launch_status(launch_row_argmax(am, dtype, stream));
+    if (st != SPEC_OK) return st;
+    GreedyArgs g;
+    g.partial = am.partial;
+    g.tokens = draft_tokens;
+    g.B = B;
+    g.K = K;
+    g.nchunk = plan.nchunk;
+    g.out_tokens = out_tokens;
+    g.out_accepted = out_accepted;
+    return launch_status(launch_greedy_resolve(g, stream));
+}
+
+spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
+                                    const int32_t *node_tokens, const int32_t *parents,
+                                    int32_t B, int32_t N, int32_t V, int32_t *out_tokens,
+                                    int32_t *out_path, int32_t *out_depth, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dtype(dtype) || !parents) return SPEC_ERR_INVALID_ARG;
+    Plan plan;
+    if (!make_plan(SPEC_MODE_TREE, B, N, V, plan)) return SPEC_ERR_INVALID_ARG;
+    TreeArgs t;
+    memset(&t, 0, sizeof t);
+    if (parents[0] != -1) return SPEC_ERR_INVALID_ARG;
+    t.tree.N = N;
+    t.tree.parent[0] = -1;
+    t.tree.depth[0] = 0;
+    int D = 0;
+    for (int v = 1; v < N; ++v) {
+        if (parents[v] < 0 || parents[v] >= v) return SPEC_ERR_INVALID_ARG;
+        t.tree.parent[v] = static_cast<int16_t>(parents[v]);
+        t.tree.depth[v] = static_cast<uint8_t>(t.tree.depth[parents[v]] + 1);
+        if (t.tree.depth[v] > D) D = t.tree.depth[v];
+    }
+    t.tree.D = D;
+    if (B == 0) return SPEC_OK;
+    if (!node_logits || !aligned(node_logits, 16)) return SPEC_ERR_INVALID_ARG;
+    if (!node_tokens || !out_tokens || !out_depth || !aligned(node_tokens, 4) ||
+        !aligned(out_tokens, 4) || !aligned(out_depth, 4) || (out_path && !aligned(out_path, 4)))
+        return SPEC_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 16))
+        return SPEC_ERR_WORKSPACE;
+    ArgmaxArgs am;
+    am.logits = node_logits;
+    am.rows = plan.rows;
+    am.V = V;
+    am.chunk = plan.chunk;
+    am.nchunk = plan.nchunk;
+    am.partial = at<int2>(workspace, plan.off_partial);
+    spec_status st = launch_status(launch_row_argmax(am, dtype, stream));
+    if (st != SPEC_OK) return st;
+    t.partial = am.partial;
+    t.tokens = node_tokens;
+    t.B = B;
+    t.nchunk = plan.nchunk;
+    t.out_tokens = out_tokens;
+    t.out_path = out_path;
+    t.out_depth = out_depth;
+    return launch_status(launch_tree_resolve(t, stream));
+}
+
+}  // extern "C"

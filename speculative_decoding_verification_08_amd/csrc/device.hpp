@@ -1,0 +1,230 @@
+// Device-side building blocks of the verify kernels for gfx950 (wave64).
+//
+// Logit rows are streamed as 16-byte vectors (8 bf16 or 4 fp32 per lane and
+// load), widened to fp32 in registers.  Softmax statistics are kept as a pair
+// (ref, z): ref is a reference point in the exponent domain, ref = m * c with
+// c = log2(e) / T and m the largest logit seen, and z = sum_i 2^(l_i*c - ref).
+// All exponentials of one row are taken against the same rounded reference,
+// so the rounding of m * c cancels between a probability's numerator and the
+// row sum.  Every reduction runs in a fixed order: results are bitwise
+// reproducible.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWG = 256;    // threads per workgroup of the streaming kernels
+constexpr int kWave = 64;   // CDNA wavefront
+constexpr int kWaves = kWG / kWave;
+
+struct Bf16 {
+    static constexpr int kVec = 8;  // elements per 16-byte vector
+};
+struct F32 {
+    static constexpr int kVec = 4;
+};
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One element of a logit array, widened exactly to fp32.
+template <class DT>
+__device__ __forceinline__ float load_one(const void *base, int64_t i);
+template <>
+__device__ __forceinline__ float load_one<Bf16>(const void *base, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(base)[i]) << 16);
+}
+template <>
+__device__ __forceinline__ float load_one<F32>(const void *base, int64_t i) {
+    return static_cast<const float *>(base)[i];
+}
+
+// A 16-byte vector widened to fp32, element order preserved.
+template <class DT>
+__device__ __forceinline__ void unpack(const uint4 &v, float *x);
+template <>
+__device__ __forceinline__ void unpack<Bf16>(const uint4 &v, float *x) {
+    x[0] = __uint_as_float(v.x << 16);
+    x[1] = __uint_as_float(v.x & 0xffff0000u);
+    x[2] = __uint_as_float(v.y << 16);
+    x[3] = __uint_as_float(v.y & 0xffff0000u);
+    x[4] = __uint_as_float(v.z << 16);
+    x[5] = __uint_as_float(v.z & 0xffff0000u);
+    x[6] = __uint_as_float(v.w << 16);
+    x[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ void unpack<F32>(const uint4 &v, float *x) {
+    x[0] = __uint_as_float(v.x);
+    x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z);
+    x[3] = __uint_as_float(v.w);
+}
+
+// Element range [g0, g1) of a flat array split into a scalar head, whole
+// 16-byte vectors [va, vb) (vector indices from the array base) and a scalar
+// tail.  The array base is 16-byte aligned.
+struct Span {
+    int64_t h0, h1, va, vb, t0, t1;
+};
+template <int VEC>
+__device__ __forceinline__ Span split_span(int64_t g0, int64_t g1) {
+    const int64_t a = (g0 + VEC - 1) / VEC * VEC;
+    if (a >= g1) return Span{g0, g1, 0, 0, g1, g1};
+    const int64_t e = g1 / VEC * VEC;
+    return Span{g0, a, a / VEC, e / VEC, e, g1};
+}
+
+// ------------------------------------------------------------------ softmax
+
+// Merge two (ref, z) pairs.  A pair with ref = -inf is empty.
+__device__ __forceinline__ void mz_merge(float &ref, float &z, float ref2, float z2) {
+    const float m = fmaxf(ref, ref2);
+    const float r = (m == -INFINITY) ? 0.f : m;
+    z = z * exp2_hw(ref - r) + z2 * exp2_hw(ref2 - r);
+    ref = m;
+}
+
+// Fold N logits into (ref, z): one max over the batch, one rescale, then one
+// exp2 per element against the new reference.
+template <int N>
+__device__ __forceinline__ void mz_batch(const float *x, float c, float &ref, float &z) {
+    float bm = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) bm = fmaxf(bm, x[i]);
+    const float rn = fmaxf(ref, bm * c);
+    const float r = (rn == -INFINITY) ? 0.f : rn;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < N; ++i) s[i & 3] += exp2_hw(fmaf(x[i], c, -r));
+    z = z * exp2_hw(ref - r) + ((s[0] + s[1]) + (s[2] + s[3]));
+    ref = rn;
+}
+
+// Workgroup merge of (ref, z); the result is valid in thread 0.
+__device__ __forceinline__ void mz_reduce_wg(float &ref, float &z) {
+    __shared__ float s_ref[kWaves], s_z[kWaves];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const float r2 = __shfl_xor(ref, off);
+        const float z2 = __shfl_xor(z, off);
+        mz_merge(ref, z, r2, z2);
+    }
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) == 0) {
+        s_ref[w] = ref;
+        s_z[w] = z;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        ref = s_ref[0];
+        z = s_z[0];
+        for (int i = 1; i < kWaves; ++i) mz_merge(ref, z, s_ref[i], s_z[i]);
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------ argmax
+
+// (value, index) with the larger value winning and the lower index breaking
+// ties; -0.0 and +0.0 compare equal.
+struct ValIdx {
+    float v;
+    int32_t i;
+};
+__device__ __forceinline__ bool vi_better(float v, int32_t i, float bv, int32_t bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+// Workgroup argmax; the result is valid in thread 0.
+__device__ __forceinline__ void vi_reduce_wg(float &v, int32_t &i) {
+    __shared__ float s_v[kWaves];
+    __shared__ int32_t s_i[kWaves];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        const float v2 = __shfl_xor(v, off);
+        const int32_t i2 = __shfl_xor(i, off);
+        if (vi_better(v2, i2, v, i)) {
+            v = v2;
+            i = i2;
+        }
+    }
+    const int w = threadIdx.x / kWave;
+    if ((threadIdx.x % kWave) == 0) {
+        s_v[w] = v;
+        s_i[w] = i;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < kWaves; ++k)
+            if (vi_better(s_v[k], s_i[k], v, i)) {
+                v = s_v[k];
+                i = s_i[k];
+            }
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------ sums
+
+// Workgroup sum in a fixed order; the result is valid in thread 0.
+__device__ __forceinline__ float sum_wg(float x) {
+    __shared__ float s_x[kWaves];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    if ((threadIdx.x % kWave) == 0) s_x[threadIdx.x / kWave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        x = s_x[0];
+        for (int k = 1; k < kWaves; ++k) x += s_x[k];
+    }
+    __syncthreads();
+    return x;
+}
+
+// Exclusive prefix sum over the workgroup's threads in thread order.
+__device__ __forceinline__ float exclusive_scan_wg(float x) {
+    __shared__ float s_tot[kWaves];
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    float inc = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float y = __shfl_up(inc, off);
+        if (lane >= off) inc += y;
+    }
+    if (lane == kWave - 1) s_tot[w] = inc;
+    float ex = __shfl_up(inc, 1);
+    if (lane == 0) ex = 0.f;
+    __syncthreads();
+    float base = 0.f;
+    for (int k = 0; k < w; ++k) base += s_tot[k];
+    __syncthreads();
+    return base + ex;
+}
+
+__device__ __forceinline__ int min_wg(int x) {
+    __shared__ int s_x[kWaves];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x = min(x, __shfl_xor(x, off));
+    if ((threadIdx.x % kWave) == 0) s_x[threadIdx.x / kWave] = x;
+    __syncthreads();
+    int r = s_x[0];
+    for (int k = 1; k < kWaves; ++k) r = min(r, s_x[k]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ int max_wg(int x) {
+    __shared__ int s_x[kWaves];
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off));
+    if ((threadIdx.x % kWave) == 0) s_x[threadIdx.x / kWave] = x;
+    __syncthreads();
+    int r = s_x[0];
+    for (int k = 1; k < kWaves; ++k) r = max(r, s_x[k]);
+    __syncthreads();
+    return r;
+}
+
+}  // namespace sv

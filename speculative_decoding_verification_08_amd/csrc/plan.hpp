@@ -1,0 +1,83 @@
+// Launch plans and kernel argument blocks of the verify library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kMaxK = 64;
+constexpr int kMaxTreeNodes = 256;
+constexpr int kChunk2 = 4096;  // elements per chunk of the residual / bonus pass
+
+// How a launch cuts the rows it streams into vocabulary chunks, and where its
+// scratch lives inside the caller's workspace.
+struct Plan {
+    int64_t rows = 0;      // rows streamed by the first pass
+    int chunk = 0;         // elements per chunk of the first pass
+    int nchunk = 0;        // chunks per row, first pass
+    int nchunk2 = 0;       // chunks per row, residual / bonus pass (chain)
+    size_t off_partial = 0, off_sums = 0, off_counters = 0;
+    size_t bytes = 0;      // total workspace
+};
+
+// Chain verify, both phases.
+struct ChainArgs {
+    const void *target;      // [B][K+1][V]
+    const void *draft;       // [B][K][V]
+    const int32_t *tokens;   // [B][K]
+    const float *u_accept;   // [B][K]
+    const float *u_sample;   // [B]
+    int32_t B, K, V;
+    float c;                 // log2(e) / T
+    int32_t chunk, nchunk, nchunk2;
+    float2 *partial;         // [B][2K+1][nchunk] (ref, z); rows 0..K target, K+1.. draft
+    float *sums;             // [B][nchunk2] weight mass per chunk
+    uint32_t *counters;      // [B] finished chunks of the second pass
+    int32_t *out_tokens;     // [B][K+1]
+    int32_t *out_accepted;   // [B]
+    float *out_diag;         // nullable [B][K+1][4]
+};
+
+// Row argmax over rows of [rows][V].
+struct ArgmaxArgs {
+    const void *logits;
+    int64_t rows;
+    int32_t V, chunk, nchunk;
+    int2 *partial;           // [rows][nchunk] (value bits, index)
+};
+
+struct GreedyArgs {
+    const int2 *partial;     // [B][K+1][nchunk]
+    const int32_t *tokens;   // [B][K]
+    int32_t B, K, nchunk;
+    int32_t *out_tokens;
+    int32_t *out_accepted;
+};
+
+// A static tree travels by value in the kernel arguments.
+struct TreeShape {
+    int16_t parent[kMaxTreeNodes];
+    uint8_t depth[kMaxTreeNodes];
+    int32_t N, D;
+};
+
+struct TreeArgs {
+    const int2 *partial;     // [B][N][nchunk]
+    const int32_t *tokens;   // [B][N]
+    int32_t B, nchunk;
+    int32_t *out_tokens;     // [B][D+1]
+    int32_t *out_path;       // nullable [B][D+1]
+    int32_t *out_depth;      // [B]
+    TreeShape tree;
+};
+
+// Host launchers (defined next to their kernels).
+hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s);
+hipError_t launch_chain_sample(const ChainArgs &a, int dtype, hipStream_t s);
+hipError_t launch_row_argmax(const ArgmaxArgs &a, int dtype, hipStream_t s);
+hipError_t launch_greedy_resolve(const GreedyArgs &a, hipStream_t s);
+hipError_t launch_tree_resolve(const TreeArgs &a, hipStream_t s);
+
+}  // namespace sv

@@ -1,0 +1,100 @@
+"""CPU tests of the C ABI: the library loads, exports every declared entry point,
+and rejects bad arguments before enqueueing anything (no GPU call is made)."""
+import ctypes
+
+import pytest
+
+sv = pytest.importorskip("speculative_decoding_verification_08_amd")
+
+FAKE = 1 << 20          # 16-byte aligned, never dereferenced: validation fails first
+FAKE_MIS = FAKE + 8     # misaligned for logits
+
+
+def test_every_declared_symbol_is_exported():
+    syms = sv.header_symbols()
+    assert {"spec_verify_chain", "spec_verify_greedy", "spec_verify_tree_greedy",
+            "spec_verify_workspace_bytes"} <= set(syms)
+    lib = sv.library()
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_workspace_bytes():
+    ws = sv.spec_verify_workspace_bytes
+    for mode, kn in ((sv.SPEC_MODE_CHAIN, 5), (sv.SPEC_MODE_GREEDY, 5), (sv.SPEC_MODE_TREE, 45)):
+        n = ws(mode, 64, kn, 128256, sv.SPEC_DTYPE_BF16)
+        assert n > 0 and n % 256 == 0
+        assert ws(mode, 128, kn, 128256, sv.SPEC_DTYPE_BF16) >= n
+    assert ws(sv.SPEC_MODE_CHAIN, 0, 0, 1, sv.SPEC_DTYPE_F32) > 0
+    bad = [(sv.SPEC_MODE_CHAIN, -1, 4, 100), (sv.SPEC_MODE_CHAIN, 2, 65, 100),
+           (sv.SPEC_MODE_CHAIN, 2, 4, 0), (sv.SPEC_MODE_CHAIN, 2, 4, (1 << 26) + 1),
+           (sv.SPEC_MODE_TREE, 2, 0, 100), (sv.SPEC_MODE_TREE, 2, 257, 100), (7, 2, 4, 100)]
+    for args in bad:
+        with pytest.raises(sv.SpecVerifyError) as e:
+            ws(*args, sv.SPEC_DTYPE_F32)
+        assert e.value.status == sv.SPEC_ERR_INVALID_ARG
+    with pytest.raises(sv.SpecVerifyError):
+        ws(sv.SPEC_MODE_CHAIN, 2, 4, 100, 5)
+
+
+def _chain(lib, **kw):
+    a = dict(t=FAKE, d=FAKE, dt=sv.SPEC_DTYPE_BF16, x=FAKE, ua=FAKE, us=FAKE, B=4, K=3, V=1000,
+             T=1.0, ot=FAKE, oa=FAKE, od=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.spec_verify_chain(a["t"], a["d"], a["dt"], a["x"], a["ua"], a["us"], a["B"], a["K"],
+                                 a["V"], ctypes.c_float(a["T"]), a["ot"], a["oa"], a["od"], a["ws"],
+                                 a["wsb"], None)
+
+
+def test_chain_argument_errors():
+    lib = sv.library()
+    E = sv.SPEC_ERR_INVALID_ARG
+    assert _chain(lib, B=0) == sv.SPEC_OK                 # empty batch: nothing to do
+    assert _chain(lib, T=0.0) == E
+    assert _chain(lib, T=-1.0) == E
+    assert _chain(lib, T=float("inf")) == E
+    assert _chain(lib, T=float("nan")) == E
+    assert _chain(lib, K=65) == E
+    assert _chain(lib, V=0) == E
+    assert _chain(lib, B=-3) == E
+    assert _chain(lib, dt=9) == E
+    assert _chain(lib, t=None) == E
+    assert _chain(lib, d=None) == E
+    assert _chain(lib, t=FAKE_MIS) == E
+    assert _chain(lib, x=None) == E
+    assert _chain(lib, us=None) == E
+    assert _chain(lib, ot=None) == E
+    assert _chain(lib, od=FAKE + 4) == E                  # diag must be 16-byte aligned
+    assert _chain(lib, ws=None) == sv.SPEC_ERR_WORKSPACE
+    need = sv.spec_verify_workspace_bytes(sv.SPEC_MODE_CHAIN, 4, 3, 1000, sv.SPEC_DTYPE_BF16)
+    assert _chain(lib, wsb=need - 1) == sv.SPEC_ERR_WORKSPACE
+
+
+def test_greedy_and_tree_argument_errors():
+    lib = sv.library()
+    E = sv.SPEC_ERR_INVALID_ARG
+    g = lib.spec_verify_greedy
+    assert g(FAKE, 1, FAKE, 0, 4, 100, FAKE, FAKE, FAKE, 1 << 20, None) == sv.SPEC_OK
+    assert g(None, 1, FAKE, 2, 4, 100, FAKE, FAKE, FAKE, 1 << 20, None) == E
+    assert g(FAKE, 1, None, 2, 4, 100, FAKE, FAKE, FAKE, 1 << 20, None) == E
+    assert g(FAKE, 1, FAKE, 2, 65, 100, FAKE, FAKE, FAKE, 1 << 20, None) == E
+    assert g(FAKE, 1, FAKE, 2, 4, 100, FAKE, FAKE, FAKE, 16, None) == sv.SPEC_ERR_WORKSPACE
+
+    def tree(parents, B=2, N=None, ws=1 << 20):
+        N = len(parents) if N is None else N
+        par = (ctypes.c_int32 * max(len(parents), 1))(*parents)
+        return lib.spec_verify_tree_greedy(FAKE, 1, FAKE, par, B, N, 100, FAKE, None, FAKE, FAKE,
+                                           ws, None)
+    assert tree([-1, 0, 0, 1], B=0) == sv.SPEC_OK
+    for bad in ([0, 0, 1], [-1, 1, 0], [-1, 0, 2], [-1, -1], [-1, 0, 5]):
+        assert tree(bad) == E, bad
+    assert tree([-1, 0, 0, 1], ws=8) == sv.SPEC_ERR_WORKSPACE
+    assert tree([-1] + list(range(256)), N=257) == E
+    assert lib.spec_verify_tree_greedy(FAKE, 1, FAKE, None, 2, 3, 100, FAKE, None, FAKE, FAKE,
+                                       1 << 20, None) == E
+
+
+def test_status_strings():
+    lib = sv.library()
+    for s in range(4):
+        assert lib.spec_verify_status_string(s)
