@@ -3,11 +3,13 @@
 One step = one chain verify (row statistics, accept/reject, residual or bonus
 draw, emit) over one batch of the chain_t1_128k workload: B=64 sequences,
 K=5 drafts, V=128256, bf16 logits, T=1 (180,584,448 logit bytes).  Inputs are
-resident in HBM before timing; several input sets rotate so that the 256 MB
-Infinity Cache cannot hold the working set between steps.
+resident in HBM before timing; enough input sets rotate (3 here, 542 MB) that
+the 256 MB Infinity Cache cannot hold the working set between steps.
+`--workload` measures the other workloads the same way.
 
-Prints one JSON line.  `roofline` covers the streaming statistics kernel (the
-dominant one), timed alone with HIP events on the launch stream;
+Prints one JSON line.  `roofline` covers the fused chain kernel (one launch per
+step, so the HIP events around the timed steps on the launch stream give its
+average duration);
 `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
 """
 from __future__ import annotations
@@ -26,7 +28,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "verify steps/s (B×(K+1)×V logits) + achieved HBM GB/s vs peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chain_stats_chain_t1_128k_traffic.json")
 STATS_KERNEL_SRC = [os.path.join(ROOT, "speculative_decoding_verification_08_amd", "csrc", f)
                     for f in ("chain.hip", "device.hpp", "plan.hpp")]
 
@@ -45,41 +46,73 @@ def to_dev(a, device):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def measured_traffic(algo_bytes: float):
-    """HBM bytes per launch from the committed PMC summary, if it was taken on this kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the statistics kernel from the committed PMC
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"k_chain_fused_{workload}_traffic.json")
+    if not os.path.exists(path):
         return None
-    t = json.load(open(TRAFFIC_FILE))
+    t = json.load(open(path))
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(inp, budget_s: float, gpu_out):
-    """The oracle as it stands, single-threaded, on whole steps of the same workload."""
+def set_bytes(w) -> int:
+    esize = 2 if w.dtype == "bf16" else 4
+    if w.mode == "chain":
+        rows = w.B * (2 * w.K + 1)
+    elif w.mode == "greedy":
+        rows = w.B * (w.K + 1)
+    else:
+        rows = w.B * (1 + sum(int(np.prod(w.branching[:i + 1])) for i in range(len(w.branching))))
+    return rows * w.V * esize
+
+
+def oracle_step(w, inp):
     import oracle
+    if w.mode == "chain":
+        return oracle.verify_chain(inp["target"], inp["draft"], inp["tokens"], inp["u_accept"],
+                                   inp["u_sample"], inp["T"])
+    if w.mode == "greedy":
+        return oracle.verify_greedy(inp["target"], inp["tokens"])
+    return oracle.verify_tree_greedy(inp["node_logits"], inp["node_tokens"], inp["parents"])
+
+
+def check(w, inp, gpu_out):
     from oracle import parity
+    if w.mode == "chain":
+        return parity.check_chain(inp, *gpu_out)
+    if w.mode == "greedy":
+        return parity.check_greedy(inp, *gpu_out)
+    return parity.check_tree(inp, *gpu_out)
+
+
+def cpu_baseline(w, inp, budget_s: float, gpu_out):
+    """The oracle as it stands, single-threaded, on whole steps of the same workload."""
     t0 = time.perf_counter()
     steps = 0
     while True:
-        oracle.verify_chain(inp["target"], inp["draft"], inp["tokens"], inp["u_accept"],
-                            inp["u_sample"], inp["T"])
+        oracle_step(w, inp)
         steps += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    counts = parity.check_chain(inp, *gpu_out)
+    counts = check(w, inp, gpu_out)
     return {"value": steps / dt, "unit": "verify steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} whole steps of input set 0 (B=64, K=5, V=128256), fp64, one thread, "
-                      f"{dt:.1f} s", "parity_on_sample": dict(counts)}
+            "sample": f"{steps} whole steps of input set 0 of {w.name}, fp64, one thread, {dt:.1f} s",
+            "parity_on_sample": dict(counts)}
 
 
 def main():
+    import workloads as W
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--rotate", type=int, default=3, help="input sets cycled through")
+    ap.add_argument("--workload", default="chain_t1_128k", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input sets cycled through (default: enough to exceed 512 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -91,35 +124,95 @@ def main():
 
     import torch
     import speculative_decoding_verification_08_amd as sv
-    import workloads as W
 
-    w = W.WORKLOADS["chain_t1_128k"]
-    B, K, V = w.B, w.K, w.V
+    w = W.WORKLOADS[args.workload]
+    B, V = w.B, w.V
+    nbytes = set_bytes(w)
+    nsets = args.rotate or max(1, -(-512_000_000 // nbytes))
     device = torch.device("cuda:0")
-    print(f"[bench] generating {args.rotate} input sets of {w.name}", file=sys.stderr, flush=True)
-    host_sets = [W.chain_inputs(w, s) for s in range(args.rotate)]
-    sets = [{k: to_dev(v, device) for k, v in h.items() if isinstance(v, np.ndarray)} for h in host_sets]
-    ws = sv.workspace(sv.SPEC_MODE_CHAIN, B, K, V, sv.SPEC_DTYPE_BF16, device)
-    out_t = torch.empty((B, K + 1), dtype=torch.int32, device=device)
-    out_a = torch.empty((B,), dtype=torch.int32, device=device)
+    print(f"[bench] generating {nsets} input sets of {w.name}", file=sys.stderr, flush=True)
+    host_sets = [W.make_inputs(w, s) for s in range(nsets)]
+    sets = [{k: to_dev(v, device) for k, v in h.items() if isinstance(v, np.ndarray)}
+            for h in host_sets]
     stream = torch.cuda.current_stream(device)
+    dt_code = sv.SPEC_DTYPE_BF16 if w.dtype == "bf16" else sv.SPEC_DTYPE_F32
 
-    def step(i):
-        s = sets[i % len(sets)]
-        sv.spec_verify_chain(s["target"], s["draft"], s["tokens"], s["u_accept"], s["u_sample"],
-                             w.T, out_tokens=out_t, out_accepted=out_a, workspace_buf=ws,
-                             stream=stream)
+    if w.mode == "chain":
+        K = w.K
+        ws = sv.workspace(sv.SPEC_MODE_CHAIN, B, K, V, dt_code, device)
+        out_t = torch.empty((B, K + 1), dtype=torch.int32, device=device)
+        out_a = torch.empty((B,), dtype=torch.int32, device=device)
 
-    def stats_only(i):
-        s = sets[i % len(sets)]
-        sv.spec_verify_chain_stats(s["target"], s["draft"], w.T, ws, stream=stream)
+        def step(i):
+            s = sets[i % nsets]
+            sv.spec_verify_chain(s["target"], s["draft"], s["tokens"], s["u_accept"],
+                                 s["u_sample"], w.T, out_tokens=out_t, out_accepted=out_a,
+                                 workspace_buf=ws, stream=stream)
+
+        def stats_phase(i):
+            s = sets[i % nsets]
+            sv.spec_verify_chain_stats(s["target"], s["draft"], s["tokens"], w.T, ws,
+                                       stream=stream)
+
+        def outputs():
+            diag = torch.empty((B, K + 1, 4), dtype=torch.float32, device=device)
+            s = sets[0]
+            tok, acc, _ = sv.spec_verify_chain(s["target"], s["draft"], s["tokens"], s["u_accept"],
+                                               s["u_sample"], w.T, out_diag=diag)
+            torch.cuda.synchronize()
+            return tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy()
+        dominant_name = "k_chain_fused (one launch per step)"
+        io_bytes = 4 * B * K + 4 * B * (K + 1) + 4 * B * (K + 2)
+        verified = B * K
+    elif w.mode == "greedy":
+        K = w.K
+        ws = sv.workspace(sv.SPEC_MODE_GREEDY, B, K, V, dt_code, device)
+        out_t = torch.empty((B, K + 1), dtype=torch.int32, device=device)
+        out_a = torch.empty((B,), dtype=torch.int32, device=device)
+
+        def step(i):
+            s = sets[i % nsets]
+            sv.spec_verify_greedy(s["target"], s["tokens"], out_tokens=out_t, out_accepted=out_a,
+                                  workspace_buf=ws, stream=stream)
+        stats_phase = None
+
+        def outputs():
+            tok, acc = sv.spec_verify_greedy(sets[0]["target"], sets[0]["tokens"])
+            torch.cuda.synchronize()
+            return tok.cpu().numpy(), acc.cpu().numpy()
+        dominant_name = "k_row_argmax + k_greedy_resolve (whole step)"
+        io_bytes = 4 * B * K + 4 * B * (K + 2)
+        verified = B * K
+    else:
+        par = host_sets[0]["parents"]
+        N = len(par)
+        D = sv.tree_max_depth(par)
+        ws = sv.workspace(sv.SPEC_MODE_TREE, B, N, V, dt_code, device)
+        out_t = torch.empty((B, D + 1), dtype=torch.int32, device=device)
+        out_p = torch.empty((B, D + 1), dtype=torch.int32, device=device)
+        out_d = torch.empty((B,), dtype=torch.int32, device=device)
+
+        def step(i):
+            s = sets[i % nsets]
+            sv.spec_verify_tree_greedy(s["node_logits"], s["node_tokens"], par, out_tokens=out_t,
+                                       out_path=out_p, out_depth=out_d, workspace_buf=ws,
+                                       stream=stream)
+        stats_phase = None
+
+        def outputs():
+            tok, path, depth = sv.spec_verify_tree_greedy(sets[0]["node_logits"],
+                                                          sets[0]["node_tokens"], par)
+            torch.cuda.synchronize()
+            return tok.cpu().numpy(), path.cpu().numpy(), depth.cpu().numpy()
+        dominant_name = "k_row_argmax + k_tree_resolve (whole step)"
+        io_bytes = 4 * B * N + 4 * B * (2 * D + 3)
+        verified = B * (N - 1)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # whole steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
@@ -128,34 +221,39 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # the streaming statistics kernel alone, back to back on the same stream
-    for i in range(args.warmup):
-        stats_only(i)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        stats_only(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_stats = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] {ms_step * 1e3:.2f} us/step, stats kernel {ms_stats * 1e3:.2f} us", file=sys.stderr,
-          flush=True)
+    # The chain step is one kernel launch, so the events around the timed
+    # steps give the dominant kernel's average duration directly.
+    ms_dom = ms_step
+    ms_stats = None
+    if stats_phase is not None:
+        # the streaming phase alone (phase entry point), for reference
+        for i in range(args.warmup):
+            stats_phase(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            stats_phase(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_stats = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {ms_step * 1e3:.2f} us/step"
+          + (f", streaming phase alone {ms_stats * 1e3:.2f} us" if ms_stats else ""),
+          file=sys.stderr, flush=True)
 
-    # outputs of set 0 for the oracle comparison and the emitted-token rate
     step(0)
-    diag = torch.empty((B, K + 1, 4), dtype=torch.float32, device=device)
-    s0 = sets[0]
-    tok, acc, _ = sv.spec_verify_chain(s0["target"], s0["draft"], s0["tokens"], s0["u_accept"],
-                                       s0["u_sample"], w.T, out_diag=diag)
-    torch.cuda.synchronize()
-    gpu_out = (tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy())
-
-    algo_bytes = B * (2 * K + 1) * V * 2                        # every logit read once
-    io_bytes = 4 * B * K + 4 * B * (K + 1) + 4 * B * (K + 2)   # tokens, uniforms, outputs
+    gpu_out = outputs()
     steps_per_s = 1e3 / ms_step
-    achieved_step = (algo_bytes + io_bytes) / (ms_step * 1e-3) / 1e9
-    achieved_stats = algo_bytes / (ms_stats * 1e-3) / 1e9
-    traffic = measured_traffic(algo_bytes)
+    achieved_step = (nbytes + io_bytes) / (ms_step * 1e-3) / 1e9
+    achieved_dom = nbytes / (ms_dom * 1e-3) / 1e9
+    emitted = (gpu_out[1] + 1).sum() if w.mode != "tree" else (gpu_out[2] + 1).sum()
+    config = {"workload": w.name, "mode": w.mode, "B": B, "V": V, "logits": w.dtype,
+              "input_sets_rotated": nsets, "logit_bytes_per_step": nbytes}
+    if w.mode == "chain":
+        config.update(K=w.K, T=w.T)
+    elif w.mode == "greedy":
+        config.update(K=w.K)
+    else:
+        config.update(branching=list(w.branching))
     line = {
         "metric": METRIC,
         "value": steps_per_s,
@@ -169,21 +267,21 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "mode": "chain", "B": B, "K": K, "V": V, "T": w.T,
-                   "logits": "bf16", "input_sets_rotated": args.rotate,
-                   "logit_bytes_per_step": algo_bytes},
+        "config": config,
         "achieved_GBps": achieved_step,
         "frac_of_hbm_peak": achieved_step / HBM_PEAK_GBPS,
-        "tokens_verified_per_s": steps_per_s * B * K,
-        "tokens_emitted_per_s": steps_per_s * float((gpu_out[1] + 1).sum()),
-        "roofline": {"kernel": "k_chain_stats", "bound": "hbm", "achieved": achieved_stats,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved_stats / HBM_PEAK_GBPS,
-                     "traffic": traffic, "avg_launch_us": ms_stats * 1e3,
-                     "algorithmic_bytes_per_launch": algo_bytes},
+        "tokens_verified_per_s": steps_per_s * verified,
+        "tokens_emitted_per_s": steps_per_s * float(emitted),
+        "roofline": {"kernel": dominant_name, "bound": "hbm", "achieved": achieved_dom,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved_dom / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(w.name) if w.mode == "chain" else None,
+                     "avg_launch_us": ms_dom * 1e3, "algorithmic_bytes_per_launch": nbytes},
     }
+    if ms_stats is not None:
+        line["streaming_phase_alone_us"] = ms_stats * 1e3
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(host_sets[0], args.cpu_seconds, gpu_out)
+        line["cpu_baseline"] = cpu_baseline(w, host_sets[0], args.cpu_seconds, gpu_out)
     print(json.dumps(line), flush=True)
 
 

@@ -26,16 +26,19 @@
  *    synchronously and nothing is enqueued then.  SPEC_ERR_LAUNCH reports a
  *    launch failure seen right after enqueueing.
  *  - The workspace (size from spec_verify_workspace_bytes) holds per-call
- *    scratch; its contents need no initialisation and are garbage afterwards.
- *    Calls that share a workspace must be ordered on one stream.
+ *    scratch and needs no initialisation.  Words that spec_verify_chain's
+ *    workgroups hand each other carry a per-call tag (from a process-wide
+ *    call counter), so stale contents of any earlier call are never taken
+ *    for fresh ones.  Calls that share a workspace must be ordered on one
+ *    stream.
  *  - Inputs that break a documented precondition (a drafted token outside
  *    [0, V), a uniform outside [0, 1), NaN or +inf logits, a row that is
  *    entirely -inf) give unspecified outputs but never an out-of-bounds
  *    access: token ids are clamped before they address memory.
  *  - Results are bitwise reproducible run to run (fixed reduction orders, no
  *    floating-point atomics).
- *  - The library keeps no state between calls and is safe to call from
- *    several host threads.
+ *  - The library keeps no state between calls beyond that call counter and is
+ *    safe to call from several host threads.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -107,8 +110,10 @@ spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_
  *                              q = 0 < p, 0 when both are 0).
  *   workspace                  at least spec_verify_workspace_bytes(CHAIN, ...).
  *
- * The step is spec_verify_chain_stats followed by spec_verify_chain_sample on
- * the same stream and workspace.
+ * The step runs as one kernel whose workgroups stream the logits and, for
+ * sequences already streamed, compute the draw while later sequences stream.
+ * spec_verify_chain_stats followed by spec_verify_chain_sample computes the
+ * same outputs with kernel boundaries between the phases.
  */
 spec_status spec_verify_chain(const void *target_logits, const void *draft_logits, spec_dtype dtype,
                               const int32_t *draft_tokens, const float *u_accept,
@@ -120,13 +125,13 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
 /*
  * First phase of the chain verify: one streaming pass over every target and
  * draft logit that leaves each row's softmax statistics (running maximum and
- * sum of exponentials, per vocabulary chunk) in the workspace.  Same argument
- * meaning as spec_verify_chain.
+ * sum of exponentials, per vocabulary chunk) and each row's logit at its
+ * drafted token in the workspace.  Same argument meaning as spec_verify_chain.
  */
 spec_status spec_verify_chain_stats(const void *target_logits, const void *draft_logits,
-                                    spec_dtype dtype, int32_t B, int32_t K, int32_t V,
-                                    float temperature, void *workspace, size_t workspace_bytes,
-                                    hipStream_t stream);
+                                    spec_dtype dtype, const int32_t *draft_tokens, int32_t B,
+                                    int32_t K, int32_t V, float temperature, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Second phase of the chain verify: acceptance of each position, the first
@@ -182,6 +187,29 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
                                     int32_t B, int32_t N, int32_t V, int32_t *out_tokens,
                                     int32_t *out_path, int32_t *out_depth, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Zero-fills a workspace (one small kernel on `stream`).  Optional: a fresh
+ * workspace works as is; zeroing only rules out a 2^-32 chance per word that
+ * uninitialised memory carries the tag of the first call that uses it.
+ * workspace_bytes must be a multiple of 4.  Safe to record in a HIP graph.
+ */
+spec_status spec_verify_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Planning query of the single fused kernel spec_verify_chain launches, for
+ * tests and tooling.  Workgroups run items of four kinds, in rounds: round s
+ * holds items[i] items of kind i for sequence s - lags[i] (kinds in order,
+ * sequences in [0, B)).  The chain uses kind 0 = streaming statistics of one
+ * vocabulary chunk of one row, 1 = resolve (accept tests and first
+ * rejection), 2 = residual/bonus mass of one chunk, 3 = finish (draw and
+ * emit), with lags 0 = lags[0] <= lags[1] <= lags[2] <= lags[3], so every
+ * item's inputs come from items of lower workgroup index.  Writes workgroup
+ * t's (*kind, *seq, *idx) and returns the launch's workgroup count, or -1 for
+ * invalid arguments.  items and lags are host arrays of 4.  Pure host code.
+ */
+int32_t spec_verify_fused_item(int32_t B, const int32_t *items, const int32_t *lags, int64_t t,
+                               int32_t *kind, int32_t *seq, int32_t *idx);
 
 /* Static text for a status code. */
 const char *spec_verify_status_string(spec_status status);

@@ -33,10 +33,10 @@ class SpecVerifyError(RuntimeError):
         super().__init__(f"{fn} failed with status {status} ({text})")
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
@@ -44,14 +44,20 @@ def _load():
                                                 ctypes.POINTER(sz)]
     lib.spec_verify_chain.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f32,
                                       vp, vp, vp, vp, sz, vp]
-    lib.spec_verify_chain_stats.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, f32, vp, sz, vp]
+    lib.spec_verify_chain_stats.argtypes = [vp, vp, ctypes.c_int, vp, i32, i32, i32, f32, vp, sz,
+                                            vp]
     lib.spec_verify_chain_sample.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i32,
                                              f32, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.spec_verify_tree_greedy.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, vp, vp, vp,
                                             vp, sz, vp]
+    lib.spec_verify_workspace_init.argtypes = [vp, sz, vp]
+    lib.spec_verify_fused_item.argtypes = [i32, vp, vp, ctypes.c_int64, ctypes.POINTER(i32),
+                                           ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.spec_verify_fused_item.restype = i32
     for fn in ("spec_verify_workspace_bytes", "spec_verify_chain", "spec_verify_chain_stats",
-               "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy"):
+               "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy",
+               "spec_verify_workspace_init"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -112,9 +118,28 @@ def spec_verify_workspace_bytes(mode: int, B: int, K_or_N: int, V: int, dtype: i
 
 
 def workspace(mode: int, B: int, K_or_N: int, V: int, dtype: int, device) -> torch.Tensor:
-    """A device byte buffer large enough for one call."""
+    """A zero-filled device byte buffer large enough for one call (zero is the
+    state a new workspace must start in; calls leave it there)."""
     n = spec_verify_workspace_bytes(mode, B, K_or_N, V, dtype)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def spec_verify_workspace_init(workspace_buf, *, stream=None):
+    _check_dev("workspace", workspace_buf, torch.uint8)
+    _call("spec_verify_workspace_init", _ptr(workspace_buf), workspace_buf.numel(),
+          _stream(workspace_buf.device, stream))
+
+
+def spec_verify_fused_item(B: int, items, lags, t: int):
+    """(kind, seq, idx, total) of workgroup t of a fused kernel's work order (host query)."""
+    it = (ctypes.c_int32 * 4)(*items)
+    lg = (ctypes.c_int32 * 4)(*lags)
+    k, s, i = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    total = _lib.spec_verify_fused_item(B, it, lg, t, ctypes.byref(k), ctypes.byref(s),
+                                        ctypes.byref(i))
+    if total < 0:
+        raise ValueError("invalid fused-plan query")
+    return k.value, s.value, i.value, total
 
 
 def _chain_check(target, draft, draft_tokens, u_accept, u_sample):
@@ -153,13 +178,15 @@ def spec_verify_chain(target_logits, draft_logits, draft_tokens, u_accept, u_sam
     return out_tokens, out_accepted, out_diag
 
 
-def spec_verify_chain_stats(target_logits, draft_logits, temperature: float, workspace_buf, *,
-                            stream=None):
+def spec_verify_chain_stats(target_logits, draft_logits, draft_tokens, temperature: float,
+                            workspace_buf, *, stream=None):
     """First phase of the chain verify (softmax statistics of every row into the workspace)."""
     dt, B, K, V = _chain_check(target_logits, draft_logits, None, None, None)
+    _check_dev("draft_tokens", draft_tokens, torch.int32, (B, K))
     dev = target_logits.device
-    _call("spec_verify_chain_stats", _ptr(target_logits), _ptr(draft_logits), dt, B, K, V,
-          float(temperature), _ptr(workspace_buf), workspace_buf.numel(), _stream(dev, stream))
+    _call("spec_verify_chain_stats", _ptr(target_logits), _ptr(draft_logits), dt,
+          _ptr(draft_tokens), B, K, V, float(temperature), _ptr(workspace_buf),
+          workspace_buf.numel(), _stream(dev, stream))
 
 
 def spec_verify_chain_sample(target_logits, draft_logits, draft_tokens, u_accept, u_sample,

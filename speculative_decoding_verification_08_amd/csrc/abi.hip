@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "plan.hpp"
 #include "spec_verify.h"
 
@@ -15,11 +17,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Elements per chunk of the streaming pass: the largest power-of-two multiple
-// of 2048 up to 16384 that still gives at least 4096 workgroups (16 per CU on
-// 256 CUs); small problems fall back to 2048.
-int first_pass_chunk(int64_t rows, int V) {
-    int ch = 16384;
+// Elements per chunk of the streaming pass: 16 KB of logits per workgroup,
+// halved (down to 2048 elements) while the grid has fewer than 4096
+// workgroups (16 per CU on 256 CUs).
+int first_pass_chunk(int64_t rows, int V, spec_dtype dtype) {
+    int ch = dtype == SPEC_DTYPE_BF16 ? 8192 : 4096;
     while (ch > 2048 && rows * ((V + ch - 1) / ch) < 4096) ch >>= 1;
     return ch;
 }
@@ -32,26 +34,31 @@ bool valid_sizes(spec_mode mode, int32_t B, int32_t KN, int32_t V) {
     return KN >= 0 && KN <= SPEC_VERIFY_MAX_K;
 }
 
-bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, Plan &p) {
-    if (!valid_sizes(mode, B, KN, V)) return false;
+bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtype, Plan &p) {
+    if (!valid_sizes(mode, B, KN, V) || !valid_dtype(dtype)) return false;
     int64_t rows;
     if (mode == SPEC_MODE_CHAIN) rows = static_cast<int64_t>(B) * (2 * KN + 1);
     else if (mode == SPEC_MODE_GREEDY) rows = static_cast<int64_t>(B) * (KN + 1);
     else rows = static_cast<int64_t>(B) * KN;
     p.rows = rows;
-    p.chunk = first_pass_chunk(rows, V);
+    p.chunk = first_pass_chunk(rows, V, dtype);
     p.nchunk = (V + p.chunk - 1) / p.chunk;
     if (rows * p.nchunk > 0x7fffffffLL) return false;  // one-dimensional grid
     size_t off = 0;
     p.off_partial = off;
-    off += align_up(static_cast<size_t>(rows) * p.nchunk * 8);
     if (mode == SPEC_MODE_CHAIN) {
-        p.nchunk2 = (V + kChunk2 - 1) / kChunk2;
+        off += align_up(static_cast<size_t>(rows) * p.nchunk * 16);
+        p.off_gather = off;
+        off += align_up(static_cast<size_t>(rows) * 8);
+        p.chunk2 = kChunk2Bytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
+        p.nchunk2 = (V + p.chunk2 - 1) / p.chunk2;
         if (static_cast<int64_t>(B) * p.nchunk2 > 0x7fffffffLL) return false;
         p.off_sums = off;
-        off += align_up(static_cast<size_t>(B) * p.nchunk2 * 4);
-        p.off_counters = off;
-        off += align_up(static_cast<size_t>(B) * 4);
+        off += align_up(static_cast<size_t>(B) * p.nchunk2 * 8);
+        p.off_seq = off;
+        off += align_up(static_cast<size_t>(B) * sizeof(SeqInfo));
+    } else {
+        off += align_up(static_cast<size_t>(rows) * p.nchunk * 8);
     }
     p.bytes = off > 0 ? off : kAlign;
     return true;
@@ -64,12 +71,36 @@ T *at(void *ws, size_t off) {
 
 spec_status launch_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH; }
 
+// Fused chain order: statistics items of sequence s, then the resolve item of
+// s - L, the mass items of s - L - 1 and the finish item of s - L - 2, with L
+// rounds ~ the workgroups the chip holds at once, so a sequence's statistics
+// are done by the time its resolve item runs.
+FusedPlan chain_fused_plan(int32_t B, int32_t K, const Plan &plan) {
+    const int32_t A = (2 * K + 1) * plan.nchunk, M = plan.nchunk2;
+    const int32_t round = A + 1 + M + 1;
+    const int32_t L = (kFusedResidentWGs + round - 1) / round;
+    const int32_t n[kKinds] = {A, 1, M, 1};
+    const int32_t lag[kKinds] = {0, L, L + 1, L + 2};
+    return make_fused_plan(B, n, lag);
+}
+
+// Tag of one fused chain call: unique in the process for 2^32 - 2 calls,
+// never 0 (zeroed memory) or the phase entry points' tag.
+uint32_t next_call_tag() {
+    static std::atomic<uint32_t> counter{0};
+    uint32_t t;
+    do {
+        t = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    } while (t <= kPhasedTag);
+    return t;
+}
+
 // Shared validation of the chain entry points.
 spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype, int32_t B,
                         int32_t K, int32_t V, float T, void *ws, size_t ws_bytes, Plan &plan,
                         ChainArgs &a) {
     if (!valid_dtype(dtype) || !(T > 0.f) || isinf(T)) return SPEC_ERR_INVALID_ARG;
-    if (!make_plan(SPEC_MODE_CHAIN, B, K, V, plan)) return SPEC_ERR_INVALID_ARG;
+    if (!make_plan(SPEC_MODE_CHAIN, B, K, V, dtype, plan)) return SPEC_ERR_INVALID_ARG;
     if (B == 0) return SPEC_OK;
     if (!target || !aligned(target, 16)) return SPEC_ERR_INVALID_ARG;
     if (K > 0 && (!draft || !aligned(draft, 16))) return SPEC_ERR_INVALID_ARG;
@@ -84,9 +115,11 @@ spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype,
     a.chunk = plan.chunk;
     a.nchunk = plan.nchunk;
     a.nchunk2 = plan.nchunk2;
-    a.partial = at<float2>(ws, plan.off_partial);
-    a.sums = at<float>(ws, plan.off_sums);
-    a.counters = at<uint32_t>(ws, plan.off_counters);
+    a.partial = at<uint64_t>(ws, plan.off_partial);
+    a.gathered = at<uint64_t>(ws, plan.off_gather);
+    a.sums = at<uint64_t>(ws, plan.off_sums);
+    a.tag = kPhasedTag;
+    a.seq = at<SeqInfo>(ws, plan.off_seq);
     return SPEC_OK;
 }
 
@@ -131,20 +164,22 @@ spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_
     if (mode != SPEC_MODE_CHAIN && mode != SPEC_MODE_GREEDY && mode != SPEC_MODE_TREE)
         return SPEC_ERR_INVALID_ARG;
     Plan p;
-    if (!make_plan(mode, B, K_or_N, V, p)) return SPEC_ERR_INVALID_ARG;
+    if (!make_plan(mode, B, K_or_N, V, dtype, p)) return SPEC_ERR_INVALID_ARG;
     *bytes = p.bytes;
     return SPEC_OK;
 }
 
 spec_status spec_verify_chain_stats(const void *target_logits, const void *draft_logits,
-                                    spec_dtype dtype, int32_t B, int32_t K, int32_t V,
-                                    float temperature, void *workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
+                                    spec_dtype dtype, const int32_t *draft_tokens, int32_t B,
+                                    int32_t K, int32_t V, float temperature, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
     Plan plan;
     ChainArgs a;
     spec_status st = chain_setup(target_logits, draft_logits, dtype, B, K, V, temperature,
                                  workspace, workspace_bytes, plan, a);
     if (st != SPEC_OK || B == 0) return st;
+    if (K > 0 && (!draft_tokens || !aligned(draft_tokens, 4))) return SPEC_ERR_INVALID_ARG;
+    a.tokens = draft_tokens;
     return launch_status(launch_chain_stats(a, dtype, stream));
 }
 
@@ -179,9 +214,36 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
     st = chain_sample_args(draft_tokens, u_accept, u_sample, B, K, out_tokens, out_accepted,
                            out_diag, a);
     if (st != SPEC_OK) return st;
-    st = launch_status(launch_chain_stats(a, dtype, stream));
-    if (st != SPEC_OK) return st;
-    return launch_status(launch_chain_sample(a, dtype, stream));
+    a.tag = next_call_tag();
+    const FusedPlan f = chain_fused_plan(B, K, plan);
+    if (f.total > 0x7fffffffLL) return SPEC_ERR_INVALID_ARG;
+    return launch_status(launch_chain_fused(a, f, dtype, stream));
+}
+
+spec_status spec_verify_workspace_init(void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    if (!workspace || !aligned(workspace, 16) || workspace_bytes % 4 != 0)
+        return SPEC_ERR_INVALID_ARG;
+    return launch_status(launch_zero_words(static_cast<uint32_t *>(workspace),
+                                           static_cast<int64_t>(workspace_bytes / 4), stream));
+}
+
+int32_t spec_verify_fused_item(int32_t B, const int32_t *items, const int32_t *lags, int64_t t,
+                               int32_t *kind, int32_t *seq, int32_t *idx) {
+    if (B < 1 || !items || !lags || !kind || !seq || !idx) return -1;
+    if (lags[0] != 0) return -1;
+    for (int i = 0; i < kKinds; ++i) {
+        if (items[i] < 0 || lags[i] < 0 || lags[i] > (1 << 20)) return -1;
+        if (i > 0 && lags[i] < lags[i - 1]) return -1;
+    }
+    const FusedPlan f = make_fused_plan(B, items, lags);
+    if (t < 0 || t >= f.total) return -1;
+    int k, s, i;
+    fused_item(f, t, k, s, i);
+    *kind = k;
+    *seq = s;
+    *idx = i;
+    return static_cast<int32_t>(f.total > 0x7fffffffLL ? -1 : f.total);
 }
 
 spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
@@ -190,7 +252,7 @@ spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
                                size_t workspace_bytes, hipStream_t stream) {
     if (!valid_dtype(dtype)) return SPEC_ERR_INVALID_ARG;
     Plan plan;
-    if (!make_plan(SPEC_MODE_GREEDY, B, K, V, plan)) return SPEC_ERR_INVALID_ARG;
+    if (!make_plan(SPEC_MODE_GREEDY, B, K, V, dtype, plan)) return SPEC_ERR_INVALID_ARG;
     if (B == 0) return SPEC_OK;
     if (!target_logits || !aligned(target_logits, 16)) return SPEC_ERR_INVALID_ARG;
     if ((K > 0 && (!draft_tokens || !aligned(draft_tokens, 4))) || !out_tokens ||
@@ -225,7 +287,7 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
                                     size_t workspace_bytes, hipStream_t stream) {
     if (!valid_dtype(dtype) || !parents) return SPEC_ERR_INVALID_ARG;
     Plan plan;
-    if (!make_plan(SPEC_MODE_TREE, B, N, V, plan)) return SPEC_ERR_INVALID_ARG;
+    if (!make_plan(SPEC_MODE_TREE, B, N, V, dtype, plan)) return SPEC_ERR_INVALID_ARG;
     TreeArgs t;
     memset(&t, 0, sizeof t);
     if (parents[0] != -1) return SPEC_ERR_INVALID_ARG;

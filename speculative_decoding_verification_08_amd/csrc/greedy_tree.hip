@@ -191,9 +191,9 @@ __global__ __launch_bounds__(kMaxTreeNodes) void k_tree_resolve(TreeArgs a) {
 hipError_t launch_row_argmax(const ArgmaxArgs &a, int dtype, hipStream_t s) {
     const int64_t grid = a.rows * a.nchunk;
     if (dtype == 1)
-        k_row_argmax<Bf16, 8><<<dim3(static_cast<uint32_t>(grid)), dim3(kWG), 0, s>>>(a);
+        k_row_argmax<Bf16, 4><<<dim3(static_cast<uint32_t>(grid)), dim3(kWG), 0, s>>>(a);
     else
-        k_row_argmax<F32, 8><<<dim3(static_cast<uint32_t>(grid)), dim3(kWG), 0, s>>>(a);
+        k_row_argmax<F32, 4><<<dim3(static_cast<uint32_t>(grid)), dim3(kWG), 0, s>>>(a);
     return hipGetLastError();
 }
 

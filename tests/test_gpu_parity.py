@@ -116,13 +116,31 @@ def test_chain_phases_equal_one_call(sv):
     t, dr = dev(d["target"]), dev(d["draft"])
     B, K, V = d["tokens"].shape[0], d["tokens"].shape[1], t.shape[-1]
     ws = sv.workspace(sv.SPEC_MODE_CHAIN, B, K, V, sv.SPEC_DTYPE_BF16, DEV)
-    sv.spec_verify_chain_stats(t, dr, 1.0, ws)
+    sv.spec_verify_chain_stats(t, dr, dev(d["tokens"]), 1.0, ws)
     diag = torch.empty((B, K + 1, 4), dtype=torch.float32, device=DEV)
     tok, acc, _ = sv.spec_verify_chain_sample(t, dr, dev(d["tokens"]), dev(d["u_accept"]),
                                               dev(d["u_sample"]), 1.0, ws, out_diag=diag)
     torch.cuda.synchronize()
     assert np.array_equal(tok.cpu().numpy(), one[0]) and np.array_equal(acc.cpu().numpy(), one[1])
     assert np.array_equal(diag.cpu().numpy(), one[2])
+
+
+def test_chain_workspace_reuse_across_shapes(sv):
+    """One workspace serves consecutive calls of different shapes: each call
+    leaves the fused kernel's counters at zero for the next."""
+    big = sv.spec_verify_workspace_bytes(sv.SPEC_MODE_CHAIN, 24, 8, 50000, sv.SPEC_DTYPE_F32)
+    ws = torch.empty(big, dtype=torch.uint8, device=DEV)
+    sv.spec_verify_workspace_init(ws)
+    shapes = [(24, 8, 50000, "f32"), (3, 2, 7000, "bf16"), (24, 8, 50000, "f32"), (1, 0, 333, "f32"),
+              (17, 5, 20001, "bf16"), (24, 8, 50000, "f32")]
+    for i, (B, K, V, dt) in enumerate(shapes):
+        case(f"workspace reuse call {i}: B={B} K={K} V={V} {dt}")
+        d = chain_case("reuse", B, K, V, dt, 0.9, recipe="peaked", sigma=0.7, step=i)
+        tok, acc, diag = sv.spec_verify_chain(dev(d["target"]), dev(d["draft"]), dev(d["tokens"]),
+                                              dev(d["u_accept"]), dev(d["u_sample"]), d["T"],
+                                              diag=True, workspace_buf=ws)
+        torch.cuda.synchronize()
+        parity.check_chain(d, tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy())
 
 
 def test_chain_full_size_128k(sv):
