@@ -7,9 +7,8 @@ resident in HBM before timing; enough input sets rotate (3 here, 542 MB) that
 the 256 MB Infinity Cache cannot hold the working set between steps.
 `--workload` measures the other workloads the same way.
 
-Prints one JSON line.  `roofline` covers the fused chain kernel (one launch per
-step, so the HIP events around the timed steps on the launch stream give its
-average duration);
+Prints one JSON line.  `roofline` covers the streaming statistics kernel (the
+dominant one), timed alone, back to back, with HIP events on the launch stream;
 `cpu_baseline` times the fp64 oracle on a bounded sample on the host.
 """
 from __future__ import annotations
@@ -49,7 +48,7 @@ def to_dev(a, device):
 def measured_traffic(workload: str):
     """HBM bytes per launch of the statistics kernel from the committed PMC
     summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"k_chain_fused_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"k_chain_stats_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     t = json.load(open(path))
@@ -115,6 +114,9 @@ def main():
                     help="input sets cycled through (default: enough to exceed 512 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run device-to-device copies of this many MB (to scale HBM "
+                         "traffic counters against a copy of known size)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verify step runs independently per "
@@ -124,6 +126,16 @@ def main():
 
     import torch
     import speculative_decoding_verification_08_amd as sv
+
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": max(args.steps, 1)}), flush=True)
+        return
 
     w = W.WORKLOADS[args.workload]
     B, V = w.B, w.V
@@ -161,7 +173,7 @@ def main():
                                                s["u_sample"], w.T, out_diag=diag)
             torch.cuda.synchronize()
             return tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy()
-        dominant_name = "k_chain_fused (one launch per step)"
+        dominant_name = "k_chain_stats"
         io_bytes = 4 * B * K + 4 * B * (K + 1) + 4 * B * (K + 2)
         verified = B * K
     elif w.mode == "greedy":
@@ -221,12 +233,11 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # The chain step is one kernel launch, so the events around the timed
-    # steps give the dominant kernel's average duration directly.
+    # The dominant kernel alone (the streaming statistics phase of the chain
+    # verify), back to back on the launch stream.  Greedy and tree steps are
+    # reported whole.
     ms_dom = ms_step
-    ms_stats = None
     if stats_phase is not None:
-        # the streaming phase alone (phase entry point), for reference
         for i in range(args.warmup):
             stats_phase(i)
         torch.cuda.synchronize()
@@ -235,9 +246,8 @@ def main():
             stats_phase(i)
         e1.record(stream)
         torch.cuda.synchronize()
-        ms_stats = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] {ms_step * 1e3:.2f} us/step"
-          + (f", streaming phase alone {ms_stats * 1e3:.2f} us" if ms_stats else ""),
+        ms_dom = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {ms_step * 1e3:.2f} us/step, {dominant_name} {ms_dom * 1e3:.2f} us",
           file=sys.stderr, flush=True)
 
     step(0)
@@ -277,8 +287,6 @@ def main():
                      "traffic": measured_traffic(w.name) if w.mode == "chain" else None,
                      "avg_launch_us": ms_dom * 1e3, "algorithmic_bytes_per_launch": nbytes},
     }
-    if ms_stats is not None:
-        line["streaming_phase_alone_us"] = ms_stats * 1e3
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, host_sets[0], args.cpu_seconds, gpu_out)

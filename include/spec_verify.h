@@ -26,11 +26,10 @@
  *    synchronously and nothing is enqueued then.  SPEC_ERR_LAUNCH reports a
  *    launch failure seen right after enqueueing.
  *  - The workspace (size from spec_verify_workspace_bytes) holds per-call
- *    scratch and needs no initialisation.  Words that spec_verify_chain's
- *    workgroups hand each other carry a per-call tag (from a process-wide
- *    call counter), so stale contents of any earlier call are never taken
- *    for fresh ones.  Calls that share a workspace must be ordered on one
- *    stream.
+ *    scratch and needs no initialisation.  Words the chain verify's kernels
+ *    hand each other carry a per-call tag (from a process-wide call counter),
+ *    so contents left by any earlier call are never taken for fresh ones.
+ *    Calls that share a workspace must be ordered on one stream.
  *  - Inputs that break a documented precondition (a drafted token outside
  *    [0, V), a uniform outside [0, 1), NaN or +inf logits, a row that is
  *    entirely -inf) give unspecified outputs but never an out-of-bounds
@@ -110,10 +109,10 @@ spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_
  *                              q = 0 < p, 0 when both are 0).
  *   workspace                  at least spec_verify_workspace_bytes(CHAIN, ...).
  *
- * The step runs as one kernel whose workgroups stream the logits and, for
- * sequences already streamed, compute the draw while later sequences stream.
- * spec_verify_chain_stats followed by spec_verify_chain_sample computes the
- * same outputs with kernel boundaries between the phases.
+ * The step is spec_verify_chain_stats followed by spec_verify_chain_sample on
+ * the same stream and workspace (two kernels).  If out_accepted[b] is -1 the
+ * sample phase found statistics not written by this call's statistics phase
+ * (only possible through the phase entry points) and out_tokens[b] is all -1.
  */
 spec_status spec_verify_chain(const void *target_logits, const void *draft_logits, spec_dtype dtype,
                               const int32_t *draft_tokens, const float *u_accept,
@@ -137,7 +136,8 @@ spec_status spec_verify_chain_stats(const void *target_logits, const void *draft
  * Second phase of the chain verify: acceptance of each position, the first
  * rejection j, and the residual or bonus draw, reading the statistics the
  * first phase left in the same workspace.  Must follow spec_verify_chain_stats
- * with identical logits, sizes and temperature on the same stream.
+ * with identical logits, tokens, sizes and temperature on the same stream;
+ * sequences whose statistics are missing get out_accepted = -1.
  */
 spec_status spec_verify_chain_sample(const void *target_logits, const void *draft_logits,
                                      spec_dtype dtype, const int32_t *draft_tokens,
@@ -187,29 +187,6 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
                                     int32_t B, int32_t N, int32_t V, int32_t *out_tokens,
                                     int32_t *out_path, int32_t *out_depth, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
-
-/*
- * Zero-fills a workspace (one small kernel on `stream`).  Optional: a fresh
- * workspace works as is; zeroing only rules out a 2^-32 chance per word that
- * uninitialised memory carries the tag of the first call that uses it.
- * workspace_bytes must be a multiple of 4.  Safe to record in a HIP graph.
- */
-spec_status spec_verify_workspace_init(void *workspace, size_t workspace_bytes, hipStream_t stream);
-
-/*
- * Planning query of the single fused kernel spec_verify_chain launches, for
- * tests and tooling.  Workgroups run items of four kinds, in rounds: round s
- * holds items[i] items of kind i for sequence s - lags[i] (kinds in order,
- * sequences in [0, B)).  The chain uses kind 0 = streaming statistics of one
- * vocabulary chunk of one row, 1 = resolve (accept tests and first
- * rejection), 2 = residual/bonus mass of one chunk, 3 = finish (draw and
- * emit), with lags 0 = lags[0] <= lags[1] <= lags[2] <= lags[3], so every
- * item's inputs come from items of lower workgroup index.  Writes workgroup
- * t's (*kind, *seq, *idx) and returns the launch's workgroup count, or -1 for
- * invalid arguments.  items and lags are host arrays of 4.  Pure host code.
- */
-int32_t spec_verify_fused_item(int32_t B, const int32_t *items, const int32_t *lags, int64_t t,
-                               int32_t *kind, int32_t *seq, int32_t *idx);
 
 /* Static text for a status code. */
 const char *spec_verify_status_string(spec_status status);

@@ -51,13 +51,8 @@ def _load(path: str = LIB_PATH):
     lib.spec_verify_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.spec_verify_tree_greedy.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, vp, vp, vp,
                                             vp, sz, vp]
-    lib.spec_verify_workspace_init.argtypes = [vp, sz, vp]
-    lib.spec_verify_fused_item.argtypes = [i32, vp, vp, ctypes.c_int64, ctypes.POINTER(i32),
-                                           ctypes.POINTER(i32), ctypes.POINTER(i32)]
-    lib.spec_verify_fused_item.restype = i32
     for fn in ("spec_verify_workspace_bytes", "spec_verify_chain", "spec_verify_chain_stats",
-               "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy",
-               "spec_verify_workspace_init"):
+               "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -118,28 +113,9 @@ def spec_verify_workspace_bytes(mode: int, B: int, K_or_N: int, V: int, dtype: i
 
 
 def workspace(mode: int, B: int, K_or_N: int, V: int, dtype: int, device) -> torch.Tensor:
-    """A zero-filled device byte buffer large enough for one call (zero is the
-    state a new workspace must start in; calls leave it there)."""
+    """A device byte buffer large enough for one call (no initialisation needed)."""
     n = spec_verify_workspace_bytes(mode, B, K_or_N, V, dtype)
-    return torch.zeros(n, dtype=torch.uint8, device=device)
-
-
-def spec_verify_workspace_init(workspace_buf, *, stream=None):
-    _check_dev("workspace", workspace_buf, torch.uint8)
-    _call("spec_verify_workspace_init", _ptr(workspace_buf), workspace_buf.numel(),
-          _stream(workspace_buf.device, stream))
-
-
-def spec_verify_fused_item(B: int, items, lags, t: int):
-    """(kind, seq, idx, total) of workgroup t of a fused kernel's work order (host query)."""
-    it = (ctypes.c_int32 * 4)(*items)
-    lg = (ctypes.c_int32 * 4)(*lags)
-    k, s, i = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    total = _lib.spec_verify_fused_item(B, it, lg, t, ctypes.byref(k), ctypes.byref(s),
-                                        ctypes.byref(i))
-    if total < 0:
-        raise ValueError("invalid fused-plan query")
-    return k.value, s.value, i.value, total
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def _chain_check(target, draft, draft_tokens, u_accept, u_sample):

@@ -55,8 +55,8 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
         if (static_cast<int64_t>(B) * p.nchunk2 > 0x7fffffffLL) return false;
         p.off_sums = off;
         off += align_up(static_cast<size_t>(B) * p.nchunk2 * 8);
-        p.off_seq = off;
-        off += align_up(static_cast<size_t>(B) * sizeof(SeqInfo));
+        p.off_counters = off;
+        off += align_up(static_cast<size_t>(B) * 4);
     } else {
         off += align_up(static_cast<size_t>(rows) * p.nchunk * 8);
     }
@@ -71,20 +71,7 @@ T *at(void *ws, size_t off) {
 
 spec_status launch_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH; }
 
-// Fused chain order: statistics items of sequence s, then the resolve item of
-// s - L, the mass items of s - L - 1 and the finish item of s - L - 2, with L
-// rounds ~ the workgroups the chip holds at once, so a sequence's statistics
-// are done by the time its resolve item runs.
-FusedPlan chain_fused_plan(int32_t B, int32_t K, const Plan &plan) {
-    const int32_t A = (2 * K + 1) * plan.nchunk, M = plan.nchunk2;
-    const int32_t round = A + 1 + M + 1;
-    const int32_t L = (kFusedResidentWGs + round - 1) / round;
-    const int32_t n[kKinds] = {A, 1, M, 1};
-    const int32_t lag[kKinds] = {0, L, L + 1, L + 2};
-    return make_fused_plan(B, n, lag);
-}
-
-// Tag of one fused chain call: unique in the process for 2^32 - 2 calls,
+// Tag of one spec_verify_chain call: unique in the process for 2^32 - 2 calls,
 // never 0 (zeroed memory) or the phase entry points' tag.
 uint32_t next_call_tag() {
     static std::atomic<uint32_t> counter{0};
@@ -118,8 +105,8 @@ spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype,
     a.partial = at<uint64_t>(ws, plan.off_partial);
     a.gathered = at<uint64_t>(ws, plan.off_gather);
     a.sums = at<uint64_t>(ws, plan.off_sums);
+    a.counters = at<uint32_t>(ws, plan.off_counters);
     a.tag = kPhasedTag;
-    a.seq = at<SeqInfo>(ws, plan.off_seq);
     return SPEC_OK;
 }
 
@@ -197,7 +184,7 @@ spec_status spec_verify_chain_sample(const void *target_logits, const void *draf
     st = chain_sample_args(draft_tokens, u_accept, u_sample, B, K, out_tokens, out_accepted,
                            out_diag, a);
     if (st != SPEC_OK) return st;
-    return launch_status(launch_chain_sample(a, dtype, stream));
+    return launch_status(launch_chain_tail(a, dtype, stream));
 }
 
 spec_status spec_verify_chain(const void *target_logits, const void *draft_logits,
@@ -215,35 +202,9 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
                            out_diag, a);
     if (st != SPEC_OK) return st;
     a.tag = next_call_tag();
-    const FusedPlan f = chain_fused_plan(B, K, plan);
-    if (f.total > 0x7fffffffLL) return SPEC_ERR_INVALID_ARG;
-    return launch_status(launch_chain_fused(a, f, dtype, stream));
-}
-
-spec_status spec_verify_workspace_init(void *workspace, size_t workspace_bytes,
-                                       hipStream_t stream) {
-    if (!workspace || !aligned(workspace, 16) || workspace_bytes % 4 != 0)
-        return SPEC_ERR_INVALID_ARG;
-    return launch_status(launch_zero_words(static_cast<uint32_t *>(workspace),
-                                           static_cast<int64_t>(workspace_bytes / 4), stream));
-}
-
-int32_t spec_verify_fused_item(int32_t B, const int32_t *items, const int32_t *lags, int64_t t,
-                               int32_t *kind, int32_t *seq, int32_t *idx) {
-    if (B < 1 || !items || !lags || !kind || !seq || !idx) return -1;
-    if (lags[0] != 0) return -1;
-    for (int i = 0; i < kKinds; ++i) {
-        if (items[i] < 0 || lags[i] < 0 || lags[i] > (1 << 20)) return -1;
-        if (i > 0 && lags[i] < lags[i - 1]) return -1;
-    }
-    const FusedPlan f = make_fused_plan(B, items, lags);
-    if (t < 0 || t >= f.total) return -1;
-    int k, s, i;
-    fused_item(f, t, k, s, i);
-    *kind = k;
-    *seq = s;
-    *idx = i;
-    return static_cast<int32_t>(f.total > 0x7fffffffLL ? -1 : f.total);
+    st = launch_status(launch_chain_stats(a, dtype, stream));
+    if (st != SPEC_OK) return st;
+    return launch_status(launch_chain_tail(a, dtype, stream));
 }
 
 spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,

@@ -1,32 +1,30 @@
-// Chain verify at T > 0 on gfx950.
+// Chain verify at T > 0 on gfx950: two kernels in stream order.
 //
-// Three kinds of work, written once as workgroup-level item functions:
+// k_chain_stats streams every logit of the step once.  One workgroup takes one
+// 16 KB vocabulary chunk of one row (target rows 0..K and draft rows 0..K-1 of
+// a sequence), folds it into softmax statistics (ref, z) and publishes them;
+// the workgroup whose chunk holds the row's drafted token also publishes that
+// logit.  This is the HBM-bound pass that carries the bytes.
 //
-//  stats item  (sequence b, row r, vocabulary chunk): streams one 16 KB chunk
-//      of a target row (rows 0..K) or draft row (0..K-1) once, folds it into
-//      softmax statistics (ref, z) and publishes them; the chunk holding the
-//      row's drafted token also publishes that logit.  These items carry all
-//      the logit bytes: the HBM-bound part.
-//  resolve item (sequence b): merges the sequence's row statistics,
-//      evaluates the accept test of every drafted token (u < p(x)/q(x),
-//      French lesson "La règle de l'exactitude"; forum post §3), finds the
-//      first rejection j and publishes j with row j's statistics.
-//  mass item   (sequence b, 16 KB chunk of row j): publishes the draw mass of
-//      its chunk: max(0, p_j - q_j) after a rejection (the residual of the
-//      same passages) or p_K when every draft was accepted (the bonus draw).
-//  finish item (sequence b): finds the chunk whose running mass first exceeds
-//      u * S, scans that chunk in index order and writes the emitted tokens.
+// k_chain_tail runs one workgroup per (sequence b, 16 KB chunk of a row).
+// Each merges the sequence's row statistics, evaluates the accept test of
+// every drafted token (u < p(x)/q(x), French lesson "La règle de
+// l'exactitude"; forum post §3) and finds the first rejection j.  It then
+// sums the draw weights of its chunk of row j: max(0, p_j - q_j) after a
+// rejection (the residual of the same passages) or p_K when every draft was
+// accepted (the bonus draw), publishes that mass and counts itself done.  The
+// last workgroup of the sequence to finish finds the chunk whose running mass
+// first exceeds u * S, scans that chunk in index order and writes the emitted
+// tokens.
 //
-// spec_verify_chain runs them as one fused kernel: workgroup t executes the
-// t-th item of an order in which every item depends only on items with lower
-// indices (fused_item), so a sequence's resolve, mass and finish work overlap
-// the streaming of later sequences.  Items hand over 64-bit words holding the call's tag
-// and a value, written and read with device-scope relaxed atomics (coherent
-// across the XCDs' L2 caches without fences); a reader waits, for a bounded
-// time, until every word it needs carries the current tag.  The phase entry
-// points run the same items as four ordinary kernels, where the kernel
-// boundary has already made every word current.  Device-scope fences, an L2
-// write-back and invalidate per workgroup on this chip, are not used.
+// Hand-over words are 64 bits: the call's tag above a 32-bit value.  Between
+// the kernels the boundary orders everything; inside the tail kernel a chunk
+// mass is published with a device-scope atomic exchange that has returned
+// before the counter increment, and read with device-scope atomic loads, so
+// no fence (an L2 write-back and invalidate per workgroup on this chip) is
+// needed.  The tags let the tail kernel check that every word it reads was
+// written for this call.  The per-sequence counters are zeroed by the
+// statistics kernel, so the workspace needs no initialisation.
 #include "device.hpp"
 #include "plan.hpp"
 
@@ -35,13 +33,24 @@ namespace {
 
 // ------------------------------------------------------------ hand-over
 
-__device__ __forceinline__ void publish(uint64_t *p, uint32_t tag, uint32_t bits) {
-    __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | bits, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+// Words the statistics kernel leaves for the tail kernel: plain stores and
+// loads (the kernel boundary orders them, and the tail kernel's workgroups of
+// one sequence share them through L2).
+__device__ __forceinline__ void put_f32(uint64_t *p, uint32_t tag, float v) {
+    *p = (static_cast<uint64_t>(tag) << 32) | __float_as_uint(v);
 }
-__device__ __forceinline__ void publish_f32(uint64_t *p, uint32_t tag, float v) {
-    publish(p, tag, __float_as_uint(v));
+// Keeps an atomic's returned value alive, so the atomic is issued with return
+// and a later s_waitcnt covers its completion.
+__device__ __forceinline__ void keep(uint64_t v) {
+    asm volatile("" ::"v"(static_cast<uint32_t>(v)), "v"(static_cast<uint32_t>(v >> 32)));
 }
+// Publish and wait until the exchange has been performed device-wide.
+__device__ __forceinline__ void publish_f32_sync(uint64_t *p, uint32_t tag, float v) {
+    keep(__hip_atomic_exchange(p, (static_cast<uint64_t>(tag) << 32) | __float_as_uint(v),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __builtin_amdgcn_s_waitcnt(0);
+}
+// Words exchanged inside the tail kernel: device-scope atomics.
 __device__ __forceinline__ uint64_t fetch(const uint64_t *p) {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -51,21 +60,6 @@ __device__ __forceinline__ bool current(uint64_t w, uint32_t tag) {
 }
 __device__ __forceinline__ float word_f32(uint64_t w) {
     return __uint_as_float(static_cast<uint32_t>(w));
-}
-__device__ __forceinline__ uint32_t word_u32(uint64_t w) { return static_cast<uint32_t>(w); }
-
-// Bounded wait of a workgroup: `stale` is this thread's count of words still
-// carrying an old tag.  Returns 1 when no thread has one, 0 to poll again,
-// -1 once 0.2 s of the 100 MHz wall clock have passed (or at once when the
-// workgroup may not wait).
-constexpr uint64_t kWaitLimitTicks = 20000000ull;
-__device__ __forceinline__ int poll_done(int stale, bool may_wait, uint64_t t0) {
-    if (!__syncthreads_or(stale)) return 1;
-    const int expired =
-        threadIdx.x == 0 && (!may_wait || wall_clock64() - t0 > kWaitLimitTicks);
-    if (__syncthreads_or(expired)) return -1;
-    __builtin_amdgcn_s_sleep(2);
-    return 0;
 }
 
 // ------------------------------------------------------------ stats item
@@ -126,13 +120,13 @@ __device__ __forceinline__ void stats_item(const ChainArgs &a, int64_t row, int 
     if (threadIdx.x == 0 && k >= 0) {
         const int x = min(max(a.tokens[b * K + k], 0), V - 1);
         if (x >= e0 && x < e1)
-            publish_f32(&a.gathered[row], a.tag, load_one<DT>(base, trow * V + x));
+            put_f32(&a.gathered[row], a.tag, load_one<DT>(base, trow * V + x));
     }
     mz_reduce_wg(ref, z);
     if (threadIdx.x == 0) {
         uint64_t *w = a.partial + 2 * (row * a.nchunk + ch);
-        publish_f32(w, a.tag, ref);
-        publish_f32(w + 1, a.tag, z);
+        put_f32(w, a.tag, ref);
+        put_f32(w + 1, a.tag, z);
     }
 }
 
@@ -211,9 +205,14 @@ __device__ __forceinline__ float lane_mass(const ChainArgs &a, const DrawRow &w,
 // every drafted token.  Returns j, the first rejected position (K if none),
 // with row j's statistics in `w` and p_k(x_k), q_k(x_k) in s_P, s_Q; sets
 // `ok` to false if the wait ran out.
+// Merges sequence b's row statistics over chunks (in chunk order) and
+// evaluates the accept test of every drafted token.  Returns j, the first
+// rejected position (K if none), with row j's statistics in `w` and
+// p_k(x_k), q_k(x_k) in s_P, s_Q; `ok` is false if a word was not written for
+// this call (the statistics phase did not run with these arguments).
 template <class DT>
-__device__ int accept_prefix(const ChainArgs &a, int b, bool may_wait, float *s_P, float *s_Q,
-                             DrawRow &w, bool &ok) {
+__device__ int accept_prefix(const ChainArgs &a, int b, float *s_P, float *s_Q, DrawRow &w,
+                             bool &ok) {
     __shared__ float s_ref[2 * kMaxK + 1], s_z[2 * kMaxK + 1];
     __shared__ float s_pr[kMergeLds], s_pz[kMergeLds];
     __shared__ int s_j;
@@ -222,45 +221,45 @@ __device__ int accept_prefix(const ChainArgs &a, int b, bool may_wait, float *s_
     const uint64_t *part = a.partial + 2 * static_cast<int64_t>(b) * np;
     const uint64_t *gat = a.gathered + static_cast<int64_t>(b) * R;
     const bool staged = np <= kMergeLds;
+    // One round trip: partials, drafted-token logits and uniforms together.
+    int stale = 0;
     float lt = 0.f, ld = 0.f;
     const float u = tid < K ? a.u_accept[b * K + tid] : 0.f;
-    const uint64_t t0 = wall_clock64();
-    ok = true;
-    for (;;) {
-        int stale = 0;
+    if (tid < K) {
+        const uint64_t wt = gat[tid], wd = gat[K + 1 + tid];
+        stale |= !current(wt, a.tag) || !current(wd, a.tag);
+        lt = word_f32(wt);
+        ld = word_f32(wd);
+    }
+    if (staged) {
         for (int i = tid; i < np; i += kWG) {
-            const uint64_t wr = fetch(part + 2 * i), wz = fetch(part + 2 * i + 1);
-            if (!current(wr, a.tag) || !current(wz, a.tag)) {
-                stale = 1;
-            } else if (staged) {
-                s_pr[i] = word_f32(wr);
-                s_pz[i] = word_f32(wz);
-            }
-        }
-        if (tid < K) {
-            const uint64_t wt = fetch(gat + tid), wd = fetch(gat + K + 1 + tid);
-            if (!current(wt, a.tag) || !current(wd, a.tag)) stale = 1;
-            lt = word_f32(wt);
-            ld = word_f32(wd);
-        }
-        const int st = poll_done(stale, may_wait, t0);
-        if (st == 1) break;
-        if (st < 0) {
-            ok = false;
-            break;
+            const uint64_t wr = part[2 * i], wz = part[2 * i + 1];
+            stale |= !current(wr, a.tag) || !current(wz, a.tag);
+            s_pr[i] = word_f32(wr);
+            s_pz[i] = word_f32(wz);
         }
     }
+    ok = !__syncthreads_or(stale);
     for (int r = tid; r < R; r += kWG) {
         float ref = -INFINITY, z = 0.f;
         for (int i = 0; i < a.nchunk; ++i) {
             const int q = r * a.nchunk + i;
-            const float pr = staged ? s_pr[q] : word_f32(fetch(part + 2 * q));
-            const float pz = staged ? s_pz[q] : word_f32(fetch(part + 2 * q + 1));
+            float pr, pz;
+            if (staged) {
+                pr = s_pr[q];
+                pz = s_pz[q];
+            } else {
+                const uint64_t wr = part[2 * q], wz = part[2 * q + 1];
+                if (!current(wr, a.tag) || !current(wz, a.tag)) ok = false;
+                pr = word_f32(wr);
+                pz = word_f32(wz);
+            }
             mz_merge(ref, z, pr, pz);
         }
         s_ref[r] = ref;
         s_z[r] = z;
     }
+    if (!staged) ok = !__syncthreads_or(!ok);
     __syncthreads();
     // Accept test u < P/Q (strict; Q = 0 accepts iff P > 0), wave 0, K <= 64.
     if (tid < kWave) {
@@ -287,141 +286,52 @@ __device__ int accept_prefix(const ChainArgs &a, int b, bool may_wait, float *s_
     return j;
 }
 
-// Row j's record as the resolve item published it: waits (bounded) until the
-// five words are current; returns false on a timeout.
-__device__ __forceinline__ bool wait_record(const ChainArgs &a, int b, bool may_wait,
-                                            uint64_t *s_info) {
-    SeqInfo &si = a.seq[b];
-    const uint64_t t0 = wall_clock64();
-    for (;;) {
-        int stale = 0;
-        if (threadIdx.x < 5) {
-            const uint64_t *f = threadIdx.x == 0   ? &si.j
-                                : threadIdx.x == 1 ? &si.rt
-                                : threadIdx.x == 2 ? &si.izt
-                                : threadIdx.x == 3 ? &si.rd
-                                                   : &si.izd;
-            const uint64_t v = fetch(f);
-            if (!current(v, a.tag)) stale = 1;
-            s_info[threadIdx.x] = v;
-        }
-        const int st = poll_done(stale, may_wait, t0);
-        if (st != 0) return st == 1;
-    }
-}
-
-__device__ __forceinline__ DrawRow draw_row(const ChainArgs &a, int b, const uint64_t *info,
-                                            int &j) {
-    const uint32_t jw = word_u32(info[0]);
-    j = jw > static_cast<uint32_t>(a.K) ? a.K : static_cast<int>(jw);
-    DrawRow w;
-    w.resid = j < a.K;
-    w.rt = word_f32(info[1]);
-    w.izt = word_f32(info[2]);
-    w.rd = word_f32(info[3]);
-    w.izd = word_f32(info[4]);
-    w.trow = (static_cast<int64_t>(b) * (a.K + 1) + j) * a.V;
-    w.drow = w.resid ? (static_cast<int64_t>(b) * a.K + j) * a.V : 0;
-    return w;
-}
-
-// Marks sequence b as timed out; the flag lands before the caller's next word.
-__device__ __forceinline__ void flag_timeout(const ChainArgs &a, int b) {
-    publish(&a.seq[b].timeout, a.tag, 1u);
-    __builtin_amdgcn_s_waitcnt(0);
-}
+// ------------------------------------------------------------ tail kernel
 
 template <class DT>
-__device__ __forceinline__ void resolve_item(const ChainArgs &a, int b, bool may_wait) {
-    __shared__ float s_P[kMaxK], s_Q[kMaxK];
-    const int K = a.K;
-    DrawRow w;
-    bool ok;
-    const int j = accept_prefix<DT>(a, b, may_wait, s_P, s_Q, w, ok);
-    SeqInfo &si = a.seq[b];
-    for (int k = threadIdx.x; k < K; k += kWG) {
-        publish_f32(&si.P[k], a.tag, s_P[k]);
-        publish_f32(&si.Q[k], a.tag, s_Q[k]);
-    }
-    if (threadIdx.x == 0) {
-        if (!ok) flag_timeout(a, b);
-        publish(&si.j, a.tag, static_cast<uint32_t>(j));
-        publish_f32(&si.rt, a.tag, w.rt);
-        publish_f32(&si.izt, a.tag, w.izt);
-        publish_f32(&si.rd, a.tag, w.rd);
-        publish_f32(&si.izd, a.tag, w.izd);
-    }
-}
-
-template <class DT>
-__device__ __forceinline__ void mass_item(const ChainArgs &a, int b, int ch, bool may_wait) {
-    __shared__ uint64_t s_info[5];
-    constexpr int C2 = Chunk2<DT>::kElems;
-    const bool ok = wait_record(a, b, may_wait, s_info);
-    int j;
-    const DrawRow w = draw_row(a, b, s_info, j);
-    const int64_t e0 = static_cast<int64_t>(ch) * C2;
-    const int64_t e1 = min(static_cast<int64_t>(a.V), e0 + C2);
-    const float mass = sum_wg(lane_mass<DT>(a, w, e0, e1));
-    if (threadIdx.x == 0) {
-        if (!ok) flag_timeout(a, b);
-        publish_f32(&a.sums[static_cast<int64_t>(b) * a.nchunk2 + ch], a.tag, mass);
-    }
-}
-
-// ------------------------------------------------------------ finish item
-
-template <class DT>
-__device__ __forceinline__ void finish_item(const ChainArgs &a, int b, bool may_wait) {
+__global__ __launch_bounds__(kWG) void k_chain_tail(ChainArgs a) {
     constexpr int VEC = DT::kVec;
     constexpr int C2 = Chunk2<DT>::kElems;
     constexpr int kSeg = C2 / kWG;  // contiguous entries per thread in the final scan
     const int K = a.K, V = a.V, tid = threadIdx.x;
+    const int b = blockIdx.x / a.nchunk2, ch = blockIdx.x % a.nchunk2;
+    const int nc = a.nchunk2;
+    __shared__ float s_P[kMaxK], s_Q[kMaxK];
     __shared__ float s_m[kSumsLds];
     __shared__ float s_S, s_tau, s_base;
-    __shared__ int s_cstar;
-    __shared__ uint64_t s_info[5];
-    SeqInfo &si = a.seq[b];
-    uint64_t *sums = a.sums + static_cast<int64_t>(b) * a.nchunk2;
-    const int nc = a.nchunk2;
-    const bool staged = nc <= kSumsLds;
-    const float us = a.u_sample[b];
+    __shared__ int s_cstar, s_last;
 
-    // Wait until the sequence record and every chunk mass are current.
-    const uint64_t t0 = wall_clock64();
-    bool timed_out = false;
-    for (;;) {
-        int stale = 0;
-        if (tid < 5) {
-            const uint64_t *f = tid == 0 ? &si.j
-                                : tid == 1 ? &si.rt
-                                : tid == 2 ? &si.izt
-                                : tid == 3 ? &si.rd
-                                           : &si.izd;
-            const uint64_t v = fetch(f);
-            if (!current(v, a.tag)) stale = 1;
-            s_info[tid] = v;
+    DrawRow w;
+    bool ok;
+    const int j = accept_prefix<DT>(a, b, s_P, s_Q, w, ok);
+
+    // This workgroup's share: the draw mass of chunk ch of row j.
+    uint64_t *sums = a.sums + static_cast<int64_t>(b) * nc;
+    {
+        const int64_t e0 = static_cast<int64_t>(ch) * C2;
+        const int64_t e1 = min(static_cast<int64_t>(V), e0 + C2);
+        const float mass = sum_wg(lane_mass<DT>(a, w, e0, e1));
+        if (tid == 0) {
+            publish_f32_sync(&sums[ch], a.tag, mass);
+            const uint32_t done = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = done == static_cast<uint32_t>(nc - 1);
         }
+        __syncthreads();
+        if (!s_last) return;
+    }
+
+    // Last workgroup of the sequence: every chunk mass has been published.
+    const bool staged = nc <= kSumsLds;
+    int stale = 0;
+    if (staged) {
         for (int i = tid; i < nc; i += kWG) {
             const uint64_t v = fetch(&sums[i]);
-            if (!current(v, a.tag)) stale = 1;
-            else if (staged) s_m[i] = word_f32(v);
-        }
-        if (a.out_diag && tid < K &&
-            (!current(fetch(&si.P[tid]), a.tag) || !current(fetch(&si.Q[tid]), a.tag)))
-            stale = 1;
-        const int st = poll_done(stale, may_wait, t0);
-        if (st == 1) break;
-        if (st < 0) {
-            timed_out = true;
-            break;
+            stale |= !current(v, a.tag);
+            s_m[i] = word_f32(v);
         }
     }
-    if (current(fetch(&si.timeout), a.tag)) timed_out = true;
-    int j;
-    DrawRow w = draw_row(a, b, s_info, j);
-
-    // Total mass, chunk masses added in chunk order.
+    ok = !__syncthreads_or(stale || !ok);
     if (tid == 0) {
         float S = 0.f;
         for (int i = 0; i < nc; ++i) S += staged ? s_m[i] : word_f32(fetch(&sums[i]));
@@ -437,7 +347,7 @@ __device__ __forceinline__ void finish_item(const ChainArgs &a, int b, bool may_
             const float mass = sum_wg(lane_mass<DT>(a, w, e0, e1));
             if (tid == 0) {
                 if (staged) s_m[i] = mass;
-                else publish_f32(&sums[i], a.tag, mass);
+                else publish_f32_sync(&sums[i], a.tag, mass);
             }
         }
         if (tid == 0) {
@@ -451,7 +361,7 @@ __device__ __forceinline__ void finish_item(const ChainArgs &a, int b, bool may_
     // Crossing chunk: the first whose inclusive running mass exceeds u * S.
     if (tid == 0) {
         const float S = s_S;
-        const float tau = us * S;
+        const float tau = a.u_sample[b] * S;
         float cum = 0.f, base = 0.f, base_last = 0.f;
         int cstar = -1, last_pos = 0;
         for (int i = 0; i < nc; ++i) {
@@ -539,10 +449,11 @@ __device__ __forceinline__ void finish_item(const ChainArgs &a, int b, bool may_
     const int pick = (found != INT32_MAX) ? found : max(last_nz, 0);
     const int32_t token = static_cast<int32_t>(c0 + pick);
 
-    // Emit x_0..x_{j-1}, then the drawn token, then -1 (all -1 after a timeout).
+    // Emit x_0..x_{j-1}, then the drawn token, then -1 (all -1 if a word
+    // was stale: the statistics phase did not run for this call).
     for (int k = tid; k <= K; k += kWG) {
         int32_t o = -1;
-        if (!timed_out) {
+        if (ok) {
             if (k < j) o = a.tokens[b * K + k];
             else if (k == j) o = token;
         }
@@ -550,7 +461,7 @@ __device__ __forceinline__ void finish_item(const ChainArgs &a, int b, bool may_
         if (a.out_diag) {
             float4 dg = make_float4(0.f, 0.f, 0.f, 0.f);
             if (k < K) {
-                const float P = word_f32(fetch(&si.P[k])), Q = word_f32(fetch(&si.Q[k]));
+                const float P = s_P[k], Q = s_Q[k];
                 dg.x = P;
                 dg.y = Q;
                 dg.z = Q > 0.f ? P / Q : (P > 0.f ? INFINITY : 0.f);
@@ -559,51 +470,17 @@ __device__ __forceinline__ void finish_item(const ChainArgs &a, int b, bool may_
             reinterpret_cast<float4 *>(a.out_diag)[static_cast<int64_t>(b) * (K + 1) + k] = dg;
         }
     }
-    if (tid == 0) a.out_accepted[b] = timed_out ? -1 : j;
+    if (tid == 0) a.out_accepted[b] = ok ? j : -1;
 }
-
-// ------------------------------------------------------------ kernels
 
 template <class DT, int U>
 __global__ __launch_bounds__(kWG) void k_chain_stats(ChainArgs a) {
-    stats_item<DT, U>(a, blockIdx.x / a.nchunk, blockIdx.x % a.nchunk);
-}
-
-template <class DT>
-__global__ __launch_bounds__(kWG) void k_chain_resolve(ChainArgs a) {
-    resolve_item<DT>(a, blockIdx.x, false);
-}
-
-template <class DT>
-__global__ __launch_bounds__(kWG) void k_chain_mass(ChainArgs a) {
-    mass_item<DT>(a, blockIdx.x / a.nchunk2, blockIdx.x % a.nchunk2, false);
-}
-
-template <class DT>
-__global__ __launch_bounds__(kWG) void k_chain_finish(ChainArgs a) {
-    finish_item<DT>(a, blockIdx.x, false);
-}
-
-template <class DT, int U>
-__global__ __launch_bounds__(kWG) void k_chain_fused(ChainArgs a, FusedPlan f) {
-    int kind, seq, idx;
-    fused_item(f, blockIdx.x, kind, seq, idx);
-    if (kind == kItemStats) {
-        const int64_t row = static_cast<int64_t>(seq) * (2 * a.K + 1) + idx / a.nchunk;
-        stats_item<DT, U>(a, row, idx % a.nchunk);
-    } else if (kind == kItemResolve) {
-        resolve_item<DT>(a, seq, true);
-    } else if (kind == kItemMass) {
-        mass_item<DT>(a, seq, idx, true);
-    } else {
-        finish_item<DT>(a, seq, true);
-    }
-}
-
-__global__ void k_zero_words(uint32_t *p, int64_t n) {
-    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        p[i] = 0u;
+    const int64_t row = blockIdx.x / a.nchunk;
+    const int ch = blockIdx.x % a.nchunk;
+    // The tail kernel's per-sequence counters start at zero for this call.
+    if (threadIdx.x == 0 && ch == 0 && row % (2 * a.K + 1) == 0)
+        a.counters[row / (2 * a.K + 1)] = 0u;
+    stats_item<DT, U>(a, row, ch);
 }
 
 }  // namespace
@@ -617,35 +494,12 @@ hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_chain_sample(const ChainArgs &a, int dtype, hipStream_t s) {
-    const int64_t grid = static_cast<int64_t>(a.B) * a.nchunk2;
-    const dim3 seqs(static_cast<uint32_t>(a.B));
-    if (dtype == 1) {
-        k_chain_resolve<Bf16><<<seqs, dim3(kWG), 0, s>>>(a);
-        k_chain_mass<Bf16><<<dim3(static_cast<uint32_t>(grid)), dim3(kWG), 0, s>>>(a);
-        k_chain_finish<Bf16><<<seqs, dim3(kWG), 0, s>>>(a);
-    } else {
-        k_chain_resolve<F32><<<seqs, dim3(kWG), 0, s>>>(a);
-        k_chain_mass<F32><<<dim3(static_cast<uint32_t>(grid)), dim3(kWG), 0, s>>>(a);
-        k_chain_finish<F32><<<seqs, dim3(kWG), 0, s>>>(a);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_chain_fused(const ChainArgs &a, const FusedPlan &f, int dtype, hipStream_t s) {
-    const dim3 grid(static_cast<uint32_t>(f.total));
+hipError_t launch_chain_tail(const ChainArgs &a, int dtype, hipStream_t s) {
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.nchunk2));
     if (dtype == 1)
-        k_chain_fused<Bf16, 4><<<grid, dim3(kWG), 0, s>>>(a, f);
+        k_chain_tail<Bf16><<<grid, dim3(kWG), 0, s>>>(a);
     else
-        k_chain_fused<F32, 4><<<grid, dim3(kWG), 0, s>>>(a, f);
-    return hipGetLastError();
-}
-
-hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    const int64_t want = (n + kWG - 1) / kWG;
-    const int64_t blocks = want < 1024 ? want : 1024;
-    k_zero_words<<<dim3(static_cast<uint32_t>(blocks)), dim3(kWG), 0, s>>>(p, n);
+        k_chain_tail<F32><<<grid, dim3(kWG), 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -98,38 +98,3 @@ def test_status_strings():
     lib = sv.library()
     for s in range(4):
         assert lib.spec_verify_status_string(s)
-
-
-@pytest.mark.parametrize("B,items,lags", [
-    (1, (5, 1, 1, 1), (0, 0, 0, 0)), (1, (9, 1, 3, 1), (0, 4, 5, 6)), (2, (3, 1, 2, 1), (0, 1, 2, 3)),
-    (8, (9, 1, 1, 1), (0, 187, 188, 189)), (64, (176, 1, 16, 1), (0, 22, 23, 24)),
-    (7, (11, 1, 5, 1), (0, 3, 3, 9)), (5, (4, 1, 4, 1), (0, 0, 1, 1)),
-    (256, (646, 1, 38, 1), (0, 6, 7, 8)), (3, (4, 0, 2, 1), (0, 0, 1, 2))])
-def test_fused_order_is_complete_and_backward(B, items, lags):
-    """Every item of every kind appears exactly once, and each kind's items of
-    a sequence sit after all items of the earlier kinds of that sequence, so
-    every wait in the fused kernel is on lower workgroup indices."""
-    total = sv.spec_verify_fused_item(B, items, lags, 0)[3]
-    assert total == B * sum(items)
-    pos = {}
-    for t in range(total):
-        k, s, i, _ = sv.spec_verify_fused_item(B, items, lags, t)
-        key = (k, s, i)
-        assert key not in pos and 0 <= s < B and 0 <= i < items[k], key
-        pos[key] = t
-    for b in range(B):
-        prev_last = -1
-        for kind in range(4):
-            ts = [pos[(kind, b, i)] for i in range(items[kind])]
-            if ts:
-                assert min(ts) > prev_last, (b, kind)
-                prev_last = max(ts)
-    with pytest.raises(ValueError):
-        sv.spec_verify_fused_item(B, items, lags, total)
-
-
-def test_fused_order_rejects_bad_plans():
-    for items, lags in [((1, 1, 1, 1), (1, 1, 1, 1)), ((1, 1, 1, 1), (0, 2, 1, 3)),
-                        ((1, -1, 1, 1), (0, 0, 0, 0))]:
-        with pytest.raises(ValueError):
-            sv.spec_verify_fused_item(4, items, lags, 0)

@@ -126,11 +126,10 @@ def test_chain_phases_equal_one_call(sv):
 
 
 def test_chain_workspace_reuse_across_shapes(sv):
-    """One workspace serves consecutive calls of different shapes: each call
-    leaves the fused kernel's counters at zero for the next."""
+    """One workspace with arbitrary prior contents serves consecutive calls of
+    different shapes."""
     big = sv.spec_verify_workspace_bytes(sv.SPEC_MODE_CHAIN, 24, 8, 50000, sv.SPEC_DTYPE_F32)
-    ws = torch.empty(big, dtype=torch.uint8, device=DEV)
-    sv.spec_verify_workspace_init(ws)
+    ws = torch.full((big,), 0x5A, dtype=torch.uint8, device=DEV)  # arbitrary prior contents
     shapes = [(24, 8, 50000, "f32"), (3, 2, 7000, "bf16"), (24, 8, 50000, "f32"), (1, 0, 333, "f32"),
               (17, 5, 20001, "bf16"), (24, 8, 50000, "f32")]
     for i, (B, K, V, dt) in enumerate(shapes):
