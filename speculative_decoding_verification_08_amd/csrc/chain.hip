@@ -50,6 +50,13 @@ __device__ __forceinline__ void publish_f32_sync(uint64_t *p, uint32_t tag, floa
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     __builtin_amdgcn_s_waitcnt(0);
 }
+// Publish without waiting (a device-scope store; readers check the tag).
+__device__ __forceinline__ void publish_f32(uint64_t *p, uint32_t tag, float v) {
+    __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | __float_as_uint(v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s of the 100 MHz wall clock
+
 // Words exchanged inside the tail kernel: device-scope atomics.
 __device__ __forceinline__ uint64_t fetch(const uint64_t *p) {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED,
@@ -164,31 +171,32 @@ __device__ __forceinline__ float lane_mass(const ChainArgs &a, const DrawRow &w,
     constexpr int NV = Chunk2<DT>::kElems / (VEC * kWG);
     float acc = 0.f;
     if (a.V % VEC == 0) {
+        // Every lane issues all its loads before using any: indices past the
+        // chunk are clamped to its last vector and their weights dropped (a
+        // branch around each load would make each one wait for the last).
+        // The bonus draw has no draft row and re-reads the target row instead.
         const uint4 *tp = static_cast<const uint4 *>(a.target);
-        const uint4 *dp = static_cast<const uint4 *>(a.draft);
+        const uint4 *dp = w.resid ? static_cast<const uint4 *>(a.draft) : tp;
         const int64_t v0 = (w.trow + e0) / VEC, nv = (e1 - e0) / VEC;
-        const int64_t d0 = (w.drow + e0) / VEC;
+        const int64_t d0 = ((w.resid ? w.drow : w.trow) + e0) / VEC;
         uint4 rt[NV], rd[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int64_t o = threadIdx.x + i * kWG;
-            if (o < nv) {
-                rt[i] = tp[v0 + o];
-                if (w.resid) rd[i] = dp[d0 + o];
-            }
+            const int64_t o = min(static_cast<int64_t>(threadIdx.x + i * kWG), nv - 1);
+            rt[i] = tp[v0 + o];
+            rd[i] = dp[d0 + o];
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int64_t o = threadIdx.x + i * kWG;
-            if (o < nv) {
-                float t[VEC], d[VEC];
-                unpack<DT>(rt[i], t);
-                if (w.resid) unpack<DT>(rd[i], d);
+            const bool in = threadIdx.x + i * kWG < nv;
+            float t[VEC], d[VEC];
+            unpack<DT>(rt[i], t);
+            unpack<DT>(rd[i], d);
+            float part = 0.f;
 #pragma unroll
-                for (int q = 0; q < VEC; ++q)
-                    acc += draw_weight(t[q], w.resid ? d[q] : 0.f, a.c, w.rt, w.izt, w.rd, w.izd,
-                                       w.resid);
-            }
+            for (int q = 0; q < VEC; ++q)
+                part += draw_weight(t[q], d[q], a.c, w.rt, w.izt, w.rd, w.izd, w.resid);
+            acc += in ? part : 0.f;
         }
     } else {
         for (int64_t e = e0 + threadIdx.x; e < e1; e += kWG) {
@@ -200,12 +208,60 @@ __device__ __forceinline__ float lane_mass(const ChainArgs &a, const DrawRow &w,
     return acc;
 }
 
-// Waits for sequence b's row statistics and drafted-token logits, merges the
-// statistics over chunks (in chunk order) and evaluates the accept test of
-// every drafted token.  Returns j, the first rejected position (K if none),
-// with row j's statistics in `w` and p_k(x_k), q_k(x_k) in s_P, s_Q; sets
-// `ok` to false if the wait ran out.
-// Merges sequence b's row statistics over chunks (in chunk order) and
+// Inclusive scan across a wavefront (lane order).
+__device__ __forceinline__ float wave_incl_scan(float x) {
+    const int lane = threadIdx.x % kWave;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// Running masses of a sequence's draw chunks, scanned 64 chunks at a time
+// by one wavefront in a fixed order (chunk masses from LDS when staged, else
+// from the published words).  Returns S, the total, in every lane.  With
+// `cstar`, also finds the crossing chunk: the first whose inclusive running
+// mass exceeds tau (the inverse CDF, strict), else the last chunk with mass
+// (tau rounded up to S), and `base`, the running mass before it.
+__device__ float scan_masses(const float *s_m, const uint64_t *sums, int nc, bool staged,
+                             float tau, int *cstar, float *base) {
+    const int lane = threadIdx.x % kWave;
+    float carry = 0.f, last_base = 0.f;
+    int found = -1, last_pos = 0;
+    float found_base = 0.f;
+    for (int i0 = 0; i0 < nc; i0 += kWave) {
+        const int i = i0 + lane;
+        float m = 0.f;
+        if (i < nc) m = staged ? s_m[i] : word_f32(fetch(&sums[i]));
+        const float incl = carry + wave_incl_scan(m);
+        float excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = carry;
+        if (cstar) {
+            const uint64_t cross = __ballot(i < nc && incl > tau);
+            if (found < 0 && cross) {
+                const int l = __ffsll(static_cast<unsigned long long>(cross)) - 1;
+                found = i0 + l;
+                found_base = __shfl(excl, l);
+            }
+            const uint64_t pos = __ballot(i < nc && m > 0.f);
+            if (pos) {
+                const int l = 63 - __clzll(static_cast<long long>(pos));
+                last_pos = i0 + l;
+                last_base = __shfl(excl, l);
+            }
+        }
+        carry = __shfl(incl, kWave - 1);
+    }
+    if (cstar) {
+        *cstar = found >= 0 ? found : last_pos;
+        *base = found >= 0 ? found_base : last_base;
+    }
+    return carry;
+}
+
+// Merges sequence b's row statistics over chunks (in a fixed order) and
 // evaluates the accept test of every drafted token.  Returns j, the first
 // rejected position (K if none), with row j's statistics in `w` and
 // p_k(x_k), q_k(x_k) in s_P, s_Q; `ok` is false if a word was not written for
@@ -221,18 +277,30 @@ __device__ int accept_prefix(const ChainArgs &a, int b, float *s_P, float *s_Q, 
     const uint64_t *part = a.partial + 2 * static_cast<int64_t>(b) * np;
     const uint64_t *gat = a.gathered + static_cast<int64_t>(b) * R;
     const bool staged = np <= kMergeLds;
-    // One round trip: partials, drafted-token logits and uniforms together.
+    // One round trip: partials, drafted-token logits and uniforms are all
+    // loaded (from clamped indices, without branches) before any is used.
     int stale = 0;
     float lt = 0.f, ld = 0.f;
-    const float u = tid < K ? a.u_accept[b * K + tid] : 0.f;
+    const float *ua = K > 0 ? a.u_accept + static_cast<int64_t>(b) * K : a.u_sample + b;
+    const int kk = min(tid, max(K - 1, 0));
+    float u = ua[kk];
+    const uint64_t wt = gat[min(tid, R - 1)], wd = gat[min(K + 1 + tid, R - 1)];
+    const int i0 = min(tid, np - 1);
+    const uint64_t wr0 = part[2 * i0], wz0 = part[2 * i0 + 1];
     if (tid < K) {
-        const uint64_t wt = gat[tid], wd = gat[K + 1 + tid];
         stale |= !current(wt, a.tag) || !current(wd, a.tag);
         lt = word_f32(wt);
         ld = word_f32(wd);
+    } else {
+        u = 0.f;
     }
     if (staged) {
-        for (int i = tid; i < np; i += kWG) {
+        if (tid < np) {
+            stale |= !current(wr0, a.tag) || !current(wz0, a.tag);
+            s_pr[tid] = word_f32(wr0);
+            s_pz[tid] = word_f32(wz0);
+        }
+        for (int i = tid + kWG; i < np; i += kWG) {
             const uint64_t wr = part[2 * i], wz = part[2 * i + 1];
             stale |= !current(wr, a.tag) || !current(wz, a.tag);
             s_pr[i] = word_f32(wr);
@@ -240,9 +308,14 @@ __device__ int accept_prefix(const ChainArgs &a, int b, float *s_P, float *s_Q, 
         }
     }
     ok = !__syncthreads_or(stale);
-    for (int r = tid; r < R; r += kWG) {
+    // Row r's chunk statistics are merged by wave r % kWaves: lane i folds
+    // chunks i, i + 64, ... in order, then a fixed butterfly merges the lanes
+    // and lane 0's result is the row's.
+    const int lane = tid % kWave;
+    bool fresh = true;
+    for (int r = tid / kWave; r < R; r += kWaves) {
         float ref = -INFINITY, z = 0.f;
-        for (int i = 0; i < a.nchunk; ++i) {
+        for (int i = lane; i < a.nchunk; i += kWave) {
             const int q = r * a.nchunk + i;
             float pr, pz;
             if (staged) {
@@ -250,16 +323,21 @@ __device__ int accept_prefix(const ChainArgs &a, int b, float *s_P, float *s_Q, 
                 pz = s_pz[q];
             } else {
                 const uint64_t wr = part[2 * q], wz = part[2 * q + 1];
-                if (!current(wr, a.tag) || !current(wz, a.tag)) ok = false;
+                fresh = fresh && current(wr, a.tag) && current(wz, a.tag);
                 pr = word_f32(wr);
                 pz = word_f32(wz);
             }
             mz_merge(ref, z, pr, pz);
         }
-        s_ref[r] = ref;
-        s_z[r] = z;
+#pragma unroll
+        for (int off = kWave / 2; off > 0; off >>= 1)
+            mz_merge(ref, z, __shfl_xor(ref, off), __shfl_xor(z, off));
+        if (lane == 0) {
+            s_ref[r] = ref;
+            s_z[r] = z;
+        }
     }
-    if (!staged) ok = !__syncthreads_or(!ok);
+    if (!staged) ok = ok && !__syncthreads_or(!fresh);
     __syncthreads();
     // Accept test u < P/Q (strict; Q = 0 accepts iff P > 0), wave 0, K <= 64.
     if (tid < kWave) {
@@ -301,6 +379,12 @@ __global__ __launch_bounds__(kWG) void k_chain_tail(ChainArgs a) {
     __shared__ float s_S, s_tau, s_base;
     __shared__ int s_cstar, s_last;
 
+    static_assert(kMaxK + 1 <= kWG, "one thread per emitted token");
+    // Drafted tokens for the emission, loaded now (thread k emits token k).
+    const int32_t *tk = K > 0 ? a.tokens + static_cast<int64_t>(b) * K
+                              : reinterpret_cast<const int32_t *>(a.u_sample + b);
+    const int32_t my_tok = tk[min(tid, max(K - 1, 0))];
+
     DrawRow w;
     bool ok;
     const int j = accept_prefix<DT>(a, b, s_P, s_Q, w, ok);
@@ -312,7 +396,7 @@ __global__ __launch_bounds__(kWG) void k_chain_tail(ChainArgs a) {
         const int64_t e1 = min(static_cast<int64_t>(V), e0 + C2);
         const float mass = sum_wg(lane_mass<DT>(a, w, e0, e1));
         if (tid == 0) {
-            publish_f32_sync(&sums[ch], a.tag, mass);
+            publish_f32(&sums[ch], a.tag, mass);
             const uint32_t done = __hip_atomic_fetch_add(&a.counters[b], 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
             s_last = done == static_cast<uint32_t>(nc - 1);
@@ -322,20 +406,32 @@ __global__ __launch_bounds__(kWG) void k_chain_tail(ChainArgs a) {
     }
 
     // Last workgroup of the sequence: every chunk mass has been published.
+    // Wave 0 stages them in LDS (one round trip; read in place past kSumsLds
+    // chunks) and scans them across its lanes for S and the crossing chunk.
     const bool staged = nc <= kSumsLds;
-    int stale = 0;
-    if (staged) {
-        for (int i = tid; i < nc; i += kWG) {
-            const uint64_t v = fetch(&sums[i]);
-            stale |= !current(v, a.tag);
-            s_m[i] = word_f32(v);
+    // The masses were stored before their counter increments but may become
+    // visible a little later: a bounded poll on the tags.
+    if (tid < kWave) {
+        bool fresh = false;
+        const uint64_t t0 = wall_clock64();
+        for (;;) {
+            fresh = true;
+            for (int i = tid; i < nc; i += kWave) {
+                const uint64_t v = fetch(&sums[i]);
+                fresh = fresh && current(v, a.tag);
+                if (staged) s_m[i] = word_f32(v);
+            }
+            fresh = __all(fresh);
+            if (fresh || wall_clock64() - t0 > kWaitTicks) break;
+            __builtin_amdgcn_s_sleep(2);
         }
+        if (tid == 0) s_last = fresh;
     }
-    ok = !__syncthreads_or(stale || !ok);
-    if (tid == 0) {
-        float S = 0.f;
-        for (int i = 0; i < nc; ++i) S += staged ? s_m[i] : word_f32(fetch(&sums[i]));
-        s_S = S;
+    __syncthreads();
+    ok = ok && s_last;
+    if (tid < kWave) {
+        const float S = scan_masses(s_m, sums, nc, staged, 0.f, nullptr, nullptr);
+        if (tid == 0) s_S = S;
     }
     __syncthreads();
     if (w.resid && s_S == 0.f) {
@@ -350,39 +446,23 @@ __global__ __launch_bounds__(kWG) void k_chain_tail(ChainArgs a) {
                 else publish_f32_sync(&sums[i], a.tag, mass);
             }
         }
-        if (tid == 0) {
-            float S = 0.f;
-            for (int i = 0; i < nc; ++i) S += staged ? s_m[i] : word_f32(fetch(&sums[i]));
-            s_S = S;
+        __syncthreads();
+        if (tid < kWave) {
+            const float S = scan_masses(s_m, sums, nc, staged, 0.f, nullptr, nullptr);
+            if (tid == 0) s_S = S;
         }
         __syncthreads();
     }
-
-    // Crossing chunk: the first whose inclusive running mass exceeds u * S.
-    if (tid == 0) {
-        const float S = s_S;
-        const float tau = a.u_sample[b] * S;
-        float cum = 0.f, base = 0.f, base_last = 0.f;
-        int cstar = -1, last_pos = 0;
-        for (int i = 0; i < nc; ++i) {
-            const float m = staged ? s_m[i] : word_f32(fetch(&sums[i]));
-            if (m > 0.f) {
-                last_pos = i;
-                base_last = cum;
-            }
-            if (cstar < 0 && cum + m > tau) {
-                cstar = i;
-                base = cum;
-            }
-            cum += m;
+    if (tid < kWave) {
+        const float tau = a.u_sample[b] * s_S;
+        int cstar;
+        float base;
+        scan_masses(s_m, sums, nc, staged, tau, &cstar, &base);
+        if (tid == 0) {
+            s_cstar = cstar;
+            s_base = base;
+            s_tau = tau;
         }
-        if (cstar < 0) {  // u * S rounded up to S: the last chunk with mass
-            cstar = last_pos;
-            base = base_last;
-        }
-        s_cstar = cstar;
-        s_base = base;
-        s_tau = tau;
     }
     __syncthreads();
 
@@ -394,29 +474,29 @@ __global__ __launch_bounds__(kWG) void k_chain_tail(ChainArgs a) {
     float wt[kSeg];
     if (V % VEC == 0) {
         constexpr int NQ = kSeg / VEC;
+        // All loads issued before any use; entries past the chunk are clamped
+        // to its last vector and get weight 0.
         const uint4 *tp = static_cast<const uint4 *>(a.target);
-        const uint4 *dp = static_cast<const uint4 *>(a.draft);
+        const uint4 *dp = w.resid ? static_cast<const uint4 *>(a.draft) : tp;
+        const int64_t tb = (w.trow + c0) / VEC, db = ((w.resid ? w.drow : w.trow) + c0) / VEC;
+        const int last = n / VEC - 1;
         uint4 rt[NQ], rd[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const int e = s0 + q * VEC;
-            if (e < n) {
-                rt[q] = tp[(w.trow + c0 + e) / VEC];
-                if (w.resid) rd[q] = dp[(w.drow + c0 + e) / VEC];
-            }
+            const int o = min((s0 + q * VEC) / VEC, last);
+            rt[q] = tp[tb + o];
+            rd[q] = dp[db + o];
         }
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int e = s0 + q * VEC;
             float t[VEC], d[VEC];
-            if (e < n) {
-                unpack<DT>(rt[q], t);
-                if (w.resid) unpack<DT>(rd[q], d);
-            }
+            unpack<DT>(rt[q], t);
+            unpack<DT>(rd[q], d);
 #pragma unroll
             for (int i = 0; i < VEC; ++i)
-                wt[q * VEC + i] = e < n ? draw_weight(t[i], w.resid ? d[i] : 0.f, a.c, w.rt, w.izt,
-                                                      w.rd, w.izd, w.resid)
+                wt[q * VEC + i] = e < n ? draw_weight(t[i], d[i], a.c, w.rt, w.izt, w.rd, w.izd,
+                                                      w.resid)
                                         : 0.f;
         }
     } else {
@@ -454,7 +534,7 @@ __global__ __launch_bounds__(kWG) void k_chain_tail(ChainArgs a) {
     for (int k = tid; k <= K; k += kWG) {
         int32_t o = -1;
         if (ok) {
-            if (k < j) o = a.tokens[b * K + k];
+            if (k < j) o = my_tok;  // k == tid here: K + 1 <= 65 < kWG
             else if (k == j) o = token;
         }
         a.out_tokens[static_cast<int64_t>(b) * (K + 1) + k] = o;
