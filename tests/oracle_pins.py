@@ -254,6 +254,39 @@ def pin_softmax_values(lib):
         assert abs(d[0, 0, 1] - 1.0 / (na + nb)) <= 1e-15
 
 
+def pin_helper_closed_forms(lib):
+    """The two oracle helpers the tests lean on, against closed forms.
+
+    acceptance_rate is sum_i min(p_i, q_i), the probability that a drafted
+    token is accepted (forum post, section 3): 1 for identical rows, 0 for
+    disjoint supports, and 0.8 for p = (0.6, 0.4), q = (0.4, 0.6).
+    draw_weights is max(0, p - q) after a rejection and p for the bonus draw
+    (French lesson, "La règle de l'exactitude"): checked entry by entry on a
+    two-level target row against a constant draft row (q = 1/V)."""
+    row = np.array([0.3, -1.2, 2.0, 0.0, 0.7], np.float32)
+    assert abs(oracle.acceptance_rate(row, row, 0.9, lib=lib) - 1.0) <= 1e-15
+    ninf = np.float32(-np.inf)
+    assert oracle.acceptance_rate(np.array([0.0, ninf], np.float32),
+                                  np.array([ninf, 0.0], np.float32), 1.0, lib=lib) == 0.0
+    for T in (1.0, 0.5):
+        t = (T * np.log(np.array([0.6, 0.4]))).astype(np.float32)
+        d = (T * np.log(np.array([0.4, 0.6]))).astype(np.float32)
+        assert abs(oracle.acceptance_rate(t, d, T, lib=lib) - 0.8) <= 1e-6, T
+    for T in (1.0, 0.7):
+        a, b, na, nb = 1.5, -0.5, 3, 9
+        V = na + nb
+        t = np.array([a] * na + [b] * nb, np.float32)
+        d = np.zeros(V, np.float32)
+        pa = 1.0 / (na + nb * np.exp((b - a) / T))
+        p = np.array([pa] * na + [pa * np.exp((b - a) / T)] * nb)
+        w, S = oracle.draw_weights(t, d, T, lib=lib)
+        want = np.maximum(p - 1.0 / V, 0.0)
+        assert np.all(np.abs(w - want) <= 1e-14), (T, w, want)
+        assert abs(S - want.sum()) <= 1e-14 and want[na:].sum() == 0.0
+        w, S = oracle.draw_weights(t, None, T, lib=lib)
+        assert np.all(np.abs(w - p) <= 1e-15) and abs(S - 1.0) <= 1e-14
+
+
 # ------------------------------------------------------------- inverse CDF
 
 def pin_inverse_cdf(lib):
@@ -417,6 +450,6 @@ def pin_chi_square(lib, n=50_000, seed=19):
 
 
 ALL_PINS = [pin_exact_law, pin_expected_tokens, pin_page_counts, pin_strict_acceptance,
-            pin_softmax_values,
+            pin_softmax_values, pin_helper_closed_forms,
             pin_inverse_cdf, pin_greedy, pin_tree_bruteforce, pin_tree_chain,
             pin_tree_figure, pin_chi_square]
