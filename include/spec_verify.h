@@ -26,10 +26,10 @@
  *    synchronously and nothing is enqueued then.  SPEC_ERR_LAUNCH reports a
  *    launch failure seen right after enqueueing.
  *  - The workspace (size from spec_verify_workspace_bytes) holds per-call
- *    scratch and needs no initialisation.  Words the chain verify's kernels
- *    hand each other carry a per-call tag (from a process-wide call counter),
- *    so contents left by any earlier call are never taken for fresh ones.
- *    Calls that share a workspace must be ordered on one stream.
+ *    scratch and needs no initialisation.  Words the chain verify's
+ *    workgroups hand each other carry a per-call tag (from a process-wide
+ *    call counter), so contents left by any earlier call are never taken for
+ *    fresh ones.  Calls that share a workspace must be ordered on one stream.
  *  - Inputs that break a documented precondition (a drafted token outside
  *    [0, V), a uniform outside [0, 1), NaN or +inf logits, a row that is
  *    entirely -inf) give unspecified outputs but never an out-of-bounds
@@ -71,7 +71,9 @@ typedef enum {
 
 #define SPEC_VERIFY_MAX_K 64            /* draft length limit of chain and greedy verify */
 #define SPEC_VERIFY_MAX_TREE_NODES 256  /* node limit of the static tree (root included) */
-#define SPEC_VERIFY_MAX_V (1 << 26)     /* vocabulary limit                              */
+#define SPEC_VERIFY_MAX_V (1 << 26)     /* vocabulary limit (greedy and tree)            */
+#define SPEC_VERIFY_MAX_CHAIN_V_BF16 (1 << 19)  /* chain verify vocabulary limit, bf16 logits */
+#define SPEC_VERIFY_MAX_CHAIN_V_F32 (1 << 18)   /* chain verify vocabulary limit, fp32 logits */
 
 /*
  * Workspace size for one call.  K_or_N is K for the chain and greedy modes
@@ -98,7 +100,8 @@ spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_
  *                              that ends the step (residual or bonus).  A draw
  *                              from weights w returns the smallest i with
  *                              w_0+...+w_i > u * sum(w).
- *   B >= 0, 0 <= K <= SPEC_VERIFY_MAX_K, 1 <= V <= SPEC_VERIFY_MAX_V, T > 0.
+ *   B >= 0, 0 <= K <= SPEC_VERIFY_MAX_K, T > 0, and 1 <= V <=
+ *   SPEC_VERIFY_MAX_CHAIN_V_BF16 (bf16) or SPEC_VERIFY_MAX_CHAIN_V_F32 (fp32).
  *   out_tokens    [B][K+1]     int32: the first out_accepted[b]+1 entries are
  *                              the emitted tokens, the rest are -1.
  *   out_accepted  [B]          int32 j in [0, K]: accepted drafts.
@@ -109,10 +112,11 @@ spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_
  *                              q = 0 < p, 0 when both are 0).
  *   workspace                  at least spec_verify_workspace_bytes(CHAIN, ...).
  *
- * The step is spec_verify_chain_stats followed by spec_verify_chain_sample on
- * the same stream and workspace (two kernels).  If out_accepted[b] is -1 the
- * sample phase found statistics not written by this call's statistics phase
- * (only possible through the phase entry points) and out_tokens[b] is all -1.
+ * Two kernel launches in stream order: spec_verify_chain_stats, then
+ * spec_verify_chain_sample, on the same workspace.  The second kernel's
+ * workgroups of one sequence hand each other words in the workspace and wait
+ * for each other (bounded, about 2 s); if a wait ever ran out, the sequence
+ * gets out_accepted[b] = -1 and out_tokens[b] all -1.
  */
 spec_status spec_verify_chain(const void *target_logits, const void *draft_logits, spec_dtype dtype,
                               const int32_t *draft_tokens, const float *u_accept,
@@ -122,10 +126,11 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
                               hipStream_t stream);
 
 /*
- * First phase of the chain verify: one streaming pass over every target and
- * draft logit that leaves each row's softmax statistics (running maximum and
- * sum of exponentials, per vocabulary chunk) and each row's logit at its
- * drafted token in the workspace.  Same argument meaning as spec_verify_chain.
+ * First phase of the chain verify (one kernel): one streaming pass over every
+ * target and draft logit that leaves each row's softmax statistics (running
+ * maximum and sum of exponentials, per vocabulary chunk) and each row's logit
+ * at its drafted token in the workspace.  Same argument meaning as
+ * spec_verify_chain.
  */
 spec_status spec_verify_chain_stats(const void *target_logits, const void *draft_logits,
                                     spec_dtype dtype, const int32_t *draft_tokens, int32_t B,
@@ -133,11 +138,12 @@ spec_status spec_verify_chain_stats(const void *target_logits, const void *draft
                                     size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Second phase of the chain verify: acceptance of each position, the first
- * rejection j, and the residual or bonus draw, reading the statistics the
- * first phase left in the same workspace.  Must follow spec_verify_chain_stats
- * with identical logits, tokens, sizes and temperature on the same stream;
- * sequences whose statistics are missing get out_accepted = -1.
+ * Second phase of the chain verify (one kernel): the accept test of each
+ * position, the first rejection j, the residual or bonus draw and the emitted
+ * tokens, from the statistics the first phase left in the same workspace.
+ * Must follow spec_verify_chain_stats with identical logits, tokens, sizes and
+ * temperature on the same stream; sequences whose statistics were not written
+ * by that phase get out_accepted = -1.
  */
 spec_status spec_verify_chain_sample(const void *target_logits, const void *draft_logits,
                                      spec_dtype dtype, const int32_t *draft_tokens,

@@ -24,6 +24,7 @@ SPEC_DTYPE_F32, SPEC_DTYPE_BF16 = 0, 1
 SPEC_MODE_CHAIN, SPEC_MODE_GREEDY, SPEC_MODE_TREE = 0, 1, 2
 SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_LAUNCH = 0, 1, 2, 3
 MAX_K, MAX_TREE_NODES, MAX_V = 64, 256, 1 << 26
+MAX_CHAIN_V_BF16, MAX_CHAIN_V_F32 = 1 << 19, 1 << 18
 
 
 class SpecVerifyError(RuntimeError):
@@ -179,7 +180,36 @@ def spec_verify_chain_sample(target_logits, draft_logits, draft_tokens, u_accept
           _ptr(draft_tokens), _ptr(u_accept), _ptr(u_sample), B, K, V, float(temperature),
           _ptr(out_tokens), _ptr(out_accepted), _ptr(out_diag), _ptr(workspace_buf),
           workspace_buf.numel(), _stream(dev, stream))
-    return out_tokens, out_accepted, out_diag
+    return out_tokens, out_accepted
+
+
+def prepare_chain(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
+                  temperature: float, out_tokens, out_accepted, workspace_buf, *, out_diag=None,
+                  stream=None):
+    """Checks and marshals the arguments of one spec_verify_chain call once and
+    returns a function that enqueues it again with no Python-side work (for
+    serving loops and graph capture).  The tensors must stay alive and keep
+    their storage while the function is used."""
+    dt, B, K, V = _chain_check(target_logits, draft_logits, draft_tokens, u_accept, u_sample)
+    dev = target_logits.device
+    _check_dev("out_tokens", out_tokens, torch.int32, (B, K + 1))
+    _check_dev("out_accepted", out_accepted, torch.int32, (B,))
+    if out_diag is not None:
+        _check_dev("out_diag", out_diag, torch.float32, (B, K + 1, 4))
+    need = spec_verify_workspace_bytes(SPEC_MODE_CHAIN, B, K, V, dt)
+    if workspace_buf.numel() < need:
+        raise SpecVerifyError("spec_verify_chain", SPEC_ERR_WORKSPACE)
+    fn = _lib.spec_verify_chain
+    args = (_ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(u_accept),
+            _ptr(u_sample), B, K, V, ctypes.c_float(float(temperature)), _ptr(out_tokens),
+            _ptr(out_accepted), _ptr(out_diag), _ptr(workspace_buf),
+            ctypes.c_size_t(workspace_buf.numel()), _stream(dev, stream))
+
+    def launch():
+        st = fn(*args)
+        if st != SPEC_OK:
+            raise SpecVerifyError("spec_verify_chain", st)
+    return launch
 
 
 def spec_verify_greedy(target_logits, draft_tokens, *, out_tokens=None, out_accepted=None,

@@ -52,11 +52,12 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
         off += align_up(static_cast<size_t>(rows) * 8);
         p.chunk2 = kChunk2Bytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
         p.nchunk2 = (V + p.chunk2 - 1) / p.chunk2;
+            // Every draw workgroup of a sequence waits for the sequence's other
+        // chunks, so a sequence's draw workgroups must fit the chip together.
+        if (p.nchunk2 > kMaxDrawChunks) return false;
         if (static_cast<int64_t>(B) * p.nchunk2 > 0x7fffffffLL) return false;
-        p.off_sums = off;
-        off += align_up(static_cast<size_t>(B) * p.nchunk2 * 8);
-        p.off_counters = off;
-        off += align_up(static_cast<size_t>(B) * 4);
+        p.off_sums = off;  // two tagged masses per chunk: residual, target
+        off += align_up(static_cast<size_t>(B) * p.nchunk2 * 16);
     } else {
         off += align_up(static_cast<size_t>(rows) * p.nchunk * 8);
     }
@@ -105,7 +106,6 @@ spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype,
     a.partial = at<uint64_t>(ws, plan.off_partial);
     a.gathered = at<uint64_t>(ws, plan.off_gather);
     a.sums = at<uint64_t>(ws, plan.off_sums);
-    a.counters = at<uint32_t>(ws, plan.off_counters);
     a.tag = kPhasedTag;
     return SPEC_OK;
 }
@@ -184,7 +184,7 @@ spec_status spec_verify_chain_sample(const void *target_logits, const void *draf
     st = chain_sample_args(draft_tokens, u_accept, u_sample, B, K, out_tokens, out_accepted,
                            out_diag, a);
     if (st != SPEC_OK) return st;
-    return launch_status(launch_chain_tail(a, dtype, stream));
+    return launch_status(launch_chain_draw(a, dtype, stream));
 }
 
 spec_status spec_verify_chain(const void *target_logits, const void *draft_logits,
@@ -204,7 +204,7 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
     a.tag = next_call_tag();
     st = launch_status(launch_chain_stats(a, dtype, stream));
     if (st != SPEC_OK) return st;
-    return launch_status(launch_chain_tail(a, dtype, stream));
+    return launch_status(launch_chain_draw(a, dtype, stream));
 }
 
 spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,

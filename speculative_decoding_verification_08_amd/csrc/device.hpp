@@ -102,28 +102,9 @@ __device__ __forceinline__ void mz_batch(const float *x, float c, float &ref, fl
     ref = rn;
 }
 
-// Workgroup merge of (ref, z); the result is valid in thread 0.
-__device__ __forceinline__ void mz_reduce_wg(float &ref, float &z) {
-    __shared__ float s_ref[kWaves], s_z[kWaves];
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        const float r2 = __shfl_xor(ref, off);
-        const float z2 = __shfl_xor(z, off);
-        mz_merge(ref, z, r2, z2);
-    }
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x % kWave) == 0) {
-        s_ref[w] = ref;
-        s_z[w] = z;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        ref = s_ref[0];
-        z = s_z[0];
-        for (int i = 1; i < kWaves; ++i) mz_merge(ref, z, s_ref[i], s_z[i]);
-    }
-    __syncthreads();
-}
+// Workgroup merge of (ref, z); the result is valid in thread 0.  Defined
+// after the DPP helpers below.
+__device__ __forceinline__ void mz_reduce_wg(float &ref, float &z);
 
 // ------------------------------------------------------------------ argmax
 
@@ -225,6 +206,171 @@ __device__ __forceinline__ int max_wg(int x) {
     for (int k = 1; k < kWaves; ++k) r = max(r, s_x[k]);
     __syncthreads();
     return r;
+}
+
+
+// ------------------------------------------------------------------ DPP
+
+// Wavefront primitives on data-parallel-primitive (DPP) lane moves: each step
+// is one VALU operation instead of an LDS-crossbar shuffle.  Row = 16 lanes.
+// Lanes whose DPP source is out of range keep `identity`.
+namespace dpp {
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kWaveShr1 = 0x138, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ float mov_f(float identity, float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(identity), __float_as_int(x),
+                                                      Ctrl, RowMask, 0xF, false));
+}
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ int mov_i(int identity, int x) {
+    return __builtin_amdgcn_update_dpp(identity, x, Ctrl, RowMask, 0xF, false);
+}
+}  // namespace dpp
+
+// Inclusive sum over lanes 0..lane of a wavefront, in a fixed order: within
+// rows of 16 by doubling shifts, then the rows' totals carried upward.
+__device__ __forceinline__ float wave_incl_sum(float x) {
+    x += dpp::mov_f<dpp::kRowShr1>(0.f, x);
+    x += dpp::mov_f<dpp::kRowShr2>(0.f, x);
+    x += dpp::mov_f<dpp::kRowShr4>(0.f, x);
+    x += dpp::mov_f<dpp::kRowShr8>(0.f, x);
+    x += dpp::mov_f<dpp::kRowBcast15, 0xA>(0.f, x);
+    x += dpp::mov_f<dpp::kRowBcast31, 0xC>(0.f, x);
+    return x;
+}
+// Value of lane 63 (uniform).
+__device__ __forceinline__ float wave_last(float x) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
+}
+__device__ __forceinline__ int wave_last_i(int x) { return __builtin_amdgcn_readlane(x, kWave - 1); }
+
+// Minimum / maximum over the wavefront (uniform result).
+__device__ __forceinline__ int wave_min_i(int x) {
+    x = min(x, dpp::mov_i<dpp::kRowShr1>(INT32_MAX, x));
+    x = min(x, dpp::mov_i<dpp::kRowShr2>(INT32_MAX, x));
+    x = min(x, dpp::mov_i<dpp::kRowShr4>(INT32_MAX, x));
+    x = min(x, dpp::mov_i<dpp::kRowShr8>(INT32_MAX, x));
+    x = min(x, dpp::mov_i<dpp::kRowBcast15, 0xA>(INT32_MAX, x));
+    x = min(x, dpp::mov_i<dpp::kRowBcast31, 0xC>(INT32_MAX, x));
+    return wave_last_i(x);
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+    x = max(x, dpp::mov_i<dpp::kRowShr1>(INT32_MIN, x));
+    x = max(x, dpp::mov_i<dpp::kRowShr2>(INT32_MIN, x));
+    x = max(x, dpp::mov_i<dpp::kRowShr4>(INT32_MIN, x));
+    x = max(x, dpp::mov_i<dpp::kRowShr8>(INT32_MIN, x));
+    x = max(x, dpp::mov_i<dpp::kRowBcast15, 0xA>(INT32_MIN, x));
+    x = max(x, dpp::mov_i<dpp::kRowBcast31, 0xC>(INT32_MIN, x));
+    return wave_last_i(x);
+}
+
+// Exclusive prefix within the wavefront from an inclusive one (lane 0: 0).
+__device__ __forceinline__ float wave_excl_from_incl(float incl) {
+    return dpp::mov_f<dpp::kWaveShr1>(0.f, incl);
+}
+
+// Two workgroup sums at once, in a fixed order; every thread gets both.
+__device__ __forceinline__ void wg_sum2(float a, float b, float &sa, float &sb) {
+    __shared__ float s_t[2][kWaves];
+    a = wave_last(wave_incl_sum(a));
+    b = wave_last(wave_incl_sum(b));
+    const int w = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) {
+        s_t[0][w] = a;
+        s_t[1][w] = b;
+    }
+    __syncthreads();
+    sa = s_t[0][0];
+    sb = s_t[1][0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) {
+        sa += s_t[0][k];
+        sb += s_t[1][k];
+    }
+}
+
+// Two exclusive prefix sums over the workgroup's threads in thread order,
+// with both totals; every thread gets the totals.  One barrier.
+__device__ __forceinline__ void wg_excl_scan2(float a, float b, float &ea, float &eb, float &ta,
+                                              float &tb) {
+    __shared__ float s_t[2][kWaves];
+    const float ia = wave_incl_sum(a), ib = wave_incl_sum(b);
+    const int w = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == kWave - 1) {
+        s_t[0][w] = ia;
+        s_t[1][w] = ib;
+    }
+    __syncthreads();
+    float ba = 0.f, bb = 0.f;
+    ta = 0.f;
+    tb = 0.f;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+        if (k == w) {
+            ba = ta;
+            bb = tb;
+        }
+        ta += s_t[0][k];
+        tb += s_t[1][k];
+    }
+    ea = ba + wave_excl_from_incl(ia);
+    eb = bb + wave_excl_from_incl(ib);
+}
+
+// Workgroup minimum of one int and maximum of another; every thread gets both.
+__device__ __forceinline__ void wg_min_max(int mn, int mx, int &rmin, int &rmax) {
+    __shared__ int s_t[2][kWaves];
+    mn = wave_min_i(mn);
+    mx = wave_max_i(mx);
+    const int w = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) {
+        s_t[0][w] = mn;
+        s_t[1][w] = mx;
+    }
+    __syncthreads();
+    rmin = s_t[0][0];
+    rmax = s_t[1][0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) {
+        rmin = min(rmin, s_t[0][k]);
+        rmax = max(rmax, s_t[1][k]);
+    }
+}
+
+// Wavefront merge of (ref, z) on DPP moves in a fixed order; the result is
+// valid in lane 63 (read it with wave_last).
+__device__ __forceinline__ void mz_wave_merge(float &ref, float &z) {
+#define SV_MZ_STEP(CTRL, MASK)                                                   \
+    {                                                                            \
+        const float r2 = dpp::mov_f<CTRL, MASK>(-INFINITY, ref);                \
+        const float z2 = dpp::mov_f<CTRL, MASK>(0.f, z);                        \
+        mz_merge(ref, z, r2, z2);                                                \
+    }
+    SV_MZ_STEP(dpp::kRowShr1, 0xF)
+    SV_MZ_STEP(dpp::kRowShr2, 0xF)
+    SV_MZ_STEP(dpp::kRowShr4, 0xF)
+    SV_MZ_STEP(dpp::kRowShr8, 0xF)
+    SV_MZ_STEP(dpp::kRowBcast15, 0xA)
+    SV_MZ_STEP(dpp::kRowBcast31, 0xC)
+#undef SV_MZ_STEP
+}
+
+__device__ __forceinline__ void mz_reduce_wg(float &ref, float &z) {
+    __shared__ float s_ref[kWaves], s_z[kWaves];
+    mz_wave_merge(ref, z);
+    const int w = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == kWave - 1) {
+        s_ref[w] = ref;
+        s_z[w] = z;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        ref = s_ref[0];
+        z = s_z[0];
+        for (int i = 1; i < kWaves; ++i) mz_merge(ref, z, s_ref[i], s_z[i]);
+    }
 }
 
 }  // namespace sv

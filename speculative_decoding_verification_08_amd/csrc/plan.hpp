@@ -10,8 +10,13 @@ namespace sv {
 constexpr int kMaxK = 64;
 constexpr int kMaxTreeNodes = 256;
 constexpr int kChunk2Bytes = 16384;  // bytes of one row per chunk of the residual / bonus pass
-constexpr int kMergeLds = 1024;  // row partials merged through LDS up to this many
-constexpr int kSumsLds = 2048;   // chunk masses staged in LDS up to this many
+constexpr int kMaxDrawChunks = 64;  // draw chunks per row: V <= 64 x 16 KB of entries
+constexpr int kMergeLds = 512;   // row partials merged through LDS up to this many
+constexpr int kSumsLds = 512;    // chunk masses staged in LDS up to this many
+// LDS floats of a draw workgroup: its sequence's row statistics and staged
+// partials during the resolve, then the staged chunk masses.
+constexpr int kDrawLds = 2 * (2 * kMaxK + 1) + 2 * kMergeLds;
+static_assert(kSumsLds <= kDrawLds, "chunk masses fit the draw workgroup's LDS");
 
 // How a launch cuts the rows it streams into vocabulary chunks, and where its
 // scratch lives inside the caller's workspace.
@@ -21,7 +26,7 @@ struct Plan {
     int nchunk = 0;        // chunks per row, first pass
     int chunk2 = 0;        // elements per chunk, residual / bonus pass (chain)
     int nchunk2 = 0;       // chunks per row, residual / bonus pass (chain)
-    size_t off_partial = 0, off_gather = 0, off_sums = 0, off_counters = 0;
+    size_t off_partial = 0, off_gather = 0, off_sums = 0;
     size_t bytes = 0;      // total workspace
 };
 
@@ -31,7 +36,7 @@ struct Plan {
 // fresh ones.
 constexpr uint32_t kPhasedTag = 1;  // tag of the phase entry points; whole calls use >= 2
 
-// Chain verify, both phases.
+// Chain verify, both kernels.
 struct ChainArgs {
     const void *target;      // [B][K+1][V]
     const void *draft;       // [B][K][V]
@@ -44,13 +49,11 @@ struct ChainArgs {
     int32_t chunk, nchunk, nchunk2;  // chunk2 = kChunk2Bytes / element size
     uint64_t *partial;       // [B][2K+1][nchunk][2] tagged (ref, z); rows 0..K target, K+1.. draft
     uint64_t *gathered;      // [B][2K+1] tagged logit of each row at its drafted token (row K unused)
-    uint64_t *sums;          // [B][nchunk2] tagged draw mass per chunk
-    uint32_t *counters;      // [B] finished tail workgroups (zeroed by the statistics kernel)
+    uint64_t *sums;          // [B][nchunk2][2] tagged residual and target mass per chunk
     int32_t *out_tokens;     // [B][K+1]
     int32_t *out_accepted;   // [B]
     float *out_diag;         // nullable [B][K+1][4]
 };
-
 
 // Row argmax over rows of [rows][V].
 struct ArgmaxArgs {
@@ -87,7 +90,7 @@ struct TreeArgs {
 
 // Host launchers (defined next to their kernels).
 hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s);
-hipError_t launch_chain_tail(const ChainArgs &a, int dtype, hipStream_t s);
+hipError_t launch_chain_draw(const ChainArgs &a, int dtype, hipStream_t s);
 hipError_t launch_row_argmax(const ArgmaxArgs &a, int dtype, hipStream_t s);
 hipError_t launch_greedy_resolve(const GreedyArgs &a, hipStream_t s);
 hipError_t launch_tree_resolve(const TreeArgs &a, hipStream_t s);

@@ -35,6 +35,14 @@ def test_workspace_bytes():
         assert e.value.status == sv.SPEC_ERR_INVALID_ARG
     with pytest.raises(sv.SpecVerifyError):
         ws(sv.SPEC_MODE_CHAIN, 2, 4, 100, 5)
+    # the chain verify's vocabulary limit (64 draw chunks of 16 KB per row)
+    assert ws(sv.SPEC_MODE_CHAIN, 2, 4, sv.MAX_CHAIN_V_BF16, sv.SPEC_DTYPE_BF16) > 0
+    assert ws(sv.SPEC_MODE_CHAIN, 2, 4, sv.MAX_CHAIN_V_F32, sv.SPEC_DTYPE_F32) > 0
+    for V, dt in ((sv.MAX_CHAIN_V_BF16 + 1, sv.SPEC_DTYPE_BF16),
+                  (sv.MAX_CHAIN_V_F32 + 1, sv.SPEC_DTYPE_F32)):
+        with pytest.raises(sv.SpecVerifyError):
+            ws(sv.SPEC_MODE_CHAIN, 2, 4, V, dt)
+    assert ws(sv.SPEC_MODE_GREEDY, 2, 4, sv.MAX_V, sv.SPEC_DTYPE_BF16) > 0
 
 
 def _chain(lib, **kw):

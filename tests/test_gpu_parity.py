@@ -109,6 +109,34 @@ def test_chain_edge_cases(sv):
     parity.check_chain(d3, *g)
 
 
+def test_chain_repeated_calls_bitwise(sv):
+    """Results are reproducible bit for bit, call after call on one workspace."""
+    d = chain_case("repeat", 9, 5, 20000, "bf16", 1.0, recipe="peaked", sigma=0.7)
+    case("chain repeated calls")
+    t, dr = dev(d["target"]), dev(d["draft"])
+    x, ua, us = dev(d["tokens"]), dev(d["u_accept"]), dev(d["u_sample"])
+    B, K, V = d["tokens"].shape[0], d["tokens"].shape[1], t.shape[-1]
+    ws = sv.workspace(sv.SPEC_MODE_CHAIN, B, K, V, sv.SPEC_DTYPE_BF16, DEV)
+    first = None
+    for _ in range(4):
+        tok, acc, diag = sv.spec_verify_chain(t, dr, x, ua, us, 1.0, diag=True, workspace_buf=ws)
+        torch.cuda.synchronize()
+        got = (tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy())
+        if first is None:
+            first = got
+            parity.check_chain(d, *got)
+        else:
+            assert all(np.array_equal(g, f) for g, f in zip(got, first))
+
+
+@pytest.mark.parametrize("B,K,V", [(1, 5, 300000), (3, 64, 2000), (128, 1, 4096)])
+def test_chain_grid_shapes(sv, B, K, V):
+    """Few large sequences, the longest draft, many short rows."""
+    case(f"chain grid B={B} K={K} V={V}")
+    d = chain_case("grid", B, K, V, "bf16", 1.0, recipe="peaked", sigma=0.7)
+    parity.check_chain(d, *run_chain(sv, d))
+
+
 def test_chain_phases_equal_one_call(sv):
     d = chain_case("phases", 9, 5, 20000, "bf16", 1.0, recipe="peaked", sigma=0.7)
     case("chain phases")
@@ -116,13 +144,33 @@ def test_chain_phases_equal_one_call(sv):
     t, dr = dev(d["target"]), dev(d["draft"])
     B, K, V = d["tokens"].shape[0], d["tokens"].shape[1], t.shape[-1]
     ws = sv.workspace(sv.SPEC_MODE_CHAIN, B, K, V, sv.SPEC_DTYPE_BF16, DEV)
-    sv.spec_verify_chain_stats(t, dr, dev(d["tokens"]), 1.0, ws)
     diag = torch.empty((B, K + 1, 4), dtype=torch.float32, device=DEV)
-    tok, acc, _ = sv.spec_verify_chain_sample(t, dr, dev(d["tokens"]), dev(d["u_accept"]),
-                                              dev(d["u_sample"]), 1.0, ws, out_diag=diag)
+    x = dev(d["tokens"])
+    sv.spec_verify_chain_stats(t, dr, x, 1.0, ws)
+    tok, acc = sv.spec_verify_chain_sample(t, dr, x, dev(d["u_accept"]), dev(d["u_sample"]), 1.0,
+                                           ws, out_diag=diag)
     torch.cuda.synchronize()
     assert np.array_equal(tok.cpu().numpy(), one[0]) and np.array_equal(acc.cpu().numpy(), one[1])
     assert np.array_equal(diag.cpu().numpy(), one[2])
+
+
+def test_chain_prepared_launch_equals_call(sv):
+    d = chain_case("prepared", 9, 5, 20000, "bf16", 1.0, recipe="peaked", sigma=0.7)
+    case("chain prepared launch")
+    one = run_chain(sv, d)
+    t, dr = dev(d["target"]), dev(d["draft"])
+    B, K, V = d["tokens"].shape[0], d["tokens"].shape[1], t.shape[-1]
+    ws = sv.workspace(sv.SPEC_MODE_CHAIN, B, K, V, sv.SPEC_DTYPE_BF16, DEV)
+    tok = torch.empty((B, K + 1), dtype=torch.int32, device=DEV)
+    acc = torch.empty((B,), dtype=torch.int32, device=DEV)
+    diag = torch.empty((B, K + 1, 4), dtype=torch.float32, device=DEV)
+    x, ua, us = dev(d["tokens"]), dev(d["u_accept"]), dev(d["u_sample"])
+    launch = sv.prepare_chain(t, dr, x, ua, us, 1.0, tok, acc, ws, out_diag=diag)
+    for _ in range(3):
+        launch()
+        torch.cuda.synchronize()
+        assert np.array_equal(tok.cpu().numpy(), one[0]) and np.array_equal(acc.cpu().numpy(), one[1])
+        assert np.array_equal(diag.cpu().numpy(), one[2])
 
 
 def test_chain_workspace_reuse_across_shapes(sv):
