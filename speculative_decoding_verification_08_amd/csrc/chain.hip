@@ -128,212 +128,104 @@ __device__ __forceinline__ void stats_item(const ChainArgs &a, int64_t b, int r,
 
 // ------------------------------------------------------------ draw weights
 
-// Entries per chunk of the residual / bonus pass: 16 KB of one row.
-template <class DT>
-struct Chunk2 {
-    static constexpr int kElems = kChunk2Bytes / (16 / DT::kVec);
-};
-
-// Draw weight of one vocabulary entry of row j.
-__device__ __forceinline__ float draw_weight(float t, float d, float c, float rt, float izt,
-                                             float rd, float izd, bool resid) {
-    const float p = __fmul_rn(exp2_hw(fmaf(t, c, -rt)), izt);
-    if (!resid) return p;
-    const float q = __fmul_rn(exp2_hw(fmaf(d, c, -rd)), izd);
-    return fmaxf(p - q, 0.f);
-}
-
-// Row j's draw weights: statistics of its target (and draft) row.
+// Draw weights of one vocabulary entry of row j: p = 2^(l*c - ref) / z of the
+// target row, and the residual max(0, p - q) with q likewise from the draft
+// row.  Both passes over an entry (chunk masses, then the search inside the
+// crossing chunk) evaluate these same expressions, so they agree bit for bit.
 struct DrawRow {
     int64_t trow, drow;  // element offsets of target row j and draft row j
     float rt, izt, rd, izd;
-    bool resid;
+    bool resid;          // j < K: a rejection, draw from the residual
+};
+__device__ __forceinline__ float weight_p(float t, float c, const DrawRow &w) {
+    return __fmul_rn(exp2_hw(fmaf(t, c, -w.rt)), w.izt);
+}
+__device__ __forceinline__ float weight_r(float p, float d, float c, const DrawRow &w) {
+    return fmaxf(fmaf(-exp2_hw(fmaf(d, c, -w.rd)), w.izd, p), 0.f);
+}
+
+// Bits of -inf: entries past the end of a row are replaced by them, which
+// gives them weight 0 in both kinds (c > 0) without a test per entry.
+template <class DT>
+struct NegInf;
+template <>
+struct NegInf<Bf16> {
+    static constexpr uint32_t kBits = 0xff80ff80u;
+};
+template <>
+struct NegInf<F32> {
+    static constexpr uint32_t kBits = 0xff800000u;
 };
 
-// Per-lane sum of the draw weights of chunk [e0, e1) of row j.  With V a
-// multiple of the vector width every lane issues all its 16-byte loads (4
-// per row) before using any.
-template <class DT>
-__device__ __forceinline__ float lane_mass(const ChainArgs &a, const DrawRow &w, int64_t e0,
-                                           int64_t e1) {
-    constexpr int VEC = DT::kVec;
-    constexpr int NV = Chunk2<DT>::kElems / (VEC * kWG);
-    float acc = 0.f;
-    if (a.V % VEC == 0) {
-        // Every lane issues all its loads before using any: indices past the
-        // chunk are clamped to its last vector and their weights dropped (a
-        // branch around each load would make each one wait for the last).
-        // The bonus draw has no draft row and re-reads the target row instead.
-        const uint4 *tp = static_cast<const uint4 *>(a.target);
-        const uint4 *dp = w.resid ? static_cast<const uint4 *>(a.draft) : tp;
-        const int64_t v0 = (w.trow + e0) / VEC, nv = (e1 - e0) / VEC;
-        const int64_t d0 = ((w.resid ? w.drow : w.trow) + e0) / VEC;
-        uint4 rt[NV], rd[NV];
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int64_t o = min(static_cast<int64_t>(threadIdx.x + i * kWG), nv - 1);
-            rt[i] = tp[v0 + o];
-            rd[i] = dp[d0 + o];
-        }
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const bool in = threadIdx.x + i * kWG < nv;
-            float t[VEC], d[VEC];
-            unpack<DT>(rt[i], t);
-            unpack<DT>(rd[i], d);
-            float part = 0.f;
-#pragma unroll
-            for (int q = 0; q < VEC; ++q)
-                part += draw_weight(t[q], d[q], a.c, w.rt, w.izt, w.rd, w.izd, w.resid);
-            acc += in ? part : 0.f;
-        }
-    } else {
-        for (int64_t e = e0 + threadIdx.x; e < e1; e += kWG) {
-            const float t = load_one<DT>(a.target, w.trow + e);
-            const float d = w.resid ? load_one<DT>(a.draft, w.drow + e) : 0.f;
-            acc += draw_weight(t, d, a.c, w.rt, w.izt, w.rd, w.izd, w.resid);
-        }
-    }
-    return acc;
-}
-
-// Running masses of a sequence's draw chunks, scanned 64 chunks at a time
-// by one wavefront in a fixed order (chunk masses from LDS when staged, else
-// from the published words).  Returns S, the total, in every lane.  With
-// `cstar`, also finds the crossing chunk: the first whose inclusive running
-// mass exceeds tau (the inverse CDF, strict), else the last chunk with mass
-// (tau rounded up to S), and `base`, the running mass before it.
-__device__ __forceinline__ float scan_masses(const float *s_m, const uint64_t *sums, int nc, bool staged,
-                             float tau, int *cstar, float *base) {
-    const int lane = threadIdx.x % kWave;
-    float carry = 0.f, last_base = 0.f;
-    int found = -1, last_pos = 0;
-    float found_base = 0.f;
-    for (int i0 = 0; i0 < nc; i0 += kWave) {
-        const int i = i0 + lane;
-        float m = 0.f;
-        if (i < nc) m = staged ? s_m[i] : word_f32(fetch(&sums[i]));
-        const float incl = carry + wave_incl_sum(m);
-        float excl = wave_excl_from_incl(incl);
-        if (lane == 0) excl = carry;
-        if (cstar) {
-            const uint64_t cross = __ballot(i < nc && incl > tau);
-            if (found < 0 && cross) {
-                const int l = __ffsll(static_cast<unsigned long long>(cross)) - 1;
-                found = i0 + l;
-                found_base = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), l));
-            }
-            const uint64_t pos = __ballot(i < nc && m > 0.f);
-            if (pos) {
-                const int l = 63 - __clzll(static_cast<long long>(pos));
-                last_pos = i0 + l;
-                last_base = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), l));
-            }
-        }
-        carry = wave_last(incl);
-    }
-    if (cstar) {
-        *cstar = found >= 0 ? found : last_pos;
-        *base = found >= 0 ? found_base : last_base;
-    }
-    return carry;
-}
-
 // Resolve of sequence b inside a draw workgroup, from the statistics the
-// first kernel left (ordered before this kernel by the stream): merges each
-// row's chunks with a fixed DPP tree, evaluates the accept test of every
-// drafted token (u < P/Q, strict; Q = 0 accepts iff P > 0) and returns j, the
-// first rejected position (K if none), with row j's statistics in `w`.
-// `ok` is false if a word was not written for this call.  With `diag` the
-// workgroup also writes p_k(x_k), q_k(x_k) and their ratio to out_diag.
+// first kernel left (ordered before this kernel by the stream).  Each group
+// of 16 lanes merges one row's chunk statistics (lane i folds chunks i,
+// i + 16, ... in order, then a fixed DPP tree), every wavefront evaluates the
+// accept test of every drafted token (u < P/Q, strict; Q = 0 accepts iff
+// P > 0) and takes j, the first rejected position (K if none), by ballot, so
+// no second barrier is needed.  Row j's statistics land in `w`.  `ok` is false
+// if a word was not written for this call.  With `diag` the workgroup also
+// writes p_k(x_k), q_k(x_k) and their ratio to out_diag.
 template <class DT>
 __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow &w, bool &ok,
                                              bool diag, float *lds) {
+    constexpr int kGroup = 16, kGroups = kWG / kGroup, kFold = 4;
     float *s_ref = lds, *s_z = s_ref + (2 * kMaxK + 1);
-    float *s_pr = s_z + (2 * kMaxK + 1), *s_pz = s_pr + kMergeLds;
-    __shared__ int s_j, s_stale;
-    const int K = a.K, V = a.V, R = 2 * K + 1, tid = threadIdx.x, lane = tid % kWave;
-    const int np = R * a.nchunk;
-    const uint64_t *part = a.partial + 2 * static_cast<int64_t>(b) * np;
+    __shared__ int s_stale[kWaves];
+    const int K = a.K, V = a.V, R = 2 * K + 1, nch = a.nchunk;
+    const int tid = threadIdx.x, lane = tid % kWave, grp = tid / kGroup, gl = tid % kGroup;
+    const uint4 *part = reinterpret_cast<const uint4 *>(a.partial) + static_cast<int64_t>(b) * R * nch;
     const uint64_t *gat = a.gathered + static_cast<int64_t>(b) * R;
-    const bool staged = np <= kMergeLds;
-    // One round trip: partials, drafted-token logits and uniforms are all
-    // loaded (from clamped indices, without branches) before any is used.
+    // Uniforms and drafted-token logits of lane k's position, loaded by every
+    // wavefront (from clamped indices) together with the first partials.
     const float *ua = K > 0 ? a.u_accept + static_cast<int64_t>(b) * K : a.u_sample + b;
-    float u = ua[min(tid, max(K - 1, 0))];
-    const uint64_t wt = gat[min(tid, R - 1)], wd = gat[min(K + 1 + tid, R - 1)];
-    const int i0 = min(tid, np - 1);
-    const uint64_t wr0 = part[2 * i0], wz0 = part[2 * i0 + 1];
-    int stale = 0;
-    float lt = 0.f, ld = 0.f;
-    if (tid < K) {
-        stale |= !current(wt, a.tag) || !current(wd, a.tag);
-        lt = word_f32(wt);
-        ld = word_f32(wd);
-    }
-    if (staged) {
-        if (tid < np) {
-            stale |= !current(wr0, a.tag) || !current(wz0, a.tag);
-            s_pr[tid] = word_f32(wr0);
-            s_pz[tid] = word_f32(wz0);
-        }
-        for (int i = tid + kWG; i < np; i += kWG) {
-            const uint64_t wr = part[2 * i], wz = part[2 * i + 1];
-            stale |= !current(wr, a.tag) || !current(wz, a.tag);
-            s_pr[i] = word_f32(wr);
-            s_pz[i] = word_f32(wz);
-        }
-    }
-    if (tid == 0) s_stale = 0;
-    __syncthreads();
-    // Row r's chunk statistics are merged by wave r % kWaves: lane i folds
-    // chunks i, i + 64, ... in order, then a fixed DPP tree merges the lanes
-    // and lane 63's result is the row's.
+    const float u = ua[min(lane, max(K - 1, 0))];
+    const uint64_t wt = gat[min(lane, R - 1)], wd = gat[min(K + 1 + lane, R - 1)];
     bool fresh = true;
-    for (int r = tid / kWave; r < R; r += kWaves) {
+    for (int r0 = 0; r0 < R; r0 += kGroups) {
+        const int r = r0 + grp, rr = min(r, R - 1);
         float ref = -INFINITY, z = 0.f;
-        for (int i = lane; i < a.nchunk; i += kWave) {
-            const int q = r * a.nchunk + i;
-            float pr, pz;
-            if (staged) {
-                pr = s_pr[q];
-                pz = s_pz[q];
-            } else {
-                const uint64_t wr = part[2 * q], wz = part[2 * q + 1];
-                fresh = fresh && current(wr, a.tag) && current(wz, a.tag);
-                pr = word_f32(wr);
-                pz = word_f32(wz);
+        for (int i0 = 0; i0 < nch; i0 += kGroup * kFold) {
+            uint4 pw[kFold];
+#pragma unroll
+            for (int f = 0; f < kFold; ++f)
+                pw[f] = part[rr * nch + min(i0 + gl + kGroup * f, nch - 1)];
+#pragma unroll
+            for (int f = 0; f < kFold; ++f) {
+                const bool in = r < R && i0 + gl + kGroup * f < nch;
+                fresh = fresh && (!in || (pw[f].y == a.tag && pw[f].w == a.tag));
+                mz_merge(ref, z, in ? __uint_as_float(pw[f].x) : -INFINITY,
+                         in ? __uint_as_float(pw[f].z) : 0.f);
             }
-            mz_merge(ref, z, pr, pz);
         }
-        mz_wave_merge(ref, z);
-        if (lane == kWave - 1) {
+        mz_row_merge(ref, z);
+        if (r < R && gl == kGroup - 1) {
             s_ref[r] = ref;
             s_z[r] = z;
         }
     }
-    if (stale || !fresh) s_stale = 1;  // benign race: every writer stores 1
+    const bool tok_ok = lane >= K || (current(wt, a.tag) && current(wd, a.tag));
+    const uint64_t stale = __ballot(!fresh || !tok_ok);
+    if (lane == 0) s_stale[tid / kWave] = stale != 0;
     __syncthreads();
-    ok = !s_stale;
-    // Accept test on wave 0 (K <= 64), first rejection by ballot.
-    if (tid < kWave) {
-        bool reject = false;
-        if (tid < K) {
-            const float P = exp2_hw(fmaf(lt, a.c, -s_ref[tid])) / s_z[tid];
-            const float Q = exp2_hw(fmaf(ld, a.c, -s_ref[K + 1 + tid])) / s_z[K + 1 + tid];
-            reject = !(Q > 0.f ? (u < P / Q) : (P > 0.f));
-            if (diag && a.out_diag) {
-                float *dg = a.out_diag + 4 * (static_cast<int64_t>(b) * (K + 1) + tid);
-                dg[0] = P;
-                dg[1] = Q;
-                dg[2] = Q > 0.f ? P / Q : (P > 0.f ? INFINITY : 0.f);
-            }
+    int any_stale = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) any_stale |= s_stale[k];
+    ok = !any_stale;
+    bool reject = false;
+    if (lane < K) {
+        const float P = exp2_hw(fmaf(word_f32(wt), a.c, -s_ref[lane])) / s_z[lane];
+        const float Q = exp2_hw(fmaf(word_f32(wd), a.c, -s_ref[K + 1 + lane])) / s_z[K + 1 + lane];
+        reject = !(Q > 0.f ? (u < P / Q) : (P > 0.f));
+        if (diag && tid < kWave && a.out_diag) {
+            float *dg = a.out_diag + 4 * (static_cast<int64_t>(b) * (K + 1) + lane);
+            dg[0] = P;
+            dg[1] = Q;
+            dg[2] = Q > 0.f ? P / Q : (P > 0.f ? INFINITY : 0.f);
         }
-        const uint64_t m = __ballot(reject);
-        if (tid == 0) s_j = m ? (__ffsll(static_cast<unsigned long long>(m)) - 1) : K;
     }
-    __syncthreads();
-    const int j = s_j;
+    const uint64_t m = __ballot(reject);
+    const int j = m ? (__ffsll(static_cast<unsigned long long>(m)) - 1) : K;
     w.resid = j < K;
     w.rt = s_ref[j];
     w.izt = 1.f / s_z[j];
@@ -344,62 +236,44 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
     return j;
 }
 
-// ------------------------------------------------------------ draw item
+// Entries per chunk of the residual / bonus pass: 16 KB of one row.
+template <class DT>
+struct Chunk2 {
+    static constexpr int kElems = kChunk2Bytes / (16 / DT::kVec);
+    static constexpr int kSeg = kElems / kWG;    // contiguous entries per thread
+    static constexpr int kNQ = kSeg / DT::kVec;  // 16-byte vectors per thread and row
+    static constexpr int kRawWords = 4 * kNQ;    // 32-bit words per thread and row
+};
 
-// Workgroup (b, ch) of the draw.  It holds entries [ch*C2, ch*C2 + C2) of row
-// j in registers (kSeg contiguous entries per thread), publishes the chunk's
-// residual mass sum max(0, p_j - q_j) and target mass sum p_j, and prepares
-// the running sums inside its chunk while the sequence's other chunks
-// publish theirs.  Once all are visible every draw workgroup of the sequence
-// computes the same S and the same crossing chunk -- the first whose
-// inclusive running mass exceeds u * S (the inverse CDF, strict), else the
-// last chunk with mass -- and the workgroup owning it picks the token and
-// writes the sequence's outputs.  An all-zero residual (reachable only
-// through rounding) draws from p_j; the bonus draw (j = K) always uses p_K.
-template <class DT, bool VecOk>
-__device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, float *s_m) {
-    constexpr int VEC = DT::kVec;
-    constexpr int C2 = Chunk2<DT>::kElems;
-    constexpr int kSeg = C2 / kWG;  // contiguous entries per thread
-    constexpr int NQ = kSeg / VEC;
-    const int K = a.K, V = a.V, tid = threadIdx.x;
-    const int nc = a.nchunk2;
-    __shared__ float s_S, s_tau, s_base;
-    __shared__ int s_cstar, s_fresh, s_resid;
-
-    static_assert(kMaxK + 1 <= kWG, "one thread per emitted token");
-    // Drafted tokens for the emission, loaded now (thread k emits token k).
-    const int32_t *tk = K > 0 ? a.tokens + static_cast<int64_t>(b) * K
-                              : reinterpret_cast<const int32_t *>(a.u_sample + b);
-    const int32_t my_tok = tk[min(tid, max(K - 1, 0))];
-
-    const float us = a.u_sample[b];
-
-    DrawRow w;
-    bool ok;
-    const int j = resolve_local<DT>(a, b, w, ok, ch == 0, s_m);
-
-    // This thread's entries of the chunk, both kinds of weight.
-    const int64_t c0 = static_cast<int64_t>(ch) * C2;
-    const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(V) - c0));
-    const int s0 = tid * kSeg;
-    uint4 rt[NQ], rd[NQ];
+// This thread's entries [s0, s0 + kSeg) of chunk c0 of row j (target, and
+// draft when Resid), as raw 16-byte vectors; entries past the row's end read
+// as -inf.  With V a multiple of the vector width all loads are issued before
+// any is used; otherwise entries are read one by one into the same layout.
+template <class DT, bool VecOk, bool Resid>
+__device__ __forceinline__ void load_chunk(const ChainArgs &a, const DrawRow &w, int64_t c0, int n,
+                                           int s0, uint4 (&rt)[Chunk2<DT>::kNQ],
+                                           uint4 (&rd)[Chunk2<DT>::kNQ]) {
+    constexpr int VEC = DT::kVec, NQ = Chunk2<DT>::kNQ;
+    constexpr uint32_t kInf = NegInf<DT>::kBits;
     if constexpr (VecOk) {
-        // All loads issued before any use; entries past the chunk are clamped
-        // to its last vector and get weight 0.  Without a draft row (bonus
-        // draw) the target row is read twice and the copy is unused.
-        const uint4 *tp = static_cast<const uint4 *>(a.target);
-        const uint4 *dp = w.resid ? static_cast<const uint4 *>(a.draft) : tp;
-        const int64_t tb = (w.trow + c0) / VEC, db = ((w.resid ? w.drow : w.trow) + c0) / VEC;
+        const uint4 *tp = static_cast<const uint4 *>(a.target) + (w.trow + c0) / VEC;
+        const uint4 *dp = static_cast<const uint4 *>(a.draft) + (w.drow + c0) / VEC;
         const int last = n / VEC - 1;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const int o = min((s0 + q * VEC) / VEC, last);
-            rt[q] = tp[tb + o];
-            rd[q] = dp[db + o];
+            const int o = min(s0 / VEC + q, last);
+            rt[q] = tp[o];
+            if (Resid) rd[q] = dp[o];
+        }
+        if (n < Chunk2<DT>::kElems) {  // the row's last chunk: whole vectors past its end
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                if (s0 + q * VEC >= n) {
+                    rt[q] = make_uint4(kInf, kInf, kInf, kInf);
+                    rd[q] = rt[q];
+                }
         }
     } else {
-        // Unaligned rows: entries one by one, packed into the same layout.
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             uint32_t wt4[4], wd4[4];
@@ -408,9 +282,11 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
                 uint32_t tb = 0, db = 0;
 #pragma unroll
                 for (int e2 = 0; e2 < VEC / 4; ++e2) {
-                    const int e = min(s0 + q * VEC + h * (VEC / 4) + e2, n - 1);
-                    const float t = load_one<DT>(a.target, w.trow + c0 + e);
-                    const float d = w.resid ? load_one<DT>(a.draft, w.drow + c0 + e) : 0.f;
+                    const int e = s0 + q * VEC + h * (VEC / 4) + e2, ec = min(e, n - 1);
+                    float t = load_one<DT>(a.target, w.trow + c0 + ec);
+                    float d = Resid ? load_one<DT>(a.draft, w.drow + c0 + ec) : 0.f;
+                    t = e < n ? t : -INFINITY;
+                    d = e < n ? d : -INFINITY;
                     if (VEC == 8) {
                         tb |= (__float_as_uint(t) >> 16) << (16 * e2);
                         db |= (__float_as_uint(d) >> 16) << (16 * e2);
@@ -426,38 +302,71 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
             rd[q] = make_uint4(wd4[0], wd4[1], wd4[2], wd4[3]);
         }
     }
-    // Weights of entry (q, i): p, and max(0, p - q) after a rejection.
-    auto weights = [&](int q, float (&wp)[VEC], float (&wr)[VEC]) {
-        float t[VEC], d[VEC];
-        unpack<DT>(rt[q], t);
-        unpack<DT>(rd[q], d);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            const bool in = s0 + q * VEC + i < n;
-            wp[i] = in ? draw_weight(t[i], 0.f, a.c, w.rt, w.izt, 0.f, 0.f, false) : 0.f;
-            wr[i] = in && w.resid
-                        ? draw_weight(t[i], d[i], a.c, w.rt, w.izt, w.rd, w.izd, true)
-                        : 0.f;
-        }
-    };
+}
+
+// Entry e of a thread's raw words (the layout load_chunk fills), widened.
+template <class DT>
+__device__ __forceinline__ float raw_entry(const uint32_t *words, int e) {
+    if constexpr (DT::kVec == 8) {
+        const uint32_t v = words[e >> 1];
+        return __uint_as_float((e & 1) ? (v & 0xffff0000u) : (v << 16));
+    } else {
+        return __uint_as_float(words[e]);
+    }
+}
+
+// ------------------------------------------------------------ draw item
+
+// Workgroup (b, ch) of the draw after the resolve.  It holds entries
+// [ch*C2, ch*C2 + C2) of row j in registers (kSeg contiguous entries per
+// thread) and publishes the chunk's residual mass sum max(0, p_j - q_j) and
+// target mass sum p_j.  Wavefront 0 polls every chunk's masses of the
+// sequence into its lanes (a sequence has at most 64 chunks), and every draw
+// workgroup of the sequence computes the same S and the same crossing chunk:
+// the first whose inclusive running mass exceeds u * S (the inverse CDF,
+// strict), else the last chunk with mass.  In the workgroup owning it, the
+// first thread whose running mass passes u * S hands its entries to
+// wavefront 0 through LDS, which finds the entry (one lane each) and writes
+// the sequence's outputs.  An all-zero residual (reachable only through
+// rounding) draws from p_j; the bonus draw (j = K) always uses p_K.
+template <class DT, bool VecOk, bool Resid>
+__device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int j, const DrawRow &w,
+                                          bool ok, float us, int32_t my_tok, float *lds) {
+    using CK = Chunk2<DT>;
+    constexpr int VEC = DT::kVec, C2 = CK::kElems, kSeg = CK::kSeg, NQ = CK::kNQ;
+    static_assert(kSeg <= kWave, "one lane per entry of a thread's segment");
+    static_assert(CK::kRawWords <= kDrawRawWords, "a thread's raw entries fit the LDS");
+    static_assert(kMaxDrawChunks <= kWave, "one lane per chunk of a sequence");
+    const int K = a.K, tid = threadIdx.x, lane = tid % kWave, nc = a.nchunk2;
+    const float c = a.c;
+    __shared__ float s_tau, s_base;
+    __shared__ int s_cstar, s_resid, s_ok;
+
+    const int64_t c0 = static_cast<int64_t>(ch) * C2;
+    const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(a.V) - c0));
+    const int s0 = tid * kSeg;
+    uint4 rt[NQ], rd[NQ];
+    load_chunk<DT, VecOk, Resid>(a, w, c0, n, s0, rt, rd);
+
     float lp = 0.f, lr = 0.f;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-        float wp[VEC], wr[VEC];
-        weights(q, wp, wr);
+        float t[VEC], d[VEC];
+        unpack<DT>(rt[q], t);
+        if (Resid) unpack<DT>(rd[q], d);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
-            lp += wp[i];
-            lr += wr[i];
+            const float p = weight_p(t[i], c, w);
+            lp += p;
+            if (Resid) lr += weight_r(p, d[i], c, w);
         }
         asm volatile("" : "+v"(lp), "+v"(lr));  // one slot at a time
     }
-    // The raw entries stay in registers for the crossing search; mark them
-    // rewritten so the weights are recomputed there instead of kept alive.
+    // The raw entries stay in registers for the crossing search.
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         asm volatile("" : "+v"(rt[q].x), "+v"(rt[q].y), "+v"(rt[q].z), "+v"(rt[q].w));
-        asm volatile("" : "+v"(rd[q].x), "+v"(rd[q].y), "+v"(rd[q].z), "+v"(rd[q].w));
+        if (Resid) asm volatile("" : "+v"(rd[q].x), "+v"(rd[q].y), "+v"(rd[q].z), "+v"(rd[q].w));
     }
     // Running sums inside the chunk and the chunk's masses, both kinds, in
     // one pass (published afterwards: a barrier after a device-scope store
@@ -470,26 +379,43 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
         publish_f32(&sums[2 * ch + 1], a.tag, mp);
     }
 
-    // Wait (bounded) for every chunk's masses; stage the chosen kind later.
-    const bool staged = nc <= kSumsLds;
+    // Wavefront 0: lane i polls chunk i's masses (bounded), then the
+    // sequence-wide choice of kind, total and crossing chunk, in registers.
+    float S = 0.f;
     if (tid < kWave) {
-        bool fresh = false;
+        const int i = min(lane, nc - 1);
+        uint64_t vr, vp;
+        bool fresh;
         const uint64_t t0 = wall_clock64();
         for (;;) {
-            fresh = true;
-            for (int i = tid; i < nc; i += kWave) {
-                const uint64_t vr = fetch(&sums[2 * i]), vp = fetch(&sums[2 * i + 1]);
-                fresh = fresh && current(vr, a.tag) && current(vp, a.tag);
-            }
-            fresh = __all(fresh);
+            vr = fetch(&sums[2 * i]);
+            vp = fetch(&sums[2 * i + 1]);
+            fresh = __all(current(vr, a.tag) && current(vp, a.tag));
             if (fresh || wall_clock64() - t0 > kWaitTicks) break;
             __builtin_amdgcn_s_sleep(2);
         }
-        if (tid == 0) s_fresh = fresh;
+        const bool in = lane < nc;
+        const float m_r = in ? word_f32(vr) : 0.f, m_p = in ? word_f32(vp) : 0.f;
+        const float inc_r = wave_incl_sum(m_r), inc_p = wave_incl_sum(m_p);
+        const bool resid = Resid && wave_last(inc_r) > 0.f;
+        const float m = resid ? m_r : m_p, incl = resid ? inc_r : inc_p;
+        S = wave_last(incl);
+        const float tau = us * S;
+        const float excl = wave_excl_from_incl(incl);
+        const uint64_t cross = __ballot(in && incl > tau), pos = __ballot(in && m > 0.f);
+        const int l = cross ? __ffsll(static_cast<unsigned long long>(cross)) - 1
+                            : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
+        const float base = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), l));
+        if (lane == 0) {
+            s_ok = fresh;
+            s_cstar = l;
+            s_base = base;
+            s_tau = tau;
+            s_resid = resid;
+        }
     }
     __syncthreads();
-    ok = ok && s_fresh;
-    if (!ok) {
+    if (!(ok && s_ok)) {
         // A bounded wait ran out: the last chunk's workgroup marks the
         // sequence as failed.
         if (ch == nc - 1) {
@@ -499,123 +425,70 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
         }
         return;
     }
-    // Residual or p: the same decision in every workgroup of the sequence.
-    if (tid < kWave) {
-        for (int i = tid; i < nc; i += kWave)
-            if (staged) s_m[i] = word_f32(fetch(&sums[2 * i]));
-        float S = staged ? scan_masses(s_m, sums, nc, true, 0.f, nullptr, nullptr) : 0.f;
-        if (!staged) {
-            float carry = 0.f;
-            for (int i0 = 0; i0 < nc; i0 += kWave) {
-                const int i = i0 + tid;
-                const float m = i < nc ? word_f32(fetch(&sums[2 * i])) : 0.f;
-                carry = carry + wave_last(wave_incl_sum(m));
-            }
-            S = carry;
-        }
-        const bool resid = w.resid && S > 0.f;
-        if (!resid) {
-            for (int i = tid; i < nc; i += kWave)
-                if (staged) s_m[i] = word_f32(fetch(&sums[2 * i + 1]));
-        }
-        if (tid == 0) s_resid = resid;
-    }
-    __syncthreads();
-    const bool resid = s_resid;
-    if (tid < kWave) {
-        // With unstaged masses the scan reads the chosen words in place.
-        const uint64_t *src = sums + (resid ? 0 : 1);
-        float S;
-        if (staged) {
-            S = scan_masses(s_m, nullptr, nc, true, 0.f, nullptr, nullptr);
-        } else {
-            float carry = 0.f;
-            for (int i0 = 0; i0 < nc; i0 += kWave) {
-                const int i = i0 + tid;
-                const float m = i < nc ? word_f32(fetch(&src[2 * i])) : 0.f;
-                carry = carry + wave_last(wave_incl_sum(m));
-            }
-            S = carry;
-        }
-        const float tau = us * S;
-        int cstar = 0;
-        float base = 0.f;
-        if (staged) {
-            scan_masses(s_m, nullptr, nc, true, tau, &cstar, &base);
-        } else {
-            // In place: the same scan over the chosen words.
-            float carry = 0.f, last_base = 0.f, found_base = 0.f;
-            int found = -1, last_pos = 0;
-            for (int i0 = 0; i0 < nc; i0 += kWave) {
-                const int i = i0 + tid;
-                const float m = i < nc ? word_f32(fetch(&src[2 * i])) : 0.f;
-                const float incl = carry + wave_incl_sum(m);
-                float excl = wave_excl_from_incl(incl);
-                if (tid == 0) excl = carry;
-                const uint64_t cross = __ballot(i < nc && incl > tau);
-                if (found < 0 && cross) {
-                    const int l = __ffsll(static_cast<unsigned long long>(cross)) - 1;
-                    found = i0 + l;
-                    found_base = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), l));
-                }
-                const uint64_t pos = __ballot(i < nc && m > 0.f);
-                if (pos) {
-                    const int l = 63 - __clzll(static_cast<long long>(pos));
-                    last_pos = i0 + l;
-                    last_base = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), l));
-                }
-                carry = wave_last(incl);
-            }
-            cstar = found >= 0 ? found : last_pos;
-            base = found >= 0 ? found_base : last_base;
-        }
-        if (tid == 0) {
-            s_S = S;
-            s_tau = tau;
-            s_cstar = cstar;
-            s_base = base;
-        }
-    }
-    __syncthreads();
     if (s_cstar != ch) return;
 
-    // The crossing chunk: the first entry (index order) whose running mass
-    // exceeds tau; if rounding leaves none, the last entry with weight.
+    // The crossing chunk.  The first thread whose running mass passes tau
+    // (else the last thread with mass) holds the drawn entry.
+    const bool resid = s_resid;
     const float tau = s_tau;
-    float run = s_base + (resid ? ex_r : ex_p);
-    int found = INT32_MAX, last_nz = -1;
+    const float start = s_base + (resid ? ex_r : ex_p), l = resid ? lr : lp;
+    int tf, tl;
+    wg_min_max(l > 0.f && start + l > tau ? tid : INT32_MAX, l > 0.f ? tid : -1, tf, tl);
+    const int ts = tf != INT32_MAX ? tf : max(tl, 0);
+    uint32_t *s_raw = reinterpret_cast<uint32_t *>(lds + kDrawRawAt);
+    float *s_start = lds + kDrawRawAt + 2 * kDrawRawWords;
+    if (tid == ts) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        float wp[VEC], wr[VEC];
-        weights(q, wp, wr);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            const float x = resid ? wr[i] : wp[i];
-            run += x;
-            if (x > 0.f) {
-                if (found == INT32_MAX && run > tau) found = s0 + q * VEC + i;
-                last_nz = s0 + q * VEC + i;
-            }
+        for (int q = 0; q < NQ; ++q) {
+            reinterpret_cast<uint4 *>(s_raw)[q] = rt[q];
+            if (Resid) reinterpret_cast<uint4 *>(s_raw + kDrawRawWords)[q] = rd[q];
         }
-        asm volatile("" : "+v"(run), "+v"(found), "+v"(last_nz));  // one slot at a time
+        *s_start = start;
     }
-    wg_min_max(found, last_nz, found, last_nz);
-    const int pick = found != INT32_MAX ? found : max(last_nz, 0);
-    const int32_t token = static_cast<int32_t>(c0 + pick);
+    __syncthreads();
+    if (tid >= kWave) return;
+    // Lane e takes entry e of that thread's segment: the first entry (index
+    // order) whose running mass exceeds tau; if rounding leaves none, the
+    // last entry with weight.
+    const int e = min(lane, kSeg - 1);
+    float x = weight_p(raw_entry<DT>(s_raw, e), c, w);
+    if (Resid && resid) x = weight_r(x, raw_entry<DT>(s_raw + kDrawRawWords, e), c, w);
+    x = lane < kSeg ? x : 0.f;
+    const float run = *s_start + wave_incl_sum(x);
+    const uint64_t f = __ballot(x > 0.f && run > tau), nz = __ballot(x > 0.f);
+    const int pick = f ? __ffsll(static_cast<unsigned long long>(f)) - 1
+                       : (nz ? 63 - __clzll(static_cast<long long>(nz)) : 0);
+    const int32_t token = static_cast<int32_t>(c0 + ts * kSeg + pick);
 
-    // Emit x_0..x_{j-1}, then the drawn token, then -1.
-    for (int k = tid; k <= K; k += kWG) {
+    // Emit x_0..x_{j-1}, then the drawn token, then -1 (lane k: position k).
+    for (int k = lane; k <= K; k += kWave) {
         int32_t o = -1;
-        if (k < j) o = my_tok;  // k == tid here: K + 1 <= 65 < kWG
+        if (k < j) o = my_tok;  // k < j <= K <= 64: k is this lane
         else if (k == j) o = token;
         a.out_tokens[static_cast<int64_t>(b) * (K + 1) + k] = o;
         if (a.out_diag) {
             float *dg = a.out_diag + 4 * (static_cast<int64_t>(b) * (K + 1) + k);
             if (k == K) dg[0] = dg[1] = dg[2] = 0.f;
-            dg[3] = k == j ? s_S : 0.f;
+            dg[3] = k == j ? S : 0.f;
         }
     }
-    if (tid == 0) a.out_accepted[b] = j;
+    if (lane == 0) a.out_accepted[b] = j;
+}
+
+template <class DT, bool VecOk>
+__device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, float *lds) {
+    const int K = a.K;
+    // Drafted tokens for the emission (lane k: token k) and the draw's
+    // uniform, loaded before the resolve.
+    const int32_t *tk = K > 0 ? a.tokens + static_cast<int64_t>(b) * K
+                              : reinterpret_cast<const int32_t *>(a.u_sample + b);
+    const int32_t my_tok = tk[min(static_cast<int>(threadIdx.x % kWave), max(K - 1, 0))];
+    const float us = a.u_sample[b];
+    DrawRow w;
+    bool ok;
+    const int j = resolve_local<DT>(a, b, w, ok, ch == 0, lds);
+    if (w.resid) draw_body<DT, VecOk, true>(a, b, ch, j, w, ok, us, my_tok, lds);
+    else draw_body<DT, VecOk, false>(a, b, ch, j, w, ok, us, my_tok, lds);
 }
 
 template <class DT, int U>
@@ -630,7 +503,7 @@ __global__ __launch_bounds__(kWG) void k_chain_stats(ChainArgs a) {
 template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
     const uint32_t nc = a.nchunk2, g = blockIdx.x, b = g / nc;
-    __shared__ float lds[kDrawLds];
+    __shared__ __align__(16) float lds[kDrawLds];
     draw_item<DT, VecOk>(a, static_cast<int>(b), static_cast<int>(g - b * nc), lds);
 }
 

@@ -339,23 +339,27 @@ __device__ __forceinline__ void wg_min_max(int mn, int mx, int &rmin, int &rmax)
     }
 }
 
-// Wavefront merge of (ref, z) on DPP moves in a fixed order; the result is
-// valid in lane 63 (read it with wave_last).
-__device__ __forceinline__ void mz_wave_merge(float &ref, float &z) {
+// Merge of (ref, z) on DPP moves in a fixed order.  The row form merges each
+// row of 16 lanes (result valid in the row's last lane); the wavefront form
+// continues across rows (result valid in lane 63, read it with wave_last).
 #define SV_MZ_STEP(CTRL, MASK)                                                   \
     {                                                                            \
         const float r2 = dpp::mov_f<CTRL, MASK>(-INFINITY, ref);                \
         const float z2 = dpp::mov_f<CTRL, MASK>(0.f, z);                        \
         mz_merge(ref, z, r2, z2);                                                \
     }
+__device__ __forceinline__ void mz_row_merge(float &ref, float &z) {
     SV_MZ_STEP(dpp::kRowShr1, 0xF)
     SV_MZ_STEP(dpp::kRowShr2, 0xF)
     SV_MZ_STEP(dpp::kRowShr4, 0xF)
     SV_MZ_STEP(dpp::kRowShr8, 0xF)
+}
+__device__ __forceinline__ void mz_wave_merge(float &ref, float &z) {
+    mz_row_merge(ref, z);
     SV_MZ_STEP(dpp::kRowBcast15, 0xA)
     SV_MZ_STEP(dpp::kRowBcast31, 0xC)
-#undef SV_MZ_STEP
 }
+#undef SV_MZ_STEP
 
 __device__ __forceinline__ void mz_reduce_wg(float &ref, float &z) {
     __shared__ float s_ref[kWaves], s_z[kWaves];

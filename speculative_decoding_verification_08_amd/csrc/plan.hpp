@@ -11,12 +11,12 @@ constexpr int kMaxK = 64;
 constexpr int kMaxTreeNodes = 256;
 constexpr int kChunk2Bytes = 16384;  // bytes of one row per chunk of the residual / bonus pass
 constexpr int kMaxDrawChunks = 64;  // draw chunks per row: V <= 64 x 16 KB of entries
-constexpr int kMergeLds = 512;   // row partials merged through LDS up to this many
-constexpr int kSumsLds = 512;    // chunk masses staged in LDS up to this many
-// LDS floats of a draw workgroup: its sequence's row statistics and staged
-// partials during the resolve, then the staged chunk masses.
-constexpr int kDrawLds = 2 * (2 * kMaxK + 1) + 2 * kMergeLds;
-static_assert(kSumsLds <= kDrawLds, "chunk masses fit the draw workgroup's LDS");
+// LDS words of a draw workgroup: its sequence's row statistics (ref, z), then
+// one thread's raw entries of the crossing chunk (16 words per row, target
+// and draft) and that thread's running mass.
+constexpr int kDrawRawWords = 16;
+constexpr int kDrawRawAt = (2 * (2 * kMaxK + 1) + 3) / 4 * 4;  // 16-byte aligned
+constexpr int kDrawLds = kDrawRawAt + 2 * kDrawRawWords + 4;
 
 // How a launch cuts the rows it streams into vocabulary chunks, and where its
 // scratch lives inside the caller's workspace.
