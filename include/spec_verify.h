@@ -112,11 +112,13 @@ spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_
  *                              q = 0 < p, 0 when both are 0).
  *   workspace                  at least spec_verify_workspace_bytes(CHAIN, ...).
  *
- * Two kernel launches in stream order: spec_verify_chain_stats, then
- * spec_verify_chain_sample, on the same workspace.  The second kernel's
- * workgroups of one sequence hand each other words in the workspace and wait
- * for each other (bounded, about 2 s); if a wait ever ran out, the sequence
- * gets out_accepted[b] = -1 and out_tokens[b] all -1.
+ * One kernel launch that computes the same as spec_verify_chain_stats
+ * followed by spec_verify_chain_sample, bit for bit.  Its workgroups hand
+ * each other words in the workspace and wait for each other (bounded, about
+ * 2 s): a sequence's draw waits for its statistics, and the draw workgroups
+ * of one sequence for each other.  If a wait ever ran out, the sequence gets
+ * out_accepted[b] = -1 and out_tokens[b] all -1.  Sizes whose one-launch grid
+ * would exceed 2^31 - 1 workgroups run as the two phases instead.
  */
 spec_status spec_verify_chain(const void *target_logits, const void *draft_logits, spec_dtype dtype,
                               const int32_t *draft_tokens, const float *u_accept,
@@ -143,7 +145,9 @@ spec_status spec_verify_chain_stats(const void *target_logits, const void *draft
  * tokens, from the statistics the first phase left in the same workspace.
  * Must follow spec_verify_chain_stats with identical logits, tokens, sizes and
  * temperature on the same stream; sequences whose statistics were not written
- * by that phase get out_accepted = -1.
+ * by that phase get out_accepted = -1.  The draw workgroups of one sequence
+ * wait for each other (bounded, about 2 s); if a wait ran out, the sequence
+ * gets out_accepted[b] = -1 and out_tokens[b] all -1.
  */
 spec_status spec_verify_chain_sample(const void *target_logits, const void *draft_logits,
                                      spec_dtype dtype, const int32_t *draft_tokens,

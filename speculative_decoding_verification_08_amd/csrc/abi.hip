@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "plan.hpp"
@@ -110,6 +111,21 @@ spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype,
     return SPEC_OK;
 }
 
+// Sequences between a sequence's statistics and its draw in the one-launch
+// chain verify.  When the whole step fits in three quarters of the
+// last-level cache, every draw comes after all statistics (the second read
+// of row j hits the cache anyway, and the streaming runs undisturbed);
+// otherwise the draws trail by what keeps about 96 MB between the two reads
+// of a row, and by at least one resident window of workgroups.
+int32_t chain_lag(int32_t B, int32_t K, int32_t V, spec_dtype dtype, int64_t per_seq) {
+    const int64_t seq_bytes =
+        static_cast<int64_t>(2 * K + 1) * V * (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
+    if (static_cast<int64_t>(B) * seq_bytes <= kLlcBytes / 4 * 3) return B;
+    const int64_t window = (kResidentWGs + per_seq - 1) / per_seq + 1;
+    const int64_t reach = kLlcBytes / 8 * 3 / seq_bytes;
+    return static_cast<int32_t>(std::min<int64_t>(B, std::max(window, reach)));
+}
+
 spec_status chain_sample_args(const int32_t *tokens, const float *ua, const float *us, int32_t B,
                               int32_t K, int32_t *out_tokens, int32_t *out_accepted,
                               float *out_diag, ChainArgs &a) {
@@ -202,6 +218,11 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
                            out_diag, a);
     if (st != SPEC_OK) return st;
     a.tag = next_call_tag();
+    const int64_t per_seq = static_cast<int64_t>(2 * K + 1) * plan.nchunk + plan.nchunk2;
+    if (static_cast<int64_t>(B) * per_seq <= 0x7fffffffLL) {
+        a.lag = chain_lag(B, K, V, dtype, per_seq);
+        return launch_status(launch_chain_fused(a, dtype, stream));
+    }
     st = launch_status(launch_chain_stats(a, dtype, stream));
     if (st != SPEC_OK) return st;
     return launch_status(launch_chain_draw(a, dtype, stream));

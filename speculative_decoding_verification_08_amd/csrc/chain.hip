@@ -1,31 +1,35 @@
-// Chain verify at T > 0 on gfx950: two kernels in stream order.
+// Chain verify at T > 0 on gfx950.
 //
-// k_chain_stats streams every logit of the step once.  One workgroup takes
+// Statistics items stream every logit of the step once.  One workgroup takes
 // one 16 KB vocabulary chunk of one row (target rows 0..K and draft rows
 // 0..K-1 of a sequence), folds it into softmax statistics (ref, z) and
 // publishes them (and, if its chunk holds the row's drafted token, that
-// logit).  This is the HBM-bound pass that carries the bytes; no workgroup of
-// it waits for another.
+// logit).  This is the HBM-bound work that carries the bytes; no statistics
+// workgroup waits for another.
 //
-// k_chain_draw runs one workgroup per (sequence b, 16 KB chunk of a row).
-// Each merges b's row statistics, evaluates the accept test of every drafted
-// token (u < p(x)/q(x), French lesson "Décodage spéculatif et Eagle", section
-// "La règle de l'exactitude"; forum post "Speculative Decoding: от идеи до
-// SOTA", §3) and finds the first rejection j.  It holds its chunk of row j in
+// Draw items run one workgroup per (sequence b, 16 KB chunk of a row).  Each
+// merges b's row statistics, evaluates the accept test of every drafted token
+// (u < p(x)/q(x), French lesson "Décodage spéculatif et Eagle", section "La
+// règle de l'exactitude"; forum post "Speculative Decoding: от идеи до SOTA",
+// §3) and finds the first rejection j.  It holds its chunk of row j in
 // registers and publishes the chunk's draw masses -- max(0, p_j - q_j) after a
 // rejection (the residual of the same passages) and p_j, the bonus draw's
 // weights when every draft was accepted.  Once every chunk's masses are
 // visible, all of b's workgroups find the chunk whose running mass first
-// exceeds u * S; that chunk's workgroup picks the token from its registers and
-// writes the sequence's outputs.
+// exceeds u * S; that chunk's workgroup picks the token and writes the
+// sequence's outputs.
+//
+// k_chain_fused runs both kinds of item in one grid (the one-call entry
+// point); k_chain_stats and k_chain_draw run them as two kernels in stream
+// order (the two-phase entry points).  Both give the same bits.
 //
 // Hand-over words are 64 bits: the call's tag above a 32-bit value, written
 // with device-scope atomic stores and read with device-scope atomic loads; a
 // reader checks the tag, so nothing left by an earlier call is taken for
-// fresh, and polls (bounded in time) until the word is visible; the
-// workspace needs no initialisation.  A draw workgroup waits for the other
-// draw workgroups of its sequence, which the hardware dispatches together (a
-// sequence has at most 64 of them, far fewer than the chip holds).
+// fresh, and waits (bounded in time) until the word is visible; the
+// workspace needs no initialisation.  A workgroup only waits for workgroups
+// of lower index (dispatched before it) or for the draw workgroups of its own
+// sequence (a sequence has at most 64, far fewer than the chip holds).
 #include "device.hpp"
 #include "plan.hpp"
 
@@ -55,6 +59,14 @@ __device__ __forceinline__ bool current(uint64_t w, uint32_t tag) {
 }
 __device__ __forceinline__ float word_f32(uint64_t w) {
     return __uint_as_float(static_cast<uint32_t>(w));
+}
+// Bounded wait (from t0) until one word carries the call's tag.  One lane
+// polls one word with a pause between reads, so waiting workgroups add little
+// traffic beside the streaming ones; the caller then reads everything it
+// needs once.
+__device__ __forceinline__ void wait_word(const uint64_t *p, uint32_t tag, uint64_t t0) {
+    while (!current(fetch(p), tag) && wall_clock64() - t0 <= kWaitTicks)
+        __builtin_amdgcn_s_sleep(4);
 }
 
 // ------------------------------------------------------------ stats item
@@ -157,61 +169,92 @@ struct NegInf<F32> {
     static constexpr uint32_t kBits = 0xff800000u;
 };
 
-// Resolve of sequence b inside a draw workgroup, from the statistics the
-// first kernel left (ordered before this kernel by the stream).  Each group
-// of 16 lanes merges one row's chunk statistics (lane i folds chunks i,
-// i + 16, ... in order, then a fixed DPP tree), every wavefront evaluates the
-// accept test of every drafted token (u < P/Q, strict; Q = 0 accepts iff
-// P > 0) and takes j, the first rejected position (K if none), by ballot, so
-// no second barrier is needed.  Row j's statistics land in `w`.  `ok` is false
-// if a word was not written for this call.  With `diag` the workgroup also
-// writes p_k(x_k), q_k(x_k) and their ratio to out_diag.
-template <class DT>
+// Resolve of sequence b inside a draw workgroup.  Each group of 16 lanes
+// merges one row's chunk statistics (lane i folds chunks i, i + 16, ... in
+// order, then a fixed DPP tree), every wavefront evaluates the accept test of
+// every drafted token (u < P/Q, strict; Q = 0 accepts iff P > 0) and takes j,
+// the first rejected position (K if none), by ballot, so no second barrier is
+// needed.  Row j's statistics land in `w`.  Without Live the statistics come
+// from a kernel ordered before this one by the stream and are read once;
+// with Live the statistics workgroups may still be running, so the words are
+// read with device-scope loads and the merge is repeated (bounded in time)
+// until every word carries the call's tag.  `ok` is false if a word was not
+// written for this call in time.  With `diag` the workgroup also writes
+// p_k(x_k), q_k(x_k) and their ratio to out_diag.
+template <class DT, bool Live>
 __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow &w, bool &ok,
                                              bool diag, float *lds) {
     constexpr int kGroup = 16, kGroups = kWG / kGroup, kFold = 4;
     float *s_ref = lds, *s_z = s_ref + (2 * kMaxK + 1);
-    __shared__ int s_stale[kWaves];
+    __shared__ int s_stale[2][kWaves + 1];
     const int K = a.K, V = a.V, R = 2 * K + 1, nch = a.nchunk;
     const int tid = threadIdx.x, lane = tid % kWave, grp = tid / kGroup, gl = tid % kGroup;
-    const uint4 *part = reinterpret_cast<const uint4 *>(a.partial) + static_cast<int64_t>(b) * R * nch;
+    const uint64_t *part = a.partial + 2 * static_cast<int64_t>(b) * R * nch;
     const uint64_t *gat = a.gathered + static_cast<int64_t>(b) * R;
-    // Uniforms and drafted-token logits of lane k's position, loaded by every
-    // wavefront (from clamped indices) together with the first partials.
+    // Uniforms of lane k's position, loaded by every wavefront.
     const float *ua = K > 0 ? a.u_accept + static_cast<int64_t>(b) * K : a.u_sample + b;
     const float u = ua[min(lane, max(K - 1, 0))];
-    const uint64_t wt = gat[min(lane, R - 1)], wd = gat[min(K + 1 + lane, R - 1)];
-    bool fresh = true;
-    for (int r0 = 0; r0 < R; r0 += kGroups) {
-        const int r = r0 + grp, rr = min(r, R - 1);
-        float ref = -INFINITY, z = 0.f;
-        for (int i0 = 0; i0 < nch; i0 += kGroup * kFold) {
-            uint4 pw[kFold];
+    const uint64_t t0 = Live ? wall_clock64() : 0;
+    uint64_t wt, wd;
+    for (int it = 0;; ++it) {
+        // First wait for the sequence's statistics workgroup dispatched last
+        // (last chunk of the last draft row); the merge checks every word
+        // and repeats if one is still missing.
+        if (Live && lane == 0) wait_word(part + 2 * (R * nch - 1), a.tag, t0);
+        // Drafted-token logits of lane k's position (clamped indices), loaded
+        // with the first partials before any is used.
+        if (Live) {
+            wt = fetch(&gat[min(lane, R - 1)]);
+            wd = fetch(&gat[min(K + 1 + lane, R - 1)]);
+        } else {
+            wt = gat[min(lane, R - 1)];
+            wd = gat[min(K + 1 + lane, R - 1)];
+        }
+        bool fresh = true;
+        for (int r0 = 0; r0 < R; r0 += kGroups) {
+            const int r = r0 + grp, rr = min(r, R - 1);
+            float ref = -INFINITY, z = 0.f;
+            for (int i0 = 0; i0 < nch; i0 += kGroup * kFold) {
+                uint64_t pr[kFold], pz[kFold];
 #pragma unroll
-            for (int f = 0; f < kFold; ++f)
-                pw[f] = part[rr * nch + min(i0 + gl + kGroup * f, nch - 1)];
+                for (int f = 0; f < kFold; ++f) {
+                    const uint64_t *pw = part + 2 * (rr * nch + min(i0 + gl + kGroup * f, nch - 1));
+                    if (Live) {
+                        pr[f] = fetch(pw);
+                        pz[f] = fetch(pw + 1);
+                    } else {
+                        const uint4 v = *reinterpret_cast<const uint4 *>(pw);
+                        pr[f] = (static_cast<uint64_t>(v.y) << 32) | v.x;
+                        pz[f] = (static_cast<uint64_t>(v.w) << 32) | v.z;
+                    }
+                }
 #pragma unroll
-            for (int f = 0; f < kFold; ++f) {
-                const bool in = r < R && i0 + gl + kGroup * f < nch;
-                fresh = fresh && (!in || (pw[f].y == a.tag && pw[f].w == a.tag));
-                mz_merge(ref, z, in ? __uint_as_float(pw[f].x) : -INFINITY,
-                         in ? __uint_as_float(pw[f].z) : 0.f);
+                for (int f = 0; f < kFold; ++f) {
+                    const bool in = r < R && i0 + gl + kGroup * f < nch;
+                    fresh = fresh && (!in || (current(pr[f], a.tag) && current(pz[f], a.tag)));
+                    mz_merge(ref, z, in ? word_f32(pr[f]) : -INFINITY, in ? word_f32(pz[f]) : 0.f);
+                }
+            }
+            mz_row_merge(ref, z);
+            if (r < R && gl == kGroup - 1) {
+                s_ref[r] = ref;
+                s_z[r] = z;
             }
         }
-        mz_row_merge(ref, z);
-        if (r < R && gl == kGroup - 1) {
-            s_ref[r] = ref;
-            s_z[r] = z;
-        }
-    }
-    const bool tok_ok = lane >= K || (current(wt, a.tag) && current(wd, a.tag));
-    const uint64_t stale = __ballot(!fresh || !tok_ok);
-    if (lane == 0) s_stale[tid / kWave] = stale != 0;
-    __syncthreads();
-    int any_stale = 0;
+        const bool tok_ok = lane >= K || (current(wt, a.tag) && current(wd, a.tag));
+        const uint64_t stale = __ballot(!fresh || !tok_ok);
+        // Double-buffered by iteration: a wavefront may start the next
+        // iteration while another still reads this one's flags.
+        if (lane == 0) s_stale[it & 1][tid / kWave] = stale != 0;
+        if (tid == 0) s_stale[it & 1][kWaves] = !Live || wall_clock64() - t0 > kWaitTicks;
+        __syncthreads();
+        int any_stale = 0;
 #pragma unroll
-    for (int k = 0; k < kWaves; ++k) any_stale |= s_stale[k];
-    ok = !any_stale;
+        for (int k = 0; k < kWaves; ++k) any_stale |= s_stale[it & 1][k];
+        ok = !any_stale;
+        if (ok || s_stale[it & 1][kWaves]) break;
+        __builtin_amdgcn_s_sleep(16);
+    }
     bool reject = false;
     if (lane < K) {
         const float P = exp2_hw(fmaf(word_f32(wt), a.c, -s_ref[lane])) / s_z[lane];
@@ -387,12 +430,15 @@ __device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int
         uint64_t vr, vp;
         bool fresh;
         const uint64_t t0 = wall_clock64();
+        // The last chunk's workgroup is dispatched last: wait for its word,
+        // then read all (repeating while any is missing).
+        if (lane == 0) wait_word(&sums[2 * (nc - 1)], a.tag, t0);
         for (;;) {
             vr = fetch(&sums[2 * i]);
             vp = fetch(&sums[2 * i + 1]);
             fresh = __all(current(vr, a.tag) && current(vp, a.tag));
             if (fresh || wall_clock64() - t0 > kWaitTicks) break;
-            __builtin_amdgcn_s_sleep(2);
+            __builtin_amdgcn_s_sleep(8);
         }
         const bool in = lane < nc;
         const float m_r = in ? word_f32(vr) : 0.f, m_p = in ? word_f32(vp) : 0.f;
@@ -475,7 +521,7 @@ __device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int
     if (lane == 0) a.out_accepted[b] = j;
 }
 
-template <class DT, bool VecOk>
+template <class DT, bool VecOk, bool Live>
 __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, float *lds) {
     const int K = a.K;
     // Drafted tokens for the emission (lane k: token k) and the draw's
@@ -486,7 +532,7 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
     const float us = a.u_sample[b];
     DrawRow w;
     bool ok;
-    const int j = resolve_local<DT>(a, b, w, ok, ch == 0, lds);
+    const int j = resolve_local<DT, Live>(a, b, w, ok, ch == 0, lds);
     if (w.resid) draw_body<DT, VecOk, true>(a, b, ch, j, w, ok, us, my_tok, lds);
     else draw_body<DT, VecOk, false>(a, b, ch, j, w, ok, us, my_tok, lds);
 }
@@ -504,7 +550,52 @@ template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
     const uint32_t nc = a.nchunk2, g = blockIdx.x, b = g / nc;
     __shared__ __align__(16) float lds[kDrawLds];
-    draw_item<DT, VecOk>(a, static_cast<int>(b), static_cast<int>(g - b * nc), lds);
+    draw_item<DT, VecOk, false>(a, static_cast<int>(b), static_cast<int>(g - b * nc), lds);
+}
+
+// The whole chain verify in one launch.  Per sequence, its S = (2K+1) *
+// nchunk statistics workgroups come first and its D = nchunk2 draw workgroups
+// `lag` sequences later: blocks of the statistics of b + lag with the draws
+// of b spread evenly among them, after
+// a prologue of the first `lag` sequences' statistics and before an epilogue
+// of the last `lag` sequences' draws.  The hardware dispatches workgroups in
+// index order, so a draw workgroup waits only for statistics workgroups of
+// lower index (dispatched before it, and they never wait) and for the draw
+// workgroups of its own sequence (dispatched together); with the lag at least
+// the chip's resident window, the statistics it needs have usually finished
+// before it starts, and the draws overlap the streaming of later sequences.
+template <class DT, bool VecOk>
+__global__ __launch_bounds__(kWG) void k_chain_fused(ChainArgs a) {
+    __shared__ __align__(16) float lds[kDrawLds];
+    const uint32_t S = (2 * a.K + 1) * a.nchunk, D = a.nchunk2, L = a.lag, B = a.B;
+    const uint32_t g = blockIdx.x, pro = L * S, steady = pro + (B - L) * (S + D);
+    uint32_t b, s;
+    bool draw;
+    if (g < pro) {
+        b = g / S;
+        s = g - b * S;
+        draw = false;
+    } else if (g < steady) {
+        // Block k: the D draws of sequence k in one run at offset o among the
+        // statistics of sequence L + k; o steps by 8 per block, so the run's
+        // place in each XCD's share of the order rotates.
+        const uint32_t h = g - pro, k = h / (S + D), p = h - k * (S + D);
+        const uint32_t o = (8 * k) % (S + 1);
+        draw = p >= o && p < o + D;
+        b = draw ? k : L + k;
+        s = draw ? p - o : (p < o ? p : p - D);
+    } else {
+        const uint32_t h = g - steady, k = h / D;
+        b = B - L + k;
+        s = h - k * D;
+        draw = true;
+    }
+    if (draw) {
+        draw_item<DT, VecOk, true>(a, static_cast<int>(b), static_cast<int>(s), lds);
+    } else {
+        const uint32_t r = s / a.nchunk;
+        stats_item<DT, 4>(a, b, static_cast<int>(r), static_cast<int>(s - r * a.nchunk));
+    }
 }
 
 }  // namespace
@@ -516,6 +607,19 @@ hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s) {
         k_chain_stats<Bf16, 4><<<g, blk, 0, s>>>(a);
     else
         k_chain_stats<F32, 4><<<g, blk, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s) {
+    const int64_t per_seq = static_cast<int64_t>(2 * a.K + 1) * a.nchunk + a.nchunk2;
+    const dim3 g(static_cast<uint32_t>(static_cast<int64_t>(a.B) * per_seq)), blk(kWG);
+    if (dtype == 1) {
+        if (a.V % Bf16::kVec == 0) k_chain_fused<Bf16, true><<<g, blk, 0, s>>>(a);
+        else k_chain_fused<Bf16, false><<<g, blk, 0, s>>>(a);
+    } else {
+        if (a.V % F32::kVec == 0) k_chain_fused<F32, true><<<g, blk, 0, s>>>(a);
+        else k_chain_fused<F32, false><<<g, blk, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -10,6 +10,13 @@ namespace sv {
 constexpr int kMaxK = 64;
 constexpr int kMaxTreeNodes = 256;
 constexpr int kChunk2Bytes = 16384;  // bytes of one row per chunk of the residual / bonus pass
+// Workgroups of 256 threads the chip holds at once (256 CUs, 8 each) and the
+// last-level (Infinity) cache in front of HBM.  The one-launch chain verify
+// places a sequence's draw at least one resident window after its
+// statistics, and close enough that the draw's second read of row j still
+// finds it in that cache.
+constexpr int kResidentWGs = 2048;
+constexpr int64_t kLlcBytes = 256ll << 20;
 constexpr int kMaxDrawChunks = 64;  // draw chunks per row: V <= 64 x 16 KB of entries
 // LDS words of a draw workgroup: its sequence's row statistics (ref, z), then
 // one thread's raw entries of the crossing chunk (16 words per row, target
@@ -47,6 +54,7 @@ struct ChainArgs {
     float c;                 // log2(e) / T
     uint32_t tag;            // this call's tag (upper half of every handed-over word)
     int32_t chunk, nchunk, nchunk2;  // chunk2 = kChunk2Bytes / element size
+    int32_t lag;             // one-launch form: sequences between a sequence's statistics and its draw
     uint64_t *partial;       // [B][2K+1][nchunk][2] tagged (ref, z); rows 0..K target, K+1.. draft
     uint64_t *gathered;      // [B][2K+1] tagged logit of each row at its drafted token (row K unused)
     uint64_t *sums;          // [B][nchunk2][2] tagged residual and target mass per chunk
@@ -91,6 +99,7 @@ struct TreeArgs {
 // Host launchers (defined next to their kernels).
 hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s);
 hipError_t launch_chain_draw(const ChainArgs &a, int dtype, hipStream_t s);
+hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s);
 hipError_t launch_row_argmax(const ArgmaxArgs &a, int dtype, hipStream_t s);
 hipError_t launch_greedy_resolve(const GreedyArgs &a, hipStream_t s);
 hipError_t launch_tree_resolve(const TreeArgs &a, hipStream_t s);
