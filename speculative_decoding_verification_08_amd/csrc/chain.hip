@@ -181,43 +181,42 @@ struct NegInf<F32> {
 // until every word carries the call's tag.  `ok` is false if a word was not
 // written for this call in time.  With `diag` the workgroup also writes
 // p_k(x_k), q_k(x_k) and their ratio to out_diag.
-template <class DT, bool Live>
+template <class DT, bool Live, int Fold>
 __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow &w, bool &ok,
                                              bool diag, float *lds) {
-    constexpr int kGroup = 16, kGroups = kWG / kGroup, kFold = 4;
+    constexpr int kGroup = 16, kGroups = kWG / kGroup;
     float *s_ref = lds, *s_z = s_ref + (2 * kMaxK + 1);
     __shared__ int s_stale[2][kWaves + 1];
     const int K = a.K, V = a.V, R = 2 * K + 1, nch = a.nchunk;
     const int tid = threadIdx.x, lane = tid % kWave, grp = tid / kGroup, gl = tid % kGroup;
     const uint64_t *part = a.partial + 2 * static_cast<int64_t>(b) * R * nch;
     const uint64_t *gat = a.gathered + static_cast<int64_t>(b) * R;
+    const uint64_t *gt = &gat[min(lane, R - 1)], *gd = &gat[min(K + 1 + lane, R - 1)];
     // Uniforms of lane k's position, loaded by every wavefront.
     const float *ua = K > 0 ? a.u_accept + static_cast<int64_t>(b) * K : a.u_sample + b;
     const float u = ua[min(lane, max(K - 1, 0))];
     const uint64_t t0 = Live ? wall_clock64() : 0;
     uint64_t wt, wd;
     for (int it = 0;; ++it) {
-        // First wait for the sequence's statistics workgroup dispatched last
-        // (last chunk of the last draft row); the merge checks every word
-        // and repeats if one is still missing.
-        if (Live && lane == 0) wait_word(part + 2 * (R * nch - 1), a.tag, t0);
         // Drafted-token logits of lane k's position (clamped indices), loaded
-        // with the first partials before any is used.
+        // with the partials before any is used.
         if (Live) {
-            wt = fetch(&gat[min(lane, R - 1)]);
-            wd = fetch(&gat[min(K + 1 + lane, R - 1)]);
+            wt = fetch(gt);
+            wd = fetch(gd);
         } else {
-            wt = gat[min(lane, R - 1)];
-            wd = gat[min(K + 1 + lane, R - 1)];
+            wt = *gt;
+            wd = *gd;
         }
-        bool fresh = true;
+        // A word this lane found missing (the first), for the wait below.
+        const uint64_t *miss = nullptr;
+        if (lane < K) miss = !current(wt, a.tag) ? gt : (!current(wd, a.tag) ? gd : nullptr);
         for (int r0 = 0; r0 < R; r0 += kGroups) {
             const int r = r0 + grp, rr = min(r, R - 1);
             float ref = -INFINITY, z = 0.f;
-            for (int i0 = 0; i0 < nch; i0 += kGroup * kFold) {
-                uint64_t pr[kFold], pz[kFold];
+            for (int i0 = 0; i0 < nch; i0 += kGroup * Fold) {
+                uint64_t pr[Fold], pz[Fold];
 #pragma unroll
-                for (int f = 0; f < kFold; ++f) {
+                for (int f = 0; f < Fold; ++f) {
                     const uint64_t *pw = part + 2 * (rr * nch + min(i0 + gl + kGroup * f, nch - 1));
                     if (Live) {
                         pr[f] = fetch(pw);
@@ -229,9 +228,11 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
                     }
                 }
 #pragma unroll
-                for (int f = 0; f < kFold; ++f) {
-                    const bool in = r < R && i0 + gl + kGroup * f < nch;
-                    fresh = fresh && (!in || (current(pr[f], a.tag) && current(pz[f], a.tag)));
+                for (int f = 0; f < Fold; ++f) {
+                    const int i = i0 + gl + kGroup * f;
+                    const bool in = r < R && i < nch;
+                    const bool cr = current(pr[f], a.tag), cz = current(pz[f], a.tag);
+                    if (in && !(cr && cz) && !miss) miss = part + 2 * (rr * nch + i) + (cr ? 1 : 0);
                     mz_merge(ref, z, in ? word_f32(pr[f]) : -INFINITY, in ? word_f32(pz[f]) : 0.f);
                 }
             }
@@ -241,8 +242,7 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
                 s_z[r] = z;
             }
         }
-        const bool tok_ok = lane >= K || (current(wt, a.tag) && current(wd, a.tag));
-        const uint64_t stale = __ballot(!fresh || !tok_ok);
+        const uint64_t stale = __ballot(miss != nullptr);
         // Double-buffered by iteration: a wavefront may start the next
         // iteration while another still reads this one's flags.
         if (lane == 0) s_stale[it & 1][tid / kWave] = stale != 0;
@@ -253,7 +253,11 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
         for (int k = 0; k < kWaves; ++k) any_stale |= s_stale[it & 1][k];
         ok = !any_stale;
         if (ok || s_stale[it & 1][kWaves]) break;
-        __builtin_amdgcn_s_sleep(16);
+        // Statistics still being written (one launch): one lane of each
+        // wavefront that missed a word waits for that word, then all read
+        // again.
+        if (stale && lane == __ffsll(static_cast<unsigned long long>(stale)) - 1)
+            wait_word(miss, a.tag, t0);
     }
     bool reject = false;
     if (lane < K) {
@@ -532,7 +536,10 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
     const float us = a.u_sample[b];
     DrawRow w;
     bool ok;
-    const int j = resolve_local<DT, Live>(a, b, w, ok, ch == 0, lds);
+    // One chunk per lane of a 16-lane group when a row has at most 16, else
+    // four per load batch.
+    const int j = a.nchunk <= 16 ? resolve_local<DT, Live, 1>(a, b, w, ok, ch == 0, lds)
+                                 : resolve_local<DT, Live, 4>(a, b, w, ok, ch == 0, lds);
     if (w.resid) draw_body<DT, VecOk, true>(a, b, ch, j, w, ok, us, my_tok, lds);
     else draw_body<DT, VecOk, false>(a, b, ch, j, w, ok, us, my_tok, lds);
 }
