@@ -196,7 +196,7 @@ def main():
             tok, acc = sv.spec_verify_greedy(sets[0]["target"], sets[0]["tokens"])
             torch.cuda.synchronize()
             return tok.cpu().numpy(), acc.cpu().numpy()
-        dominant_name = "k_row_argmax + k_greedy_resolve (whole step)"
+        dominant_name = "k_greedy (whole step)"
         io_bytes = 4 * B * K + 4 * B * (K + 2)
         verified = B * K
     else:
@@ -220,7 +220,7 @@ def main():
                                                           sets[0]["node_tokens"], par)
             torch.cuda.synchronize()
             return tok.cpu().numpy(), path.cpu().numpy(), depth.cpu().numpy()
-        dominant_name = "k_row_argmax + k_tree_resolve (whole step)"
+        dominant_name = "k_tree (whole step)"
         io_bytes = 4 * B * N + 4 * B * (2 * D + 3)
         verified = B * (N - 1)
 

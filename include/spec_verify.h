@@ -165,6 +165,10 @@ spec_status spec_verify_chain_sample(const void *target_logits, const void *draf
  *   target_logits [B][K+1][V], draft_tokens [B][K] int32,
  *   out_tokens [B][K+1] (-1 padded), out_accepted [B].
  *   B >= 0, 0 <= K <= SPEC_VERIFY_MAX_K, 1 <= V <= SPEC_VERIFY_MAX_V.
+ *
+ * One kernel launch.  Each sequence's resolve waits (bounded, about 2 s) for
+ * the argmax workgroups of its rows; if a wait ever ran out, the sequence
+ * gets out_accepted[b] = -1 and out_tokens[b] all -1.
  */
 spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
                                const int32_t *draft_tokens, int32_t B, int32_t K, int32_t V,
@@ -191,6 +195,10 @@ spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
  *                          then the argmax of the last node's row, then -1.
  *   out_path   nullable [B][D+1]  node ids root..last, then -1.
  *   out_depth  [B]         accepted depth d (out_tokens holds d+1 tokens).
+ *
+ * One kernel launch.  Each tree's resolve waits (bounded, about 2 s) for the
+ * argmax workgroups of its node rows; if a wait ever ran out, the tree gets
+ * out_depth[b] = -1 and out_tokens[b], out_path[b] all -1.
  */
 spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
                                     const int32_t *node_tokens, const int32_t *parents,

@@ -18,14 +18,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Elements per chunk of the streaming pass: 16 KB of logits per workgroup,
-// halved (down to 2048 elements) while the grid has fewer than 4096
-// workgroups (16 per CU on 256 CUs).
-int first_pass_chunk(int64_t rows, int V, spec_dtype dtype) {
-    int ch = dtype == SPEC_DTYPE_BF16 ? 8192 : 4096;
-    while (ch > 2048 && rows * ((V + ch - 1) / ch) < 4096) ch >>= 1;
-    return ch;
-}
+// Elements per chunk of the streaming pass: 16 KB of logits per workgroup.
+// Smaller chunks for small grids measured slower on MI355X (each workgroup's
+// reduce and hand-over is a fixed cost), so the size does not depend on the
+// grid.
+int first_pass_chunk(spec_dtype dtype) { return dtype == SPEC_DTYPE_BF16 ? 8192 : 4096; }
 
 bool valid_dtype(spec_dtype d) { return d == SPEC_DTYPE_F32 || d == SPEC_DTYPE_BF16; }
 
@@ -42,7 +39,7 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
     else if (mode == SPEC_MODE_GREEDY) rows = static_cast<int64_t>(B) * (KN + 1);
     else rows = static_cast<int64_t>(B) * KN;
     p.rows = rows;
-    p.chunk = first_pass_chunk(rows, V, dtype);
+    p.chunk = first_pass_chunk(dtype);
     p.nchunk = (V + p.chunk - 1) / p.chunk;
     if (rows * p.nchunk > 0x7fffffffLL) return false;  // one-dimensional grid
     size_t off = 0;
@@ -60,7 +57,9 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
         p.off_sums = off;  // two tagged masses per chunk: residual, target
         off += align_up(static_cast<size_t>(B) * p.nchunk2 * 16);
     } else {
-        off += align_up(static_cast<size_t>(rows) * p.nchunk * 8);
+        // One launch: argmax workgroups, then one resolve workgroup per sequence.
+        if (rows * p.nchunk + B > 0x7fffffffLL) return false;
+        off += align_up(static_cast<size_t>(rows) * p.nchunk * 16);  // two tagged words
     }
     p.bytes = off > 0 ? off : kAlign;
     return true;
@@ -242,24 +241,20 @@ spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
         return SPEC_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 16))
         return SPEC_ERR_WORKSPACE;
-    ArgmaxArgs am;
-    am.logits = target_logits;
-    am.rows = plan.rows;
-    am.V = V;
-    am.chunk = plan.chunk;
-    am.nchunk = plan.nchunk;
-    am.partial = at<int2>(workspace, plan.off_partial);
-    spec_status st = launch_status(launch_row_argmax(am, dtype, stream));
-    if (st != SPEC_OK) return st;
     GreedyArgs g;
-    g.partial = am.partial;
+    g.am.logits = target_logits;
+    g.am.rows = plan.rows;
+    g.am.V = V;
+    g.am.chunk = plan.chunk;
+    g.am.nchunk = plan.nchunk;
+    g.am.tag = next_call_tag();
+    g.am.partial = at<uint64_t>(workspace, plan.off_partial);
     g.tokens = draft_tokens;
     g.B = B;
     g.K = K;
-    g.nchunk = plan.nchunk;
     g.out_tokens = out_tokens;
     g.out_accepted = out_accepted;
-    return launch_status(launch_greedy_resolve(g, stream));
+    return launch_status(launch_greedy(g, dtype, stream));
 }
 
 spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
@@ -291,23 +286,19 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
         return SPEC_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 16))
         return SPEC_ERR_WORKSPACE;
-    ArgmaxArgs am;
-    am.logits = node_logits;
-    am.rows = plan.rows;
-    am.V = V;
-    am.chunk = plan.chunk;
-    am.nchunk = plan.nchunk;
-    am.partial = at<int2>(workspace, plan.off_partial);
-    spec_status st = launch_status(launch_row_argmax(am, dtype, stream));
-    if (st != SPEC_OK) return st;
-    t.partial = am.partial;
+    t.am.logits = node_logits;
+    t.am.rows = plan.rows;
+    t.am.V = V;
+    t.am.chunk = plan.chunk;
+    t.am.nchunk = plan.nchunk;
+    t.am.tag = next_call_tag();
+    t.am.partial = at<uint64_t>(workspace, plan.off_partial);
     t.tokens = node_tokens;
     t.B = B;
-    t.nchunk = plan.nchunk;
     t.out_tokens = out_tokens;
     t.out_path = out_path;
     t.out_depth = out_depth;
-    return launch_status(launch_tree_resolve(t, stream));
+    return launch_status(launch_tree(t, dtype, stream));
 }
 
 }  // extern "C"

@@ -31,43 +31,11 @@
 // of lower index (dispatched before it) or for the draw workgroups of its own
 // sequence (a sequence has at most 64, far fewer than the chip holds).
 #include "device.hpp"
+#include "handover.hpp"
 #include "plan.hpp"
 
 namespace sv {
 namespace {
-
-// ------------------------------------------------------------ hand-over
-
-constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s of the 100 MHz wall clock
-
-__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t bits) {
-    return (static_cast<uint64_t>(tag) << 32) | bits;
-}
-// Publish without waiting (a device-scope store; readers check the tag).
-__device__ __forceinline__ void publish(uint64_t *p, uint32_t tag, uint32_t bits) {
-    __hip_atomic_store(p, tagged(tag, bits), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void publish_f32(uint64_t *p, uint32_t tag, float v) {
-    publish(p, tag, __float_as_uint(v));
-}
-__device__ __forceinline__ uint64_t fetch(const uint64_t *p) {
-    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ bool current(uint64_t w, uint32_t tag) {
-    return static_cast<uint32_t>(w >> 32) == tag;
-}
-__device__ __forceinline__ float word_f32(uint64_t w) {
-    return __uint_as_float(static_cast<uint32_t>(w));
-}
-// Bounded wait (from t0) until one word carries the call's tag.  One lane
-// polls one word with a pause between reads, so waiting workgroups add little
-// traffic beside the streaming ones; the caller then reads everything it
-// needs once.
-__device__ __forceinline__ void wait_word(const uint64_t *p, uint32_t tag, uint64_t t0) {
-    while (!current(fetch(p), tag) && wall_clock64() - t0 <= kWaitTicks)
-        __builtin_amdgcn_s_sleep(4);
-}
 
 // ------------------------------------------------------------ stats item
 
@@ -181,9 +149,10 @@ struct NegInf<F32> {
 // until every word carries the call's tag.  `ok` is false if a word was not
 // written for this call in time.  With `diag` the workgroup also writes
 // p_k(x_k), q_k(x_k) and their ratio to out_diag.
-template <class DT, bool Live, int Fold>
+template <class DT, bool Live, int Fold, int kPasses>
 __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow &w, bool &ok,
                                              bool diag, float *lds) {
+    // The loads of kPasses row groups (16 rows each) go out together.
     constexpr int kGroup = 16, kGroups = kWG / kGroup;
     float *s_ref = lds, *s_z = s_ref + (2 * kMaxK + 1);
     __shared__ int s_stale[2][kWaves + 1];
@@ -210,36 +179,53 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
         // A word this lane found missing (the first), for the wait below.
         const uint64_t *miss = nullptr;
         if (lane < K) miss = !current(wt, a.tag) ? gt : (!current(wd, a.tag) ? gd : nullptr);
-        for (int r0 = 0; r0 < R; r0 += kGroups) {
-            const int r = r0 + grp, rr = min(r, R - 1);
-            float ref = -INFINITY, z = 0.f;
-            for (int i0 = 0; i0 < nch; i0 += kGroup * Fold) {
-                uint64_t pr[Fold], pz[Fold];
+        for (int r0 = 0; r0 < R; r0 += kGroups * kPasses) {
+            float ref[kPasses], z[kPasses];
 #pragma unroll
-                for (int f = 0; f < Fold; ++f) {
-                    const uint64_t *pw = part + 2 * (rr * nch + min(i0 + gl + kGroup * f, nch - 1));
-                    if (Live) {
-                        pr[f] = fetch(pw);
-                        pz[f] = fetch(pw + 1);
-                    } else {
-                        const uint4 v = *reinterpret_cast<const uint4 *>(pw);
-                        pr[f] = (static_cast<uint64_t>(v.y) << 32) | v.x;
-                        pz[f] = (static_cast<uint64_t>(v.w) << 32) | v.z;
+            for (int q = 0; q < kPasses; ++q) {
+                ref[q] = -INFINITY;
+                z[q] = 0.f;
+            }
+            for (int i0 = 0; i0 < nch; i0 += kGroup * Fold) {
+                uint64_t pr[kPasses][Fold], pz[kPasses][Fold];
+#pragma unroll
+                for (int q = 0; q < kPasses; ++q) {
+                    const int rr = min(r0 + grp + kGroups * q, R - 1);
+#pragma unroll
+                    for (int f = 0; f < Fold; ++f) {
+                        const uint64_t *pw = part + 2 * (rr * nch + min(i0 + gl + kGroup * f, nch - 1));
+                        if (Live) {
+                            pr[q][f] = fetch(pw);
+                            pz[q][f] = fetch(pw + 1);
+                        } else {
+                            const uint4 v = *reinterpret_cast<const uint4 *>(pw);
+                            pr[q][f] = (static_cast<uint64_t>(v.y) << 32) | v.x;
+                            pz[q][f] = (static_cast<uint64_t>(v.w) << 32) | v.z;
+                        }
                     }
                 }
 #pragma unroll
-                for (int f = 0; f < Fold; ++f) {
-                    const int i = i0 + gl + kGroup * f;
-                    const bool in = r < R && i < nch;
-                    const bool cr = current(pr[f], a.tag), cz = current(pz[f], a.tag);
-                    if (in && !(cr && cz) && !miss) miss = part + 2 * (rr * nch + i) + (cr ? 1 : 0);
-                    mz_merge(ref, z, in ? word_f32(pr[f]) : -INFINITY, in ? word_f32(pz[f]) : 0.f);
+                for (int q = 0; q < kPasses; ++q) {
+                    const int r = r0 + grp + kGroups * q, rr = min(r, R - 1);
+#pragma unroll
+                    for (int f = 0; f < Fold; ++f) {
+                        const int i = i0 + gl + kGroup * f;
+                        const bool in = r < R && i < nch;
+                        const bool cr = current(pr[q][f], a.tag), cz = current(pz[q][f], a.tag);
+                        if (in && !(cr && cz) && !miss) miss = part + 2 * (rr * nch + i) + (cr ? 1 : 0);
+                        mz_merge(ref[q], z[q], in ? word_f32(pr[q][f]) : -INFINITY,
+                                 in ? word_f32(pz[q][f]) : 0.f);
+                    }
                 }
             }
-            mz_row_merge(ref, z);
-            if (r < R && gl == kGroup - 1) {
-                s_ref[r] = ref;
-                s_z[r] = z;
+#pragma unroll
+            for (int q = 0; q < kPasses; ++q) {
+                mz_row_merge(ref[q], z[q]);
+                const int r = r0 + grp + kGroups * q;
+                if (r < R && gl == kGroup - 1) {
+                    s_ref[r] = ref[q];
+                    s_z[r] = z[q];
+                }
             }
         }
         const uint64_t stale = __ballot(miss != nullptr);
@@ -536,10 +522,14 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
     const float us = a.u_sample[b];
     DrawRow w;
     bool ok;
-    // One chunk per lane of a 16-lane group when a row has at most 16, else
-    // four per load batch.
-    const int j = a.nchunk <= 16 ? resolve_local<DT, Live, 1>(a, b, w, ok, ch == 0, lds)
-                                 : resolve_local<DT, Live, 4>(a, b, w, ok, ch == 0, lds);
+    // One chunk per lane of a 16-lane group when a row has at most 16 (the
+    // loads of up to four groups of 16 rows together), else four chunks per
+    // lane and load batch.
+    const int R = 2 * a.K + 1;
+    const int j = a.nchunk > 16 ? resolve_local<DT, Live, 4, 1>(a, b, w, ok, ch == 0, lds)
+                  : R <= 16     ? resolve_local<DT, Live, 1, 1>(a, b, w, ok, ch == 0, lds)
+                  : R <= 32     ? resolve_local<DT, Live, 1, 2>(a, b, w, ok, ch == 0, lds)
+                                : resolve_local<DT, Live, 1, 4>(a, b, w, ok, ch == 0, lds);
     if (w.resid) draw_body<DT, VecOk, true>(a, b, ch, j, w, ok, us, my_tok, lds);
     else draw_body<DT, VecOk, false>(a, b, ch, j, w, ok, us, my_tok, lds);
 }

@@ -1,24 +1,29 @@
-// Greedy verify at T = 0 on gfx950: a row-argmax streaming pass, then a small
-// per-sequence resolve (French lesson, "La règle de l'exactitude", greedy case,
-// for the chain; "Vérifie l'attention des arbres" and the EAGLE section for the
-// tree: one target pass scores every candidate and the longest accepted branch
-// wins).
+// Greedy verify at T = 0 on gfx950, one launch per call (French lesson, "La
+// règle de l'exactitude", greedy case, for the chain; "Vérifie l'attention des
+// arbres" and the EAGLE section for the tree: one target pass scores every
+// candidate and the longest accepted branch wins).
 //
-// k_row_argmax: one workgroup per vocabulary chunk of one row; 16-byte loads,
+// Argmax items: one workgroup per vocabulary chunk of one row; 16-byte loads,
 // per-lane (max, lowest index) kept in index order, then a workgroup reduce.
 // Values are compared as floats widened exactly from bf16, so ties and -0.0 ==
-// +0.0 behave as on the raw logits.
+// +0.0 behave as on the raw logits.  Each publishes its chunk's (value, index)
+// as two tagged words.
+//
+// Resolve items: one workgroup per sequence (or tree), placed after every
+// argmax workgroup of the grid, so it only waits (bounded) for workgroups of
+// lower index.  Each group of 16 lanes merges one row's chunk partials with a
+// DPP tree; the comparison is exact, so the result does not depend on the
+// merge order.
 #include "device.hpp"
+#include "handover.hpp"
 #include "plan.hpp"
 
 namespace sv {
 namespace {
 
 template <class DT, int U>
-__global__ __launch_bounds__(kWG) void k_row_argmax(ArgmaxArgs a) {
+__device__ __forceinline__ void argmax_item(const ArgmaxArgs &a, int64_t row, int ch) {
     constexpr int VEC = DT::kVec;
-    const int64_t row = blockIdx.x / a.nchunk;
-    const int ch = blockIdx.x % a.nchunk;
     const int64_t rbase = row * a.V;
     const int64_t g0 = rbase + static_cast<int64_t>(ch) * a.chunk;
     const int64_t g1 = min(g0 + a.chunk, rbase + a.V);
@@ -81,66 +86,174 @@ __global__ __launch_bounds__(kWG) void k_row_argmax(ArgmaxArgs a) {
         }
     }
     vi_reduce_wg(bv, bi);
-    if (threadIdx.x == 0) a.partial[row * a.nchunk + ch] = make_int2(__float_as_int(bv), bi);
+    if (threadIdx.x == 0) {
+        uint64_t *w = a.partial + 2 * (row * a.nchunk + ch);
+        publish(w, a.tag, __float_as_uint(bv));
+        publish(w + 1, a.tag, static_cast<uint32_t>(bi));
+    }
 }
 
-// argmax of one row from its chunk partials (chunks in index order).
-__device__ __forceinline__ int32_t merge_argmax(const int2 *p, int nchunk) {
-    float bv = -INFINITY;
-    int32_t bi = INT32_MAX;
-    for (int i = 0; i < nchunk; ++i) {
-        const float v = __int_as_float(p[i].x);
-        if (vi_better(v, p[i].y, bv, bi)) {
-            bv = v;
-            bi = p[i].y;
+// argmax of rows [0, nrows) of one sequence from their tagged chunk partials
+// part[nrows][nch][2] into s_a (an all -inf row, outside the contract, maps to
+// 0).  Group g of 16 lanes takes rows g, g + 16, ... (the loads of kPasses
+// such rows issued together); lane i folds chunks i, i + 16, ...
+// (Fold per load batch), then four DPP steps leave the row's (max, lowest
+// index) in the group's last lane.  Words still missing are waited for
+// (bounded) and everything is read again.  Ends with a barrier; returns false
+// if a word did not arrive in time.
+template <int Fold, int kPasses>
+__device__ __forceinline__ bool merge_argmax_rows(const uint64_t *part, int nrows, int nch,
+                                                  uint32_t tag, int32_t *s_a) {
+    constexpr int kGroup = 16, kGroups = kWG / kGroup;
+    __shared__ int s_stale[2][kWaves + 1];
+    const int tid = threadIdx.x, lane = tid % kWave, grp = tid / kGroup, gl = tid % kGroup;
+    const uint64_t t0 = wall_clock64();
+    for (int it = 0;; ++it) {
+        const uint64_t *miss = nullptr;
+        for (int r0 = 0; r0 < nrows; r0 += kGroups * kPasses) {
+            float bv[kPasses];
+            int32_t bi[kPasses];
+#pragma unroll
+            for (int q = 0; q < kPasses; ++q) {
+                bv[q] = -INFINITY;
+                bi[q] = INT32_MAX;
+            }
+            for (int i0 = 0; i0 < nch; i0 += kGroup * Fold) {
+                uint64_t pv[kPasses][Fold], pi[kPasses][Fold];
+#pragma unroll
+                for (int q = 0; q < kPasses; ++q) {
+                    const int rr = min(r0 + grp + kGroups * q, nrows - 1);
+#pragma unroll
+                    for (int f = 0; f < Fold; ++f) {
+                        const uint64_t *pw = part + 2 * (rr * nch + min(i0 + gl + kGroup * f, nch - 1));
+                        pv[q][f] = fetch(pw);
+                        pi[q][f] = fetch(pw + 1);
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < kPasses; ++q) {
+                    const int r = r0 + grp + kGroups * q, rr = min(r, nrows - 1);
+#pragma unroll
+                    for (int f = 0; f < Fold; ++f) {
+                        const int i = i0 + gl + kGroup * f;
+                        const bool in = r < nrows && i < nch;
+                        const bool cv = current(pv[q][f], tag), ci = current(pi[q][f], tag);
+                        if (in && !(cv && ci) && !miss) miss = part + 2 * (rr * nch + i) + (cv ? 1 : 0);
+                        const float v = word_f32(pv[q][f]);
+                        const int32_t x = static_cast<int32_t>(static_cast<uint32_t>(pi[q][f]));
+                        if (in && vi_better(v, x, bv[q], bi[q])) {
+                            bv[q] = v;
+                            bi[q] = x;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kPasses; ++q) {
+                float v = bv[q];
+                int32_t x = bi[q];
+#define SV_AM_STEP(CTRL)                                                      \
+    {                                                                         \
+        const float v2 = dpp::mov_f<CTRL>(-INFINITY, v);                     \
+        const int32_t i2 = dpp::mov_i<CTRL>(INT32_MAX, x);                   \
+        if (vi_better(v2, i2, v, x)) {                                        \
+            v = v2;                                                           \
+            x = i2;                                                           \
+        }                                                                     \
+    }
+                SV_AM_STEP(dpp::kRowShr1)
+                SV_AM_STEP(dpp::kRowShr2)
+                SV_AM_STEP(dpp::kRowShr4)
+                SV_AM_STEP(dpp::kRowShr8)
+#undef SV_AM_STEP
+                const int r = r0 + grp + kGroups * q;
+                if (r < nrows && gl == kGroup - 1) s_a[r] = x == INT32_MAX ? 0 : x;
+            }
         }
+        const uint64_t stale = __ballot(miss != nullptr);
+        // Double-buffered by iteration: a wavefront may start the next
+        // iteration while another still reads this one's flags.
+        if (lane == 0) s_stale[it & 1][tid / kWave] = stale != 0;
+        if (tid == 0) s_stale[it & 1][kWaves] = wall_clock64() - t0 > kWaitTicks;
+        __syncthreads();
+        int any_stale = 0;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) any_stale |= s_stale[it & 1][k];
+        if (!any_stale) return true;
+        if (s_stale[it & 1][kWaves]) return false;
+        if (stale && lane == __ffsll(static_cast<unsigned long long>(stale)) - 1)
+            wait_word(miss, tag, t0);
     }
-    return bi == INT32_MAX ? 0 : bi;  // an all -inf row (outside the contract) maps to 0
 }
 
-constexpr int kGreedyThreads = 2 * kWave;  // rows 0..K with K <= 64
+__device__ __forceinline__ bool merge_argmax(const uint64_t *part, int nrows, int nch, uint32_t tag,
+                                             int32_t *s_a) {
+    return nch > 16     ? merge_argmax_rows<4, 1>(part, nrows, nch, tag, s_a)
+           : nrows <= 16 ? merge_argmax_rows<1, 1>(part, nrows, nch, tag, s_a)
+           : nrows <= 32 ? merge_argmax_rows<1, 2>(part, nrows, nch, tag, s_a)
+                         : merge_argmax_rows<1, 4>(part, nrows, nch, tag, s_a);
+}
 
-__global__ __launch_bounds__(kGreedyThreads) void k_greedy_resolve(GreedyArgs a) {
-    const int b = blockIdx.x, k = threadIdx.x, K = a.K;
+// Sequence b of the greedy chain: a_k = argmax of target row k; j = the first
+// k < K with x_k != a_k (else K); emits x_0..x_{j-1}, a_j.  Wavefront 0 does
+// the test and the emission (lane k: position k).
+__device__ __forceinline__ void greedy_resolve_item(const GreedyArgs &a, int b) {
     __shared__ int32_t s_a[kMaxK + 1];
-    __shared__ int s_j;
-    if (k <= K) s_a[k] = merge_argmax(a.partial + (static_cast<int64_t>(b) * (K + 1) + k) * a.nchunk, a.nchunk);
-    __syncthreads();
-    if (k < kWave) {
-        const bool mismatch = k < K && a.tokens[b * K + k] != s_a[k];
-        const uint64_t m = __ballot(mismatch);
-        if (k == 0) s_j = m ? (__ffsll(static_cast<unsigned long long>(m)) - 1) : K;
+    const int K = a.K, nch = a.am.nchunk, lane = threadIdx.x % kWave;
+    const int32_t tok = K > 0 ? a.tokens[static_cast<int64_t>(b) * K + min(lane, K - 1)] : 0;
+    const uint64_t *part = a.am.partial + 2 * static_cast<int64_t>(b) * (K + 1) * nch;
+    const bool ok = merge_argmax(part, K + 1, nch, a.am.tag, s_a);
+    if (threadIdx.x >= kWave) return;
+    int32_t *ot = a.out_tokens + static_cast<int64_t>(b) * (K + 1);
+    if (!ok) {
+        for (int k = lane; k <= K; k += kWave) ot[k] = -1;
+        if (lane == 0) a.out_accepted[b] = -1;
+        return;
     }
-    __syncthreads();
-    const int j = s_j;
-    if (k <= K) {
+    const uint64_t m = __ballot(lane < K && tok != s_a[lane]);
+    const int j = m ? (__ffsll(static_cast<unsigned long long>(m)) - 1) : K;
+    for (int k = lane; k <= K; k += kWave) {
         int32_t o = -1;
-        if (k < j) o = a.tokens[b * K + k];
+        if (k < j) o = tok;  // k < j <= K <= 64: k is this lane
         else if (k == j) o = s_a[k];
-        a.out_tokens[static_cast<int64_t>(b) * (K + 1) + k] = o;
+        ot[k] = o;
     }
-    if (k == 0) a.out_accepted[b] = j;
+    if (lane == 0) a.out_accepted[b] = j;
 }
 
-__global__ __launch_bounds__(kMaxTreeNodes) void k_tree_resolve(TreeArgs a) {
-    const int b = blockIdx.x, v = threadIdx.x;
-    const int N = a.tree.N, D = a.tree.D;
+// Tree b: node v matches iff its token equals its parent's argmax; a node is
+// accepted iff it and all its ancestors match; the deepest accepted node wins
+// (lowest index among equals); emits the path's tokens, then that node's
+// argmax.
+__device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, int b) {
     __shared__ int32_t s_a[kMaxTreeNodes];
     __shared__ int s_ok[kMaxTreeNodes];
     __shared__ int s_anc[kMaxTreeNodes];
     __shared__ int s_best;
     __shared__ int s_path[kMaxTreeNodes];
-    if (v < N) s_a[v] = merge_argmax(a.partial + (static_cast<int64_t>(b) * N + v) * a.nchunk, a.nchunk);
-    __syncthreads();
-    // match[v]: v's token equals its parent's argmax; accepted = all matches
-    // on the path to the root, folded by pointer jumping (depth <= 255).
-    int par = v < N ? a.tree.parent[v] : -1;
+    static_assert(kMaxTreeNodes == kWG, "one thread per node");
+    const int v = threadIdx.x;
+    const int N = a.tree.N, D = a.tree.D, nch = a.am.nchunk;
+    const int32_t tok = v < N ? a.tokens[static_cast<int64_t>(b) * N + v] : 0;
+    const uint64_t *part = a.am.partial + 2 * static_cast<int64_t>(b) * N * nch;
+    if (!merge_argmax(part, N, nch, a.am.tag, s_a)) {
+        if (v <= D) {
+            a.out_tokens[static_cast<int64_t>(b) * (D + 1) + v] = -1;
+            if (a.out_path) a.out_path[static_cast<int64_t>(b) * (D + 1) + v] = -1;
+        }
+        if (v == 0) a.out_depth[b] = -1;
+        return;
+    }
+    // match[v], then accepted = all matches on the path to the root, folded
+    // by pointer jumping: after the steps of 1, 2, 4, ... <= D every node has
+    // folded all of its at most D ancestors.
+    const int par = v < N ? a.tree.parent[v] : -1;
     if (v < N) {
-        s_ok[v] = (v == 0) ? 1 : (a.tokens[static_cast<int64_t>(b) * N + v] == s_a[par]);
+        s_ok[v] = (v == 0) ? 1 : (tok == s_a[par]);
         s_anc[v] = par;
     }
     __syncthreads();
-    for (int step = 1; step < kMaxTreeNodes; step <<= 1) {
+    for (int step = 1; step <= D; step <<= 1) {
         int ok = 0, anc = -1;
         if (v < N) {
             anc = s_anc[v];
@@ -165,45 +278,60 @@ __global__ __launch_bounds__(kMaxTreeNodes) void k_tree_resolve(TreeArgs a) {
     if (v == 0) {
         const int best = s_best;
         const int d = a.tree.depth[best];
-        int *path = s_path;
         int node = best;
         for (int i = d; i >= 0; --i) {
-            path[i] = node;
+            s_path[i] = node;
             node = a.tree.parent[node];
         }
-        int32_t *ot = a.out_tokens + static_cast<int64_t>(b) * (D + 1);
-        for (int i = 0; i <= D; ++i) {
-            int32_t o = -1;
-            if (i < d) o = a.tokens[static_cast<int64_t>(b) * N + path[i + 1]];
-            else if (i == d) o = s_a[best];
-            ot[i] = o;
-        }
-        if (a.out_path) {
-            int32_t *op = a.out_path + static_cast<int64_t>(b) * (D + 1);
-            for (int i = 0; i <= D; ++i) op[i] = i <= d ? path[i] : -1;
-        }
-        a.out_depth[b] = d;
+    }
+    __syncthreads();
+    // Thread i writes entry i of the path outputs.
+    const int best = s_best, d = a.tree.depth[best];
+    if (v <= D) {
+        int32_t o = -1;
+        if (v < d) o = a.tokens[static_cast<int64_t>(b) * N + s_path[v + 1]];
+        else if (v == d) o = s_a[best];
+        a.out_tokens[static_cast<int64_t>(b) * (D + 1) + v] = o;
+        if (a.out_path) a.out_path[static_cast<int64_t>(b) * (D + 1) + v] = v <= d ? s_path[v] : -1;
+    }
+    if (v == 0) a.out_depth[b] = d;
+}
+
+template <class DT>
+__global__ __launch_bounds__(kWG) void k_greedy(GreedyArgs a) {
+    const uint32_t nam = static_cast<uint32_t>(a.am.rows) * a.am.nchunk, g = blockIdx.x;
+    if (g < nam) {
+        const uint32_t row = g / a.am.nchunk;
+        argmax_item<DT, 4>(a.am, row, static_cast<int>(g - row * a.am.nchunk));
+    } else {
+        greedy_resolve_item(a, static_cast<int>(g - nam));
+    }
+}
+
+template <class DT>
+__global__ __launch_bounds__(kWG) void k_tree(TreeArgs a) {
+    const uint32_t nam = static_cast<uint32_t>(a.am.rows) * a.am.nchunk, g = blockIdx.x;
+    if (g < nam) {
+        const uint32_t row = g / a.am.nchunk;
+        argmax_item<DT, 4>(a.am, row, static_cast<int>(g - row * a.am.nchunk));
+    } else {
+        tree_resolve_item(a, static_cast<int>(g - nam));
     }
 }
 
 }  // namespace
 
-hipError_t launch_row_argmax(const ArgmaxArgs &a, int dtype, hipStream_t s) {
-    const int64_t grid = a.rows * a.nchunk;
-    if (dtype == 1)
-        k_row_argmax<Bf16, 4><<<dim3(static_cast<uint32_t>(grid)), dim3(kWG), 0, s>>>(a);
-    else
-        k_row_argmax<F32, 4><<<dim3(static_cast<uint32_t>(grid)), dim3(kWG), 0, s>>>(a);
+hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t s) {
+    const dim3 g(static_cast<uint32_t>(a.am.rows * a.am.nchunk + a.B)), blk(kWG);
+    if (dtype == 1) k_greedy<Bf16><<<g, blk, 0, s>>>(a);
+    else k_greedy<F32><<<g, blk, 0, s>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_greedy_resolve(const GreedyArgs &a, hipStream_t s) {
-    k_greedy_resolve<<<dim3(static_cast<uint32_t>(a.B)), dim3(kGreedyThreads), 0, s>>>(a);
-    return hipGetLastError();
-}
-
-hipError_t launch_tree_resolve(const TreeArgs &a, hipStream_t s) {
-    k_tree_resolve<<<dim3(static_cast<uint32_t>(a.B)), dim3(kMaxTreeNodes), 0, s>>>(a);
+hipError_t launch_tree(const TreeArgs &a, int dtype, hipStream_t s) {
+    const dim3 g(static_cast<uint32_t>(a.am.rows * a.am.nchunk + a.B)), blk(kWG);
+    if (dtype == 1) k_tree<Bf16><<<g, blk, 0, s>>>(a);
+    else k_tree<F32><<<g, blk, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -63,20 +63,23 @@ struct ChainArgs {
     float *out_diag;         // nullable [B][K+1][4]
 };
 
-// Row argmax over rows of [rows][V].
+// Row argmax over rows of [rows][V], one workgroup per (row, chunk).
 struct ArgmaxArgs {
     const void *logits;
     int64_t rows;
     int32_t V, chunk, nchunk;
-    int2 *partial;           // [rows][nchunk] (value bits, index)
+    uint32_t tag;            // this call's tag (upper half of every handed-over word)
+    uint64_t *partial;       // [rows][nchunk][2] tagged (value bits, index)
 };
 
+// Greedy chain verify in one launch: the argmax workgroups of rows
+// [B][K+1], then one resolve workgroup per sequence.
 struct GreedyArgs {
-    const int2 *partial;     // [B][K+1][nchunk]
+    ArgmaxArgs am;
     const int32_t *tokens;   // [B][K]
-    int32_t B, K, nchunk;
-    int32_t *out_tokens;
-    int32_t *out_accepted;
+    int32_t B, K;
+    int32_t *out_tokens;     // [B][K+1]
+    int32_t *out_accepted;   // [B]
 };
 
 // A static tree travels by value in the kernel arguments.
@@ -86,10 +89,12 @@ struct TreeShape {
     int32_t N, D;
 };
 
+// Greedy static-tree verify in one launch: the argmax workgroups of node rows
+// [B][N], then one resolve workgroup per tree.
 struct TreeArgs {
-    const int2 *partial;     // [B][N][nchunk]
+    ArgmaxArgs am;
     const int32_t *tokens;   // [B][N]
-    int32_t B, nchunk;
+    int32_t B;
     int32_t *out_tokens;     // [B][D+1]
     int32_t *out_path;       // nullable [B][D+1]
     int32_t *out_depth;      // [B]
@@ -100,8 +105,7 @@ struct TreeArgs {
 hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s);
 hipError_t launch_chain_draw(const ChainArgs &a, int dtype, hipStream_t s);
 hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s);
-hipError_t launch_row_argmax(const ArgmaxArgs &a, int dtype, hipStream_t s);
-hipError_t launch_greedy_resolve(const GreedyArgs &a, hipStream_t s);
-hipError_t launch_tree_resolve(const TreeArgs &a, hipStream_t s);
+hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t s);
+hipError_t launch_tree(const TreeArgs &a, int dtype, hipStream_t s);
 
 }  // namespace sv
