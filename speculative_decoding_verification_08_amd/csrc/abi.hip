@@ -50,6 +50,8 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
         off += align_up(static_cast<size_t>(rows) * 8);
         p.chunk2 = kChunk2Bytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
         p.nchunk2 = (V + p.chunk2 - 1) / p.chunk2;
+        // The bonus draw takes its chunk masses from the statistics chunks.
+        if (p.chunk2 != p.chunk) return false;
             // Every draw workgroup of a sequence waits for the sequence's other
         // chunks, so a sequence's draw workgroups must fit the chip together.
         if (p.nchunk2 > kMaxDrawChunks) return false;

@@ -142,19 +142,24 @@ struct NegInf<F32> {
 // order, then a fixed DPP tree), every wavefront evaluates the accept test of
 // every drafted token (u < P/Q, strict; Q = 0 accepts iff P > 0) and takes j,
 // the first rejected position (K if none), by ballot, so no second barrier is
-// needed.  Row j's statistics land in `w`.  Without Live the statistics come
-// from a kernel ordered before this one by the stream and are read once;
-// with Live the statistics workgroups may still be running, so the words are
-// read with device-scope loads and the merge is repeated (bounded in time)
-// until every word carries the call's tag.  `ok` is false if a word was not
-// written for this call in time.  With `diag` the workgroup also writes
-// p_k(x_k), q_k(x_k) and their ratio to out_diag.
+// needed.  The accept tests never read the bonus row (target row K), so j < K
+// is decided without it; the bonus row is needed only when j = K, and then
+// its per-chunk statistics are left in LDS for the bonus draw.  Row j's
+// statistics land in `w`.  Without Live the statistics come from a kernel
+// ordered before this one by the stream and are read once; with Live the
+// statistics workgroups may still be running, so the words are read with
+// device-scope loads, and while a needed word is missing one lane of each
+// wavefront that saw it waits for it (bounded) and everything is read again.
+// `ok` is false if a needed word was not written for this call in time.
+// With `diag` the workgroup also writes p_k(x_k), q_k(x_k) and their ratio to
+// out_diag.
 template <class DT, bool Live, int Fold, int kPasses>
 __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow &w, bool &ok,
                                              bool diag, float *lds) {
     // The loads of kPasses row groups (16 rows each) go out together.
     constexpr int kGroup = 16, kGroups = kWG / kGroup;
     float *s_ref = lds, *s_z = s_ref + (2 * kMaxK + 1);
+    float *s_kref = lds + kDrawBonusAt, *s_kz = s_kref + kMaxDrawChunks;
     __shared__ int s_stale[2][kWaves + 1];
     const int K = a.K, V = a.V, R = 2 * K + 1, nch = a.nchunk;
     const int tid = threadIdx.x, lane = tid % kWave, grp = tid / kGroup, gl = tid % kGroup;
@@ -166,6 +171,8 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
     const float u = ua[min(lane, max(K - 1, 0))];
     const uint64_t t0 = Live ? wall_clock64() : 0;
     uint64_t wt, wd;
+    float P = 0.f, Q = 0.f;
+    int j = K;
     for (int it = 0;; ++it) {
         // Drafted-token logits of lane k's position (clamped indices), loaded
         // with the partials before any is used.
@@ -176,8 +183,9 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
             wt = *gt;
             wd = *gd;
         }
-        // A word this lane found missing (the first), for the wait below.
-        const uint64_t *miss = nullptr;
+        // The first missing word this lane found among the rows the accept
+        // tests read, and in the bonus row.
+        const uint64_t *miss = nullptr, *miss_k = nullptr;
         if (lane < K) miss = !current(wt, a.tag) ? gt : (!current(wd, a.tag) ? gd : nullptr);
         for (int r0 = 0; r0 < R; r0 += kGroups * kPasses) {
             float ref[kPasses], z[kPasses];
@@ -212,9 +220,18 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
                         const int i = i0 + gl + kGroup * f;
                         const bool in = r < R && i < nch;
                         const bool cr = current(pr[q][f], a.tag), cz = current(pz[q][f], a.tag);
-                        if (in && !(cr && cz) && !miss) miss = part + 2 * (rr * nch + i) + (cr ? 1 : 0);
-                        mz_merge(ref[q], z[q], in ? word_f32(pr[q][f]) : -INFINITY,
-                                 in ? word_f32(pz[q][f]) : 0.f);
+                        const float fr = in ? word_f32(pr[q][f]) : -INFINITY;
+                        const float fz = in ? word_f32(pz[q][f]) : 0.f;
+                        if (in && !(cr && cz)) {
+                            const uint64_t *mw = part + 2 * (rr * nch + i) + (cr ? 1 : 0);
+                            if (r == K) miss_k = miss_k ? miss_k : mw;
+                            else miss = miss ? miss : mw;
+                        }
+                        if (r == K && in) {
+                            s_kref[i] = fr;
+                            s_kz[i] = fz;
+                        }
+                        mz_merge(ref[q], z[q], fr, fz);
                     }
                 }
             }
@@ -228,37 +245,44 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
                 }
             }
         }
-        const uint64_t stale = __ballot(miss != nullptr);
+        const uint64_t st = __ballot(miss != nullptr), st_k = __ballot(miss_k != nullptr);
         // Double-buffered by iteration: a wavefront may start the next
         // iteration while another still reads this one's flags.
-        if (lane == 0) s_stale[it & 1][tid / kWave] = stale != 0;
+        if (lane == 0) s_stale[it & 1][tid / kWave] = (st ? 1 : 0) | (st_k ? 2 : 0);
         if (tid == 0) s_stale[it & 1][kWaves] = !Live || wall_clock64() - t0 > kWaitTicks;
         __syncthreads();
-        int any_stale = 0;
+        int any = 0;
 #pragma unroll
-        for (int k = 0; k < kWaves; ++k) any_stale |= s_stale[it & 1][k];
-        ok = !any_stale;
-        if (ok || s_stale[it & 1][kWaves]) break;
-        // Statistics still being written (one launch): one lane of each
-        // wavefront that missed a word waits for that word, then all read
-        // again.
-        if (stale && lane == __ffsll(static_cast<unsigned long long>(stale)) - 1)
-            wait_word(miss, a.tag, t0);
-    }
-    bool reject = false;
-    if (lane < K) {
-        const float P = exp2_hw(fmaf(word_f32(wt), a.c, -s_ref[lane])) / s_z[lane];
-        const float Q = exp2_hw(fmaf(word_f32(wd), a.c, -s_ref[K + 1 + lane])) / s_z[K + 1 + lane];
-        reject = !(Q > 0.f ? (u < P / Q) : (P > 0.f));
-        if (diag && tid < kWave && a.out_diag) {
-            float *dg = a.out_diag + 4 * (static_cast<int64_t>(b) * (K + 1) + lane);
-            dg[0] = P;
-            dg[1] = Q;
-            dg[2] = Q > 0.f ? P / Q : (P > 0.f ? INFINITY : 0.f);
+        for (int k = 0; k < kWaves; ++k) any |= s_stale[it & 1][k];
+        if (!(any & 1)) {
+            bool reject = false;
+            if (lane < K) {
+                P = exp2_hw(fmaf(word_f32(wt), a.c, -s_ref[lane])) / s_z[lane];
+                Q = exp2_hw(fmaf(word_f32(wd), a.c, -s_ref[K + 1 + lane])) / s_z[K + 1 + lane];
+                reject = !(Q > 0.f ? (u < P / Q) : (P > 0.f));
+            }
+            const uint64_t m = __ballot(reject);
+            j = m ? (__ffsll(static_cast<unsigned long long>(m)) - 1) : K;
+            if (j < K || !(any & 2)) {
+                ok = true;
+                break;
+            }
         }
+        if (s_stale[it & 1][kWaves]) {
+            ok = false;
+            break;
+        }
+        // One lane of each wavefront that missed a needed word waits for it.
+        const uint64_t need = (any & 1) ? st : st_k;
+        if (need && lane == __ffsll(static_cast<unsigned long long>(need)) - 1)
+            wait_word((any & 1) ? miss : miss_k, a.tag, t0);
     }
-    const uint64_t m = __ballot(reject);
-    const int j = m ? (__ffsll(static_cast<unsigned long long>(m)) - 1) : K;
+    if (ok && diag && tid < K && a.out_diag) {
+        float *dg = a.out_diag + 4 * (static_cast<int64_t>(b) * (K + 1) + lane);
+        dg[0] = P;
+        dg[1] = Q;
+        dg[2] = Q > 0.f ? P / Q : (P > 0.f ? INFINITY : 0.f);
+    }
     w.resid = j < K;
     w.rt = s_ref[j];
     w.izt = 1.f / s_z[j];
@@ -350,38 +374,17 @@ __device__ __forceinline__ float raw_entry(const uint32_t *words, int e) {
 
 // ------------------------------------------------------------ draw item
 
-// Workgroup (b, ch) of the draw after the resolve.  It holds entries
-// [ch*C2, ch*C2 + C2) of row j in registers (kSeg contiguous entries per
-// thread) and publishes the chunk's residual mass sum max(0, p_j - q_j) and
-// target mass sum p_j.  Wavefront 0 polls every chunk's masses of the
-// sequence into its lanes (a sequence has at most 64 chunks), and every draw
-// workgroup of the sequence computes the same S and the same crossing chunk:
-// the first whose inclusive running mass exceeds u * S (the inverse CDF,
-// strict), else the last chunk with mass.  In the workgroup owning it, the
-// first thread whose running mass passes u * S hands its entries to
-// wavefront 0 through LDS, which finds the entry (one lane each) and writes
-// the sequence's outputs.  An all-zero residual (reachable only through
-// rounding) draws from p_j; the bonus draw (j = K) always uses p_K.
+// Row j's entries of this workgroup's chunk, as draw weights: per-thread
+// sums of p and (with Resid) of max(0, p - q), the raw entries staying in
+// registers for the crossing search.
 template <class DT, bool VecOk, bool Resid>
-__device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int j, const DrawRow &w,
-                                          bool ok, float us, int32_t my_tok, float *lds) {
-    using CK = Chunk2<DT>;
-    constexpr int VEC = DT::kVec, C2 = CK::kElems, kSeg = CK::kSeg, NQ = CK::kNQ;
-    static_assert(kSeg <= kWave, "one lane per entry of a thread's segment");
-    static_assert(CK::kRawWords <= kDrawRawWords, "a thread's raw entries fit the LDS");
-    static_assert(kMaxDrawChunks <= kWave, "one lane per chunk of a sequence");
-    const int K = a.K, tid = threadIdx.x, lane = tid % kWave, nc = a.nchunk2;
-    const float c = a.c;
-    __shared__ float s_tau, s_base;
-    __shared__ int s_cstar, s_resid, s_ok;
-
-    const int64_t c0 = static_cast<int64_t>(ch) * C2;
-    const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(a.V) - c0));
-    const int s0 = tid * kSeg;
-    uint4 rt[NQ], rd[NQ];
+__device__ __forceinline__ void chunk_weights(const ChainArgs &a, const DrawRow &w, int64_t c0, int n,
+                                              int s0, uint4 (&rt)[Chunk2<DT>::kNQ],
+                                              uint4 (&rd)[Chunk2<DT>::kNQ], float &lp, float &lr) {
+    constexpr int VEC = DT::kVec, NQ = Chunk2<DT>::kNQ;
     load_chunk<DT, VecOk, Resid>(a, w, c0, n, s0, rt, rd);
-
-    float lp = 0.f, lr = 0.f;
+    lp = 0.f;
+    lr = 0.f;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         float t[VEC], d[VEC];
@@ -389,65 +392,126 @@ __device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int
         if (Resid) unpack<DT>(rd[q], d);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
-            const float p = weight_p(t[i], c, w);
+            const float p = weight_p(t[i], a.c, w);
             lp += p;
-            if (Resid) lr += weight_r(p, d[i], c, w);
+            if (Resid) lr += weight_r(p, d[i], a.c, w);
         }
         asm volatile("" : "+v"(lp), "+v"(lr));  // one slot at a time
     }
-    // The raw entries stay in registers for the crossing search.
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         asm volatile("" : "+v"(rt[q].x), "+v"(rt[q].y), "+v"(rt[q].z), "+v"(rt[q].w));
         if (Resid) asm volatile("" : "+v"(rd[q].x), "+v"(rd[q].y), "+v"(rd[q].z), "+v"(rd[q].w));
     }
-    // Running sums inside the chunk and the chunk's masses, both kinds, in
-    // one pass (published afterwards: a barrier after a device-scope store
-    // would wait for it to complete).
-    uint64_t *sums = a.sums + 2 * static_cast<int64_t>(b) * nc;
-    float ex_r, ex_p, mr, mp;
-    wg_excl_scan2(lr, lp, ex_r, ex_p, mr, mp);
-    if (tid == 0) {
-        publish_f32(&sums[2 * ch], a.tag, mr);
-        publish_f32(&sums[2 * ch + 1], a.tag, mp);
-    }
+}
 
-    // Wavefront 0: lane i polls chunk i's masses (bounded), then the
-    // sequence-wide choice of kind, total and crossing chunk, in registers.
-    float S = 0.f;
-    if (tid < kWave) {
-        const int i = min(lane, nc - 1);
-        uint64_t vr, vp;
-        bool fresh;
-        const uint64_t t0 = wall_clock64();
-        // The last chunk's workgroup is dispatched last: wait for its word,
-        // then read all (repeating while any is missing).
-        if (lane == 0) wait_word(&sums[2 * (nc - 1)], a.tag, t0);
-        for (;;) {
-            vr = fetch(&sums[2 * i]);
-            vp = fetch(&sums[2 * i + 1]);
-            fresh = __all(current(vr, a.tag) && current(vp, a.tag));
-            if (fresh || wall_clock64() - t0 > kWaitTicks) break;
-            __builtin_amdgcn_s_sleep(8);
+// Wavefront 0: from the chunk masses of the sequence (lane i: chunk i), the
+// total S, tau = u * S and the crossing chunk -- the first whose inclusive
+// running mass exceeds tau (the inverse CDF, strict), else the last chunk
+// with mass -- with the running mass before it.
+__device__ __forceinline__ void crossing_chunk(float m, bool in, float us, float &S, float &tau,
+                                               int &cstar, float &base) {
+    const float incl = wave_incl_sum(m);
+    S = wave_last(incl);
+    tau = us * S;
+    const float excl = wave_excl_from_incl(incl);
+    const uint64_t cross = __ballot(in && incl > tau), pos = __ballot(in && m > 0.f);
+    cstar = cross ? __ffsll(static_cast<unsigned long long>(cross)) - 1
+                  : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
+    base = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), cstar));
+}
+
+// Workgroup (b, ch) of the draw after the resolve.
+//
+// After a rejection (Resid) it holds entries [ch*C2, ch*C2 + C2) of rows j in
+// registers (kSeg contiguous entries per thread) and publishes the chunk's
+// residual mass sum max(0, p_j - q_j) and target mass sum p_j.  Wavefront 0
+// reads every chunk's masses of the sequence into its lanes (a sequence has
+// at most 64 chunks), and every draw workgroup of the sequence computes the
+// same S and the same crossing chunk.  An all-zero residual (reachable only
+// through rounding) draws from p_j.
+//
+// For the bonus draw (j = K) the chunk masses of p_K follow from the bonus
+// row's chunk statistics, z_c * 2^(ref_c - ref) / z, with no second read of
+// the row; only the crossing chunk's workgroup loads its entries.
+//
+// In the crossing chunk's workgroup the first thread whose running mass
+// passes u * S hands its entries to wavefront 0 through LDS, which finds the
+// entry (one lane each) and writes the sequence's outputs.
+template <class DT, bool VecOk, bool Resid>
+__device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int j, const DrawRow &w,
+                                          bool ok, float us, int32_t my_tok, float *lds) {
+    using CK = Chunk2<DT>;
+    constexpr int C2 = CK::kElems, kSeg = CK::kSeg, NQ = CK::kNQ;
+    static_assert(kSeg <= kWave, "one lane per entry of a thread's segment");
+    static_assert(CK::kRawWords <= kDrawRawWords, "a thread's raw entries fit the LDS");
+    static_assert(kMaxDrawChunks <= kWave, "one lane per chunk of a sequence");
+    const int K = a.K, tid = threadIdx.x, lane = tid % kWave, nc = a.nchunk2;
+    __shared__ float s_tau, s_base;
+    __shared__ int s_cstar, s_resid, s_ok;
+
+    const int64_t c0 = static_cast<int64_t>(ch) * C2;
+    const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(a.V) - c0));
+    const int s0 = tid * kSeg;
+    uint4 rt[NQ], rd[NQ];
+    float lp = 0.f, lr = 0.f, ex_r = 0.f, ex_p = 0.f, S = 0.f;
+    if constexpr (Resid) {
+        chunk_weights<DT, VecOk, true>(a, w, c0, n, s0, rt, rd, lp, lr);
+        // Running sums inside the chunk and the chunk's masses, both kinds,
+        // in one pass (published afterwards: a barrier after a device-scope
+        // store would wait for it to complete).
+        uint64_t *sums = a.sums + 2 * static_cast<int64_t>(b) * nc;
+        float mr, mp;
+        wg_excl_scan2(lr, lp, ex_r, ex_p, mr, mp);
+        if (tid == 0) {
+            publish_f32(&sums[2 * ch], a.tag, mr);
+            publish_f32(&sums[2 * ch + 1], a.tag, mp);
         }
-        const bool in = lane < nc;
-        const float m_r = in ? word_f32(vr) : 0.f, m_p = in ? word_f32(vp) : 0.f;
-        const float inc_r = wave_incl_sum(m_r), inc_p = wave_incl_sum(m_p);
-        const bool resid = Resid && wave_last(inc_r) > 0.f;
-        const float m = resid ? m_r : m_p, incl = resid ? inc_r : inc_p;
-        S = wave_last(incl);
-        const float tau = us * S;
-        const float excl = wave_excl_from_incl(incl);
-        const uint64_t cross = __ballot(in && incl > tau), pos = __ballot(in && m > 0.f);
-        const int l = cross ? __ffsll(static_cast<unsigned long long>(cross)) - 1
-                            : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
-        const float base = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), l));
-        if (lane == 0) {
-            s_ok = fresh;
-            s_cstar = l;
-            s_base = base;
-            s_tau = tau;
-            s_resid = resid;
+        if (tid < kWave) {
+            const int i = min(lane, nc - 1);
+            uint64_t vr, vp;
+            bool fresh;
+            const uint64_t t0 = wall_clock64();
+            // The last chunk's workgroup is dispatched last: wait for its
+            // word, then read all (repeating while any is missing).
+            if (lane == 0) wait_word(&sums[2 * (nc - 1)], a.tag, t0);
+            for (;;) {
+                vr = fetch(&sums[2 * i]);
+                vp = fetch(&sums[2 * i + 1]);
+                fresh = __all(current(vr, a.tag) && current(vp, a.tag));
+                if (fresh || wall_clock64() - t0 > kWaitTicks) break;
+                __builtin_amdgcn_s_sleep(8);
+            }
+            const bool in = lane < nc;
+            const float m_r = in ? word_f32(vr) : 0.f, m_p = in ? word_f32(vp) : 0.f;
+            const bool resid = wave_last(wave_incl_sum(m_r)) > 0.f;
+            float tau, base;
+            int cstar;
+            crossing_chunk(resid ? m_r : m_p, in, us, S, tau, cstar, base);
+            if (lane == 0) {
+                s_ok = fresh;
+                s_cstar = cstar;
+                s_base = base;
+                s_tau = tau;
+                s_resid = resid;
+            }
+        }
+    } else {
+        if (tid < kWave) {
+            const bool in = lane < nc;
+            const float *s_kref = lds + kDrawBonusAt, *s_kz = s_kref + kMaxDrawChunks;
+            const int i = min(lane, nc - 1);
+            const float m = in ? __fmul_rn(s_kz[i] * exp2_hw(s_kref[i] - w.rt), w.izt) : 0.f;
+            float tau, base;
+            int cstar;
+            crossing_chunk(m, in, us, S, tau, cstar, base);
+            if (lane == 0) {
+                s_ok = 1;
+                s_cstar = cstar;
+                s_base = base;
+                s_tau = tau;
+                s_resid = 0;
+            }
         }
     }
     __syncthreads();
@@ -462,10 +526,16 @@ __device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int
         return;
     }
     if (s_cstar != ch) return;
+    if constexpr (!Resid) {
+        // The bonus draw's crossing chunk: its entries and running sums now.
+        chunk_weights<DT, VecOk, false>(a, w, c0, n, s0, rt, rd, lp, lr);
+        float mr, mp;
+        wg_excl_scan2(0.f, lp, ex_r, ex_p, mr, mp);
+    }
 
     // The crossing chunk.  The first thread whose running mass passes tau
     // (else the last thread with mass) holds the drawn entry.
-    const bool resid = s_resid;
+    const bool resid = Resid && s_resid;
     const float tau = s_tau;
     const float start = s_base + (resid ? ex_r : ex_p), l = resid ? lr : lp;
     int tf, tl;
@@ -487,8 +557,8 @@ __device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int
     // order) whose running mass exceeds tau; if rounding leaves none, the
     // last entry with weight.
     const int e = min(lane, kSeg - 1);
-    float x = weight_p(raw_entry<DT>(s_raw, e), c, w);
-    if (Resid && resid) x = weight_r(x, raw_entry<DT>(s_raw + kDrawRawWords, e), c, w);
+    float x = weight_p(raw_entry<DT>(s_raw, e), a.c, w);
+    if (Resid && resid) x = weight_r(x, raw_entry<DT>(s_raw + kDrawRawWords, e), a.c, w);
     x = lane < kSeg ? x : 0.f;
     const float run = *s_start + wave_incl_sum(x);
     const uint64_t f = __ballot(x > 0.f && run > tau), nz = __ballot(x > 0.f);
@@ -561,6 +631,8 @@ __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
 // workgroups of its own sequence (dispatched together); with the lag at least
 // the chip's resident window, the statistics it needs have usually finished
 // before it starts, and the draws overlap the streaming of later sequences.
+// With lag = B every draw comes after every statistics workgroup, and the
+// bonus rows are streamed last.
 template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_chain_fused(ChainArgs a) {
     __shared__ __align__(16) float lds[kDrawLds];
@@ -589,10 +661,31 @@ __global__ __launch_bounds__(kWG) void k_chain_fused(ChainArgs a) {
     }
     if (draw) {
         draw_item<DT, VecOk, true>(a, static_cast<int>(b), static_cast<int>(s), lds);
-    } else {
-        const uint32_t r = s / a.nchunk;
-        stats_item<DT, 4>(a, b, static_cast<int>(r), static_cast<int>(s - r * a.nchunk));
+        return;
     }
+    uint32_t r, ch;
+    if (L == B) {
+        // Every draw follows every statistics workgroup: the bonus rows
+        // (target row K, read only by a draw with every draft accepted) are
+        // streamed last, after the other rows of all sequences, so draws
+        // after a rejection can run while they stream.
+        const uint32_t nch = a.nchunk, Sn = S - nch;
+        if (g < B * Sn) {
+            b = g / Sn;
+            const uint32_t p = g - b * Sn, rr = p / nch;
+            r = rr < static_cast<uint32_t>(a.K) ? rr : rr + 1;
+            ch = p - rr * nch;
+        } else {
+            const uint32_t h = g - B * Sn;
+            b = h / nch;
+            r = a.K;
+            ch = h - b * nch;
+        }
+    } else {
+        r = s / a.nchunk;
+        ch = s - r * a.nchunk;
+    }
+    stats_item<DT, 4>(a, b, static_cast<int>(r), static_cast<int>(ch));
 }
 
 }  // namespace

@@ -18,12 +18,14 @@ constexpr int kChunk2Bytes = 16384;  // bytes of one row per chunk of the residu
 constexpr int kResidentWGs = 2048;
 constexpr int64_t kLlcBytes = 256ll << 20;
 constexpr int kMaxDrawChunks = 64;  // draw chunks per row: V <= 64 x 16 KB of entries
-// LDS words of a draw workgroup: its sequence's row statistics (ref, z), then
-// one thread's raw entries of the crossing chunk (16 words per row, target
-// and draft) and that thread's running mass.
+// LDS words of a draw workgroup: its sequence's row statistics (ref, z), one
+// thread's raw entries of the crossing chunk (16 words per row, target and
+// draft) and that thread's running mass, then the bonus row's per-chunk
+// statistics (ref, z).
 constexpr int kDrawRawWords = 16;
 constexpr int kDrawRawAt = (2 * (2 * kMaxK + 1) + 3) / 4 * 4;  // 16-byte aligned
-constexpr int kDrawLds = kDrawRawAt + 2 * kDrawRawWords + 4;
+constexpr int kDrawBonusAt = kDrawRawAt + 2 * kDrawRawWords + 4;
+constexpr int kDrawLds = kDrawBonusAt + 2 * kMaxDrawChunks;
 
 // How a launch cuts the rows it streams into vocabulary chunks, and where its
 // scratch lives inside the caller's workspace.
