@@ -130,9 +130,9 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
 /*
  * First phase of the chain verify (one kernel): one streaming pass over every
  * target and draft logit that leaves each row's softmax statistics (running
- * maximum and sum of exponentials, per vocabulary chunk) and each row's logit
- * at its drafted token in the workspace.  Same argument meaning as
- * spec_verify_chain.
+ * maximum and sum of exponentials, per vocabulary chunk) in the workspace.
+ * Same argument meaning as spec_verify_chain; draft_tokens is checked like
+ * there, and read by the second phase.
  */
 spec_status spec_verify_chain_stats(const void *target_logits, const void *draft_logits,
                                     spec_dtype dtype, const int32_t *draft_tokens, int32_t B,

@@ -46,8 +46,6 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
     p.off_partial = off;
     if (mode == SPEC_MODE_CHAIN) {
         off += align_up(static_cast<size_t>(rows) * p.nchunk * 16);
-        p.off_gather = off;
-        off += align_up(static_cast<size_t>(rows) * 8);
         p.chunk2 = kChunk2Bytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
         p.nchunk2 = (V + p.chunk2 - 1) / p.chunk2;
         // The bonus draw takes its chunk masses from the statistics chunks.
@@ -106,7 +104,6 @@ spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype,
     a.nchunk = plan.nchunk;
     a.nchunk2 = plan.nchunk2;
     a.partial = at<uint64_t>(ws, plan.off_partial);
-    a.gathered = at<uint64_t>(ws, plan.off_gather);
     a.sums = at<uint64_t>(ws, plan.off_sums);
     a.tag = kPhasedTag;
     return SPEC_OK;

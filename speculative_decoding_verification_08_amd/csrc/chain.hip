@@ -3,12 +3,12 @@
 // Statistics items stream every logit of the step once.  One workgroup takes
 // one 16 KB vocabulary chunk of one row (target rows 0..K and draft rows
 // 0..K-1 of a sequence), folds it into softmax statistics (ref, z) and
-// publishes them (and, if its chunk holds the row's drafted token, that
-// logit).  This is the HBM-bound work that carries the bytes; no statistics
-// workgroup waits for another.
+// publishes them.  This is the HBM-bound work that carries the bytes; no
+// statistics workgroup waits for another.
 //
 // Draw items run one workgroup per (sequence b, 16 KB chunk of a row).  Each
-// merges b's row statistics, evaluates the accept test of every drafted token
+// merges b's row statistics, reads the logits at the drafted tokens from the
+// inputs, evaluates the accept test of every drafted token
 // (u < p(x)/q(x), French lesson "Décodage spéculatif et Eagle", section "La
 // règle de l'exactitude"; forum post "Speculative Decoding: от идеи до SOTA",
 // §3) and finds the first rejection j.  It holds its chunk of row j in
@@ -46,18 +46,8 @@ __device__ __forceinline__ void stats_item(const ChainArgs &a, int64_t b, int r,
     constexpr int VEC = DT::kVec;
     const int K = a.K, V = a.V, R = 2 * K + 1;
     const int64_t row = b * R + r;
-    const void *base;
-    int64_t trow;
-    int k;  // drafted position this row scores, -1 for the bonus row
-    if (r <= K) {
-        base = a.target;
-        trow = b * (K + 1) + r;
-        k = r < K ? r : -1;
-    } else {
-        base = a.draft;
-        trow = b * K + (r - K - 1);
-        k = r - K - 1;
-    }
+    const void *base = r <= K ? a.target : a.draft;
+    const int64_t trow = r <= K ? b * (K + 1) + r : b * K + (r - K - 1);
     const int64_t e0 = static_cast<int64_t>(ch) * a.chunk;
     const int64_t e1 = min(e0 + a.chunk, static_cast<int64_t>(V));
     const Span s = split_span<VEC>(trow * V + e0, trow * V + e1);
@@ -92,11 +82,6 @@ __device__ __forceinline__ void stats_item(const ChainArgs &a, int64_t b, int r,
             const float x = load_one<DT>(base, t);
             mz_batch<1>(&x, a.c, ref, z);
         }
-    }
-    if (threadIdx.x == 0 && k >= 0) {
-        const int x = min(max(a.tokens[b * K + k], 0), V - 1);
-        if (x >= e0 && x < e1)
-            publish_f32(&a.gathered[row], a.tag, load_one<DT>(base, trow * V + x));
     }
     mz_reduce_wg(ref, z);
     if (threadIdx.x == 0) {
@@ -164,29 +149,25 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
     const int K = a.K, V = a.V, R = 2 * K + 1, nch = a.nchunk;
     const int tid = threadIdx.x, lane = tid % kWave, grp = tid / kGroup, gl = tid % kGroup;
     const uint64_t *part = a.partial + 2 * static_cast<int64_t>(b) * R * nch;
-    const uint64_t *gat = a.gathered + static_cast<int64_t>(b) * R;
-    const uint64_t *gt = &gat[min(lane, R - 1)], *gd = &gat[min(K + 1 + lane, R - 1)];
-    // Uniforms of lane k's position, loaded by every wavefront.
+    // Lane k's position: its uniform, and the drafted token's logits in target
+    // row k and draft row k, read straight from the inputs (every wavefront,
+    // clamped indices) before anything waits.
+    const int kk = min(lane, max(K - 1, 0));
     const float *ua = K > 0 ? a.u_accept + static_cast<int64_t>(b) * K : a.u_sample + b;
-    const float u = ua[min(lane, max(K - 1, 0))];
+    const float u = ua[kk];
+    float lt = 0.f, ld = 0.f;
+    if (K > 0) {
+        const int x = min(max(a.tokens[static_cast<int64_t>(b) * K + kk], 0), V - 1);
+        lt = load_one<DT>(a.target, (static_cast<int64_t>(b) * (K + 1) + kk) * V + x);
+        ld = load_one<DT>(a.draft, (static_cast<int64_t>(b) * K + kk) * V + x);
+    }
     const uint64_t t0 = Live ? wall_clock64() : 0;
-    uint64_t wt, wd;
     float P = 0.f, Q = 0.f;
     int j = K;
     for (int it = 0;; ++it) {
-        // Drafted-token logits of lane k's position (clamped indices), loaded
-        // with the partials before any is used.
-        if (Live) {
-            wt = fetch(gt);
-            wd = fetch(gd);
-        } else {
-            wt = *gt;
-            wd = *gd;
-        }
         // The first missing word this lane found among the rows the accept
         // tests read, and in the bonus row.
         const uint64_t *miss = nullptr, *miss_k = nullptr;
-        if (lane < K) miss = !current(wt, a.tag) ? gt : (!current(wd, a.tag) ? gd : nullptr);
         for (int r0 = 0; r0 < R; r0 += kGroups * kPasses) {
             float ref[kPasses], z[kPasses];
 #pragma unroll
@@ -257,8 +238,8 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
         if (!(any & 1)) {
             bool reject = false;
             if (lane < K) {
-                P = exp2_hw(fmaf(word_f32(wt), a.c, -s_ref[lane])) / s_z[lane];
-                Q = exp2_hw(fmaf(word_f32(wd), a.c, -s_ref[K + 1 + lane])) / s_z[K + 1 + lane];
+                P = exp2_hw(fmaf(lt, a.c, -s_ref[lane])) / s_z[lane];
+                Q = exp2_hw(fmaf(ld, a.c, -s_ref[K + 1 + lane])) / s_z[K + 1 + lane];
                 reject = !(Q > 0.f ? (u < P / Q) : (P > 0.f));
             }
             const uint64_t m = __ballot(reject);

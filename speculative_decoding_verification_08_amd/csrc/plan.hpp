@@ -35,7 +35,7 @@ struct Plan {
     int nchunk = 0;        // chunks per row, first pass
     int chunk2 = 0;        // elements per chunk, residual / bonus pass (chain)
     int nchunk2 = 0;       // chunks per row, residual / bonus pass (chain)
-    size_t off_partial = 0, off_gather = 0, off_sums = 0;
+    size_t off_partial = 0, off_sums = 0;
     size_t bytes = 0;      // total workspace
 };
 
@@ -58,7 +58,6 @@ struct ChainArgs {
     int32_t chunk, nchunk, nchunk2;  // chunk2 = kChunk2Bytes / element size
     int32_t lag;             // one-launch form: sequences between a sequence's statistics and its draw
     uint64_t *partial;       // [B][2K+1][nchunk][2] tagged (ref, z); rows 0..K target, K+1.. draft
-    uint64_t *gathered;      // [B][2K+1] tagged logit of each row at its drafted token (row K unused)
     uint64_t *sums;          // [B][nchunk2][2] tagged residual and target mass per chunk
     int32_t *out_tokens;     // [B][K+1]
     int32_t *out_accepted;   // [B]
