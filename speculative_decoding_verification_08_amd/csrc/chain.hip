@@ -601,72 +601,83 @@ __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
     draw_item<DT, VecOk, false>(a, static_cast<int>(b), static_cast<int>(g - b * nc), lds);
 }
 
-// The whole chain verify in one launch.  Per sequence, its S = (2K+1) *
-// nchunk statistics workgroups come first and its D = nchunk2 draw workgroups
-// `lag` sequences later: blocks of the statistics of b + lag with the draws
-// of b spread evenly among them, after
-// a prologue of the first `lag` sequences' statistics and before an epilogue
-// of the last `lag` sequences' draws.  The hardware dispatches workgroups in
-// index order, so a draw workgroup waits only for statistics workgroups of
-// lower index (dispatched before it, and they never wait) and for the draw
-// workgroups of its own sequence (dispatched together); with the lag at least
-// the chip's resident window, the statistics it needs have usually finished
-// before it starts, and the draws overlap the streaming of later sequences.
-// With lag = B every draw comes after every statistics workgroup, and the
-// bonus rows are streamed last.
+// The whole chain verify in one launch.  Per sequence there are S = (2K+1) *
+// nchunk statistics workgroups and D = nchunk2 draw workgroups.  The hardware
+// dispatches workgroups in index order, and a draw workgroup waits only for
+// statistics workgroups it needs and for the draw workgroups of its own
+// sequence (dispatched together), so the order of the grid decides how draws
+// overlap streaming.
+//
+// With lag < B: blocks of the statistics of sequence b + lag with the draws of
+// b in one run among them, after a prologue of the first `lag` sequences'
+// statistics and before an epilogue of the last `lag` sequences' draws.  A
+// draw only waits for workgroups of lower index; with the lag at least the
+// chip's resident window, the statistics it needs have usually finished
+// before it starts.
+//
+// With lag = B: the statistics of every row but the bonus rows (target row K,
+// read only by a draw with every draft accepted) come first, sequence by
+// sequence, then the bonus rows, then every draw, so draws after a rejection
+// can start while the bonus rows stream.  (Placing the draws ahead of the
+// bonus rows measured slower.)
 template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_chain_fused(ChainArgs a) {
     __shared__ __align__(16) float lds[kDrawLds];
-    const uint32_t S = (2 * a.K + 1) * a.nchunk, D = a.nchunk2, L = a.lag, B = a.B;
-    const uint32_t g = blockIdx.x, pro = L * S, steady = pro + (B - L) * (S + D);
-    uint32_t b, s;
+    const uint32_t nch = a.nchunk, S = (2 * a.K + 1) * nch, D = a.nchunk2, L = a.lag, B = a.B;
+    const uint32_t g = blockIdx.x;
+    // Decode the workgroup's item: a draw (b, chunk) or statistics (b, row, chunk).
+    uint32_t b, r = 0, ch;
     bool draw;
-    if (g < pro) {
-        b = g / S;
-        s = g - b * S;
-        draw = false;
-    } else if (g < steady) {
-        // Block k: the D draws of sequence k in one run at offset o among the
-        // statistics of sequence L + k; o steps by 8 per block, so the run's
-        // place in each XCD's share of the order rotates.
-        const uint32_t h = g - pro, k = h / (S + D), p = h - k * (S + D);
-        const uint32_t o = (8 * k) % (S + 1);
-        draw = p >= o && p < o + D;
-        b = draw ? k : L + k;
-        s = draw ? p - o : (p < o ? p : p - D);
-    } else {
-        const uint32_t h = g - steady, k = h / D;
-        b = B - L + k;
-        s = h - k * D;
-        draw = true;
-    }
-    if (draw) {
-        draw_item<DT, VecOk, true>(a, static_cast<int>(b), static_cast<int>(s), lds);
-        return;
-    }
-    uint32_t r, ch;
     if (L == B) {
-        // Every draw follows every statistics workgroup: the bonus rows
-        // (target row K, read only by a draw with every draft accepted) are
-        // streamed last, after the other rows of all sequences, so draws
-        // after a rejection can run while they stream.
-        const uint32_t nch = a.nchunk, Sn = S - nch;
-        if (g < B * Sn) {
+        const uint32_t Sn = S - nch, nNB = B * Sn, d0 = nNB + B * nch;
+        draw = g >= d0;
+        if (draw) {
+            b = (g - d0) / D;
+            ch = g - d0 - b * D;
+        } else if (g < nNB) {
             b = g / Sn;
             const uint32_t p = g - b * Sn, rr = p / nch;
             r = rr < static_cast<uint32_t>(a.K) ? rr : rr + 1;
             ch = p - rr * nch;
         } else {
-            const uint32_t h = g - B * Sn;
+            const uint32_t h = g - nNB;
             b = h / nch;
             r = a.K;
             ch = h - b * nch;
         }
     } else {
-        r = s / a.nchunk;
-        ch = s - r * a.nchunk;
+        const uint32_t pro = L * S, steady = pro + (B - L) * (S + D);
+        uint32_t s;
+        if (g < pro) {
+            b = g / S;
+            s = g - b * S;
+            draw = false;
+        } else if (g < steady) {
+            // Block k: the D draws of sequence k in one run at offset o among
+            // the statistics of sequence L + k; o steps by 8 per block, so the
+            // run's place in each XCD's share of the order rotates.
+            const uint32_t h = g - pro, k = h / (S + D), p = h - k * (S + D);
+            const uint32_t o = (8 * k) % (S + 1);
+            draw = p >= o && p < o + D;
+            b = draw ? k : L + k;
+            s = draw ? p - o : (p < o ? p : p - D);
+        } else {
+            const uint32_t h = g - steady, k = h / D;
+            b = B - L + k;
+            s = h - k * D;
+            draw = true;
+        }
+        if (draw) {
+            ch = s;
+        } else {
+            r = s / nch;
+            ch = s - r * nch;
+        }
     }
-    stats_item<DT, 4>(a, b, static_cast<int>(r), static_cast<int>(ch));
+    if (draw)
+        draw_item<DT, VecOk, true>(a, static_cast<int>(b), static_cast<int>(ch), lds);
+    else
+        stats_item<DT, 4>(a, b, static_cast<int>(r), static_cast<int>(ch));
 }
 
 }  // namespace
