@@ -262,6 +262,14 @@ def main():
     achieved_step = (nbytes + io_bytes) / (ms_step * 1e-3) / 1e9
     achieved_dom = nbytes / (ms_dom * 1e-3) / 1e9
     emitted = (gpu_out[1] + 1).sum() if w.mode != "tree" else (gpu_out[2] + 1).sum()
+    # Acceptance on the timed batch (input set 0): mean accepted drafts per
+    # sequence, and for chains the per-token acceptance rate alpha = accepted
+    # / tested (a sequence tests positions up to its first rejection).
+    acc = gpu_out[1] if w.mode != "tree" else gpu_out[2]
+    acceptance = {"mean_accepted": float(np.mean(acc))}
+    if w.mode != "tree":
+        tested = acc + (acc < w.K)
+        acceptance["alpha"] = float(acc.sum() / max(int(tested.sum()), 1))
     config = {"workload": w.name, "mode": w.mode, "B": B, "V": V, "logits": w.dtype,
               "input_sets_rotated": nsets, "logit_bytes_per_step": nbytes}
     if w.mode == "chain":
@@ -288,6 +296,7 @@ def main():
         "frac_of_hbm_peak": achieved_step / HBM_PEAK_GBPS,
         "tokens_verified_per_s": steps_per_s * verified,
         "tokens_emitted_per_s": steps_per_s * float(emitted),
+        "acceptance": acceptance,
         "roofline": {"kernel": dominant_name, "bound": "hbm", "achieved": achieved_dom,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved_dom / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(w.name) if w.mode == "chain" else None,
