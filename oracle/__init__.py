@@ -63,6 +63,8 @@ def _bind(lib):
     lib.oracle_verify_greedy.restype = i
     lib.oracle_verify_tree_greedy.argtypes = [vp, i, i32p, i32p, i, i, i, vp, vp, vp]
     lib.oracle_verify_tree_greedy.restype = i
+    lib.oracle_verify_tree_greedy_dyn.argtypes = [vp, i, i32p, i32p, i32p, i, i, i, vp, vp, vp]
+    lib.oracle_verify_tree_greedy_dyn.restype = i
     return lib
 
 
@@ -219,4 +221,22 @@ def verify_tree_greedy(node_logits, node_tokens, parents, *, lib=None):
                                        _ptr(out_t), _ptr(out_p), _ptr(out_d))
     if rc != 0:
         raise ValueError(f"oracle_verify_tree_greedy rejected its arguments (code {rc})")
+    return out_t, out_p, out_d
+
+
+def verify_tree_greedy_dyn(node_logits, node_tokens, parents, node_count, *, lib=None):
+    """Greedy verify on per-sequence trees -> (tokens [B][Nmax], path [B][Nmax], depth [B])."""
+    lib = lib or load()
+    t, dt = _logits(node_logits)
+    B, Nmax, V = t.shape
+    tok = _i32(node_tokens).reshape(B, Nmax)
+    par = _i32(parents).reshape(B, Nmax)
+    cnt = _i32(node_count).reshape(B)
+    out_t = np.empty((B, Nmax), np.int32)
+    out_p = np.empty((B, Nmax), np.int32)
+    out_d = np.empty((B,), np.int32)
+    rc = lib.oracle_verify_tree_greedy_dyn(_ptr(t), dt, _ptr(tok), _ptr(par), _ptr(cnt), B, Nmax, V,
+                                           _ptr(out_t), _ptr(out_p), _ptr(out_d))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_tree_greedy_dyn rejected its arguments (code {rc})")
     return out_t, out_p, out_d

@@ -503,3 +503,78 @@ int oracle_verify_tree_greedy(const void *node_logits, int dtype, const int32_t 
     free(depth);
     return OR_OK;
 }
+
+/*
+ * Greedy verify on per-sequence candidate trees, T = 0 (French lesson, EAGLE
+ * section: the second version of EAGLE shapes each step's tree to the draft's
+ * confidence, wider where it is unsure; forum post §6).  The verify rule is the
+ * static tree's, applied to each sequence's own tree:
+ *   node_logits [B][Nmax][V], node_tokens [B][Nmax], parents [B][Nmax] and
+ *   node_count [B]: sequence b has nodes 0..n-1 with n = node_count[b],
+ *   1 <= n <= Nmax, parents[b][0] = -1 and 0 <= parents[b][v] < v; rows and
+ *   tokens at v >= n are padding and are not read.
+ * Node v (0 < v < n) matches iff its token equals the argmax of its parent's
+ * row; a node is accepted iff it and all its ancestors match; the deepest
+ * accepted node wins, the lowest node index among equally deep ones.  Output,
+ * each row padded with -1 to Nmax entries:
+ *   out_path [B][Nmax]: node ids root..best (nullable),
+ *   out_tokens [B][Nmax]: tokens of path[1..d], then the argmax at best,
+ *   out_depth [B]: d.
+ */
+int oracle_verify_tree_greedy_dyn(const void *node_logits, int dtype, const int32_t *node_tokens,
+                                  const int32_t *parents, const int32_t *node_count, int B,
+                                  int Nmax, int V, int32_t *out_tokens, int32_t *out_path,
+                                  int32_t *out_depth)
+{
+    if (B < 0 || Nmax < 1 || V < 1 || (dtype != OR_F32 && dtype != OR_BF16))
+        return OR_BAD_ARG;
+    if (B > 0 && (!node_logits || !node_tokens || !parents || !node_count || !out_tokens ||
+                  !out_depth))
+        return OR_BAD_ARG;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parents + (size_t)b * Nmax;
+        const int n = node_count[b];
+        if (n < 1 || n > Nmax || par[0] != -1)
+            return OR_BAD_ARG;
+        for (int v = 1; v < n; ++v)
+            if (par[v] < 0 || par[v] >= v)
+                return OR_BAD_ARG;
+    }
+    int *dep = (int *)malloc(sizeof(int) * (size_t)Nmax * 4);
+    if (!dep)
+        return OR_NO_MEMORY;
+    int *acc = dep + Nmax, *am = dep + 2 * Nmax, *route = dep + 3 * Nmax;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parents + (size_t)b * Nmax;
+        const int32_t *tok = node_tokens + (size_t)b * Nmax;
+        const int n = node_count[b];
+        dep[0] = 0;
+        for (int v = 1; v < n; ++v)
+            dep[v] = dep[par[v]] + 1;
+        for (int v = 0; v < n; ++v)
+            am[v] = row_argmax(node_logits, dtype, (size_t)b * Nmax + (size_t)v, V);
+        acc[0] = 1;
+        for (int v = 1; v < n; ++v)
+            acc[v] = acc[par[v]] && tok[v] == am[par[v]];
+        int top = 0;
+        for (int v = 1; v < n; ++v)
+            if (acc[v] && dep[v] > dep[top])
+                top = v;
+        const int d = dep[top];
+        for (int v = top, i = d; i >= 0; --i) {
+            route[i] = v;
+            v = par[v];
+        }
+        int32_t *ot = out_tokens + (size_t)b * Nmax;
+        for (int i = 0; i < Nmax; ++i)
+            ot[i] = i < d ? tok[route[i + 1]] : (i == d ? am[top] : -1);
+        if (out_path) {
+            int32_t *op = out_path + (size_t)b * Nmax;
+            for (int i = 0; i < Nmax; ++i)
+                op[i] = i <= d ? route[i] : -1;
+        }
+        out_depth[b] = d;
+    }
+    free(dep);
+    return OR_OK;
+}

@@ -423,6 +423,82 @@ def pin_tree_figure(lib):
         assert list(out_t[0, :d + 1]) == case["emitted"], case["name"]
 
 
+def _dyn_case(rng, B, Nmax, V, dtype, p_match=0.7):
+    """Per-sequence random trees (parents[b][v] uniform below v), ragged node
+    counts, small-integer logits (ties likely), padding rows and tokens filled
+    with noise that must not be read."""
+    counts = rng.integers(1, Nmax + 1, size=B).astype(np.int32)
+    parents = np.full((B, Nmax), 7, np.int32)
+    for b in range(B):
+        parents[b, 0] = -1
+        for v in range(1, counts[b]):
+            parents[b, v] = rng.integers(0, v)
+    vals = (rng.integers(-2, 3, size=(B, Nmax, V)) * 0.5).astype(np.float32)
+    logits = bf16_bits(vals) if dtype == "bf16" else vals
+    amax = np.argmax(widen(logits), axis=-1)
+    tokens = rng.integers(0, V, size=(B, Nmax)).astype(np.int32)
+    for b in range(B):
+        for v in range(1, counts[b]):
+            if rng.random() < p_match:
+                tokens[b, v] = amax[b, parents[b, v]]
+    return logits, tokens, parents, counts
+
+
+def pin_tree_dyn_bruteforce(lib, seed=23):
+    """Per-sequence trees against the brute-force path enumeration of each
+    sequence's own tree; outputs padded with -1 to Nmax."""
+    rng = np.random.default_rng(seed)
+    for trial in range(60):
+        Nmax, B, V = int(rng.integers(1, 20)), 5, 6
+        dtype = "bf16" if trial % 2 else "f32"
+        logits, tokens, parents, counts = _dyn_case(rng, B, Nmax, V, dtype)
+        out_t, out_p, out_d = oracle.verify_tree_greedy_dyn(logits, tokens, parents, counts, lib=lib)
+        for b in range(B):
+            n = counts[b]
+            path, toks = tree_bruteforce(widen(logits[b, :n]), tokens[b, :n], list(parents[b, :n]))
+            d = len(path) - 1
+            assert out_d[b] == d, (trial, b, out_d[b], path)
+            assert list(out_p[b, :d + 1]) == path and np.all(out_p[b, d + 1:] == -1)
+            assert list(out_t[b, :d + 1]) == toks and np.all(out_t[b, d + 1:] == -1)
+
+
+def pin_tree_dyn_padding(lib, seed=29):
+    """Rows, tokens and parents past a sequence's node count are never read:
+    rewriting them leaves every output unchanged."""
+    rng = np.random.default_rng(seed)
+    for trial in range(20):
+        Nmax, B, V = 12, 6, 5
+        logits, tokens, parents, counts = _dyn_case(rng, B, Nmax, V, "f32")
+        ref = oracle.verify_tree_greedy_dyn(logits, tokens, parents, counts, lib=lib)
+        l2, t2, p2 = logits.copy(), tokens.copy(), parents.copy()
+        for b in range(B):
+            n = counts[b]
+            l2[b, n:] = rng.integers(-9, 9, size=l2[b, n:].shape)
+            t2[b, n:] = rng.integers(0, V, size=Nmax - n)
+            p2[b, n:] = rng.integers(-5, 50, size=Nmax - n)
+        out = oracle.verify_tree_greedy_dyn(l2, t2, p2, counts, lib=lib)
+        assert all(np.array_equal(x, y) for x, y in zip(ref, out)), trial
+
+
+def pin_tree_dyn_chain(lib, seed=31):
+    """A per-sequence chain of n nodes (parents v - 1) is the greedy chain with
+    K = n - 1 drafts over that sequence's first n rows."""
+    rng = np.random.default_rng(seed)
+    Nmax, V = 7, 11
+    for trial in range(40):
+        n = int(rng.integers(1, Nmax + 1))
+        vals = (rng.integers(-3, 4, size=(1, Nmax, V)) * 0.5).astype(np.float32)
+        amax = np.argmax(vals, axis=-1)
+        x = np.where(rng.random(n - 1) < 0.75, amax[0, :n - 1], rng.integers(0, V, n - 1)).astype(np.int32)
+        parents = np.full((1, Nmax), 0, np.int32)
+        parents[0, :n] = [-1] + list(range(n - 1))
+        tokens = np.zeros((1, Nmax), np.int32)
+        tokens[0, 1:n] = x
+        t_t, _, t_d = oracle.verify_tree_greedy_dyn(vals, tokens, parents, np.array([n], np.int32), lib=lib)
+        g_t, g_a = oracle.verify_greedy(vals[:, :n], x[None], lib=lib)
+        assert t_d[0] == g_a[0] and np.array_equal(t_t[0, :n], g_t[0]) and np.all(t_t[0, n:] == -1)
+
+
 # ------------------------------------------------------------- chi-square
 
 def pin_chi_square(lib, n=50_000, seed=19):
@@ -452,4 +528,5 @@ def pin_chi_square(lib, n=50_000, seed=19):
 ALL_PINS = [pin_exact_law, pin_expected_tokens, pin_page_counts, pin_strict_acceptance,
             pin_softmax_values, pin_helper_closed_forms,
             pin_inverse_cdf, pin_greedy, pin_tree_bruteforce, pin_tree_chain,
-            pin_tree_figure, pin_chi_square]
+            pin_tree_figure, pin_tree_dyn_bruteforce, pin_tree_dyn_padding, pin_tree_dyn_chain,
+            pin_chi_square]

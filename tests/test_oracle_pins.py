@@ -83,6 +83,14 @@ MUTANTS = [
     ("tree ties to the highest index", "if (ok[v] && depth[v] > depth[best])",
      "if (ok[v] && depth[v] >= depth[best])", 0),
     ("tree ignores ancestors", "ok[v] = ok[parents[v]] &&", "ok[v] = 1 &&", 0),
+    ("per-sequence tree compares with the node's own argmax", "tok[v] == am[par[v]];",
+     "tok[v] == am[v];", 0),
+    ("per-sequence tree ties to the highest index", "if (acc[v] && dep[v] > dep[top])",
+     "if (acc[v] && dep[v] >= dep[top])", 0),
+    ("per-sequence tree ignores ancestors", "acc[v] = acc[par[v]] &&", "acc[v] = 1 &&", 0),
+    ("per-sequence tree rows strided by the node count",
+     "row_argmax(node_logits, dtype, (size_t)b * Nmax + (size_t)v, V);",
+     "row_argmax(node_logits, dtype, (size_t)b * n + (size_t)v, V);", 0),
     ("acceptance rate takes the larger mass", "a += p[i] < q[i] ? p[i] : q[i];",
      "a += p[i] < q[i] ? q[i] : p[i];", 0),
     ("draw weights keep the negative part", "            out_w[i] = d > 0.0 ? d : 0.0;",
@@ -92,7 +100,7 @@ MUTANTS = [
 QUICK_PINS = [P.pin_exact_law, P.pin_expected_tokens, P.pin_page_counts, P.pin_strict_acceptance,
               P.pin_softmax_values, P.pin_helper_closed_forms,
               P.pin_inverse_cdf, P.pin_greedy, P.pin_tree_bruteforce, P.pin_tree_figure,
-              P.pin_chi_square]
+              P.pin_tree_dyn_bruteforce, P.pin_tree_dyn_padding, P.pin_chi_square]
 
 
 def _mutant_lib(tmpdir, pattern, repl, which):
