@@ -60,12 +60,17 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-def set_bytes(w) -> int:
+def set_bytes(w, inputs=None) -> int:
+    """Logit bytes one step reads (every row once).  Per-sequence trees read
+    only their trees' rows: their node counts when `inputs` are given, else
+    the bound of Nmax rows per sequence."""
     esize = 2 if w.dtype == "bf16" else 4
     if w.mode == "chain":
         rows = w.B * (2 * w.K + 1)
     elif w.mode == "greedy":
         rows = w.B * (w.K + 1)
+    elif w.mode == "tree_dyn":
+        rows = int(inputs["node_count"].sum()) if inputs is not None else w.B * w.K
     else:
         rows = w.B * (1 + sum(int(np.prod(w.branching[:i + 1])) for i in range(len(w.branching))))
     return rows * w.V * esize
@@ -78,6 +83,9 @@ def oracle_step(w, inp):
                                    inp["u_sample"], inp["T"])
     if w.mode == "greedy":
         return oracle.verify_greedy(inp["target"], inp["tokens"])
+    if w.mode == "tree_dyn":
+        return oracle.verify_tree_greedy_dyn(inp["node_logits"], inp["node_tokens"], inp["parents"],
+                                             inp["node_count"])
     return oracle.verify_tree_greedy(inp["node_logits"], inp["node_tokens"], inp["parents"])
 
 
@@ -87,6 +95,8 @@ def check(w, inp, gpu_out):
         return parity.check_chain(inp, *gpu_out)
     if w.mode == "greedy":
         return parity.check_greedy(inp, *gpu_out)
+    if w.mode == "tree_dyn":
+        return parity.check_tree_dyn(inp, *gpu_out)
     return parity.check_tree(inp, *gpu_out)
 
 
@@ -143,10 +153,15 @@ def main():
     w = W.WORKLOADS[args.workload]
     B, V = w.B, w.V
     nbytes = set_bytes(w)
-    nsets = args.rotate or max(1, -(-512_000_000 // nbytes))
+    # Per-sequence trees hold 5/8 of Nmax nodes on average (counts uniform in
+    # [Nmax/4, Nmax]).
+    est = nbytes * 5 // 8 if w.mode == "tree_dyn" else nbytes
+    nsets = args.rotate or max(1, -(-512_000_000 // est))
     device = torch.device("cuda:0")
     print(f"[bench] generating {nsets} input sets of {w.name}", file=sys.stderr, flush=True)
     host_sets = [W.make_inputs(w, s) for s in range(nsets)]
+    if w.mode == "tree_dyn":  # the mean over the rotated sets, each timed equally often
+        nbytes = int(round(np.mean([set_bytes(w, h) for h in host_sets])))
     sets = [{k: to_dev(v, device) for k, v in h.items() if isinstance(v, np.ndarray)}
             for h in host_sets]
     stream = torch.cuda.current_stream(device)
@@ -199,6 +214,29 @@ def main():
         dominant_name = "k_greedy (whole step)"
         io_bytes = 4 * B * K + 4 * B * (K + 2)
         verified = B * K
+    elif w.mode == "tree_dyn":
+        Nmax = w.K
+        ws = sv.workspace(sv.SPEC_MODE_TREE_DYN, B, Nmax, V, dt_code, device)
+        out_t = torch.empty((B, Nmax), dtype=torch.int32, device=device)
+        out_p = torch.empty((B, Nmax), dtype=torch.int32, device=device)
+        out_d = torch.empty((B,), dtype=torch.int32, device=device)
+
+        def step(i):
+            s = sets[i % nsets]
+            sv.spec_verify_tree_greedy_dyn(s["node_logits"], s["node_tokens"], s["parents"],
+                                           s["node_count"], out_tokens=out_t, out_path=out_p,
+                                           out_depth=out_d, workspace_buf=ws, stream=stream)
+        stats_phase = None
+
+        def outputs():
+            s = sets[0]
+            tok, path, depth = sv.spec_verify_tree_greedy_dyn(s["node_logits"], s["node_tokens"],
+                                                              s["parents"], s["node_count"])
+            torch.cuda.synchronize()
+            return tok.cpu().numpy(), path.cpu().numpy(), depth.cpu().numpy()
+        dominant_name = "k_tree_dyn (whole step)"
+        io_bytes = 4 * B * Nmax * 2 + 4 * B + 4 * B * (2 * Nmax + 1)
+        verified = float(np.mean([(h["node_count"] - 1).sum() for h in host_sets]))
     else:
         par = host_sets[0]["parents"]
         N = len(par)
@@ -261,13 +299,14 @@ def main():
     steps_per_s = 1e3 / ms_step
     achieved_step = (nbytes + io_bytes) / (ms_step * 1e-3) / 1e9
     achieved_dom = nbytes / (ms_dom * 1e-3) / 1e9
-    emitted = (gpu_out[1] + 1).sum() if w.mode != "tree" else (gpu_out[2] + 1).sum()
+    is_tree = w.mode in ("tree", "tree_dyn")
+    emitted = (gpu_out[2] + 1).sum() if is_tree else (gpu_out[1] + 1).sum()
     # Acceptance on the timed batch (input set 0): mean accepted drafts per
     # sequence, and for chains the per-token acceptance rate alpha = accepted
     # / tested (a sequence tests positions up to its first rejection).
-    acc = gpu_out[1] if w.mode != "tree" else gpu_out[2]
+    acc = gpu_out[2] if is_tree else gpu_out[1]
     acceptance = {"mean_accepted": float(np.mean(acc))}
-    if w.mode != "tree":
+    if not is_tree:
         tested = acc + (acc < w.K)
         acceptance["alpha"] = float(acc.sum() / max(int(tested.sum()), 1))
     config = {"workload": w.name, "mode": w.mode, "B": B, "V": V, "logits": w.dtype,
@@ -276,6 +315,8 @@ def main():
         config.update(K=w.K, T=w.T)
     elif w.mode == "greedy":
         config.update(K=w.K)
+    elif w.mode == "tree_dyn":
+        config.update(Nmax=w.K, mean_nodes=float(np.mean([h["node_count"].mean() for h in host_sets])))
     else:
         config.update(branching=list(w.branching))
     line = {

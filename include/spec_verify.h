@@ -59,7 +59,8 @@ typedef enum {
 typedef enum {
     SPEC_MODE_CHAIN = 0,  /* spec_verify_chain (T > 0)           */
     SPEC_MODE_GREEDY = 1, /* spec_verify_greedy (T = 0, chain)   */
-    SPEC_MODE_TREE = 2    /* spec_verify_tree_greedy (T = 0)     */
+    SPEC_MODE_TREE = 2,   /* spec_verify_tree_greedy (T = 0)     */
+    SPEC_MODE_TREE_DYN = 3 /* spec_verify_tree_greedy_dyn (T = 0) */
 } spec_mode;
 
 typedef enum {
@@ -76,8 +77,9 @@ typedef enum {
 #define SPEC_VERIFY_MAX_CHAIN_V_F32 (1 << 18)   /* chain verify vocabulary limit, fp32 logits */
 
 /*
- * Workspace size for one call.  K_or_N is K for the chain and greedy modes
- * and N (nodes, root included) for the tree mode.  Pure host arithmetic.
+ * Workspace size for one call.  K_or_N is K for the chain and greedy modes,
+ * N (nodes, root included) for the tree mode and Nmax for the per-sequence
+ * tree mode.  Pure host arithmetic.
  * Returns SPEC_ERR_INVALID_ARG (and leaves *bytes alone) for sizes the entry
  * point would reject.
  */
@@ -205,6 +207,40 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
                                     int32_t B, int32_t N, int32_t V, int32_t *out_tokens,
                                     int32_t *out_path, int32_t *out_depth, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Greedy verify on per-sequence candidate trees, T = 0 (French lesson, EAGLE
+ * section: the second version of EAGLE shapes each step's tree to the draft's
+ * confidence; forum post §6).  The rule of spec_verify_tree_greedy, applied to
+ * each sequence's own tree:
+ *
+ *   node_logits [B][Nmax][V]  row v of sequence b is the target's distribution
+ *                             after the path root..v of b's tree.
+ *   node_tokens [B][Nmax]     int32 token of node v; column 0 (the root) unused.
+ *   parents     [B][Nmax]     DEVICE pointer, int32: parents[b][0] = -1 and
+ *                             0 <= parents[b][v] < v for v < node_count[b].
+ *   node_count  [B]           DEVICE pointer, int32: 1 <= node_count[b] <= Nmax.
+ *   1 <= Nmax <= SPEC_VERIFY_MAX_TREE_NODES, 1 <= V <= SPEC_VERIFY_MAX_V.
+ * Rows, tokens and parents at v >= node_count[b] are padding and are not read.
+ * Outputs, each row padded with -1 to Nmax entries:
+ *   out_tokens [B][Nmax]   tokens of the accepted path's nodes below the root,
+ *                          then the argmax of the last node's row.
+ *   out_path   nullable [B][Nmax]  node ids root..last.
+ *   out_depth  [B]         accepted depth d (out_tokens holds d+1 tokens).
+ *
+ * The tree arrays live on the device, so they are not checked on the host: a
+ * node count is clamped to [1, Nmax], and a node whose parent entry is out of
+ * range is never accepted (nor is its subtree); no entry outside the arrays
+ * is read.  One kernel launch; each tree's resolve waits (bounded, about 2 s)
+ * for the argmax workgroups of its node rows; if a wait ever ran out, the tree
+ * gets out_depth[b] = -1 and out_tokens[b], out_path[b] all -1.
+ */
+spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtype,
+                                        const int32_t *node_tokens, const int32_t *parents,
+                                        const int32_t *node_count, int32_t B, int32_t Nmax,
+                                        int32_t V, int32_t *out_tokens, int32_t *out_path,
+                                        int32_t *out_depth, void *workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
 const char *spec_verify_status_string(spec_status status);

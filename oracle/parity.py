@@ -21,7 +21,7 @@ from collections import Counter
 
 import numpy as np
 
-from . import draw_weights, verify_chain, verify_greedy, verify_tree_greedy
+from . import draw_weights, verify_chain, verify_greedy, verify_tree_greedy, verify_tree_greedy_dyn
 
 REL = 1e-5
 RATIO_BAND = 1e-6
@@ -121,4 +121,25 @@ def check_tree(inp: dict, gpu_tokens, gpu_path, gpu_depth, seqs=None) -> Counter
             bad.append(f"seq {b}: gpu {g_tok[i].tolist()} depth {g_depth[i]} "
                        f"oracle {o_tok[i].tolist()} depth {o_depth[i]}")
     assert not bad, "tree parity violations:\n" + "\n".join(bad[:20])
+    return Counter(sequences=len(seqs), exact=len(seqs))
+
+
+def check_tree_dyn(inp: dict, gpu_tokens, gpu_path, gpu_depth, seqs=None) -> Counter:
+    """Per-sequence trees: depth, tokens and path exactly equal to the oracle's
+    (argmax ties go to the lowest index, so the result is unique)."""
+    B = inp["node_logits"].shape[0]
+    seqs = np.arange(B) if seqs is None else np.asarray(seqs)
+    o_tok, o_path, o_depth = verify_tree_greedy_dyn(inp["node_logits"][seqs], inp["node_tokens"][seqs],
+                                                    inp["parents"][seqs], inp["node_count"][seqs])
+    g_tok, g_depth = np.asarray(gpu_tokens)[seqs], np.asarray(gpu_depth)[seqs]
+    g_path = None if gpu_path is None else np.asarray(gpu_path)[seqs]
+    bad = []
+    for i, b in enumerate(seqs):
+        same = g_depth[i] == o_depth[i] and np.array_equal(g_tok[i], o_tok[i])
+        if g_path is not None:
+            same = same and np.array_equal(g_path[i], o_path[i])
+        if not same:
+            bad.append(f"seq {b}: gpu {g_tok[i].tolist()} depth {g_depth[i]} "
+                       f"oracle {o_tok[i].tolist()} depth {o_depth[i]}")
+    assert not bad, "per-sequence tree parity violations:\n" + "\n".join(bad[:20])
     return Counter(sequences=len(seqs), exact=len(seqs))

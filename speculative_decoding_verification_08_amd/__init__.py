@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "spec_verify.h")
 
 SPEC_DTYPE_F32, SPEC_DTYPE_BF16 = 0, 1
-SPEC_MODE_CHAIN, SPEC_MODE_GREEDY, SPEC_MODE_TREE = 0, 1, 2
+SPEC_MODE_CHAIN, SPEC_MODE_GREEDY, SPEC_MODE_TREE, SPEC_MODE_TREE_DYN = 0, 1, 2, 3
 SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_LAUNCH = 0, 1, 2, 3
 MAX_K, MAX_TREE_NODES, MAX_V = 64, 256, 1 << 26
 MAX_CHAIN_V_BF16, MAX_CHAIN_V_F32 = 1 << 19, 1 << 18
@@ -52,8 +52,11 @@ def _load(path: str = LIB_PATH):
     lib.spec_verify_greedy.argtypes = [vp, ctypes.c_int, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.spec_verify_tree_greedy.argtypes = [vp, ctypes.c_int, vp, vp, i32, i32, i32, vp, vp, vp,
                                             vp, sz, vp]
+    lib.spec_verify_tree_greedy_dyn.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, vp, vp,
+                                                vp, vp, sz, vp]
     for fn in ("spec_verify_workspace_bytes", "spec_verify_chain", "spec_verify_chain_stats",
-               "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy"):
+               "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy",
+               "spec_verify_tree_greedy_dyn"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -265,4 +268,31 @@ def spec_verify_tree_greedy(node_logits, node_tokens, parents, *, with_path=True
     _call("spec_verify_tree_greedy", _ptr(node_logits), dt, _ptr(node_tokens), par, B, N, V,
           _ptr(out_tokens), _ptr(out_path), _ptr(out_depth), _ptr(workspace_buf),
           workspace_buf.numel(), _stream(dev, stream))
+    return out_tokens, out_path, out_depth
+
+
+def spec_verify_tree_greedy_dyn(node_logits, node_tokens, parents, node_count, *, with_path=True,
+                                out_tokens=None, out_path=None, out_depth=None, workspace_buf=None,
+                                stream=None):
+    """Greedy verify on per-sequence trees (T = 0).  `parents` [B][Nmax] and
+    `node_count` [B] are int32 device tensors.  Returns (tokens [B][Nmax],
+    path [B][Nmax] or None, depth [B]), rows padded with -1."""
+    _check_dev("node_logits", node_logits)
+    dt = _dtype_code(node_logits)
+    B, Nmax, V = node_logits.shape
+    _check_dev("node_tokens", node_tokens, torch.int32, (B, Nmax))
+    _check_dev("parents", parents, torch.int32, (B, Nmax))
+    _check_dev("node_count", node_count, torch.int32, (B,))
+    dev = node_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, Nmax), dtype=torch.int32, device=dev)
+    if out_path is None and with_path:
+        out_path = torch.empty((B, Nmax), dtype=torch.int32, device=dev)
+    if out_depth is None:
+        out_depth = torch.empty((B,), dtype=torch.int32, device=dev)
+    if workspace_buf is None:
+        workspace_buf = workspace(SPEC_MODE_TREE_DYN, B, Nmax, V, dt, dev)
+    _call("spec_verify_tree_greedy_dyn", _ptr(node_logits), dt, _ptr(node_tokens), _ptr(parents),
+          _ptr(node_count), B, Nmax, V, _ptr(out_tokens), _ptr(out_path), _ptr(out_depth),
+          _ptr(workspace_buf), workspace_buf.numel(), _stream(dev, stream))
     return out_tokens, out_path, out_depth

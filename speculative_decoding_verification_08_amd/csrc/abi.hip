@@ -28,7 +28,8 @@ bool valid_dtype(spec_dtype d) { return d == SPEC_DTYPE_F32 || d == SPEC_DTYPE_B
 
 bool valid_sizes(spec_mode mode, int32_t B, int32_t KN, int32_t V) {
     if (B < 0 || V < 1 || V > SPEC_VERIFY_MAX_V) return false;
-    if (mode == SPEC_MODE_TREE) return KN >= 1 && KN <= SPEC_VERIFY_MAX_TREE_NODES;
+    if (mode == SPEC_MODE_TREE || mode == SPEC_MODE_TREE_DYN)
+        return KN >= 1 && KN <= SPEC_VERIFY_MAX_TREE_NODES;
     return KN >= 0 && KN <= SPEC_VERIFY_MAX_K;
 }
 
@@ -162,7 +163,8 @@ const char *spec_verify_status_string(spec_status status) {
 spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_N, int32_t V,
                                         spec_dtype dtype, size_t *bytes) {
     if (!bytes || !valid_dtype(dtype)) return SPEC_ERR_INVALID_ARG;
-    if (mode != SPEC_MODE_CHAIN && mode != SPEC_MODE_GREEDY && mode != SPEC_MODE_TREE)
+    if (mode != SPEC_MODE_CHAIN && mode != SPEC_MODE_GREEDY && mode != SPEC_MODE_TREE &&
+        mode != SPEC_MODE_TREE_DYN)
         return SPEC_ERR_INVALID_ARG;
     Plan p;
     if (!make_plan(mode, B, K_or_N, V, dtype, p)) return SPEC_ERR_INVALID_ARG;
@@ -298,6 +300,42 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
     t.out_path = out_path;
     t.out_depth = out_depth;
     return launch_status(launch_tree(t, dtype, stream));
+}
+
+spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtype,
+                                        const int32_t *node_tokens, const int32_t *parents,
+                                        const int32_t *node_count, int32_t B, int32_t Nmax,
+                                        int32_t V, int32_t *out_tokens, int32_t *out_path,
+                                        int32_t *out_depth, void *workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return SPEC_ERR_INVALID_ARG;
+    Plan plan;
+    if (!make_plan(SPEC_MODE_TREE_DYN, B, Nmax, V, dtype, plan)) return SPEC_ERR_INVALID_ARG;
+    if (B == 0) return SPEC_OK;
+    if (!node_logits || !aligned(node_logits, 16)) return SPEC_ERR_INVALID_ARG;
+    if (!node_tokens || !parents || !node_count || !out_tokens || !out_depth ||
+        !aligned(node_tokens, 4) || !aligned(parents, 4) || !aligned(node_count, 4) ||
+        !aligned(out_tokens, 4) || !aligned(out_depth, 4) || (out_path && !aligned(out_path, 4)))
+        return SPEC_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 16))
+        return SPEC_ERR_WORKSPACE;
+    TreeDynArgs t;
+    t.am.logits = node_logits;
+    t.am.rows = plan.rows;
+    t.am.V = V;
+    t.am.chunk = plan.chunk;
+    t.am.nchunk = plan.nchunk;
+    t.am.tag = next_call_tag();
+    t.am.partial = at<uint64_t>(workspace, plan.off_partial);
+    t.tokens = node_tokens;
+    t.parents = parents;
+    t.node_count = node_count;
+    t.B = B;
+    t.Nmax = Nmax;
+    t.out_tokens = out_tokens;
+    t.out_path = out_path;
+    t.out_depth = out_depth;
+    return launch_status(launch_tree_dyn(t, dtype, stream));
 }
 
 }  // extern "C"

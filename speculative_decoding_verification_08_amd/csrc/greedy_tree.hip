@@ -297,6 +297,97 @@ __device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, int b) {
     if (v == 0) a.out_depth[b] = d;
 }
 
+// Tree b of a batch of per-sequence trees: n = node_count[b] (clamped to
+// [1, Nmax]) nodes with parents[b][v] < v; the static tree's rule on that
+// tree.  A node whose parent entry is out of range is unattached: neither it
+// nor its subtree is accepted, and nothing outside the tree is read.  Depths
+// and acceptance are both folded by pointer jumping, ceil(log2 n) steps.
+__device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, int b) {
+    __shared__ int32_t s_a[kMaxTreeNodes];
+    __shared__ int s_ok[kMaxTreeNodes], s_anc[kMaxTreeNodes], s_dep[kMaxTreeNodes];
+    __shared__ int s_par[kMaxTreeNodes], s_path[kMaxTreeNodes];
+    __shared__ int s_best;
+    static_assert(kMaxTreeNodes == kWG, "one thread per node");
+    const int v = threadIdx.x, Nmax = a.Nmax, nch = a.am.nchunk;
+    const int64_t row0 = static_cast<int64_t>(b) * Nmax;
+    const int n = min(max(a.node_count[b], 1), Nmax);
+    const int32_t tok = v < n ? a.tokens[row0 + v] : 0;
+    int par = v < n ? a.parents[row0 + v] : -1;
+    const bool valid = v > 0 && v < n && par >= 0 && par < v;
+    if (!valid) par = -1;
+    const uint64_t *part = a.am.partial + 2 * row0 * nch;
+    if (!merge_argmax(part, n, nch, a.am.tag, s_a)) {
+        if (v < Nmax) {
+            a.out_tokens[row0 + v] = -1;
+            if (a.out_path) a.out_path[row0 + v] = -1;
+        }
+        if (v == 0) a.out_depth[b] = -1;
+        return;
+    }
+    if (v < n) {
+        s_ok[v] = v == 0 ? 1 : (valid && tok == s_a[max(par, 0)]);
+        s_anc[v] = par;
+        s_dep[v] = v == 0 ? 0 : 1;
+        s_par[v] = par;
+    }
+    __syncthreads();
+    for (int step = 1; step < n; step <<= 1) {
+        int ok = 0, anc = -1, dep = 0;
+        if (v < n) {
+            anc = s_anc[v];
+            ok = s_ok[v];
+            dep = s_dep[v];
+            if (anc >= 0) {
+                ok &= s_ok[anc];
+                dep += s_dep[anc];
+                anc = s_anc[anc];
+            }
+        }
+        __syncthreads();
+        if (v < n) {
+            s_ok[v] = ok;
+            s_anc[v] = anc;
+            s_dep[v] = dep;
+        }
+        __syncthreads();
+    }
+    // Deepest accepted node, lowest index among equals (the root always is).
+    const int key = (v < n && s_ok[v]) ? ((s_dep[v] << 16) | (0xFFFF - v)) : -1;
+    const int best_key = max_wg(key);
+    if (v == 0) {
+        const int best = 0xFFFF - (best_key & 0xFFFF);
+        s_best = best;
+        int node = best;
+        for (int i = s_dep[best]; i >= 0; --i) {
+            s_path[i] = node;
+            node = s_par[node];
+        }
+    }
+    __syncthreads();
+    const int best = s_best, d = s_dep[best];
+    if (v < Nmax) {
+        int32_t o = -1;
+        if (v < d) o = a.tokens[row0 + s_path[v + 1]];
+        else if (v == d) o = s_a[best];
+        a.out_tokens[row0 + v] = o;
+        if (a.out_path) a.out_path[row0 + v] = v <= d ? s_path[v] : -1;
+    }
+    if (v == 0) a.out_depth[b] = d;
+}
+
+template <class DT>
+__global__ __launch_bounds__(kWG) void k_tree_dyn(TreeDynArgs a) {
+    const uint32_t nam = static_cast<uint32_t>(a.am.rows) * a.am.nchunk, g = blockIdx.x;
+    if (g < nam) {
+        const uint32_t row = g / a.am.nchunk, b = row / a.Nmax, v = row - b * a.Nmax;
+        // Rows past the tree's node count are padding: not read.
+        if (v >= static_cast<uint32_t>(min(max(a.node_count[b], 1), a.Nmax))) return;
+        argmax_item<DT, 4>(a.am, row, static_cast<int>(g - row * a.am.nchunk));
+    } else {
+        tree_dyn_resolve_item(a, static_cast<int>(g - nam));
+    }
+}
+
 template <class DT>
 __global__ __launch_bounds__(kWG) void k_greedy(GreedyArgs a) {
     const uint32_t nam = static_cast<uint32_t>(a.am.rows) * a.am.nchunk, g = blockIdx.x;
@@ -332,6 +423,13 @@ hipError_t launch_tree(const TreeArgs &a, int dtype, hipStream_t s) {
     const dim3 g(static_cast<uint32_t>(a.am.rows * a.am.nchunk + a.B)), blk(kWG);
     if (dtype == 1) k_tree<Bf16><<<g, blk, 0, s>>>(a);
     else k_tree<F32><<<g, blk, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_dyn(const TreeDynArgs &a, int dtype, hipStream_t s) {
+    const dim3 g(static_cast<uint32_t>(a.am.rows * a.am.nchunk + a.B)), blk(kWG);
+    if (dtype == 1) k_tree_dyn<Bf16><<<g, blk, 0, s>>>(a);
+    else k_tree_dyn<F32><<<g, blk, 0, s>>>(a);
     return hipGetLastError();
 }
 

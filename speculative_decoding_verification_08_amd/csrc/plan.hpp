@@ -102,11 +102,26 @@ struct TreeArgs {
     TreeShape tree;
 };
 
+// Greedy verify on per-sequence trees in one launch: the argmax workgroups of
+// node rows [B][Nmax] (rows past a tree's node count skip), then one resolve
+// workgroup per tree.
+struct TreeDynArgs {
+    ArgmaxArgs am;
+    const int32_t *tokens;      // [B][Nmax]
+    const int32_t *parents;     // [B][Nmax]
+    const int32_t *node_count;  // [B]
+    int32_t B, Nmax;
+    int32_t *out_tokens;        // [B][Nmax]
+    int32_t *out_path;          // nullable [B][Nmax]
+    int32_t *out_depth;         // [B]
+};
+
 // Host launchers (defined next to their kernels).
 hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s);
 hipError_t launch_chain_draw(const ChainArgs &a, int dtype, hipStream_t s);
 hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s);
 hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t s);
 hipError_t launch_tree(const TreeArgs &a, int dtype, hipStream_t s);
+hipError_t launch_tree_dyn(const TreeDynArgs &a, int dtype, hipStream_t s);
 
 }  // namespace sv

@@ -338,3 +338,85 @@ def test_tree_full_size_128k(sv):
         g = run_tree(sv, d)
         parity.check_tree(d, *g)
         print("tree_128k mean depth", g[2].mean())
+
+
+# ------------------------------------------------------------------ per-sequence trees
+
+def run_tree_dyn(sv, d):
+    tok, path, depth = sv.spec_verify_tree_greedy_dyn(dev(d["node_logits"]), dev(d["node_tokens"]),
+                                                      dev(d["parents"]), dev(d["node_count"]))
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), path.cpu().numpy(), depth.cpu().numpy()
+
+
+def test_tree_dyn_random_shapes(sv):
+    for trial in range(12):
+        Nmax = [1, 2, 9, 64, 130, 256][trial % 6]
+        dtype = "bf16" if trial % 2 else "f32"
+        V = [1, 100, 2053, 16384][trial % 4]
+        w = W.Workload("td", 94, "tree_dyn", B=6, K=Nmax, V=V, dtype=dtype, recipe="peaked")
+        case(f"per-sequence trees trial {trial} Nmax={Nmax} V={V} {dtype}")
+        d = W.tree_dyn_inputs(w, trial, p_match=0.85, nmin=1)
+        parity.check_tree_dyn(d, *run_tree_dyn(sv, d))
+
+
+def test_tree_dyn_shared_tree_equals_static(sv):
+    """Every sequence with the same full tree: the static entry point's result."""
+    w = W.Workload("t", 95, "tree", B=7, V=5003, dtype="bf16", recipe="peaked",
+                   branching=(3, 2, 2))
+    d = W.tree_inputs(w, 0, p_match=0.8)
+    N = len(d["parents"])
+    par = np.tile(d["parents"], (7, 1)).astype(np.int32)
+    cnt = np.full(7, N, np.int32)
+    case("per-sequence trees, one shared tree")
+    s_tok, s_path, s_depth = run_tree(sv, d)
+    tok, path, depth = sv.spec_verify_tree_greedy_dyn(dev(d["node_logits"]), dev(d["node_tokens"]),
+                                                      dev(par), dev(cnt))
+    torch.cuda.synchronize()
+    tok, path, depth = tok.cpu().numpy(), path.cpu().numpy(), depth.cpu().numpy()
+    D = s_tok.shape[1] - 1
+    assert np.array_equal(depth, s_depth)
+    assert np.array_equal(tok[:, :D + 1], s_tok) and np.all(tok[:, D + 1:] == -1)
+    assert np.array_equal(path[:, :D + 1], s_path) and np.all(path[:, D + 1:] == -1)
+
+
+def test_tree_dyn_out_of_range_entries(sv):
+    """Tree arrays live on the device and are not checked on the host: a node
+    count is clamped to [1, Nmax] and a node whose parent is out of range is
+    never accepted, nor is its subtree.  Expected: the oracle on the same trees
+    with each such node re-attached to the root and given a token that matches
+    nothing."""
+    w = W.Workload("td", 96, "tree_dyn", B=8, K=24, V=777, dtype="f32", recipe="peaked")
+    d = W.tree_dyn_inputs(w, 0, p_match=1.0, nmin=8)
+    par, cnt, tok = d["parents"].copy(), d["node_count"].copy(), d["node_tokens"].copy()
+    cnt[0], cnt[1] = 0, 999          # clamped to 1 and to Nmax
+    par[1, 1:] = np.maximum(par[1, 1:], 0)
+    par[1, 0] = -1
+    bad = {2: 5, 3: 1, 4: 7}         # node -> out-of-range parent (>= v or negative)
+    exp_par, exp_tok = par.copy(), tok.copy()
+    for b, v in bad.items():
+        par[b, v] = v if b != 3 else -3
+        exp_par[b, v] = 0
+        exp_tok[b, v] = -1
+    exp_cnt = np.clip(cnt, 1, w.K).astype(np.int32)
+    # sequence 1 now has Nmax nodes: padding rows get parents and tokens in range
+    for v in range(1, w.K):
+        if v >= d["node_count"][1]:
+            par[1, v] = exp_par[1, v] = v - 1
+    case("per-sequence trees with out-of-range entries")
+    g = sv.spec_verify_tree_greedy_dyn(dev(d["node_logits"]), dev(tok), dev(par), dev(cnt))
+    torch.cuda.synchronize()
+    g = [x.cpu().numpy() for x in g]
+    o = oracle.verify_tree_greedy_dyn(d["node_logits"], exp_tok, exp_par, exp_cnt)
+    for x, y in zip(g, o):
+        assert np.array_equal(x, y)
+
+
+def test_tree_dyn_full_size_128k(sv):
+    w = W.WORKLOADS["tree_dyn_128k"]
+    for step in (0, 1):
+        case(f"tree_dyn_128k full size step {step}")
+        d = W.tree_dyn_inputs(w, step)
+        g = run_tree_dyn(sv, d)
+        parity.check_tree_dyn(d, *g)
+        print("tree_dyn_128k mean depth", g[2].mean())

@@ -36,8 +36,15 @@ def test_shapes_of_every_workload_at_small_sizes():
             assert d["tokens"].shape == (2, w.K) and d["u_sample"].shape == (2,)
         elif w.mode == "greedy":
             assert d["target"].shape == (2, w.K + 1, 300) and d["tokens"].shape == (2, w.K)
-        else:
+        elif w.mode == "tree":
             assert d["node_logits"].shape == (2, 45, 300) and d["parents"].shape == (45,)
+        else:
+            assert d["node_logits"].shape == (2, w.K, 300) and d["parents"].shape == (2, w.K)
+            assert d["node_tokens"].shape == (2, w.K) and d["node_count"].shape == (2,)
+            for b in range(2):
+                n = d["node_count"][b]
+                assert w.K // 4 <= n <= w.K and d["parents"][b, 0] == -1
+                assert all(0 <= d["parents"][b, v] < v for v in range(1, n))
         arr = d.get("target", d.get("node_logits"))
         assert arr.dtype == (np.uint16 if w.dtype == "bf16" else np.float32)
 

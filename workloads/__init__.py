@@ -25,6 +25,11 @@ Workloads (sizes and distributions as specified for this verify step):
                    (4, 2, 2, 1) in breadth-first order (N = 45 nodes); rows as in
                    chain_t1_128k's target; the k-th child of node u carries u's
                    argmax with probability 0.6, else u's (k+1)-th ranked token.
+  tree_dyn_128k    greedy verify on per-sequence trees, B=32, at most 64 nodes,
+                   V=128256, bf16; each sequence's tree has a node count uniform
+                   in [16, 64] and is grown breadth-first with 1 to 4 children
+                   per node (a stand-in for trees shaped by the draft's
+                   confidence); rows and node tokens as in tree_128k.
 
 Drafted tokens are "sampled from q" with the Gumbel-max construction
 (argmax_i of d_i / T + G_i with G_i standard Gumbel), which draws exactly from
@@ -51,11 +56,11 @@ C3_SIGMA = 0.66
 class Workload:
     name: str
     wid: int                 # seed component
-    mode: str                # "chain" | "greedy" | "tree"
+    mode: str                # "chain" | "greedy" | "tree" | "tree_dyn"
     B: int
     V: int
     dtype: str               # "f32" | "bf16"
-    K: int = 0               # chain / greedy draft length
+    K: int = 0               # chain / greedy draft length; tree_dyn: most nodes per tree
     T: float = 0.0           # chain temperature
     branching: tuple = field(default_factory=tuple)   # tree only
     recipe: str = "normal"   # target rows: "normal" | "peaked" | "zipf"
@@ -79,6 +84,8 @@ WORKLOADS = {
                                T=0.7, recipe="zipf", sigma=0.8, steps=100),
     "tree_128k": Workload("tree_128k", 5, "tree", B=32, V=128256, dtype="bf16",
                           branching=(4, 2, 2, 1), recipe="peaked"),
+    "tree_dyn_128k": Workload("tree_dyn_128k", 6, "tree_dyn", B=32, V=128256, dtype="bf16",
+                              K=64, recipe="peaked"),
 }
 
 TARGET, DRAFT_NOISE, STRUCTURE, DRAFT_TOKENS, UNIFORMS = range(5)
@@ -232,6 +239,28 @@ def _ranked(row: np.ndarray, n: int) -> np.ndarray:
     return cand[order][:n]
 
 
+def _node_tokens(vals_b: np.ndarray, par: np.ndarray, n: int, rng3, p_match: float) -> np.ndarray:
+    """Tokens of nodes 1..n-1 of one tree: the k-th child of node u carries u's
+    argmax with probability p_match, else u's (k+1)-th ranked token."""
+    ordinal = np.zeros(n, np.int64)  # 1-based place of each node among its parent's children
+    seen = {}
+    for v in range(1, n):
+        seen[par[v]] = seen.get(par[v], 0) + 1
+        ordinal[v] = seen[par[v]]
+    nrank = int(ordinal.max()) + 1 if n > 1 else 1
+    tokens = np.zeros(n, np.int32)
+    ranks = {}
+    for v in range(1, n):
+        u = int(par[v])
+        if u not in ranks:
+            ranks[u] = _ranked(vals_b[u], nrank)
+        r = ranks[u]
+        k = int(ordinal[v])
+        take_top = rng3.random() < p_match
+        tokens[v] = r[0] if take_top or k >= len(r) else r[k]
+    return tokens
+
+
 def tree_inputs(w: Workload, step: int = 0, p_match: float = 0.6, parents=None) -> dict:
     """Inputs of one greedy tree step: node_logits [B][N][V], node_tokens [B][N], parents [N]."""
     assert w.mode == "tree"
@@ -240,25 +269,47 @@ def tree_inputs(w: Workload, step: int = 0, p_match: float = 0.6, parents=None) 
     rng0, rng2, rng3 = rng_for(w, TARGET, step), rng_for(w, STRUCTURE, step), rng_for(w, DRAFT_TOKENS, step)
     logits = _store(_target_rows(w, B * N, rng0, rng2), w.dtype).reshape(B, N, V)
     vals = as_f32(logits)
-    # ordinal (1-based) of each node among its parent's children
-    ordinal = np.zeros(N, np.int64)
-    seen = {}
-    for v in range(1, N):
-        seen[par[v]] = seen.get(par[v], 0) + 1
-        ordinal[v] = seen[par[v]]
-    nrank = int(ordinal.max()) + 1 if N > 1 else 1
-    tokens = np.zeros((B, N), np.int32)
-    for b in range(B):
-        ranks = {}
-        for v in range(1, N):
-            u = int(par[v])
-            if u not in ranks:
-                ranks[u] = _ranked(vals[b, u], nrank)
-            r = ranks[u]
-            k = int(ordinal[v])
-            take_top = rng3.random() < p_match
-            tokens[b, v] = r[0] if take_top or k >= len(r) else r[k]
+    tokens = np.stack([_node_tokens(vals[b], par, N, rng3, p_match) for b in range(B)])
     return dict(node_logits=logits, node_tokens=tokens, parents=par, dtype=w.dtype)
+
+
+def dyn_tree(rng, nmax: int, nmin: int = 1, max_children: int = 4) -> np.ndarray:
+    """One tree of n nodes (n uniform in [nmin, nmax]) grown breadth-first,
+    each node taking 1..max_children children until n nodes exist: parents in
+    topological order (parents[0] = -1, parents[v] < v)."""
+    n = int(rng.integers(nmin, nmax + 1))
+    parents, queue = [-1], [0]
+    while len(parents) < n:
+        u = queue.pop(0)
+        for _ in range(int(rng.integers(1, max_children + 1))):
+            if len(parents) == n:
+                break
+            parents.append(u)
+            queue.append(len(parents) - 1)
+    return np.asarray(parents, np.int32)
+
+
+def tree_dyn_inputs(w: Workload, step: int = 0, p_match: float = 0.6, nmin: int | None = None) -> dict:
+    """Inputs of one greedy step on per-sequence trees: node_logits [B][Nmax][V],
+    node_tokens [B][Nmax], parents [B][Nmax], node_count [B].  Padding (nodes
+    past a tree's count) has logits like any row, token 0 and parent 0."""
+    assert w.mode == "tree_dyn"
+    B, Nmax, V = w.B, w.K, w.V
+    rng0, rng2, rng3 = rng_for(w, TARGET, step), rng_for(w, STRUCTURE, step), rng_for(w, DRAFT_TOKENS, step)
+    nmin = max(1, Nmax // 4) if nmin is None else nmin
+    trees = [dyn_tree(rng2, Nmax, nmin) for _ in range(B)]
+    logits = _store(_target_rows(w, B * Nmax, rng0, rng2), w.dtype).reshape(B, Nmax, V)
+    vals = as_f32(logits)
+    parents = np.zeros((B, Nmax), np.int32)
+    tokens = np.zeros((B, Nmax), np.int32)
+    counts = np.zeros(B, np.int32)
+    for b, par in enumerate(trees):
+        n = len(par)
+        counts[b] = n
+        parents[b, :n] = par
+        tokens[b, :n] = _node_tokens(vals[b], par, n, rng3, p_match)
+    return dict(node_logits=logits, node_tokens=tokens, parents=parents, node_count=counts,
+                dtype=w.dtype)
 
 
 def make_inputs(w: Workload, step: int = 0) -> dict:
@@ -266,4 +317,6 @@ def make_inputs(w: Workload, step: int = 0) -> dict:
         return chain_inputs(w, step)
     if w.mode == "greedy":
         return greedy_inputs(w, step)
+    if w.mode == "tree_dyn":
+        return tree_dyn_inputs(w, step)
     return tree_inputs(w, step)
