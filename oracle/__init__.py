@@ -65,6 +65,8 @@ def _bind(lib):
     lib.oracle_verify_tree_greedy.restype = i
     lib.oracle_verify_tree_greedy_dyn.argtypes = [vp, i, i32p, i32p, i32p, i, i, i, vp, vp, vp]
     lib.oracle_verify_tree_greedy_dyn.restype = i
+    lib.oracle_topk.argtypes = [vp, i, i, i, i, vp, vp]
+    lib.oracle_topk.restype = i
     return lib
 
 
@@ -240,3 +242,19 @@ def verify_tree_greedy_dyn(node_logits, node_tokens, parents, node_count, *, lib
     if rc != 0:
         raise ValueError(f"oracle_verify_tree_greedy_dyn rejected its arguments (code {rc})")
     return out_t, out_p, out_d
+
+
+def topk(logits, k, *, lib=None):
+    """Top-k of each row: (indices [rows][k], values [rows][k] float32), by value
+    descending then index ascending."""
+    lib = lib or load()
+    t, dt = _logits(logits)
+    V = t.shape[-1]
+    t2 = t.reshape(-1, V)
+    rows = t2.shape[0]
+    out_i = np.empty((rows, k), np.int32)
+    out_v = np.empty((rows, k), np.float32)
+    rc = lib.oracle_topk(_ptr(t2), dt, rows, V, k, _ptr(out_i), _ptr(out_v))
+    if rc != 0:
+        raise ValueError(f"oracle_topk rejected its arguments (code {rc})")
+    return out_i.reshape(t.shape[:-1] + (k,)), out_v.reshape(t.shape[:-1] + (k,))

@@ -578,3 +578,46 @@ int oracle_verify_tree_greedy_dyn(const void *node_logits, int dtype, const int3
     free(dep);
     return OR_OK;
 }
+
+/*
+ * Top-k of draft rows, the expansion step of an EAGLE-style tree drafter
+ * (French lesson, EAGLE section: a tree of 4 to 8 candidates per depth, and
+ * its exercise: the draft proposes its top branches at each depth).
+ *   logits [rows][V]; 1 <= k <= 8, k <= V.
+ *   out_idx [rows][k]: the k entries of largest value, by value descending and
+ *     then index ascending (so -0.0 ties +0.0 and the lower index comes first);
+ *   out_val [rows][k] (nullable): their logits, as stored (bf16 widened).
+ * k rounds per row, each taking the best entry not yet taken.
+ */
+int oracle_topk(const void *logits, int dtype, int rows, int V, int k, int32_t *out_idx,
+                float *out_val)
+{
+    if (rows < 0 || V < 1 || k < 1 || k > 8 || k > V || (dtype != OR_F32 && dtype != OR_BF16))
+        return OR_BAD_ARG;
+    if (rows > 0 && (!logits || !out_idx))
+        return OR_BAD_ARG;
+    for (int r = 0; r < rows; ++r) {
+        int taken[8];
+        for (int q = 0; q < k; ++q) {
+            int best = -1;
+            double bv = 0.0;
+            for (int i = 0; i < V; ++i) {
+                int used = 0;
+                for (int t = 0; t < q; ++t)
+                    used |= taken[t] == i;
+                if (used)
+                    continue;
+                double v = logit_at(logits, dtype, (size_t)r * (size_t)V + (size_t)i);
+                if (best < 0 || v > bv) {
+                    bv = v;
+                    best = i;
+                }
+            }
+            taken[q] = best;
+            out_idx[(size_t)r * k + q] = best;
+            if (out_val)
+                out_val[(size_t)r * k + q] = (float)bv;
+        }
+    }
+    return OR_OK;
+}

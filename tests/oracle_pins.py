@@ -499,6 +499,39 @@ def pin_tree_dyn_chain(lib, seed=31):
         assert t_d[0] == g_a[0] and np.array_equal(t_t[0, :n], g_t[0]) and np.all(t_t[0, n:] == -1)
 
 
+# ------------------------------------------------------------- top-k
+
+def pin_topk_sort(lib, seed=41):
+    """Against a stable sort by (value descending, index ascending) of the
+    widened values (numpy's lexsort), on rows full of ties, with -0.0 and
+    +0.0 mixed and -inf entries."""
+    rng = np.random.default_rng(seed)
+    for trial in range(60):
+        V = int(rng.integers(1, 40))
+        k = int(rng.integers(1, min(8, V) + 1))
+        vals = (rng.integers(-3, 4, size=(7, V)) * 0.5).astype(np.float32)
+        vals[rng.random((7, V)) < 0.2] = -0.0
+        vals[rng.random((7, V)) < 0.1] = -np.inf
+        dtype = "bf16" if trial % 2 else "f32"
+        logits = bf16_bits(vals) if dtype == "bf16" else vals
+        w = widen(logits)
+        idx, val = oracle.topk(logits, k, lib=lib)
+        for r in range(w.shape[0]):
+            order = np.lexsort((np.arange(V), -w[r].astype(np.float64)))[:k]
+            assert list(idx[r]) == list(order), (trial, r, list(idx[r]), list(order))
+            assert np.array_equal(val[r], w[r][order])
+
+
+def pin_topk_argmax(lib, seed=43):
+    """k = 1 is the row argmax; the values come back in descending order."""
+    rng = np.random.default_rng(seed)
+    vals = rng.standard_normal((50, 300)).astype(np.float32)
+    idx, val = oracle.topk(vals, 1, lib=lib)
+    assert np.array_equal(idx[:, 0], np.argmax(vals, axis=1))
+    idx8, val8 = oracle.topk(vals, 8, lib=lib)
+    assert np.all(np.diff(val8, axis=1) <= 0) and np.array_equal(idx8[:, 0], idx[:, 0])
+
+
 # ------------------------------------------------------------- chi-square
 
 def pin_chi_square(lib, n=50_000, seed=19):
@@ -529,4 +562,4 @@ ALL_PINS = [pin_exact_law, pin_expected_tokens, pin_page_counts, pin_strict_acce
             pin_softmax_values, pin_helper_closed_forms,
             pin_inverse_cdf, pin_greedy, pin_tree_bruteforce, pin_tree_chain,
             pin_tree_figure, pin_tree_dyn_bruteforce, pin_tree_dyn_padding, pin_tree_dyn_chain,
-            pin_chi_square]
+            pin_topk_sort, pin_topk_argmax, pin_chi_square]

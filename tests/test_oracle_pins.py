@@ -88,6 +88,8 @@ MUTANTS = [
     ("per-sequence tree ties to the highest index", "if (acc[v] && dep[v] > dep[top])",
      "if (acc[v] && dep[v] >= dep[top])", 0),
     ("per-sequence tree ignores ancestors", "acc[v] = acc[par[v]] &&", "acc[v] = 1 &&", 0),
+    ("top-k ties to the highest index", "if (best < 0 || v > bv) {", "if (best < 0 || v >= bv) {", 0),
+    ("top-k takes an entry twice", "used |= taken[t] == i;", "used |= 0;", 0),
     ("per-sequence tree rows strided by the node count",
      "row_argmax(node_logits, dtype, (size_t)b * Nmax + (size_t)v, V);",
      "row_argmax(node_logits, dtype, (size_t)b * n + (size_t)v, V);", 0),
@@ -100,7 +102,7 @@ MUTANTS = [
 QUICK_PINS = [P.pin_exact_law, P.pin_expected_tokens, P.pin_page_counts, P.pin_strict_acceptance,
               P.pin_softmax_values, P.pin_helper_closed_forms,
               P.pin_inverse_cdf, P.pin_greedy, P.pin_tree_bruteforce, P.pin_tree_figure,
-              P.pin_tree_dyn_bruteforce, P.pin_tree_dyn_padding, P.pin_chi_square]
+              P.pin_tree_dyn_bruteforce, P.pin_tree_dyn_padding, P.pin_topk_sort, P.pin_chi_square]
 
 
 def _mutant_lib(tmpdir, pattern, repl, which):
