@@ -71,6 +71,8 @@ def set_bytes(w, inputs=None) -> int:
         rows = w.B * (w.K + 1)
     elif w.mode == "tree_dyn":
         rows = int(inputs["node_count"].sum()) if inputs is not None else w.B * w.K
+    elif w.mode == "topk":
+        rows = w.B
     else:
         rows = w.B * (1 + sum(int(np.prod(w.branching[:i + 1])) for i in range(len(w.branching))))
     return rows * w.V * esize
@@ -86,6 +88,8 @@ def oracle_step(w, inp):
     if w.mode == "tree_dyn":
         return oracle.verify_tree_greedy_dyn(inp["node_logits"], inp["node_tokens"], inp["parents"],
                                              inp["node_count"])
+    if w.mode == "topk":
+        return oracle.topk(inp["logits"], w.K)
     return oracle.verify_tree_greedy(inp["node_logits"], inp["node_tokens"], inp["parents"])
 
 
@@ -97,6 +101,8 @@ def check(w, inp, gpu_out):
         return parity.check_greedy(inp, *gpu_out)
     if w.mode == "tree_dyn":
         return parity.check_tree_dyn(inp, *gpu_out)
+    if w.mode == "topk":
+        return parity.check_topk(inp, *gpu_out)
     return parity.check_tree(inp, *gpu_out)
 
 
@@ -111,7 +117,8 @@ def cpu_baseline(w, inp, budget_s: float, gpu_out):
             break
     dt = time.perf_counter() - t0
     counts = check(w, inp, gpu_out)
-    return {"value": steps / dt, "unit": "verify steps/s", "cores": 1, "kind": "oracle",
+    unit = "top-k steps/s" if w.mode == "topk" else "verify steps/s"
+    return {"value": steps / dt, "unit": unit, "cores": 1, "kind": "oracle",
             "sample": f"{steps} whole steps of input set 0 of {w.name}, fp64, one thread, {dt:.1f} s",
             "parity_on_sample": dict(counts)}
 
@@ -237,6 +244,24 @@ def main():
         dominant_name = "k_tree_dyn (whole step)"
         io_bytes = 4 * B * Nmax * 2 + 4 * B + 4 * B * (2 * Nmax + 1)
         verified = float(np.mean([(h["node_count"] - 1).sum() for h in host_sets]))
+    elif w.mode == "topk":
+        k = w.K
+        ws = sv.workspace(sv.SPEC_MODE_TOPK, B, k, V, dt_code, device)
+        out_i = torch.empty((B, k), dtype=torch.int32, device=device)
+        out_v = torch.empty((B, k), dtype=torch.float32, device=device)
+
+        def step(i):
+            sv.spec_draft_topk(sets[i % nsets]["logits"], k, out_idx=out_i, out_val=out_v,
+                               workspace_buf=ws, stream=stream)
+        stats_phase = None
+
+        def outputs():
+            idx, val = sv.spec_draft_topk(sets[0]["logits"], k)
+            torch.cuda.synchronize()
+            return idx.cpu().numpy(), val.cpu().numpy()
+        dominant_name = "k_topk (whole step)"
+        io_bytes = 8 * B * k
+        verified = 0
     else:
         par = host_sets[0]["parents"]
         N = len(par)
@@ -300,15 +325,17 @@ def main():
     achieved_step = (nbytes + io_bytes) / (ms_step * 1e-3) / 1e9
     achieved_dom = nbytes / (ms_dom * 1e-3) / 1e9
     is_tree = w.mode in ("tree", "tree_dyn")
-    emitted = (gpu_out[2] + 1).sum() if is_tree else (gpu_out[1] + 1).sum()
-    # Acceptance on the timed batch (input set 0): mean accepted drafts per
-    # sequence, and for chains the per-token acceptance rate alpha = accepted
-    # / tested (a sequence tests positions up to its first rejection).
-    acc = gpu_out[2] if is_tree else gpu_out[1]
-    acceptance = {"mean_accepted": float(np.mean(acc))}
-    if not is_tree:
-        tested = acc + (acc < w.K)
-        acceptance["alpha"] = float(acc.sum() / max(int(tested.sum()), 1))
+    acceptance = None
+    if w.mode != "topk":
+        emitted = (gpu_out[2] + 1).sum() if is_tree else (gpu_out[1] + 1).sum()
+        # Acceptance on the timed batch (input set 0): mean accepted drafts per
+        # sequence, and for chains the per-token acceptance rate alpha = accepted
+        # / tested (a sequence tests positions up to its first rejection).
+        acc = gpu_out[2] if is_tree else gpu_out[1]
+        acceptance = {"mean_accepted": float(np.mean(acc))}
+        if not is_tree:
+            tested = acc + (acc < w.K)
+            acceptance["alpha"] = float(acc.sum() / max(int(tested.sum()), 1))
     config = {"workload": w.name, "mode": w.mode, "B": B, "V": V, "logits": w.dtype,
               "input_sets_rotated": nsets, "logit_bytes_per_step": nbytes}
     if w.mode == "chain":
@@ -317,12 +344,14 @@ def main():
         config.update(K=w.K)
     elif w.mode == "tree_dyn":
         config.update(Nmax=w.K, mean_nodes=float(np.mean([h["node_count"].mean() for h in host_sets])))
+    elif w.mode == "topk":
+        config.update(rows=B, k=w.K)
     else:
         config.update(branching=list(w.branching))
     line = {
         "metric": METRIC,
         "value": steps_per_s,
-        "unit": "verify steps/s",
+        "unit": "top-k steps/s" if w.mode == "topk" else "verify steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -336,7 +365,7 @@ def main():
         "achieved_GBps": achieved_step,
         "frac_of_hbm_peak": achieved_step / HBM_PEAK_GBPS,
         "tokens_verified_per_s": steps_per_s * verified,
-        "tokens_emitted_per_s": steps_per_s * float(emitted),
+        "tokens_emitted_per_s": steps_per_s * float(emitted) if acceptance else None,
         "acceptance": acceptance,
         "roofline": {"kernel": dominant_name, "bound": "hbm", "achieved": achieved_dom,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved_dom / HBM_PEAK_GBPS,

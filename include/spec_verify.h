@@ -60,7 +60,8 @@ typedef enum {
     SPEC_MODE_CHAIN = 0,  /* spec_verify_chain (T > 0)           */
     SPEC_MODE_GREEDY = 1, /* spec_verify_greedy (T = 0, chain)   */
     SPEC_MODE_TREE = 2,   /* spec_verify_tree_greedy (T = 0)     */
-    SPEC_MODE_TREE_DYN = 3 /* spec_verify_tree_greedy_dyn (T = 0) */
+    SPEC_MODE_TREE_DYN = 3, /* spec_verify_tree_greedy_dyn (T = 0) */
+    SPEC_MODE_TOPK = 4      /* spec_draft_topk                     */
 } spec_mode;
 
 typedef enum {
@@ -75,11 +76,14 @@ typedef enum {
 #define SPEC_VERIFY_MAX_V (1 << 26)     /* vocabulary limit (greedy and tree)            */
 #define SPEC_VERIFY_MAX_CHAIN_V_BF16 (1 << 19)  /* chain verify vocabulary limit, bf16 logits */
 #define SPEC_VERIFY_MAX_CHAIN_V_F32 (1 << 18)   /* chain verify vocabulary limit, fp32 logits */
+#define SPEC_TOPK_MAX_K 8               /* spec_draft_topk: k limit                      */
+#define SPEC_TOPK_MAX_V (1 << 19)       /* spec_draft_topk: vocabulary limit             */
 
 /*
  * Workspace size for one call.  K_or_N is K for the chain and greedy modes,
  * N (nodes, root included) for the tree mode and Nmax for the per-sequence
- * tree mode.  Pure host arithmetic.
+ * tree mode; for SPEC_MODE_TOPK, B is the row count and K_or_N is k.  Pure
+ * host arithmetic.
  * Returns SPEC_ERR_INVALID_ARG (and leaves *bytes alone) for sizes the entry
  * point would reject.
  */
@@ -241,6 +245,32 @@ spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtyp
                                         int32_t V, int32_t *out_tokens, int32_t *out_path,
                                         int32_t *out_depth, void *workspace,
                                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Per-row top-k of draft logits: the expansion step of an EAGLE-style tree
+ * drafter, which grows each depth of the candidate tree from the draft's k
+ * most likely tokens (French lesson, EAGLE section: 4 to 8 candidates per
+ * depth; its exercises: the top three branches at each depth).  Softmax at
+ * any temperature keeps the order of the logits, so the top k of the logits
+ * are the top k of the draft distribution.
+ *
+ *   logits  [rows][V]   bf16 or fp32 (dtype), 16-byte aligned.
+ *   1 <= k <= SPEC_TOPK_MAX_K, k <= V <= SPEC_TOPK_MAX_V, rows >= 0.
+ *   out_idx [rows][k]   int32: the k entries of largest value, by value
+ *                       descending, equal values by index ascending (values
+ *                       compare as floats, so -0.0 ties +0.0).
+ *   out_val nullable [rows][k]  float32: their values.
+ *   workspace           at least spec_verify_workspace_bytes(TOPK, rows, k, V).
+ *
+ * NaN logits give unspecified outputs (never an out-of-bounds access).  One
+ * kernel launch: a workgroup per (row, 16 KB of the row) leaves its k best,
+ * and a workgroup per row, after all of those, merges them; the merge waits
+ * (bounded, about 2 s) for its row's lists, and if a wait ever ran out the
+ * row gets out_idx = -1 (and out_val = NaN).
+ */
+spec_status spec_draft_topk(const void *logits, spec_dtype dtype, int32_t rows, int32_t V,
+                            int32_t k, int32_t *out_idx, float *out_val, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
 const char *spec_verify_status_string(spec_status status);

@@ -21,7 +21,8 @@ from collections import Counter
 
 import numpy as np
 
-from . import draw_weights, verify_chain, verify_greedy, verify_tree_greedy, verify_tree_greedy_dyn
+from . import (draw_weights, topk, verify_chain, verify_greedy, verify_tree_greedy,
+               verify_tree_greedy_dyn)
 
 REL = 1e-5
 RATIO_BAND = 1e-6
@@ -143,3 +144,24 @@ def check_tree_dyn(inp: dict, gpu_tokens, gpu_path, gpu_depth, seqs=None) -> Cou
                        f"oracle {o_tok[i].tolist()} depth {o_depth[i]}")
     assert not bad, "per-sequence tree parity violations:\n" + "\n".join(bad[:20])
     return Counter(sequences=len(seqs), exact=len(seqs))
+
+
+def check_topk(inp: dict, gpu_idx, gpu_val=None, rows=None) -> Counter:
+    """Top-k: indices exactly equal to the oracle's (the order by value, then
+    index, is total, so the result is unique) and values equal to the logits
+    at those indices, bit for bit as float32."""
+    x = inp["logits"]
+    V = x.shape[-1]
+    x2 = x.reshape(-1, V)
+    gi = np.asarray(gpu_idx).reshape(x2.shape[0], -1)
+    k = gi.shape[1]
+    rows = np.arange(x2.shape[0]) if rows is None else np.asarray(rows)
+    o_idx, o_val = topk(x2[rows], k)
+    bad = [f"row {r}: gpu {gi[r].tolist()} oracle {o_idx[i].tolist()}"
+           for i, r in enumerate(rows) if not np.array_equal(gi[r], o_idx[i])]
+    assert not bad, "top-k index parity violations:\n" + "\n".join(bad[:20])
+    if gpu_val is not None:
+        gv = np.asarray(gpu_val, np.float32).reshape(x2.shape[0], -1)[rows]
+        assert np.array_equal(gv.view(np.uint32), o_val.view(np.uint32)), \
+            "top-k values differ from the oracle's"
+    return Counter(rows=len(rows), exact=len(rows))

@@ -21,10 +21,11 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "spec_verify.h")
 
 SPEC_DTYPE_F32, SPEC_DTYPE_BF16 = 0, 1
-SPEC_MODE_CHAIN, SPEC_MODE_GREEDY, SPEC_MODE_TREE, SPEC_MODE_TREE_DYN = 0, 1, 2, 3
+SPEC_MODE_CHAIN, SPEC_MODE_GREEDY, SPEC_MODE_TREE, SPEC_MODE_TREE_DYN, SPEC_MODE_TOPK = 0, 1, 2, 3, 4
 SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_LAUNCH = 0, 1, 2, 3
 MAX_K, MAX_TREE_NODES, MAX_V = 64, 256, 1 << 26
 MAX_CHAIN_V_BF16, MAX_CHAIN_V_F32 = 1 << 19, 1 << 18
+TOPK_MAX_K, TOPK_MAX_V = 8, 1 << 19
 
 
 class SpecVerifyError(RuntimeError):
@@ -54,9 +55,10 @@ def _load(path: str = LIB_PATH):
                                             vp, sz, vp]
     lib.spec_verify_tree_greedy_dyn.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, vp, vp,
                                                 vp, vp, sz, vp]
+    lib.spec_draft_topk.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, vp, sz, vp]
     for fn in ("spec_verify_workspace_bytes", "spec_verify_chain", "spec_verify_chain_stats",
                "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy",
-               "spec_verify_tree_greedy_dyn"):
+               "spec_verify_tree_greedy_dyn", "spec_draft_topk"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -67,7 +69,7 @@ _lib = _load()
 def header_symbols(path: str = HEADER_PATH) -> list[str]:
     """Entry points declared in the public header."""
     text = open(path).read()
-    return sorted(set(re.findall(r"^\S.*?\b(spec_verify_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\S.*?\b(spec_(?:verify|draft)_\w+)\s*\(", text, flags=re.M)))
 
 
 def library():
@@ -296,3 +298,32 @@ def spec_verify_tree_greedy_dyn(node_logits, node_tokens, parents, node_count, *
           _ptr(node_count), B, Nmax, V, _ptr(out_tokens), _ptr(out_path), _ptr(out_depth),
           _ptr(workspace_buf), workspace_buf.numel(), _stream(dev, stream))
     return out_tokens, out_path, out_depth
+
+
+def spec_draft_topk(logits, k, *, with_values=True, out_idx=None, out_val=None, workspace_buf=None,
+                    stream=None):
+    """Per-row top-k of draft logits [..., V] (bf16 or fp32): the k largest by
+    value descending, equal values by index ascending.  Returns (idx [..., k]
+    int32, values [..., k] float32 or None)."""
+    _check_dev("logits", logits)
+    dt = _dtype_code(logits)
+    if logits.dim() < 1:
+        raise ValueError("logits must have a vocabulary dimension")
+    lead, V = tuple(logits.shape[:-1]), logits.shape[-1]
+    rows = 1
+    for d in lead:
+        rows *= d
+    dev = logits.device
+    if out_idx is None:
+        out_idx = torch.empty(lead + (k,), dtype=torch.int32, device=dev)
+    else:
+        _check_dev("out_idx", out_idx, torch.int32, lead + (k,))
+    if out_val is None and with_values:
+        out_val = torch.empty(lead + (k,), dtype=torch.float32, device=dev)
+    elif out_val is not None:
+        _check_dev("out_val", out_val, torch.float32, lead + (k,))
+    if workspace_buf is None:
+        workspace_buf = workspace(SPEC_MODE_TOPK, rows, k, V, dt, dev)
+    _call("spec_draft_topk", _ptr(logits), dt, rows, V, k, _ptr(out_idx), _ptr(out_val),
+          _ptr(workspace_buf), workspace_buf.numel(), _stream(dev, stream))
+    return out_idx, out_val

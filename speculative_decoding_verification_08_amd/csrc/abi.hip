@@ -1,6 +1,6 @@
 // C ABI of the verify library: argument validation, launch planning and the
 // workspace layout.  Everything here is host code; the kernels live in
-// chain.hip and greedy_tree.hip.
+// chain.hip, greedy_tree.hip and topk.hip.
 #include <math.h>
 #include <string.h>
 
@@ -8,6 +8,7 @@
 #include <atomic>
 
 #include "plan.hpp"
+#include "topk.hpp"
 #include "spec_verify.h"
 
 namespace sv {
@@ -28,6 +29,7 @@ bool valid_dtype(spec_dtype d) { return d == SPEC_DTYPE_F32 || d == SPEC_DTYPE_B
 
 bool valid_sizes(spec_mode mode, int32_t B, int32_t KN, int32_t V) {
     if (B < 0 || V < 1 || V > SPEC_VERIFY_MAX_V) return false;
+    if (mode == SPEC_MODE_TOPK) return KN >= 1 && KN <= SPEC_TOPK_MAX_K && KN <= V && V <= SPEC_TOPK_MAX_V;
     if (mode == SPEC_MODE_TREE || mode == SPEC_MODE_TREE_DYN)
         return KN >= 1 && KN <= SPEC_VERIFY_MAX_TREE_NODES;
     return KN >= 0 && KN <= SPEC_VERIFY_MAX_K;
@@ -38,6 +40,7 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
     int64_t rows;
     if (mode == SPEC_MODE_CHAIN) rows = static_cast<int64_t>(B) * (2 * KN + 1);
     else if (mode == SPEC_MODE_GREEDY) rows = static_cast<int64_t>(B) * (KN + 1);
+    else if (mode == SPEC_MODE_TOPK) rows = B;
     else rows = static_cast<int64_t>(B) * KN;
     p.rows = rows;
     p.chunk = first_pass_chunk(dtype);
@@ -57,6 +60,14 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
         if (static_cast<int64_t>(B) * p.nchunk2 > 0x7fffffffLL) return false;
         p.off_sums = off;  // two tagged masses per chunk: residual, target
         off += align_up(static_cast<size_t>(B) * p.nchunk2 * 16);
+    } else if (mode == SPEC_MODE_TOPK) {
+        // One launch: a workgroup per (row, chunk), then a merge workgroup per
+        // row, whose wavefront holds all of the row's nchunk * k candidates.
+        p.chunk = kChunk2Bytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
+        p.nchunk = (V + p.chunk - 1) / p.chunk;
+        if (p.nchunk * KN > kTopkMergeCands) return false;
+        if (rows * p.nchunk + rows > 0x7fffffffLL) return false;
+        off += align_up(static_cast<size_t>(rows) * p.nchunk * kMaxTopK * 16);
     } else {
         // One launch: argmax workgroups, then one resolve workgroup per sequence.
         if (rows * p.nchunk + B > 0x7fffffffLL) return false;
@@ -164,7 +175,7 @@ spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_
                                         spec_dtype dtype, size_t *bytes) {
     if (!bytes || !valid_dtype(dtype)) return SPEC_ERR_INVALID_ARG;
     if (mode != SPEC_MODE_CHAIN && mode != SPEC_MODE_GREEDY && mode != SPEC_MODE_TREE &&
-        mode != SPEC_MODE_TREE_DYN)
+        mode != SPEC_MODE_TREE_DYN && mode != SPEC_MODE_TOPK)
         return SPEC_ERR_INVALID_ARG;
     Plan p;
     if (!make_plan(mode, B, K_or_N, V, dtype, p)) return SPEC_ERR_INVALID_ARG;
@@ -336,6 +347,32 @@ spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtyp
     t.out_path = out_path;
     t.out_depth = out_depth;
     return launch_status(launch_tree_dyn(t, dtype, stream));
+}
+
+spec_status spec_draft_topk(const void *logits, spec_dtype dtype, int32_t rows, int32_t V,
+                            int32_t k, int32_t *out_idx, float *out_val, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dtype(dtype)) return SPEC_ERR_INVALID_ARG;
+    Plan plan;
+    if (!make_plan(SPEC_MODE_TOPK, rows, k, V, dtype, plan)) return SPEC_ERR_INVALID_ARG;
+    if (rows == 0) return SPEC_OK;
+    if (!logits || !aligned(logits, 16) || !out_idx || !aligned(out_idx, 4) ||
+        (out_val && !aligned(out_val, 4)))
+        return SPEC_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < plan.bytes || !aligned(workspace, 16))
+        return SPEC_ERR_WORKSPACE;
+    TopkArgs a;
+    a.logits = logits;
+    a.rows = rows;
+    a.V = V;
+    a.chunk = plan.chunk;
+    a.nchunk = plan.nchunk;
+    a.k = k;
+    a.tag = next_call_tag();
+    a.partial = at<uint64_t>(workspace, plan.off_partial);
+    a.out_idx = out_idx;
+    a.out_val = out_val;
+    return launch_status(launch_topk(a, dtype, stream));
 }
 
 }  // extern "C"

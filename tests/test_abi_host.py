@@ -13,7 +13,8 @@ FAKE_MIS = FAKE + 8     # misaligned for logits
 def test_every_declared_symbol_is_exported():
     syms = sv.header_symbols()
     assert {"spec_verify_chain", "spec_verify_greedy", "spec_verify_tree_greedy",
-            "spec_verify_workspace_bytes"} <= set(syms)
+            "spec_verify_tree_greedy_dyn", "spec_verify_workspace_bytes",
+            "spec_draft_topk"} <= set(syms)
     lib = sv.library()
     for s in syms:
         assert hasattr(lib, s), s
@@ -100,6 +101,34 @@ def test_greedy_and_tree_argument_errors():
     assert tree([-1] + list(range(256)), N=257) == E
     assert lib.spec_verify_tree_greedy(FAKE, 1, FAKE, None, 2, 3, 100, FAKE, None, FAKE, FAKE,
                                        1 << 20, None) == E
+
+
+def test_topk_argument_errors():
+    lib = sv.library()
+    ws = sv.spec_verify_workspace_bytes
+    E, BF, F32 = sv.SPEC_ERR_INVALID_ARG, sv.SPEC_DTYPE_BF16, sv.SPEC_DTYPE_F32
+    # 16 KB chunks, 8 slots of two 8-byte words each per (row, chunk)
+    assert ws(sv.SPEC_MODE_TOPK, 512, 8, 128256, BF) == 512 * 16 * 128
+    assert ws(sv.SPEC_MODE_TOPK, 3, 1, 5000, F32) == 3 * 2 * 128
+    for V, dt in ((sv.TOPK_MAX_V, BF), (sv.TOPK_MAX_V, F32)):
+        assert ws(sv.SPEC_MODE_TOPK, 2, sv.TOPK_MAX_K, V, dt) > 0
+    for rows, k, V in ((-1, 4, 100), (2, 0, 100), (2, 9, 100), (2, 5, 4),
+                       (2, 4, sv.TOPK_MAX_V + 1)):
+        with pytest.raises(sv.SpecVerifyError) as e:
+            ws(sv.SPEC_MODE_TOPK, rows, k, V, BF)
+        assert e.value.status == E
+    t = lib.spec_draft_topk
+    big = 1 << 30
+    assert t(FAKE, BF, 0, 100, 4, FAKE, None, FAKE, big, None) == sv.SPEC_OK
+    assert t(None, BF, 2, 100, 4, FAKE, None, FAKE, big, None) == E
+    assert t(FAKE_MIS, BF, 2, 100, 4, FAKE, None, FAKE, big, None) == E
+    assert t(FAKE, BF, 2, 100, 4, None, None, FAKE, big, None) == E
+    assert t(FAKE, BF, 2, 100, 4, FAKE + 2, None, FAKE, big, None) == E
+    assert t(FAKE, BF, 2, 100, 4, FAKE, FAKE + 2, FAKE, big, None) == E
+    assert t(FAKE, BF, 2, 100, 9, FAKE, None, FAKE, big, None) == E
+    assert t(FAKE, 5, 2, 100, 4, FAKE, None, FAKE, big, None) == E
+    assert t(FAKE, BF, 2, 100, 4, FAKE, None, None, big, None) == sv.SPEC_ERR_WORKSPACE
+    assert t(FAKE, BF, 2, 100, 4, FAKE, None, FAKE, 16, None) == sv.SPEC_ERR_WORKSPACE
 
 
 def test_status_strings():

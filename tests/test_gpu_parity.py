@@ -420,3 +420,72 @@ def test_tree_dyn_full_size_128k(sv):
         g = run_tree_dyn(sv, d)
         parity.check_tree_dyn(d, *g)
         print("tree_dyn_128k mean depth", g[2].mean())
+
+
+# ------------------------------------------------------------------ top-k
+
+def run_topk(sv, x, k):
+    idx, val = sv.spec_draft_topk(dev(x), k)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), val.cpu().numpy()
+
+
+def topk_case(rows, V, dtype, step=0, recipe="peaked", sigma=0.66):
+    w = W.Workload("tk", 95, "topk", B=rows, V=V, dtype=dtype, K=8, recipe=recipe, sigma=sigma)
+    return W.topk_inputs(w, step)["logits"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 7, 100, 4095, 4096, 4097, 8192, 8193, 20001, 128256])
+def test_topk_sizes(sv, dtype, V):
+    x = topk_case(5, V, dtype, step=V % 97)
+    for k in sorted({1, 3, 8} & set(range(1, min(V, 8) + 1)) | {min(V, 8)}):
+        case(f"top-k V={V} k={k} {dtype}")
+        parity.check_topk({"logits": x}, *run_topk(sv, x, k))
+
+
+def test_topk_ties_zeros_and_infinities(sv):
+    rng = np.random.default_rng(1234)
+    for dtype in ("f32", "bf16"):
+        rows = []
+        rows.append(np.zeros(20001, np.float32))                           # all equal: exact rounds
+        rows.append(rng.integers(0, 3, 20001).astype(np.float32))          # heavy ties at the top
+        z = np.zeros(20001, np.float32)
+        z[rng.choice(20001, 9000, replace=False)] = -0.0                   # -0.0 ties +0.0
+        rows.append(z)
+        ninf = np.full(20001, -np.inf, np.float32)
+        ninf[[5, 17000]] = [1.0, 2.0]                                      # fewer than k finite
+        rows.append(ninf)
+        ninf2 = np.full(20001, -np.inf, np.float32)                        # all -inf
+        rows.append(ninf2)
+        peaks = rng.standard_normal(20001).astype(np.float32)
+        peaks[rng.choice(20001, 300, replace=False)] = 50.0                # 300 ties above theta
+        rows.append(peaks)
+        x = np.stack(rows)
+        x = W.bf16_bits(x) if dtype == "bf16" else x
+        for k in (1, 4, 8):
+            case(f"top-k ties {dtype} k={k}")
+            parity.check_topk({"logits": x}, *run_topk(sv, x, k))
+
+
+def test_topk_shapes_and_repeat(sv):
+    x = topk_case(24, 9000, "bf16", step=3).reshape(2, 3, 4, 9000)
+    case("top-k leading dims [2][3][4]")
+    i1, v1 = run_topk(sv, x, 6)
+    assert i1.shape == (2, 3, 4, 6)
+    parity.check_topk({"logits": x}, i1, v1)
+    i2, v2 = run_topk(sv, x, 6)
+    assert np.array_equal(i1, i2) and np.array_equal(v1, v2)
+    idx, val = sv.spec_draft_topk(dev(x), 6, with_values=False)
+    torch.cuda.synchronize()
+    assert val is None and np.array_equal(idx.cpu().numpy(), i1)
+    e_idx, _ = sv.spec_draft_topk(dev(np.zeros((0, 100), np.float32)), 4)
+    assert e_idx.shape == (0, 4)
+
+
+def test_topk_full_size_128k(sv):
+    w = W.WORKLOADS["topk_128k"]
+    for step in (0, 1):
+        case(f"topk_128k full size step {step}")
+        x = W.topk_inputs(w, step)["logits"]
+        parity.check_topk({"logits": x}, *run_topk(sv, x, w.K))

@@ -38,6 +38,8 @@ def test_shapes_of_every_workload_at_small_sizes():
             assert d["target"].shape == (2, w.K + 1, 300) and d["tokens"].shape == (2, w.K)
         elif w.mode == "tree":
             assert d["node_logits"].shape == (2, 45, 300) and d["parents"].shape == (45,)
+        elif w.mode == "topk":
+            assert d["logits"].shape == (2, 300) and d["k"] == w.K
         else:
             assert d["node_logits"].shape == (2, w.K, 300) and d["parents"].shape == (2, w.K)
             assert d["node_tokens"].shape == (2, w.K) and d["node_count"].shape == (2,)
@@ -45,7 +47,7 @@ def test_shapes_of_every_workload_at_small_sizes():
                 n = d["node_count"][b]
                 assert w.K // 4 <= n <= w.K and d["parents"][b, 0] == -1
                 assert all(0 <= d["parents"][b, v] < v for v in range(1, n))
-        arr = d.get("target", d.get("node_logits"))
+        arr = d.get("target", d.get("node_logits", d.get("logits")))
         assert arr.dtype == (np.uint16 if w.dtype == "bf16" else np.float32)
 
 

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the speculative-sampling verify step.
 
 This module only *makes inputs*: logits with the shapes and value
-distributions of the five workloads below, drafted tokens, and the uniforms the
+distributions of the workloads below, drafted tokens, and the uniforms the
 verify step consumes.  It holds none of the verify step's arithmetic (no
 softmax, no acceptance test, no residual, no inverse CDF), and both the GPU
 tests and the CPU oracle take their inputs from here.
@@ -30,6 +30,9 @@ Workloads (sizes and distributions as specified for this verify step):
                    in [16, 64] and is grown breadth-first with 1 to 4 children
                    per node (a stand-in for trees shaped by the draft's
                    confidence); rows and node tokens as in tree_128k.
+  topk_128k        top-k of draft rows for tree expansion, 512 rows (64
+                   sequences x 8 frontier nodes), V=128256, bf16, k=8; rows are
+                   chain_t1_128k's draft rows (peaked target + N(0, C3_SIGMA^2)).
 
 Drafted tokens are "sampled from q" with the Gumbel-max construction
 (argmax_i of d_i / T + G_i with G_i standard Gumbel), which draws exactly from
@@ -56,11 +59,11 @@ C3_SIGMA = 0.66
 class Workload:
     name: str
     wid: int                 # seed component
-    mode: str                # "chain" | "greedy" | "tree" | "tree_dyn"
+    mode: str                # "chain" | "greedy" | "tree" | "tree_dyn" | "topk"
     B: int
     V: int
     dtype: str               # "f32" | "bf16"
-    K: int = 0               # chain / greedy draft length; tree_dyn: most nodes per tree
+    K: int = 0               # chain / greedy draft length; tree_dyn: most nodes per tree; topk: k
     T: float = 0.0           # chain temperature
     branching: tuple = field(default_factory=tuple)   # tree only
     recipe: str = "normal"   # target rows: "normal" | "peaked" | "zipf"
@@ -86,6 +89,8 @@ WORKLOADS = {
                           branching=(4, 2, 2, 1), recipe="peaked"),
     "tree_dyn_128k": Workload("tree_dyn_128k", 6, "tree_dyn", B=32, V=128256, dtype="bf16",
                               K=64, recipe="peaked"),
+    "topk_128k": Workload("topk_128k", 7, "topk", B=512, V=128256, dtype="bf16", K=8,
+                          recipe="peaked", sigma=C3_SIGMA),
 }
 
 TARGET, DRAFT_NOISE, STRUCTURE, DRAFT_TOKENS, UNIFORMS = range(5)
@@ -312,6 +317,17 @@ def tree_dyn_inputs(w: Workload, step: int = 0, p_match: float = 0.6, nmin: int 
                 dtype=w.dtype)
 
 
+def topk_inputs(w: Workload, step: int = 0) -> dict:
+    """Draft rows [B][V] for a top-k expansion step: the target recipe plus
+    N(0, sigma^2) draft noise (sigma 0 leaves the target rows)."""
+    assert w.mode == "topk"
+    rng0, rng1, rng2 = rng_for(w, TARGET, step), rng_for(w, DRAFT_NOISE, step), rng_for(w, STRUCTURE, step)
+    x = _target_rows(w, w.B, rng0, rng2)
+    if w.sigma > 0:
+        x += _normal(rng1, x.shape, w.sigma)
+    return dict(logits=_store(x, w.dtype), k=w.K, dtype=w.dtype)
+
+
 def make_inputs(w: Workload, step: int = 0) -> dict:
     if w.mode == "chain":
         return chain_inputs(w, step)
@@ -319,4 +335,6 @@ def make_inputs(w: Workload, step: int = 0) -> dict:
         return greedy_inputs(w, step)
     if w.mode == "tree_dyn":
         return tree_dyn_inputs(w, step)
+    if w.mode == "topk":
+        return topk_inputs(w, step)
     return tree_inputs(w, step)
