@@ -26,10 +26,15 @@
  *    synchronously and nothing is enqueued then.  SPEC_ERR_LAUNCH reports a
  *    launch failure seen right after enqueueing.
  *  - The workspace (size from spec_verify_workspace_bytes) holds per-call
- *    scratch and needs no initialisation.  Words the chain verify's
+ *    scratch.  It must be zero-filled once before its first use (for
+ *    example with hipMemsetAsync); after that it can serve any number of
+ *    calls of any entry point and shape without clearing.  Words that
  *    workgroups hand each other carry a per-call tag (from a process-wide
- *    call counter), so contents left by any earlier call are never taken for
- *    fresh ones.  Calls that share a workspace must be ordered on one stream.
+ *    call counter, never 0), so words left by an earlier call of this
+ *    library, or zeros, are never taken for fresh ones.  Memory with other
+ *    prior contents could hold a word that looks fresh (a small integer in
+ *    its upper half), so an unzeroed workspace gives unspecified outputs.
+ *    Calls that share a workspace must be ordered on one stream.
  *  - Inputs that break a documented precondition (a drafted token outside
  *    [0, V), a uniform outside [0, 1), NaN or +inf logits, a row that is
  *    entirely -inf) give unspecified outputs but never an out-of-bounds
@@ -264,9 +269,9 @@ spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtyp
  *
  * NaN logits give unspecified outputs (never an out-of-bounds access).  One
  * kernel launch: a workgroup per (row, 16 KB of the row) leaves its k best,
- * and a workgroup per row, after all of those, merges them; the merge waits
- * (bounded, about 2 s) for its row's lists, and if a wait ever ran out the
- * row gets out_idx = -1 (and out_val = NaN).
+ * and the row's last workgroup to finish merges them.  The merge waits
+ * (bounded, about 2 s) for each list entry to carry the call's tag; if a
+ * wait ever ran out the row gets out_idx = -1 (and out_val = NaN).
  */
 spec_status spec_draft_topk(const void *logits, spec_dtype dtype, int32_t rows, int32_t V,
                             int32_t k, int32_t *out_idx, float *out_val, void *workspace,

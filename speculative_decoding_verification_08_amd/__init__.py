@@ -112,6 +112,25 @@ def _call(fn, *args):
         raise SpecVerifyError(fn, st)
 
 
+def _enqueue(prepare, keep, fn, *args):
+    """Calls entry point `fn` now, or with `prepare` returns a function that
+    enqueues the same call again with no Python-side checks (for serving
+    loops and graph capture).  The function holds the tensors in `keep` (every
+    tensor of the call), so their storage outlives it; their contents may be
+    rewritten in place between launches."""
+    f = getattr(_lib, fn)
+
+    def launch():
+        st = f(*args)
+        if st != SPEC_OK:
+            raise SpecVerifyError(fn, st)
+    launch.keep = keep
+    if prepare:
+        return launch
+    launch()
+    return None
+
+
 def spec_verify_workspace_bytes(mode: int, B: int, K_or_N: int, V: int, dtype: int) -> int:
     out = ctypes.c_size_t(0)
     _call("spec_verify_workspace_bytes", mode, B, K_or_N, V, dtype, ctypes.byref(out))
@@ -119,9 +138,11 @@ def spec_verify_workspace_bytes(mode: int, B: int, K_or_N: int, V: int, dtype: i
 
 
 def workspace(mode: int, B: int, K_or_N: int, V: int, dtype: int, device) -> torch.Tensor:
-    """A device byte buffer large enough for one call (no initialisation needed)."""
+    """A zero-filled device byte buffer large enough for one call.  Zeroed
+    once, it can be reused for any later calls (their hand-over words carry
+    per-call tags); a buffer with other prior contents must be zeroed first."""
     n = spec_verify_workspace_bytes(mode, B, K_or_N, V, dtype)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def _chain_check(target, draft, draft_tokens, u_accept, u_sample):
@@ -193,8 +214,8 @@ def prepare_chain(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
                   stream=None):
     """Checks and marshals the arguments of one spec_verify_chain call once and
     returns a function that enqueues it again with no Python-side work (for
-    serving loops and graph capture).  The tensors must stay alive and keep
-    their storage while the function is used."""
+    serving loops and graph capture).  The function holds every tensor of the
+    call; their contents may be rewritten in place between launches."""
     dt, B, K, V = _chain_check(target_logits, draft_logits, draft_tokens, u_accept, u_sample)
     dev = target_logits.device
     _check_dev("out_tokens", out_tokens, torch.int32, (B, K + 1))
@@ -214,12 +235,15 @@ def prepare_chain(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
         st = fn(*args)
         if st != SPEC_OK:
             raise SpecVerifyError("spec_verify_chain", st)
+    launch.keep = (target_logits, draft_logits, draft_tokens, u_accept, u_sample, out_tokens,
+                   out_accepted, out_diag, workspace_buf)
     return launch
 
 
 def spec_verify_greedy(target_logits, draft_tokens, *, out_tokens=None, out_accepted=None,
-                       workspace_buf=None, stream=None):
-    """Greedy chain verify (T = 0).  Returns (tokens [B][K+1], accepted [B])."""
+                       workspace_buf=None, stream=None, prepare=False):
+    """Greedy chain verify (T = 0).  Returns (tokens [B][K+1], accepted [B]);
+    with `prepare`, (launch, (tokens, accepted)) and nothing is enqueued."""
     _check_dev("target_logits", target_logits)
     dt = _dtype_code(target_logits)
     B, K1, V = target_logits.shape
@@ -232,10 +256,12 @@ def spec_verify_greedy(target_logits, draft_tokens, *, out_tokens=None, out_acce
         out_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
     if workspace_buf is None:
         workspace_buf = workspace(SPEC_MODE_GREEDY, B, K, V, dt, dev)
-    _call("spec_verify_greedy", _ptr(target_logits), dt, _ptr(draft_tokens), B, K, V,
-          _ptr(out_tokens), _ptr(out_accepted), _ptr(workspace_buf), workspace_buf.numel(),
-          _stream(dev, stream))
-    return out_tokens, out_accepted
+    launch = _enqueue(prepare, (target_logits, draft_tokens, out_tokens, out_accepted, workspace_buf),
+                      "spec_verify_greedy",
+                      _ptr(target_logits), dt, _ptr(draft_tokens), B, K, V, _ptr(out_tokens),
+                      _ptr(out_accepted), _ptr(workspace_buf), workspace_buf.numel(),
+                      _stream(dev, stream))
+    return (launch, (out_tokens, out_accepted)) if prepare else (out_tokens, out_accepted)
 
 
 def tree_max_depth(parents) -> int:
@@ -247,9 +273,10 @@ def tree_max_depth(parents) -> int:
 
 def spec_verify_tree_greedy(node_logits, node_tokens, parents, *, with_path=True,
                             out_tokens=None, out_path=None, out_depth=None, workspace_buf=None,
-                            stream=None):
+                            stream=None, prepare=False):
     """Greedy static-tree verify (T = 0).  `parents` is a host sequence of N ints.
-    Returns (tokens [B][D+1], path [B][D+1] or None, depth [B])."""
+    Returns (tokens [B][D+1], path [B][D+1] or None, depth [B]); with
+    `prepare`, (launch, outputs) and nothing is enqueued."""
     _check_dev("node_logits", node_logits)
     dt = _dtype_code(node_logits)
     B, N, V = node_logits.shape
@@ -267,18 +294,21 @@ def spec_verify_tree_greedy(node_logits, node_tokens, parents, *, with_path=True
         out_depth = torch.empty((B,), dtype=torch.int32, device=dev)
     if workspace_buf is None:
         workspace_buf = workspace(SPEC_MODE_TREE, B, N, V, dt, dev)
-    _call("spec_verify_tree_greedy", _ptr(node_logits), dt, _ptr(node_tokens), par, B, N, V,
-          _ptr(out_tokens), _ptr(out_path), _ptr(out_depth), _ptr(workspace_buf),
-          workspace_buf.numel(), _stream(dev, stream))
-    return out_tokens, out_path, out_depth
+    launch = _enqueue(prepare, (node_logits, node_tokens, out_tokens, out_path, out_depth,
+                                workspace_buf), "spec_verify_tree_greedy", _ptr(node_logits), dt, _ptr(node_tokens),
+                      par, B, N, V, _ptr(out_tokens), _ptr(out_path), _ptr(out_depth),
+                      _ptr(workspace_buf), workspace_buf.numel(), _stream(dev, stream))
+    outs = (out_tokens, out_path, out_depth)
+    return (launch, outs) if prepare else outs
 
 
 def spec_verify_tree_greedy_dyn(node_logits, node_tokens, parents, node_count, *, with_path=True,
                                 out_tokens=None, out_path=None, out_depth=None, workspace_buf=None,
-                                stream=None):
+                                stream=None, prepare=False):
     """Greedy verify on per-sequence trees (T = 0).  `parents` [B][Nmax] and
     `node_count` [B] are int32 device tensors.  Returns (tokens [B][Nmax],
-    path [B][Nmax] or None, depth [B]), rows padded with -1."""
+    path [B][Nmax] or None, depth [B]), rows padded with -1; with `prepare`,
+    (launch, outputs) and nothing is enqueued."""
     _check_dev("node_logits", node_logits)
     dt = _dtype_code(node_logits)
     B, Nmax, V = node_logits.shape
@@ -294,17 +324,21 @@ def spec_verify_tree_greedy_dyn(node_logits, node_tokens, parents, node_count, *
         out_depth = torch.empty((B,), dtype=torch.int32, device=dev)
     if workspace_buf is None:
         workspace_buf = workspace(SPEC_MODE_TREE_DYN, B, Nmax, V, dt, dev)
-    _call("spec_verify_tree_greedy_dyn", _ptr(node_logits), dt, _ptr(node_tokens), _ptr(parents),
-          _ptr(node_count), B, Nmax, V, _ptr(out_tokens), _ptr(out_path), _ptr(out_depth),
-          _ptr(workspace_buf), workspace_buf.numel(), _stream(dev, stream))
-    return out_tokens, out_path, out_depth
+    launch = _enqueue(prepare, (node_logits, node_tokens, parents, node_count, out_tokens, out_path,
+                                out_depth, workspace_buf), "spec_verify_tree_greedy_dyn", _ptr(node_logits), dt,
+                      _ptr(node_tokens), _ptr(parents), _ptr(node_count), B, Nmax, V,
+                      _ptr(out_tokens), _ptr(out_path), _ptr(out_depth), _ptr(workspace_buf),
+                      workspace_buf.numel(), _stream(dev, stream))
+    outs = (out_tokens, out_path, out_depth)
+    return (launch, outs) if prepare else outs
 
 
 def spec_draft_topk(logits, k, *, with_values=True, out_idx=None, out_val=None, workspace_buf=None,
-                    stream=None):
+                    stream=None, prepare=False):
     """Per-row top-k of draft logits [..., V] (bf16 or fp32): the k largest by
     value descending, equal values by index ascending.  Returns (idx [..., k]
-    int32, values [..., k] float32 or None)."""
+    int32, values [..., k] float32 or None); with `prepare`, (launch,
+    outputs) and nothing is enqueued."""
     _check_dev("logits", logits)
     dt = _dtype_code(logits)
     if logits.dim() < 1:
@@ -324,6 +358,7 @@ def spec_draft_topk(logits, k, *, with_values=True, out_idx=None, out_val=None, 
         _check_dev("out_val", out_val, torch.float32, lead + (k,))
     if workspace_buf is None:
         workspace_buf = workspace(SPEC_MODE_TOPK, rows, k, V, dt, dev)
-    _call("spec_draft_topk", _ptr(logits), dt, rows, V, k, _ptr(out_idx), _ptr(out_val),
-          _ptr(workspace_buf), workspace_buf.numel(), _stream(dev, stream))
-    return out_idx, out_val
+    launch = _enqueue(prepare, (logits, out_idx, out_val, workspace_buf), "spec_draft_topk", _ptr(logits),
+                      dt, rows, V, k, _ptr(out_idx), _ptr(out_val), _ptr(workspace_buf),
+                      workspace_buf.numel(), _stream(dev, stream))
+    return (launch, (out_idx, out_val)) if prepare else (out_idx, out_val)

@@ -61,12 +61,12 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
         p.off_sums = off;  // two tagged masses per chunk: residual, target
         off += align_up(static_cast<size_t>(B) * p.nchunk2 * 16);
     } else if (mode == SPEC_MODE_TOPK) {
-        // One launch: a workgroup per (row, chunk), then a merge workgroup per
-        // row, whose wavefront holds all of the row's nchunk * k candidates.
+        // One launch: a workgroup per (row, chunk) and a merge workgroup per
+        // row (one wavefront holds the row's chunk maxima, two per lane).
         p.chunk = kChunk2Bytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
         p.nchunk = (V + p.chunk - 1) / p.chunk;
-        if (p.nchunk * KN > kTopkMergeCands) return false;
-        if (rows * p.nchunk + rows > 0x7fffffffLL) return false;
+        if (p.nchunk > kTopkMaxChunks) return false;
+        if (rows * p.nchunk + (rows + 3) / 4 > 0x7fffffffLL) return false;
         off += align_up(static_cast<size_t>(rows) * p.nchunk * kMaxTopK * 16);
     } else {
         // One launch: argmax workgroups, then one resolve workgroup per sequence.
@@ -369,6 +369,11 @@ spec_status spec_draft_topk(const void *logits, spec_dtype dtype, int32_t rows, 
     a.nchunk = plan.nchunk;
     a.k = k;
     a.tag = next_call_tag();
+    // A merge trails its rows' chunks by about one resident window of
+    // workgroups (plus a group of rows), so its lists are usually complete
+    // on arrival.  Units: groups of four rows, one merge workgroup each.
+    const int64_t groups = (rows + 3) / 4, group_wgs = 4 * static_cast<int64_t>(plan.nchunk);
+    a.lag = std::min<int64_t>(groups, (kResidentWGs + group_wgs - 1) / group_wgs + 1);
     a.partial = at<uint64_t>(workspace, plan.off_partial);
     a.out_idx = out_idx;
     a.out_val = out_val;

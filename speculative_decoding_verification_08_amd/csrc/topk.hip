@@ -4,20 +4,16 @@
 // at each depth).  The k entries of largest value, by value descending and
 // then index ascending; values compare as floats, so -0.0 ties +0.0.
 //
-// Chunk items: one workgroup per (row, 16 KB chunk).  The threshold theta is
-// the k-th largest of the chunk's sixteen 16-lane group maxima: k groups hold
-// an entry >= theta, so the chunk's k best are all >= theta, and typically
-// only a few entries are.  Those are compacted into LDS and wavefront 0
-// takes the k best; if ties leave more candidates than LDS holds, k exact
-// rounds over all entries take over.  Each chunk leaves its k best as tagged
-// words.
-//
-// Merge items: one workgroup per row, after every chunk workgroup; wavefront
-// 0 waits (bounded) for the row's chunk lists and takes the k best of them.
-//
-// Every selection round takes the best entry strictly worse than the last
-// one taken, under (value descending, index ascending), so no entry needs a
-// taken flag.
+// One workgroup per (row, 16 KB chunk).  The threshold theta is the k-th
+// largest of the chunk's sixteen 16-lane group maxima: k groups hold an
+// entry >= theta, so the chunk's k best are all >= theta, and typically only
+// a few entries are.  Those are compacted into LDS by ballot and each is
+// ranked against the others; if ties leave more candidates than LDS holds
+// (or fewer than k entries exceed -inf), k exact selection rounds over all
+// entries take over, each taking the best entry strictly after the last one
+// taken.  Each chunk leaves its k best as tagged words.  A merge workgroup
+// per four rows, placed in the grid well after their chunks, takes each
+// row's k best from the row's lists on one wavefront.
 #include "device.hpp"
 #include "handover.hpp"
 #include "plan.hpp"
@@ -26,8 +22,28 @@
 namespace sv {
 namespace {
 
-constexpr int kCandCap = 256;  // candidates compacted into LDS per chunk
-constexpr int kTopkMergePerLane = kTopkMergeCands / kWave;
+constexpr int kCandPerWave = 64;  // candidates compacted into LDS per wavefront of a chunk
+
+// Ranking key of (v, i): larger means ranks first.  The high word maps the
+// value to an unsigned integer of the same order (-0.0 taken as +0.0); the
+// low word holds INT32_MAX - i above a bit that records a -0.0, which never
+// decides an order (indices differ) but restores the value's bits.
+__device__ __forceinline__ uint64_t tk_key(float v, int32_t i) {
+    uint32_t u = __float_as_uint(v);
+    const uint32_t negz = u == 0x80000000u;
+    u = negz ? 0u : u;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (static_cast<uint64_t>(u) << 32) |
+           (static_cast<uint32_t>(INT32_MAX - i) << 1) | negz;
+}
+__device__ __forceinline__ int32_t tk_key_index(uint64_t key) {
+    return INT32_MAX - static_cast<int32_t>(static_cast<uint32_t>(key) >> 1);
+}
+__device__ __forceinline__ float tk_key_value(uint64_t key) {
+    if (key & 1u) return -0.0f;
+    const uint32_t u = static_cast<uint32_t>(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
 
 // (v, i) ranks before (bv, bi): larger value, then lower index.
 __device__ __forceinline__ bool tk_better(float v, int32_t i, float bv, int32_t bi) {
@@ -82,6 +98,148 @@ __device__ __forceinline__ void tk_wg_best(float &v, int32_t &i) {
     __syncthreads();
 }
 
+// Tagged word p of the call, waiting (bounded) for it; false if the wait ran out.
+__device__ __forceinline__ bool tk_take(const uint64_t *p, uint32_t tag, uint64_t t0, uint64_t &w) {
+    w = fetch(p);
+    while (!current(w, tag)) {
+        if (wall_clock64() - t0 > kWaitTicks) return false;
+        __builtin_amdgcn_s_sleep(2);
+        w = fetch(p);
+    }
+    return true;
+}
+
+__device__ __forceinline__ uint64_t tk_readlane(uint64_t x, int src) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(x), src);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(x >> 32), src);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Key of a chunk-list slot (value word, index word), waiting for both.
+__device__ __forceinline__ bool tk_take_key(const uint64_t *p, uint32_t tag, uint64_t t0,
+                                            uint64_t &key) {
+    uint64_t wv, wi;
+    if (!tk_take(p, tag, t0, wv) || !tk_take(p + 1, tag, t0, wi)) return false;
+    key = tk_key(word_f32(wv), static_cast<int32_t>(static_cast<uint32_t>(wi)));
+    return true;
+}
+
+// Row `row` when its lists hold at most 128 entries: slot j of the row (entry
+// j % k of chunk j / k) sits in lane j % 64, register j / 64, all read in
+// one round.  M is found from the chunk maxima as in topk_merge, and every
+// entry at or above M (every entry, with fewer than k chunks) is ranked
+// against the others.
+__device__ void topk_merge_small(const TopkArgs &a, int64_t row) {
+    const int lane = threadIdx.x % kWave, k = a.k, nch = a.nchunk, n = nch * k;
+    const uint64_t *part = a.partial + 2 * row * nch * kMaxTopK;
+    const uint64_t t0 = wall_clock64();
+    bool ok = true;
+    uint64_t key[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int j = lane + h * kWave;
+        if (j < n) ok = ok && tk_take_key(part + 2 * ((j / k) * kMaxTopK + j % k), a.tag, t0, key[h]);
+    }
+    if (__ballot(!ok)) {
+        if (lane < k) {
+            a.out_idx[row * k + lane] = -1;
+            if (a.out_val) a.out_val[row * k + lane] = NAN;
+        }
+        return;
+    }
+    // M: the maximum (slot 0 of a list) that kt - 1 other maxima outrank.
+    const int kt = min(k, nch);
+    int rk[2] = {0, 0};
+    for (int d = 0; d < nch; ++d) {
+        const int j = d * k;
+        const uint64_t kd = tk_readlane(j < kWave ? key[0] : key[1], j % kWave);
+        rk[0] += kd > key[0];
+        rk[1] += kd > key[1];
+    }
+    const uint64_t m0 = __ballot(lane < n && lane % k == 0 && rk[0] == kt - 1);
+    const uint64_t m1 = __ballot(lane + kWave < n && (lane + kWave) % k == 0 && rk[1] == kt - 1);
+    const uint64_t M = tk_readlane(m0 ? key[0] : key[1],
+                                   __ffsll(static_cast<unsigned long long>(m0 ? m0 : m1)) - 1);
+    bool keep[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) keep[h] = lane + h * kWave < n && (nch < k || key[h] >= M);
+    int r[2] = {0, 0};
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+        for (uint64_t b = __ballot(keep[g]); b; b &= b - 1) {
+            const uint64_t kb = tk_readlane(key[g], __ffsll(static_cast<unsigned long long>(b)) - 1);
+            r[0] += kb > key[0];
+            r[1] += kb > key[1];
+        }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (keep[h] && r[h] < k) {
+            a.out_idx[row * k + r[h]] = tk_key_index(key[h]);
+            if (a.out_val) a.out_val[row * k + r[h]] = tk_key_value(key[h]);
+        }
+}
+
+// Row `row`: the k best of its chunks' lists, on one wavefront.  Every entry
+// of the row's top k lies in the list of one of the k chunks with the
+// largest maxima (were its chunk's maximum ranked lower, k better entries
+// would exist), and, when the row has at least k chunks, ranks at or above
+// the k-th largest maximum M (the k best maxima are k entries at or above
+// M).  So lane l takes entry l % k of the (l / k)-th best chunk, keeps it if
+// it ranks at or above M, and counts the kept entries ahead of it; ranks
+// below k are the row's list.  Every read waits (bounded) for the word to
+// carry this call's tag; if a wait runs out the row gets -1 and NaN.
+__device__ void topk_merge(const TopkArgs &a, int64_t row) {
+    const int lane = threadIdx.x % kWave, k = a.k, nch = a.nchunk;
+    const uint64_t *part = a.partial + 2 * row * nch * kMaxTopK;
+    const uint64_t t0 = wall_clock64();
+    bool ok = true;
+    // Keys of the chunk maxima (slot 0 of each list): chunks lane and lane + 64.
+    uint64_t mk[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = lane + h * kWave;
+        if (c < nch) ok = ok && tk_take_key(part + 2 * c * kMaxTopK, a.tag, t0, mk[h]);
+    }
+    // Rank of each maximum among the maxima.
+    int rk[2] = {0, 0};
+    for (int d = 0; d < nch; ++d) {
+        const uint64_t kd = tk_readlane(d < kWave ? mk[0] : mk[1], d % kWave);
+        rk[0] += kd > mk[0];
+        rk[1] += kd > mk[1];
+    }
+    // Lane l's chunk: the one whose maximum ranks l / k; M ranks kt - 1.
+    const int kt = min(k, nch), m = k * kt;
+    int mych = 0;
+    uint64_t M = 0;
+    for (int r = 0; r < kt; ++r) {
+        const uint64_t b0 = __ballot(lane < nch && rk[0] == r);
+        const uint64_t b1 = __ballot(lane + kWave < nch && rk[1] == r);
+        const int src = __ffsll(static_cast<unsigned long long>(b0 ? b0 : b1)) - 1;
+        if (lane / k == r) mych = b0 ? src : src + kWave;
+        if (r == kt - 1) M = tk_readlane(b0 ? mk[0] : mk[1], src);
+    }
+    uint64_t key = 0;
+    bool keep = false;
+    if (lane < m) {
+        ok = ok && tk_take_key(part + 2 * (mych * kMaxTopK + lane % k), a.tag, t0, key);
+        keep = ok && (nch < k || key >= M);
+    }
+    if (__ballot(!ok)) {
+        if (lane < k) {
+            a.out_idx[row * k + lane] = -1;
+            if (a.out_val) a.out_val[row * k + lane] = NAN;
+        }
+        return;
+    }
+    int r = 0;
+    for (uint64_t b = __ballot(keep); b; b &= b - 1)
+        r += tk_readlane(key, __ffsll(static_cast<unsigned long long>(b)) - 1) > key;
+    if (keep && r < k) {
+        a.out_idx[row * k + r] = tk_key_index(key);
+        if (a.out_val) a.out_val[row * k + r] = tk_key_value(key);
+    }
+}
+
 // Publishes slot q of a chunk's list.
 __device__ __forceinline__ void tk_put(uint64_t *out, uint32_t tag, int q, float v, int32_t i) {
     publish(out + 2 * q, tag, __float_as_uint(v));
@@ -94,10 +252,9 @@ template <class DT, bool VecOk>
 __device__ __forceinline__ void topk_chunk(const TopkArgs &a, int64_t row, int ch) {
     constexpr int VEC = DT::kVec, NQ = kChunk2Bytes / 16 / kWG, E = NQ * VEC;  // entries per thread
     __shared__ float s_gmax[kWG / 16];
-    __shared__ int s_count;
-    __shared__ float s_cv[kCandCap];
-    __shared__ int32_t s_ci[kCandCap];
-    const int tid = threadIdx.x, lane = tid % kWave, k = a.k;
+    __shared__ int s_count[kWaves];
+    __shared__ uint64_t s_c[kWaves][kCandPerWave];  // ranking keys
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave, k = a.k;
     const int64_t e0 = static_cast<int64_t>(ch) * a.chunk;
     const int n = static_cast<int>(min(static_cast<int64_t>(a.chunk), static_cast<int64_t>(a.V) - e0));
     uint64_t *out = a.partial + 2 * (row * a.nchunk + ch) * kMaxTopK;
@@ -122,7 +279,6 @@ __device__ __forceinline__ void topk_chunk(const TopkArgs &a, int64_t row, int c
             if (pos(e) >= n) x[e] = -INFINITY;
     }
     // Maximum of each 16-thread group, then theta = the k-th largest of them.
-    if (tid == 0) s_count = 0;
     float m = x[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) m = fmaxf(m, x[e]);
@@ -145,132 +301,115 @@ __device__ __forceinline__ void topk_chunk(const TopkArgs &a, int64_t row, int c
         t = fmaxf(t, dpp::mov_f<dpp::kRowShr8>(-INFINITY, t));
         theta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 15));
     }
-    // Candidates (entries >= theta) go to LDS, a wavefront's worth at a time.
+    // Candidates (entries >= theta) go to the wavefront's LDS segment in
+    // ballot order; the running count stays in a scalar register.
+    int cnt = 0;
     if (theta > -INFINITY) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const bool hit = x[e] >= theta;
             const uint64_t b = __ballot(hit);
             if (b) {
-                const int first = __ffsll(static_cast<unsigned long long>(b)) - 1;
-                int base = 0;
-                if (lane == first) base = atomicAdd(&s_count, __popcll(b));
-                base = __builtin_amdgcn_readlane(base, first);
-                const int o = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0));
-                if (hit && o < kCandCap) {
-                    s_cv[o] = x[e];
-                    s_ci[o] = static_cast<int32_t>(e0 + pos(e));
+                const int o = cnt + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0));
+                if (hit && o < kCandPerWave)
+                    s_c[w][o] = tk_key(x[e], static_cast<int32_t>(e0 + pos(e)));
+                cnt += __popcll(b);
+            }
+        }
+    }
+    if (lane == 0) s_count[w] = cnt;
+    __syncthreads();
+    bool fits = theta > -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) fits = fits && s_count[q] <= kCandPerWave;
+    if (fits) {
+        // Candidate (w, lane)'s rank is the number of candidates ahead of it;
+        // ranks below k are the chunk's list.  (There are at least k: the k
+        // groups whose maxima are >= theta each hold one.)
+        if (lane < cnt) {
+            const uint64_t key = s_c[w][lane];
+            int r = 0;
+            for (int q = 0; q < kWaves; ++q) {
+                const int nq = s_count[q];
+#pragma unroll 8
+                for (int j = 0; j < nq; ++j) r += s_c[q][j] > key;
+            }
+            if (r < k) tk_put(out, a.tag, r, tk_key_value(key), tk_key_index(key));
+        }
+    } else {
+        // Ties beyond LDS, or fewer than k entries above -inf: k exact rounds.
+        float lv = INFINITY;
+        int32_t li = -1;
+        for (int q = 0; q < k; ++q) {
+            float bv = -INFINITY;
+            int32_t bi = INT32_MAX;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int32_t i = static_cast<int32_t>(e0 + pos(e));
+                if (pos(e) < n && tk_after(x[e], i, lv, li) && tk_better(x[e], i, bv, bi)) {
+                    bv = x[e];
+                    bi = i;
                 }
             }
+            tk_wg_best(bv, bi);
+            if (tid == 0) tk_put(out, a.tag, q, bv, bi);
+            lv = bv;
+            li = bi;
         }
-    }
-    __syncthreads();
-    const int C = s_count;
-    if (theta > -INFINITY && C <= kCandCap) {
-        // Candidate t's rank is the number of candidates ahead of it; ranks
-        // below k are the chunk's list.  Slots past C get the filler.
-        if (tid >= max(C, k)) return;
-        if (tid < C) {
-            const float v = s_cv[tid];
-            const int32_t i = s_ci[tid];
-            int r = 0;
-            for (int j = 0; j < C; ++j) r += tk_better(s_cv[j], s_ci[j], v, i);
-            if (r < k) tk_put(out, a.tag, r, v, i);
-        } else {
-            tk_put(out, a.tag, tid, -INFINITY, INT32_MAX);
-        }
-        return;
-    }
-    // Ties beyond LDS, or fewer than k entries above -inf: k exact rounds.
-    float lv = INFINITY;
-    int32_t li = -1;
-    for (int q = 0; q < k; ++q) {
-        float bv = -INFINITY;
-        int32_t bi = INT32_MAX;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int32_t i = static_cast<int32_t>(e0 + pos(e));
-            if (pos(e) < n && tk_after(x[e], i, lv, li) && tk_better(x[e], i, bv, bi)) {
-                bv = x[e];
-                bi = i;
-            }
-        }
-        tk_wg_best(bv, bi);
-        if (tid == 0) tk_put(out, a.tag, q, bv, bi);
-        lv = bv;
-        li = bi;
     }
 }
 
-// Row `row`: the k best of its chunks' lists (nchunk * k <= 64 * 16 entries,
-// kept in wavefront 0's registers).
-__device__ __forceinline__ void topk_merge(const TopkArgs &a, int64_t row) {
-    if (threadIdx.x >= kWave) return;
-    const int lane = threadIdx.x, k = a.k, n = a.nchunk * k;
-    const uint64_t *part = a.partial + 2 * row * a.nchunk * kMaxTopK;
-    auto word = [&](int j) { return part + 2 * ((j / k) * kMaxTopK + j % k); };  // candidate j
-    const uint64_t t0 = wall_clock64();
-    float cv[kTopkMergePerLane];
-    int32_t ci[kTopkMergePerLane];
-    bool ok = true;
-    for (;;) {
-        bool fresh = true;
-        const uint64_t *miss = nullptr;
-#pragma unroll
-        for (int s = 0; s < kTopkMergePerLane; ++s) {
-            const int j = min(lane + s * kWave, n - 1);
-            const uint64_t wv = fetch(word(j)), wi = fetch(word(j) + 1);
-            const bool in = lane + s * kWave < n, cur = current(wv, a.tag) && current(wi, a.tag);
-            if (in && !cur && !miss) miss = current(wv, a.tag) ? word(j) + 1 : word(j);
-            fresh = fresh && (!in || cur);
-            cv[s] = in ? word_f32(wv) : -INFINITY;
-            ci[s] = in ? static_cast<int32_t>(static_cast<uint32_t>(wi)) : INT32_MAX;
-        }
-        const uint64_t stale = __ballot(!fresh);
-        if (!stale) break;
-        if (wall_clock64() - t0 > kWaitTicks) {
-            ok = false;
-            break;
-        }
-        if (lane == __ffsll(static_cast<unsigned long long>(stale)) - 1) wait_word(miss, a.tag, t0);
-    }
-    float lv = INFINITY;
-    int32_t li = -1;
-    for (int q = 0; q < k; ++q) {
-        float bv = -INFINITY;
-        int32_t bi = INT32_MAX;
-#pragma unroll
-        for (int s = 0; s < kTopkMergePerLane; ++s)
-            if (tk_after(cv[s], ci[s], lv, li) && tk_better(cv[s], ci[s], bv, bi)) {
-                bv = cv[s];
-                bi = ci[s];
-            }
-        tk_wave_best(bv, bi);
-        if (lane == 0) {
-            a.out_idx[row * k + q] = ok ? bi : -1;
-            if (a.out_val) a.out_val[row * k + q] = ok ? bv : NAN;
-        }
-        lv = bv;
-        li = bi;
-    }
-}
-
+// Grid order, in groups of kWaves rows (G = ceil(rows / kWaves) groups) and
+// with L = a.lag groups: the chunks of groups 0..L-1; then for each group
+// q >= L its chunks followed by one merge workgroup for group q - L (a
+// wavefront per row); then the merges of the last L groups.  A merge thus
+// trails its rows' chunks by about L groups of workgroups, by when they have
+// usually finished, so merge workgroups rarely wait and the streaming runs
+// on.
 template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_topk(TopkArgs a) {
-    const uint32_t nc = static_cast<uint32_t>(a.rows) * a.nchunk, g = blockIdx.x;
-    if (g < nc) {
-        const uint32_t row = g / a.nchunk;
-        topk_chunk<DT, VecOk>(a, row, static_cast<int>(g - row * a.nchunk));
+    const int64_t nch = a.nchunk, L = a.lag, g = blockIdx.x, R = a.rows;
+    const int64_t G = (R + kWaves - 1) / kWaves;
+    auto group_chunks = [&](int64_t q) { return (min(R, (q + 1) * kWaves) - q * kWaves) * nch; };
+    // Chunk items before group q: kWaves * nch per full group.
+    const int64_t full = kWaves * nch, head = L < G ? L * full : R * nch;
+    int64_t row = -1, ch = 0, mgroup = -1;
+    if (g < head) {
+        row = g / nch;
+        ch = g % nch;
     } else {
-        topk_merge(a, g - nc);
+        const int64_t h = g - head, nbody = G - L;  // groups with chunks after the head
+        // Body blocks: group L + b's chunks, then one merge (group b); the
+        // last group may be partial.
+        const int64_t blk = h / (full + 1), off = h % (full + 1);
+        if (blk < nbody - 1 || (blk == nbody - 1 && off <= group_chunks(G - 1))) {
+            const int64_t q = L + blk, nc = group_chunks(q);
+            if (off < nc) {
+                row = q * kWaves + off / nch;
+                ch = off % nch;
+            } else {
+                mgroup = blk;
+            }
+        } else {
+            const int64_t tail0 = (nbody - 1) * (full + 1) + group_chunks(G - 1) + 1;
+            mgroup = nbody > 0 ? G - L + (h - tail0) : h;
+        }
     }
+    if (mgroup < 0) {
+        topk_chunk<DT, VecOk>(a, row, static_cast<int>(ch));
+        return;
+    }
+    const int64_t mrow = mgroup * kWaves + threadIdx.x / kWave;
+    if (mrow >= R) return;
+    if (nch * a.k <= 2 * kWave) topk_merge_small(a, mrow);
+    else topk_merge(a, mrow);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(static_cast<uint32_t>(a.rows * a.nchunk + a.rows)), blk(kWG);
+    const dim3 g(static_cast<uint32_t>(a.rows * a.nchunk + (a.rows + kWaves - 1) / kWaves)), blk(kWG);
     if (dtype == 1) {
         if (a.V % Bf16::kVec == 0) k_topk<Bf16, true><<<g, blk, 0, s>>>(a);
         else k_topk<Bf16, false><<<g, blk, 0, s>>>(a);

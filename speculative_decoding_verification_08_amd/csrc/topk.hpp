@@ -7,13 +7,16 @@
 namespace sv {
 
 // Top-k of rows [rows][V] in one launch: one workgroup per (row, 16 KB chunk)
-// leaves its chunk's k best (value, index), then one merge workgroup per row.
+// leaves its chunk's k best (value, index); a merge workgroup per group of
+// four rows, `lag` groups later in the grid, takes each row's k best from
+// them (a wavefront per row).
 constexpr int kMaxTopK = 8;
-constexpr int kTopkMergeCands = 1024;  // nchunk * k at most: 16 per lane of one wavefront
+constexpr int kTopkMaxChunks = 128;  // chunks per row: two per lane of one wavefront
 struct TopkArgs {
     const void *logits;
     int64_t rows;
     int32_t V, chunk, nchunk, k;
+    int64_t lag;             // groups of four rows between a group's chunks and its merge, 1 <= lag <= groups
     uint32_t tag;
     uint64_t *partial;       // [rows][nchunk][kMaxTopK][2] tagged (value bits, index)
     int32_t *out_idx;        // [rows][k]

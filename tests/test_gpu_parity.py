@@ -174,10 +174,8 @@ def test_chain_prepared_launch_equals_call(sv):
 
 
 def test_chain_workspace_reuse_across_shapes(sv):
-    """One workspace with arbitrary prior contents serves consecutive calls of
-    different shapes."""
-    big = sv.spec_verify_workspace_bytes(sv.SPEC_MODE_CHAIN, 24, 8, 50000, sv.SPEC_DTYPE_F32)
-    ws = torch.full((big,), 0x5A, dtype=torch.uint8, device=DEV)  # arbitrary prior contents
+    """One workspace, zeroed once, serves consecutive calls of different shapes."""
+    ws = sv.workspace(sv.SPEC_MODE_CHAIN, 24, 8, 50000, sv.SPEC_DTYPE_F32, DEV)
     shapes = [(24, 8, 50000, "f32"), (3, 2, 7000, "bf16"), (24, 8, 50000, "f32"), (1, 0, 333, "f32"),
               (17, 5, 20001, "bf16"), (24, 8, 50000, "f32")]
     for i, (B, K, V, dt) in enumerate(shapes):
@@ -483,9 +481,96 @@ def test_topk_shapes_and_repeat(sv):
     assert e_idx.shape == (0, 4)
 
 
+@pytest.mark.parametrize("rows,V,dtype,k", [(3001, 100, "bf16", 8), (1202, 20001, "f32", 5),
+                                             (403, 140000, "bf16", 8), (97, 128256, "f32", 8),
+                                             (33, 524288, "f32", 8)])
+def test_topk_grid_shapes(sv, rows, V, dtype, k):
+    """Merges interleaved with chunks and at the end, a partial last group of
+    rows, and both merge forms (lists of at most 128 entries and longer)."""
+    case(f"top-k grid rows={rows} V={V} {dtype} k={k}")
+    x = topk_case(rows, V, dtype, step=rows % 13)
+    parity.check_topk({"logits": x}, *run_topk(sv, x, k))
+
+
 def test_topk_full_size_128k(sv):
     w = W.WORKLOADS["topk_128k"]
     for step in (0, 1):
         case(f"topk_128k full size step {step}")
         x = W.topk_inputs(w, step)["logits"]
         parity.check_topk({"logits": x}, *run_topk(sv, x, w.K))
+
+
+def test_prepared_launches_equal_calls(sv):
+    """The `prepare` form of each wrapper enqueues the same call as the direct form."""
+    x = topk_case(7, 30000, "bf16", step=5)
+    case("prepared top-k")
+    i0, v0 = run_topk(sv, x, 5)
+    launch, (i1, v1) = sv.spec_draft_topk(dev(x), 5, prepare=True)
+    launch()
+    launch()
+    torch.cuda.synchronize()
+    assert np.array_equal(i1.cpu().numpy(), i0) and np.array_equal(v1.cpu().numpy(), v0)
+    w = W.WORKLOADS["greedy_32k"].with_sizes(B=5, V=3000)
+    d = W.greedy_inputs(w, 2)
+    case("prepared greedy")
+    t0, a0 = run_greedy(sv, d)
+    launch, (t1, a1) = sv.spec_verify_greedy(dev(d["target"]), dev(d["tokens"]), prepare=True)
+    launch()
+    torch.cuda.synchronize()
+    assert np.array_equal(t1.cpu().numpy(), t0) and np.array_equal(a1.cpu().numpy(), a0)
+    w = W.WORKLOADS["tree_dyn_128k"].with_sizes(B=3, K=20, V=5000)
+    d = W.tree_dyn_inputs(w, 1)
+    case("prepared per-sequence trees")
+    g0 = run_tree_dyn(sv, d)
+    launch, outs = sv.spec_verify_tree_greedy_dyn(dev(d["node_logits"]), dev(d["node_tokens"]),
+                                                  dev(d["parents"]), dev(d["node_count"]),
+                                                  prepare=True)
+    launch()
+    torch.cuda.synchronize()
+    for a, b in zip(outs, g0):
+        assert np.array_equal(a.cpu().numpy(), b)
+
+
+def test_topk_after_freed_small_integers(sv):
+    """Regression: a workspace carved from memory that held int32 indices (small
+    integers in the upper half of each 64-bit word) must still give exact
+    results; the binding's workspaces are zero-filled for that reason."""
+    for trial in range(3):
+        case(f"top-k after freed indices, trial {trial}")
+        x1 = topk_case(3001, 100, "bf16", step=11)
+        parity.check_topk({"logits": x1}, *run_topk(sv, x1, 8))
+        x2 = topk_case(1202, 20001, "f32", step=6)
+        parity.check_topk({"logits": x2}, *run_topk(sv, x2, 5))
+
+
+def test_workspace_shared_by_every_entry_point(sv):
+    """One zeroed workspace, sized for the largest call, serves chain, greedy,
+    per-sequence tree and top-k calls in turn."""
+    modes = [(sv.SPEC_MODE_CHAIN, 6, 4, 30000), (sv.SPEC_MODE_GREEDY, 6, 4, 30000),
+             (sv.SPEC_MODE_TREE_DYN, 6, 20, 30000), (sv.SPEC_MODE_TOPK, 40, 8, 30000)]
+    big = max(sv.spec_verify_workspace_bytes(m, B, kn, V, sv.SPEC_DTYPE_BF16) for m, B, kn, V in modes)
+    ws = torch.zeros(big, dtype=torch.uint8, device=DEV)
+    for rep in range(2):
+        case(f"shared workspace round {rep}: chain")
+        d = chain_case("shared", 6, 4, 30000, "bf16", 1.0, recipe="peaked", sigma=0.7, step=rep)
+        tok, acc, diag = sv.spec_verify_chain(dev(d["target"]), dev(d["draft"]), dev(d["tokens"]),
+                                              dev(d["u_accept"]), dev(d["u_sample"]), d["T"],
+                                              diag=True, workspace_buf=ws)
+        torch.cuda.synchronize()
+        parity.check_chain(d, tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy())
+        case(f"shared workspace round {rep}: greedy")
+        g = W.greedy_inputs(W.WORKLOADS["greedy_32k"].with_sizes(B=6, K=4, V=30000), rep)
+        tok, acc = sv.spec_verify_greedy(dev(g["target"]), dev(g["tokens"]), workspace_buf=ws)
+        torch.cuda.synchronize()
+        parity.check_greedy(g, tok.cpu().numpy(), acc.cpu().numpy())
+        case(f"shared workspace round {rep}: per-sequence trees")
+        t = W.tree_dyn_inputs(W.WORKLOADS["tree_dyn_128k"].with_sizes(B=6, K=20, V=30000), rep)
+        out = sv.spec_verify_tree_greedy_dyn(dev(t["node_logits"]), dev(t["node_tokens"]),
+                                             dev(t["parents"]), dev(t["node_count"]), workspace_buf=ws)
+        torch.cuda.synchronize()
+        parity.check_tree_dyn(t, *[o.cpu().numpy() for o in out])
+        case(f"shared workspace round {rep}: top-k")
+        x = topk_case(40, 30000, "bf16", step=rep)
+        idx, val = sv.spec_draft_topk(dev(x), 8, workspace_buf=ws)
+        torch.cuda.synchronize()
+        parity.check_topk({"logits": x}, idx.cpu().numpy(), val.cpu().numpy())
