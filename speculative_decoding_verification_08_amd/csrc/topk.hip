@@ -7,8 +7,8 @@
 // One workgroup per (row, 16 KB chunk).  The threshold theta is the k-th
 // largest of the chunk's sixteen 16-lane group maxima: k groups hold an
 // entry >= theta, so the chunk's k best are all >= theta, and typically only
-// a few entries are.  Those are compacted into LDS by ballot and each is
-// ranked against the others; if ties leave more candidates than LDS holds
+// a few entries are.  Those are compacted into LDS by ballot, and one
+// wavefront ranks them, one per lane; if ties leave more than 64 candidates
 // (or fewer than k entries exceed -inf), k exact selection rounds over all
 // entries take over, each taking the best entry strictly after the last one
 // taken.  Each chunk leaves its k best as tagged words.  A merge workgroup
@@ -45,25 +45,17 @@ __device__ __forceinline__ float tk_key_value(uint64_t key) {
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
-// (v, i) ranks before (bv, bi): larger value, then lower index.
-__device__ __forceinline__ bool tk_better(float v, int32_t i, float bv, int32_t bi) {
-    return v > bv || (v == bv && i < bi);
-}
-// (v, i) ranks after (lv, li), the last entry taken.
-__device__ __forceinline__ bool tk_after(float v, int32_t i, float lv, int32_t li) {
-    return tk_better(lv, li, v, i);
-}
+// Key of the filler (-inf, INT32_MAX): below every entry's key.
+constexpr uint64_t kFillKey = static_cast<uint64_t>(0x007fffffu) << 32;
 
-// Wavefront argmax of (v, i) under tk_better; the result in every lane.
-__device__ __forceinline__ void tk_wave_best(float &v, int32_t &i) {
-#define SV_TK_STEP(CTRL, MASK)                                                 \
-    {                                                                          \
-        const float v2 = dpp::mov_f<CTRL, MASK>(-INFINITY, v);                 \
-        const int32_t i2 = dpp::mov_i<CTRL, MASK>(INT32_MAX, i);               \
-        if (tk_better(v2, i2, v, i)) {                                         \
-            v = v2;                                                            \
-            i = i2;                                                            \
-        }                                                                      \
+// Wavefront maximum of a key; the result in every lane.
+__device__ __forceinline__ uint64_t tk_wave_max_key(uint64_t x) {
+#define SV_TK_STEP(CTRL, MASK)                                                               \
+    {                                                                                        \
+        const uint32_t lo = dpp::mov_i<CTRL, MASK>(0, static_cast<int>(x));                  \
+        const uint32_t hi = dpp::mov_i<CTRL, MASK>(0, static_cast<int>(x >> 32));            \
+        const uint64_t y = (static_cast<uint64_t>(hi) << 32) | lo;                           \
+        x = y > x ? y : x;                                                                   \
     }
     SV_TK_STEP(dpp::kRowShr1, 0xF)
     SV_TK_STEP(dpp::kRowShr2, 0xF)
@@ -72,41 +64,22 @@ __device__ __forceinline__ void tk_wave_best(float &v, int32_t &i) {
     SV_TK_STEP(dpp::kRowBcast15, 0xA)
     SV_TK_STEP(dpp::kRowBcast31, 0xC)
 #undef SV_TK_STEP
-    v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
-    i = __builtin_amdgcn_readlane(i, kWave - 1);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(x), kWave - 1);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(x >> 32), kWave - 1);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// Workgroup argmax of (v, i); the result in every thread.  Two barriers.
-__device__ __forceinline__ void tk_wg_best(float &v, int32_t &i) {
-    __shared__ float s_v[kWaves];
-    __shared__ int32_t s_i[kWaves];
-    tk_wave_best(v, i);
-    const int w = threadIdx.x / kWave;
-    if (threadIdx.x % kWave == 0) {
-        s_v[w] = v;
-        s_i[w] = i;
-    }
+// Workgroup maximum of a key; the result in every thread.  Two barriers.
+__device__ __forceinline__ uint64_t tk_wg_max_key(uint64_t x) {
+    __shared__ uint64_t s_k[kWaves];
+    x = tk_wave_max_key(x);
+    if (threadIdx.x % kWave == 0) s_k[threadIdx.x / kWave] = x;
     __syncthreads();
-    v = s_v[0];
-    i = s_i[0];
+    x = s_k[0];
 #pragma unroll
-    for (int q = 1; q < kWaves; ++q)
-        if (tk_better(s_v[q], s_i[q], v, i)) {
-            v = s_v[q];
-            i = s_i[q];
-        }
+    for (int q = 1; q < kWaves; ++q) x = s_k[q] > x ? s_k[q] : x;
     __syncthreads();
-}
-
-// Tagged word p of the call, waiting (bounded) for it; false if the wait ran out.
-__device__ __forceinline__ bool tk_take(const uint64_t *p, uint32_t tag, uint64_t t0, uint64_t &w) {
-    w = fetch(p);
-    while (!current(w, tag)) {
-        if (wall_clock64() - t0 > kWaitTicks) return false;
-        __builtin_amdgcn_s_sleep(2);
-        w = fetch(p);
-    }
-    return true;
+    return x;
 }
 
 __device__ __forceinline__ uint64_t tk_readlane(uint64_t x, int src) {
@@ -115,12 +88,30 @@ __device__ __forceinline__ uint64_t tk_readlane(uint64_t x, int src) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// Key of a chunk-list slot (value word, index word), waiting for both.
-__device__ __forceinline__ bool tk_take_key(const uint64_t *p, uint32_t tag, uint64_t t0,
-                                            uint64_t &key) {
-    uint64_t wv, wi;
-    if (!tk_take(p, tag, t0, wv) || !tk_take(p + 1, tag, t0, wi)) return false;
-    key = tk_key(word_f32(wv), static_cast<int32_t>(static_cast<uint32_t>(wi)));
+// Keys of up to H chunk-list slots (value word, index word each): every word
+// is read at once, then any that lacks the call's tag is read again (bounded
+// wait) until it has it.  False if a wait ran out.
+template <int H>
+__device__ __forceinline__ bool tk_take_keys(const uint64_t *const (&p)[H], const bool (&in)[H],
+                                             uint32_t tag, uint64_t t0, uint64_t (&key)[H]) {
+    uint64_t wv[H], wi[H];
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+        if (in[h]) {
+            wv[h] = fetch(p[h]);
+            wi[h] = fetch(p[h] + 1);
+        }
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+        if (in[h]) {
+            while (!current(wv[h], tag) || !current(wi[h], tag)) {
+                if (wall_clock64() - t0 > kWaitTicks) return false;
+                __builtin_amdgcn_s_sleep(2);
+                wv[h] = fetch(p[h]);
+                wi[h] = fetch(p[h] + 1);
+            }
+            key[h] = tk_key(word_f32(wv[h]), static_cast<int32_t>(static_cast<uint32_t>(wi[h])));
+        }
     return true;
 }
 
@@ -133,13 +124,16 @@ __device__ void topk_merge_small(const TopkArgs &a, int64_t row) {
     const int lane = threadIdx.x % kWave, k = a.k, nch = a.nchunk, n = nch * k;
     const uint64_t *part = a.partial + 2 * row * nch * kMaxTopK;
     const uint64_t t0 = wall_clock64();
-    bool ok = true;
     uint64_t key[2] = {0, 0};
+    const uint64_t *p[2];
+    bool in[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int j = lane + h * kWave;
-        if (j < n) ok = ok && tk_take_key(part + 2 * ((j / k) * kMaxTopK + j % k), a.tag, t0, key[h]);
+        in[h] = j < n;
+        p[h] = part + 2 * ((j / k) * kMaxTopK + j % k);
     }
+    const bool ok = tk_take_keys<2>(p, in, a.tag, t0, key);
     if (__ballot(!ok)) {
         if (lane < k) {
             a.out_idx[row * k + lane] = -1;
@@ -195,10 +189,10 @@ __device__ void topk_merge(const TopkArgs &a, int64_t row) {
     bool ok = true;
     // Keys of the chunk maxima (slot 0 of each list): chunks lane and lane + 64.
     uint64_t mk[2] = {0, 0};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int c = lane + h * kWave;
-        if (c < nch) ok = ok && tk_take_key(part + 2 * c * kMaxTopK, a.tag, t0, mk[h]);
+    {
+        const uint64_t *p[2] = {part + 2 * lane * kMaxTopK, part + 2 * (lane + kWave) * kMaxTopK};
+        const bool in[2] = {lane < nch, lane + kWave < nch};
+        ok = tk_take_keys<2>(p, in, a.tag, t0, mk);
     }
     // Rank of each maximum among the maxima.
     int rk[2] = {0, 0};
@@ -218,12 +212,13 @@ __device__ void topk_merge(const TopkArgs &a, int64_t row) {
         if (lane / k == r) mych = b0 ? src : src + kWave;
         if (r == kt - 1) M = tk_readlane(b0 ? mk[0] : mk[1], src);
     }
-    uint64_t key = 0;
-    bool keep = false;
-    if (lane < m) {
-        ok = ok && tk_take_key(part + 2 * (mych * kMaxTopK + lane % k), a.tag, t0, key);
-        keep = ok && (nch < k || key >= M);
+    uint64_t key[1] = {0};
+    {
+        const uint64_t *p[1] = {part + 2 * (mych * kMaxTopK + lane % k)};
+        const bool in[1] = {lane < m};
+        ok = ok && tk_take_keys<1>(p, in, a.tag, t0, key);
     }
+    const bool keep = ok && lane < m && (nch < k || key[0] >= M);
     if (__ballot(!ok)) {
         if (lane < k) {
             a.out_idx[row * k + lane] = -1;
@@ -233,10 +228,10 @@ __device__ void topk_merge(const TopkArgs &a, int64_t row) {
     }
     int r = 0;
     for (uint64_t b = __ballot(keep); b; b &= b - 1)
-        r += tk_readlane(key, __ffsll(static_cast<unsigned long long>(b)) - 1) > key;
+        r += tk_readlane(key[0], __ffsll(static_cast<unsigned long long>(b)) - 1) > key[0];
     if (keep && r < k) {
-        a.out_idx[row * k + r] = tk_key_index(key);
-        if (a.out_val) a.out_val[row * k + r] = tk_key_value(key);
+        a.out_idx[row * k + r] = tk_key_index(key[0]);
+        if (a.out_val) a.out_val[row * k + r] = tk_key_value(key[0]);
     }
 }
 
@@ -267,6 +262,8 @@ __device__ __forceinline__ void topk_chunk(const TopkArgs &a, int64_t row, int c
         const int last = n / VEC - 1;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) raw[q] = vp[min(tid + q * kWG, last)];
+        // Every load in flight before the first wait: one memory round trip.
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) unpack<DT>(raw[q], x + q * VEC);
     } else {
@@ -320,42 +317,45 @@ __device__ __forceinline__ void topk_chunk(const TopkArgs &a, int64_t row, int c
     }
     if (lane == 0) s_count[w] = cnt;
     __syncthreads();
-    bool fits = theta > -INFINITY;
+    int C = 0;
 #pragma unroll
-    for (int q = 0; q < kWaves; ++q) fits = fits && s_count[q] <= kCandPerWave;
-    if (fits) {
-        // Candidate (w, lane)'s rank is the number of candidates ahead of it;
-        // ranks below k are the chunk's list.  (There are at least k: the k
+    for (int q = 0; q < kWaves; ++q) C += s_count[q];
+    if (theta > -INFINITY && C <= kWave) {
+        // Wavefront 0 takes candidate `lane` (segments in wave order) and
+        // ranks it by the number of candidates ahead of it; ranks below k
+        // are the chunk's list.  (There are at least k candidates: the k
         // groups whose maxima are >= theta each hold one.)
-        if (lane < cnt) {
-            const uint64_t key = s_c[w][lane];
-            int r = 0;
-            for (int q = 0; q < kWaves; ++q) {
-                const int nq = s_count[q];
-#pragma unroll 8
-                for (int j = 0; j < nq; ++j) r += s_c[q][j] > key;
-            }
-            if (r < k) tk_put(out, a.tag, r, tk_key_value(key), tk_key_index(key));
-        }
-    } else {
-        // Ties beyond LDS, or fewer than k entries above -inf: k exact rounds.
-        float lv = INFINITY;
-        int32_t li = -1;
-        for (int q = 0; q < k; ++q) {
-            float bv = -INFINITY;
-            int32_t bi = INT32_MAX;
+        if (w != 0) return;
+        uint64_t key = 0;
+        int base = 0;
 #pragma unroll
+        for (int q = 0; q < kWaves; ++q) {
+            const int nq = s_count[q];
+            if (lane >= base && lane < base + nq) key = s_c[q][lane - base];
+            base += nq;
+        }
+        int r = 0;
+        for (int j = 0; j < C; ++j) r += tk_readlane(key, j) > key;
+        if (lane < C && r < k) tk_put(out, a.tag, r, tk_key_value(key), tk_key_index(key));
+    } else {
+        // Ties beyond 64 candidates, or fewer than k entries above -inf: k
+        // exact rounds, each taking the best key below the last one taken.
+        // They re-read the chunk (a rare path, so the registers holding it
+        // are not kept alive for it).
+        uint64_t last = ~0ull;
+        for (int q = 0; q < k; ++q) {
+            uint64_t best = kFillKey;
             for (int e = 0; e < E; ++e) {
-                const int32_t i = static_cast<int32_t>(e0 + pos(e));
-                if (pos(e) < n && tk_after(x[e], i, lv, li) && tk_better(x[e], i, bv, bi)) {
-                    bv = x[e];
-                    bi = i;
+                const int at = pos(e);
+                if (at < n) {
+                    const uint64_t key = tk_key(load_one<DT>(a.logits, row * a.V + e0 + at),
+                                                static_cast<int32_t>(e0 + at));
+                    if (key < last && key > best) best = key;
                 }
             }
-            tk_wg_best(bv, bi);
-            if (tid == 0) tk_put(out, a.tag, q, bv, bi);
-            lv = bv;
-            li = bi;
+            best = tk_wg_max_key(best);
+            if (tid == 0) tk_put(out, a.tag, q, tk_key_value(best), tk_key_index(best));
+            last = best;
         }
     }
 }
