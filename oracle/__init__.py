@@ -67,6 +67,8 @@ def _bind(lib):
     lib.oracle_verify_tree_greedy_dyn.restype = i
     lib.oracle_topk.argtypes = [vp, i, i, i, i, vp, vp]
     lib.oracle_topk.restype = i
+    lib.oracle_kv_commit.argtypes = [vp, vp, i, i, i, i, ctypes.c_int64, vp, i, vp, vp, vp]
+    lib.oracle_kv_commit.restype = i
     return lib
 
 
@@ -258,3 +260,31 @@ def topk(logits, k, *, lib=None):
     if rc != 0:
         raise ValueError(f"oracle_topk rejected its arguments (code {rc})")
     return out_i.reshape(t.shape[:-1] + (k,)), out_v.reshape(t.shape[:-1] + (k,))
+
+
+def kv_commit(scratch, cache, path, count, length, *, lib=None):
+    """KV commit: a copy of `cache` [planes][B][S][row] (uint8) with each
+    sequence's accepted scratch rows (`scratch` [planes][B][N][row]) written at
+    its slots length[b] .. length[b] + count[b] - 1, and the new lengths.
+    `path` [B][P] int32 or None (row i).  Sequences whose arguments are out of
+    range are left as they were."""
+    lib = lib or load()
+    scratch = np.ascontiguousarray(scratch, dtype=np.uint8)
+    out = np.array(cache, dtype=np.uint8, copy=True, order="C")
+    planes, B, N, row = scratch.shape
+    assert out.shape[:2] == (planes, B) and out.shape[3] == row, "scratch and cache disagree"
+    S = out.shape[2]
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    length = np.ascontiguousarray(length, dtype=np.int32)
+    new_len = np.empty(B, np.int32)
+    if path is not None:
+        path = np.ascontiguousarray(path, dtype=np.int32)
+        P = path.shape[1]
+    else:
+        P = 0
+    rc = lib.oracle_kv_commit(_ptr(scratch), _ptr(out), planes, B, N, S, row,
+                              None if path is None else _ptr(path), P, _ptr(count), _ptr(length),
+                              _ptr(new_len))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_commit rejected its arguments (code {rc})")
+    return out, new_len

@@ -621,3 +621,62 @@ int oracle_topk(const void *logits, int dtype, int rows, int V, int k, int32_t *
     }
     return OR_OK;
 }
+
+/*
+ * KV commit after verify (the Arabic lesson, section on rolling the KV cache
+ * back, and its key-terms entry "KV rollback": the verifier's forward writes
+ * the drafted positions' keys and values to a scratch buffer first; the ones
+ * the verify accepts are committed to the cache and the rest discarded; its
+ * exercises check that after a rejection the cache reads the prefix followed
+ * by the accepted drafts).  Byte copies only, no arithmetic.
+ *
+ *   scratch [planes][B][N][row_bytes]  keys / values the forward wrote, one row
+ *                                      per scratch position (a chain's drafts, or
+ *                                      a tree's nodes);
+ *   cache   [planes][B][S][row_bytes]  the per-sequence cache, slots 0..len-1 in use;
+ *   path    [B][P] or NULL             scratch row of the i-th committed entry
+ *                                      (NULL: row i);
+ *   count   [B]                        entries to commit;
+ *   len     [B]                        slots in use before the commit;
+ *   new_len [B]                        slots in use after it.
+ * Sequence b is committed iff 0 <= count[b] <= P (P = N when path is NULL),
+ * 0 <= len[b], len[b] + count[b] <= S and every path[b][i], i < count[b], lies
+ * in [0, N).  Then for every plane, cache slot len[b] + i receives scratch row
+ * path[b][i] for i < count[b], and new_len[b] = len[b] + count[b].  Otherwise
+ * nothing of b is written and new_len[b] = len[b].
+ */
+int oracle_kv_commit(const void *scratch, void *cache, int planes, int B, int N, int S,
+                     int64_t row_bytes, const int32_t *path, int P, const int32_t *count,
+                     const int32_t *len, int32_t *new_len)
+{
+    if (planes < 0 || B < 0 || N < 0 || S < 0 || row_bytes < 0 || (path && P < 0))
+        return OR_BAD_ARG;
+    if (B > 0 && (!count || !len || !new_len))
+        return OR_BAD_ARG;
+    if (!path)
+        P = N;
+    const unsigned char *src = (const unsigned char *)scratch;
+    unsigned char *dst = (unsigned char *)cache;
+    for (int b = 0; b < B; ++b) {
+        int c = count[b], L = len[b];
+        int ok = c >= 0 && c <= P && L >= 0 && (int64_t)L + c <= S;
+        for (int i = 0; ok && i < c; ++i) {
+            int r = path ? path[(size_t)b * P + i] : i;
+            if (r < 0 || r >= N)
+                ok = 0;
+        }
+        if (!ok) {
+            new_len[b] = L;
+            continue;
+        }
+        for (int l = 0; l < planes; ++l)
+            for (int i = 0; i < c; ++i) {
+                int r = path ? path[(size_t)b * P + i] : i;
+                size_t from = (((size_t)l * B + b) * N + r) * (size_t)row_bytes;
+                size_t to = (((size_t)l * B + b) * S + L + i) * (size_t)row_bytes;
+                memcpy(dst + to, src + from, (size_t)row_bytes);
+            }
+        new_len[b] = L + c;
+    }
+    return OR_OK;
+}

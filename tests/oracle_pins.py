@@ -532,6 +532,131 @@ def pin_topk_argmax(lib, seed=43):
     assert np.all(np.diff(val8, axis=1) <= 0) and np.array_equal(idx8[:, 0], idx[:, 0])
 
 
+# ------------------------------------------------------------- KV commit
+
+def _kv_of(tokens, planes, row, salt=0):
+    """Synthetic key/value rows: a fixed byte pattern per (plane, token), so a
+    cache's contents can be predicted from the token sequence alone."""
+    t = np.asarray(tokens, np.int64)
+    out = np.empty((planes, len(t), row), np.uint8)
+    for l in range(planes):
+        for j, tok in enumerate(t):
+            out[l, j] = ((tok * 131 + l * 17 + salt + np.arange(row) * 7) % 251).astype(np.uint8)
+    return out
+
+
+def pin_kv_rollback_exercise(lib):
+    """The Arabic lesson's rollback exercise (tests/golden/kv_rollback_exercise.json):
+    10 cached tokens, 5 drafts pushed to the scratch buffer, a rejection at the
+    third; the cache must read the prefix and then the first two drafts, with
+    length 12 and nothing past it written."""
+    g = json.load(open(os.path.join(GOLDEN, "kv_rollback_exercise.json")))
+    planes, row, S = 4, 24, 16
+    prefix = np.arange(100, 100 + g["prefix_tokens"])
+    drafts = np.arange(500, 500 + g["drafts_pushed"])
+    cache = np.full((planes, 1, S, row), 0xEE, np.uint8)
+    cache[:, 0, :len(prefix)] = _kv_of(prefix, planes, row)
+    scratch = _kv_of(drafts, planes, row)[:, None]
+    accepted = g["rejected_draft"] - 1
+    assert accepted == g["accepted_drafts"]
+    out, new_len = oracle.kv_commit(scratch, cache, None, [accepted], [len(prefix)], lib=lib)
+    assert new_len[0] == g["cache_length_after"]
+    want = _kv_of(np.concatenate([prefix, drafts[:accepted]]), planes, row)
+    assert np.array_equal(out[:, 0, :new_len[0]], want)
+    assert np.all(out[:, 0, new_len[0]:] == 0xEE)
+
+
+def pin_kv_commit_tree_path(lib, seed=53):
+    """After a greedy tree verify, committing the accepted path (root included)
+    leaves the cache reading the prefix, the root token and the accepted
+    tokens, in order; predicted from the token sequence alone."""
+    rng = np.random.default_rng(seed)
+    planes, row = 3, 16
+    for trial in range(40):
+        N, V, B = int(rng.integers(1, 16)), 6, 3
+        parents = [-1] + [int(rng.integers(0, v)) for v in range(1, N)]
+        logits = (rng.integers(-3, 4, size=(B, N, V)) * 0.5).astype(np.float32)
+        tokens = rng.integers(0, V, size=(B, N)).astype(np.int32)
+        amax = np.argmax(logits, axis=-1)
+        for b in range(B):   # make acceptance likely: a child often carries its parent's argmax
+            for v in range(1, N):
+                if rng.random() < 0.7:
+                    tokens[b, v] = amax[b, parents[v]]
+        root_tok = rng.integers(0, V, size=B)
+        tokens[:, 0] = root_tok
+        out_t, out_p, out_d = oracle.verify_tree_greedy(logits, tokens, parents, lib=lib)
+        S = 12 + N
+        lens = rng.integers(0, 12, size=B).astype(np.int32)
+        prefixes = [rng.integers(0, V, size=int(lens[b])) for b in range(B)]
+        cache = np.zeros((planes, B, S, row), np.uint8)
+        scratch = np.zeros((planes, B, N, row), np.uint8)
+        for b in range(B):
+            cache[:, b, :lens[b]] = _kv_of(prefixes[b], planes, row)
+            scratch[:, b] = _kv_of(tokens[b], planes, row)
+        count = (out_d + 1).astype(np.int32)
+        out, new_len = oracle.kv_commit(scratch, cache, out_p, count, lens, lib=lib)
+        for b in range(B):
+            d = int(out_d[b])
+            seq = np.concatenate([prefixes[b], [root_tok[b]], out_t[b, :d]])
+            assert new_len[b] == lens[b] + d + 1
+            assert np.array_equal(out[:, b, :new_len[b]], _kv_of(seq, planes, row)), (trial, b)
+            assert not out[:, b, new_len[b]:].any()
+
+
+def pin_kv_commit_invariants(lib, seed=59):
+    """Random commits: slots outside [len, len + count) never change; a
+    sequence whose count, length or path is out of range is left whole and
+    keeps its length; two commits in a row equal one commit of both parts."""
+    rng = np.random.default_rng(seed)
+    for trial in range(60):
+        planes, B, N, S, row = int(rng.integers(1, 4)), 5, int(rng.integers(1, 9)), 14, 8
+        scratch = rng.integers(0, 256, size=(planes, B, N, row)).astype(np.uint8)
+        cache = rng.integers(0, 256, size=(planes, B, S, row)).astype(np.uint8)
+        P = N + 1
+        path = rng.integers(0, N, size=(B, P)).astype(np.int32)
+        count = rng.integers(0, N + 1, size=B).astype(np.int32)
+        lens = rng.integers(0, S + 1, size=B).astype(np.int32)
+        bad = rng.random(B) < 0.4
+        for b in np.nonzero(bad)[0]:
+            kind = int(rng.integers(0, 4))
+            if kind == 0:
+                count[b] = P + 1
+            elif kind == 1:
+                count[b] = max(count[b], 1)
+                path[b, int(rng.integers(0, count[b]))] = int(rng.choice([-1, N]))
+            elif kind == 2:
+                lens[b] = S - count[b] + 1
+            else:
+                count[b] = -1
+        out, new_len = oracle.kv_commit(scratch, cache, path, count, lens, lib=lib)
+        for b in range(B):
+            valid = (0 <= count[b] <= P and lens[b] >= 0 and lens[b] + count[b] <= S
+                     and np.all((path[b, :max(count[b], 0)] >= 0) & (path[b, :max(count[b], 0)] < N)))
+            if not valid:
+                assert new_len[b] == lens[b] and np.array_equal(out[:, b], cache[:, b]), (trial, b)
+                continue
+            c, L = int(count[b]), int(lens[b])
+            assert new_len[b] == L + c
+            assert np.array_equal(out[:, b, :L], cache[:, b, :L])
+            assert np.array_equal(out[:, b, L + c:], cache[:, b, L + c:])
+            for i in range(c):
+                assert np.array_equal(out[:, b, L + i], scratch[:, b, path[b, i]]), (trial, b, i)
+        # two commits equal one: split each valid sequence's count in two
+        ok = np.array([0 <= count[b] <= P and 0 <= lens[b] and lens[b] + count[b] <= S
+                       and np.all((path[b, :max(count[b], 0)] >= 0) & (path[b, :max(count[b], 0)] < N))
+                       for b in range(B)])
+        c1 = np.where(ok, count // 2, 0).astype(np.int32)
+        c2 = np.where(ok, count - c1, 0).astype(np.int32)
+        mid, l1 = oracle.kv_commit(scratch, cache, path, c1, lens, lib=lib)
+        path2 = np.zeros_like(path)
+        for b in range(B):
+            path2[b, :P - c1[b]] = path[b, c1[b]:]
+        two, l2 = oracle.kv_commit(scratch, mid, path2, c2, l1, lib=lib)
+        one, l12 = oracle.kv_commit(scratch, cache, path, np.where(ok, count, 0).astype(np.int32),
+                                    lens, lib=lib)
+        assert np.array_equal(two, one) and np.array_equal(l2, l12), trial
+
+
 # ------------------------------------------------------------- chi-square
 
 def pin_chi_square(lib, n=50_000, seed=19):
@@ -562,4 +687,5 @@ ALL_PINS = [pin_exact_law, pin_expected_tokens, pin_page_counts, pin_strict_acce
             pin_softmax_values, pin_helper_closed_forms,
             pin_inverse_cdf, pin_greedy, pin_tree_bruteforce, pin_tree_chain,
             pin_tree_figure, pin_tree_dyn_bruteforce, pin_tree_dyn_padding, pin_tree_dyn_chain,
-            pin_topk_sort, pin_topk_argmax, pin_chi_square]
+            pin_topk_sort, pin_topk_argmax, pin_kv_rollback_exercise, pin_kv_commit_tree_path,
+            pin_kv_commit_invariants, pin_chi_square]

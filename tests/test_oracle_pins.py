@@ -97,12 +97,21 @@ MUTANTS = [
      "a += p[i] < q[i] ? q[i] : p[i];", 0),
     ("draw weights keep the negative part", "            out_w[i] = d > 0.0 ? d : 0.0;",
      "            out_w[i] = d;", 0),
+    ("KV commit writes from slot 0, ignoring the length", "* S + L + i) * (size_t)row_bytes;",
+     "* S + i) * (size_t)row_bytes;", 0),
+    ("KV commit ignores the path", "                int r = path ? path[(size_t)b * P + i] : i;",
+     "                int r = i;", 0),
+    ("KV commit keeps the old length", "        new_len[b] = L + c;", "        new_len[b] = L;", 0),
+    ("KV commit swaps plane and sequence strides", "size_t from = (((size_t)l * B + b) * N + r)",
+     "size_t from = (((size_t)b * planes + l) * N + r)", 0),
 ]
 
 QUICK_PINS = [P.pin_exact_law, P.pin_expected_tokens, P.pin_page_counts, P.pin_strict_acceptance,
               P.pin_softmax_values, P.pin_helper_closed_forms,
               P.pin_inverse_cdf, P.pin_greedy, P.pin_tree_bruteforce, P.pin_tree_figure,
-              P.pin_tree_dyn_bruteforce, P.pin_tree_dyn_padding, P.pin_topk_sort, P.pin_chi_square]
+              P.pin_tree_dyn_bruteforce, P.pin_tree_dyn_padding, P.pin_topk_sort,
+              P.pin_kv_rollback_exercise, P.pin_kv_commit_tree_path, P.pin_kv_commit_invariants,
+              P.pin_chi_square]
 
 
 def _mutant_lib(tmpdir, pattern, repl, which):
