@@ -277,6 +277,44 @@ spec_status spec_draft_topk(const void *logits, spec_dtype dtype, int32_t rows, 
                             int32_t k, int32_t *out_idx, float *out_val, void *workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * KV commit after verify (Arabic lesson, section on rolling the KV cache back,
+ * its key-terms entry "KV rollback", and its rollback exercise; forum post
+ * §10 on the cost of rolling the target's cache back).  The verifier's
+ * forward writes every drafted position's keys and values to a scratch
+ * buffer; this call copies the accepted ones, in order, to the end of each
+ * sequence's cache and reports the new lengths.  Rejected entries are simply
+ * not copied.
+ *
+ *   scratch  [planes][B][N][row_bytes]  DEVICE, 16-byte aligned: one row per
+ *                                       scratch position (a chain's drafts, or a
+ *                                       tree's nodes in the order the verify
+ *                                       numbers them).
+ *   cache    [planes][B][S][row_bytes]  DEVICE, 16-byte aligned; must not overlap
+ *                                       scratch.
+ *   planes   >= 1: e.g. 2 x layers (keys and values of each layer).
+ *   row_bytes  a positive multiple of 16 (heads x head_dim x element size).
+ *   path     nullable DEVICE [B][P] int32: scratch row of the i-th committed
+ *            entry, e.g. out_path of spec_verify_tree_greedy(_dyn) (root
+ *            included).  NULL means row i (a chain), and then P = N.
+ *   count    DEVICE [B] int32: entries to commit, e.g. out_depth + 1 for a
+ *            tree, or the accepted count (plus one if scratch row 0 holds the
+ *            step's first input) for a chain.
+ *   cache_len DEVICE [B] int32: slots in use before the commit.
+ *   new_len  DEVICE [B] int32: slots in use after it; must not alias cache_len.
+ *
+ * Sequence b is committed iff 0 <= count[b] <= P, 0 <= cache_len[b],
+ * cache_len[b] + count[b] <= S and every path[b][i], i < count[b], lies in
+ * [0, N): then for every plane, slot cache_len[b] + i receives scratch row
+ * path[b][i], and new_len[b] = cache_len[b] + count[b].  Otherwise nothing of
+ * b is written and new_len[b] = cache_len[b] (the device arrays cannot be
+ * checked on the host).  One kernel launch; no workspace.
+ */
+spec_status spec_kv_commit(const void *scratch, void *cache, int32_t planes, int32_t B, int32_t N,
+                           int32_t S, int64_t row_bytes, const int32_t *path, int32_t P,
+                           const int32_t *count, const int32_t *cache_len, int32_t *new_len,
+                           hipStream_t stream);
+
 /* Static text for a status code. */
 const char *spec_verify_status_string(spec_status status);
 

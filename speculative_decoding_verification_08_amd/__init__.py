@@ -56,9 +56,11 @@ def _load(path: str = LIB_PATH):
     lib.spec_verify_tree_greedy_dyn.argtypes = [vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, vp, vp,
                                                 vp, vp, sz, vp]
     lib.spec_draft_topk.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.spec_kv_commit.argtypes = [vp, vp, i32, i32, i32, i32, ctypes.c_int64, vp, i32, vp, vp, vp,
+                                   vp]
     for fn in ("spec_verify_workspace_bytes", "spec_verify_chain", "spec_verify_chain_stats",
                "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy",
-               "spec_verify_tree_greedy_dyn", "spec_draft_topk"):
+               "spec_verify_tree_greedy_dyn", "spec_draft_topk", "spec_kv_commit"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -69,7 +71,7 @@ _lib = _load()
 def header_symbols(path: str = HEADER_PATH) -> list[str]:
     """Entry points declared in the public header."""
     text = open(path).read()
-    return sorted(set(re.findall(r"^\S.*?\b(spec_(?:verify|draft)_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\S.*?\b(spec_(?:verify|draft|kv)_\w+)\s*\(", text, flags=re.M)))
 
 
 def library():
@@ -362,3 +364,42 @@ def spec_draft_topk(logits, k, *, with_values=True, out_idx=None, out_val=None, 
                       dt, rows, V, k, _ptr(out_idx), _ptr(out_val), _ptr(workspace_buf),
                       workspace_buf.numel(), _stream(dev, stream))
     return (launch, (out_idx, out_val)) if prepare else (out_idx, out_val)
+
+
+def spec_kv_commit(scratch, cache, count, cache_len, *, path=None, new_len=None, stream=None,
+                   prepare=False):
+    """KV commit after verify: for each sequence b, scratch rows path[b][i]
+    (row i when `path` is None), i < count[b], are copied to cache slots
+    cache_len[b] + i of every plane.  `scratch` is [planes][B][N][...] and
+    `cache` [planes][B][S][...], same dtype and row shape, contiguous device
+    tensors; `path` int32 [B][P] or None; `count` and `cache_len` int32 [B].
+    Returns new_len (int32 [B]); with `prepare`, (launch, new_len) and nothing
+    is enqueued."""
+    _check_dev("scratch", scratch)
+    _check_dev("cache", cache, scratch.dtype)
+    if scratch.dim() < 4 or cache.dim() != scratch.dim():
+        raise ValueError("scratch and cache must be [planes][B][rows][...] with the same row shape")
+    planes, B, N = scratch.shape[:3]
+    S = cache.shape[2]
+    if tuple(cache.shape[:2]) != (planes, B) or tuple(cache.shape[3:]) != tuple(scratch.shape[3:]):
+        raise ValueError(f"cache {tuple(cache.shape)} does not match scratch {tuple(scratch.shape)}")
+    row_bytes = scratch.element_size()
+    for d in scratch.shape[3:]:
+        row_bytes *= d
+    _check_dev("count", count, torch.int32, (B,))
+    _check_dev("cache_len", cache_len, torch.int32, (B,))
+    P = N
+    if path is not None:
+        _check_dev("path", path, torch.int32)
+        if path.dim() != 2 or path.shape[0] != B:
+            raise ValueError("path must be [B][P]")
+        P = path.shape[1]
+    dev = scratch.device
+    if new_len is None:
+        new_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    else:
+        _check_dev("new_len", new_len, torch.int32, (B,))
+    launch = _enqueue(prepare, (scratch, cache, path, count, cache_len, new_len), "spec_kv_commit",
+                      _ptr(scratch), _ptr(cache), planes, B, N, S, row_bytes, _ptr(path), P,
+                      _ptr(count), _ptr(cache_len), _ptr(new_len), _stream(dev, stream))
+    return (launch, new_len) if prepare else new_len

@@ -1,6 +1,6 @@
 // C ABI of the verify library: argument validation, launch planning and the
 // workspace layout.  Everything here is host code; the kernels live in
-// chain.hip, greedy_tree.hip and topk.hip.
+// chain.hip, greedy_tree.hip, topk.hip and kv.hip.
 #include <math.h>
 #include <string.h>
 
@@ -8,6 +8,7 @@
 #include <atomic>
 
 #include "plan.hpp"
+#include "kv.hpp"
 #include "topk.hpp"
 #include "spec_verify.h"
 
@@ -378,6 +379,46 @@ spec_status spec_draft_topk(const void *logits, spec_dtype dtype, int32_t rows, 
     a.out_idx = out_idx;
     a.out_val = out_val;
     return launch_status(launch_topk(a, dtype, stream));
+}
+
+spec_status spec_kv_commit(const void *scratch, void *cache, int32_t planes, int32_t B, int32_t N,
+                           int32_t S, int64_t row_bytes, const int32_t *path, int32_t P,
+                           const int32_t *count, const int32_t *cache_len, int32_t *new_len,
+                           hipStream_t stream) {
+    if (planes < 1 || B < 0 || N < 0 || S < 0 || row_bytes < 16 || row_bytes % 16 != 0)
+        return SPEC_ERR_INVALID_ARG;
+    if (!path) P = N;
+    if (P < 0) return SPEC_ERR_INVALID_ARG;
+    const int64_t vpr = row_bytes / 16;
+    // 32-bit vector indices inside a sequence's window, and a one-dimensional grid.
+    if (vpr > 0x7fffffffLL || static_cast<int64_t>(P) * vpr > 0x7fffffffLL ||
+        static_cast<int64_t>(planes) * B > 0x7fffffffLL)
+        return SPEC_ERR_INVALID_ARG;
+    if (B == 0) return SPEC_OK;
+    if (!scratch || !cache || !aligned(scratch, 16) || !aligned(cache, 16) || !count ||
+        !cache_len || !new_len || !aligned(count, 4) || !aligned(cache_len, 4) ||
+        !aligned(new_len, 4) || (path && !aligned(path, 4)) || new_len == cache_len)
+        return SPEC_ERR_INVALID_ARG;
+    // The two buffers must not overlap (a copy between overlapping rows could
+    // read a row it has already overwritten).
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(scratch), c0 = reinterpret_cast<uintptr_t>(cache);
+    const uint64_t sbytes = static_cast<uint64_t>(planes) * B * N * row_bytes;
+    const uint64_t cbytes = static_cast<uint64_t>(planes) * B * S * row_bytes;
+    if (sbytes > 0 && cbytes > 0 && s0 < c0 + cbytes && c0 < s0 + sbytes) return SPEC_ERR_INVALID_ARG;
+    KvArgs a;
+    a.scratch = static_cast<const uint4 *>(scratch);
+    a.cache = static_cast<uint4 *>(cache);
+    a.planes = planes;
+    a.B = B;
+    a.N = N;
+    a.S = S;
+    a.P = P;
+    a.vpr = static_cast<int32_t>(vpr);
+    a.path = path;
+    a.count = count;
+    a.len = cache_len;
+    a.new_len = new_len;
+    return launch_status(launch_kv_commit(a, stream));
 }
 
 }  // extern "C"

@@ -14,7 +14,7 @@ def test_every_declared_symbol_is_exported():
     syms = sv.header_symbols()
     assert {"spec_verify_chain", "spec_verify_greedy", "spec_verify_tree_greedy",
             "spec_verify_tree_greedy_dyn", "spec_verify_workspace_bytes",
-            "spec_draft_topk"} <= set(syms)
+            "spec_draft_topk", "spec_kv_commit"} <= set(syms)
     lib = sv.library()
     for s in syms:
         assert hasattr(lib, s), s
@@ -129,6 +129,31 @@ def test_topk_argument_errors():
     assert t(FAKE, 5, 2, 100, 4, FAKE, None, FAKE, big, None) == E
     assert t(FAKE, BF, 2, 100, 4, FAKE, None, None, big, None) == sv.SPEC_ERR_WORKSPACE
     assert t(FAKE, BF, 2, 100, 4, FAKE, None, FAKE, 16, None) == sv.SPEC_ERR_WORKSPACE
+
+
+def test_kv_commit_argument_errors():
+    lib = sv.library()
+    E = sv.SPEC_ERR_INVALID_ARG
+    k = lib.spec_kv_commit
+    big = 1 << 32
+    A, C = FAKE, FAKE + big      # scratch and cache far apart (never dereferenced)
+    # B = 0 returns before anything is touched
+    assert k(A, C, 2, 0, 8, 16, 64, None, 0, FAKE, FAKE, FAKE + 64, None) == sv.SPEC_OK
+    base = dict(s=A, c=C, planes=2, B=3, N=8, S=16, row=64, path=None, P=0, cnt=FAKE,
+                ln=FAKE + 64, nl=FAKE + 128)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return k(a["s"], a["c"], a["planes"], a["B"], a["N"], a["S"], a["row"], a["path"], a["P"],
+                 a["cnt"], a["ln"], a["nl"], None)
+    assert call(planes=0) == E
+    assert call(row=8) == E and call(row=72) == E and call(row=0) == E
+    assert call(s=None) == E and call(c=FAKE_MIS) == E
+    assert call(cnt=None) == E and call(ln=FAKE + 2) == E
+    assert call(nl=FAKE + 64) == E                     # new_len aliases cache_len
+    assert call(c=A + 64) == E                         # cache overlaps scratch
+    assert call(path=FAKE, P=-1) == E
+    assert call(N=-1) == E and call(S=-1) == E
 
 
 def test_status_strings():

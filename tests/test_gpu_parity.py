@@ -574,3 +574,121 @@ def test_workspace_shared_by_every_entry_point(sv):
         idx, val = sv.spec_draft_topk(dev(x), 8, workspace_buf=ws)
         torch.cuda.synchronize()
         parity.check_topk({"logits": x}, idx.cpu().numpy(), val.cpu().numpy())
+
+
+# ------------------------------------------------------------------ KV commit
+
+def run_kv(sv, scratch, cache, path, count, length):
+    s_d, c_d = dev(scratch), dev(cache)
+    p_d = None if path is None else dev(np.ascontiguousarray(path, np.int32))
+    nl = sv.spec_kv_commit(s_d, c_d, dev(np.asarray(count, np.int32)),
+                           dev(np.asarray(length, np.int32)), path=p_d)
+    torch.cuda.synchronize()
+    return c_d.cpu().numpy(), nl.cpu().numpy()
+
+
+def kv_case(rng, planes, B, N, S, row, with_path=True, bad_frac=0.3):
+    scratch = rng.integers(0, 256, size=(planes, B, N, row), dtype=np.uint8)
+    cache = rng.integers(0, 256, size=(planes, B, S, row), dtype=np.uint8)
+    P = N + 2 if with_path else N
+    path = rng.integers(0, max(N, 1), size=(B, P)).astype(np.int32) if with_path else None
+    count = rng.integers(0, min(N, S) + 1, size=B).astype(np.int32)
+    length = np.array([rng.integers(0, S - c + 1) for c in count], np.int32)
+    for b in np.nonzero(rng.random(B) < bad_frac)[0]:
+        kind = int(rng.integers(0, 4))
+        if kind == 0:
+            count[b] = P + 1
+        elif kind == 1 and with_path and count[b] > 0:
+            path[b, int(rng.integers(0, count[b]))] = int(rng.choice([-1, N]))
+        elif kind == 2:
+            length[b] = S - count[b] + 1
+        else:
+            count[b] = -1
+    return scratch, cache, path, count, length
+
+
+@pytest.mark.parametrize("planes,B,N,S,row", [(1, 1, 1, 1, 16), (3, 5, 9, 20, 48), (2, 17, 64, 80, 2048),
+                                              (4, 3, 130, 300, 4112), (1, 40, 5, 7, 32)])
+def test_kv_commit_random_shapes(sv, planes, B, N, S, row):
+    rng = np.random.default_rng(planes * 1000 + B * 10 + N)
+    for with_path in (True, False):
+        case(f"KV commit planes={planes} B={B} N={N} S={S} row={row} path={with_path}")
+        scratch, cache, path, count, length = kv_case(rng, planes, B, N, S, row, with_path)
+        want_c, want_l = oracle.kv_commit(scratch, cache, path, count, length)
+        got_c, got_l = run_kv(sv, scratch, cache, path, count, length)
+        assert np.array_equal(got_l, want_l)
+        assert np.array_equal(got_c, want_c)
+
+
+def test_kv_commit_rollback_exercise(sv):
+    """The Arabic lesson's exercise: 10 cached tokens, 5 drafts, rejection at the third."""
+    case("KV rollback exercise")
+    planes, row, S = 4, 64, 16
+    rng = np.random.default_rng(3)
+    cache = rng.integers(0, 256, size=(planes, 1, S, row), dtype=np.uint8)
+    scratch = rng.integers(0, 256, size=(planes, 1, 5, row), dtype=np.uint8)
+    got_c, got_l = run_kv(sv, scratch, cache, None, [2], [10])
+    assert got_l[0] == 12
+    assert np.array_equal(got_c[:, 0, :10], cache[:, 0, :10])
+    assert np.array_equal(got_c[:, 0, 10:12], scratch[:, 0, :2])
+    assert np.array_equal(got_c[:, 0, 12:], cache[:, 0, 12:])
+
+
+def test_kv_commit_after_tree_verify(sv):
+    """A per-sequence tree verify on the GPU, then its accepted paths (root
+    included) committed on the GPU, equals the oracle's verify and commit."""
+    w = W.WORKLOADS["tree_dyn_128k"].with_sizes(B=9, K=24, V=3000)
+    d = W.tree_dyn_inputs(w, 4, p_match=0.85, nmin=4)
+    case("KV commit after per-sequence tree verify")
+    tok, path, depth = sv.spec_verify_tree_greedy_dyn(dev(d["node_logits"]), dev(d["node_tokens"]),
+                                                      dev(d["parents"]), dev(d["node_count"]))
+    _, o_path, o_depth = oracle.verify_tree_greedy_dyn(d["node_logits"], d["node_tokens"],
+                                                       d["parents"], d["node_count"])
+    planes, row, S = 6, 256, 40
+    rng = np.random.default_rng(8)
+    scratch = rng.integers(0, 256, size=(planes, 9, 24, row), dtype=np.uint8)
+    cache = rng.integers(0, 256, size=(planes, 9, S, row), dtype=np.uint8)
+    length = rng.integers(0, S - 24, size=9).astype(np.int32)
+    s_d, c_d = dev(scratch), dev(cache)
+    count = (depth + 1).to(torch.int32)
+    nl = sv.spec_kv_commit(s_d, c_d, count, dev(length), path=path)
+    torch.cuda.synchronize()
+    want_c, want_l = oracle.kv_commit(scratch, cache, o_path, (o_depth + 1).astype(np.int32), length)
+    assert np.array_equal(nl.cpu().numpy(), want_l)
+    assert np.array_equal(c_d.cpu().numpy(), want_c)
+
+
+def kv_cache_pattern(shape):
+    """Deterministic initial cache for the full-size case: byte j of the flat
+    array is (j * 7 + 3) mod 251."""
+    out = torch.empty(shape, dtype=torch.uint8, device=DEV)
+    per = int(np.prod(shape[1:]))
+    for l in range(shape[0]):   # a plane at a time keeps the int64 temporary small
+        j = torch.arange(l * per, (l + 1) * per, dtype=torch.int64, device=DEV)
+        out[l] = ((j * 7 + 3) % 251).to(torch.uint8).view(shape[1:])
+    return out
+
+
+def test_kv_commit_full_size(sv):
+    """kv_commit_b64 in the benchmark's configuration; every new length
+    checked, and 48 (plane, sequence) windows compared in full."""
+    w = W.WORKLOADS["kv_commit_b64"]
+    case("kv_commit_b64 full size")
+    scratch = W.kv_scratch(w, 0)
+    p = W.kv_paths(w, 0)
+    shape = (w.planes, w.B, w.slots, w.row_bytes)
+    c_d = kv_cache_pattern(shape)
+    s_d = dev(scratch)
+    nl = sv.spec_kv_commit(s_d, c_d, dev(p["count"]), dev(p["cache_len"]), path=dev(p["path"]))
+    torch.cuda.synchronize()
+    assert np.array_equal(nl.cpu().numpy(), p["cache_len"] + p["count"])
+    rng = np.random.default_rng(1)
+    per = w.slots * w.row_bytes
+    for _ in range(48):
+        l, b = int(rng.integers(0, w.planes)), int(rng.integers(0, w.B))
+        base = (l * w.B + b) * per
+        init = ((np.arange(base, base + per, dtype=np.int64) * 7 + 3) % 251).astype(np.uint8)
+        want, _ = oracle.kv_commit(scratch[l:l + 1, b:b + 1], init.reshape(1, 1, w.slots, w.row_bytes),
+                                   p["path"][b:b + 1], p["count"][b:b + 1], p["cache_len"][b:b + 1])
+        got = c_d[l, b].cpu().numpy()
+        assert np.array_equal(got, want[0, 0]), (l, b)

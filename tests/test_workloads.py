@@ -40,6 +40,14 @@ def test_shapes_of_every_workload_at_small_sizes():
             assert d["node_logits"].shape == (2, 45, 300) and d["parents"].shape == (45,)
         elif w.mode == "topk":
             assert d["logits"].shape == (2, 300) and d["k"] == w.K
+        elif w.mode == "kv":
+            assert d["path"].shape == (2, w.K) and d["count"].shape == (2,)
+            assert np.all(d["path"][:, 0] == 0) and np.all((1 <= d["count"]) & (d["count"] <= 8))
+            assert np.all(d["cache_len"] + d["count"] <= w.slots)
+            for b in range(2):
+                c = d["count"][b]
+                assert np.all(np.diff(d["path"][b, :c]) > 0) and np.all(d["path"][b, :c] < w.K)
+            continue
         else:
             assert d["node_logits"].shape == (2, w.K, 300) and d["parents"].shape == (2, w.K)
             assert d["node_tokens"].shape == (2, w.K) and d["node_count"].shape == (2,)

@@ -33,6 +33,13 @@ Workloads (sizes and distributions as specified for this verify step):
   topk_128k        top-k of draft rows for tree expansion, 512 rows (64
                    sequences x 8 frontier nodes), V=128256, bf16, k=8; rows are
                    chain_t1_128k's draft rows (peaked target + N(0, C3_SIGMA^2)).
+  kv_commit_b64    KV commit after a tree verify, B=64 sequences, 64 planes (32
+                   layers x keys and values), 2048-byte rows (8 KV heads x head
+                   dim 128 x bf16), N=64 scratch rows (the tree's nodes), S=512
+                   cache slots; per sequence a cache length uniform in [0, 440]
+                   and an accepted path of 1 to 8 entries (root, then strictly
+                   increasing node ids, as along a breadth-first tree's root
+                   path).  Scratch and cache contents are random bytes.
 
 Drafted tokens are "sampled from q" with the Gumbel-max construction
 (argmax_i of d_i / T + G_i with G_i standard Gumbel), which draws exactly from
@@ -59,17 +66,21 @@ C3_SIGMA = 0.66
 class Workload:
     name: str
     wid: int                 # seed component
-    mode: str                # "chain" | "greedy" | "tree" | "tree_dyn" | "topk"
+    mode: str                # "chain" | "greedy" | "tree" | "tree_dyn" | "topk" | "kv"
     B: int
     V: int
     dtype: str               # "f32" | "bf16"
-    K: int = 0               # chain / greedy draft length; tree_dyn: most nodes per tree; topk: k
+    K: int = 0               # chain / greedy draft length; tree_dyn: most nodes per tree; topk: k;
+                             # kv: scratch rows per sequence
     T: float = 0.0           # chain temperature
     branching: tuple = field(default_factory=tuple)   # tree only
     recipe: str = "normal"   # target rows: "normal" | "peaked" | "zipf"
     target_sd: float = 2.0   # sd of the "normal" recipe
     sigma: float = 0.0       # sd of the draft noise (chain)
     steps: int = 1000
+    planes: int = 0          # kv: planes (layers x keys/values)
+    row_bytes: int = 0       # kv: bytes per row of a plane
+    slots: int = 0           # kv: cache slots per sequence
 
     def with_sizes(self, **kw) -> "Workload":
         """Same recipe at other sizes (for small parity cases)."""
@@ -91,6 +102,8 @@ WORKLOADS = {
                               K=64, recipe="peaked"),
     "topk_128k": Workload("topk_128k", 7, "topk", B=512, V=128256, dtype="bf16", K=8,
                           recipe="peaked", sigma=C3_SIGMA),
+    "kv_commit_b64": Workload("kv_commit_b64", 8, "kv", B=64, V=0, dtype="u8", K=64, planes=64,
+                              row_bytes=2048, slots=512),
 }
 
 TARGET, DRAFT_NOISE, STRUCTURE, DRAFT_TOKENS, UNIFORMS = range(5)
@@ -328,6 +341,36 @@ def topk_inputs(w: Workload, step: int = 0) -> dict:
     return dict(logits=_store(x, w.dtype), k=w.K, dtype=w.dtype)
 
 
+def kv_paths(w: Workload, step: int = 0, max_count: int = 8) -> dict:
+    """The per-step part of a KV commit: path [B][N] (root, then strictly
+    increasing node ids; entries past the count are 0), count [B] uniform in
+    [1, max_count], cache_len [B] uniform in [0, S - max_count]."""
+    assert w.mode == "kv"
+    rng = rng_for(w, STRUCTURE, step)
+    B, N, S = w.B, w.K, w.slots
+    mc = max(1, min(max_count, N))
+    count = rng.integers(1, mc + 1, size=B).astype(np.int32)
+    path = np.zeros((B, N), np.int32)
+    for b in range(B):
+        c = int(count[b])
+        if c > 1:
+            path[b, 1:c] = np.sort(rng.choice(np.arange(1, N), size=c - 1, replace=False))
+    cache_len = rng.integers(0, max(S - mc, 0) + 1, size=B).astype(np.int32)
+    return dict(path=path, count=count, cache_len=cache_len)
+
+
+def kv_scratch(w: Workload, step: int = 0) -> np.ndarray:
+    """Scratch rows [planes][B][N][row_bytes] of random bytes."""
+    rng = rng_for(w, TARGET, step)
+    return rng.integers(0, 256, size=(w.planes, w.B, w.K, w.row_bytes), dtype=np.uint8)
+
+
+def kv_cache_init(w: Workload, step: int = 0) -> np.ndarray:
+    """Initial cache [planes][B][S][row_bytes] of random bytes (small sizes only)."""
+    rng = rng_for(w, DRAFT_NOISE, step)
+    return rng.integers(0, 256, size=(w.planes, w.B, w.slots, w.row_bytes), dtype=np.uint8)
+
+
 def make_inputs(w: Workload, step: int = 0) -> dict:
     if w.mode == "chain":
         return chain_inputs(w, step)
@@ -337,4 +380,6 @@ def make_inputs(w: Workload, step: int = 0) -> dict:
         return tree_dyn_inputs(w, step)
     if w.mode == "topk":
         return topk_inputs(w, step)
+    if w.mode == "kv":
+        return kv_paths(w, step)
     return tree_inputs(w, step)
