@@ -17,6 +17,7 @@ alone (the two-phase entry point's first kernel) is reported beside it.
 from __future__ import annotations
 
 import argparse
+import functools
 import hashlib
 import json
 import os
@@ -60,6 +61,40 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
+def kv_bytes(w, count) -> int:
+    """KV commit: every committed row read from the scratch and written to
+    the cache, in every plane."""
+    return 2 * int(np.asarray(count).sum()) * w.planes * w.row_bytes
+
+
+def kv_cache_pattern(w, device):
+    """The initial cache on the device: byte j of the flat array is
+    (7 j + 3) mod 251 (filled a plane at a time)."""
+    import torch
+    shape = (w.planes, w.B, w.slots, w.row_bytes)
+    out = torch.empty(shape, dtype=torch.uint8, device=device)
+    per = w.B * w.slots * w.row_bytes
+    for l in range(w.planes):
+        j = torch.arange(l * per, (l + 1) * per, dtype=torch.int64, device=device)
+        out[l] = ((j * 7 + 3) % 251).to(torch.uint8).view(shape[1:])
+    return out
+
+
+@functools.lru_cache(maxsize=2)
+def kv_scratch_host(w):
+    """The KV commit's scratch rows on the host, generated once per workload."""
+    import workloads as W
+    return W.kv_scratch(w, 0)
+
+
+def kv_sample(w, inp):
+    """The CPU leg's sample of a KV commit step: plane 0 of every sequence."""
+    per = w.B * w.slots * w.row_bytes
+    cache0 = ((np.arange(per, dtype=np.int64) * 7 + 3) % 251).astype(np.uint8)
+    return dict(scratch=kv_scratch_host(w)[:1], cache=cache0.reshape(1, w.B, w.slots, w.row_bytes),
+                **{k: inp[k] for k in ("path", "count", "cache_len")})
+
+
 def set_bytes(w, inputs=None) -> int:
     """Logit bytes one step reads (every row once).  Per-sequence trees read
     only their trees' rows: their node counts when `inputs` are given, else
@@ -73,6 +108,8 @@ def set_bytes(w, inputs=None) -> int:
         rows = int(inputs["node_count"].sum()) if inputs is not None else w.B * w.K
     elif w.mode == "topk":
         rows = w.B
+    elif w.mode == "kv":
+        return kv_bytes(w, inputs["count"]) if inputs is not None else 2 * w.B * 4 * w.planes * w.row_bytes
     else:
         rows = w.B * (1 + sum(int(np.prod(w.branching[:i + 1])) for i in range(len(w.branching))))
     return rows * w.V * esize
@@ -90,6 +127,9 @@ def oracle_step(w, inp):
                                              inp["node_count"])
     if w.mode == "topk":
         return oracle.topk(inp["logits"], w.K)
+    if w.mode == "kv":
+        return oracle.kv_commit(inp["scratch"], inp["cache"], inp["path"], inp["count"],
+                                inp["cache_len"])
     return oracle.verify_tree_greedy(inp["node_logits"], inp["node_tokens"], inp["parents"])
 
 
@@ -103,11 +143,22 @@ def check(w, inp, gpu_out):
         return parity.check_tree_dyn(inp, *gpu_out)
     if w.mode == "topk":
         return parity.check_topk(inp, *gpu_out)
+    if w.mode == "kv":   # plane 0 of every sequence, and every new length
+        want_c, want_l = oracle_step(w, inp)
+        got_c0, got_l = gpu_out
+        assert np.array_equal(got_l, want_l), "KV commit lengths differ from the oracle's"
+        assert np.array_equal(got_c0, want_c[0]), "KV commit plane 0 differs from the oracle's"
+        return {"sequences": int(w.B), "exact": int(w.B)}
     return parity.check_tree(inp, *gpu_out)
 
 
 def cpu_baseline(w, inp, budget_s: float, gpu_out):
-    """The oracle as it stands, single-threaded, on whole steps of the same workload."""
+    """The oracle as it stands, single-threaded, on whole steps of the same
+    workload (for the KV commit, on one plane of the step, scaled)."""
+    scale, what = 1.0, "whole steps"
+    if w.mode == "kv":
+        inp = kv_sample(w, inp)
+        scale, what = 1.0 / w.planes, f"steps on plane 0 of {w.planes} (rate scaled by 1/{w.planes})"
     t0 = time.perf_counter()
     steps = 0
     while True:
@@ -117,9 +168,9 @@ def cpu_baseline(w, inp, budget_s: float, gpu_out):
             break
     dt = time.perf_counter() - t0
     counts = check(w, inp, gpu_out)
-    unit = "top-k steps/s" if w.mode == "topk" else "verify steps/s"
-    return {"value": steps / dt, "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": f"{steps} whole steps of input set 0 of {w.name}, fp64, one thread, {dt:.1f} s",
+    unit = {"topk": "top-k steps/s", "kv": "KV commit steps/s"}.get(w.mode, "verify steps/s")
+    return {"value": steps / dt * scale, "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{steps} {what} of input set 0 of {w.name}, one thread, {dt:.1f} s",
             "parity_on_sample": dict(counts)}
 
 
@@ -167,7 +218,7 @@ def main():
     device = torch.device("cuda:0")
     print(f"[bench] generating {nsets} input sets of {w.name}", file=sys.stderr, flush=True)
     host_sets = [W.make_inputs(w, s) for s in range(nsets)]
-    if w.mode == "tree_dyn":  # the mean over the rotated sets, each timed equally often
+    if w.mode in ("tree_dyn", "kv"):  # the mean over the rotated sets, each timed equally often
         nbytes = int(round(np.mean([set_bytes(w, h) for h in host_sets])))
     sets = [{k: to_dev(v, device) for k, v in h.items() if isinstance(v, np.ndarray)}
             for h in host_sets]
@@ -248,6 +299,27 @@ def main():
         dominant_name = "k_tree_dyn (whole step)"
         io_bytes = 4 * B * Nmax * 2 + 4 * B + 4 * B * (2 * Nmax + 1)
         verified = float(np.mean([(h["node_count"] - 1).sum() for h in host_sets]))
+    elif w.mode == "kv":
+        scratch = to_dev(kv_scratch_host(w), device)
+        cache = kv_cache_pattern(w, device)
+        new_len = torch.empty((B,), dtype=torch.int32, device=device)
+        launches = [sv.spec_kv_commit(scratch, cache, s["count"], s["cache_len"], path=s["path"],
+                                      new_len=new_len, stream=stream, prepare=True)[0]
+                    for s in sets]
+
+        def step(i):
+            launches[i % nsets]()
+        stats_phase = None
+
+        def outputs():
+            c = kv_cache_pattern(w, device)
+            s = sets[0]
+            nl = sv.spec_kv_commit(scratch, c, s["count"], s["cache_len"], path=s["path"])
+            torch.cuda.synchronize()
+            return c[0].cpu().numpy(), nl.cpu().numpy()
+        dominant_name = "k_kv_commit (whole step)"
+        io_bytes = 4 * B * (w.K + 3)
+        verified = 0
     elif w.mode == "topk":
         k = w.K
         ws = sv.workspace(sv.SPEC_MODE_TOPK, B, k, V, dt_code, device)
@@ -334,7 +406,7 @@ def main():
     achieved_dom = nbytes / (ms_dom * 1e-3) / 1e9
     is_tree = w.mode in ("tree", "tree_dyn")
     acceptance = None
-    if w.mode != "topk":
+    if w.mode not in ("topk", "kv"):
         emitted = (gpu_out[2] + 1).sum() if is_tree else (gpu_out[1] + 1).sum()
         # Acceptance on the timed batch (input set 0): mean accepted drafts per
         # sequence, and for chains the per-token acceptance rate alpha = accepted
@@ -354,12 +426,18 @@ def main():
         config.update(Nmax=w.K, mean_nodes=float(np.mean([h["node_count"].mean() for h in host_sets])))
     elif w.mode == "topk":
         config.update(rows=B, k=w.K)
+    elif w.mode == "kv":
+        config.update(planes=w.planes, row_bytes=w.row_bytes, scratch_rows=w.K, cache_slots=w.slots,
+                      mean_committed=float(np.mean([h["count"].mean() for h in host_sets])))
+        for key in ("logit_bytes_per_step", "V", "logits"):
+            config.pop(key, None)
+        config["bytes_per_step"] = nbytes
     else:
         config.update(branching=list(w.branching))
     line = {
         "metric": METRIC,
         "value": steps_per_s,
-        "unit": "top-k steps/s" if w.mode == "topk" else "verify steps/s",
+        "unit": {"topk": "top-k steps/s", "kv": "KV commit steps/s"}.get(w.mode, "verify steps/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -367,7 +445,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "u8" if w.mode == "kv" else "f32",
         "data": "synthetic",
         "config": config,
         "achieved_GBps": achieved_step,
