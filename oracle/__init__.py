@@ -69,6 +69,8 @@ def _bind(lib):
     lib.oracle_topk.restype = i
     lib.oracle_kv_commit.argtypes = [vp, vp, i, i, i, i, ctypes.c_int64, vp, i, vp, vp, vp]
     lib.oracle_kv_commit.restype = i
+    lib.oracle_tree_mask.argtypes = [vp, vp, i, i, vp, vp]
+    lib.oracle_tree_mask.restype = i
     return lib
 
 
@@ -288,3 +290,23 @@ def kv_commit(scratch, cache, path, count, length, *, lib=None):
     if rc != 0:
         raise ValueError(f"oracle_kv_commit rejected its arguments (code {rc})")
     return out, new_len
+
+
+def tree_mask(parents, node_count=None, *, lib=None):
+    """Tree attention mask: (mask [B][N][ceil(N/32)] uint32 ancestor bits,
+    depth [B][N] int32), per sequence from parents [B][N] (or one tree [N])
+    and node_count [B] or None."""
+    lib = lib or load()
+    par = np.ascontiguousarray(parents, dtype=np.int32)
+    if par.ndim == 1:
+        par = par[None]
+    B, N = par.shape
+    W = (N + 31) // 32
+    mask = np.empty((B, N, W), np.uint32)
+    depth = np.empty((B, N), np.int32)
+    cnt = None if node_count is None else np.ascontiguousarray(node_count, dtype=np.int32)
+    rc = lib.oracle_tree_mask(_ptr(par), None if cnt is None else _ptr(cnt), B, N, _ptr(mask),
+                              _ptr(depth))
+    if rc != 0:
+        raise ValueError(f"oracle_tree_mask rejected its arguments (code {rc})")
+    return mask, depth

@@ -680,3 +680,64 @@ int oracle_kv_commit(const void *scratch, void *cache, int planes, int B, int N,
     }
     return OR_OK;
 }
+
+/*
+ * Tree attention mask (the French lesson, section on verifying a tree with
+ * attention: one forward over the tree where each token attends only to its
+ * ancestors; the forum post §10 adds that this needs custom masks and
+ * position ids).
+ *
+ *   parents    [B][N]  parents[b][0] is the root's entry; node v > 0 is
+ *                      attached when 0 <= parents[b][v] < v and its parent is
+ *                      attached (the root always is);
+ *   node_count [B] or NULL (all N): nodes v >= node_count[b] are padding
+ *                      (node_count is clamped to [1, N]);
+ *   mask  [B][N][W] uint32, W = ceil(N / 32): for an attached node v, bit j
+ *                      (word j / 32, bit j % 32) is set iff j == v or j is an
+ *                      ancestor of v; rows of other nodes are all zero;
+ *   depth [B][N] int32: the number of ancestors of an attached node, -1 for
+ *                      the others (a position id is the cache length plus it).
+ * Each node walks to the root through its parent entries, one step at a time.
+ */
+int oracle_tree_mask(const int32_t *parents, const int32_t *node_count, int B, int N,
+                     uint32_t *mask, int32_t *depth)
+{
+    if (B < 0 || N < 1 || (B > 0 && (!parents || !mask || !depth)))
+        return OR_BAD_ARG;
+    int W = (N + 31) / 32;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *par = parents + (size_t)b * N;
+        int n = node_count ? node_count[b] : N;
+        if (n < 1)
+            n = 1;
+        if (n > N)
+            n = N;
+        for (int v = 0; v < N; ++v) {
+            uint32_t *row = mask + ((size_t)b * N + v) * W;
+            for (int w = 0; w < W; ++w)
+                row[w] = 0;
+            depth[(size_t)b * N + v] = -1;
+            if (v >= n)
+                continue;
+            int cur = v, steps = 0, attached = 1;
+            row[cur / 32] |= 1u << (cur % 32);
+            while (cur != 0) {
+                int p = par[cur];
+                if (p < 0 || p >= cur) {
+                    attached = 0;
+                    break;
+                }
+                cur = p;
+                row[cur / 32] |= 1u << (cur % 32);
+                ++steps;
+            }
+            if (!attached) {
+                for (int w = 0; w < W; ++w)
+                    row[w] = 0;
+                continue;
+            }
+            depth[(size_t)b * N + v] = steps;
+        }
+    }
+    return OR_OK;
+}

@@ -657,6 +657,84 @@ def pin_kv_commit_invariants(lib, seed=59):
         assert np.array_equal(two, one) and np.array_equal(l2, l12), trial
 
 
+# ------------------------------------------------------------- tree attention mask
+
+def _mask_bits(mask_rows, N):
+    """Boolean [.., N, N] from packed ancestor words [.., N, ceil(N/32)]."""
+    w = np.asarray(mask_rows, np.uint32)
+    j = np.arange(N)
+    return ((w[..., j // 32] >> (j % 32).astype(np.uint32)) & 1).astype(bool)
+
+
+def pin_tree_mask_figure(lib):
+    """The French lesson's drawn tree: each node attends to itself and its
+    ancestors only (tests/golden/tree_mask_p1_figure.json, written by hand)."""
+    g = json.load(open(os.path.join(GOLDEN, "tree_mask_p1_figure.json")))
+    mask, depth = oracle.tree_mask(g["parents"], lib=lib)
+    assert np.array_equal(_mask_bits(mask[0], 7), np.array(g["mask"], bool))
+    assert list(depth[0]) == g["depth"]
+
+
+def _subtrees(par, n):
+    """Descendant sets by walking children lists top-down from each node,
+    over the attached nodes below n (an independent construction)."""
+    children = [[] for _ in range(n)]
+    attached = [False] * n
+    attached[0] = True
+    for v in range(1, n):
+        p = par[v]
+        if 0 <= p < v and attached[p]:
+            attached[v] = True
+            children[p].append(v)
+    sub = []
+    for j in range(n):
+        seen, stack = set(), [j] if attached[j] else []
+        while stack:
+            u = stack.pop()
+            seen.add(u)
+            stack.extend(children[u])
+        sub.append(seen)
+    return attached, sub
+
+
+def pin_tree_mask_descendants(lib, seed=61):
+    """Random per-sequence trees with padding and out-of-range parent
+    entries: mask[i][j] holds iff i lies in j's subtree (children lists
+    walked top-down), and depth is the number of strict ancestors."""
+    rng = np.random.default_rng(seed)
+    for trial in range(60):
+        N, B = int(rng.integers(1, 80)), 4
+        par = np.zeros((B, N), np.int32)
+        counts = rng.integers(0, N + 3, size=B).astype(np.int32)   # clamped to [1, N]
+        for b in range(B):
+            par[b, 0] = -1
+            for v in range(1, N):
+                par[b, v] = rng.integers(0, v) if rng.random() > 0.05 else rng.choice([-1, v, v + 5])
+        mask, depth = oracle.tree_mask(par, counts, lib=lib)
+        bits = _mask_bits(mask, N)
+        for b in range(B):
+            n = int(min(max(counts[b], 1), N))
+            attached, sub = _subtrees(par[b], n)
+            want = np.zeros((N, N), bool)
+            for j in range(n):
+                for i in sub[j]:
+                    want[i, j] = True
+            assert np.array_equal(bits[b], want), (trial, b)
+            for v in range(N):
+                d = int(want[v].sum()) - 1 if v < n and attached[v] else -1
+                assert depth[b, v] == d, (trial, b, v)
+
+
+def pin_tree_mask_chain(lib):
+    """A chain (parents v - 1) is plain causal attention: a lower-triangular
+    mask, and depth v."""
+    for N in (1, 5, 32, 33, 100):
+        par = np.arange(-1, N - 1, dtype=np.int32)
+        mask, depth = oracle.tree_mask(par, lib=lib)
+        assert np.array_equal(_mask_bits(mask[0], N), np.tril(np.ones((N, N), bool)))
+        assert list(depth[0]) == list(range(N))
+
+
 # ------------------------------------------------------------- chi-square
 
 def pin_chi_square(lib, n=50_000, seed=19):
@@ -688,4 +766,5 @@ ALL_PINS = [pin_exact_law, pin_expected_tokens, pin_page_counts, pin_strict_acce
             pin_inverse_cdf, pin_greedy, pin_tree_bruteforce, pin_tree_chain,
             pin_tree_figure, pin_tree_dyn_bruteforce, pin_tree_dyn_padding, pin_tree_dyn_chain,
             pin_topk_sort, pin_topk_argmax, pin_kv_rollback_exercise, pin_kv_commit_tree_path,
-            pin_kv_commit_invariants, pin_chi_square]
+            pin_kv_commit_invariants, pin_tree_mask_figure, pin_tree_mask_descendants,
+            pin_tree_mask_chain, pin_chi_square]

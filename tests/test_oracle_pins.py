@@ -104,6 +104,14 @@ MUTANTS = [
     ("KV commit keeps the old length", "        new_len[b] = L + c;", "        new_len[b] = L;", 0),
     ("KV commit swaps plane and sequence strides", "size_t from = (((size_t)l * B + b) * N + r)",
      "size_t from = (((size_t)b * planes + l) * N + r)", 0),
+    ("tree mask leaves out the node itself", "            row[cur / 32] |= 1u << (cur % 32);\n            while",
+     "            while", 0),
+    ("tree mask depth counts the node itself", "            depth[(size_t)b * N + v] = steps;",
+     "            depth[(size_t)b * N + v] = steps + 1;", 0),
+    ("tree mask keeps padding rows", "            if (v >= n)\n                continue;\n            int cur",
+     "            int cur", 0),
+    ("tree mask keeps unattached rows", "            if (!attached) {\n                for (int w = 0; w < W; ++w)\n                    row[w] = 0;\n                continue;",
+     "            if (!attached) {\n                continue;", 0),
 ]
 
 QUICK_PINS = [P.pin_exact_law, P.pin_expected_tokens, P.pin_page_counts, P.pin_strict_acceptance,
@@ -111,7 +119,7 @@ QUICK_PINS = [P.pin_exact_law, P.pin_expected_tokens, P.pin_page_counts, P.pin_s
               P.pin_inverse_cdf, P.pin_greedy, P.pin_tree_bruteforce, P.pin_tree_figure,
               P.pin_tree_dyn_bruteforce, P.pin_tree_dyn_padding, P.pin_topk_sort,
               P.pin_kv_rollback_exercise, P.pin_kv_commit_tree_path, P.pin_kv_commit_invariants,
-              P.pin_chi_square]
+              P.pin_tree_mask_figure, P.pin_tree_mask_descendants, P.pin_chi_square]
 
 
 def _mutant_lib(tmpdir, pattern, repl, which):
