@@ -315,6 +315,31 @@ spec_status spec_kv_commit(const void *scratch, void *cache, int32_t planes, int
                            const int32_t *count, const int32_t *cache_len, int32_t *new_len,
                            hipStream_t stream);
 
+/*
+ * Tree attention mask for the verify forward (French lesson, section on
+ * verifying a tree with attention: each drafted token attends only to its
+ * ancestors in the tree, so the whole tree is verified in one forward; forum
+ * post §10: this needs custom masks and position ids).  Per sequence and
+ * node, the packed set of nodes the node attends to (itself and its
+ * ancestors) and its depth (its position id is the cache length plus the
+ * depth).
+ *
+ *   parents    DEVICE [B][N] int32, the numbering of spec_verify_tree_greedy(_dyn):
+ *              node v > 0 is attached when 0 <= parents[b][v] < v and its
+ *              parent is attached; node 0 is the root.
+ *   node_count nullable DEVICE [B] int32: nodes v >= node_count[b] are padding
+ *              (clamped to [1, N]); NULL means N for every sequence.
+ *   1 <= N <= SPEC_VERIFY_MAX_TREE_NODES.
+ *   mask       DEVICE [B][N][ceil(N/32)] uint32: for an attached node v, bit j % 32
+ *              of word j / 32 is set iff j == v or j is an ancestor of v; the rows
+ *              of padding and unattached nodes are all zero.
+ *   depth      DEVICE [B][N] int32: the number of ancestors, -1 for padding and
+ *              unattached nodes.
+ * One kernel launch; no workspace.
+ */
+spec_status spec_tree_mask(const int32_t *parents, const int32_t *node_count, int32_t B, int32_t N,
+                           uint32_t *mask, int32_t *depth, hipStream_t stream);
+
 /* Static text for a status code. */
 const char *spec_verify_status_string(spec_status status);
 

@@ -58,9 +58,11 @@ def _load(path: str = LIB_PATH):
     lib.spec_draft_topk.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.spec_kv_commit.argtypes = [vp, vp, i32, i32, i32, i32, ctypes.c_int64, vp, i32, vp, vp, vp,
                                    vp]
+    lib.spec_tree_mask.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     for fn in ("spec_verify_workspace_bytes", "spec_verify_chain", "spec_verify_chain_stats",
                "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy",
-               "spec_verify_tree_greedy_dyn", "spec_draft_topk", "spec_kv_commit"):
+               "spec_verify_tree_greedy_dyn", "spec_draft_topk", "spec_kv_commit",
+               "spec_tree_mask"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -71,7 +73,7 @@ _lib = _load()
 def header_symbols(path: str = HEADER_PATH) -> list[str]:
     """Entry points declared in the public header."""
     text = open(path).read()
-    return sorted(set(re.findall(r"^\S.*?\b(spec_(?:verify|draft|kv)_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\S.*?\b(spec_(?:verify|draft|kv|tree)_\w+)\s*\(", text, flags=re.M)))
 
 
 def library():
@@ -403,3 +405,29 @@ def spec_kv_commit(scratch, cache, count, cache_len, *, path=None, new_len=None,
                       _ptr(scratch), _ptr(cache), planes, B, N, S, row_bytes, _ptr(path), P,
                       _ptr(count), _ptr(cache_len), _ptr(new_len), _stream(dev, stream))
     return (launch, new_len) if prepare else new_len
+
+
+def spec_tree_mask(parents, node_count=None, *, mask=None, depth=None, stream=None, prepare=False):
+    """Tree attention mask: parents int32 [B][N] (device), node_count int32
+    [B] or None.  Returns (mask uint32-as-int32 [B][N][ceil(N/32)], depth
+    int32 [B][N]); bit j % 32 of word j / 32 of row v is set iff node v
+    attends to node j.  With `prepare`, (launch, outputs)."""
+    _check_dev("parents", parents, torch.int32)
+    if parents.dim() != 2:
+        raise ValueError("parents must be [B][N]")
+    B, N = parents.shape
+    W = (N + 31) // 32
+    if node_count is not None:
+        _check_dev("node_count", node_count, torch.int32, (B,))
+    dev = parents.device
+    if mask is None:
+        mask = torch.empty((B, N, W), dtype=torch.int32, device=dev)   # uint32 bits
+    else:
+        _check_dev("mask", mask, torch.int32, (B, N, W))
+    if depth is None:
+        depth = torch.empty((B, N), dtype=torch.int32, device=dev)
+    else:
+        _check_dev("depth", depth, torch.int32, (B, N))
+    launch = _enqueue(prepare, (parents, node_count, mask, depth), "spec_tree_mask", _ptr(parents),
+                      _ptr(node_count), B, N, _ptr(mask), _ptr(depth), _stream(dev, stream))
+    return (launch, (mask, depth)) if prepare else (mask, depth)

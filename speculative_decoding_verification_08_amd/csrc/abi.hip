@@ -1,6 +1,6 @@
 // C ABI of the verify library: argument validation, launch planning and the
 // workspace layout.  Everything here is host code; the kernels live in
-// chain.hip, greedy_tree.hip, topk.hip and kv.hip.
+// chain.hip, greedy_tree.hip, topk.hip, kv.hip and tree_mask.hip.
 #include <math.h>
 #include <string.h>
 
@@ -9,6 +9,7 @@
 
 #include "plan.hpp"
 #include "kv.hpp"
+#include "tree_mask.hpp"
 #include "topk.hpp"
 #include "spec_verify.h"
 
@@ -419,6 +420,24 @@ spec_status spec_kv_commit(const void *scratch, void *cache, int32_t planes, int
     a.len = cache_len;
     a.new_len = new_len;
     return launch_status(launch_kv_commit(a, stream));
+}
+
+spec_status spec_tree_mask(const int32_t *parents, const int32_t *node_count, int32_t B, int32_t N,
+                           uint32_t *mask, int32_t *depth, hipStream_t stream) {
+    if (B < 0 || N < 1 || N > SPEC_VERIFY_MAX_TREE_NODES || N > kMaxMaskNodes)
+        return SPEC_ERR_INVALID_ARG;
+    if (B == 0) return SPEC_OK;
+    if (!parents || !mask || !depth || !aligned(parents, 4) || !aligned(mask, 4) ||
+        !aligned(depth, 4) || (node_count && !aligned(node_count, 4)))
+        return SPEC_ERR_INVALID_ARG;
+    MaskArgs a;
+    a.parents = parents;
+    a.node_count = node_count;
+    a.B = B;
+    a.N = N;
+    a.mask = mask;
+    a.depth = depth;
+    return launch_status(launch_tree_mask(a, stream));
 }
 
 }  // extern "C"

@@ -14,7 +14,7 @@ def test_every_declared_symbol_is_exported():
     syms = sv.header_symbols()
     assert {"spec_verify_chain", "spec_verify_greedy", "spec_verify_tree_greedy",
             "spec_verify_tree_greedy_dyn", "spec_verify_workspace_bytes",
-            "spec_draft_topk", "spec_kv_commit"} <= set(syms)
+            "spec_draft_topk", "spec_kv_commit", "spec_tree_mask"} <= set(syms)
     lib = sv.library()
     for s in syms:
         assert hasattr(lib, s), s
@@ -154,6 +154,20 @@ def test_kv_commit_argument_errors():
     assert call(c=A + 64) == E                         # cache overlaps scratch
     assert call(path=FAKE, P=-1) == E
     assert call(N=-1) == E and call(S=-1) == E
+
+
+def test_tree_mask_argument_errors():
+    lib = sv.library()
+    E = sv.SPEC_ERR_INVALID_ARG
+    m = lib.spec_tree_mask
+    assert m(FAKE, None, 0, 10, FAKE, FAKE, None) == sv.SPEC_OK
+    assert m(FAKE, None, 2, 0, FAKE, FAKE, None) == E
+    assert m(FAKE, None, 2, 257, FAKE, FAKE, None) == E
+    assert m(FAKE, None, -1, 10, FAKE, FAKE, None) == E
+    assert m(None, None, 2, 10, FAKE, FAKE, None) == E
+    assert m(FAKE, None, 2, 10, None, FAKE, None) == E
+    assert m(FAKE, FAKE + 2, 2, 10, FAKE, FAKE, None) == E
+    assert m(FAKE, None, 2, 10, FAKE, FAKE + 1, None) == E
 
 
 def test_status_strings():

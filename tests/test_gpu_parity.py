@@ -692,3 +692,52 @@ def test_kv_commit_full_size(sv):
                                    p["path"][b:b + 1], p["count"][b:b + 1], p["cache_len"][b:b + 1])
         got = c_d[l, b].cpu().numpy()
         assert np.array_equal(got, want[0, 0]), (l, b)
+
+
+# ------------------------------------------------------------------ tree attention mask
+
+def run_mask(sv, parents, counts=None):
+    m, d = sv.spec_tree_mask(dev(np.ascontiguousarray(parents, np.int32)),
+                             None if counts is None else dev(np.asarray(counts, np.int32)))
+    torch.cuda.synchronize()
+    return m.cpu().numpy().view(np.uint32), d.cpu().numpy()
+
+
+@pytest.mark.parametrize("N", [1, 7, 32, 33, 64, 100, 256])
+def test_tree_mask_random_trees(sv, N):
+    rng = np.random.default_rng(N)
+    B = 9
+    par = np.zeros((B, N), np.int32)
+    for b in range(B):
+        par[b, 0] = -1
+        for v in range(1, N):
+            par[b, v] = rng.integers(0, v) if rng.random() > 0.04 else rng.choice([-1, v, v + 3])
+    for counts in (None, rng.integers(-1, N + 2, size=B).astype(np.int32)):
+        case(f"tree mask N={N} counts={'none' if counts is None else 'ragged'}")
+        want_m, want_d = oracle.tree_mask(par, counts)
+        got_m, got_d = run_mask(sv, par, counts)
+        assert np.array_equal(got_d, want_d)
+        assert np.array_equal(got_m, want_m)
+
+
+def test_tree_mask_figure_and_chain(sv):
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tree_mask_p1_figure.json")))
+    case("tree mask of the drawn tree")
+    m, d = run_mask(sv, np.array([g["parents"]], np.int32))
+    bits = ((m[0][:, np.arange(7) // 32] >> (np.arange(7) % 32).astype(np.uint32)) & 1).astype(int)
+    assert bits.tolist() == g["mask"] and d[0].tolist() == g["depth"]
+    case("tree mask of a 256-node chain")
+    m, d = run_mask(sv, np.arange(-1, 255, dtype=np.int32)[None])
+    want_m, want_d = oracle.tree_mask(np.arange(-1, 255, dtype=np.int32))
+    assert np.array_equal(m, want_m) and np.array_equal(d, want_d)
+
+
+def test_tree_mask_full_size(sv):
+    w = W.WORKLOADS["tree_mask_b64"]
+    for step in (0, 1):
+        case(f"tree_mask_b64 step {step}")
+        t = W.tree_mask_inputs(w, step)
+        want_m, want_d = oracle.tree_mask(t["parents"], t["node_count"])
+        got_m, got_d = run_mask(sv, t["parents"], t["node_count"])
+        assert np.array_equal(got_m, want_m) and np.array_equal(got_d, want_d)

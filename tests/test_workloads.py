@@ -40,6 +40,13 @@ def test_shapes_of_every_workload_at_small_sizes():
             assert d["node_logits"].shape == (2, 45, 300) and d["parents"].shape == (45,)
         elif w.mode == "topk":
             assert d["logits"].shape == (2, 300) and d["k"] == w.K
+        elif w.mode == "mask":
+            assert d["parents"].shape == (2, w.K) and d["node_count"].shape == (2,)
+            for b in range(2):
+                n = d["node_count"][b]
+                assert w.K // 4 <= n <= w.K and d["parents"][b, 0] == -1
+                assert all(0 <= d["parents"][b, v] < v for v in range(1, n))
+            continue
         elif w.mode == "kv":
             assert d["path"].shape == (2, w.K) and d["count"].shape == (2,)
             assert np.all(d["path"][:, 0] == 0) and np.all((1 <= d["count"]) & (d["count"] <= 8))

@@ -40,6 +40,9 @@ Workloads (sizes and distributions as specified for this verify step):
                    and an accepted path of 1 to 8 entries (root, then strictly
                    increasing node ids, as along a breadth-first tree's root
                    path).  Scratch and cache contents are random bytes.
+  tree_mask_b64    tree attention mask for 64 sequences' trees of at most 64
+                   nodes, shaped as in tree_dyn_128k (counts uniform in
+                   [16, 64], 1 to 4 children per node, breadth-first).
 
 Drafted tokens are "sampled from q" with the Gumbel-max construction
 (argmax_i of d_i / T + G_i with G_i standard Gumbel), which draws exactly from
@@ -66,7 +69,7 @@ C3_SIGMA = 0.66
 class Workload:
     name: str
     wid: int                 # seed component
-    mode: str                # "chain" | "greedy" | "tree" | "tree_dyn" | "topk" | "kv"
+    mode: str                # "chain" | "greedy" | "tree" | "tree_dyn" | "topk" | "kv" | "mask"
     B: int
     V: int
     dtype: str               # "f32" | "bf16"
@@ -104,6 +107,7 @@ WORKLOADS = {
                           recipe="peaked", sigma=C3_SIGMA),
     "kv_commit_b64": Workload("kv_commit_b64", 8, "kv", B=64, V=0, dtype="u8", K=64, planes=64,
                               row_bytes=2048, slots=512),
+    "tree_mask_b64": Workload("tree_mask_b64", 9, "mask", B=64, V=0, dtype="i32", K=64),
 }
 
 TARGET, DRAFT_NOISE, STRUCTURE, DRAFT_TOKENS, UNIFORMS = range(5)
@@ -371,6 +375,22 @@ def kv_cache_init(w: Workload, step: int = 0) -> np.ndarray:
     return rng.integers(0, 256, size=(w.planes, w.B, w.slots, w.row_bytes), dtype=np.uint8)
 
 
+def tree_mask_inputs(w: Workload, step: int = 0, nmin: int | None = None) -> dict:
+    """Per-sequence trees for the attention mask: parents [B][Nmax] (padding
+    parent 0) and node_count [B]."""
+    assert w.mode == "mask"
+    rng = rng_for(w, STRUCTURE, step)
+    B, Nmax = w.B, w.K
+    nmin = max(1, Nmax // 4) if nmin is None else nmin
+    parents = np.zeros((B, Nmax), np.int32)
+    counts = np.zeros(B, np.int32)
+    for b in range(B):
+        par = dyn_tree(rng, Nmax, nmin)
+        counts[b] = len(par)
+        parents[b, :len(par)] = par
+    return dict(parents=parents, node_count=counts)
+
+
 def make_inputs(w: Workload, step: int = 0) -> dict:
     if w.mode == "chain":
         return chain_inputs(w, step)
@@ -382,4 +402,6 @@ def make_inputs(w: Workload, step: int = 0) -> dict:
         return topk_inputs(w, step)
     if w.mode == "kv":
         return kv_paths(w, step)
+    if w.mode == "mask":
+        return tree_mask_inputs(w, step)
     return tree_inputs(w, step)
