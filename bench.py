@@ -110,6 +110,8 @@ def set_bytes(w, inputs=None) -> int:
         rows = w.B
     elif w.mode == "kv":
         return kv_bytes(w, inputs["count"]) if inputs is not None else 2 * w.B * 4 * w.planes * w.row_bytes
+    elif w.mode == "mask":   # parents and counts read, mask words and depths written
+        return w.B * w.K * 4 + w.B * 4 + w.B * w.K * ((w.K + 31) // 32) * 4 + w.B * w.K * 4
     else:
         rows = w.B * (1 + sum(int(np.prod(w.branching[:i + 1])) for i in range(len(w.branching))))
     return rows * w.V * esize
@@ -130,6 +132,8 @@ def oracle_step(w, inp):
     if w.mode == "kv":
         return oracle.kv_commit(inp["scratch"], inp["cache"], inp["path"], inp["count"],
                                 inp["cache_len"])
+    if w.mode == "mask":
+        return oracle.tree_mask(inp["parents"], inp["node_count"])
     return oracle.verify_tree_greedy(inp["node_logits"], inp["node_tokens"], inp["parents"])
 
 
@@ -143,6 +147,11 @@ def check(w, inp, gpu_out):
         return parity.check_tree_dyn(inp, *gpu_out)
     if w.mode == "topk":
         return parity.check_topk(inp, *gpu_out)
+    if w.mode == "mask":
+        want_m, want_d = oracle_step(w, inp)
+        assert np.array_equal(gpu_out[0], want_m) and np.array_equal(gpu_out[1], want_d), \
+            "tree mask differs from the oracle's"
+        return {"sequences": int(w.B), "exact": int(w.B)}
     if w.mode == "kv":   # plane 0 of every sequence, and every new length
         want_c, want_l = oracle_step(w, inp)
         got_c0, got_l = gpu_out
@@ -168,7 +177,8 @@ def cpu_baseline(w, inp, budget_s: float, gpu_out):
             break
     dt = time.perf_counter() - t0
     counts = check(w, inp, gpu_out)
-    unit = {"topk": "top-k steps/s", "kv": "KV commit steps/s"}.get(w.mode, "verify steps/s")
+    unit = {"topk": "top-k steps/s", "kv": "KV commit steps/s",
+            "mask": "tree mask steps/s"}.get(w.mode, "verify steps/s")
     return {"value": steps / dt * scale, "unit": unit, "cores": 1, "kind": "oracle",
             "sample": f"{steps} {what} of input set 0 of {w.name}, one thread, {dt:.1f} s",
             "parity_on_sample": dict(counts)}
@@ -215,6 +225,8 @@ def main():
     # [Nmax/4, Nmax]).
     est = nbytes * 5 // 8 if w.mode == "tree_dyn" else nbytes
     nsets = args.rotate or max(1, -(-512_000_000 // est))
+    if w.mode == "mask":   # 64 KB per step lives in L2 whatever rotates; a few sets suffice
+        nsets = args.rotate or 4
     device = torch.device("cuda:0")
     print(f"[bench] generating {nsets} input sets of {w.name}", file=sys.stderr, flush=True)
     host_sets = [W.make_inputs(w, s) for s in range(nsets)]
@@ -320,6 +332,21 @@ def main():
         dominant_name = "k_kv_commit (whole step)"
         io_bytes = 4 * B * (w.K + 3)
         verified = 0
+    elif w.mode == "mask":
+        launches = [sv.spec_tree_mask(s["parents"], s["node_count"], stream=stream, prepare=True)[0]
+                    for s in sets]
+
+        def step(i):
+            launches[i % nsets]()
+        stats_phase = None
+
+        def outputs():
+            m, d = sv.spec_tree_mask(sets[0]["parents"], sets[0]["node_count"])
+            torch.cuda.synchronize()
+            return m.cpu().numpy().view(np.uint32), d.cpu().numpy()
+        dominant_name = "k_tree_mask (whole step)"
+        io_bytes = 0
+        verified = 0
     elif w.mode == "topk":
         k = w.K
         ws = sv.workspace(sv.SPEC_MODE_TOPK, B, k, V, dt_code, device)
@@ -406,7 +433,7 @@ def main():
     achieved_dom = nbytes / (ms_dom * 1e-3) / 1e9
     is_tree = w.mode in ("tree", "tree_dyn")
     acceptance = None
-    if w.mode not in ("topk", "kv"):
+    if w.mode not in ("topk", "kv", "mask"):
         emitted = (gpu_out[2] + 1).sum() if is_tree else (gpu_out[1] + 1).sum()
         # Acceptance on the timed batch (input set 0): mean accepted drafts per
         # sequence, and for chains the per-token acceptance rate alpha = accepted
@@ -426,6 +453,11 @@ def main():
         config.update(Nmax=w.K, mean_nodes=float(np.mean([h["node_count"].mean() for h in host_sets])))
     elif w.mode == "topk":
         config.update(rows=B, k=w.K)
+    elif w.mode == "mask":
+        config.update(Nmax=w.K, mean_nodes=float(np.mean([h["node_count"].mean() for h in host_sets])))
+        for key in ("logit_bytes_per_step", "V", "logits"):
+            config.pop(key, None)
+        config["bytes_per_step"] = nbytes
     elif w.mode == "kv":
         config.update(planes=w.planes, row_bytes=w.row_bytes, scratch_rows=w.K, cache_slots=w.slots,
                       mean_committed=float(np.mean([h["count"].mean() for h in host_sets])))
@@ -437,7 +469,8 @@ def main():
     line = {
         "metric": METRIC,
         "value": steps_per_s,
-        "unit": {"topk": "top-k steps/s", "kv": "KV commit steps/s"}.get(w.mode, "verify steps/s"),
+        "unit": {"topk": "top-k steps/s", "kv": "KV commit steps/s",
+                 "mask": "tree mask steps/s"}.get(w.mode, "verify steps/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -445,7 +478,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8" if w.mode == "kv" else "f32",
+        "dtype": {"kv": "u8", "mask": "int32"}.get(w.mode, "f32"),
         "data": "synthetic",
         "config": config,
         "achieved_GBps": achieved_step,
