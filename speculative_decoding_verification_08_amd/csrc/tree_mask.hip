@@ -6,11 +6,12 @@
 // mask and position ids.
 //
 // One workgroup per sequence, one thread per node (N <= 256).  The parent
-// entries go to LDS; each thread walks its node's chain to the root, setting
-// bits in up to 8 register words (a step's word is chosen by a compare per
-// word, so nothing is indexed dynamically).  A node past the count, or whose
-// chain meets a parent entry outside [0, node), gets an empty row and depth
-// -1.  The walk takes at most `node` steps (indices strictly fall).
+// entries go to LDS; each thread walks its node's chain to the root once for
+// its depth (a node past the count, or whose chain meets a parent entry
+// outside [0, node), gets an empty row and depth -1), then once per output
+// word, accumulating that word in a register and stopping when the indices
+// fall below it.  Every walk takes at most `node` steps (indices strictly
+// fall), and nothing is indexed dynamically.
 #include "device.hpp"
 #include "tree_mask.hpp"
 
@@ -26,41 +27,36 @@ __global__ __launch_bounds__(kWG) void k_tree_mask(MaskArgs a) {
     n = min(max(n, 1), N);
     __syncthreads();
     if (v >= N) return;
-    uint32_t row[kMaxMaskWords];
-#pragma unroll
-    for (int w = 0; w < kMaxMaskWords; ++w) row[w] = 0;
+    // First walk: is the node attached, and how deep is it.
     int d = -1;
     if (v < n) {
-        auto mark = [&](int j) {
-#pragma unroll
-            for (int w = 0; w < kMaxMaskWords; ++w)
-                if (w == (j >> 5)) row[w] |= 1u << (j & 31);
-        };
         int cur = v, steps = 0;
-        bool attached = true;
-        mark(cur);
         while (cur != 0) {
             const int p = s_par[cur];
             if (p < 0 || p >= cur) {
-                attached = false;
+                steps = -1;
                 break;
             }
             cur = p;
-            mark(cur);
             ++steps;
         }
-        if (attached) {
-            d = steps;
-        } else {
-#pragma unroll
-            for (int w = 0; w < kMaxMaskWords; ++w) row[w] = 0;
-        }
+        d = steps;
     }
-    uint32_t *out = a.mask + (static_cast<int64_t>(b) * N + v) * W;
-#pragma unroll
-    for (int w = 0; w < kMaxMaskWords; ++w)
-        if (w < W) out[w] = row[w];
     a.depth[static_cast<int64_t>(b) * N + v] = d;
+    // One walk per output word (in one register), stopping below the word.
+    uint32_t *out = a.mask + (static_cast<int64_t>(b) * N + v) * W;
+    for (int w = 0; w < W; ++w) {
+        uint32_t acc = 0;
+        if (d >= 0 && v >= 32 * w) {
+            int cur = v;
+            for (;;) {
+                if ((cur >> 5) == w) acc |= 1u << (cur & 31);
+                if (cur == 0 || cur < 32 * w) break;
+                cur = s_par[cur];
+            }
+        }
+        out[w] = acc;
+    }
 }
 
 }  // namespace

@@ -6,8 +6,7 @@
 
 namespace sv {
 
-constexpr int kMaxMaskNodes = 256;                 // one thread per node
-constexpr int kMaxMaskWords = kMaxMaskNodes / 32;  // packed ancestor words per row
+constexpr int kMaxMaskNodes = 256;  // one thread per node
 
 struct MaskArgs {
     const int32_t *parents;     // [B][N]
