@@ -26,10 +26,11 @@
 // Hand-over words are 64 bits: the call's tag above a 32-bit value, written
 // with device-scope atomic stores and read with device-scope atomic loads; a
 // reader checks the tag, so nothing left by an earlier call is taken for
-// fresh, and waits (bounded in time) until the word is visible; the
-// workspace needs no initialisation.  A workgroup only waits for workgroups
-// of lower index (dispatched before it) or for the draw workgroups of its own
-// sequence (a sequence has at most 64, far fewer than the chip holds).
+// fresh, and waits (bounded in time) until the word is visible.  Tags are
+// never 0, so a workspace zeroed once before first use needs no clearing.  A
+// workgroup only waits for workgroups of lower index (dispatched before it)
+// or for the draw workgroups of its own sequence (a sequence has at most 64,
+// far fewer than the chip holds).
 #include "device.hpp"
 #include "handover.hpp"
 #include "plan.hpp"

@@ -3,7 +3,8 @@
 // 32-bit value, written with a device-scope atomic store (no wait) and read
 // with a device-scope atomic load, so it is seen across XCDs.  A reader
 // checks the tag, so a word left by an earlier call of any shape is never
-// taken for fresh, and the workspace needs no initialisation.  Waits are
+// taken for fresh; tags are never 0, so a workspace zeroed once before its
+// first use needs no clearing between calls.  Waits are
 // bounded by the 100 MHz wall clock.
 #pragma once
 
