@@ -170,6 +170,26 @@ def test_tree_mask_argument_errors():
     assert m(FAKE, None, 2, 10, FAKE, FAKE + 1, None) == E
 
 
+def test_abi_from_plain_c(tmp_path):
+    """The header and library serve a plain C11 program (gcc, no C++ or Python)."""
+    import os
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(sv.LIB_PATH)
+    exe = str(tmp_path / "abi_from_c")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(root, "include"), "-I", "/opt/rocm/include",
+                    "-o", exe, os.path.join(root, "tests", "c", "abi_from_c.c"),
+                    "-L", libdir, "-l:libspecverify.so", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "C ABI checks passed" in out.stdout
+
+
 def test_status_strings():
     lib = sv.library()
     for s in range(4):
