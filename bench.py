@@ -192,7 +192,20 @@ def cpu_baseline(w, inp, budget_s: float, gpu_out):
             "mask": "tree mask steps/s"}.get(w.mode, "verify steps/s")
     return {"value": steps / dt * scale, "unit": unit, "cores": 1, "kind": "oracle",
             "sample": f"{steps} {what} of input set 0 of {w.name}, one thread, {dt:.1f} s",
-            "parity_on_sample": dict(counts)}
+            "host": host_cpu(), "parity_on_sample": dict(counts)}
+
+
+def host_cpu() -> dict:
+    """The host the CPU leg ran on: CPU model and the threads the OS offers."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu": model, "threads_available": os.cpu_count()}
 
 
 def main():
@@ -450,10 +463,15 @@ def main():
         # sequence, and for chains the per-token acceptance rate alpha = accepted
         # / tested (a sequence tests positions up to its first rejection).
         acc = gpu_out[2] if is_tree else gpu_out[1]
-        acceptance = {"mean_accepted": float(np.mean(acc))}
+        acceptance = {"mean_accepted": float(np.mean(acc)), "mean_emitted": float(np.mean(acc) + 1)}
         if not is_tree:
             tested = acc + (acc < w.K)
-            acceptance["alpha"] = float(acc.sum() / max(int(tested.sum()), 1))
+            alpha = float(acc.sum() / max(int(tested.sum()), 1))
+            acceptance["alpha"] = alpha
+            # Tokens per step if every position were accepted with probability alpha
+            # independently: (1 - alpha^(K+1)) / (1 - alpha).
+            acceptance["expected_emitted_at_alpha"] = (
+                float((1 - alpha ** (w.K + 1)) / (1 - alpha)) if alpha < 1 else float(w.K + 1))
     config = {"workload": w.name, "mode": w.mode, "B": B, "V": V, "logits": w.dtype,
               "input_sets_rotated": nsets, "logit_bytes_per_step": nbytes}
     if w.mode == "chain":
