@@ -741,3 +741,59 @@ def test_tree_mask_full_size(sv):
         want_m, want_d = oracle.tree_mask(t["parents"], t["node_count"])
         got_m, got_d = run_mask(sv, t["parents"], t["node_count"])
         assert np.array_equal(got_m, want_m) and np.array_equal(got_d, want_d)
+
+
+# ------------------------------------------------------------------ mixed random configurations
+
+def test_random_configurations_every_entry_point(sv):
+    """Forty seeded random configurations across every entry point, each
+    compared with the oracle (small sizes, ragged vocabularies, both dtypes)."""
+    rng = np.random.default_rng(2026)
+    modes = ["chain", "greedy", "tree", "tree_dyn", "topk", "mask", "kv"]
+    for trial in range(40):
+        mode = modes[trial % len(modes)]
+        dtype = "bf16" if rng.random() < 0.5 else "f32"
+        V = int(rng.choice([1, 3, 255, 4096, 8191, 8200, 20011, 40000]))
+        case(f"random configuration {trial}: {mode} V={V} {dtype}")
+        if mode == "chain":
+            B, K = int(rng.integers(1, 9)), int(rng.integers(0, 9))
+            d = chain_case("rnd", B, K, V, dtype, float(rng.choice([0.5, 1.0, 1.7])), recipe="peaked",
+                           sigma=float(rng.choice([0.3, 0.8])), step=trial)
+            parity.check_chain(d, *run_chain(sv, d))
+        elif mode == "greedy":
+            w = W.WORKLOADS["greedy_32k"].with_sizes(B=int(rng.integers(1, 9)), K=int(rng.integers(0, 9)),
+                                                   V=V, dtype=dtype)
+            d = W.greedy_inputs(w, trial)
+            parity.check_greedy(d, *run_greedy(sv, d))
+        elif mode == "tree":
+            N = int(rng.integers(1, 30))
+            par = [-1] + [int(rng.integers(0, v)) for v in range(1, N)]
+            w = W.WORKLOADS["tree_128k"].with_sizes(B=int(rng.integers(1, 6)), V=V, dtype=dtype)
+            d = W.tree_inputs(w, trial, parents=np.array(par, np.int32))
+            parity.check_tree(d, *run_tree(sv, d))
+        elif mode == "tree_dyn":
+            w = W.Workload("td", 96, "tree_dyn", B=int(rng.integers(1, 6)), K=int(rng.integers(1, 40)), V=V,
+                           dtype=dtype, recipe="peaked")
+            d = W.tree_dyn_inputs(w, trial, p_match=0.85, nmin=1)
+            parity.check_tree_dyn(d, *run_tree_dyn(sv, d))
+        elif mode == "topk":
+            x = topk_case(int(rng.integers(1, 20)), V, dtype, step=trial)
+            k = int(rng.integers(1, min(V, 8) + 1))
+            parity.check_topk({"logits": x}, *run_topk(sv, x, k))
+        elif mode == "mask":
+            N, B = int(rng.integers(1, 257)), int(rng.integers(1, 5))
+            par = np.zeros((B, N), np.int32)
+            for b in range(B):
+                par[b] = [-1] + [int(rng.integers(0, v)) for v in range(1, N)]
+            cnt = rng.integers(1, N + 1, size=B).astype(np.int32)
+            want_m, want_d = oracle.tree_mask(par, cnt)
+            got_m, got_d = run_mask(sv, par, cnt)
+            assert np.array_equal(got_m, want_m) and np.array_equal(got_d, want_d)
+        else:
+            planes, B, N = int(rng.integers(1, 5)), int(rng.integers(1, 12)), int(rng.integers(1, 40))
+            S, row = int(rng.integers(N, N + 30)), 16 * int(rng.integers(1, 40))
+            scratch, cache, path, count, length = kv_case(rng, planes, B, N, S, row,
+                                                          with_path=bool(rng.random() < 0.7))
+            want_c, want_l = oracle.kv_commit(scratch, cache, path, count, length)
+            got_c, got_l = run_kv(sv, scratch, cache, path, count, length)
+            assert np.array_equal(got_l, want_l) and np.array_equal(got_c, want_c)
