@@ -797,3 +797,84 @@ def test_random_configurations_every_entry_point(sv):
             want_c, want_l = oracle.kv_commit(scratch, cache, path, count, length)
             got_c, got_l = run_kv(sv, scratch, cache, path, count, length)
             assert np.array_equal(got_l, want_l) and np.array_equal(got_c, want_c)
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_graph_capture_mask_and_kv_commit(sv):
+    """The tree mask and the KV commit hand no words between workgroups, so a
+    captured HIP graph of both replays correctly: three replays with new
+    trees, paths and lengths copied into the captured inputs (and eager work
+    and a synchronisation between replays), each against the oracle."""
+    rng = np.random.default_rng(77)
+    B, N, planes, S, row = 4, 20, 2, 40, 64
+    par_d = torch.zeros((B, N), dtype=torch.int32, device=DEV)
+    cnt_d = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    path_d = torch.zeros((B, N), dtype=torch.int32, device=DEV)
+    count_d = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    len_d = torch.zeros((B,), dtype=torch.int32, device=DEV)
+    scratch_h = rng.integers(0, 256, size=(planes, B, N, row), dtype=np.uint8)
+    scratch_d = dev(scratch_h)
+    cache_d = torch.zeros((planes, B, S, row), dtype=torch.uint8, device=DEV)
+    mask_d = torch.zeros((B, N, 1), dtype=torch.int32, device=DEV)
+    depth_d = torch.zeros((B, N), dtype=torch.int32, device=DEV)
+    nl_d = torch.zeros((B,), dtype=torch.int32, device=DEV)
+
+    def fresh_inputs(step):
+        par = np.zeros((B, N), np.int32)
+        for b in range(B):
+            par[b] = [-1] + [int(rng.integers(0, v)) for v in range(1, N)]
+        cnt = rng.integers(1, N + 1, size=B).astype(np.int32)
+        path = np.zeros((B, N), np.int32)
+        count = rng.integers(0, 6, size=B).astype(np.int32)
+        for b in range(B):
+            path[b, :count[b]] = np.sort(rng.choice(N, size=count[b], replace=False))
+        length = rng.integers(0, S - 6, size=B).astype(np.int32)
+        cache = rng.integers(0, 256, size=(planes, B, S, row), dtype=np.uint8)
+        return par, cnt, path, count, length, cache
+
+    def load(inputs):
+        par, cnt, path, count, length, cache = inputs
+        par_d.copy_(torch.from_numpy(par))
+        cnt_d.copy_(torch.from_numpy(cnt))
+        path_d.copy_(torch.from_numpy(path))
+        count_d.copy_(torch.from_numpy(count))
+        len_d.copy_(torch.from_numpy(length))
+        cache_d.copy_(torch.from_numpy(cache))
+
+    def check(inputs):
+        par, cnt, path, count, length, cache = inputs
+        want_m, want_d = oracle.tree_mask(par, cnt)
+        want_c, want_l = oracle.kv_commit(scratch_h, cache, path, count, length)
+        assert np.array_equal(mask_d.cpu().numpy().view(np.uint32), want_m)
+        assert np.array_equal(depth_d.cpu().numpy(), want_d)
+        assert np.array_equal(cache_d.cpu().numpy(), want_c)
+        assert np.array_equal(nl_d.cpu().numpy(), want_l)
+
+    case("graph capture: warm-up and capture")
+    first = fresh_inputs(0)
+    load(first)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):   # warm-up outside the capture, on the capture stream
+            sv.spec_tree_mask(par_d, cnt_d, mask=mask_d, depth=depth_d)
+            sv.spec_kv_commit(scratch_d, cache_d, count_d, len_d, path=path_d, new_len=nl_d)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        sv.spec_tree_mask(par_d, cnt_d, mask=mask_d, depth=depth_d)
+        sv.spec_kv_commit(scratch_d, cache_d, count_d, len_d, path=path_d, new_len=nl_d)
+    for rep in range(3):
+        case(f"graph capture: replay {rep}")
+        inputs = fresh_inputs(rep + 1)
+        load(inputs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(inputs)
+        # eager work between replays
+        sv.spec_tree_mask(par_d, cnt_d)
+        torch.cuda.synchronize()
