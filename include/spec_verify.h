@@ -35,6 +35,13 @@
  *    prior contents could hold a word that looks fresh (a small integer in
  *    its upper half), so an unzeroed workspace gives unspecified outputs.
  *    Calls that share a workspace must be ordered on one stream.
+ *  - Graph capture: every entry point can be recorded into a HIP graph.  A
+ *    call made while its stream is being captured also records a one-thread
+ *    kernel that advances a tag word kept in the first 256 bytes of its
+ *    workspace, and its workgroups read their tag from that word, so each
+ *    replay has a tag of its own (graph tags have bit 31 set; host tags never
+ *    do).  Eager calls and replays may share a workspace.  The tree mask and
+ *    the KV commit hand no words between workgroups and record one kernel.
  *  - Inputs that break a documented precondition (a drafted token outside
  *    [0, V), a uniform outside [0, 1), NaN or +inf logits, a row that is
  *    entirely -inf) give unspecified outputs but never an out-of-bounds

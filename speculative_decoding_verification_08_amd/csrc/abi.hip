@@ -48,7 +48,7 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
     p.chunk = first_pass_chunk(dtype);
     p.nchunk = (V + p.chunk - 1) / p.chunk;
     if (rows * p.nchunk > 0x7fffffffLL) return false;  // one-dimensional grid
-    size_t off = 0;
+    size_t off = kWorkspaceHeader;  // the graph tag word comes first
     p.off_partial = off;
     if (mode == SPEC_MODE_CHAIN) {
         off += align_up(static_cast<size_t>(rows) * p.nchunk * 16);
@@ -90,11 +90,28 @@ spec_status launch_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPE
 // never 0 (zeroed memory) or the phase entry points' tag.
 uint32_t next_call_tag() {
     static std::atomic<uint32_t> counter{0};
-    uint32_t t;
-    do {
-        t = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
-    } while (t <= kPhasedTag);
-    return t;
+    // [kPhasedTag + 1, kGraphTagBit): never 0, the phase tag or a graph tag.
+    return counter.fetch_add(1u, std::memory_order_relaxed) % (kGraphTagBit - kPhasedTag - 1u) +
+           kPhasedTag + 1u;
+}
+
+// The tag of one call.  While `stream` is being captured into a graph, the
+// call records a one-thread kernel that advances the tag word at the start of
+// the workspace, and its workgroups read their tag from that word, so every
+// replay has a tag of its own; otherwise the tag comes from the host counter.
+spec_status call_tag(void *ws, hipStream_t stream, uint32_t &tag, const uint32_t *&src) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return SPEC_ERR_LAUNCH;
+    if (cs == hipStreamCaptureStatusActive) {
+        uint32_t *word = static_cast<uint32_t *>(ws);
+        if (launch_advance_tag(word, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+        tag = 0;
+        src = word;
+    } else {
+        tag = next_call_tag();
+        src = nullptr;
+    }
+    return SPEC_OK;
 }
 
 // Shared validation of the chain entry points.
@@ -230,7 +247,8 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
     st = chain_sample_args(draft_tokens, u_accept, u_sample, B, K, out_tokens, out_accepted,
                            out_diag, a);
     if (st != SPEC_OK) return st;
-    a.tag = next_call_tag();
+    st = call_tag(workspace, stream, a.tag, a.tag_src);
+    if (st != SPEC_OK) return st;
     const int64_t per_seq = static_cast<int64_t>(2 * K + 1) * plan.nchunk + plan.nchunk2;
     if (static_cast<int64_t>(B) * per_seq <= 0x7fffffffLL) {
         a.lag = chain_lag(B, K, V, dtype, per_seq);
@@ -261,7 +279,8 @@ spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
     g.am.V = V;
     g.am.chunk = plan.chunk;
     g.am.nchunk = plan.nchunk;
-    g.am.tag = next_call_tag();
+    const spec_status st = call_tag(workspace, stream, g.am.tag, g.am.tag_src);
+    if (st != SPEC_OK) return st;
     g.am.partial = at<uint64_t>(workspace, plan.off_partial);
     g.tokens = draft_tokens;
     g.B = B;
@@ -305,7 +324,8 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
     t.am.V = V;
     t.am.chunk = plan.chunk;
     t.am.nchunk = plan.nchunk;
-    t.am.tag = next_call_tag();
+    const spec_status st = call_tag(workspace, stream, t.am.tag, t.am.tag_src);
+    if (st != SPEC_OK) return st;
     t.am.partial = at<uint64_t>(workspace, plan.off_partial);
     t.tokens = node_tokens;
     t.B = B;
@@ -338,7 +358,8 @@ spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtyp
     t.am.V = V;
     t.am.chunk = plan.chunk;
     t.am.nchunk = plan.nchunk;
-    t.am.tag = next_call_tag();
+    const spec_status st = call_tag(workspace, stream, t.am.tag, t.am.tag_src);
+    if (st != SPEC_OK) return st;
     t.am.partial = at<uint64_t>(workspace, plan.off_partial);
     t.tokens = node_tokens;
     t.parents = parents;
@@ -370,7 +391,8 @@ spec_status spec_draft_topk(const void *logits, spec_dtype dtype, int32_t rows, 
     a.chunk = plan.chunk;
     a.nchunk = plan.nchunk;
     a.k = k;
-    a.tag = next_call_tag();
+    const spec_status st = call_tag(workspace, stream, a.tag, a.tag_src);
+    if (st != SPEC_OK) return st;
     // A merge trails its rows' chunks by about one resident window of
     // workgroups (plus a group of rows), so its lists are usually complete
     // on arrival.  Units: groups of four rows, one merge workgroup each.

@@ -588,6 +588,7 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
 
 template <class DT, int U>
 __global__ __launch_bounds__(kWG) void k_chain_stats(ChainArgs a) {
+    if (a.tag_src) a.tag = *a.tag_src;  // a graph replay's tag
     // 32-bit index arithmetic (the grid is below 2^31 workgroups): a 64-bit
     // division is a long instruction sequence ahead of the first load.
     const uint32_t R = 2 * a.K + 1, S = R * a.nchunk;
@@ -597,6 +598,7 @@ __global__ __launch_bounds__(kWG) void k_chain_stats(ChainArgs a) {
 
 template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
+    if (a.tag_src) a.tag = *a.tag_src;  // a graph replay's tag
     const uint32_t nc = a.nchunk2, g = blockIdx.x, b = g / nc;
     __shared__ __align__(16) float lds[kDrawLds];
     draw_item<DT, VecOk, false>(a, static_cast<int>(b), static_cast<int>(g - b * nc), lds);
@@ -623,6 +625,7 @@ __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
 // bonus rows measured slower.)
 template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_chain_fused(ChainArgs a) {
+    if (a.tag_src) a.tag = *a.tag_src;  // a graph replay's tag
     __shared__ __align__(16) float lds[kDrawLds];
     const uint32_t nch = a.nchunk, S = (2 * a.K + 1) * nch, D = a.nchunk2, L = a.lag, B = a.B;
     const uint32_t g = blockIdx.x;

@@ -197,12 +197,12 @@ __device__ __forceinline__ bool merge_argmax(const uint64_t *part, int nrows, in
 // Sequence b of the greedy chain: a_k = argmax of target row k; j = the first
 // k < K with x_k != a_k (else K); emits x_0..x_{j-1}, a_j.  Wavefront 0 does
 // the test and the emission (lane k: position k).
-__device__ __forceinline__ void greedy_resolve_item(const GreedyArgs &a, int b) {
+__device__ __forceinline__ void greedy_resolve_item(const GreedyArgs &a, const ArgmaxArgs &am, int b) {
     __shared__ int32_t s_a[kMaxK + 1];
-    const int K = a.K, nch = a.am.nchunk, lane = threadIdx.x % kWave;
+    const int K = a.K, nch = am.nchunk, lane = threadIdx.x % kWave;
     const int32_t tok = K > 0 ? a.tokens[static_cast<int64_t>(b) * K + min(lane, K - 1)] : 0;
-    const uint64_t *part = a.am.partial + 2 * static_cast<int64_t>(b) * (K + 1) * nch;
-    const bool ok = merge_argmax(part, K + 1, nch, a.am.tag, s_a);
+    const uint64_t *part = am.partial + 2 * static_cast<int64_t>(b) * (K + 1) * nch;
+    const bool ok = merge_argmax(part, K + 1, nch, am.tag, s_a);
     if (threadIdx.x >= kWave) return;
     int32_t *ot = a.out_tokens + static_cast<int64_t>(b) * (K + 1);
     if (!ok) {
@@ -225,7 +225,7 @@ __device__ __forceinline__ void greedy_resolve_item(const GreedyArgs &a, int b) 
 // accepted iff it and all its ancestors match; the deepest accepted node wins
 // (lowest index among equals); emits the path's tokens, then that node's
 // argmax.
-__device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, int b) {
+__device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, const ArgmaxArgs &am, int b) {
     __shared__ int32_t s_a[kMaxTreeNodes];
     __shared__ int s_ok[kMaxTreeNodes];
     __shared__ int s_anc[kMaxTreeNodes];
@@ -233,10 +233,10 @@ __device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, int b) {
     __shared__ int s_path[kMaxTreeNodes];
     static_assert(kMaxTreeNodes == kWG, "one thread per node");
     const int v = threadIdx.x;
-    const int N = a.tree.N, D = a.tree.D, nch = a.am.nchunk;
+    const int N = a.tree.N, D = a.tree.D, nch = am.nchunk;
     const int32_t tok = v < N ? a.tokens[static_cast<int64_t>(b) * N + v] : 0;
-    const uint64_t *part = a.am.partial + 2 * static_cast<int64_t>(b) * N * nch;
-    if (!merge_argmax(part, N, nch, a.am.tag, s_a)) {
+    const uint64_t *part = am.partial + 2 * static_cast<int64_t>(b) * N * nch;
+    if (!merge_argmax(part, N, nch, am.tag, s_a)) {
         if (v <= D) {
             a.out_tokens[static_cast<int64_t>(b) * (D + 1) + v] = -1;
             if (a.out_path) a.out_path[static_cast<int64_t>(b) * (D + 1) + v] = -1;
@@ -302,21 +302,21 @@ __device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, int b) {
 // tree.  A node whose parent entry is out of range is unattached: neither it
 // nor its subtree is accepted, and nothing outside the tree is read.  Depths
 // and acceptance are both folded by pointer jumping, ceil(log2 n) steps.
-__device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, int b) {
+__device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, const ArgmaxArgs &am, int b) {
     __shared__ int32_t s_a[kMaxTreeNodes];
     __shared__ int s_ok[kMaxTreeNodes], s_anc[kMaxTreeNodes], s_dep[kMaxTreeNodes];
     __shared__ int s_par[kMaxTreeNodes], s_path[kMaxTreeNodes];
     __shared__ int s_best;
     static_assert(kMaxTreeNodes == kWG, "one thread per node");
-    const int v = threadIdx.x, Nmax = a.Nmax, nch = a.am.nchunk;
+    const int v = threadIdx.x, Nmax = a.Nmax, nch = am.nchunk;
     const int64_t row0 = static_cast<int64_t>(b) * Nmax;
     const int n = min(max(a.node_count[b], 1), Nmax);
     const int32_t tok = v < n ? a.tokens[row0 + v] : 0;
     int par = v < n ? a.parents[row0 + v] : -1;
     const bool valid = v > 0 && v < n && par >= 0 && par < v;
     if (!valid) par = -1;
-    const uint64_t *part = a.am.partial + 2 * row0 * nch;
-    if (!merge_argmax(part, n, nch, a.am.tag, s_a)) {
+    const uint64_t *part = am.partial + 2 * row0 * nch;
+    if (!merge_argmax(part, n, nch, am.tag, s_a)) {
         if (v < Nmax) {
             a.out_tokens[row0 + v] = -1;
             if (a.out_path) a.out_path[row0 + v] = -1;
@@ -377,36 +377,48 @@ __device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, int 
 
 template <class DT>
 __global__ __launch_bounds__(kWG) void k_tree_dyn(TreeDynArgs a) {
+    // The argument block stays untouched (writing into it would copy it to
+    // scratch); the argmax arguments with the call's tag are a local copy.
+    ArgmaxArgs am = a.am;
+    if (am.tag_src) am.tag = *am.tag_src;  // a graph replay's tag
     const uint32_t nam = static_cast<uint32_t>(a.am.rows) * a.am.nchunk, g = blockIdx.x;
     if (g < nam) {
         const uint32_t row = g / a.am.nchunk, b = row / a.Nmax, v = row - b * a.Nmax;
         // Rows past the tree's node count are padding: not read.
         if (v >= static_cast<uint32_t>(min(max(a.node_count[b], 1), a.Nmax))) return;
-        argmax_item<DT, 4>(a.am, row, static_cast<int>(g - row * a.am.nchunk));
+        argmax_item<DT, 4>(am, row, static_cast<int>(g - row * a.am.nchunk));
     } else {
-        tree_dyn_resolve_item(a, static_cast<int>(g - nam));
+        tree_dyn_resolve_item(a, am, static_cast<int>(g - nam));
     }
 }
 
 template <class DT>
 __global__ __launch_bounds__(kWG) void k_greedy(GreedyArgs a) {
+    // The argument block stays untouched (writing into it would copy it to
+    // scratch); the argmax arguments with the call's tag are a local copy.
+    ArgmaxArgs am = a.am;
+    if (am.tag_src) am.tag = *am.tag_src;  // a graph replay's tag
     const uint32_t nam = static_cast<uint32_t>(a.am.rows) * a.am.nchunk, g = blockIdx.x;
     if (g < nam) {
         const uint32_t row = g / a.am.nchunk;
-        argmax_item<DT, 4>(a.am, row, static_cast<int>(g - row * a.am.nchunk));
+        argmax_item<DT, 4>(am, row, static_cast<int>(g - row * a.am.nchunk));
     } else {
-        greedy_resolve_item(a, static_cast<int>(g - nam));
+        greedy_resolve_item(a, am, static_cast<int>(g - nam));
     }
 }
 
 template <class DT>
 __global__ __launch_bounds__(kWG) void k_tree(TreeArgs a) {
+    // The argument block stays untouched (writing into it would copy it to
+    // scratch); the argmax arguments with the call's tag are a local copy.
+    ArgmaxArgs am = a.am;
+    if (am.tag_src) am.tag = *am.tag_src;  // a graph replay's tag
     const uint32_t nam = static_cast<uint32_t>(a.am.rows) * a.am.nchunk, g = blockIdx.x;
     if (g < nam) {
         const uint32_t row = g / a.am.nchunk;
-        argmax_item<DT, 4>(a.am, row, static_cast<int>(g - row * a.am.nchunk));
+        argmax_item<DT, 4>(am, row, static_cast<int>(g - row * a.am.nchunk));
     } else {
-        tree_resolve_item(a, static_cast<int>(g - nam));
+        tree_resolve_item(a, am, static_cast<int>(g - nam));
     }
 }
 

@@ -44,6 +44,10 @@ struct Plan {
 // call's, so words left by earlier calls (of any shape) are never taken for
 // fresh ones.
 constexpr uint32_t kPhasedTag = 1;  // tag of the phase entry points; whole calls use >= 2
+// Tags of calls recorded into a graph have bit 31 set: each replay's tag is
+// advanced on the device (launch_advance_tag), in a range host tags never use.
+constexpr uint32_t kGraphTagBit = 0x80000000u;
+constexpr size_t kWorkspaceHeader = 256;  // bytes at the start of every workspace: the graph tag word
 
 // Chain verify, both kernels.
 struct ChainArgs {
@@ -55,6 +59,7 @@ struct ChainArgs {
     int32_t B, K, V;
     float c;                 // log2(e) / T
     uint32_t tag;            // this call's tag (upper half of every handed-over word)
+    const uint32_t *tag_src; // nullable: read the tag from this device word instead (graph replays)
     int32_t chunk, nchunk, nchunk2;  // chunk2 = kChunk2Bytes / element size
     int32_t lag;             // one-launch form: sequences between a sequence's statistics and its draw
     uint64_t *partial;       // [B][2K+1][nchunk][2] tagged (ref, z); rows 0..K target, K+1.. draft
@@ -70,6 +75,7 @@ struct ArgmaxArgs {
     int64_t rows;
     int32_t V, chunk, nchunk;
     uint32_t tag;            // this call's tag (upper half of every handed-over word)
+    const uint32_t *tag_src; // nullable: read the tag from this device word instead (graph replays)
     uint64_t *partial;       // [rows][nchunk][2] tagged (value bits, index)
 };
 
@@ -123,5 +129,6 @@ hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s);
 hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t s);
 hipError_t launch_tree(const TreeArgs &a, int dtype, hipStream_t s);
 hipError_t launch_tree_dyn(const TreeDynArgs &a, int dtype, hipStream_t s);
+hipError_t launch_advance_tag(uint32_t *word, hipStream_t s);
 
 }  // namespace sv

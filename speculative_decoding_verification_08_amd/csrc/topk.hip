@@ -369,6 +369,7 @@ __device__ __forceinline__ void topk_chunk(const TopkArgs &a, int64_t row, int c
 // on.
 template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_topk(TopkArgs a) {
+    if (a.tag_src) a.tag = *a.tag_src;  // a graph replay's tag
     const int64_t nch = a.nchunk, L = a.lag, g = blockIdx.x, R = a.rows;
     const int64_t G = (R + kWaves - 1) / kWaves;
     auto group_chunks = [&](int64_t q) { return (min(R, (q + 1) * kWaves) - q * kWaves) * nch; };

@@ -18,6 +18,7 @@ struct TopkArgs {
     int32_t V, chunk, nchunk, k;
     int64_t lag;             // groups of four rows between a group's chunks and its merge, 1 <= lag <= groups
     uint32_t tag;
+    const uint32_t *tag_src; // nullable: read the tag from this device word instead (graph replays)
     uint64_t *partial;       // [rows][nchunk][kMaxTopK][2] tagged (value bits, index)
     int32_t *out_idx;        // [rows][k]
     float *out_val;          // nullable [rows][k]

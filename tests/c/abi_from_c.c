@@ -27,7 +27,7 @@ int main(void)
                n > 0 && n % 256 == 0,
            "chain workspace size");
     expect(spec_verify_workspace_bytes(SPEC_MODE_TOPK, 512, 8, 128256, SPEC_DTYPE_BF16, &n) == SPEC_OK &&
-               n == 512u * 16u * 128u,
+               n == 256u + 512u * 16u * 128u,
            "top-k workspace size");
     expect(spec_verify_workspace_bytes(SPEC_MODE_TOPK, 2, 9, 100, SPEC_DTYPE_F32, &n) == SPEC_ERR_INVALID_ARG,
            "top-k k > 8 rejected");

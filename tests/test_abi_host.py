@@ -108,8 +108,8 @@ def test_topk_argument_errors():
     ws = sv.spec_verify_workspace_bytes
     E, BF, F32 = sv.SPEC_ERR_INVALID_ARG, sv.SPEC_DTYPE_BF16, sv.SPEC_DTYPE_F32
     # 16 KB chunks, 8 slots of two 8-byte words each per (row, chunk)
-    assert ws(sv.SPEC_MODE_TOPK, 512, 8, 128256, BF) == 512 * 16 * 128
-    assert ws(sv.SPEC_MODE_TOPK, 3, 1, 5000, F32) == 3 * 2 * 128
+    assert ws(sv.SPEC_MODE_TOPK, 512, 8, 128256, BF) == 256 + 512 * 16 * 128  # header + lists
+    assert ws(sv.SPEC_MODE_TOPK, 3, 1, 5000, F32) == 256 + 3 * 2 * 128
     for V, dt in ((sv.TOPK_MAX_V, BF), (sv.TOPK_MAX_V, F32)):
         assert ws(sv.SPEC_MODE_TOPK, 2, sv.TOPK_MAX_K, V, dt) > 0
     for rows, k, V in ((-1, 4, 100), (2, 0, 100), (2, 9, 100), (2, 5, 4),

@@ -878,3 +878,95 @@ def test_graph_capture_mask_and_kv_commit(sv):
         # eager work between replays
         sv.spec_tree_mask(par_d, cnt_d)
         torch.cuda.synchronize()
+
+
+def test_graph_capture_tagged_entry_points(sv):
+    """Chain verify, greedy verify, per-sequence tree verify and top-k captured
+    into one HIP graph: each replay records its own tag (a one-thread kernel
+    advances the workspace's tag word), so three replays with new inputs, with
+    eager calls on the same workspaces in between, all match the oracle."""
+    rng = np.random.default_rng(91)
+    B, K, V = 5, 4, 9000
+    wc = W.Workload("gc", 97, "chain", B=B, K=K, V=V, dtype="bf16", T=1.0, recipe="peaked", sigma=0.6)
+    wg = W.WORKLOADS["greedy_32k"].with_sizes(B=B, K=K, V=V)
+    wt = W.Workload("gt", 98, "tree_dyn", B=B, K=16, V=V, dtype="bf16", recipe="peaked")
+    wk = W.Workload("gk", 99, "topk", B=12, V=V, dtype="bf16", K=8, recipe="peaked", sigma=0.6)
+
+    def gen(step):
+        return (W.chain_inputs(wc, step), W.greedy_inputs(wg, step),
+                W.tree_dyn_inputs(wt, step, p_match=0.85, nmin=1), W.topk_inputs(wk, step)["logits"])
+
+    c0, g0, t0, k0 = gen(0)
+    # captured inputs (device, rewritten in place before each replay)
+    ci = {k: dev(c0[k]) for k in ("target", "draft", "tokens", "u_accept", "u_sample")}
+    gi = {k: dev(g0[k]) for k in ("target", "tokens")}
+    ti = {k: dev(t0[k]) for k in ("node_logits", "node_tokens", "parents", "node_count")}
+    ki = dev(k0)
+    ws_c = sv.workspace(sv.SPEC_MODE_CHAIN, B, K, V, sv.SPEC_DTYPE_BF16, DEV)
+    ws_g = sv.workspace(sv.SPEC_MODE_GREEDY, B, K, V, sv.SPEC_DTYPE_BF16, DEV)
+    ws_t = sv.workspace(sv.SPEC_MODE_TREE_DYN, B, 16, V, sv.SPEC_DTYPE_BF16, DEV)
+    ws_k = sv.workspace(sv.SPEC_MODE_TOPK, 12, 8, V, sv.SPEC_DTYPE_BF16, DEV)
+    oc = (torch.empty((B, K + 1), dtype=torch.int32, device=DEV), torch.empty(B, dtype=torch.int32, device=DEV),
+          torch.empty((B, K + 1, 4), dtype=torch.float32, device=DEV))
+    og = (torch.empty((B, K + 1), dtype=torch.int32, device=DEV), torch.empty(B, dtype=torch.int32, device=DEV))
+    ot = (torch.empty((B, 16), dtype=torch.int32, device=DEV), torch.empty((B, 16), dtype=torch.int32, device=DEV),
+          torch.empty(B, dtype=torch.int32, device=DEV))
+    ok_ = (torch.empty((12, 8), dtype=torch.int32, device=DEV), torch.empty((12, 8), dtype=torch.float32, device=DEV))
+
+    def step(stream=None):
+        sv.spec_verify_chain(ci["target"], ci["draft"], ci["tokens"], ci["u_accept"], ci["u_sample"], 1.0,
+                             out_tokens=oc[0], out_accepted=oc[1], out_diag=oc[2], workspace_buf=ws_c,
+                             stream=stream)
+        sv.spec_verify_greedy(gi["target"], gi["tokens"], out_tokens=og[0], out_accepted=og[1],
+                              workspace_buf=ws_g, stream=stream)
+        sv.spec_verify_tree_greedy_dyn(ti["node_logits"], ti["node_tokens"], ti["parents"], ti["node_count"],
+                                       out_tokens=ot[0], out_path=ot[1], out_depth=ot[2], workspace_buf=ws_t,
+                                       stream=stream)
+        sv.spec_draft_topk(ki, 8, out_idx=ok_[0], out_val=ok_[1], workspace_buf=ws_k, stream=stream)
+
+    def load(inputs):
+        c, g, t, k = inputs
+        for name in ci:
+            src = c[name]
+            src_t = torch.from_numpy(np.ascontiguousarray(src).view(np.int16)).view(torch.bfloat16) \
+                if src.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(src))
+            ci[name].copy_(src_t)
+        gi["target"].copy_(torch.from_numpy(g["target"].view(np.int16)).view(torch.bfloat16))
+        gi["tokens"].copy_(torch.from_numpy(g["tokens"]))
+        ti["node_logits"].copy_(torch.from_numpy(t["node_logits"].view(np.int16)).view(torch.bfloat16))
+        for name in ("node_tokens", "parents", "node_count"):
+            ti[name].copy_(torch.from_numpy(t[name]))
+        ki.copy_(torch.from_numpy(k.view(np.int16)).view(torch.bfloat16))
+
+    def check(inputs):
+        c, g, t, k = inputs
+        parity.check_chain(c, oc[0].cpu().numpy(), oc[1].cpu().numpy(), oc[2].cpu().numpy())
+        parity.check_greedy(g, og[0].cpu().numpy(), og[1].cpu().numpy())
+        parity.check_tree_dyn(t, *[o.cpu().numpy() for o in ot])
+        parity.check_topk({"logits": k}, ok_[0].cpu().numpy(), ok_[1].cpu().numpy())
+
+    case("graph capture of tagged entry points: warm-up and capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    check((c0, g0, t0, k0))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        case(f"graph capture of tagged entry points: replay {rep}")
+        inputs = gen(rep + 1)
+        load(inputs)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        check(inputs)
+        # an eager call on the same workspaces between replays (host tags)
+        inputs = gen(rep + 10)
+        load(inputs)
+        step()
+        torch.cuda.synchronize()
+        check(inputs)
