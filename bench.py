@@ -208,6 +208,49 @@ def host_cpu() -> dict:
     return {"cpu": model, "threads_available": os.cpu_count()}
 
 
+def graph_replay(make, sets, stream, G: int, steps: int) -> dict:
+    """Per-step time of G consecutive steps (input sets in turn) captured in
+    one HIP graph and replayed back to back: what a serving loop that records
+    its steps pays, without the per-launch host cost.  The last captured
+    step's outputs are checked, bit for bit, against an eager call on the same
+    input set."""
+    import torch
+    cap = torch.cuda.Stream()
+    prepared = [make(s, cap) for s in sets]   # launches bound to the capture stream
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):               # one eager pass on the capture stream first
+        for p in prepared:
+            p[0]()
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for i in range(G):
+            prepared[i % len(sets)][0]()
+    reps = max(1, -(-steps // G))
+    with torch.cuda.stream(stream):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * G)
+    last = prepared[(G - 1) % len(sets)]
+    replayed = [o.clone() for o in last[1]]
+    with torch.cuda.stream(cap):
+        last[0]()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(replayed, last[1]))
+    if not same:
+        raise SystemExit("bench.py: a replayed graph's outputs differ from an eager call's")
+    print(f"[bench] graph of {G} steps: {us:.2f} us/step over {reps} replays", file=sys.stderr, flush=True)
+    return {"steps_per_graph": G, "replays": reps, "us_per_step": us, "steps_per_s": 1e6 / us,
+            "outputs_equal_eager": same}
+
+
 def main():
     import workloads as W
     ap = argparse.ArgumentParser()
@@ -219,6 +262,9 @@ def main():
                     help="input sets cycled through (default: enough to exceed 512 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph-steps", type=int, default=20,
+                    help="also time this many consecutive steps captured in one HIP graph and "
+                         "replayed (0: skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run device-to-device copies of this many MB (to scale HBM "
                          "traffic counters against a copy of known size)")
@@ -267,12 +313,9 @@ def main():
         out_t = torch.empty((B, K + 1), dtype=torch.int32, device=device)
         out_a = torch.empty((B,), dtype=torch.int32, device=device)
 
-        launches = [sv.prepare_chain(s["target"], s["draft"], s["tokens"], s["u_accept"],
-                                     s["u_sample"], w.T, out_t, out_a, ws, stream=stream)
-                    for s in sets]
-
-        def step(i):
-            launches[i % nsets]()
+        def make(s, st):
+            return (sv.prepare_chain(s["target"], s["draft"], s["tokens"], s["u_accept"],
+                                     s["u_sample"], w.T, out_t, out_a, ws, stream=st), (out_t, out_a))
 
         def stats_phase(i):
             s = sets[i % nsets]
@@ -295,12 +338,9 @@ def main():
         out_t = torch.empty((B, K + 1), dtype=torch.int32, device=device)
         out_a = torch.empty((B,), dtype=torch.int32, device=device)
 
-        launches = [sv.spec_verify_greedy(s["target"], s["tokens"], out_tokens=out_t,
-                                          out_accepted=out_a, workspace_buf=ws, stream=stream,
-                                          prepare=True)[0] for s in sets]
-
-        def step(i):
-            launches[i % nsets]()
+        def make(s, st):
+            return sv.spec_verify_greedy(s["target"], s["tokens"], out_tokens=out_t, out_accepted=out_a,
+                                         workspace_buf=ws, stream=st, prepare=True)
         stats_phase = None
 
         def outputs():
@@ -317,13 +357,11 @@ def main():
         out_p = torch.empty((B, Nmax), dtype=torch.int32, device=device)
         out_d = torch.empty((B,), dtype=torch.int32, device=device)
 
-        launches = [sv.spec_verify_tree_greedy_dyn(s["node_logits"], s["node_tokens"], s["parents"],
-                                                   s["node_count"], out_tokens=out_t, out_path=out_p,
-                                                   out_depth=out_d, workspace_buf=ws, stream=stream,
-                                                   prepare=True)[0] for s in sets]
-
-        def step(i):
-            launches[i % nsets]()
+        def make(s, st):
+            return sv.spec_verify_tree_greedy_dyn(s["node_logits"], s["node_tokens"], s["parents"],
+                                                  s["node_count"], out_tokens=out_t, out_path=out_p,
+                                                  out_depth=out_d, workspace_buf=ws, stream=st,
+                                                  prepare=True)
         stats_phase = None
 
         def outputs():
@@ -339,12 +377,10 @@ def main():
         scratch = to_dev(kv_scratch_host(w), device)
         cache = kv_cache_pattern(w, device)
         new_len = torch.empty((B,), dtype=torch.int32, device=device)
-        launches = [sv.spec_kv_commit(scratch, cache, s["count"], s["cache_len"], path=s["path"],
-                                      new_len=new_len, stream=stream, prepare=True)[0]
-                    for s in sets]
-
-        def step(i):
-            launches[i % nsets]()
+        def make(s, st):
+            launch, nl = sv.spec_kv_commit(scratch, cache, s["count"], s["cache_len"], path=s["path"],
+                                           new_len=new_len, stream=st, prepare=True)
+            return launch, (nl, cache[0, 0])
         stats_phase = None
 
         def outputs():
@@ -357,11 +393,8 @@ def main():
         io_bytes = 4 * B * (w.K + 3)
         verified = 0
     elif w.mode == "mask":
-        launches = [sv.spec_tree_mask(s["parents"], s["node_count"], stream=stream, prepare=True)[0]
-                    for s in sets]
-
-        def step(i):
-            launches[i % nsets]()
+        def make(s, st):
+            return sv.spec_tree_mask(s["parents"], s["node_count"], stream=st, prepare=True)
         stats_phase = None
 
         def outputs():
@@ -377,11 +410,9 @@ def main():
         out_i = torch.empty((B, k), dtype=torch.int32, device=device)
         out_v = torch.empty((B, k), dtype=torch.float32, device=device)
 
-        launches = [sv.spec_draft_topk(s["logits"], k, out_idx=out_i, out_val=out_v, workspace_buf=ws,
-                                       stream=stream, prepare=True)[0] for s in sets]
-
-        def step(i):
-            launches[i % nsets]()
+        def make(s, st):
+            return sv.spec_draft_topk(s["logits"], k, out_idx=out_i, out_val=out_v, workspace_buf=ws,
+                                      stream=st, prepare=True)
         stats_phase = None
 
         def outputs():
@@ -400,13 +431,10 @@ def main():
         out_p = torch.empty((B, D + 1), dtype=torch.int32, device=device)
         out_d = torch.empty((B,), dtype=torch.int32, device=device)
 
-        launches = [sv.spec_verify_tree_greedy(s["node_logits"], s["node_tokens"], par,
-                                               out_tokens=out_t, out_path=out_p, out_depth=out_d,
-                                               workspace_buf=ws, stream=stream, prepare=True)[0]
-                    for s in sets]
-
-        def step(i):
-            launches[i % nsets]()
+        def make(s, st):
+            return sv.spec_verify_tree_greedy(s["node_logits"], s["node_tokens"], par, out_tokens=out_t,
+                                              out_path=out_p, out_depth=out_d, workspace_buf=ws,
+                                              stream=st, prepare=True)
         stats_phase = None
 
         def outputs():
@@ -417,6 +445,11 @@ def main():
         dominant_name = "k_tree (whole step)"
         io_bytes = 4 * B * N + 4 * B * (2 * D + 3)
         verified = B * (N - 1)
+
+    launches = [make(s, stream)[0] for s in sets]
+
+    def step(i):
+        launches[i % nsets]()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -449,6 +482,8 @@ def main():
     print(f"[bench] {ms_step * 1e3:.2f} us/step"
           + (f", statistics pass alone {ms_stats * 1e3:.2f} us" if ms_stats else ""),
           file=sys.stderr, flush=True)
+
+    graph = graph_replay(make, sets, stream, args.graph_steps, args.steps) if args.graph_steps else None
 
     step(0)
     gpu_out = outputs()
@@ -525,6 +560,8 @@ def main():
             "kernel": "k_chain_stats", "avg_launch_us": ms_stats * 1e3,
             "achieved": nbytes / (ms_stats * 1e-3) / 1e9, "unit": "GB/s",
             "frac": nbytes / (ms_stats * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    if graph is not None:
+        line["graph_replay"] = graph
     if not args.no_cpu_baseline:
         print("[bench] oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, host_sets[0], args.cpu_seconds, gpu_out)
