@@ -375,21 +375,87 @@ __device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, cons
     if (v == 0) a.out_depth[b] = d;
 }
 
+// Batches of at most kCompactTrees trees use the compact order: every
+// workgroup reads all node counts, so the argmax items cover the real rows
+// only, tree by tree, the resolve items follow them at once, and the
+// workgroups left over (one per padding chunk) return at the end of the grid.
+// Larger batches keep one item per (tree, row slot, chunk) and skip padding
+// rows where they fall.
+constexpr int kCountsPerLane = 4, kCompactTrees = kWave * kCountsPerLane;
+
+// Compact order with lane l holding the clamped node counts of trees
+// P l .. P l + P - 1 (0 past B): returns T, the batch's real rows, and for
+// R < T the tree b and node v of real row R (the first lane whose running
+// total passes R, then one of that lane's trees).
+template <int P>
+__device__ __forceinline__ uint32_t locate_row(const TreeDynArgs &a, uint32_t R, uint32_t &b, uint32_t &v) {
+    const int lane = threadIdx.x % kWave, B = a.B, Nmax = a.Nmax;
+    int n[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        const int t = lane * P + j;
+        const int c = a.node_count[min(t, B - 1)];
+        n[j] = t < B ? min(max(c, 1), Nmax) : 0;
+    }
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) s += n[j];
+    const int incl = wave_incl_sum_i(s);
+    const uint32_t T = static_cast<uint32_t>(wave_last_i(incl));
+    if (R < T) {
+        const uint64_t hit = __ballot(static_cast<uint32_t>(incl) > R);
+        const int L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        uint32_t r = R - static_cast<uint32_t>(__builtin_amdgcn_readlane(incl - s, L));
+        uint32_t t = static_cast<uint32_t>(L) * P;
+#pragma unroll
+        for (int j = 0; j < P - 1; ++j) {
+            const uint32_t m = static_cast<uint32_t>(__builtin_amdgcn_readlane(n[j], L));
+            if (r < m) break;
+            r -= m;
+            ++t;
+        }
+        b = t;
+        v = r;
+    }
+    return T;
+}
+
 template <class DT>
 __global__ __launch_bounds__(kWG) void k_tree_dyn(TreeDynArgs a) {
     // The argument block stays untouched (writing into it would copy it to
     // scratch); the argmax arguments with the call's tag are a local copy.
     ArgmaxArgs am = a.am;
     if (am.tag_src) am.tag = *am.tag_src;  // a graph replay's tag
-    const uint32_t nam = static_cast<uint32_t>(a.am.rows) * a.am.nchunk, g = blockIdx.x;
-    if (g < nam) {
-        const uint32_t row = g / a.am.nchunk, b = row / a.Nmax, v = row - b * a.Nmax;
-        // Rows past the tree's node count are padding: not read.
-        if (v >= static_cast<uint32_t>(min(max(a.node_count[b], 1), a.Nmax))) return;
-        argmax_item<DT, 4>(am, row, static_cast<int>(g - row * a.am.nchunk));
+    const uint32_t nch = a.am.nchunk, g = blockIdx.x, B = static_cast<uint32_t>(a.B);
+    // This workgroup's item: an argmax item (row, ch), the resolve of tree
+    // `row`, or nothing.
+    uint32_t row = 0, ch = 0;
+    bool argmax = false, resolve = false;
+    if (B <= static_cast<uint32_t>(kCompactTrees)) {
+        const uint32_t R = g / nch;
+        uint32_t b = 0, v = 0;
+        const uint32_t T = B <= static_cast<uint32_t>(kWave) ? locate_row<1>(a, R, b, v)
+                                                             : locate_row<kCountsPerLane>(a, R, b, v);
+        const uint32_t nam = T * nch;
+        argmax = g < nam;
+        resolve = !argmax && g < nam + B;
+        row = argmax ? b * static_cast<uint32_t>(a.Nmax) + v : g - nam;
+        ch = g - R * nch;
     } else {
-        tree_dyn_resolve_item(a, am, static_cast<int>(g - nam));
+        const uint32_t nam = static_cast<uint32_t>(a.am.rows) * nch;
+        if (g < nam) {
+            const uint32_t slot = g / nch, b = slot / a.Nmax, v = slot - b * a.Nmax;
+            // Rows past the tree's node count are padding: not read.
+            argmax = v < static_cast<uint32_t>(min(max(a.node_count[b], 1), a.Nmax));
+            row = slot;
+            ch = g - slot * nch;
+        } else {
+            resolve = true;
+            row = g - nam;
+        }
     }
+    if (argmax) argmax_item<DT, 4>(am, row, static_cast<int>(ch));
+    else if (resolve) tree_dyn_resolve_item(a, am, static_cast<int>(row));
 }
 
 template <class DT>

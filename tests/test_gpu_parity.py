@@ -358,6 +358,30 @@ def test_tree_dyn_random_shapes(sv):
         parity.check_tree_dyn(d, *run_tree_dyn(sv, d))
 
 
+def test_tree_dyn_batch_sizes_around_the_compact_limit(sv):
+    """Batches of up to 256 trees take the compact item order (argmax items on
+    real rows only), larger ones one item per row slot: both sides of the
+    limit, with some counts out of range (clamped to [1, Nmax])."""
+    for i, B in enumerate([1, 64, 255, 256, 257, 300]):
+        Nmax = [3, 9, 5, 12, 7, 4][i]
+        dtype = "bf16" if i % 2 else "f32"
+        w = W.Workload("td", 97, "tree_dyn", B=B, K=Nmax, V=[300, 2053][i % 2], dtype=dtype, recipe="peaked")
+        d = W.tree_dyn_inputs(w, i, p_match=0.85, nmin=1)
+        cnt = d["node_count"].copy()
+        cnt[::7] = 0
+        cnt[3::11] = Nmax + 5
+        cnt[5::13] = -4
+        case(f"per-sequence trees B={B} Nmax={Nmax} {dtype}")
+        g = sv.spec_verify_tree_greedy_dyn(dev(d["node_logits"]), dev(d["node_tokens"]), dev(d["parents"]),
+                                           dev(cnt))
+        torch.cuda.synchronize()
+        g = [x.cpu().numpy() for x in g]
+        o = oracle.verify_tree_greedy_dyn(d["node_logits"], d["node_tokens"], d["parents"],
+                                          np.clip(cnt, 1, Nmax).astype(np.int32))
+        for x, y in zip(g, o):
+            assert np.array_equal(x, y)
+
+
 def test_tree_dyn_shared_tree_equals_static(sv):
     """Every sequence with the same full tree: the static entry point's result."""
     w = W.Workload("t", 95, "tree", B=7, V=5003, dtype="bf16", recipe="peaked",
