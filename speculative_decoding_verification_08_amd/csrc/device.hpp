@@ -240,16 +240,6 @@ __device__ __forceinline__ float wave_incl_sum(float x) {
     x += dpp::mov_f<dpp::kRowBcast31, 0xC>(0.f, x);
     return x;
 }
-// The same over integers (exact whatever the order).
-__device__ __forceinline__ int wave_incl_sum_i(int x) {
-    x += dpp::mov_i<dpp::kRowShr1>(0, x);
-    x += dpp::mov_i<dpp::kRowShr2>(0, x);
-    x += dpp::mov_i<dpp::kRowShr4>(0, x);
-    x += dpp::mov_i<dpp::kRowShr8>(0, x);
-    x += dpp::mov_i<dpp::kRowBcast15, 0xA>(0, x);
-    x += dpp::mov_i<dpp::kRowBcast31, 0xC>(0, x);
-    return x;
-}
 // Value of lane 63 (uniform).
 __device__ __forceinline__ float wave_last(float x) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));

@@ -383,6 +383,18 @@ __device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, cons
 // rows where they fall.
 constexpr int kCountsPerLane = 4, kCompactTrees = kWave * kCountsPerLane;
 
+// Inclusive integer sum over lanes 0..lane of a wavefront (DPP, as the
+// float scan: within rows of 16, then the rows' totals carried upward).
+__device__ __forceinline__ int wave_incl_sum_i(int x) {
+    x += dpp::mov_i<dpp::kRowShr1>(0, x);
+    x += dpp::mov_i<dpp::kRowShr2>(0, x);
+    x += dpp::mov_i<dpp::kRowShr4>(0, x);
+    x += dpp::mov_i<dpp::kRowShr8>(0, x);
+    x += dpp::mov_i<dpp::kRowBcast15, 0xA>(0, x);
+    x += dpp::mov_i<dpp::kRowBcast31, 0xC>(0, x);
+    return x;
+}
+
 // Compact order with lane l holding the clamped node counts of trees
 // P l .. P l + P - 1 (0 past B): returns T, the batch's real rows, and for
 // R < T the tree b and node v of real row R (the first lane whose running
