@@ -49,6 +49,10 @@ __device__ __forceinline__ void argmax_item(const ArgmaxArgs &a, int64_t row, in
         uint4 raw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) raw[u] = vp[v + u * kWG];
+        // Every load in flight before the first wait: left to itself the
+        // scheduler starts on the first vector before issuing the last two,
+        // which then leave one memory round trip later.
+        __builtin_amdgcn_sched_barrier(0);
         float x[U * VEC];
 #pragma unroll
         for (int u = 0; u < U; ++u) unpack<DT>(raw[u], x + u * VEC);
