@@ -256,7 +256,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: enough for about "
+                         "0.3 s, at least 100, so that clocks have settled)")
     ap.add_argument("--workload", default="chain_t1_128k", choices=sorted(W.WORKLOADS))
     ap.add_argument("--rotate", type=int, default=0,
                     help="input sets cycled through (default: enough to exceed 512 MB)")
@@ -451,8 +453,23 @@ def main():
     def step(i):
         launches[i % nsets]()
 
+    done = 0
+    if args.warmup is None:
+        # The clocks ramp up over about a tenth of a second of load: size the
+        # warm-up from a short trial (counted in it; its first steps carry
+        # one-time costs, so only the second half is timed) so that the timed
+        # steps run settled.
+        for done in range(1, 21):
+            step(done - 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for done in range(21, 41):
+            step(done - 1)
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t0) / 20
+        args.warmup = max(100, int(0.3 / max(per, 1e-7)))
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
+    for i in range(done, args.warmup):
         step(i)
     torch.cuda.synchronize()
 
