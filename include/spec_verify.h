@@ -40,8 +40,10 @@
  *    kernel that advances a tag word kept in the first 256 bytes of its
  *    workspace, and its workgroups read their tag from that word, so each
  *    replay has a tag of its own (graph tags have bit 31 set; host tags never
- *    do).  Eager calls and replays may share a workspace.  The tree mask and
- *    the KV commit hand no words between workgroups and record one kernel.
+ *    do).  Eager calls and replays may share a workspace.  The extra kernel
+ *    is one more kernel boundary per recorded call (about 1-2 us on MI355X).
+ *    The tree mask and the KV commit hand no words between workgroups and
+ *    record one kernel.
  *  - Inputs that break a documented precondition (a drafted token outside
  *    [0, V), a uniform outside [0, 1), NaN or +inf logits, a row that is
  *    entirely -inf) give unspecified outputs but never an out-of-bounds
