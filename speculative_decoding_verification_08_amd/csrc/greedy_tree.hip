@@ -409,9 +409,12 @@ __device__ __forceinline__ uint32_t locate_row(const TreeDynArgs &a, uint32_t R,
     int n[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) {
+        // Every lane loads (a clamped, in-range address) and masks afterwards:
+        // a select on t < B lets the compiler sink each load into a branch of
+        // its own, and the loads then leave one after another.
         const int t = lane * P + j;
         const int c = a.node_count[min(t, B - 1)];
-        n[j] = t < B ? min(max(c, 1), Nmax) : 0;
+        n[j] = min(max(c, 1), Nmax) & -static_cast<int>(t < B);
     }
     int s = 0;
 #pragma unroll
