@@ -349,6 +349,29 @@ spec_status spec_kv_commit(const void *scratch, void *cache, int32_t planes, int
 spec_status spec_tree_mask(const int32_t *parents, const int32_t *node_count, int32_t B, int32_t N,
                            uint32_t *mask, int32_t *depth, hipStream_t stream);
 
+/*
+ * Failures recorded in a workspace.  The verify kernels wait for each other
+ * within a launch, and each wait is bounded (about 2 s).  A wait that runs
+ * out leaves -1 in the outputs of its sequence (tree, or top-k row) and adds
+ * one to a counter in the workspace header.  The same happens for every
+ * sequence of spec_verify_chain_sample when the workspace holds no statistics
+ * from spec_verify_chain_stats for its call.  So the counter is 0 as long as
+ * every output written through this workspace is valid.
+ *
+ *   workspace, workspace_bytes  a workspace of any entry point (at least 256
+ *                               bytes: the header).
+ *   reset                       nonzero: set the counter back to 0 after
+ *                               reading it.
+ *   failures                    HOST pointer: receives the counter.
+ *
+ * Enqueues a 4-byte device-to-host copy (and, with reset, a 4-byte clear) on
+ * `stream` and synchronises that stream, so it must not be called while the
+ * stream is being captured.  Returns SPEC_ERR_INVALID_ARG for a missing or
+ * too small workspace, SPEC_ERR_LAUNCH if the runtime reports an error.
+ */
+spec_status spec_verify_workspace_failures(void *workspace, size_t workspace_bytes, int32_t reset,
+                                           uint32_t *failures, hipStream_t stream);
+
 /* Static text for a status code. */
 const char *spec_verify_status_string(spec_status status);
 

@@ -59,10 +59,11 @@ def _load(path: str = LIB_PATH):
     lib.spec_kv_commit.argtypes = [vp, vp, i32, i32, i32, i32, ctypes.c_int64, vp, i32, vp, vp, vp,
                                    vp]
     lib.spec_tree_mask.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    lib.spec_verify_workspace_failures.argtypes = [vp, sz, i32, ctypes.POINTER(ctypes.c_uint32), vp]
     for fn in ("spec_verify_workspace_bytes", "spec_verify_chain", "spec_verify_chain_stats",
                "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy",
                "spec_verify_tree_greedy_dyn", "spec_draft_topk", "spec_kv_commit",
-               "spec_tree_mask"):
+               "spec_tree_mask", "spec_verify_workspace_failures"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -147,6 +148,24 @@ def workspace(mode: int, B: int, K_or_N: int, V: int, dtype: int, device) -> tor
     per-call tags); a buffer with other prior contents must be zeroed first."""
     n = spec_verify_workspace_bytes(mode, B, K_or_N, V, dtype)
     return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def workspace_failures(workspace_buf, *, reset=False, stream=None) -> int:
+    """Bounded waits that ran out (and chain samples without statistics) since
+    the workspace was zeroed or last reset; 0 means every output written
+    through it is valid.  Synchronises the stream."""
+    _check_dev("workspace_buf", workspace_buf, torch.uint8)
+    out = ctypes.c_uint32(0)
+    _call("spec_verify_workspace_failures", _ptr(workspace_buf), workspace_buf.numel(), int(bool(reset)),
+          ctypes.byref(out), _stream(workspace_buf.device, stream))
+    return out.value
+
+
+def check_workspace(workspace_buf, *, stream=None) -> None:
+    """Raises SpecVerifyError if any bounded wait ran out on this workspace."""
+    n = workspace_failures(workspace_buf, stream=stream)
+    if n:
+        raise SpecVerifyError(f"workspace reports {n} failed wait(s);", SPEC_ERR_LAUNCH)
 
 
 def _chain_check(target, draft, draft_tokens, u_accept, u_sample):

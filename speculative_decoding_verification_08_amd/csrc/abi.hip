@@ -4,8 +4,12 @@
 #include <math.h>
 #include <string.h>
 
+#include <unistd.h>
+
 #include <algorithm>
 #include <atomic>
+#include <chrono>
+#include <random>
 
 #include "plan.hpp"
 #include "kv.hpp"
@@ -45,7 +49,8 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
     else if (mode == SPEC_MODE_TOPK) rows = B;
     else rows = static_cast<int64_t>(B) * KN;
     p.rows = rows;
-    p.chunk = first_pass_chunk(dtype);
+    p.chunk = mode == SPEC_MODE_CHAIN ? kStatChunkBytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4)
+                                      : first_pass_chunk(dtype);
     p.nchunk = (V + p.chunk - 1) / p.chunk;
     if (rows * p.nchunk > 0x7fffffffLL) return false;  // one-dimensional grid
     size_t off = kWorkspaceHeader;  // the graph tag word comes first
@@ -54,14 +59,17 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
         off += align_up(static_cast<size_t>(rows) * p.nchunk * 16);
         p.chunk2 = kChunk2Bytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
         p.nchunk2 = (V + p.chunk2 - 1) / p.chunk2;
-        // The bonus draw takes its chunk masses from the statistics chunks.
-        if (p.chunk2 != p.chunk) return false;
-            // Every draw workgroup of a sequence waits for the sequence's other
+        // The bonus draw takes the mass of a draw chunk from the statistics
+        // of the two statistics chunks it covers.
+        if (p.chunk2 != 2 * p.chunk || p.nchunk > kMaxStatChunks) return false;
+        // Every draw workgroup of a sequence waits for the sequence's other
         // chunks, so a sequence's draw workgroups must fit the chip together.
         if (p.nchunk2 > kMaxDrawChunks) return false;
         if (static_cast<int64_t>(B) * p.nchunk2 > 0x7fffffffLL) return false;
         p.off_sums = off;  // two tagged masses per chunk: residual, target
         off += align_up(static_cast<size_t>(B) * p.nchunk2 * 16);
+        p.off_rec = off;   // one record per sequence
+        off += align_up(static_cast<size_t>(B) * kRecWords * 8);
     } else if (mode == SPEC_MODE_TOPK) {
         // One launch: a workgroup per (row, chunk) and a merge workgroup per
         // row (one wavefront holds the row's chunk maxima, two per lane).
@@ -86,13 +94,21 @@ T *at(void *ws, size_t off) {
 
 spec_status launch_status(hipError_t e) { return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH; }
 
-// Tag of one spec_verify_chain call: unique in the process for 2^32 - 2 calls,
-// never 0 (zeroed memory) or the phase entry points' tag.
+// Tag of one host call: a process-wide counter in [1, 2^31), so never 0 (a
+// zeroed word) and never a graph tag.  It starts at a random value, so that a
+// workspace whose words were left by another process or another load of the
+// library holds this process's tags only by a 2^-31 chance.
+uint32_t random_tag_start() {
+    std::random_device rd;
+    uint64_t x = (static_cast<uint64_t>(rd()) << 32) ^ rd();
+    x ^= static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count());
+    x ^= static_cast<uint64_t>(getpid()) << 17;
+    x *= 0x9e3779b97f4a7c15ull;
+    return static_cast<uint32_t>(x >> 33);
+}
 uint32_t next_call_tag() {
-    static std::atomic<uint32_t> counter{0};
-    // [kPhasedTag + 1, kGraphTagBit): never 0, the phase tag or a graph tag.
-    return counter.fetch_add(1u, std::memory_order_relaxed) % (kGraphTagBit - kPhasedTag - 1u) +
-           kPhasedTag + 1u;
+    static std::atomic<uint32_t> counter{random_tag_start()};
+    return counter.fetch_add(1u, std::memory_order_relaxed) % (kGraphTagBit - 1u) + 1u;
 }
 
 // The tag of one call.  While `stream` is being captured into a graph, the
@@ -131,28 +147,30 @@ spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype,
     a.K = K;
     a.V = V;
     a.c = static_cast<float>(1.4426950408889634 / static_cast<double>(T));
+    a.hdr = static_cast<uint32_t *>(ws);
     a.chunk = plan.chunk;
     a.nchunk = plan.nchunk;
     a.nchunk2 = plan.nchunk2;
+    a.S = static_cast<uint32_t>(2 * K) * plan.nchunk;
+    a.D = plan.nchunk2;
+    a.fd_nch = make_fastdiv(plan.nchunk);
+    a.fd_D = make_fastdiv(a.D);
     a.partial = at<uint64_t>(ws, plan.off_partial);
     a.sums = at<uint64_t>(ws, plan.off_sums);
-    a.tag = kPhasedTag;
+    a.rec = at<uint64_t>(ws, plan.off_rec);
     return SPEC_OK;
 }
 
-// Sequences between a sequence's statistics and its draw in the one-launch
-// chain verify.  When the whole step fits in three quarters of the
-// last-level cache, every draw comes after all statistics (the second read
-// of row j hits the cache anyway, and the streaming runs undisturbed);
-// otherwise the draws trail by what keeps about 96 MB between the two reads
-// of a row, and by at least one resident window of workgroups.
-int32_t chain_lag(int32_t B, int32_t K, int32_t V, spec_dtype dtype, int64_t per_seq) {
-    const int64_t seq_bytes =
-        static_cast<int64_t>(2 * K + 1) * V * (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
-    if (static_cast<int64_t>(B) * seq_bytes <= kLlcBytes / 4 * 3) return B;
-    const int64_t window = (kResidentWGs + per_seq - 1) / per_seq + 1;
-    const int64_t reach = kLlcBytes / 8 * 3 / seq_bytes;
-    return static_cast<int32_t>(std::min<int64_t>(B, std::max(window, reach)));
+// The one-launch schedule (see k_chain_fused): grid size, or 0 if it would
+// not fit a one-dimensional grid.
+uint32_t chain_schedule(ChainArgs &a) {
+    const uint64_t B = a.B, S = a.S, D = a.D, nch = a.nchunk;
+    const uint64_t total = B * (S + D + nch + 3);
+    if (total > 0x7fffffffull) return 0;
+    a.fd_S1 = make_fastdiv(static_cast<uint32_t>(S + 1));
+    a.blocks_end = static_cast<uint32_t>(S + (B - 1) * (S + 1));
+    a.bon_end = static_cast<uint32_t>(a.blocks_end + B * nch);
+    return static_cast<uint32_t>(total);
 }
 
 spec_status chain_sample_args(const int32_t *tokens, const float *ua, const float *us, int32_t B,
@@ -213,6 +231,8 @@ spec_status spec_verify_chain_stats(const void *target_logits, const void *draft
     if (st != SPEC_OK || B == 0) return st;
     if (K > 0 && (!draft_tokens || !aligned(draft_tokens, 4))) return SPEC_ERR_INVALID_ARG;
     a.tokens = draft_tokens;
+    st = call_tag(workspace, stream, a.tag, a.tag_src);
+    if (st != SPEC_OK) return st;
     return launch_status(launch_chain_stats(a, dtype, stream));
 }
 
@@ -230,6 +250,9 @@ spec_status spec_verify_chain_sample(const void *target_logits, const void *draf
     st = chain_sample_args(draft_tokens, u_accept, u_sample, B, K, out_tokens, out_accepted,
                            out_diag, a);
     if (st != SPEC_OK) return st;
+    st = call_tag(workspace, stream, a.tag, a.tag_src);
+    if (st != SPEC_OK) return st;
+    a.sample_phase = true;  // the statistics carry the tag the stats phase recorded
     return launch_status(launch_chain_draw(a, dtype, stream));
 }
 
@@ -249,14 +272,23 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
     if (st != SPEC_OK) return st;
     st = call_tag(workspace, stream, a.tag, a.tag_src);
     if (st != SPEC_OK) return st;
-    const int64_t per_seq = static_cast<int64_t>(2 * K + 1) * plan.nchunk + plan.nchunk2;
-    if (static_cast<int64_t>(B) * per_seq <= 0x7fffffffLL) {
-        a.lag = chain_lag(B, K, V, dtype, per_seq);
-        return launch_status(launch_chain_fused(a, dtype, stream));
-    }
+    if (chain_schedule(a) != 0) return launch_status(launch_chain_fused(a, dtype, stream));
+    // Too large for one grid: the two kernels of the phase entry points, the
+    // draws reading the statistics under this call's own tag.
     st = launch_status(launch_chain_stats(a, dtype, stream));
     if (st != SPEC_OK) return st;
     return launch_status(launch_chain_draw(a, dtype, stream));
+}
+
+spec_status spec_verify_workspace_failures(void *workspace, size_t workspace_bytes, int32_t reset,
+                                           uint32_t *failures, hipStream_t stream) {
+    if (!workspace || workspace_bytes < kWorkspaceHeader || !aligned(workspace, 16) || !failures)
+        return SPEC_ERR_INVALID_ARG;
+    uint32_t *word = static_cast<uint32_t *>(workspace) + kHdrFailures;
+    if (hipMemcpyAsync(failures, word, sizeof *failures, hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return SPEC_ERR_LAUNCH;
+    if (reset && hipMemsetAsync(word, 0, sizeof *word, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+    return hipStreamSynchronize(stream) == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
 }
 
 spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,

@@ -1,36 +1,33 @@
 // Chain verify at T > 0 on gfx950.
 //
 // Statistics items stream every logit of the step once.  One workgroup takes
-// one 16 KB vocabulary chunk of one row (target rows 0..K and draft rows
+// one 8 KB vocabulary chunk of one row (target rows 0..K and draft rows
 // 0..K-1 of a sequence), folds it into softmax statistics (ref, z) and
 // publishes them.  This is the HBM-bound work that carries the bytes; no
 // statistics workgroup waits for another.
 //
-// Draw items run one workgroup per (sequence b, 16 KB chunk of a row).  Each
-// merges b's row statistics, reads the logits at the drafted tokens from the
-// inputs, evaluates the accept test of every drafted token
-// (u < p(x)/q(x), French lesson "Décodage spéculatif et Eagle", section "La
-// règle de l'exactitude"; forum post "Speculative Decoding: от идеи до SOTA",
-// §3) and finds the first rejection j.  It holds its chunk of row j in
-// registers and publishes the chunk's draw masses -- max(0, p_j - q_j) after a
-// rejection (the residual of the same passages) and p_j, the bonus draw's
-// weights when every draft was accepted.  Once every chunk's masses are
-// visible, all of b's workgroups find the chunk whose running mass first
-// exceeds u * S; that chunk's workgroup picks the token and writes the
-// sequence's outputs.
+// A resolver per sequence merges the statistics of the rows the accept tests
+// read, evaluates the accept test of every drafted token (u < p(x)/q(x),
+// French lesson "Décodage spéculatif et Eagle", section "La règle de
+// l'exactitude"; forum post "Speculative Decoding: от идеи до SOTA", §3),
+// finds the first rejection j and publishes a record: j and row j's
+// normalisers.  After a rejection, draw items (one per 16 KB chunk of row j)
+// publish the chunk's mass of the residual max(0, p_j - q_j) (the residual of
+// the same passages) and of p_j; the sequence's finisher finds the chunk
+// whose running mass first exceeds u * S, reads it again and draws the token.
+// When every draft is accepted, the sequence's bonus item draws from p_K,
+// whose chunk masses follow from the bonus row's statistics.
 //
-// k_chain_fused runs both kinds of item in one grid (the one-call entry
-// point); k_chain_stats and k_chain_draw run them as two kernels in stream
-// order (the two-phase entry points).  Both give the same bits.
+// k_chain_fused runs every item in one grid (the one-call entry point);
+// k_chain_stats and k_chain_draw run them as two kernels in stream order (the
+// two-phase entry points).  Both give the same bits.
 //
 // Hand-over words are 64 bits: the call's tag above a 32-bit value, written
 // with device-scope atomic stores and read with device-scope atomic loads; a
 // reader checks the tag, so nothing left by an earlier call is taken for
 // fresh, and waits (bounded in time) until the word is visible.  Tags are
-// never 0, so a workspace zeroed once before first use needs no clearing.  A
-// workgroup only waits for workgroups of lower index (dispatched before it)
-// or for the draw workgroups of its own sequence (a sequence has at most 64,
-// far fewer than the chip holds).
+// never 0, so a workspace zeroed once before first use needs no clearing.  An
+// item only waits for workgroups of lower index (dispatched before it).
 #include "device.hpp"
 #include "handover.hpp"
 #include "plan.hpp"
@@ -38,57 +35,68 @@
 namespace sv {
 namespace {
 
+// Bits of -inf: entries past the end of a row are replaced by them, which
+// gives them weight 0 in both kinds (c > 0) without a test per entry.
+template <class DT>
+struct NegInf;
+template <>
+struct NegInf<Bf16> {
+    static constexpr uint32_t kBits = 0xff80ff80u;
+};
+template <>
+struct NegInf<F32> {
+    static constexpr uint32_t kBits = 0xff800000u;
+};
+
 // ------------------------------------------------------------ stats item
 
 // Row r of sequence b (r <= K: target row r; r > K: draft row r - K - 1),
-// chunk ch.
-template <class DT, int U>
+// chunk ch: a.chunk entries, 8 KB, two 16-byte vectors per thread.  With V a
+// multiple of the vector width every chunk starts on a vector (the vectors
+// past the end of a row's last chunk read as -inf); otherwise the entries are
+// read one by one.  Loads are non-temporal: a logit is streamed once, and its
+// second read by a draw comes from HBM either way.
+template <class DT, bool VecOk>
 __device__ __forceinline__ void stats_item(const ChainArgs &a, int64_t b, int r, int ch) {
-    constexpr int VEC = DT::kVec;
+    constexpr int VEC = DT::kVec, U = kStatVecs, N = U * VEC;
+    constexpr uint32_t kInf = NegInf<DT>::kBits;
     const int K = a.K, V = a.V, R = 2 * K + 1;
     const int64_t row = b * R + r;
     const void *base = r <= K ? a.target : a.draft;
     const int64_t trow = r <= K ? b * (K + 1) + r : b * K + (r - K - 1);
     const int64_t e0 = static_cast<int64_t>(ch) * a.chunk;
-    const int64_t e1 = min(e0 + a.chunk, static_cast<int64_t>(V));
-    const Span s = split_span<VEC>(trow * V + e0, trow * V + e1);
-
-    float ref = -INFINITY, z = 0.f;
-    {
-        const int64_t h = s.h0 + threadIdx.x;
-        if (h < s.h1) {
-            const float x = load_one<DT>(base, h);
-            mz_batch<1>(&x, a.c, ref, z);
-        }
-    }
-    const uint4 *vp = static_cast<const uint4 *>(base);
-    int64_t v = s.va + threadIdx.x;
-    for (; v + (U - 1) * kWG < s.vb; v += U * kWG) {
+    const int n = static_cast<int>(min(static_cast<int64_t>(a.chunk), static_cast<int64_t>(V) - e0));
+    const int tid = threadIdx.x;
+    float x[N];
+    if constexpr (VecOk) {
+        const uint4 *vp = static_cast<const uint4 *>(base) + (trow * V + e0) / VEC;
+        const int nv = n / VEC, last = nv - 1;
         uint4 raw[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = vp[v + u * kWG];
-        float x[U * VEC];
+        for (int u = 0; u < U; ++u) raw[u] = load_nt(vp + min(tid + u * kWG, last));
+        if (nv < U * kWG) {  // the row's last chunk
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (tid + u * kWG > last) raw[u] = make_uint4(kInf, kInf, kInf, kInf);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) unpack<DT>(raw[u], x + u * VEC);
-        mz_batch<U * VEC>(x, a.c, ref, z);
-    }
-    for (; v < s.vb; v += kWG) {
-        float x[VEC];
-        unpack<DT>(vp[v], x);
-        mz_batch<VEC>(x, a.c, ref, z);
-    }
-    {
-        const int64_t t = s.t0 + threadIdx.x;
-        if (t < s.t1) {
-            const float x = load_one<DT>(base, t);
-            mz_batch<1>(&x, a.c, ref, z);
+    } else {
+        const int64_t g0 = trow * V + e0;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int e = tid + i * kWG;
+            const float v = load_one<DT>(base, g0 + min(e, n - 1));
+            x[i] = e < n ? v : -INFINITY;
         }
     }
-    mz_reduce_wg(ref, z);
-    if (threadIdx.x == 0) {
+    float ref = -INFINITY, z = 0.f;
+    mz_chunk_wg<N>(x, a.c, ref, z);
+    if (tid == 0) {
+        const uint32_t tag = a.tag_src ? *a.tag_src : a.tag;  // a graph replay's tag
         uint64_t *w = a.partial + 2 * (row * a.nchunk + ch);
-        publish_f32(w, a.tag, ref);
-        publish_f32(w + 1, a.tag, z);
+        publish_f32(w, tag, ref);
+        publish_f32(w + 1, tag, z);
     }
 }
 
@@ -110,44 +118,28 @@ __device__ __forceinline__ float weight_r(float p, float d, float c, const DrawR
     return fmaxf(fmaf(-exp2_hw(fmaf(d, c, -w.rd)), w.izd, p), 0.f);
 }
 
-// Bits of -inf: entries past the end of a row are replaced by them, which
-// gives them weight 0 in both kinds (c > 0) without a test per entry.
-template <class DT>
-struct NegInf;
-template <>
-struct NegInf<Bf16> {
-    static constexpr uint32_t kBits = 0xff80ff80u;
-};
-template <>
-struct NegInf<F32> {
-    static constexpr uint32_t kBits = 0xff800000u;
-};
-
-// Resolve of sequence b inside a draw workgroup.  Each group of 16 lanes
-// merges one row's chunk statistics (lane i folds chunks i, i + 16, ... in
-// order, then a fixed DPP tree), every wavefront evaluates the accept test of
-// every drafted token (u < P/Q, strict; Q = 0 accepts iff P > 0) and takes j,
-// the first rejected position (K if none), by ballot, so no second barrier is
-// needed.  The accept tests never read the bonus row (target row K), so j < K
-// is decided without it; the bonus row is needed only when j = K, and then
-// its per-chunk statistics are left in LDS for the bonus draw.  Row j's
-// statistics land in `w`.  Without Live the statistics come from a kernel
-// ordered before this one by the stream and are read once; with Live the
-// statistics workgroups may still be running, so the words are read with
-// device-scope loads, and while a needed word is missing one lane of each
-// wavefront that saw it waits for it (bounded) and everything is read again.
-// `ok` is false if a needed word was not written for this call in time.
-// With `diag` the workgroup also writes p_k(x_k), q_k(x_k) and their ratio to
-// out_diag.
+// Resolve of sequence b (one workgroup per sequence).  Each group of 16 lanes
+// merges the chunk statistics of one of the 2K rows the accept tests read
+// (target rows 0..K-1, draft rows 0..K-1; lane i folds chunks i, i + 16, ...
+// in order, then a fixed DPP tree, in double precision), every wavefront
+// evaluates the accept test of every drafted token (u < P/Q, strict; Q = 0
+// accepts iff P > 0) and takes j, the first rejected position (K if none), by
+// ballot.  Row j's statistics land in `w` (row K's are the bonus item's).
+// Without Live the statistics come from a kernel ordered before this one by
+// the stream and are read once; with Live the statistics workgroups may still
+// be running, so the words are read with device-scope loads, and while one is
+// missing one lane of each wavefront that saw it waits for it (bounded) and
+// everything is read again.  `ok` is false if a word was not written in time.
+// Statistics words carry `ptag`.  The workgroup also writes p_k(x_k),
+// q_k(x_k) and their ratio to out_diag.
 template <class DT, bool Live, int Fold, int kPasses>
-__device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow &w, bool &ok,
-                                             bool diag, float *lds) {
+__device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, uint32_t ptag, DrawRow &w,
+                                             bool &ok, float *lds) {
     // The loads of kPasses row groups (16 rows each) go out together.
     constexpr int kGroup = 16, kGroups = kWG / kGroup;
     float *s_ref = lds, *s_z = s_ref + (2 * kMaxK + 1);
-    float *s_kref = lds + kDrawBonusAt, *s_kz = s_kref + kMaxDrawChunks;
     __shared__ int s_stale[2][kWaves + 1];
-    const int K = a.K, V = a.V, R = 2 * K + 1, nch = a.nchunk;
+    const int K = a.K, V = a.V, R = 2 * K + 1, R2 = 2 * K, nch = a.nchunk;
     const int tid = threadIdx.x, lane = tid % kWave, grp = tid / kGroup, gl = tid % kGroup;
     const uint64_t *part = a.partial + 2 * static_cast<int64_t>(b) * R * nch;
     // Lane k's position: its uniform, and the drafted token's logits in target
@@ -163,24 +155,29 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
         ld = load_one<DT>(a.draft, (static_cast<int64_t>(b) * K + kk) * V + x);
     }
     const uint64_t t0 = Live ? wall_clock64() : 0;
+    // The statistics items of a sequence are dispatched in row order, the
+    // draft row K - 1 last: one lane waits for that row's last word before
+    // the whole read.
+    if (Live && K > 0 && tid == 0)
+        wait_word(part + 2 * ((2 * K) * nch + nch - 1) + 1, ptag, t0);
     float P = 0.f, Q = 0.f;
     int j = K;
-    for (int it = 0;; ++it) {
-        // The first missing word this lane found among the rows the accept
-        // tests read, and in the bonus row.
-        const uint64_t *miss = nullptr, *miss_k = nullptr;
-        for (int r0 = 0; r0 < R; r0 += kGroups * kPasses) {
-            float ref[kPasses], z[kPasses];
+    ok = true;
+    for (int it = 0; K > 0; ++it) {
+        const uint64_t *miss = nullptr;  // the first missing word this lane found
+        for (int r0 = 0; r0 < R2; r0 += kGroups * kPasses) {
+            float ref[kPasses];
+            double z[kPasses];
 #pragma unroll
             for (int q = 0; q < kPasses; ++q) {
                 ref[q] = -INFINITY;
-                z[q] = 0.f;
+                z[q] = 0.0;
             }
             for (int i0 = 0; i0 < nch; i0 += kGroup * Fold) {
                 uint64_t pr[kPasses][Fold], pz[kPasses][Fold];
 #pragma unroll
                 for (int q = 0; q < kPasses; ++q) {
-                    const int rr = min(r0 + grp + kGroups * q, R - 1);
+                    const int rs = min(r0 + grp + kGroups * q, R2 - 1), rr = rs < K ? rs : rs + 1;
 #pragma unroll
                     for (int f = 0; f < Fold; ++f) {
                         const uint64_t *pw = part + 2 * (rr * nch + min(i0 + gl + kGroup * f, nch - 1));
@@ -196,47 +193,40 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
                 }
 #pragma unroll
                 for (int q = 0; q < kPasses; ++q) {
-                    const int r = r0 + grp + kGroups * q, rr = min(r, R - 1);
+                    const int rs = r0 + grp + kGroups * q, rsc = min(rs, R2 - 1), rr = rsc < K ? rsc : rsc + 1;
 #pragma unroll
                     for (int f = 0; f < Fold; ++f) {
                         const int i = i0 + gl + kGroup * f;
-                        const bool in = r < R && i < nch;
-                        const bool cr = current(pr[q][f], a.tag), cz = current(pz[q][f], a.tag);
+                        const bool in = rs < R2 && i < nch;
+                        const bool cr = current(pr[q][f], ptag), cz = current(pz[q][f], ptag);
                         const float fr = in ? word_f32(pr[q][f]) : -INFINITY;
                         const float fz = in ? word_f32(pz[q][f]) : 0.f;
-                        if (in && !(cr && cz)) {
-                            const uint64_t *mw = part + 2 * (rr * nch + i) + (cr ? 1 : 0);
-                            if (r == K) miss_k = miss_k ? miss_k : mw;
-                            else miss = miss ? miss : mw;
-                        }
-                        if (r == K && in) {
-                            s_kref[i] = fr;
-                            s_kz[i] = fz;
-                        }
-                        mz_merge(ref[q], z[q], fr, fz);
+                        if (in && !(cr && cz) && !miss) miss = part + 2 * (rr * nch + i) + (cr ? 1 : 0);
+                        mz_merge_d(ref[q], z[q], fr, static_cast<double>(fz));
                     }
                 }
             }
 #pragma unroll
             for (int q = 0; q < kPasses; ++q) {
-                mz_row_merge(ref[q], z[q]);
-                const int r = r0 + grp + kGroups * q;
-                if (r < R && gl == kGroup - 1) {
-                    s_ref[r] = ref[q];
-                    s_z[r] = z[q];
+                mz_row_merge_d(ref[q], z[q]);
+                const int rs = r0 + grp + kGroups * q;
+                if (rs < R2 && gl == kGroup - 1) {
+                    const int rr = rs < K ? rs : rs + 1;
+                    s_ref[rr] = ref[q];
+                    s_z[rr] = static_cast<float>(z[q]);
                 }
             }
         }
-        const uint64_t st = __ballot(miss != nullptr), st_k = __ballot(miss_k != nullptr);
+        const uint64_t st = __ballot(miss != nullptr);
         // Double-buffered by iteration: a wavefront may start the next
         // iteration while another still reads this one's flags.
-        if (lane == 0) s_stale[it & 1][tid / kWave] = (st ? 1 : 0) | (st_k ? 2 : 0);
+        if (lane == 0) s_stale[it & 1][tid / kWave] = st ? 1 : 0;
         if (tid == 0) s_stale[it & 1][kWaves] = !Live || wall_clock64() - t0 > kWaitTicks;
         __syncthreads();
         int any = 0;
 #pragma unroll
         for (int k = 0; k < kWaves; ++k) any |= s_stale[it & 1][k];
-        if (!(any & 1)) {
+        if (!any) {
             bool reject = false;
             if (lane < K) {
                 P = exp2_hw(fmaf(lt, a.c, -s_ref[lane])) / s_z[lane];
@@ -245,33 +235,28 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, DrawRow 
             }
             const uint64_t m = __ballot(reject);
             j = m ? (__ffsll(static_cast<unsigned long long>(m)) - 1) : K;
-            if (j < K || !(any & 2)) {
-                ok = true;
-                break;
-            }
+            break;
         }
         if (s_stale[it & 1][kWaves]) {
             ok = false;
             break;
         }
-        // One lane of each wavefront that missed a needed word waits for it.
-        const uint64_t need = (any & 1) ? st : st_k;
-        if (need && lane == __ffsll(static_cast<unsigned long long>(need)) - 1)
-            wait_word((any & 1) ? miss : miss_k, a.tag, t0);
+        // One lane of each wavefront that missed a word waits for it.
+        if (st && lane == __ffsll(static_cast<unsigned long long>(st)) - 1) wait_word(miss, ptag, t0);
     }
-    if (ok && diag && tid < K && a.out_diag) {
+    if (ok && tid < K && a.out_diag) {
         float *dg = a.out_diag + 4 * (static_cast<int64_t>(b) * (K + 1) + lane);
         dg[0] = P;
         dg[1] = Q;
         dg[2] = Q > 0.f ? P / Q : (P > 0.f ? INFINITY : 0.f);
     }
     w.resid = j < K;
-    w.rt = s_ref[j];
-    w.izt = 1.f / s_z[j];
-    w.rd = w.resid ? s_ref[K + 1 + j] : 0.f;
-    w.izd = w.resid ? 1.f / s_z[K + 1 + j] : 0.f;
-    w.trow = (static_cast<int64_t>(b) * (K + 1) + j) * V;
-    w.drow = w.resid ? (static_cast<int64_t>(b) * K + j) * V : 0;
+    if (w.resid) {
+        w.rt = s_ref[j];
+        w.izt = 1.f / s_z[j];
+        w.rd = s_ref[K + 1 + j];
+        w.izd = 1.f / s_z[K + 1 + j];
+    }
     return j;
 }
 
@@ -403,123 +388,33 @@ __device__ __forceinline__ void crossing_chunk(float m, bool in, float us, float
     base = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), cstar));
 }
 
-// Workgroup (b, ch) of the draw after the resolve.
-//
-// After a rejection (Resid) it holds entries [ch*C2, ch*C2 + C2) of rows j in
-// registers (kSeg contiguous entries per thread) and publishes the chunk's
-// residual mass sum max(0, p_j - q_j) and target mass sum p_j.  Wavefront 0
-// reads every chunk's masses of the sequence into its lanes (a sequence has
-// at most 64 chunks), and every draw workgroup of the sequence computes the
-// same S and the same crossing chunk.  An all-zero residual (reachable only
-// through rounding) draws from p_j.
-//
-// For the bonus draw (j = K) the chunk masses of p_K follow from the bonus
-// row's chunk statistics, z_c * 2^(ref_c - ref) / z, with no second read of
-// the row; only the crossing chunk's workgroup loads its entries.
-//
-// In the crossing chunk's workgroup the first thread whose running mass
-// passes u * S hands its entries to wavefront 0 through LDS, which finds the
-// entry (one lane each) and writes the sequence's outputs.
-template <class DT, bool VecOk, bool Resid>
-__device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int j, const DrawRow &w,
-                                          bool ok, float us, int32_t my_tok, float *lds) {
-    using CK = Chunk2<DT>;
-    constexpr int C2 = CK::kElems, kSeg = CK::kSeg, NQ = CK::kNQ;
-    static_assert(kSeg <= kWave, "one lane per entry of a thread's segment");
-    static_assert(CK::kRawWords <= kDrawRawWords, "a thread's raw entries fit the LDS");
-    static_assert(kMaxDrawChunks <= kWave, "one lane per chunk of a sequence");
-    const int K = a.K, tid = threadIdx.x, lane = tid % kWave, nc = a.nchunk2;
-    __shared__ float s_tau, s_base;
-    __shared__ int s_cstar, s_resid, s_ok;
+// A sequence whose bounded wait ran out, or whose statistics were not left
+// for this call: its outputs read -1 and the workspace's failure count grows.
+__device__ __forceinline__ void fail_sequence(const ChainArgs &a, int b) {
+    const int K = a.K;
+    for (int k = threadIdx.x; k <= K; k += kWG)
+        a.out_tokens[static_cast<int64_t>(b) * (K + 1) + k] = -1;
+    if (threadIdx.x == 0) {
+        a.out_accepted[b] = -1;
+        __hip_atomic_fetch_add(a.hdr + kHdrFailures, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
 
-    const int64_t c0 = static_cast<int64_t>(ch) * C2;
-    const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(a.V) - c0));
-    const int s0 = tid * kSeg;
-    uint4 rt[NQ], rd[NQ];
-    float lp = 0.f, lr = 0.f, ex_r = 0.f, ex_p = 0.f, S = 0.f;
-    if constexpr (Resid) {
-        chunk_weights<DT, VecOk, true>(a, w, c0, n, s0, rt, rd, lp, lr);
-        // Running sums inside the chunk and the chunk's masses, both kinds,
-        // in one pass (published afterwards: a barrier after a device-scope
-        // store would wait for it to complete).
-        uint64_t *sums = a.sums + 2 * static_cast<int64_t>(b) * nc;
-        float mr, mp;
-        wg_excl_scan2(lr, lp, ex_r, ex_p, mr, mp);
-        if (tid == 0) {
-            publish_f32(&sums[2 * ch], a.tag, mr);
-            publish_f32(&sums[2 * ch + 1], a.tag, mp);
-        }
-        if (tid < kWave) {
-            const int i = min(lane, nc - 1);
-            uint64_t vr, vp;
-            bool fresh;
-            const uint64_t t0 = wall_clock64();
-            // The last chunk's workgroup is dispatched last: wait for its
-            // word, then read all (repeating while any is missing).
-            if (lane == 0) wait_word(&sums[2 * (nc - 1)], a.tag, t0);
-            for (;;) {
-                vr = fetch(&sums[2 * i]);
-                vp = fetch(&sums[2 * i + 1]);
-                fresh = __all(current(vr, a.tag) && current(vp, a.tag));
-                if (fresh || wall_clock64() - t0 > kWaitTicks) break;
-                __builtin_amdgcn_s_sleep(8);
-            }
-            const bool in = lane < nc;
-            const float m_r = in ? word_f32(vr) : 0.f, m_p = in ? word_f32(vp) : 0.f;
-            const bool resid = wave_last(wave_incl_sum(m_r)) > 0.f;
-            float tau, base;
-            int cstar;
-            crossing_chunk(resid ? m_r : m_p, in, us, S, tau, cstar, base);
-            if (lane == 0) {
-                s_ok = fresh;
-                s_cstar = cstar;
-                s_base = base;
-                s_tau = tau;
-                s_resid = resid;
-            }
-        }
-    } else {
-        if (tid < kWave) {
-            const bool in = lane < nc;
-            const float *s_kref = lds + kDrawBonusAt, *s_kz = s_kref + kMaxDrawChunks;
-            const int i = min(lane, nc - 1);
-            const float m = in ? __fmul_rn(s_kz[i] * exp2_hw(s_kref[i] - w.rt), w.izt) : 0.f;
-            float tau, base;
-            int cstar;
-            crossing_chunk(m, in, us, S, tau, cstar, base);
-            if (lane == 0) {
-                s_ok = 1;
-                s_cstar = cstar;
-                s_base = base;
-                s_tau = tau;
-                s_resid = 0;
-            }
-        }
-    }
-    __syncthreads();
-    if (!(ok && s_ok)) {
-        // A bounded wait ran out: the last chunk's workgroup marks the
-        // sequence as failed.
-        if (ch == nc - 1) {
-            for (int k = tid; k <= K; k += kWG)
-                a.out_tokens[static_cast<int64_t>(b) * (K + 1) + k] = -1;
-            if (tid == 0) a.out_accepted[b] = -1;
-        }
-        return;
-    }
-    if (s_cstar != ch) return;
-    if constexpr (!Resid) {
-        // The bonus draw's crossing chunk: its entries and running sums now.
-        chunk_weights<DT, VecOk, false>(a, w, c0, n, s0, rt, rd, lp, lr);
-        float mr, mp;
-        wg_excl_scan2(0.f, lp, ex_r, ex_p, mr, mp);
-    }
-
-    // The crossing chunk.  The first thread whose running mass passes tau
-    // (else the last thread with mass) holds the drawn entry.
-    const bool resid = Resid && s_resid;
-    const float tau = s_tau;
-    const float start = s_base + (resid ? ex_r : ex_p), l = resid ? lr : lp;
+// The search inside the crossing chunk (entries [c0, c0 + C2) of row j) and
+// the emission.  The first thread whose running mass passes tau (else the last
+// thread with mass) hands its raw entries to wavefront 0 through LDS; lane e
+// takes entry e of that thread's segment, and the first entry whose running
+// mass exceeds tau (else the last with weight) is the drawn token.  Wavefront
+// 0 writes x_0..x_{j-1}, the drawn token, then -1.  `start` and `l` are this
+// thread's running mass before its segment and its segment's mass.
+template <class DT, bool Resid>
+__device__ __forceinline__ void search_emit(const ChainArgs &a, int b, int64_t c0, int j,
+                                            const DrawRow &w, bool resid, float tau, float start,
+                                            float l, const uint4 (&rt)[Chunk2<DT>::kNQ],
+                                            const uint4 (&rd)[Chunk2<DT>::kNQ], float S,
+                                            int32_t my_tok, float *lds) {
+    constexpr int kSeg = Chunk2<DT>::kSeg, NQ = Chunk2<DT>::kNQ;
+    const int K = a.K, tid = threadIdx.x, lane = tid % kWave;
     int tf, tl;
     wg_min_max(l > 0.f && start + l > tau ? tid : INT32_MAX, l > 0.f ? tid : -1, tf, tl);
     const int ts = tf != INT32_MAX ? tf : max(tl, 0);
@@ -535,9 +430,6 @@ __device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int
     }
     __syncthreads();
     if (tid >= kWave) return;
-    // Lane e takes entry e of that thread's segment: the first entry (index
-    // order) whose running mass exceeds tau; if rounding leaves none, the
-    // last entry with weight.
     const int e = min(lane, kSeg - 1);
     float x = weight_p(raw_entry<DT>(s_raw, e), a.c, w);
     if (Resid && resid) x = weight_r(x, raw_entry<DT>(s_raw + kDrawRawWords, e), a.c, w);
@@ -547,8 +439,6 @@ __device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int
     const int pick = f ? __ffsll(static_cast<unsigned long long>(f)) - 1
                        : (nz ? 63 - __clzll(static_cast<long long>(nz)) : 0);
     const int32_t token = static_cast<int32_t>(c0 + ts * kSeg + pick);
-
-    // Emit x_0..x_{j-1}, then the drawn token, then -1 (lane k: position k).
     for (int k = lane; k <= K; k += kWave) {
         int32_t o = -1;
         if (k < j) o = my_tok;  // k < j <= K <= 64: k is this lane
@@ -563,142 +453,421 @@ __device__ __forceinline__ void draw_body(const ChainArgs &a, int b, int ch, int
     if (lane == 0) a.out_accepted[b] = j;
 }
 
-template <class DT, bool VecOk, bool Live>
+// The tags of an item: `tag` for the words this launch's workgroups hand each
+// other, `ptag` for the statistics words (the phase word's tag in the
+// two-phase form, else the call's own).
+__device__ __forceinline__ void item_tags(const ChainArgs &a, uint32_t &ptag, uint32_t &tag) {
+    tag = a.tag_src ? *a.tag_src : a.tag;
+    ptag = a.sample_phase ? __hip_atomic_load(a.hdr + kHdrPhaseTag, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT)
+                          : tag;
+}
+
+// Resolver item of sequence b: the accept tests and j, published as the
+// sequence's record -- j, then row j's (ref, 1/z) of the target and the draft
+// -- for its draw items and bonus item.  A failed resolve publishes j = -1.
+template <class DT, bool Live>
+__device__ __forceinline__ void resolver_item(const ChainArgs &a, int b, float *lds) {
+    uint32_t ptag, tag;
+    item_tags(a, ptag, tag);
+    DrawRow w;
+    bool ok = false;
+    int j = -1;
+    if (ptag != 0) {  // else the two-phase form without statistics for this call
+        const int R = 2 * a.K + 1;
+        j = a.nchunk > 16 ? resolve_local<DT, Live, 4, 1>(a, b, ptag, w, ok, lds)
+            : R <= 16     ? resolve_local<DT, Live, 1, 1>(a, b, ptag, w, ok, lds)
+            : R <= 32     ? resolve_local<DT, Live, 1, 2>(a, b, ptag, w, ok, lds)
+                          : resolve_local<DT, Live, 1, 4>(a, b, ptag, w, ok, lds);
+    }
+    if (!ok) {
+        fail_sequence(a, b);
+        j = -1;
+    }
+    if (threadIdx.x == 0) {
+        uint64_t *rec = a.rec + kRecWords * static_cast<int64_t>(b);
+        const bool r = ok && j < a.K;
+        publish_f32(rec + 1, tag, r ? w.rt : 0.f);
+        publish_f32(rec + 2, tag, r ? w.izt : 0.f);
+        publish_f32(rec + 3, tag, r ? w.rd : 0.f);
+        publish_f32(rec + 4, tag, r ? w.izd : 0.f);
+        publish(rec, tag, static_cast<uint32_t>(j));
+    }
+}
+
+// Wavefront 0 waits (bounded) until every word of sequence b's record
+// carries `tag`, and shares it through LDS.  Returns false if it did not in
+// time; else j (-1 for a failed resolve) and row j's statistics.
+__device__ __forceinline__ bool read_record(const ChainArgs &a, int b, uint32_t tag, int &j,
+                                            DrawRow &w) {
+    __shared__ uint32_t s_rec[kRecWords + 1];
+    const int lane = threadIdx.x % kWave;
+    if (threadIdx.x < kWave) {
+        const uint64_t *rec = a.rec + kRecWords * static_cast<int64_t>(b);
+        const uint64_t t0 = wall_clock64();
+        uint64_t v;
+        bool fresh;
+        for (;;) {
+            v = lane < 5 ? fetch(rec + lane) : tagged(tag, 0);
+            fresh = __all(current(v, tag));
+            if (fresh || wall_clock64() - t0 > kWaitTicks) break;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        if (lane < 5) s_rec[lane] = static_cast<uint32_t>(v);
+        if (lane == 0) s_rec[kRecWords] = fresh;
+    }
+    __syncthreads();
+    j = static_cast<int32_t>(s_rec[0]);
+    w.rt = __uint_as_float(s_rec[1]);
+    w.izt = __uint_as_float(s_rec[2]);
+    w.rd = __uint_as_float(s_rec[3]);
+    w.izd = __uint_as_float(s_rec[4]);
+    return s_rec[kRecWords] != 0;
+}
+
+// Draw item (b, ch) after a rejection at j < K: the masses of entries
+// [ch*C2, ch*C2 + C2) of rows j -- the residual max(0, p_j - q_j) and the
+// target p_j -- summed in the order the finisher's scan of the same chunk
+// uses, so the two agree bit for bit.  It waits for nothing but the record
+// and leaves the draw to the sequence's finisher.
+template <class DT, bool VecOk>
 __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, float *lds) {
-    const int K = a.K;
-    // Drafted tokens for the emission (lane k: token k) and the draw's
-    // uniform, loaded before the resolve.
+    using CK = Chunk2<DT>;
+    constexpr int C2 = CK::kElems, kSeg = CK::kSeg, NQ = CK::kNQ;
+    const int K = a.K, tid = threadIdx.x;
+    uint32_t ptag, tag;
+    item_tags(a, ptag, tag);
+    int j;
+    DrawRow w;
+    if (!read_record(a, b, tag, j, w) || j < 0 || j >= K) return;  // the finisher reports failures
+    w.resid = true;
+    w.trow = (static_cast<int64_t>(b) * (K + 1) + j) * a.V;
+    w.drow = (static_cast<int64_t>(b) * K + j) * a.V;
+    const int64_t c0 = static_cast<int64_t>(ch) * C2;
+    const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(a.V) - c0));
+    uint4 rt[NQ], rd[NQ];
+    float lp, lr, ex_r, ex_p, mr, mp;
+    chunk_weights<DT, VecOk, true>(a, w, c0, n, tid * kSeg, rt, rd, lp, lr);
+    wg_excl_scan2(lr, lp, ex_r, ex_p, mr, mp);
+    if (tid == 0) {
+        uint64_t *sums = a.sums + 2 * (static_cast<int64_t>(b) * a.nchunk2 + ch);
+        publish_f32(sums, tag, mr);
+        publish_f32(sums + 1, tag, mp);
+    }
+}
+
+// Finisher of sequence b after a rejection at j < K.  Wavefront 0 waits
+// (bounded) until every chunk's masses carry the call's tag (lane i: chunk i;
+// a sequence has at most 64 chunks), takes the total S of the residual (of
+// p_j if the residual is all zero, reachable only through rounding), tau = u
+// * S and the crossing chunk; the workgroup then loads that chunk of rows j
+// again and searches it.
+template <class DT, bool VecOk>
+__device__ __forceinline__ void finisher_item(const ChainArgs &a, int b, float *lds) {
+    using CK = Chunk2<DT>;
+    constexpr int C2 = CK::kElems, kSeg = CK::kSeg, NQ = CK::kNQ;
+    static_assert(kSeg <= kWave, "one lane per entry of a thread's segment");
+    static_assert(CK::kRawWords <= kDrawRawWords, "a thread's raw entries fit the LDS");
+    static_assert(kMaxDrawChunks <= kWave, "one lane per chunk of a sequence");
+    const int K = a.K, tid = threadIdx.x, lane = tid % kWave, nc = a.nchunk2;
+    __shared__ float s_tau, s_base, s_S;
+    __shared__ int s_cstar, s_resid, s_ok;
     const int32_t *tk = K > 0 ? a.tokens + static_cast<int64_t>(b) * K
                               : reinterpret_cast<const int32_t *>(a.u_sample + b);
-    const int32_t my_tok = tk[min(static_cast<int>(threadIdx.x % kWave), max(K - 1, 0))];
+    const int32_t my_tok = tk[min(lane, max(K - 1, 0))];
     const float us = a.u_sample[b];
+    uint32_t ptag, tag;
+    item_tags(a, ptag, tag);
+    int j;
     DrawRow w;
-    bool ok;
-    // One chunk per lane of a 16-lane group when a row has at most 16 (the
-    // loads of up to four groups of 16 rows together), else four chunks per
-    // lane and load batch.
-    const int R = 2 * a.K + 1;
-    const int j = a.nchunk > 16 ? resolve_local<DT, Live, 4, 1>(a, b, w, ok, ch == 0, lds)
-                  : R <= 16     ? resolve_local<DT, Live, 1, 1>(a, b, w, ok, ch == 0, lds)
-                  : R <= 32     ? resolve_local<DT, Live, 1, 2>(a, b, w, ok, ch == 0, lds)
-                                : resolve_local<DT, Live, 1, 4>(a, b, w, ok, ch == 0, lds);
-    if (w.resid) draw_body<DT, VecOk, true>(a, b, ch, j, w, ok, us, my_tok, lds);
-    else draw_body<DT, VecOk, false>(a, b, ch, j, w, ok, us, my_tok, lds);
-}
-
-template <class DT, int U>
-__global__ __launch_bounds__(kWG) void k_chain_stats(ChainArgs a) {
-    if (a.tag_src) a.tag = *a.tag_src;  // a graph replay's tag
-    // 32-bit index arithmetic (the grid is below 2^31 workgroups): a 64-bit
-    // division is a long instruction sequence ahead of the first load.
-    const uint32_t R = 2 * a.K + 1, S = R * a.nchunk;
-    const uint32_t g = blockIdx.x, b = g / S, pos = g - b * S, r = pos / a.nchunk;
-    stats_item<DT, U>(a, b, static_cast<int>(r), static_cast<int>(pos - r * a.nchunk));
-}
-
-template <class DT, bool VecOk>
-__global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
-    if (a.tag_src) a.tag = *a.tag_src;  // a graph replay's tag
-    const uint32_t nc = a.nchunk2, g = blockIdx.x, b = g / nc;
-    __shared__ __align__(16) float lds[kDrawLds];
-    draw_item<DT, VecOk, false>(a, static_cast<int>(b), static_cast<int>(g - b * nc), lds);
-}
-
-// The whole chain verify in one launch.  Per sequence there are S = (2K+1) *
-// nchunk statistics workgroups and D = nchunk2 draw workgroups.  The hardware
-// dispatches workgroups in index order, and a draw workgroup waits only for
-// statistics workgroups it needs and for the draw workgroups of its own
-// sequence (dispatched together), so the order of the grid decides how draws
-// overlap streaming.
-//
-// With lag < B: blocks of the statistics of sequence b + lag with the draws of
-// b in one run among them, after a prologue of the first `lag` sequences'
-// statistics and before an epilogue of the last `lag` sequences' draws.  A
-// draw only waits for workgroups of lower index; with the lag at least the
-// chip's resident window, the statistics it needs have usually finished
-// before it starts.
-//
-// With lag = B: the statistics of every row but the bonus rows (target row K,
-// read only by a draw with every draft accepted) come first, sequence by
-// sequence, then the bonus rows, then every draw, so draws after a rejection
-// can start while the bonus rows stream.  (Placing the draws ahead of the
-// bonus rows measured slower.)
-template <class DT, bool VecOk>
-__global__ __launch_bounds__(kWG) void k_chain_fused(ChainArgs a) {
-    if (a.tag_src) a.tag = *a.tag_src;  // a graph replay's tag
-    __shared__ __align__(16) float lds[kDrawLds];
-    const uint32_t nch = a.nchunk, S = (2 * a.K + 1) * nch, D = a.nchunk2, L = a.lag, B = a.B;
-    const uint32_t g = blockIdx.x;
-    // Decode the workgroup's item: a draw (b, chunk) or statistics (b, row, chunk).
-    uint32_t b, r = 0, ch;
-    bool draw;
-    if (L == B) {
-        const uint32_t Sn = S - nch, nNB = B * Sn, d0 = nNB + B * nch;
-        draw = g >= d0;
-        if (draw) {
-            b = (g - d0) / D;
-            ch = g - d0 - b * D;
-        } else if (g < nNB) {
-            b = g / Sn;
-            const uint32_t p = g - b * Sn, rr = p / nch;
-            r = rr < static_cast<uint32_t>(a.K) ? rr : rr + 1;
-            ch = p - rr * nch;
-        } else {
-            const uint32_t h = g - nNB;
-            b = h / nch;
-            r = a.K;
-            ch = h - b * nch;
+    if (!read_record(a, b, tag, j, w)) {
+        fail_sequence(a, b);
+        return;
+    }
+    if (j < 0 || j >= K) return;  // a failed resolve (reported), or the bonus item's draw
+    w.resid = true;
+    w.trow = (static_cast<int64_t>(b) * (K + 1) + j) * a.V;
+    w.drow = (static_cast<int64_t>(b) * K + j) * a.V;
+    if (tid < kWave) {
+        const uint64_t *sums = a.sums + 2 * static_cast<int64_t>(b) * nc;
+        const int i = min(lane, nc - 1);
+        uint64_t vr, vp;
+        bool fresh;
+        const uint64_t t0 = wall_clock64();
+        for (;;) {
+            vr = fetch(&sums[2 * i]);
+            vp = fetch(&sums[2 * i + 1]);
+            fresh = __all(current(vr, tag) && current(vp, tag));
+            if (fresh || wall_clock64() - t0 > kWaitTicks) break;
+            __builtin_amdgcn_s_sleep(8);
         }
-    } else {
-        const uint32_t pro = L * S, steady = pro + (B - L) * (S + D);
-        uint32_t s;
-        if (g < pro) {
-            b = g / S;
-            s = g - b * S;
-            draw = false;
-        } else if (g < steady) {
-            // Block k: the D draws of sequence k in one run at offset o among
-            // the statistics of sequence L + k; o steps by 8 per block, so the
-            // run's place in each XCD's share of the order rotates.
-            const uint32_t h = g - pro, k = h / (S + D), p = h - k * (S + D);
-            const uint32_t o = (8 * k) % (S + 1);
-            draw = p >= o && p < o + D;
-            b = draw ? k : L + k;
-            s = draw ? p - o : (p < o ? p : p - D);
-        } else {
-            const uint32_t h = g - steady, k = h / D;
-            b = B - L + k;
-            s = h - k * D;
-            draw = true;
-        }
-        if (draw) {
-            ch = s;
-        } else {
-            r = s / nch;
-            ch = s - r * nch;
+        const bool in = lane < nc;
+        const float m_r = in ? word_f32(vr) : 0.f, m_p = in ? word_f32(vp) : 0.f;
+        const bool resid = wave_last(wave_incl_sum(m_r)) > 0.f;
+        float S, tau, base;
+        int cstar;
+        crossing_chunk(resid ? m_r : m_p, in, us, S, tau, cstar, base);
+        if (lane == 0) {
+            s_ok = fresh;
+            s_cstar = cstar;
+            s_base = base;
+            s_tau = tau;
+            s_S = S;
+            s_resid = resid;
         }
     }
-    if (draw)
-        draw_item<DT, VecOk, true>(a, static_cast<int>(b), static_cast<int>(ch), lds);
-    else
-        stats_item<DT, 4>(a, b, static_cast<int>(r), static_cast<int>(ch));
+    __syncthreads();
+    if (!s_ok) {
+        fail_sequence(a, b);
+        return;
+    }
+    const int ch = s_cstar;
+    const bool resid = s_resid;
+    const int64_t c0 = static_cast<int64_t>(ch) * C2;
+    const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(a.V) - c0));
+    uint4 rt[NQ], rd[NQ];
+    float lp, lr, ex_r, ex_p, mr, mp;
+    chunk_weights<DT, VecOk, true>(a, w, c0, n, tid * kSeg, rt, rd, lp, lr);
+    wg_excl_scan2(lr, lp, ex_r, ex_p, mr, mp);
+    search_emit<DT, true>(a, b, c0, j, w, resid, s_tau, s_base + (resid ? ex_r : ex_p),
+                          resid ? lr : lp, rt, rd, s_S, my_tok, lds);
+}
+
+// The bonus row's statistics of sequence b, on wavefront 0: per statistics
+// chunk into LDS (lane i holds chunks i and i + 64), and merged in double
+// precision into the row's (ref, 1/z).  With Live the words are read with
+// device-scope loads until all carry `ptag` (bounded).  Returns false if a
+// word was not written in time.
+template <bool Live>
+__device__ __forceinline__ bool bonus_row(const ChainArgs &a, int b, uint32_t ptag, float &rt,
+                                          float &izt, float *lds) {
+    static_assert(kMaxStatChunks <= 2 * kWave, "two statistics chunks per lane");
+    __shared__ float s_rt, s_izt;
+    __shared__ int s_okb;
+    const int K = a.K, nch = a.nchunk, lane = threadIdx.x % kWave;
+    float *s_kref = lds + kDrawBonusAt, *s_kz = s_kref + kMaxStatChunks;
+    if (threadIdx.x < kWave) {
+        const uint64_t *part = a.partial + 2 * ((static_cast<int64_t>(b) * (2 * K + 1) + K) * nch);
+        const int i0 = min(lane, nch - 1), i1 = min(lane + kWave, nch - 1);
+        const bool in0 = lane < nch, in1 = lane + kWave < nch;
+        const uint64_t t0 = Live ? wall_clock64() : 0;
+        uint64_t w[4];
+        bool fresh;
+        for (;;) {
+            w[0] = fetch(part + 2 * i0);
+            w[1] = fetch(part + 2 * i0 + 1);
+            w[2] = fetch(part + 2 * i1);
+            w[3] = fetch(part + 2 * i1 + 1);
+            fresh = __all((!in0 || (current(w[0], ptag) && current(w[1], ptag))) &&
+                          (!in1 || (current(w[2], ptag) && current(w[3], ptag))));
+            if (fresh || !Live || wall_clock64() - t0 > kWaitTicks) break;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        const float r0 = in0 ? word_f32(w[0]) : -INFINITY, z0 = in0 ? word_f32(w[1]) : 0.f;
+        const float r1 = in1 ? word_f32(w[2]) : -INFINITY, z1 = in1 ? word_f32(w[3]) : 0.f;
+        if (in0) {
+            s_kref[lane] = r0;
+            s_kz[lane] = z0;
+        }
+        if (in1) {
+            s_kref[lane + kWave] = r1;
+            s_kz[lane + kWave] = z1;
+        }
+        float ref = r0;
+        double z = z0;
+        mz_merge_d(ref, z, r1, z1);
+        mz_wave_merge_d(ref, z);
+        if (lane == kWave - 1) {
+            s_rt = ref;
+            s_izt = 1.f / static_cast<float>(z);
+            s_okb = fresh;
+        }
+    }
+    __syncthreads();
+    rt = s_rt;
+    izt = s_izt;
+    return s_okb != 0;
+}
+
+// Bonus item of sequence b: if every draft was accepted, it draws the bonus
+// token from p_K.  The mass of each draw chunk follows from the bonus row's
+// statistics, z_c * 2^(ref_c - ref) / z over the two statistics chunks it
+// covers, with no second read of the row; only the crossing chunk's entries
+// are loaded.
+template <class DT, bool VecOk, bool Live>
+__device__ __forceinline__ void bonus_item(const ChainArgs &a, int b, float *lds) {
+    using CK = Chunk2<DT>;
+    constexpr int C2 = CK::kElems, kSeg = CK::kSeg, NQ = CK::kNQ;
+    const int K = a.K, tid = threadIdx.x, lane = tid % kWave, nc = a.nchunk2;
+    __shared__ float s_tau, s_base, s_S;
+    __shared__ int s_cstar;
+    const int32_t *tk = K > 0 ? a.tokens + static_cast<int64_t>(b) * K
+                              : reinterpret_cast<const int32_t *>(a.u_sample + b);
+    const int32_t my_tok = tk[min(lane, max(K - 1, 0))];
+    const float us = a.u_sample[b];
+    uint32_t ptag, tag;
+    item_tags(a, ptag, tag);
+    int j;
+    DrawRow w;
+    if (!read_record(a, b, tag, j, w)) {
+        fail_sequence(a, b);
+        return;
+    }
+    if (j != K) return;  // a residual draw, or a failed resolve (reported)
+    if (!bonus_row<Live>(a, b, ptag, w.rt, w.izt, lds)) {
+        fail_sequence(a, b);
+        return;
+    }
+    w.resid = false;
+    w.trow = (static_cast<int64_t>(b) * (K + 1) + K) * a.V;
+    w.drow = 0;
+    w.rd = w.izd = 0.f;
+    if (tid < kWave) {
+        // Draw chunk i covers statistics chunks 2i and 2i + 1 (the last draw
+        // chunk of a row may cover one).
+        const float *s_kref = lds + kDrawBonusAt, *s_kz = s_kref + kMaxStatChunks;
+        const bool in = lane < nc;
+        const int i = min(lane, nc - 1), i0 = 2 * i, i1 = min(2 * i + 1, a.nchunk - 1);
+        const float z1 = i1 > i0 ? s_kz[i1] * exp2_hw(s_kref[i1] - w.rt) : 0.f;
+        const float m = in ? __fmul_rn(s_kz[i0] * exp2_hw(s_kref[i0] - w.rt) + z1, w.izt) : 0.f;
+        float S, tau, base;
+        int cstar;
+        crossing_chunk(m, in, us, S, tau, cstar, base);
+        if (lane == 0) {
+            s_cstar = cstar;
+            s_base = base;
+            s_tau = tau;
+            s_S = S;
+        }
+    }
+    __syncthreads();
+    const int ch = s_cstar;
+    const int64_t c0 = static_cast<int64_t>(ch) * C2;
+    const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(a.V) - c0));
+    uint4 rt[NQ], rd[NQ];
+    float lp, lr, ex_r, ex_p, mr, mp;
+    chunk_weights<DT, VecOk, false>(a, w, c0, n, tid * kSeg, rt, rd, lp, lr);
+    wg_excl_scan2(0.f, lp, ex_r, ex_p, mr, mp);
+    search_emit<DT, false>(a, b, c0, K, w, false, s_tau, s_base + ex_p, lp, rt, rd, s_S, my_tok, lds);
+}
+
+// Grid (chunk, row, sequence): the hardware hands out the item, so nothing
+// stands between a workgroup's start and its first loads.  Workgroup (0, 0,
+// 0) records the call's tag in the workspace header for the draws.
+template <class DT, bool VecOk>
+__global__ __launch_bounds__(kWG) void k_chain_stats(ChainArgs a) {
+    stats_item<DT, VecOk>(a, blockIdx.z, static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.x));
+    if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0)
+        a.hdr[kHdrPhaseTag] = a.tag_src ? *a.tag_src : a.tag;
+}
+
+// The draws of the two-phase form: B resolvers, B * D draw items, B
+// finishers and B bonus items (each waits only for items of lower index).
+template <class DT, bool VecOk>
+__global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
+    __shared__ __align__(16) float lds[kDrawLds];
+    const uint32_t g = blockIdx.x, B = a.B, nd = B * a.D;
+    if (g < B) {
+        resolver_item<DT, false>(a, static_cast<int>(g), lds);
+    } else if (g < B + nd) {
+        const uint32_t h = g - B, b = fdiv(h, a.fd_D);
+        draw_item<DT, VecOk>(a, static_cast<int>(b), static_cast<int>(h - b * a.D), lds);
+    } else if (g < 2 * B + nd) {
+        finisher_item<DT, VecOk>(a, static_cast<int>(g - B - nd), lds);
+    } else {
+        bonus_item<DT, VecOk, false>(a, static_cast<int>(g - 2 * B - nd), lds);
+    }
+}
+
+// The whole chain verify in one launch.  Per sequence: S statistics items of
+// the rows the accept tests read (target rows 0..K-1, draft rows 0..K-1), a
+// resolver, nchunk statistics items of the bonus row, D draw items, a
+// finisher and a bonus item.  The hardware dispatches workgroups in index
+// order, and an item waits only for workgroups of lower index (dispatched
+// before it), in this order:
+//   block k      the statistics of sequence k, then the resolver of k - 1;
+//   bonus        the statistics of every bonus row;
+//   tail         the resolver of sequence B - 1, every draw item, every
+//                finisher, every bonus item.
+// Each resolver finds its statistics done or nearly so, and the stream of
+// logits runs undisturbed: draws placed among the statistics measured slower
+// at every lag tried (their second read of row j takes slots and bandwidth
+// from the stream), so the second reads all come after it, where the bonus
+// draws, which need none, also run.
+template <class DT, bool VecOk>
+__global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
+    __shared__ __align__(16) float lds[kDrawLds];
+    // The statistics items' arguments are loaded with the schedule's, in one
+    // batch ahead of the decode: otherwise the compiler sinks them into the
+    // item's branch, and every workgroup waits for a second round of argument
+    // loads before its first logit load.
+    asm volatile("" ::"s"(a.target), "s"(a.draft), "s"(a.partial), "s"(a.c), "s"(a.V), "s"(a.chunk),
+                 "s"(a.tag), "s"(a.tag_src));
+    const uint32_t g = blockIdx.x, S = a.S, D = a.D, K = a.K, B = a.B;
+    uint32_t b = 0, p = 0;
+    int kind;  // 0 statistics (non-bonus rows), 1 resolver, 2 draw, 3 finisher, 4 bonus-row statistics, 5 bonus item
+    if (g < S) {
+        kind = 0;
+        p = g;
+    } else if (g < a.blocks_end) {
+        const uint32_t h = g - S, kk = fdiv(h, a.fd_S1), q = h - kk * (S + 1);
+        kind = q < S ? 0 : 1;
+        b = q < S ? kk + 1 : kk;
+        p = q;
+    } else if (g < a.bon_end) {
+        const uint32_t h = g - a.blocks_end;
+        b = fdiv(h, a.fd_nch);
+        p = h - b * a.nchunk;
+        kind = 4;
+    } else {
+        const uint32_t h = g - a.bon_end;
+        if (h == 0) {
+            kind = 1;
+            b = B - 1;
+        } else if (h - 1 < B * D) {
+            kind = 2;
+            b = fdiv(h - 1, a.fd_D);
+            p = h - 1 - b * D;
+        } else if (h - 1 - B * D < B) {
+            kind = 3;
+            b = h - 1 - B * D;
+        } else {
+            kind = 5;
+            b = h - 1 - B * D - B;
+        }
+    }
+    if (kind == 0) {
+        const uint32_t rr = fdiv(p, a.fd_nch), ch = p - rr * a.nchunk;
+        stats_item<DT, VecOk>(a, b, static_cast<int>(rr < K ? rr : rr + 1), static_cast<int>(ch));
+    } else if (kind == 4) {
+        stats_item<DT, VecOk>(a, b, static_cast<int>(K), static_cast<int>(p));
+    } else if (kind == 1) {
+        resolver_item<DT, true>(a, static_cast<int>(b), lds);
+    } else if (kind == 2) {
+        draw_item<DT, VecOk>(a, static_cast<int>(b), static_cast<int>(p), lds);
+    } else if (kind == 3) {
+        finisher_item<DT, VecOk>(a, static_cast<int>(b), lds);
+    } else {
+        bonus_item<DT, VecOk, true>(a, static_cast<int>(b), lds);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(static_cast<uint32_t>(static_cast<int64_t>(a.B) * (2 * a.K + 1) * a.nchunk)),
-        blk(kWG);
-    if (dtype == 1)
-        k_chain_stats<Bf16, 4><<<g, blk, 0, s>>>(a);
-    else
-        k_chain_stats<F32, 4><<<g, blk, 0, s>>>(a);
+    const dim3 g(a.nchunk, 2 * a.K + 1, a.B), blk(kWG);
+    if (dtype == 1) {
+        if (a.V % Bf16::kVec == 0) k_chain_stats<Bf16, true><<<g, blk, 0, s>>>(a);
+        else k_chain_stats<Bf16, false><<<g, blk, 0, s>>>(a);
+    } else {
+        if (a.V % F32::kVec == 0) k_chain_stats<F32, true><<<g, blk, 0, s>>>(a);
+        else k_chain_stats<F32, false><<<g, blk, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s) {
-    const int64_t per_seq = static_cast<int64_t>(2 * a.K + 1) * a.nchunk + a.nchunk2;
-    const dim3 g(static_cast<uint32_t>(static_cast<int64_t>(a.B) * per_seq)), blk(kWG);
+    const dim3 g(a.bon_end + 1 + static_cast<uint32_t>(a.B) * (a.D + 2)), blk(kWG);
     if (dtype == 1) {
         if (a.V % Bf16::kVec == 0) k_chain_fused<Bf16, true><<<g, blk, 0, s>>>(a);
         else k_chain_fused<Bf16, false><<<g, blk, 0, s>>>(a);
@@ -710,7 +879,7 @@ hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_chain_draw(const ChainArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.nchunk2)), blk(kWG);
+    const dim3 g(static_cast<uint32_t>(a.B) * (a.D + 3)), blk(kWG);
     if (dtype == 1) {
         if (a.V % Bf16::kVec == 0) k_chain_draw<Bf16, true><<<g, blk, 0, s>>>(a);
         else k_chain_draw<Bf16, false><<<g, blk, 0, s>>>(a);

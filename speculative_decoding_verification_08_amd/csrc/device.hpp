@@ -28,6 +28,14 @@ struct F32 {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A 16-byte load marked non-temporal: a streamed logit is read once, so it
+// should not displace data that is reused from the caches.
+__device__ __forceinline__ uint4 load_nt(const uint4 *p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // One element of a logit array, widened exactly to fp32.
 template <class DT>
 __device__ __forceinline__ float load_one(const void *base, int64_t i);
@@ -83,6 +91,18 @@ __device__ __forceinline__ void mz_merge(float &ref, float &z, float ref2, float
     const float m = fmaxf(ref, ref2);
     const float r = (m == -INFINITY) ? 0.f : m;
     z = z * exp2_hw(ref - r) + z2 * exp2_hw(ref2 - r);
+    ref = m;
+}
+
+// The same with z in double precision.  A row's sum of exponentials is
+// formed from per-thread fp32 sums of a few dozen terms, and every sum above
+// that level (across lanes, wavefronts and chunks) is taken in double: the
+// residual max(0, p - q) cancels most of p and q, so an error in either
+// normaliser reaches the residual's mass amplified by 1 / mass.
+__device__ __forceinline__ void mz_merge_d(float &ref, double &z, float ref2, double z2) {
+    const float m = fmaxf(ref, ref2);
+    const float r = (m == -INFINITY) ? 0.f : m;
+    z = z * static_cast<double>(exp2_hw(ref - r)) + z2 * static_cast<double>(exp2_hw(ref2 - r));
     ref = m;
 }
 
@@ -227,6 +247,15 @@ template <int Ctrl, int RowMask = 0xF>
 __device__ __forceinline__ int mov_i(int identity, int x) {
     return __builtin_amdgcn_update_dpp(identity, x, Ctrl, RowMask, 0xF, false);
 }
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ double mov_d(double identity, double x) {
+    const long long xi = __double_as_longlong(x), ii = __double_as_longlong(identity);
+    const int lo = __builtin_amdgcn_update_dpp(static_cast<int>(ii), static_cast<int>(xi), Ctrl,
+                                               RowMask, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(static_cast<int>(ii >> 32), static_cast<int>(xi >> 32),
+                                               Ctrl, RowMask, 0xF, false);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
+}
 }  // namespace dpp
 
 // Inclusive sum over lanes 0..lane of a wavefront, in a fixed order: within
@@ -239,6 +268,22 @@ __device__ __forceinline__ float wave_incl_sum(float x) {
     x += dpp::mov_f<dpp::kRowBcast15, 0xA>(0.f, x);
     x += dpp::mov_f<dpp::kRowBcast31, 0xC>(0.f, x);
     return x;
+}
+// The same in double precision.
+__device__ __forceinline__ double wave_incl_sum_d(double x) {
+    x += dpp::mov_d<dpp::kRowShr1>(0.0, x);
+    x += dpp::mov_d<dpp::kRowShr2>(0.0, x);
+    x += dpp::mov_d<dpp::kRowShr4>(0.0, x);
+    x += dpp::mov_d<dpp::kRowShr8>(0.0, x);
+    x += dpp::mov_d<dpp::kRowBcast15, 0xA>(0.0, x);
+    x += dpp::mov_d<dpp::kRowBcast31, 0xC>(0.0, x);
+    return x;
+}
+__device__ __forceinline__ double wave_last_d(double x) {
+    const long long v = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(v), 63);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), 63);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
 }
 // Value of lane 63 (uniform).
 __device__ __forceinline__ float wave_last(float x) {
@@ -359,6 +404,24 @@ __device__ __forceinline__ void mz_wave_merge(float &ref, float &z) {
     SV_MZ_STEP(dpp::kRowBcast15, 0xA)
     SV_MZ_STEP(dpp::kRowBcast31, 0xC)
 }
+#define SV_MZ_STEP_D(CTRL, MASK)                                                 \
+    {                                                                            \
+        const float r2 = dpp::mov_f<CTRL, MASK>(-INFINITY, ref);                \
+        const double z2 = dpp::mov_d<CTRL, MASK>(0.0, z);                       \
+        mz_merge_d(ref, z, r2, z2);                                              \
+    }
+__device__ __forceinline__ void mz_row_merge_d(float &ref, double &z) {
+    SV_MZ_STEP_D(dpp::kRowShr1, 0xF)
+    SV_MZ_STEP_D(dpp::kRowShr2, 0xF)
+    SV_MZ_STEP_D(dpp::kRowShr4, 0xF)
+    SV_MZ_STEP_D(dpp::kRowShr8, 0xF)
+}
+__device__ __forceinline__ void mz_wave_merge_d(float &ref, double &z) {
+    mz_row_merge_d(ref, z);
+    SV_MZ_STEP_D(dpp::kRowBcast15, 0xA)
+    SV_MZ_STEP_D(dpp::kRowBcast31, 0xC)
+}
+#undef SV_MZ_STEP_D
 #undef SV_MZ_STEP
 
 __device__ __forceinline__ void mz_reduce_wg(float &ref, float &z) {
@@ -374,6 +437,50 @@ __device__ __forceinline__ void mz_reduce_wg(float &ref, float &z) {
         ref = s_ref[0];
         z = s_z[0];
         for (int i = 1; i < kWaves; ++i) mz_merge(ref, z, s_ref[i], s_z[i]);
+    }
+}
+
+
+// Maximum over the wavefront (uniform result).
+__device__ __forceinline__ float wave_max_f(float x) {
+    x = fmaxf(x, dpp::mov_f<dpp::kRowShr1>(-INFINITY, x));
+    x = fmaxf(x, dpp::mov_f<dpp::kRowShr2>(-INFINITY, x));
+    x = fmaxf(x, dpp::mov_f<dpp::kRowShr4>(-INFINITY, x));
+    x = fmaxf(x, dpp::mov_f<dpp::kRowShr8>(-INFINITY, x));
+    x = fmaxf(x, dpp::mov_f<dpp::kRowBcast15, 0xA>(-INFINITY, x));
+    x = fmaxf(x, dpp::mov_f<dpp::kRowBcast31, 0xC>(-INFINITY, x));
+    return wave_last(x);
+}
+
+// Softmax statistics of N logits per thread over the workgroup, valid in
+// thread 0.  Every wavefront takes its largest logit as the reference, so
+// each logit costs one exp2 and no rescaling; the four wavefronts' (ref, z)
+// are then merged in order by thread 0.
+template <int N>
+__device__ __forceinline__ void mz_chunk_wg(const float *x, float c, float &ref, float &z) {
+    __shared__ float s_ref[kWaves];
+    __shared__ double s_z[kWaves];
+    float m = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) m = fmaxf(m, x[i]);
+    const float rw = wave_max_f(m) * c;
+    const float r = rw == -INFINITY ? 0.f : rw;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < N; ++i) s[i & 3] += exp2_hw(fmaf(x[i], c, -r));
+    const double zw =
+        wave_last_d(wave_incl_sum_d(static_cast<double>((s[0] + s[1]) + (s[2] + s[3]))));
+    const int w = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) {
+        s_ref[w] = rw;
+        s_z[w] = zw;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        ref = s_ref[0];
+        double zd = s_z[0];
+        for (int i = 1; i < kWaves; ++i) mz_merge_d(ref, zd, s_ref[i], s_z[i]);
+        z = static_cast<float>(zd);
     }
 }
 

@@ -10,22 +10,24 @@ namespace sv {
 constexpr int kMaxK = 64;
 constexpr int kMaxTreeNodes = 256;
 constexpr int kChunk2Bytes = 16384;  // bytes of one row per chunk of the residual / bonus pass
-// Workgroups of 256 threads the chip holds at once (256 CUs, 8 each) and the
-// last-level (Infinity) cache in front of HBM.  The one-launch chain verify
-// places a sequence's draw at least one resident window after its
-// statistics, and close enough that the draw's second read of row j still
-// finds it in that cache.
+// The chain's statistics items take 8 KB of a row each (two 16-byte vectors
+// per thread); a draw chunk is two statistics chunks.
+constexpr int kStatVecs = 2;
+constexpr int kStatChunkBytes = kStatVecs * 16 * 256;
+constexpr int kMaxStatChunks = 128;  // statistics chunks per row: V <= 128 x 8 KB of entries
+// Workgroups of 256 threads the chip holds at once (256 CUs, 8 each): the
+// top-k merges trail their rows' chunks by about this many workgroups.
 constexpr int kResidentWGs = 2048;
-constexpr int64_t kLlcBytes = 256ll << 20;
+constexpr int kRecWords = 8;       // words per sequence record (five used)
 constexpr int kMaxDrawChunks = 64;  // draw chunks per row: V <= 64 x 16 KB of entries
 // LDS words of a draw workgroup: its sequence's row statistics (ref, z), one
 // thread's raw entries of the crossing chunk (16 words per row, target and
-// draft) and that thread's running mass, then the bonus row's per-chunk
-// statistics (ref, z).
+// draft) and that thread's running mass, then the bonus row's statistics
+// (ref, z) per statistics chunk.
 constexpr int kDrawRawWords = 16;
 constexpr int kDrawRawAt = (2 * (2 * kMaxK + 1) + 3) / 4 * 4;  // 16-byte aligned
 constexpr int kDrawBonusAt = kDrawRawAt + 2 * kDrawRawWords + 4;
-constexpr int kDrawLds = kDrawBonusAt + 2 * kMaxDrawChunks;
+constexpr int kDrawLds = kDrawBonusAt + 2 * kMaxStatChunks;
 
 // How a launch cuts the rows it streams into vocabulary chunks, and where its
 // scratch lives inside the caller's workspace.
@@ -35,21 +37,44 @@ struct Plan {
     int nchunk = 0;        // chunks per row, first pass
     int chunk2 = 0;        // elements per chunk, residual / bonus pass (chain)
     int nchunk2 = 0;       // chunks per row, residual / bonus pass (chain)
-    size_t off_partial = 0, off_sums = 0;
+    size_t off_partial = 0, off_sums = 0, off_rec = 0;
     size_t bytes = 0;      // total workspace
 };
 
 // Words handed between workgroups carry the call's tag in their upper 32 bits
 // and a 32-bit value below; a reader checks that a word's tag is the current
 // call's, so words left by earlier calls (of any shape) are never taken for
-// fresh ones.
-constexpr uint32_t kPhasedTag = 1;  // tag of the phase entry points; whole calls use >= 2
+// fresh ones.  Host tags come from a process-wide counter that starts at a
+// random value; they are never 0 and never have bit 31 set.
 // Tags of calls recorded into a graph have bit 31 set: each replay's tag is
 // advanced on the device (launch_advance_tag), in a range host tags never use.
 constexpr uint32_t kGraphTagBit = 0x80000000u;
-constexpr size_t kWorkspaceHeader = 256;  // bytes at the start of every workspace: the graph tag word
+// The first 256 bytes of every workspace: three 32-bit words.
+constexpr size_t kWorkspaceHeader = 256;
+constexpr int kHdrGraphTag = 0;  // the tag word of calls recorded into a graph
+constexpr int kHdrPhaseTag = 1;  // the tag of the statistics the last chain_stats call left
+constexpr int kHdrFailures = 2;  // count of bounded waits that ran out (and stale statistics)
 
-// Chain verify, both kernels.
+// Division by a divisor fixed for the launch, without a division sequence:
+// q = (mulhi(n, m) + n) >> s, exact for n < 2^31 (Granlund and Montgomery's
+// method with a 33-bit multiplier whose top bit is implicit).
+struct FastDiv {
+    uint32_t m = 0, s = 0;
+};
+inline FastDiv make_fastdiv(uint32_t d) {  // d >= 1
+    FastDiv f;
+    if (d == 0) return f;
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    f.s = l;
+    f.m = static_cast<uint32_t>(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    return f;
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// Chain verify, all kernels.
 struct ChainArgs {
     const void *target;      // [B][K+1][V]
     const void *draft;       // [B][K][V]
@@ -60,10 +85,17 @@ struct ChainArgs {
     float c;                 // log2(e) / T
     uint32_t tag;            // this call's tag (upper half of every handed-over word)
     const uint32_t *tag_src; // nullable: read the tag from this device word instead (graph replays)
+    uint32_t *hdr;           // the workspace header words
+    bool sample_phase;       // the draws of the two-phase form: statistics carry the phase word's tag
     int32_t chunk, nchunk, nchunk2;  // chunk2 = kChunk2Bytes / element size
-    int32_t lag;             // one-launch form: sequences between a sequence's statistics and its draw
+    // One-launch schedule: S statistics items per sequence that do not read
+    // the bonus row, D draw items per sequence; where the blocks of
+    // statistics and resolvers end, and where the bonus rows' statistics end.
+    uint32_t S, D, blocks_end, bon_end;
+    FastDiv fd_nch, fd_D, fd_S1;
     uint64_t *partial;       // [B][2K+1][nchunk][2] tagged (ref, z); rows 0..K target, K+1.. draft
     uint64_t *sums;          // [B][nchunk2][2] tagged residual and target mass per chunk
+    uint64_t *rec;           // [B][kRecWords] tagged record of each resolve: j, row j's (ref, 1/z) x 2
     int32_t *out_tokens;     // [B][K+1]
     int32_t *out_accepted;   // [B]
     float *out_diag;         // nullable [B][K+1][4]

@@ -2,8 +2,7 @@
 // one-thread kernel before its own, so every replay advances the word in the
 // workspace header and the call's workgroups read their tag from it: no two
 // replays share a tag, as no two host calls do.  Graph tags keep bit 31 set
-// (host tags never do) and skip the values a zeroed word and the phase entry
-// points use.
+// (host tags never do) and never equal 0, the value of a zeroed word.
 #include "plan.hpp"
 
 namespace sv {
@@ -12,7 +11,7 @@ namespace {
 __global__ void k_advance_tag(uint32_t *word) {
     if (threadIdx.x == 0 && blockIdx.x == 0) {
         uint32_t t = (*word & ~kGraphTagBit) + 1u;
-        if (t >= kGraphTagBit || t <= kPhasedTag) t = kPhasedTag + 1u;
+        if (t >= kGraphTagBit) t = 1u;
         *word = t | kGraphTagBit;
     }
 }
