@@ -57,14 +57,12 @@ bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtyp
     p.off_partial = off;
     if (mode == SPEC_MODE_CHAIN) {
         off += align_up(static_cast<size_t>(rows) * p.nchunk * 16);
-        p.chunk2 = kChunk2Bytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
+        p.chunk2 = kDrawChunkBytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
         p.nchunk2 = (V + p.chunk2 - 1) / p.chunk2;
-        // The bonus draw takes the mass of a draw chunk from the statistics
-        // of the two statistics chunks it covers.
-        if (p.chunk2 != 2 * p.chunk || p.nchunk > kMaxStatChunks) return false;
-        // Every draw workgroup of a sequence waits for the sequence's other
-        // chunks, so a sequence's draw workgroups must fit the chip together.
-        if (p.nchunk2 > kMaxDrawChunks) return false;
+        // The bonus draw takes a draw chunk's mass from the statistics of the
+        // same chunk, and a finisher holds two chunks' masses per lane.
+        if (p.chunk2 != p.chunk || p.nchunk > kMaxStatChunks || p.nchunk2 > kMaxDrawChunks)
+            return false;
         if (static_cast<int64_t>(B) * p.nchunk2 > 0x7fffffffLL) return false;
         p.off_sums = off;  // two tagged masses per chunk: residual, target
         off += align_up(static_cast<size_t>(B) * p.nchunk2 * 16);

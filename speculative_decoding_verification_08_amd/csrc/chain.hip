@@ -260,42 +260,52 @@ __device__ __forceinline__ int resolve_local(const ChainArgs &a, int b, uint32_t
     return j;
 }
 
-// Entries per chunk of the residual / bonus pass: 16 KB of one row.
+// Entries per chunk of the residual / bonus pass: 8 KB of one row, in
+// rounds of one 16-byte vector per thread: vector q * kWG + t of the chunk is
+// thread t's q-th, so every load instruction of a wavefront reads 1 KB of
+// consecutive bytes, and index order is round by round, thread by thread.
 template <class DT>
 struct Chunk2 {
-    static constexpr int kElems = kChunk2Bytes / (16 / DT::kVec);
-    static constexpr int kSeg = kElems / kWG;    // contiguous entries per thread
-    static constexpr int kNQ = kSeg / DT::kVec;  // 16-byte vectors per thread and row
-    static constexpr int kRawWords = 4 * kNQ;    // 32-bit words per thread and row
+    static constexpr int kElems = kDrawChunkBytes / (16 / DT::kVec);
+    static constexpr int kNQ = kElems / (kWG * DT::kVec);  // rounds: 16-byte vectors per thread and row
 };
 
-// This thread's entries [s0, s0 + kSeg) of chunk c0 of row j (target, and
-// draft when Resid), as raw 16-byte vectors; entries past the row's end read
-// as -inf.  With V a multiple of the vector width all loads are issued before
-// any is used; otherwise entries are read one by one into the same layout.
+// This thread's vectors of chunk c0 of row j (target, and draft when Resid),
+// raw; entries past the row's end read as -inf.  With V a multiple of the
+// vector width all loads are issued before any is used; otherwise entries are
+// read one by one into the same layout.
 template <class DT, bool VecOk, bool Resid>
 __device__ __forceinline__ void load_chunk(const ChainArgs &a, const DrawRow &w, int64_t c0, int n,
-                                           int s0, uint4 (&rt)[Chunk2<DT>::kNQ],
+                                           uint4 (&rt)[Chunk2<DT>::kNQ],
                                            uint4 (&rd)[Chunk2<DT>::kNQ]) {
     constexpr int VEC = DT::kVec, NQ = Chunk2<DT>::kNQ;
     constexpr uint32_t kInf = NegInf<DT>::kBits;
+    const int tid = threadIdx.x;
     if constexpr (VecOk) {
         const uint4 *tp = static_cast<const uint4 *>(a.target) + (w.trow + c0) / VEC;
         const uint4 *dp = static_cast<const uint4 *>(a.draft) + (w.drow + c0) / VEC;
         const int last = n / VEC - 1;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
-            const int o = min(s0 / VEC + q, last);
+            const int o = min(tid + q * kWG, last);
             rt[q] = tp[o];
             if (Resid) rd[q] = dp[o];
         }
-        if (n < Chunk2<DT>::kElems) {  // the row's last chunk: whole vectors past its end
+        // The row's last chunk: whole vectors past its end read as -inf
+        // (selects, not branches, so the vectors stay in registers).
 #pragma unroll
-            for (int q = 0; q < NQ; ++q)
-                if (s0 + q * VEC >= n) {
-                    rt[q] = make_uint4(kInf, kInf, kInf, kInf);
-                    rd[q] = rt[q];
-                }
+        for (int q = 0; q < NQ; ++q) {
+            const bool in = tid + q * kWG <= last;
+            rt[q].x = in ? rt[q].x : kInf;
+            rt[q].y = in ? rt[q].y : kInf;
+            rt[q].z = in ? rt[q].z : kInf;
+            rt[q].w = in ? rt[q].w : kInf;
+            if (Resid) {
+                rd[q].x = in ? rd[q].x : kInf;
+                rd[q].y = in ? rd[q].y : kInf;
+                rd[q].z = in ? rd[q].z : kInf;
+                rd[q].w = in ? rd[q].w : kInf;
+            }
         }
     } else {
 #pragma unroll
@@ -306,7 +316,7 @@ __device__ __forceinline__ void load_chunk(const ChainArgs &a, const DrawRow &w,
                 uint32_t tb = 0, db = 0;
 #pragma unroll
                 for (int e2 = 0; e2 < VEC / 4; ++e2) {
-                    const int e = s0 + q * VEC + h * (VEC / 4) + e2, ec = min(e, n - 1);
+                    const int e = (tid + q * kWG) * VEC + h * (VEC / 4) + e2, ec = min(e, n - 1);
                     float t = load_one<DT>(a.target, w.trow + c0 + ec);
                     float d = Resid ? load_one<DT>(a.draft, w.drow + c0 + ec) : 0.f;
                     t = e < n ? t : -INFINITY;
@@ -328,7 +338,7 @@ __device__ __forceinline__ void load_chunk(const ChainArgs &a, const DrawRow &w,
     }
 }
 
-// Entry e of a thread's raw words (the layout load_chunk fills), widened.
+// Entry e of one raw 16-byte vector (as 32-bit words), widened.
 template <class DT>
 __device__ __forceinline__ float raw_entry(const uint32_t *words, int e) {
     if constexpr (DT::kVec == 8) {
@@ -341,30 +351,33 @@ __device__ __forceinline__ float raw_entry(const uint32_t *words, int e) {
 
 // ------------------------------------------------------------ draw item
 
-// Row j's entries of this workgroup's chunk, as draw weights: per-thread
-// sums of p and (with Resid) of max(0, p - q), the raw entries staying in
-// registers for the crossing search.
+// Row j's entries of this workgroup's chunk, as draw weights: per-thread,
+// per-round sums of p and (with Resid) of max(0, p - q), the raw entries
+// staying in registers for the crossing search.
 template <class DT, bool VecOk, bool Resid>
 __device__ __forceinline__ void chunk_weights(const ChainArgs &a, const DrawRow &w, int64_t c0, int n,
-                                              int s0, uint4 (&rt)[Chunk2<DT>::kNQ],
-                                              uint4 (&rd)[Chunk2<DT>::kNQ], float &lp, float &lr) {
+                                              uint4 (&rt)[Chunk2<DT>::kNQ],
+                                              uint4 (&rd)[Chunk2<DT>::kNQ],
+                                              float (&lp)[Chunk2<DT>::kNQ],
+                                              float (&lr)[Chunk2<DT>::kNQ]) {
     constexpr int VEC = DT::kVec, NQ = Chunk2<DT>::kNQ;
-    load_chunk<DT, VecOk, Resid>(a, w, c0, n, s0, rt, rd);
-    lp = 0.f;
-    lr = 0.f;
+    load_chunk<DT, VecOk, Resid>(a, w, c0, n, rt, rd);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         float t[VEC], d[VEC];
         unpack<DT>(rt[q], t);
         if (Resid) unpack<DT>(rd[q], d);
+        float sp = 0.f, sr = 0.f;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
             const float p = weight_p(t[i], a.c, w);
-            lp += p;
-            if (Resid) lr += weight_r(p, d[i], a.c, w);
+            sp += p;
+            if (Resid) sr += weight_r(p, d[i], a.c, w);
         }
-        asm volatile("" : "+v"(lp), "+v"(lr));  // one slot at a time
+        lp[q] = sp;
+        lr[q] = sr;
     }
+    // The raw entries stay in registers for the crossing search.
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
         asm volatile("" : "+v"(rt[q].x), "+v"(rt[q].y), "+v"(rt[q].z), "+v"(rt[q].w));
@@ -372,20 +385,67 @@ __device__ __forceinline__ void chunk_weights(const ChainArgs &a, const DrawRow 
     }
 }
 
-// Wavefront 0: from the chunk masses of the sequence (lane i: chunk i), the
-// total S, tau = u * S and the crossing chunk -- the first whose inclusive
-// running mass exceeds tau (the inverse CDF, strict), else the last chunk
-// with mass -- with the running mass before it.
-__device__ __forceinline__ void crossing_chunk(float m, bool in, float us, float &S, float &tau,
+// Exclusive prefix sums in index order (round by round, thread by thread) of
+// two kinds of per-thread, per-round masses, and the chunk's two totals; every
+// thread gets the totals.  A fixed order, so the draw item that publishes a
+// chunk's masses and the workgroup that searches the chunk agree bit for bit.
+template <int NQ>
+__device__ __forceinline__ void round_scan2(const float (&x)[NQ], const float (&y)[NQ],
+                                            float (&ex)[NQ], float (&ey)[NQ], float &tx, float &ty) {
+    __shared__ float s_t[2][NQ][kWaves];
+    float ix[NQ], iy[NQ];
+    const int w = threadIdx.x / kWave;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        ix[q] = wave_incl_sum(x[q]);
+        iy[q] = wave_incl_sum(y[q]);
+        if (threadIdx.x % kWave == kWave - 1) {
+            s_t[0][q][w] = ix[q];
+            s_t[1][q][w] = iy[q];
+        }
+    }
+    __syncthreads();
+    tx = 0.f;
+    ty = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        float bx = 0.f, by = 0.f;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+            if (k == w) {
+                bx = tx;
+                by = ty;
+            }
+            tx += s_t[0][q][k];
+            ty += s_t[1][q][k];
+        }
+        ex[q] = bx + wave_excl_from_incl(ix[q]);
+        ey[q] = by + wave_excl_from_incl(iy[q]);
+    }
+}
+
+// Wavefront 0: from the chunk masses of the sequence (lane i: chunks 2i and
+// 2i + 1, m0 and m1, zero past the last chunk), the total S, tau = u * S and
+// the crossing chunk -- the first whose inclusive running mass exceeds tau
+// (the inverse CDF, strict), else the last chunk with mass -- with the
+// running mass before it.
+__device__ __forceinline__ void crossing_chunk(float m0, float m1, float us, float &S, float &tau,
                                                int &cstar, float &base) {
-    const float incl = wave_incl_sum(m);
+    const float incl = wave_incl_sum(m0 + m1);
     S = wave_last(incl);
     tau = us * S;
     const float excl = wave_excl_from_incl(incl);
-    const uint64_t cross = __ballot(in && incl > tau), pos = __ballot(in && m > 0.f);
-    cstar = cross ? __ffsll(static_cast<unsigned long long>(cross)) - 1
-                  : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
-    base = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), cstar));
+    const uint64_t cross = __ballot(incl > tau), pos = __ballot(m0 > 0.f || m1 > 0.f);
+    const int l = cross ? __ffsll(static_cast<unsigned long long>(cross)) - 1
+                        : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
+    const float e = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(excl), l));
+    const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m0), l));
+    const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m1), l));
+    // The pair's first chunk crosses if its own running mass passes tau;
+    // without a crossing, the pair's last chunk with mass is taken.
+    const bool second = cross ? !(e + a0 > tau) : a1 > 0.f;
+    cstar = 2 * l + (second ? 1 : 0);
+    base = second ? e + a0 : e;
 }
 
 // A sequence whose bounded wait ran out, or whose statistics were not left
@@ -401,44 +461,55 @@ __device__ __forceinline__ void fail_sequence(const ChainArgs &a, int b) {
 }
 
 // The search inside the crossing chunk (entries [c0, c0 + C2) of row j) and
-// the emission.  The first thread whose running mass passes tau (else the last
-// thread with mass) hands its raw entries to wavefront 0 through LDS; lane e
-// takes entry e of that thread's segment, and the first entry whose running
+// the emission.  The first vector (index order) whose running mass passes tau
+// (else the last vector with mass) is handed by its thread to wavefront 0
+// through LDS; lane e takes entry e of it, and the first entry whose running
 // mass exceeds tau (else the last with weight) is the drawn token.  Wavefront
-// 0 writes x_0..x_{j-1}, the drawn token, then -1.  `start` and `l` are this
-// thread's running mass before its segment and its segment's mass.
+// 0 writes x_0..x_{j-1}, the drawn token, then -1.  `start[q]` and `l[q]` are
+// the running mass before this thread's vector of round q and its mass.
 template <class DT, bool Resid>
 __device__ __forceinline__ void search_emit(const ChainArgs &a, int b, int64_t c0, int j,
-                                            const DrawRow &w, bool resid, float tau, float start,
-                                            float l, const uint4 (&rt)[Chunk2<DT>::kNQ],
+                                            const DrawRow &w, bool resid, float tau,
+                                            const float (&start)[Chunk2<DT>::kNQ],
+                                            const float (&l)[Chunk2<DT>::kNQ],
+                                            const uint4 (&rt)[Chunk2<DT>::kNQ],
                                             const uint4 (&rd)[Chunk2<DT>::kNQ], float S,
                                             int32_t my_tok, float *lds) {
-    constexpr int kSeg = Chunk2<DT>::kSeg, NQ = Chunk2<DT>::kNQ;
+    constexpr int VEC = DT::kVec, NQ = Chunk2<DT>::kNQ;
+    static_assert(VEC <= kWave, "one lane per entry of a vector");
     const int K = a.K, tid = threadIdx.x, lane = tid % kWave;
-    int tf, tl;
-    wg_min_max(l > 0.f && start + l > tau ? tid : INT32_MAX, l > 0.f ? tid : -1, tf, tl);
-    const int ts = tf != INT32_MAX ? tf : max(tl, 0);
-    uint32_t *s_raw = reinterpret_cast<uint32_t *>(lds + kDrawRawAt);
-    float *s_start = lds + kDrawRawAt + 2 * kDrawRawWords;
-    if (tid == ts) {
+    int cand = INT32_MAX, last = -1;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            reinterpret_cast<uint4 *>(s_raw)[q] = rt[q];
-            if (Resid) reinterpret_cast<uint4 *>(s_raw + kDrawRawWords)[q] = rd[q];
+    for (int q = NQ - 1; q >= 0; --q) {
+        if (l[q] > 0.f && start[q] + l[q] > tau) cand = q * kWG + tid;
+        if (l[q] > 0.f && last < 0) last = q * kWG + tid;
+    }
+    int vf, vl;
+    wg_min_max(cand, last, vf, vl);
+    const int vs = vf != INT32_MAX ? vf : max(vl, 0);  // the vector searched, index in the chunk
+    uint32_t *s_raw = reinterpret_cast<uint32_t *>(lds + kDrawRawAt);
+    float *s_start = lds + kDrawRawAt + 8;
+    // The owner of vector vs stores its round vs / kWG: one store per round,
+    // under a uniform condition, so no register array is indexed at run time.
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        if (vs / kWG == q && tid == vs % kWG) {
+            reinterpret_cast<uint4 *>(s_raw)[0] = rt[q];
+            if (Resid) reinterpret_cast<uint4 *>(s_raw)[1] = rd[q];
+            *s_start = start[q];
         }
-        *s_start = start;
     }
     __syncthreads();
     if (tid >= kWave) return;
-    const int e = min(lane, kSeg - 1);
+    const int e = min(lane, VEC - 1);
     float x = weight_p(raw_entry<DT>(s_raw, e), a.c, w);
-    if (Resid && resid) x = weight_r(x, raw_entry<DT>(s_raw + kDrawRawWords, e), a.c, w);
-    x = lane < kSeg ? x : 0.f;
+    if (Resid && resid) x = weight_r(x, raw_entry<DT>(s_raw + 4, e), a.c, w);
+    x = lane < VEC ? x : 0.f;
     const float run = *s_start + wave_incl_sum(x);
     const uint64_t f = __ballot(x > 0.f && run > tau), nz = __ballot(x > 0.f);
     const int pick = f ? __ffsll(static_cast<unsigned long long>(f)) - 1
                        : (nz ? 63 - __clzll(static_cast<long long>(nz)) : 0);
-    const int32_t token = static_cast<int32_t>(c0 + ts * kSeg + pick);
+    const int32_t token = static_cast<int32_t>(c0 + static_cast<int64_t>(vs) * VEC + pick);
     for (int k = lane; k <= K; k += kWave) {
         int32_t o = -1;
         if (k < j) o = my_tok;  // k < j <= K <= 64: k is this lane
@@ -533,7 +604,7 @@ __device__ __forceinline__ bool read_record(const ChainArgs &a, int b, uint32_t 
 template <class DT, bool VecOk>
 __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, float *lds) {
     using CK = Chunk2<DT>;
-    constexpr int C2 = CK::kElems, kSeg = CK::kSeg, NQ = CK::kNQ;
+    constexpr int C2 = CK::kElems, NQ = CK::kNQ;
     const int K = a.K, tid = threadIdx.x;
     uint32_t ptag, tag;
     item_tags(a, ptag, tag);
@@ -546,9 +617,9 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
     const int64_t c0 = static_cast<int64_t>(ch) * C2;
     const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(a.V) - c0));
     uint4 rt[NQ], rd[NQ];
-    float lp, lr, ex_r, ex_p, mr, mp;
-    chunk_weights<DT, VecOk, true>(a, w, c0, n, tid * kSeg, rt, rd, lp, lr);
-    wg_excl_scan2(lr, lp, ex_r, ex_p, mr, mp);
+    float lp[NQ], lr[NQ], ex_r[NQ], ex_p[NQ], mr, mp;
+    chunk_weights<DT, VecOk, true>(a, w, c0, n, rt, rd, lp, lr);
+    round_scan2<NQ>(lr, lp, ex_r, ex_p, mr, mp);
     if (tid == 0) {
         uint64_t *sums = a.sums + 2 * (static_cast<int64_t>(b) * a.nchunk2 + ch);
         publish_f32(sums, tag, mr);
@@ -565,10 +636,8 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
 template <class DT, bool VecOk>
 __device__ __forceinline__ void finisher_item(const ChainArgs &a, int b, float *lds) {
     using CK = Chunk2<DT>;
-    constexpr int C2 = CK::kElems, kSeg = CK::kSeg, NQ = CK::kNQ;
-    static_assert(kSeg <= kWave, "one lane per entry of a thread's segment");
-    static_assert(CK::kRawWords <= kDrawRawWords, "a thread's raw entries fit the LDS");
-    static_assert(kMaxDrawChunks <= kWave, "one lane per chunk of a sequence");
+    constexpr int C2 = CK::kElems, NQ = CK::kNQ;
+    static_assert(kMaxDrawChunks <= 2 * kWave, "two chunks per lane of a sequence");
     const int K = a.K, tid = threadIdx.x, lane = tid % kWave, nc = a.nchunk2;
     __shared__ float s_tau, s_base, s_S;
     __shared__ int s_cstar, s_resid, s_ok;
@@ -590,23 +659,27 @@ __device__ __forceinline__ void finisher_item(const ChainArgs &a, int b, float *
     w.drow = (static_cast<int64_t>(b) * K + j) * a.V;
     if (tid < kWave) {
         const uint64_t *sums = a.sums + 2 * static_cast<int64_t>(b) * nc;
-        const int i = min(lane, nc - 1);
-        uint64_t vr, vp;
+        const int i0 = min(2 * lane, nc - 1), i1 = min(2 * lane + 1, nc - 1);
+        const bool in0 = 2 * lane < nc, in1 = 2 * lane + 1 < nc;
+        uint64_t w[4];
         bool fresh;
         const uint64_t t0 = wall_clock64();
         for (;;) {
-            vr = fetch(&sums[2 * i]);
-            vp = fetch(&sums[2 * i + 1]);
-            fresh = __all(current(vr, tag) && current(vp, tag));
+            w[0] = fetch(&sums[2 * i0]);
+            w[1] = fetch(&sums[2 * i0 + 1]);
+            w[2] = fetch(&sums[2 * i1]);
+            w[3] = fetch(&sums[2 * i1 + 1]);
+            fresh = __all(current(w[0], tag) && current(w[1], tag) && current(w[2], tag) &&
+                          current(w[3], tag));
             if (fresh || wall_clock64() - t0 > kWaitTicks) break;
             __builtin_amdgcn_s_sleep(8);
         }
-        const bool in = lane < nc;
-        const float m_r = in ? word_f32(vr) : 0.f, m_p = in ? word_f32(vp) : 0.f;
-        const bool resid = wave_last(wave_incl_sum(m_r)) > 0.f;
+        const float r0 = in0 ? word_f32(w[0]) : 0.f, p0 = in0 ? word_f32(w[1]) : 0.f;
+        const float r1 = in1 ? word_f32(w[2]) : 0.f, p1 = in1 ? word_f32(w[3]) : 0.f;
+        const bool resid = wave_last(wave_incl_sum(r0 + r1)) > 0.f;
         float S, tau, base;
         int cstar;
-        crossing_chunk(resid ? m_r : m_p, in, us, S, tau, cstar, base);
+        crossing_chunk(resid ? r0 : p0, resid ? r1 : p1, us, S, tau, cstar, base);
         if (lane == 0) {
             s_ok = fresh;
             s_cstar = cstar;
@@ -626,11 +699,15 @@ __device__ __forceinline__ void finisher_item(const ChainArgs &a, int b, float *
     const int64_t c0 = static_cast<int64_t>(ch) * C2;
     const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(a.V) - c0));
     uint4 rt[NQ], rd[NQ];
-    float lp, lr, ex_r, ex_p, mr, mp;
-    chunk_weights<DT, VecOk, true>(a, w, c0, n, tid * kSeg, rt, rd, lp, lr);
-    wg_excl_scan2(lr, lp, ex_r, ex_p, mr, mp);
-    search_emit<DT, true>(a, b, c0, j, w, resid, s_tau, s_base + (resid ? ex_r : ex_p),
-                          resid ? lr : lp, rt, rd, s_S, my_tok, lds);
+    float lp[NQ], lr[NQ], ex_r[NQ], ex_p[NQ], mr, mp, start[NQ], l[NQ];
+    chunk_weights<DT, VecOk, true>(a, w, c0, n, rt, rd, lp, lr);
+    round_scan2<NQ>(lr, lp, ex_r, ex_p, mr, mp);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        start[q] = s_base + (resid ? ex_r[q] : ex_p[q]);
+        l[q] = resid ? lr[q] : lp[q];
+    }
+    search_emit<DT, true>(a, b, c0, j, w, resid, s_tau, start, l, rt, rd, s_S, my_tok, lds);
 }
 
 // The bonus row's statistics of sequence b, on wavefront 0: per statistics
@@ -697,7 +774,7 @@ __device__ __forceinline__ bool bonus_row(const ChainArgs &a, int b, uint32_t pt
 template <class DT, bool VecOk, bool Live>
 __device__ __forceinline__ void bonus_item(const ChainArgs &a, int b, float *lds) {
     using CK = Chunk2<DT>;
-    constexpr int C2 = CK::kElems, kSeg = CK::kSeg, NQ = CK::kNQ;
+    constexpr int C2 = CK::kElems, NQ = CK::kNQ;
     const int K = a.K, tid = threadIdx.x, lane = tid % kWave, nc = a.nchunk2;
     __shared__ float s_tau, s_base, s_S;
     __shared__ int s_cstar;
@@ -723,16 +800,15 @@ __device__ __forceinline__ void bonus_item(const ChainArgs &a, int b, float *lds
     w.drow = 0;
     w.rd = w.izd = 0.f;
     if (tid < kWave) {
-        // Draw chunk i covers statistics chunks 2i and 2i + 1 (the last draw
-        // chunk of a row may cover one).
+        // A draw chunk is a statistics chunk: its mass of p_K follows from
+        // the chunk's (ref, z).
         const float *s_kref = lds + kDrawBonusAt, *s_kz = s_kref + kMaxStatChunks;
-        const bool in = lane < nc;
-        const int i = min(lane, nc - 1), i0 = 2 * i, i1 = min(2 * i + 1, a.nchunk - 1);
-        const float z1 = i1 > i0 ? s_kz[i1] * exp2_hw(s_kref[i1] - w.rt) : 0.f;
-        const float m = in ? __fmul_rn(s_kz[i0] * exp2_hw(s_kref[i0] - w.rt) + z1, w.izt) : 0.f;
+        const int i0 = min(2 * lane, nc - 1), i1 = min(2 * lane + 1, nc - 1);
+        const float m0 = 2 * lane < nc ? __fmul_rn(s_kz[i0] * exp2_hw(s_kref[i0] - w.rt), w.izt) : 0.f;
+        const float m1 = 2 * lane + 1 < nc ? __fmul_rn(s_kz[i1] * exp2_hw(s_kref[i1] - w.rt), w.izt) : 0.f;
         float S, tau, base;
         int cstar;
-        crossing_chunk(m, in, us, S, tau, cstar, base);
+        crossing_chunk(m0, m1, us, S, tau, cstar, base);
         if (lane == 0) {
             s_cstar = cstar;
             s_base = base;
@@ -745,10 +821,12 @@ __device__ __forceinline__ void bonus_item(const ChainArgs &a, int b, float *lds
     const int64_t c0 = static_cast<int64_t>(ch) * C2;
     const int n = static_cast<int>(min(static_cast<int64_t>(C2), static_cast<int64_t>(a.V) - c0));
     uint4 rt[NQ], rd[NQ];
-    float lp, lr, ex_r, ex_p, mr, mp;
-    chunk_weights<DT, VecOk, false>(a, w, c0, n, tid * kSeg, rt, rd, lp, lr);
-    wg_excl_scan2(0.f, lp, ex_r, ex_p, mr, mp);
-    search_emit<DT, false>(a, b, c0, K, w, false, s_tau, s_base + ex_p, lp, rt, rd, s_S, my_tok, lds);
+    float lp[NQ], lr[NQ], ex_r[NQ], ex_p[NQ], mr, mp, start[NQ];
+    chunk_weights<DT, VecOk, false>(a, w, c0, n, rt, rd, lp, lr);
+    round_scan2<NQ>(lr, lp, ex_r, ex_p, mr, mp);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) start[q] = s_base + ex_p[q];
+    search_emit<DT, false>(a, b, c0, K, w, false, s_tau, start, lp, rt, rd, s_S, my_tok, lds);
 }
 
 // Grid (chunk, row, sequence): the hardware hands out the item, so nothing

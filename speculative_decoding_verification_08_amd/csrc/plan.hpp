@@ -15,18 +15,20 @@ constexpr int kChunk2Bytes = 16384;  // bytes of one row per chunk of the residu
 constexpr int kStatVecs = 2;
 constexpr int kStatChunkBytes = kStatVecs * 16 * 256;
 constexpr int kMaxStatChunks = 128;  // statistics chunks per row: V <= 128 x 8 KB of entries
+// The draws' chunks are the statistics chunks: 8 KB of a row, two 16-byte
+// vectors per thread.
+constexpr int kDrawChunkBytes = kStatChunkBytes;
 // Workgroups of 256 threads the chip holds at once (256 CUs, 8 each): the
 // top-k merges trail their rows' chunks by about this many workgroups.
 constexpr int kResidentWGs = 2048;
 constexpr int kRecWords = 8;       // words per sequence record (five used)
-constexpr int kMaxDrawChunks = 64;  // draw chunks per row: V <= 64 x 16 KB of entries
-// LDS words of a draw workgroup: its sequence's row statistics (ref, z), one
-// thread's raw entries of the crossing chunk (16 words per row, target and
-// draft) and that thread's running mass, then the bonus row's statistics
-// (ref, z) per statistics chunk.
-constexpr int kDrawRawWords = 16;
+constexpr int kMaxDrawChunks = kMaxStatChunks;  // draw chunks per row (two per lane of a wavefront)
+// LDS words of a draw workgroup: its sequence's row statistics (ref, z), the
+// vector searched in the crossing chunk (4 words per row, target and draft)
+// and its running mass, then the bonus row's statistics (ref, z) per
+// statistics chunk.
 constexpr int kDrawRawAt = (2 * (2 * kMaxK + 1) + 3) / 4 * 4;  // 16-byte aligned
-constexpr int kDrawBonusAt = kDrawRawAt + 2 * kDrawRawWords + 4;
+constexpr int kDrawBonusAt = kDrawRawAt + 12;
 constexpr int kDrawLds = kDrawBonusAt + 2 * kMaxStatChunks;
 
 // How a launch cuts the rows it streams into vocabulary chunks, and where its
