@@ -35,7 +35,7 @@ _lib = None
 def build(out_path: str = _LIB, src_path: str = _SRC, extra_flags=()) -> str:
     """Compile the oracle with gcc: plain IEEE double arithmetic, no FMA contraction."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", *extra_flags, "-o", out_path + ".tmp",
+           "-fno-fast-math", "-fopenmp", "-Wall", "-Wextra", *extra_flags, "-o", out_path + ".tmp",
            src_path, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(out_path + ".tmp", out_path)
@@ -71,7 +71,19 @@ def _bind(lib):
     lib.oracle_kv_commit.restype = i
     lib.oracle_tree_mask.argtypes = [vp, vp, i, i, vp, vp]
     lib.oracle_tree_mask.restype = i
+    lib.oracle_set_threads.argtypes = [i]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_get_threads.argtypes = []
+    lib.oracle_get_threads.restype = i
     return lib
+
+
+def set_threads(n: int, *, lib=None) -> int:
+    """Threads the oracle spreads sequences over (n <= 0: every processor).
+    Returns the count now in force.  Results do not depend on it."""
+    lib = lib or load()
+    lib.oracle_set_threads(int(n))
+    return lib.oracle_get_threads()
 
 
 def load(path: str | None = None):

@@ -11,8 +11,10 @@ Chain verify (T > 0):
       1e-5*S of the running sums that separate the two tokens (the end of the
       lower token's interval and the start of the higher one's), and the GPU's
       token has positive weight;
-  - p_k(x_k), q_k(x_k) and the drawn mass S agree to 1e-5 relative (plus an
-    absolute floor of 1e-30, below which fp32 has no normal numbers to spare).
+  - p_k(x_k), q_k(x_k) and the drawn mass S agree to 1e-5 relative, plus an
+    absolute floor of 2^-126 (about 1.2e-38), the smallest normal fp32 number:
+    below it the GPU's fp32 probabilities are subnormal or flushed to zero, so
+    no relative match is possible there.
 Greedy chain and tree verify: every output matches exactly.
 """
 from __future__ import annotations
@@ -27,7 +29,7 @@ from . import (draw_weights, topk, verify_chain, verify_greedy, verify_tree_gree
 REL = 1e-5
 RATIO_BAND = 1e-6
 CDF_BAND = 1e-5
-ABS_FLOOR = 1e-30
+ABS_FLOOR = float(np.finfo(np.float32).tiny)   # 2^-126
 
 
 def _close(g, o, rel=REL):

@@ -13,6 +13,9 @@
  * letters; its formulas are read with the letters exchanged back.
  *
  * Everything is computed in double precision with scalar loops in index order.
+ * Sequences (rows, trees) are independent: with OpenMP they are spread over
+ * threads, and each one's arithmetic is exactly the single-threaded one, so
+ * the results are bitwise the same at any thread count.
  * bf16 inputs are widened exactly (bf16 bits become the top half of an fp32,
  * which is then converted to double); fp32 inputs and the caller's uniforms are
  * promoted to double.  Build with -ffp-contract=off and without fast-math so
@@ -34,12 +37,24 @@
  *     sequence for whichever draw (residual or bonus) ends the step.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 enum { OR_F32 = 0, OR_BF16 = 1 };
 enum { OR_OK = 0, OR_BAD_ARG = 1, OR_NO_MEMORY = 2 };
+
+/* Threads the parallel loops over sequences use (0 or less: OpenMP's default). */
+void oracle_set_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
+}
+
+int oracle_get_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* One logit, widened to double.  bf16 is the upper 16 bits of an IEEE fp32. */
 static double logit_at(const void *base, int dtype, size_t idx)
@@ -248,15 +263,19 @@ int oracle_verify_chain_f64u(const void *target, const void *draft, int dtype,
 {
     if (!chain_args_ok(target, draft, dtype, x, B, K, V, T))
         return OR_BAD_ARG;
+    int rc = OR_OK;
+#pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
-        int rc = chain_one(target, draft, dtype, (size_t)b, x + (size_t)b * K,
-                           ua + (size_t)b * K, us[b], K, V, T,
-                           out_tokens + (size_t)b * (K + 1), out_accepted + b,
-                           out_diag ? out_diag + (size_t)b * 4 * (K + 1) : NULL);
-        if (rc != OR_OK)
-            return rc;
+        int r = chain_one(target, draft, dtype, (size_t)b, x + (size_t)b * K,
+                          ua + (size_t)b * K, us[b], K, V, T,
+                          out_tokens + (size_t)b * (K + 1), out_accepted + b,
+                          out_diag ? out_diag + (size_t)b * 4 * (K + 1) : NULL);
+        if (r != OR_OK) {
+#pragma omp critical
+            rc = r;
+        }
     }
-    return OR_OK;
+    return rc;
 }
 
 /* Same, with the float32 uniforms the GPU library takes. */
@@ -411,6 +430,7 @@ int oracle_verify_greedy(const void *target, int dtype, const int32_t *x, int B,
         return OR_BAD_ARG;
     if (B > 0 && (!target || !out_tokens || !out_accepted || (K > 0 && !x)))
         return OR_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
         int32_t *out = out_tokens + (size_t)b * (K + 1);
         int j = K;
@@ -461,10 +481,9 @@ int oracle_verify_tree_greedy(const void *node_logits, int dtype, const int32_t 
     if (B > 0 && (!node_logits || !node_tokens || !out_tokens || !out_depth))
         return OR_BAD_ARG;
 
-    int *depth = (int *)malloc(sizeof(int) * (size_t)N * 4);
+    int *depth = (int *)malloc(sizeof(int) * (size_t)N);
     if (!depth)
         return OR_NO_MEMORY;
-    int *ok = depth + N, *amax = depth + 2 * N, *path = depth + 3 * N;
     int D = 0;
     depth[0] = 0;
     for (int v = 1; v < N; ++v) {
@@ -472,7 +491,16 @@ int oracle_verify_tree_greedy(const void *node_logits, int dtype, const int32_t 
         if (depth[v] > D)
             D = depth[v];
     }
+    int rc = OR_OK;
+#pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
+        int *ok = (int *)malloc(sizeof(int) * (size_t)N * 3);
+        if (!ok) {
+#pragma omp critical
+            rc = OR_NO_MEMORY;
+            continue;
+        }
+        int *amax = ok + N, *path = ok + 2 * N;
         for (int v = 0; v < N; ++v)
             amax[v] = row_argmax(node_logits, dtype, (size_t)b * N + (size_t)v, V);
         ok[0] = 1;
@@ -499,9 +527,10 @@ int oracle_verify_tree_greedy(const void *node_logits, int dtype, const int32_t 
                 op[i] = i <= d ? path[i] : -1;
         }
         out_depth[b] = d;
+        free(ok);
     }
     free(depth);
-    return OR_OK;
+    return rc;
 }
 
 /*
@@ -540,11 +569,16 @@ int oracle_verify_tree_greedy_dyn(const void *node_logits, int dtype, const int3
             if (par[v] < 0 || par[v] >= v)
                 return OR_BAD_ARG;
     }
-    int *dep = (int *)malloc(sizeof(int) * (size_t)Nmax * 4);
-    if (!dep)
-        return OR_NO_MEMORY;
-    int *acc = dep + Nmax, *am = dep + 2 * Nmax, *route = dep + 3 * Nmax;
+    int rc = OR_OK;
+#pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
+        int *dep = (int *)malloc(sizeof(int) * (size_t)Nmax * 4);
+        if (!dep) {
+#pragma omp critical
+            rc = OR_NO_MEMORY;
+            continue;
+        }
+        int *acc = dep + Nmax, *am = dep + 2 * Nmax, *route = dep + 3 * Nmax;
         const int32_t *par = parents + (size_t)b * Nmax;
         const int32_t *tok = node_tokens + (size_t)b * Nmax;
         const int n = node_count[b];
@@ -574,9 +608,9 @@ int oracle_verify_tree_greedy_dyn(const void *node_logits, int dtype, const int3
                 op[i] = i <= d ? route[i] : -1;
         }
         out_depth[b] = d;
+        free(dep);
     }
-    free(dep);
-    return OR_OK;
+    return rc;
 }
 
 /*
@@ -596,6 +630,7 @@ int oracle_topk(const void *logits, int dtype, int rows, int V, int k, int32_t *
         return OR_BAD_ARG;
     if (rows > 0 && (!logits || !out_idx))
         return OR_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
     for (int r = 0; r < rows; ++r) {
         int taken[8];
         for (int q = 0; q < k; ++q) {

@@ -1,6 +1,10 @@
 import os
 import sys
 
+# The oracle spreads sequences over OpenMP threads; idle threads sleep rather
+# than spin, so that several test processes can share the cores.
+os.environ.setdefault("OMP_WAIT_POLICY", "PASSIVE")
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)

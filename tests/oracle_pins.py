@@ -231,6 +231,31 @@ def pin_strict_acceptance(lib):
     assert acc[0] == 0 and out[0, 0] != 1
 
 
+def pin_zero_draft_probability(lib):
+    """A drafted token the draft gives zero probability (Arabic lesson "Speculative
+    decoding: draft, verify, repeat", "Build it" step 1: a zero draft probability
+    makes the ratio infinite, so the token is accepted whatever u is) -- unless the
+    target gives it zero probability too, when it is rejected: a token the target
+    cannot emit never is (the output law is p).  Reachable through -inf draft
+    logits.  The replacement after such a rejection never is the drafted token."""
+    V, B = 5, 6
+    ninf = np.float32(-np.inf)
+    rng = np.random.default_rng(37)
+    tl = rng.standard_normal((B, 2, V)).astype(np.float32)
+    dl = rng.standard_normal((B, 1, V)).astype(np.float32)
+    tokens = np.full((B, 1), 2, np.int32)
+    dl[:, 0, 2] = ninf                                     # q(x) = 0
+    ua = np.array([[0.0], [0.5], [0.99999994], [0.25], [0.75], [0.9]], np.float32)
+    us = rng.random((B,), dtype=np.float32)
+    out, acc, d = oracle.verify_chain(tl, dl, tokens, ua, us, 1.0, diag=True, lib=lib)
+    assert np.all(acc == 1) and np.all(out[:, 0] == 2), (acc, out)
+    assert np.all(d[:, 0, 1] == 0.0) and np.all(d[:, 0, 0] > 0.0) and np.all(np.isinf(d[:, 0, 2]))
+    tl[:, 0, 2] = ninf                                     # p(x) = 0 as well
+    out, acc, d = oracle.verify_chain(tl, dl, tokens, ua, us, 1.0, diag=True, lib=lib)
+    assert np.all(acc == 0) and np.all(out[:, 0] != 2) and np.all(out[:, 0] >= 0), (acc, out)
+    assert np.all(d[:, 0, :3] == 0.0)
+
+
 # ------------------------------------------------------------- softmax values
 
 def pin_softmax_values(lib):
@@ -252,6 +277,31 @@ def pin_softmax_values(lib):
         want = 1.0 / (na + nb * np.exp((b - a) / T))
         assert abs(d[0, 0, 0] - want) <= 1e-14 * want, (T, d[0, 0, 0], want)
         assert abs(d[0, 0, 1] - 1.0 / (na + nb)) <= 1e-15
+
+
+def pin_row_helpers(lib):
+    """The single-row helpers: softmax_row is p = softmax(l / T) (constant row ->
+    1/V exactly; two-level row -> closed form; -inf entries -> 0) and row_argmax is
+    numpy's argmax over the widened values (first index among ties, -0.0 ties +0.0)."""
+    for T in (1.0, 0.7, 2.5):
+        p = oracle.softmax_row(np.full(9, -0.625, np.float32), T, lib=lib)
+        assert np.all(p == 1.0 / 9)
+        a, b, na, nb = 1.5, -0.5, 3, 9
+        row = np.array([a] * na + [b] * nb + [-np.inf], np.float32)
+        p = oracle.softmax_row(row, T, lib=lib)
+        pa = 1.0 / (na + nb * np.exp((b - a) / T))
+        assert np.all(np.abs(p[:na] - pa) <= 1e-15 * pa) and p[-1] == 0.0
+        assert np.all(np.abs(p[na:na + nb] - pa * np.exp((b - a) / T)) <= 1e-15)
+        pb = oracle.softmax_row(bf16_bits(row), T, lib=lib)          # bf16 widened exactly
+        assert np.array_equal(pb, p)
+    rng = np.random.default_rng(47)
+    for dtype in ("f32", "bf16"):
+        for _ in range(20):
+            v = rng.integers(-3, 4, 50).astype(np.float32)          # many ties
+            v[rng.random(50) < 0.1] = -0.0
+            r = bf16_bits(v) if dtype == "bf16" else v
+            assert oracle.row_argmax(r, lib=lib) == int(np.argmax(widen(r)))
+    assert oracle.row_argmax(np.array([-0.0, 0.0, -1.0], np.float32), lib=lib) == 0
 
 
 def pin_helper_closed_forms(lib):
@@ -762,7 +812,7 @@ def pin_chi_square(lib, n=50_000, seed=19):
 
 
 ALL_PINS = [pin_exact_law, pin_expected_tokens, pin_page_counts, pin_strict_acceptance,
-            pin_softmax_values, pin_helper_closed_forms,
+            pin_zero_draft_probability, pin_softmax_values, pin_row_helpers, pin_helper_closed_forms,
             pin_inverse_cdf, pin_greedy, pin_tree_bruteforce, pin_tree_chain,
             pin_tree_figure, pin_tree_dyn_bruteforce, pin_tree_dyn_padding, pin_tree_dyn_chain,
             pin_topk_sort, pin_topk_argmax, pin_kv_rollback_exercise, pin_kv_commit_tree_path,

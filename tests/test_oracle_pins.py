@@ -68,6 +68,9 @@ MUTANTS = [
     ("residual positive part dropped", "w[i] = d > 0.0 ? d : 0.0;", "w[i] = d;", 0),
     ("acceptance ratio inverted", "return u < P / Q;", "return u < Q / P;", 0),
     ("non-strict acceptance", "return u < P / Q;", "return u <= P / Q;", 0),
+    ("zero draft probability always rejects", "    return P > 0.0;\n}", "    return 0;\n}", 0),
+    ("zero draft probability accepts whatever p", "    return P > 0.0;\n}", "    return 1;\n}", 0),
+    ("single-row softmax ignores the temperature", "    softmax_T(l, V, T, out_p);", "    softmax_T(l, V, 1.0, out_p);", 0),
     ("temperature ignored", "p[i] = exp((l[i] - m) / T);", "p[i] = exp(l[i] - m);", 0),
     ("bonus from row K-1", "seq * (size_t)(K + 1) + (size_t)K, V, l);",
      "seq * (size_t)(K + 1) + (size_t)(K > 0 ? K - 1 : 0), V, l);", 0),
@@ -115,7 +118,8 @@ MUTANTS = [
 ]
 
 QUICK_PINS = [P.pin_exact_law, P.pin_expected_tokens, P.pin_page_counts, P.pin_strict_acceptance,
-              P.pin_softmax_values, P.pin_helper_closed_forms,
+              P.pin_zero_draft_probability, P.pin_softmax_values, P.pin_row_helpers,
+              P.pin_helper_closed_forms,
               P.pin_inverse_cdf, P.pin_greedy, P.pin_tree_bruteforce, P.pin_tree_figure,
               P.pin_tree_dyn_bruteforce, P.pin_tree_dyn_padding, P.pin_topk_sort,
               P.pin_kv_rollback_exercise, P.pin_kv_commit_tree_path, P.pin_kv_commit_invariants,
