@@ -312,6 +312,7 @@ spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
     const spec_status st = call_tag(workspace, stream, g.am.tag, g.am.tag_src);
     if (st != SPEC_OK) return st;
     g.am.partial = at<uint64_t>(workspace, plan.off_partial);
+    g.am.hdr = static_cast<uint32_t *>(workspace);
     g.tokens = draft_tokens;
     g.B = B;
     g.K = K;
@@ -357,6 +358,7 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
     const spec_status st = call_tag(workspace, stream, t.am.tag, t.am.tag_src);
     if (st != SPEC_OK) return st;
     t.am.partial = at<uint64_t>(workspace, plan.off_partial);
+    t.am.hdr = static_cast<uint32_t *>(workspace);
     t.tokens = node_tokens;
     t.B = B;
     t.out_tokens = out_tokens;
@@ -391,6 +393,7 @@ spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtyp
     const spec_status st = call_tag(workspace, stream, t.am.tag, t.am.tag_src);
     if (st != SPEC_OK) return st;
     t.am.partial = at<uint64_t>(workspace, plan.off_partial);
+    t.am.hdr = static_cast<uint32_t *>(workspace);
     t.tokens = node_tokens;
     t.parents = parents;
     t.node_count = node_count;
@@ -429,6 +432,7 @@ spec_status spec_draft_topk(const void *logits, spec_dtype dtype, int32_t rows, 
     const int64_t groups = (rows + 3) / 4, group_wgs = 4 * static_cast<int64_t>(plan.nchunk);
     a.lag = std::min<int64_t>(groups, (kResidentWGs + group_wgs - 1) / group_wgs + 1);
     a.partial = at<uint64_t>(workspace, plan.off_partial);
+    a.hdr = static_cast<uint32_t *>(workspace);
     a.out_idx = out_idx;
     a.out_val = out_val;
     return launch_status(launch_topk(a, dtype, stream));

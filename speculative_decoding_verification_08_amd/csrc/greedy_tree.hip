@@ -211,7 +211,10 @@ __device__ __forceinline__ void greedy_resolve_item(const GreedyArgs &a, const A
     int32_t *ot = a.out_tokens + static_cast<int64_t>(b) * (K + 1);
     if (!ok) {
         for (int k = lane; k <= K; k += kWave) ot[k] = -1;
-        if (lane == 0) a.out_accepted[b] = -1;
+        if (lane == 0) {
+            a.out_accepted[b] = -1;
+            count_failure(am.hdr);
+        }
         return;
     }
     const uint64_t m = __ballot(lane < K && tok != s_a[lane]);
@@ -245,7 +248,10 @@ __device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, const Argma
             a.out_tokens[static_cast<int64_t>(b) * (D + 1) + v] = -1;
             if (a.out_path) a.out_path[static_cast<int64_t>(b) * (D + 1) + v] = -1;
         }
-        if (v == 0) a.out_depth[b] = -1;
+        if (v == 0) {
+            a.out_depth[b] = -1;
+            count_failure(am.hdr);
+        }
         return;
     }
     // match[v], then accepted = all matches on the path to the root, folded
@@ -325,7 +331,10 @@ __device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, cons
             a.out_tokens[row0 + v] = -1;
             if (a.out_path) a.out_path[row0 + v] = -1;
         }
-        if (v == 0) a.out_depth[b] = -1;
+        if (v == 0) {
+            a.out_depth[b] = -1;
+            count_failure(am.hdr);
+        }
         return;
     }
     if (v < n) {

@@ -45,5 +45,11 @@ __device__ __forceinline__ void wait_word(const uint64_t *p, uint32_t tag, uint6
         __builtin_amdgcn_s_sleep(4);
 }
 
+// A bounded wait ran out: count it in the workspace header (the failure
+// word, third of the header's 32-bit words), one thread per failed output.
+__device__ __forceinline__ void count_failure(uint32_t *hdr) {
+    __hip_atomic_fetch_add(hdr + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace
 }  // namespace sv

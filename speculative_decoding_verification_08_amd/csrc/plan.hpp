@@ -56,6 +56,7 @@ constexpr size_t kWorkspaceHeader = 256;
 constexpr int kHdrGraphTag = 0;  // the tag word of calls recorded into a graph
 constexpr int kHdrPhaseTag = 1;  // the tag of the statistics the last chain_stats call left
 constexpr int kHdrFailures = 2;  // count of bounded waits that ran out (and stale statistics)
+static_assert(kHdrFailures == 2, "count_failure writes the third header word");
 
 // Division by a divisor fixed for the launch, without a division sequence:
 // q = (mulhi(n, m) + n) >> s, exact for n < 2^31 (Granlund and Montgomery's
@@ -111,6 +112,7 @@ struct ArgmaxArgs {
     uint32_t tag;            // this call's tag (upper half of every handed-over word)
     const uint32_t *tag_src; // nullable: read the tag from this device word instead (graph replays)
     uint64_t *partial;       // [rows][nchunk][2] tagged (value bits, index)
+    uint32_t *hdr;           // the workspace header words
 };
 
 // Greedy chain verify in one launch: the argmax workgroups of rows

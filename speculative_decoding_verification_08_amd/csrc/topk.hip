@@ -139,6 +139,7 @@ __device__ void topk_merge_small(const TopkArgs &a, int64_t row) {
             a.out_idx[row * k + lane] = -1;
             if (a.out_val) a.out_val[row * k + lane] = NAN;
         }
+        if (lane == 0) count_failure(a.hdr);
         return;
     }
     // M: the maximum (slot 0 of a list) that kt - 1 other maxima outrank.
@@ -224,6 +225,7 @@ __device__ void topk_merge(const TopkArgs &a, int64_t row) {
             a.out_idx[row * k + lane] = -1;
             if (a.out_val) a.out_val[row * k + lane] = NAN;
         }
+        if (lane == 0) count_failure(a.hdr);
         return;
     }
     int r = 0;

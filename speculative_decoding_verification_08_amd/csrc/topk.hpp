@@ -22,6 +22,7 @@ struct TopkArgs {
     uint64_t *partial;       // [rows][nchunk][kMaxTopK][2] tagged (value bits, index)
     int32_t *out_idx;        // [rows][k]
     float *out_val;          // nullable [rows][k]
+    uint32_t *hdr;           // the workspace header words
 };
 
 hipError_t launch_topk(const TopkArgs &a, int dtype, hipStream_t s);

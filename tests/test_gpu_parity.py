@@ -54,18 +54,6 @@ def chain_case(name, B, K, V, dtype, T, recipe="normal", sigma=0.5, step=0, targ
 
 # ------------------------------------------------------------------ chain
 
-def test_chain_small_workload_all_steps(sv):
-    w = W.WORKLOADS["chain_t1_small"]
-    total = {}
-    for step in range(0, 200, 10):
-        case(f"chain_t1_small step {step}")
-        d = W.chain_inputs(w, step)
-        n = parity.check_chain(d, *run_chain(sv, d))
-        for k, v in n.items():
-            total[k] = total.get(k, 0) + v
-    print("chain_t1_small", total)
-
-
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("K,V,T", [(0, 517, 1.0), (1, 1003, 0.7), (3, 4099, 1.0), (8, 9001, 1.3),
                                    (5, 40003, 1.0), (2, 8, 1.0), (4, 1, 1.0)])
@@ -203,15 +191,6 @@ def test_chain_full_size_128k(sv):
         assert all(np.array_equal(a, b) for a, b in zip(g, g2))
 
 
-def test_chain_full_size_152k_fp32(sv):
-    w = W.WORKLOADS["chain_t07_152k"]
-    case("chain_t07_152k full size, oracle on every 8th sequence")
-    d = W.chain_inputs(w, 0)
-    g = run_chain(sv, d)
-    n = parity.check_chain(d, *g, seqs=np.arange(0, w.B, 8))
-    print("chain_t07_152k", dict(n), "mean accepted", g[1].mean())
-
-
 def test_chain_non_default_stream(sv):
     d = chain_case("stream", 16, 4, 30000, "bf16", 1.0, recipe="peaked", sigma=0.7)
     case("chain on a side stream")
@@ -286,15 +265,6 @@ def test_greedy_ties_and_signed_zero(sv):
         d = dict(target=logits, tokens=tokens)
         case(f"greedy ties {dtype}")
         parity.check_greedy(d, *run_greedy(sv, d))
-
-
-def test_greedy_full_size_32k(sv):
-    w = W.WORKLOADS["greedy_32k"]
-    for step in range(3):
-        case(f"greedy_32k full size step {step}")
-        d = W.greedy_inputs(w, step)
-        g = run_greedy(sv, d)
-        parity.check_greedy(d, *g)
 
 
 # ------------------------------------------------------------------ tree
