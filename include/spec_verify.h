@@ -18,7 +18,8 @@
  *
  * Conventions shared by every entry point:
  *  - Every pointer except `parents` and `workspace_bytes`-style out-params is
- *    a DEVICE pointer owned by the caller.  The library allocates nothing.
+ *    a DEVICE pointer owned by the caller.  The library allocates nothing
+ *    (spec_verify_chain_noalloc uses a fixed array of its own instead).
  *  - Logit arrays are row-major with the vocabulary innermost and must be
  *    16-byte aligned at their base; other arrays need natural alignment.
  *  - Work is enqueued on `stream` and nothing is synchronised: outputs are
@@ -50,8 +51,9 @@
  *    access: token ids are clamped before they address memory.
  *  - Results are bitwise reproducible run to run (fixed reduction orders, no
  *    floating-point atomics).
- *  - The library keeps no state between calls beyond that call counter and is
- *    safe to call from several host threads.
+ *  - The library keeps no state between calls beyond that call counter (and
+ *    the device array of spec_verify_chain_noalloc) and is safe to call from
+ *    several host threads.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -82,7 +84,9 @@ typedef enum {
     SPEC_OK = 0,
     SPEC_ERR_INVALID_ARG = 1, /* a size, pointer, dtype, temperature or tree is invalid */
     SPEC_ERR_WORKSPACE = 2,   /* workspace missing or smaller than required            */
-    SPEC_ERR_LAUNCH = 3       /* the HIP runtime reported an error at enqueue          */
+    SPEC_ERR_LAUNCH = 3,      /* the HIP runtime reported an error at enqueue          */
+    SPEC_ERR_SCRATCH_LIMIT = 4 /* spec_verify_chain_noalloc: the call needs more scratch
+                                  than SPEC_VERIFY_NOALLOC_SCRATCH_BYTES                 */
 } spec_status;
 
 #define SPEC_VERIFY_MAX_K 64            /* draft length limit of chain and greedy verify */
@@ -92,6 +96,7 @@ typedef enum {
 #define SPEC_VERIFY_MAX_CHAIN_V_F32 (1 << 18)   /* chain verify vocabulary limit, fp32 logits */
 #define SPEC_TOPK_MAX_K 8               /* spec_draft_topk: k limit                      */
 #define SPEC_TOPK_MAX_V (1 << 19)       /* spec_draft_topk: vocabulary limit             */
+#define SPEC_VERIFY_NOALLOC_SCRATCH_BYTES (8u << 20) /* spec_verify_chain_noalloc's array */
 
 /*
  * Workspace size for one call.  K_or_N is K for the chain and greedy modes,
@@ -175,6 +180,35 @@ spec_status spec_verify_chain_sample(const void *target_logits, const void *draf
                                      int32_t K, int32_t V, float temperature, int32_t *out_tokens,
                                      int32_t *out_accepted, float *out_diag, void *workspace,
                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * spec_verify_chain without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops and
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and kernels as
+ * spec_verify_chain; the workspace is a fixed array of
+ * SPEC_VERIFY_NOALLOC_SCRATCH_BYTES in the library's device memory, one copy
+ * per GPU, held until the process ends.  The call allocates and frees
+ * nothing.
+ *
+ * Returns SPEC_ERR_SCRATCH_LIMIT, before any HIP call, when
+ * spec_verify_workspace_bytes(SPEC_MODE_CHAIN, B, K, V, dtype) exceeds that
+ * size (B = 256, K = 8, V = 151936 fp32 needs 5.3 MiB), and
+ * SPEC_ERR_INVALID_ARG for sizes spec_verify_chain rejects.  The first call on
+ * a device looks up that device's copy (the current device; `stream` must
+ * belong to it); SPEC_ERR_LAUNCH if that fails.
+ *
+ * Every call on one GPU uses the same array, which keeps the last call's
+ * words.  Calls ordered on one stream (eager calls and graph replays alike)
+ * need nothing cleared in between; calls that overlap on one GPU (other
+ * streams, other host threads) race on the array and give unspecified
+ * outputs.
+ */
+spec_status spec_verify_chain_noalloc(const void *target_logits, const void *draft_logits,
+                                      spec_dtype dtype, const int32_t *draft_tokens,
+                                      const float *u_accept, const float *u_sample, int32_t B,
+                                      int32_t K, int32_t V, float temperature,
+                                      int32_t *out_tokens, int32_t *out_accepted, float *out_diag,
+                                      hipStream_t stream);
 
 /*
  * Greedy chain verify, T = 0 (French lesson, "La règle de l'exactitude",

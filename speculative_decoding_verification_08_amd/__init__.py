@@ -23,6 +23,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "spec_verify.h")
 SPEC_DTYPE_F32, SPEC_DTYPE_BF16 = 0, 1
 SPEC_MODE_CHAIN, SPEC_MODE_GREEDY, SPEC_MODE_TREE, SPEC_MODE_TREE_DYN, SPEC_MODE_TOPK = 0, 1, 2, 3, 4
 SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_LAUNCH = 0, 1, 2, 3
+SPEC_ERR_SCRATCH_LIMIT = 4
+NOALLOC_SCRATCH_BYTES = 8 << 20
 MAX_K, MAX_TREE_NODES, MAX_V = 64, 256, 1 << 26
 MAX_CHAIN_V_BF16, MAX_CHAIN_V_F32 = 1 << 19, 1 << 18
 TOPK_MAX_K, TOPK_MAX_V = 8, 1 << 19
@@ -60,10 +62,12 @@ def _load(path: str = LIB_PATH):
                                    vp]
     lib.spec_tree_mask.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     lib.spec_verify_workspace_failures.argtypes = [vp, sz, i32, ctypes.POINTER(ctypes.c_uint32), vp]
+    lib.spec_verify_chain_noalloc.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, f32,
+                                              vp, vp, vp, vp]
     for fn in ("spec_verify_workspace_bytes", "spec_verify_chain", "spec_verify_chain_stats",
                "spec_verify_chain_sample", "spec_verify_greedy", "spec_verify_tree_greedy",
                "spec_verify_tree_greedy_dyn", "spec_draft_topk", "spec_kv_commit",
-               "spec_tree_mask", "spec_verify_workspace_failures"):
+               "spec_tree_mask", "spec_verify_workspace_failures", "spec_verify_chain_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     return lib
 
@@ -201,6 +205,26 @@ def spec_verify_chain(target_logits, draft_logits, draft_tokens, u_accept, u_sam
           _ptr(u_accept), _ptr(u_sample), B, K, V, float(temperature), _ptr(out_tokens),
           _ptr(out_accepted), _ptr(out_diag), _ptr(workspace_buf), workspace_buf.numel(),
           _stream(dev, stream))
+    return out_tokens, out_accepted, out_diag
+
+
+def spec_verify_chain_noalloc(target_logits, draft_logits, draft_tokens, u_accept, u_sample,
+                              temperature: float, *, out_tokens=None, out_accepted=None,
+                              diag=False, out_diag=None, stream=None):
+    """spec_verify_chain on the library's fixed device array instead of a
+    workspace (the outputs are the caller's tensors, allocated here when not
+    given).  Returns (tokens [B][K+1], accepted [B], diag or None)."""
+    dt, B, K, V = _chain_check(target_logits, draft_logits, draft_tokens, u_accept, u_sample)
+    dev = target_logits.device
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if out_accepted is None:
+        out_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_diag is None and diag:
+        out_diag = torch.empty((B, K + 1, 4), dtype=torch.float32, device=dev)
+    _call("spec_verify_chain_noalloc", _ptr(target_logits), _ptr(draft_logits), dt,
+          _ptr(draft_tokens), _ptr(u_accept), _ptr(u_sample), B, K, V, float(temperature),
+          _ptr(out_tokens), _ptr(out_accepted), _ptr(out_diag), _stream(dev, stream))
     return out_tokens, out_accepted, out_diag
 
 

@@ -202,6 +202,7 @@ const char *spec_verify_status_string(spec_status status) {
         case SPEC_ERR_INVALID_ARG: return "invalid argument";
         case SPEC_ERR_WORKSPACE: return "workspace missing or too small";
         case SPEC_ERR_LAUNCH: return "kernel launch failed";
+        case SPEC_ERR_SCRATCH_LIMIT: return "sizes need more scratch than the fixed device array holds";
     }
     return "unknown status";
 }

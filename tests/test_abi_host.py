@@ -194,3 +194,22 @@ def test_status_strings():
     lib = sv.library()
     for s in range(4):
         assert lib.spec_verify_status_string(s)
+
+
+def test_noalloc_limits_checked_before_any_device_call():
+    """Sizes past the fixed array, and sizes the chain verify rejects, return
+    before the entry point touches the device (none here)."""
+    lib = sv.library()
+    fn = lib.spec_verify_chain_noalloc
+
+    def call(B, K, V, dt=sv.SPEC_DTYPE_F32):
+        return fn(FAKE, FAKE, dt, FAKE, FAKE, FAKE, B, K, V, ctypes.c_float(1.0), FAKE, FAKE, None,
+                  None)
+    need = sv.spec_verify_workspace_bytes(sv.SPEC_MODE_CHAIN, 256, 8, 151936, sv.SPEC_DTYPE_F32)
+    assert need <= sv.NOALLOC_SCRATCH_BYTES                  # the batched-serving shape fits
+    assert call(4096, 64, 1 << 17) == sv.SPEC_ERR_SCRATCH_LIMIT
+    assert call(512, 8, 151936) == sv.SPEC_ERR_SCRATCH_LIMIT
+    assert call(2, 4, 0) == sv.SPEC_ERR_INVALID_ARG
+    assert call(2, 65, 100) == sv.SPEC_ERR_INVALID_ARG
+    assert call(0, 4, 100) == sv.SPEC_OK
+    assert "scratch" in lib.spec_verify_status_string(sv.SPEC_ERR_SCRATCH_LIMIT).decode()
