@@ -12,6 +12,7 @@
 #include <random>
 
 #include "plan.hpp"
+#include "planning.hpp"
 #include "kv.hpp"
 #include "tree_mask.hpp"
 #include "topk.hpp"
@@ -20,70 +21,7 @@
 namespace sv {
 namespace {
 
-constexpr size_t kAlign = 256;
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-
-// Elements per chunk of the streaming pass: 16 KB of logits per workgroup.
-// Smaller chunks for small grids measured slower on MI355X (each workgroup's
-// reduce and hand-over is a fixed cost), so the size does not depend on the
-// grid.
-int first_pass_chunk(spec_dtype dtype) { return dtype == SPEC_DTYPE_BF16 ? 8192 : 4096; }
-
-bool valid_dtype(spec_dtype d) { return d == SPEC_DTYPE_F32 || d == SPEC_DTYPE_BF16; }
-
-bool valid_sizes(spec_mode mode, int32_t B, int32_t KN, int32_t V) {
-    if (B < 0 || V < 1 || V > SPEC_VERIFY_MAX_V) return false;
-    if (mode == SPEC_MODE_TOPK) return KN >= 1 && KN <= SPEC_TOPK_MAX_K && KN <= V && V <= SPEC_TOPK_MAX_V;
-    if (mode == SPEC_MODE_TREE || mode == SPEC_MODE_TREE_DYN)
-        return KN >= 1 && KN <= SPEC_VERIFY_MAX_TREE_NODES;
-    return KN >= 0 && KN <= SPEC_VERIFY_MAX_K;
-}
-
-bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dtype, Plan &p) {
-    if (!valid_sizes(mode, B, KN, V) || !valid_dtype(dtype)) return false;
-    int64_t rows;
-    if (mode == SPEC_MODE_CHAIN) rows = static_cast<int64_t>(B) * (2 * KN + 1);
-    else if (mode == SPEC_MODE_GREEDY) rows = static_cast<int64_t>(B) * (KN + 1);
-    else if (mode == SPEC_MODE_TOPK) rows = B;
-    else rows = static_cast<int64_t>(B) * KN;
-    p.rows = rows;
-    p.chunk = mode == SPEC_MODE_CHAIN ? kStatChunkBytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4)
-                                      : first_pass_chunk(dtype);
-    p.nchunk = (V + p.chunk - 1) / p.chunk;
-    if (rows * p.nchunk > 0x7fffffffLL) return false;  // one-dimensional grid
-    size_t off = kWorkspaceHeader;  // the graph tag word comes first
-    p.off_partial = off;
-    if (mode == SPEC_MODE_CHAIN) {
-        off += align_up(static_cast<size_t>(rows) * p.nchunk * 16);
-        p.chunk2 = kDrawChunkBytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
-        p.nchunk2 = (V + p.chunk2 - 1) / p.chunk2;
-        // The bonus draw takes a draw chunk's mass from the statistics of the
-        // same chunk, and a finisher holds two chunks' masses per lane.
-        if (p.chunk2 != p.chunk || p.nchunk > kMaxStatChunks || p.nchunk2 > kMaxDrawChunks)
-            return false;
-        if (static_cast<int64_t>(B) * p.nchunk2 > 0x7fffffffLL) return false;
-        p.off_sums = off;  // two tagged masses per chunk: residual, target
-        off += align_up(static_cast<size_t>(B) * p.nchunk2 * 16);
-        p.off_rec = off;   // one record per sequence
-        off += align_up(static_cast<size_t>(B) * kRecWords * 8);
-    } else if (mode == SPEC_MODE_TOPK) {
-        // One launch: a workgroup per (row, chunk) and a merge workgroup per
-        // row (one wavefront holds the row's chunk maxima, two per lane).
-        p.chunk = kChunk2Bytes / (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
-        p.nchunk = (V + p.chunk - 1) / p.chunk;
-        if (p.nchunk > kTopkMaxChunks) return false;
-        if (rows * p.nchunk + (rows + 3) / 4 > 0x7fffffffLL) return false;
-        off += align_up(static_cast<size_t>(rows) * p.nchunk * kMaxTopK * 16);
-    } else {
-        // One launch: argmax workgroups, then one resolve workgroup per sequence.
-        if (rows * p.nchunk + B > 0x7fffffffLL) return false;
-        off += align_up(static_cast<size_t>(rows) * p.nchunk * 16);  // two tagged words
-    }
-    p.bytes = off > 0 ? off : kAlign;
-    return true;
-}
 
 template <class T>
 T *at(void *ws, size_t off) {
@@ -149,26 +87,11 @@ spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype,
     a.chunk = plan.chunk;
     a.nchunk = plan.nchunk;
     a.nchunk2 = plan.nchunk2;
-    a.S = static_cast<uint32_t>(2 * K) * plan.nchunk;
-    a.D = plan.nchunk2;
-    a.fd_nch = make_fastdiv(plan.nchunk);
-    a.fd_D = make_fastdiv(a.D);
+    chain_grid_fields(plan, K, a);
     a.partial = at<uint64_t>(ws, plan.off_partial);
     a.sums = at<uint64_t>(ws, plan.off_sums);
     a.rec = at<uint64_t>(ws, plan.off_rec);
     return SPEC_OK;
-}
-
-// The one-launch schedule (see k_chain_fused): grid size, or 0 if it would
-// not fit a one-dimensional grid.
-uint32_t chain_schedule(ChainArgs &a) {
-    const uint64_t B = a.B, S = a.S, D = a.D, nch = a.nchunk;
-    const uint64_t total = B * (S + D + nch + 3);
-    if (total > 0x7fffffffull) return 0;
-    a.fd_S1 = make_fastdiv(static_cast<uint32_t>(S + 1));
-    a.blocks_end = static_cast<uint32_t>(S + (B - 1) * (S + 1));
-    a.bon_end = static_cast<uint32_t>(a.blocks_end + B * nch);
-    return static_cast<uint32_t>(total);
 }
 
 spec_status chain_sample_args(const int32_t *tokens, const float *ua, const float *us, int32_t B,
@@ -427,11 +350,7 @@ spec_status spec_draft_topk(const void *logits, spec_dtype dtype, int32_t rows, 
     a.k = k;
     const spec_status st = call_tag(workspace, stream, a.tag, a.tag_src);
     if (st != SPEC_OK) return st;
-    // A merge trails its rows' chunks by about one resident window of
-    // workgroups (plus a group of rows), so its lists are usually complete
-    // on arrival.  Units: groups of four rows, one merge workgroup each.
-    const int64_t groups = (rows + 3) / 4, group_wgs = 4 * static_cast<int64_t>(plan.nchunk);
-    a.lag = std::min<int64_t>(groups, (kResidentWGs + group_wgs - 1) / group_wgs + 1);
+    a.lag = topk_lag(rows, plan.nchunk);
     a.partial = at<uint64_t>(workspace, plan.off_partial);
     a.hdr = static_cast<uint32_t *>(workspace);
     a.out_idx = out_idx;

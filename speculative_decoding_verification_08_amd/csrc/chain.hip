@@ -30,6 +30,7 @@
 // item only waits for workgroups of lower index (dispatched before it).
 #include "device.hpp"
 #include "handover.hpp"
+#include "grid_order.hpp"
 #include "plan.hpp"
 
 namespace sv {
@@ -844,29 +845,15 @@ __global__ __launch_bounds__(kWG) void k_chain_stats(ChainArgs a) {
 template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
     __shared__ __align__(16) float lds[kDrawLds];
-    const uint32_t g = blockIdx.x, B = a.B, nd = B * a.D;
-    if (g < B) {
-        resolver_item<DT, false>(a, static_cast<int>(g), lds);
-    } else if (g < B + nd) {
-        const uint32_t h = g - B, b = fdiv(h, a.fd_D);
-        draw_item<DT, VecOk>(a, static_cast<int>(b), static_cast<int>(h - b * a.D), lds);
-    } else if (g < 2 * B + nd) {
-        finisher_item<DT, VecOk>(a, static_cast<int>(g - B - nd), lds);
-    } else {
-        bonus_item<DT, VecOk, false>(a, static_cast<int>(g - 2 * B - nd), lds);
-    }
+    const ChainItem it = chain_draw_item(blockIdx.x, a);
+    const int b = static_cast<int>(it.b);
+    if (it.kind == kItemResolver) resolver_item<DT, false>(a, b, lds);
+    else if (it.kind == kItemDraw) draw_item<DT, VecOk>(a, b, static_cast<int>(it.p), lds);
+    else if (it.kind == kItemFinisher) finisher_item<DT, VecOk>(a, b, lds);
+    else bonus_item<DT, VecOk, false>(a, b, lds);
 }
 
-// The whole chain verify in one launch.  Per sequence: S statistics items of
-// the rows the accept tests read (target rows 0..K-1, draft rows 0..K-1), a
-// resolver, nchunk statistics items of the bonus row, D draw items, a
-// finisher and a bonus item.  The hardware dispatches workgroups in index
-// order, and an item waits only for workgroups of lower index (dispatched
-// before it), in this order:
-//   block k      the statistics of sequence k, then the resolver of k - 1;
-//   bonus        the statistics of every bonus row;
-//   tail         the resolver of sequence B - 1, every draw item, every
-//                finisher, every bonus item.
+// The whole chain verify in one launch, in the order of chain_fused_item.
 // Each resolver finds its statistics done or nearly so, and the stream of
 // logits runs undisturbed: draws placed among the statistics measured slower
 // at every lag tried (their second read of row j takes slots and bandwidth
@@ -881,52 +868,22 @@ __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
     // loads before its first logit load.
     asm volatile("" ::"s"(a.target), "s"(a.draft), "s"(a.partial), "s"(a.c), "s"(a.V), "s"(a.chunk),
                  "s"(a.tag), "s"(a.tag_src));
-    const uint32_t g = blockIdx.x, S = a.S, D = a.D, K = a.K, B = a.B;
-    uint32_t b = 0, p = 0;
-    int kind;  // 0 statistics (non-bonus rows), 1 resolver, 2 draw, 3 finisher, 4 bonus-row statistics, 5 bonus item
-    if (g < S) {
-        kind = 0;
-        p = g;
-    } else if (g < a.blocks_end) {
-        const uint32_t h = g - S, kk = fdiv(h, a.fd_S1), q = h - kk * (S + 1);
-        kind = q < S ? 0 : 1;
-        b = q < S ? kk + 1 : kk;
-        p = q;
-    } else if (g < a.bon_end) {
-        const uint32_t h = g - a.blocks_end;
-        b = fdiv(h, a.fd_nch);
-        p = h - b * a.nchunk;
-        kind = 4;
+    const ChainItem it = chain_fused_item(blockIdx.x, a);
+    const int b = static_cast<int>(it.b);
+    if (it.kind == kItemStats) {
+        int row, ch;
+        chain_stats_row(it.p, a, row, ch);
+        stats_item<DT, VecOk>(a, it.b, row, ch);
+    } else if (it.kind == kItemBonusStats) {
+        stats_item<DT, VecOk>(a, it.b, a.K, static_cast<int>(it.p));
+    } else if (it.kind == kItemResolver) {
+        resolver_item<DT, true>(a, b, lds);
+    } else if (it.kind == kItemDraw) {
+        draw_item<DT, VecOk>(a, b, static_cast<int>(it.p), lds);
+    } else if (it.kind == kItemFinisher) {
+        finisher_item<DT, VecOk>(a, b, lds);
     } else {
-        const uint32_t h = g - a.bon_end;
-        if (h == 0) {
-            kind = 1;
-            b = B - 1;
-        } else if (h - 1 < B * D) {
-            kind = 2;
-            b = fdiv(h - 1, a.fd_D);
-            p = h - 1 - b * D;
-        } else if (h - 1 - B * D < B) {
-            kind = 3;
-            b = h - 1 - B * D;
-        } else {
-            kind = 5;
-            b = h - 1 - B * D - B;
-        }
-    }
-    if (kind == 0) {
-        const uint32_t rr = fdiv(p, a.fd_nch), ch = p - rr * a.nchunk;
-        stats_item<DT, VecOk>(a, b, static_cast<int>(rr < K ? rr : rr + 1), static_cast<int>(ch));
-    } else if (kind == 4) {
-        stats_item<DT, VecOk>(a, b, static_cast<int>(K), static_cast<int>(p));
-    } else if (kind == 1) {
-        resolver_item<DT, true>(a, static_cast<int>(b), lds);
-    } else if (kind == 2) {
-        draw_item<DT, VecOk>(a, static_cast<int>(b), static_cast<int>(p), lds);
-    } else if (kind == 3) {
-        finisher_item<DT, VecOk>(a, static_cast<int>(b), lds);
-    } else {
-        bonus_item<DT, VecOk, true>(a, static_cast<int>(b), lds);
+        bonus_item<DT, VecOk, true>(a, b, lds);
     }
 }
 
@@ -945,7 +902,7 @@ hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(a.bon_end + 1 + static_cast<uint32_t>(a.B) * (a.D + 2)), blk(kWG);
+    const dim3 g(chain_fused_grid(a)), blk(kWG);
     if (dtype == 1) {
         if (a.V % Bf16::kVec == 0) k_chain_fused<Bf16, true><<<g, blk, 0, s>>>(a);
         else k_chain_fused<Bf16, false><<<g, blk, 0, s>>>(a);
@@ -957,7 +914,7 @@ hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_chain_draw(const ChainArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(static_cast<uint32_t>(a.B) * (a.D + 3)), blk(kWG);
+    const dim3 g(chain_draw_grid(a)), blk(kWG);
     if (dtype == 1) {
         if (a.V % Bf16::kVec == 0) k_chain_draw<Bf16, true><<<g, blk, 0, s>>>(a);
         else k_chain_draw<Bf16, false><<<g, blk, 0, s>>>(a);

@@ -16,9 +16,12 @@
 // merge order.
 #include "device.hpp"
 #include "handover.hpp"
+#include "grid_order.hpp"
 #include "plan.hpp"
 
 namespace sv {
+
+static_assert(kCompactTrees == kWave * kCountsPerLane, "one wavefront holds every count");
 namespace {
 
 template <class DT, int U>
@@ -388,14 +391,6 @@ __device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, cons
     if (v == 0) a.out_depth[b] = d;
 }
 
-// Batches of at most kCompactTrees trees use the compact order: every
-// workgroup reads all node counts, so the argmax items cover the real rows
-// only, tree by tree, the resolve items follow them at once, and the
-// workgroups left over (one per padding chunk) return at the end of the grid.
-// Larger batches keep one item per (tree, row slot, chunk) and skip padding
-// rows where they fall.
-constexpr int kCountsPerLane = 4, kCompactTrees = kWave * kCountsPerLane;
-
 // Inclusive integer sum over lanes 0..lane of a wavefront (DPP, as the
 // float scan: within rows of 16, then the rows' totals carried upward).
 __device__ __forceinline__ int wave_incl_sum_i(int x) {
@@ -408,23 +403,18 @@ __device__ __forceinline__ int wave_incl_sum_i(int x) {
     return x;
 }
 
-// Compact order with lane l holding the clamped node counts of trees
-// P l .. P l + P - 1 (0 past B): returns T, the batch's real rows, and for
-// R < T the tree b and node v of real row R (the first lane whose running
-// total passes R, then one of that lane's trees).
+// Compact order with lane l holding the row counts of trees P l .. P l + P - 1
+// (0 past B): returns T, the batch's real rows, and for R < T the tree b and
+// node v of real row R (the first lane whose running total passes R, then one
+// of that lane's trees).
 template <int P>
 __device__ __forceinline__ uint32_t locate_row(const TreeDynArgs &a, uint32_t R, uint32_t &b, uint32_t &v) {
-    const int lane = threadIdx.x % kWave, B = a.B, Nmax = a.Nmax;
+    const int lane = threadIdx.x % kWave;
     int n[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-        // Every lane loads (a clamped, in-range address) and masks afterwards:
-        // a select on t < B lets the compiler sink each load into a branch of
-        // its own, and the loads then leave one after another.
-        const int t = lane * P + j;
-        const int c = a.node_count[min(t, B - 1)];
-        n[j] = min(max(c, 1), Nmax) & -static_cast<int>(t < B);
-    }
+    // Every lane loads (a clamped, in-range address) and masks afterwards: a
+    // select on t < B lets the compiler sink each load into a branch of its
+    // own, and the loads then leave one after another.
+    lane_tree_rows<P>(a.node_count, a.B, a.Nmax, lane, n);
     int s = 0;
 #pragma unroll
     for (int j = 0; j < P; ++j) s += n[j];
@@ -433,17 +423,9 @@ __device__ __forceinline__ uint32_t locate_row(const TreeDynArgs &a, uint32_t R,
     if (R < T) {
         const uint64_t hit = __ballot(static_cast<uint32_t>(incl) > R);
         const int L = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-        uint32_t r = R - static_cast<uint32_t>(__builtin_amdgcn_readlane(incl - s, L));
-        uint32_t t = static_cast<uint32_t>(L) * P;
-#pragma unroll
-        for (int j = 0; j < P - 1; ++j) {
-            const uint32_t m = static_cast<uint32_t>(__builtin_amdgcn_readlane(n[j], L));
-            if (r < m) break;
-            r -= m;
-            ++t;
-        }
-        b = t;
-        v = r;
+        const uint32_t r = R - static_cast<uint32_t>(__builtin_amdgcn_readlane(incl - s, L));
+        lane_row<P>(r, static_cast<uint32_t>(L) * P,
+                    [&](int j) { return static_cast<uint32_t>(__builtin_amdgcn_readlane(n[j], L)); }, b, v);
     }
     return T;
 }
@@ -457,33 +439,19 @@ __global__ __launch_bounds__(kWG) void k_tree_dyn(TreeDynArgs a) {
     const uint32_t nch = a.am.nchunk, g = blockIdx.x, B = static_cast<uint32_t>(a.B);
     // This workgroup's item: an argmax item (row, ch), the resolve of tree
     // `row`, or nothing.
-    uint32_t row = 0, ch = 0;
-    bool argmax = false, resolve = false;
+    TreeDynItem it;
     if (B <= static_cast<uint32_t>(kCompactTrees)) {
         const uint32_t R = g / nch;
         uint32_t b = 0, v = 0;
         const uint32_t T = B <= static_cast<uint32_t>(kWave) ? locate_row<1>(a, R, b, v)
                                                              : locate_row<kCountsPerLane>(a, R, b, v);
-        const uint32_t nam = T * nch;
-        argmax = g < nam;
-        resolve = !argmax && g < nam + B;
-        row = argmax ? b * static_cast<uint32_t>(a.Nmax) + v : g - nam;
-        ch = g - R * nch;
+        it = tree_dyn_compact_item(g, nch, T, b, v, B, static_cast<uint32_t>(a.Nmax));
     } else {
-        const uint32_t nam = static_cast<uint32_t>(a.am.rows) * nch;
-        if (g < nam) {
-            const uint32_t slot = g / nch, b = slot / a.Nmax, v = slot - b * a.Nmax;
-            // Rows past the tree's node count are padding: not read.
-            argmax = v < static_cast<uint32_t>(min(max(a.node_count[b], 1), a.Nmax));
-            row = slot;
-            ch = g - slot * nch;
-        } else {
-            resolve = true;
-            row = g - nam;
-        }
+        it = tree_dyn_full_item(g, nch, static_cast<uint32_t>(a.am.rows), static_cast<uint32_t>(a.Nmax),
+                                a.node_count);
     }
-    if (argmax) argmax_item<DT, 4>(am, row, static_cast<int>(ch));
-    else if (resolve) tree_dyn_resolve_item(a, am, static_cast<int>(row));
+    if (it.argmax) argmax_item<DT, 4>(am, it.row, static_cast<int>(it.ch));
+    else if (it.resolve) tree_dyn_resolve_item(a, am, static_cast<int>(it.row));
 }
 
 template <class DT>
@@ -492,13 +460,9 @@ __global__ __launch_bounds__(kWG) void k_greedy(GreedyArgs a) {
     // scratch); the argmax arguments with the call's tag are a local copy.
     ArgmaxArgs am = a.am;
     if (am.tag_src) am.tag = *am.tag_src;  // a graph replay's tag
-    const uint32_t nam = static_cast<uint32_t>(a.am.rows) * a.am.nchunk, g = blockIdx.x;
-    if (g < nam) {
-        const uint32_t row = g / a.am.nchunk;
-        argmax_item<DT, 4>(am, row, static_cast<int>(g - row * a.am.nchunk));
-    } else {
-        greedy_resolve_item(a, am, static_cast<int>(g - nam));
-    }
+    const ArgmaxItem it = argmax_item_of(blockIdx.x, a.am.nchunk, static_cast<uint32_t>(a.am.rows));
+    if (it.argmax) argmax_item<DT, 4>(am, it.row, static_cast<int>(it.ch));
+    else greedy_resolve_item(a, am, static_cast<int>(it.row));
 }
 
 template <class DT>
@@ -507,33 +471,29 @@ __global__ __launch_bounds__(kWG) void k_tree(TreeArgs a) {
     // scratch); the argmax arguments with the call's tag are a local copy.
     ArgmaxArgs am = a.am;
     if (am.tag_src) am.tag = *am.tag_src;  // a graph replay's tag
-    const uint32_t nam = static_cast<uint32_t>(a.am.rows) * a.am.nchunk, g = blockIdx.x;
-    if (g < nam) {
-        const uint32_t row = g / a.am.nchunk;
-        argmax_item<DT, 4>(am, row, static_cast<int>(g - row * a.am.nchunk));
-    } else {
-        tree_resolve_item(a, am, static_cast<int>(g - nam));
-    }
+    const ArgmaxItem it = argmax_item_of(blockIdx.x, a.am.nchunk, static_cast<uint32_t>(a.am.rows));
+    if (it.argmax) argmax_item<DT, 4>(am, it.row, static_cast<int>(it.ch));
+    else tree_resolve_item(a, am, static_cast<int>(it.row));
 }
 
 }  // namespace
 
 hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(static_cast<uint32_t>(a.am.rows * a.am.nchunk + a.B)), blk(kWG);
+    const dim3 g(argmax_grid(a.am.rows, a.am.nchunk, a.B)), blk(kWG);
     if (dtype == 1) k_greedy<Bf16><<<g, blk, 0, s>>>(a);
     else k_greedy<F32><<<g, blk, 0, s>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_tree(const TreeArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(static_cast<uint32_t>(a.am.rows * a.am.nchunk + a.B)), blk(kWG);
+    const dim3 g(argmax_grid(a.am.rows, a.am.nchunk, a.B)), blk(kWG);
     if (dtype == 1) k_tree<Bf16><<<g, blk, 0, s>>>(a);
     else k_tree<F32><<<g, blk, 0, s>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_tree_dyn(const TreeDynArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(static_cast<uint32_t>(a.am.rows * a.am.nchunk + a.B)), blk(kWG);
+    const dim3 g(argmax_grid(a.am.rows, a.am.nchunk, a.B)), blk(kWG);
     if (dtype == 1) k_tree_dyn<Bf16><<<g, blk, 0, s>>>(a);
     else k_tree_dyn<F32><<<g, blk, 0, s>>>(a);
     return hipGetLastError();

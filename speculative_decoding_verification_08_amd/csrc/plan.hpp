@@ -73,8 +73,9 @@ inline FastDiv make_fastdiv(uint32_t d) {  // d >= 1
     f.m = static_cast<uint32_t>(((1ull << 32) * ((1ull << l) - d)) / d + 1);
     return f;
 }
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-    return (__umulhi(n, f.m) + n) >> f.s;
+__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    const uint32_t hi = static_cast<uint32_t>((static_cast<uint64_t>(n) * f.m) >> 32);
+    return (hi + n) >> f.s;  // hi < n for n < 2^31, so the sum does not wrap
 }
 
 // Chain verify, all kernels.

@@ -16,10 +16,13 @@
 // row's k best from the row's lists on one wavefront.
 #include "device.hpp"
 #include "handover.hpp"
+#include "grid_order.hpp"
 #include "plan.hpp"
 #include "topk.hpp"
 
 namespace sv {
+
+static_assert(kTopkGroupRows == kWaves, "a merge workgroup holds one wavefront per row");
 namespace {
 
 constexpr int kCandPerWave = 64;  // candidates compacted into LDS per wavefront of a chunk
@@ -362,57 +365,29 @@ __device__ __forceinline__ void topk_chunk(const TopkArgs &a, int64_t row, int c
     }
 }
 
-// Grid order, in groups of kWaves rows (G = ceil(rows / kWaves) groups) and
-// with L = a.lag groups: the chunks of groups 0..L-1; then for each group
-// q >= L its chunks followed by one merge workgroup for group q - L (a
-// wavefront per row); then the merges of the last L groups.  A merge thus
-// trails its rows' chunks by about L groups of workgroups, by when they have
-// usually finished, so merge workgroups rarely wait and the streaming runs
-// on.
+// The order of topk_item: a merge trails its rows' chunks by about `lag`
+// groups of workgroups, by when they have usually finished, so merge
+// workgroups rarely wait and the streaming runs on.
 template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_topk(TopkArgs a) {
     if (a.tag_src) a.tag = *a.tag_src;  // a graph replay's tag
-    const int64_t nch = a.nchunk, L = a.lag, g = blockIdx.x, R = a.rows;
-    const int64_t G = (R + kWaves - 1) / kWaves;
-    auto group_chunks = [&](int64_t q) { return (min(R, (q + 1) * kWaves) - q * kWaves) * nch; };
-    // Chunk items before group q: kWaves * nch per full group.
-    const int64_t full = kWaves * nch, head = L < G ? L * full : R * nch;
-    int64_t row = -1, ch = 0, mgroup = -1;
-    if (g < head) {
-        row = g / nch;
-        ch = g % nch;
-    } else {
-        const int64_t h = g - head, nbody = G - L;  // groups with chunks after the head
-        // Body blocks: group L + b's chunks, then one merge (group b); the
-        // last group may be partial.
-        const int64_t blk = h / (full + 1), off = h % (full + 1);
-        if (blk < nbody - 1 || (blk == nbody - 1 && off <= group_chunks(G - 1))) {
-            const int64_t q = L + blk, nc = group_chunks(q);
-            if (off < nc) {
-                row = q * kWaves + off / nch;
-                ch = off % nch;
-            } else {
-                mgroup = blk;
-            }
-        } else {
-            const int64_t tail0 = (nbody - 1) * (full + 1) + group_chunks(G - 1) + 1;
-            mgroup = nbody > 0 ? G - L + (h - tail0) : h;
-        }
-    }
+    const int64_t R = a.rows;
+    const TopkItem it = topk_item(blockIdx.x, R, a.nchunk, a.lag);
+    const int64_t row = it.row, ch = it.ch, mgroup = it.mgroup;
     if (mgroup < 0) {
         topk_chunk<DT, VecOk>(a, row, static_cast<int>(ch));
         return;
     }
-    const int64_t mrow = mgroup * kWaves + threadIdx.x / kWave;
+    const int64_t mrow = mgroup * kTopkGroupRows + threadIdx.x / kWave;
     if (mrow >= R) return;
-    if (nch * a.k <= 2 * kWave) topk_merge_small(a, mrow);
+    if (static_cast<int64_t>(a.nchunk) * a.k <= 2 * kWave) topk_merge_small(a, mrow);
     else topk_merge(a, mrow);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(static_cast<uint32_t>(a.rows * a.nchunk + (a.rows + kWaves - 1) / kWaves)), blk(kWG);
+    const dim3 g(topk_grid(a.rows, a.nchunk)), blk(kWG);
     if (dtype == 1) {
         if (a.V % Bf16::kVec == 0) k_topk<Bf16, true><<<g, blk, 0, s>>>(a);
         else k_topk<Bf16, false><<<g, blk, 0, s>>>(a);

@@ -1,0 +1,54 @@
+"""Host emulation of the one-launch grid orders (chain, greedy and static
+tree, per-sequence trees in both orders, top-k): every workgroup of each
+launch goes through the decode the kernels run, with the arguments the C ABI
+plans, and must cover each item once, after every item it waits for, with
+every index in bounds.  Planted mistakes in the decode arguments must be
+caught.  Runs on the CPU (hipcc's host pass)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "tests", "c", "grid_order_check.cpp")
+CSRC = os.path.join(ROOT, "speculative_decoding_verification_08_amd", "csrc")
+MUTANTS = {
+    1: "fast-division multiplier one too small",
+    2: "one-launch blocks of S workgroups instead of S + 1",
+    3: "bonus-row statistics end one workgroup early",
+    4: "one-launch draw items per sequence off by one",
+    5: "two-phase draw items per sequence off by one",
+    6: "compact tree order with rows of Nmax - 1",
+    7: "top-k chunks per row off by one",
+}
+
+
+def _hipcc():
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    pytest.skip("hipcc not found")
+
+
+@pytest.fixture(scope="module")
+def checker(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("grid_order") / "grid_order_check")
+    cmd = [_hipcc(), "-x", "hip", "--offload-host-only", "-O1", "-std=c++17", "-Wall",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", out, SRC]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=300)
+    return out
+
+
+def test_grid_orders_cover_every_item_after_its_dependencies(checker):
+    r = subprocess.run([checker], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    assert r.stdout.startswith("ok "), r.stdout
+    assert int(r.stdout.split()[1]) > 400
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=[MUTANTS[m] for m in sorted(MUTANTS)])
+def test_planted_schedule_mistakes_are_caught(checker, mutant):
+    r = subprocess.run([checker, str(mutant)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1, (MUTANTS[mutant], r.stdout, r.stderr[-2000:])
+    assert "failures" in r.stderr
