@@ -67,12 +67,21 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enums are 32-bit integers on both sides.  In C++ they get that fixed
+ * underlying type, so every int32 value a C caller passes (a bad dtype or
+ * mode included) is a valid value that the checks can reject. */
+#ifdef __cplusplus
+#define SPEC_ENUM_BASE : int32_t
+#else
+#define SPEC_ENUM_BASE
+#endif
+
+typedef enum SPEC_ENUM_BASE {
     SPEC_DTYPE_F32 = 0,  /* IEEE float32 logits                      */
     SPEC_DTYPE_BF16 = 1  /* bfloat16 logits (upper half of a float32) */
 } spec_dtype;
 
-typedef enum {
+typedef enum SPEC_ENUM_BASE {
     SPEC_MODE_CHAIN = 0,  /* spec_verify_chain (T > 0)           */
     SPEC_MODE_GREEDY = 1, /* spec_verify_greedy (T = 0, chain)   */
     SPEC_MODE_TREE = 2,   /* spec_verify_tree_greedy (T = 0)     */
@@ -80,7 +89,7 @@ typedef enum {
     SPEC_MODE_TOPK = 4      /* spec_draft_topk                     */
 } spec_mode;
 
-typedef enum {
+typedef enum SPEC_ENUM_BASE {
     SPEC_OK = 0,
     SPEC_ERR_INVALID_ARG = 1, /* a size, pointer, dtype, temperature or tree is invalid */
     SPEC_ERR_WORKSPACE = 2,   /* workspace missing or smaller than required            */
