@@ -3,16 +3,18 @@
 One step = one chain verify (row statistics, accept/reject, residual or bonus
 draw, emit) over one batch of the chain_t1_128k workload: B=64 sequences,
 K=5 drafts, V=128256, bf16 logits, T=1 (180,584,448 logit bytes).  Inputs are
-resident in HBM before timing; enough input sets rotate (3 here, 542 MB) that
-the 256 MB Infinity Cache cannot hold the working set between steps.
-`--workload` measures the other workloads the same way.
+resident in HBM before timing; enough logit sets rotate (3 here, 542 MB) that
+the 256 MB Infinity Cache cannot hold the working set between steps, and every
+timed step draws with uniforms of its own.  `--workload` measures the other
+workloads the same way.
 
 Prints one JSON line.  A chain step is one kernel (k_chain_fused: the
 statistics pass over every logit, the accept test, the residual or bonus draw
 and the emission), so `roofline` covers that kernel, i.e. the whole step,
 timed back to back with HIP events on the launch stream; the statistics pass
 alone (the two-phase entry point's first kernel) is reported beside it.
-`cpu_baseline` times the fp64 oracle on a bounded sample on the host.
+`cpu_baseline` times the fp64 oracle on a bounded sample on the host, on one
+thread and on the host threads the process may use.
 """
 from __future__ import annotations
 
@@ -173,30 +175,46 @@ def check(w, inp, gpu_out):
 
 
 def cpu_baseline(w, inp, budget_s: float, gpu_out):
-    """The oracle as it stands, single-threaded, on whole steps of the same
-    workload (for the KV commit, on one plane of the step, scaled)."""
+    """The oracle as it stands on whole steps of the same workload (for the KV
+    commit, on one plane of the step, scaled), timed twice: on one thread, and
+    with its sequences spread over the host threads this process may use
+    (OMP_NUM_THREADS when set, else its CPU affinity).  Each leg takes about
+    half of `budget_s`.  The oracle's results do not depend on the thread
+    count."""
+    import oracle
     scale, what = 1.0, "whole steps"
     if w.mode == "kv":
         inp = kv_sample(w, inp)
         scale, what = 1.0 / w.planes, f"steps on plane 0 of {w.planes} (rate scaled by 1/{w.planes})"
-    t0 = time.perf_counter()
-    steps = 0
-    while True:
-        oracle_step(w, inp)
-        steps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
+    host = host_cpu()
+
+    def leg(threads):
+        used = oracle.set_threads(threads)
+        oracle_step(w, inp)                     # untimed: first-touch and thread start-up
+        t0 = time.perf_counter()
+        steps = 0
+        while True:
+            oracle_step(w, inp)
+            steps += 1
+            if time.perf_counter() - t0 >= budget_s / 2:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": steps / dt * scale, "cores": used,
+                "sample": f"{steps} {what} of input set 0 of {w.name}, {used} thread(s), {dt:.1f} s"}
+    one = leg(1)
+    many = leg(host["threads_usable"])
+    oracle.set_threads(1)
     counts = check(w, inp, gpu_out)
     unit = {"topk": "top-k steps/s", "kv": "KV commit steps/s",
             "mask": "tree mask steps/s"}.get(w.mode, "verify steps/s")
-    return {"value": steps / dt * scale, "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": f"{steps} {what} of input set 0 of {w.name}, one thread, {dt:.1f} s",
-            "host": host_cpu(), "parity_on_sample": dict(counts)}
+    return {"value": many["value"], "unit": unit, "cores": many["cores"], "kind": "oracle",
+            "sample": many["sample"], "single_thread": one, "host": host,
+            "parity_on_sample": dict(counts)}
 
 
 def host_cpu() -> dict:
-    """The host the CPU leg ran on: CPU model and the threads the OS offers."""
+    """The host the CPU leg ran on: CPU model, the processors the OS shows
+    (nproc), and the threads this process may use."""
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -205,7 +223,11 @@ def host_cpu() -> dict:
                 break
     except OSError:
         pass
-    return {"cpu": model, "threads_available": os.cpu_count()}
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    usable = int(omp) if omp.isdigit() and int(omp) > 0 else affinity
+    return {"cpu": model, "nproc": os.cpu_count(), "affinity": affinity,
+            "OMP_NUM_THREADS": omp or None, "threads_usable": min(usable, affinity)}
 
 
 def graph_replay(make, sets, stream, G: int, steps: int) -> dict:
@@ -308,6 +330,7 @@ def main():
             for h in host_sets]
     stream = torch.cuda.current_stream(device)
     dt_code = sv.SPEC_DTYPE_BF16 if w.dtype == "bf16" else sv.SPEC_DTYPE_F32
+    step_launches = None   # per-step launches, where inputs change every step
 
     if w.mode == "chain":
         K = w.K
@@ -319,10 +342,11 @@ def main():
             return (sv.prepare_chain(s["target"], s["draft"], s["tokens"], s["u_accept"],
                                      s["u_sample"], w.T, out_t, out_a, ws, stream=st), (out_t, out_a))
 
+        stats_launches = [sv.spec_verify_chain_stats(s["target"], s["draft"], s["tokens"], w.T, ws,
+                                                     stream=stream, prepare=True) for s in sets]
+
         def stats_phase(i):
-            s = sets[i % nsets]
-            sv.spec_verify_chain_stats(s["target"], s["draft"], s["tokens"], w.T, ws,
-                                       stream=stream)
+            stats_launches[i % nsets]()
 
         def outputs():
             diag = torch.empty((B, K + 1, 4), dtype=torch.float32, device=device)
@@ -334,6 +358,16 @@ def main():
         dominant_name = "k_chain_fused (whole step)"
         io_bytes = 4 * B * K + 4 * B * (K + 1) + 4 * B * (K + 2)
         verified = B * K
+        # Fresh uniforms for every timed step: step i draws with the uniforms
+        # of workload step i, on logit set i mod nsets (all resident before
+        # timing starts).
+        nu = max(args.steps, 1)
+        uni = [W.chain_uniforms(w, i) for i in range(nu)]
+        ua_all = torch.from_numpy(np.stack([u[0] for u in uni])).to(device)
+        us_all = torch.from_numpy(np.stack([u[1] for u in uni])).to(device)
+        step_launches = [sv.prepare_chain(sets[i % nsets]["target"], sets[i % nsets]["draft"],
+                                          sets[i % nsets]["tokens"], ua_all[i], us_all[i], w.T, out_t,
+                                          out_a, ws, stream=stream) for i in range(nu)]
     elif w.mode == "greedy":
         K = w.K
         ws = sv.workspace(sv.SPEC_MODE_GREEDY, B, K, V, dt_code, device)
@@ -448,10 +482,10 @@ def main():
         io_bytes = 4 * B * N + 4 * B * (2 * D + 3)
         verified = B * (N - 1)
 
-    launches = [make(s, stream)[0] for s in sets]
+    launches = step_launches or [make(s, stream)[0] for s in sets]
 
     def step(i):
-        launches[i % nsets]()
+        launches[i % len(launches)]()
 
     done = 0
     if args.warmup is None:
@@ -527,7 +561,8 @@ def main():
     config = {"workload": w.name, "mode": w.mode, "B": B, "V": V, "logits": w.dtype,
               "input_sets_rotated": nsets, "logit_bytes_per_step": nbytes}
     if w.mode == "chain":
-        config.update(K=w.K, T=w.T)
+        config.update(K=w.K, T=w.T, uniforms=f"fresh each timed step ({len(launches)} sets)",
+                      arithmetic="fp32 exponentials and ratios, fp64 sums")
     elif w.mode == "greedy":
         config.update(K=w.K)
     elif w.mode == "tree_dyn":
@@ -559,7 +594,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"kv": "u8", "mask": "int32"}.get(w.mode, "f32"),
+        "dtype": {"kv": "u8", "mask": "int32"}.get(w.mode, w.dtype),
         "data": "synthetic",
         "config": config,
         "achieved_GBps": achieved_step,

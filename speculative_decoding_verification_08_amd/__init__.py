@@ -229,14 +229,16 @@ def spec_verify_chain_noalloc(target_logits, draft_logits, draft_tokens, u_accep
 
 
 def spec_verify_chain_stats(target_logits, draft_logits, draft_tokens, temperature: float,
-                            workspace_buf, *, stream=None):
-    """First phase of the chain verify (softmax statistics of every row into the workspace)."""
+                            workspace_buf, *, stream=None, prepare=False):
+    """First phase of the chain verify (softmax statistics of every row into the
+    workspace).  With `prepare`, returns a function that enqueues the call again."""
     dt, B, K, V = _chain_check(target_logits, draft_logits, None, None, None)
     _check_dev("draft_tokens", draft_tokens, torch.int32, (B, K))
     dev = target_logits.device
-    _call("spec_verify_chain_stats", _ptr(target_logits), _ptr(draft_logits), dt,
-          _ptr(draft_tokens), B, K, V, float(temperature), _ptr(workspace_buf),
-          workspace_buf.numel(), _stream(dev, stream))
+    return _enqueue(prepare, (target_logits, draft_logits, draft_tokens, workspace_buf),
+                    "spec_verify_chain_stats", _ptr(target_logits), _ptr(draft_logits), dt,
+                    _ptr(draft_tokens), B, K, V, ctypes.c_float(float(temperature)),
+                    _ptr(workspace_buf), ctypes.c_size_t(workspace_buf.numel()), _stream(dev, stream))
 
 
 def spec_verify_chain_sample(target_logits, draft_logits, draft_tokens, u_accept, u_sample,

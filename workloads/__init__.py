@@ -204,6 +204,12 @@ def _uniforms(w: Workload, step: int, B: int, K: int):
 
 # ---------------------------------------------------------------- public makers
 
+def chain_uniforms(w: Workload, step: int):
+    """The uniforms of chain step `step` alone (u_accept [B][K], u_sample [B]):
+    the same values chain_inputs(w, step) holds, without its logits."""
+    return _uniforms(w, step, w.B, w.K)
+
+
 def chain_inputs(w: Workload, step: int = 0) -> dict:
     """Inputs of one chain verify step: target [B][K+1][V], draft [B][K][V],
     tokens [B][K] int32, u_accept [B][K] f32, u_sample [B] f32, T, dtype."""
