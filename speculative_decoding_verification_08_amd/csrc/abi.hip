@@ -233,6 +233,7 @@ spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
     g.am.V = V;
     g.am.chunk = plan.chunk;
     g.am.nchunk = plan.nchunk;
+    g.am.fd_nch = make_fastdiv(plan.nchunk);
     const spec_status st = call_tag(workspace, stream, g.am.tag, g.am.tag_src);
     if (st != SPEC_OK) return st;
     g.am.partial = at<uint64_t>(workspace, plan.off_partial);
@@ -279,6 +280,7 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
     t.am.V = V;
     t.am.chunk = plan.chunk;
     t.am.nchunk = plan.nchunk;
+    t.am.fd_nch = make_fastdiv(plan.nchunk);
     const spec_status st = call_tag(workspace, stream, t.am.tag, t.am.tag_src);
     if (st != SPEC_OK) return st;
     t.am.partial = at<uint64_t>(workspace, plan.off_partial);
@@ -314,6 +316,7 @@ spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtyp
     t.am.V = V;
     t.am.chunk = plan.chunk;
     t.am.nchunk = plan.nchunk;
+    t.am.fd_nch = make_fastdiv(plan.nchunk);
     const spec_status st = call_tag(workspace, stream, t.am.tag, t.am.tag_src);
     if (st != SPEC_OK) return st;
     t.am.partial = at<uint64_t>(workspace, plan.off_partial);

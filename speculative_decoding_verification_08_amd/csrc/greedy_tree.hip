@@ -24,19 +24,21 @@ namespace sv {
 static_assert(kCompactTrees == kWave * kCountsPerLane, "one wavefront holds every count");
 namespace {
 
-template <class DT, int U>
+// With VecOk (V a multiple of the vector width) every chunk starts and ends
+// on a vector, so there is no unaligned head or tail to read one by one.
+template <class DT, int U, bool VecOk>
 __device__ __forceinline__ void argmax_item(const ArgmaxArgs &a, int64_t row, int ch) {
     constexpr int VEC = DT::kVec;
     const int64_t rbase = row * a.V;
     const int64_t g0 = rbase + static_cast<int64_t>(ch) * a.chunk;
     const int64_t g1 = min(g0 + a.chunk, rbase + a.V);
-    const Span s = split_span<VEC>(g0, g1);
+    const Span s = VecOk ? Span{g0, g0, g0 / VEC, g1 / VEC, g1, g1} : split_span<VEC>(g0, g1);
 
     // Each lane visits its elements in increasing index order, so a strict
     // comparison keeps the lowest index among equal values.
     float bv = -INFINITY;
     int32_t bi = INT32_MAX;
-    {
+    if (!VecOk) {
         const int64_t h = s.h0 + threadIdx.x;
         if (h < s.h1) {
             const float x = load_one<DT>(a.logits, h);
@@ -82,7 +84,7 @@ __device__ __forceinline__ void argmax_item(const ArgmaxArgs &a, int64_t row, in
                 bi = static_cast<int32_t>(v * VEC + i - rbase);
             }
     }
-    {
+    if (!VecOk) {
         const int64_t t = s.t0 + threadIdx.x;
         if (t < s.t1) {
             const float x = load_one<DT>(a.logits, t);
@@ -430,7 +432,7 @@ __device__ __forceinline__ uint32_t locate_row(const TreeDynArgs &a, uint32_t R,
     return T;
 }
 
-template <class DT>
+template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_tree_dyn(TreeDynArgs a) {
     // The argument block stays untouched (writing into it would copy it to
     // scratch); the argmax arguments with the call's tag are a local copy.
@@ -450,29 +452,35 @@ __global__ __launch_bounds__(kWG) void k_tree_dyn(TreeDynArgs a) {
         it = tree_dyn_full_item(g, nch, static_cast<uint32_t>(a.am.rows), static_cast<uint32_t>(a.Nmax),
                                 a.node_count);
     }
-    if (it.argmax) argmax_item<DT, 4>(am, it.row, static_cast<int>(it.ch));
+    if (it.argmax) argmax_item<DT, 4, VecOk>(am, it.row, static_cast<int>(it.ch));
     else if (it.resolve) tree_dyn_resolve_item(a, am, static_cast<int>(it.row));
 }
 
-template <class DT>
+template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_greedy(GreedyArgs a) {
     // The argument block stays untouched (writing into it would copy it to
     // scratch); the argmax arguments with the call's tag are a local copy.
     ArgmaxArgs am = a.am;
     if (am.tag_src) am.tag = *am.tag_src;  // a graph replay's tag
-    const ArgmaxItem it = argmax_item_of(blockIdx.x, a.am.nchunk, static_cast<uint32_t>(a.am.rows));
-    if (it.argmax) argmax_item<DT, 4>(am, it.row, static_cast<int>(it.ch));
+    // The argmax items' arguments in one batch ahead of the decode, so no
+    // second round of argument loads stands before the first logit load.
+    asm volatile("" ::"s"(a.am.logits), "s"(a.am.V), "s"(a.am.chunk), "s"(a.am.partial), "s"(a.am.tag));
+    const ArgmaxItem it = argmax_item_of(blockIdx.x, a.am.nchunk, a.am.fd_nch, static_cast<uint32_t>(a.am.rows));
+    if (it.argmax) argmax_item<DT, 4, VecOk>(am, it.row, static_cast<int>(it.ch));
     else greedy_resolve_item(a, am, static_cast<int>(it.row));
 }
 
-template <class DT>
+template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_tree(TreeArgs a) {
     // The argument block stays untouched (writing into it would copy it to
     // scratch); the argmax arguments with the call's tag are a local copy.
     ArgmaxArgs am = a.am;
     if (am.tag_src) am.tag = *am.tag_src;  // a graph replay's tag
-    const ArgmaxItem it = argmax_item_of(blockIdx.x, a.am.nchunk, static_cast<uint32_t>(a.am.rows));
-    if (it.argmax) argmax_item<DT, 4>(am, it.row, static_cast<int>(it.ch));
+    // The argmax items' arguments in one batch ahead of the decode, so no
+    // second round of argument loads stands before the first logit load.
+    asm volatile("" ::"s"(a.am.logits), "s"(a.am.V), "s"(a.am.chunk), "s"(a.am.partial), "s"(a.am.tag));
+    const ArgmaxItem it = argmax_item_of(blockIdx.x, a.am.nchunk, a.am.fd_nch, static_cast<uint32_t>(a.am.rows));
+    if (it.argmax) argmax_item<DT, 4, VecOk>(am, it.row, static_cast<int>(it.ch));
     else tree_resolve_item(a, am, static_cast<int>(it.row));
 }
 
@@ -480,22 +488,40 @@ __global__ __launch_bounds__(kWG) void k_tree(TreeArgs a) {
 
 hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t s) {
     const dim3 g(argmax_grid(a.am.rows, a.am.nchunk, a.B)), blk(kWG);
-    if (dtype == 1) k_greedy<Bf16><<<g, blk, 0, s>>>(a);
-    else k_greedy<F32><<<g, blk, 0, s>>>(a);
+    const bool vec = a.am.V % (dtype == 1 ? Bf16::kVec : F32::kVec) == 0;
+    if (dtype == 1) {
+        if (vec) k_greedy<Bf16, true><<<g, blk, 0, s>>>(a);
+        else k_greedy<Bf16, false><<<g, blk, 0, s>>>(a);
+    } else {
+        if (vec) k_greedy<F32, true><<<g, blk, 0, s>>>(a);
+        else k_greedy<F32, false><<<g, blk, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_tree(const TreeArgs &a, int dtype, hipStream_t s) {
     const dim3 g(argmax_grid(a.am.rows, a.am.nchunk, a.B)), blk(kWG);
-    if (dtype == 1) k_tree<Bf16><<<g, blk, 0, s>>>(a);
-    else k_tree<F32><<<g, blk, 0, s>>>(a);
+    const bool vec = a.am.V % (dtype == 1 ? Bf16::kVec : F32::kVec) == 0;
+    if (dtype == 1) {
+        if (vec) k_tree<Bf16, true><<<g, blk, 0, s>>>(a);
+        else k_tree<Bf16, false><<<g, blk, 0, s>>>(a);
+    } else {
+        if (vec) k_tree<F32, true><<<g, blk, 0, s>>>(a);
+        else k_tree<F32, false><<<g, blk, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_tree_dyn(const TreeDynArgs &a, int dtype, hipStream_t s) {
     const dim3 g(argmax_grid(a.am.rows, a.am.nchunk, a.B)), blk(kWG);
-    if (dtype == 1) k_tree_dyn<Bf16><<<g, blk, 0, s>>>(a);
-    else k_tree_dyn<F32><<<g, blk, 0, s>>>(a);
+    const bool vec = a.am.V % (dtype == 1 ? Bf16::kVec : F32::kVec) == 0;
+    if (dtype == 1) {
+        if (vec) k_tree_dyn<Bf16, true><<<g, blk, 0, s>>>(a);
+        else k_tree_dyn<Bf16, false><<<g, blk, 0, s>>>(a);
+    } else {
+        if (vec) k_tree_dyn<F32, true><<<g, blk, 0, s>>>(a);
+        else k_tree_dyn<F32, false><<<g, blk, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -38,9 +38,9 @@ struct ChainItem {
 // statistics items, a resolver, nchunk bonus-row statistics items, D draw
 // items, a finisher and a bonus item, laid out as
 //   block k   the statistics of sequence k, then the resolver of k - 1;
+//   then      the resolver of B - 1;
 //   bonus     the bonus rows' statistics, sequence by sequence;
-//   tail      the resolver of B - 1, every draw item, every finisher, every
-//             bonus item.
+//   tail      every draw item, every finisher, every bonus item.
 __host__ __device__ __forceinline__ ChainItem chain_fused_item(uint32_t g, const ChainArgs &a) {
     const uint32_t S = a.S, D = a.D, B = a.B;
     ChainItem it{kItemStats, 0, 0};
@@ -51,26 +51,26 @@ __host__ __device__ __forceinline__ ChainItem chain_fused_item(uint32_t g, const
         it.kind = q < S ? kItemStats : kItemResolver;
         it.b = q < S ? kk + 1 : kk;
         it.p = q;
+    } else if (g == a.blocks_end) {
+        it.kind = kItemResolver;
+        it.b = B - 1;
     } else if (g < a.bon_end) {
-        const uint32_t h = g - a.blocks_end;
+        const uint32_t h = g - a.blocks_end - 1;
         it.b = fdiv(h, a.fd_nch);
         it.p = h - it.b * a.nchunk;
         it.kind = kItemBonusStats;
     } else {
         const uint32_t h = g - a.bon_end;
-        if (h == 0) {
-            it.kind = kItemResolver;
-            it.b = B - 1;
-        } else if (h - 1 < B * D) {
+        if (h < B * D) {
             it.kind = kItemDraw;
-            it.b = fdiv(h - 1, a.fd_D);
-            it.p = h - 1 - it.b * D;
-        } else if (h - 1 - B * D < B) {
+            it.b = fdiv(h, a.fd_D);
+            it.p = h - it.b * D;
+        } else if (h - B * D < B) {
             it.kind = kItemFinisher;
-            it.b = h - 1 - B * D;
+            it.b = h - B * D;
         } else {
             it.kind = kItemBonus;
-            it.b = h - 1 - B * D - B;
+            it.b = h - B * D - B;
         }
     }
     return it;
@@ -78,7 +78,7 @@ __host__ __device__ __forceinline__ ChainItem chain_fused_item(uint32_t g, const
 
 // Workgroups of the one-launch grid and of the draws of the two-phase form.
 inline uint32_t chain_fused_grid(const ChainArgs &a) {
-    return a.bon_end + 1 + static_cast<uint32_t>(a.B) * (a.D + 2);
+    return a.bon_end + static_cast<uint32_t>(a.B) * (a.D + 2);
 }
 inline uint32_t chain_draw_grid(const ChainArgs &a) { return static_cast<uint32_t>(a.B) * (a.D + 3); }
 
@@ -168,10 +168,11 @@ struct ArgmaxItem {
     uint32_t row;  // argmax: the row; resolve: the sequence
     uint32_t ch;
 };
-__host__ __device__ __forceinline__ ArgmaxItem argmax_item_of(uint32_t g, uint32_t nch, uint32_t rows) {
+__host__ __device__ __forceinline__ ArgmaxItem argmax_item_of(uint32_t g, uint32_t nch, FastDiv fd_nch,
+                                                              uint32_t rows) {
     const uint32_t nam = rows * nch;
     if (g < nam) {
-        const uint32_t row = g / nch;
+        const uint32_t row = fdiv(g, fd_nch);
         return ArgmaxItem{true, row, g - row * nch};
     }
     return ArgmaxItem{false, g - nam, 0};

@@ -110,6 +110,7 @@ struct ArgmaxArgs {
     const void *logits;
     int64_t rows;
     int32_t V, chunk, nchunk;
+    FastDiv fd_nch;          // division by nchunk
     uint32_t tag;            // this call's tag (upper half of every handed-over word)
     const uint32_t *tag_src; // nullable: read the tag from this device word instead (graph replays)
     uint64_t *partial;       // [rows][nchunk][2] tagged (value bits, index)

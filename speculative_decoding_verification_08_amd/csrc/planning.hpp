@@ -94,7 +94,7 @@ inline uint32_t chain_schedule(ChainArgs &a) {
     if (total > 0x7fffffffull) return 0;
     a.fd_S1 = make_fastdiv(static_cast<uint32_t>(S + 1));
     a.blocks_end = static_cast<uint32_t>(S + (B - 1) * (S + 1));
-    a.bon_end = static_cast<uint32_t>(a.blocks_end + B * nch);
+    a.bon_end = static_cast<uint32_t>(a.blocks_end + 1 + B * nch);
     return static_cast<uint32_t>(total);
 }
 

@@ -194,7 +194,8 @@ static void check_argmax(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_
     const uint32_t n = argmax_grid(rows, nch, B);
     std::vector<int64_t> am(rows * nch, -1), res(B, -1);
     for (uint32_t g = 0; g < n; ++g) {
-        const ArgmaxItem it = argmax_item_of(g, static_cast<uint32_t>(nch), static_cast<uint32_t>(rows));
+        const ArgmaxItem it = argmax_item_of(g, static_cast<uint32_t>(nch), make_fastdiv(static_cast<uint32_t>(nch)),
+                                             static_cast<uint32_t>(rows));
         if (it.argmax) {
             CHECK(it.row < rows && it.ch < nch, "g=%u", g);
             if (it.row < rows && it.ch < nch) {
