@@ -91,6 +91,11 @@ spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype,
     a.partial = at<uint64_t>(ws, plan.off_partial);
     a.sums = at<uint64_t>(ws, plan.off_sums);
     a.rec = at<uint64_t>(ws, plan.off_rec);
+    a.pairs = at<uint64_t>(ws, plan.off_pairs);
+    // Skipping bonus-row chunks after a rejection costs each bonus-row item
+    // one read of its record first: worth it once the bonus rows are more
+    // than a few hundred chunks.
+    a.gate_bonus = static_cast<int64_t>(B) * plan.nchunk >= 512;
     return SPEC_OK;
 }
 
@@ -194,7 +199,16 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
     if (st != SPEC_OK) return st;
     st = call_tag(workspace, stream, a.tag, a.tag_src);
     if (st != SPEC_OK) return st;
-    if (chain_schedule(a) != 0) return launch_status(launch_chain_fused(a, dtype, stream));
+    // The position-major order when no per-position diagnostics are asked for
+    // (they need every position's statistics) and one position's items fill
+    // the chip (smaller batches wait on its resolvers' chain instead).  Its
+    // rows after a rejection are skipped only for long drafts: the check
+    // delays every gated item by one read, which measured slower for K = 5
+    // (64 x 5 x 128256 bf16: 43.0 against 38.7 us) and faster for K = 8
+    // (256 x 8 x 151936 fp32: 384 against 436 us).
+    a.early_exit = out_diag == nullptr && 2ll * plan.nchunk * B >= 2048 && chain_ex_schedule(a) != 0;
+    a.gate_rows = a.early_exit && K >= 6;
+    if (a.early_exit || chain_schedule(a) != 0) return launch_status(launch_chain_fused(a, dtype, stream));
     // Too large for one grid: the two kernels of the phase entry points, the
     // draws reading the statistics under this call's own tag.
     st = launch_status(launch_chain_stats(a, dtype, stream));

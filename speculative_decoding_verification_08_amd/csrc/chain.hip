@@ -567,6 +567,183 @@ __device__ __forceinline__ void resolver_item(const ChainArgs &a, int b, float *
     }
 }
 
+// ------------------------------------------------------------ position-major form
+
+// Statistics of target row k and draft row k of sequence b, merged exactly as
+// resolve_local merges a row (lane i of a group of 16 folds chunks i, i + 16,
+// ... in order in double precision, then the same DPP tree), so P_k and Q_k
+// come out bit for bit as the sequence resolver's.  Group 0 takes the target
+// row, group 1 the draft row; wavefront 0 reads until every word carries
+// `ptag` (bounded).  Returns false if a word did not come in time.
+__device__ __forceinline__ bool pair_stats(const ChainArgs &a, int b, int k, uint32_t ptag, float &rt,
+                                           float &zt, float &rd, float &zd) {
+    constexpr int kGroup = 16;
+    __shared__ float s_ref[2], s_z[2];
+    __shared__ int s_ok;
+    const int tid = threadIdx.x, K = a.K, nch = a.nchunk;
+    if (tid < kWave) {
+        const int grp = tid / kGroup, gl = tid % kGroup;
+        const int row = grp == 0 ? k : K + 1 + k;
+        const uint64_t *part = a.partial + 2 * ((static_cast<int64_t>(b) * (2 * K + 1) + row) * nch);
+        const uint64_t t0 = wall_clock64();
+        float ref;
+        double z;
+        bool fresh;
+        for (;;) {
+            ref = -INFINITY;
+            z = 0.0;
+            bool mine = true;
+            if (grp < 2) {
+                for (int i = gl; i < nch; i += kGroup) {
+                    const uint64_t pr = fetch(part + 2 * i), pz = fetch(part + 2 * i + 1);
+                    mine = mine && current(pr, ptag) && current(pz, ptag);
+                    mz_merge_d(ref, z, word_f32(pr), static_cast<double>(word_f32(pz)));
+                }
+            }
+            fresh = __all(mine);
+            if (fresh || wall_clock64() - t0 > kWaitTicks) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        mz_row_merge_d(ref, z);
+        if (grp < 2 && gl == kGroup - 1) {
+            s_ref[grp] = ref;
+            s_z[grp] = static_cast<float>(z);
+        }
+        if (tid == 0) s_ok = fresh;
+    }
+    __syncthreads();
+    rt = s_ref[0];
+    zt = s_z[0];
+    rd = s_ref[1];
+    zd = s_z[1];
+    return s_ok != 0;
+}
+
+// Publishes sequence b's record: j, then row j's (ref, 1/z) of the target and
+// the draft (zeros unless 0 <= j < K).
+__device__ __forceinline__ void publish_record(const ChainArgs &a, int b, uint32_t tag, int j, float rt,
+                                               float izt, float rd, float izd) {
+    uint64_t *rec = a.rec + kRecWords * static_cast<int64_t>(b);
+    const bool r = j >= 0 && j < a.K;
+    publish_f32(rec + 1, tag, r ? rt : 0.f);
+    publish_f32(rec + 2, tag, r ? izt : 0.f);
+    publish_f32(rec + 3, tag, r ? rd : 0.f);
+    publish_f32(rec + 4, tag, r ? izd : 0.f);
+    publish(rec, tag, static_cast<uint32_t>(j));
+}
+
+// Pair resolver of position k of sequence b (position-major form).  It waits
+// (bounded) for the outcomes of positions 0..k-1 of the sequence; if one of
+// them ended the accept tests it records a skip and stops.  Otherwise it
+// merges the statistics of target row k and draft row k, takes the accept
+// test u < P/Q (strict; Q = 0 accepts iff P > 0) as the sequence resolver
+// does, and publishes the outcome.  The first rejecting position publishes
+// the sequence's record (j = k), and so does the last position when every
+// draft is accepted (j = K).  A word that does not come in time fails the
+// sequence (record j = -1).
+template <class DT>
+__device__ __forceinline__ void pair_resolver_item(const ChainArgs &a, int b, int k) {
+    __shared__ int s_prev;
+    const int K = a.K, V = a.V, tid = threadIdx.x, lane = tid % kWave;
+    const uint32_t tag = a.tag_src ? *a.tag_src : a.tag;
+    uint64_t *pairs = a.pairs + static_cast<int64_t>(b) * K;
+    // The drafted token's logits and the uniform, issued before anything waits.
+    float lt = 0.f, ld = 0.f, u = 0.f;
+    if (tid == 0) {
+        const int x = min(max(a.tokens[static_cast<int64_t>(b) * K + k], 0), V - 1);
+        lt = load_one<DT>(a.target, (static_cast<int64_t>(b) * (K + 1) + k) * V + x);
+        ld = load_one<DT>(a.draft, (static_cast<int64_t>(b) * K + k) * V + x);
+        u = a.u_accept[static_cast<int64_t>(b) * K + k];
+    }
+    if (tid < kWave) {
+        static_assert(kMaxK <= kWave, "one earlier position per lane");
+        const uint64_t t0 = wall_clock64();
+        uint64_t v;
+        bool fresh;
+        for (;;) {
+            v = lane < k ? fetch(pairs + lane) : tagged(tag, kPairAccept);
+            fresh = __all(current(v, tag));
+            if (fresh || wall_clock64() - t0 > kWaitTicks) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const bool stop = __any(static_cast<uint32_t>(v) != kPairAccept);
+        if (lane == 0) s_prev = !fresh ? 2 : (stop ? 1 : 0);
+    }
+    __syncthreads();
+    if (s_prev != 0) {
+        if (s_prev == 2) fail_sequence(a, b);
+        if (tid == 0) {
+            if (s_prev == 2) publish_record(a, b, tag, -1, 0.f, 0.f, 0.f, 0.f);
+            publish(pairs + k, tag, s_prev == 2 ? kPairFail : kPairSkip);
+        }
+        return;
+    }
+    float rt, zt, rd, zd;
+    if (!pair_stats(a, b, k, tag, rt, zt, rd, zd)) {
+        fail_sequence(a, b);
+        if (tid == 0) {
+            publish_record(a, b, tag, -1, 0.f, 0.f, 0.f, 0.f);
+            publish(pairs + k, tag, kPairFail);
+        }
+        return;
+    }
+    if (tid == 0) {
+        const float P = exp2_hw(fmaf(lt, a.c, -rt)) / zt;
+        const float Q = exp2_hw(fmaf(ld, a.c, -rd)) / zd;
+        const bool reject = !(Q > 0.f ? (u < P / Q) : (P > 0.f));
+        if (a.out_diag) {
+            float *dg = a.out_diag + 4 * (static_cast<int64_t>(b) * (K + 1) + k);
+            dg[0] = P;
+            dg[1] = Q;
+            dg[2] = Q > 0.f ? P / Q : (P > 0.f ? INFINITY : 0.f);
+        }
+        if (reject) publish_record(a, b, tag, k, rt, 1.f / zt, rd, 1.f / zd);
+        else if (k == K - 1) publish_record(a, b, tag, K, 0.f, 0.f, 0.f, 0.f);
+        publish(pairs + k, tag, reject ? kPairReject : kPairAccept);
+    }
+}
+
+// A hand-over word read through the caches, without waiting: it may be stale
+// (an earlier value of this call's word, or a word of an earlier call), never
+// wrong, and a stale word only costs the skip it would have allowed.  The
+// device-scope read measured no better and delays the item more.
+__device__ __forceinline__ uint64_t plain_word(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Whether a statistics item of position k >= 2 of sequence b may skip its
+// chunk: a published outcome of a position up to k - 2 ended the sequence's
+// accept tests.  Uniform over the workgroup (thread 0 reads, LDS shares).
+__device__ __forceinline__ bool rows_not_needed(const ChainArgs &a, int b, int k) {
+    __shared__ int s_skip;
+    if (threadIdx.x == 0) {
+        const uint32_t tag = a.tag_src ? *a.tag_src : a.tag;
+        const uint64_t *pairs = a.pairs + static_cast<int64_t>(b) * a.K;
+        bool skip = false;
+        for (int i = 0; i + 2 <= k; ++i) {
+            const uint64_t v = plain_word(pairs + i);
+            skip = skip || (current(v, tag) && static_cast<uint32_t>(v) != kPairAccept);
+        }
+        s_skip = skip;
+    }
+    __syncthreads();
+    return s_skip != 0;
+}
+
+// Whether a bonus-row statistics item of sequence b may skip its chunk: the
+// sequence's record, already published, says a draft was rejected (or the
+// resolve failed).  Uniform over the workgroup.
+__device__ __forceinline__ bool bonus_not_needed(const ChainArgs &a, int b) {
+    __shared__ int s_skip;
+    if (threadIdx.x == 0) {
+        const uint32_t tag = a.tag_src ? *a.tag_src : a.tag;
+        const uint64_t v = plain_word(a.rec + kRecWords * static_cast<int64_t>(b));
+        s_skip = current(v, tag) && static_cast<int32_t>(static_cast<uint32_t>(v)) != a.K;
+    }
+    __syncthreads();
+    return s_skip != 0;
+}
+
 // Wavefront 0 waits (bounded) until every word of sequence b's record
 // carries `tag`, and shares it through LDS.  Returns false if it did not in
 // time; else j (-1 for a failed resolve) and row j's statistics.
@@ -853,13 +1030,22 @@ __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
     else bonus_item<DT, VecOk, false>(a, b, lds);
 }
 
-// The whole chain verify in one launch, in the order of chain_fused_item.
-// Each resolver finds its statistics done or nearly so, and the stream of
-// logits runs undisturbed: draws placed among the statistics measured slower
-// at every lag tried (their second read of row j takes slots and bandwidth
-// from the stream), so the second reads all come after it, where the bonus
-// draws, which need none, also run.
-template <class DT, bool VecOk>
+// The whole chain verify in one launch, in one of three orders (each its own
+// kernel, so that each carries only its own decode and item kinds: an unused
+// branch measured 4 us slower on 64 x 5 x 128256 bf16 through the scalar
+// registers it cost the statistics items):
+//   kSeqMajor        chain_fused_item, one resolver per sequence;
+//   kPosMajor        chain_ex_item, one pair resolver per position;
+//   kPosMajorGated   the same, and statistics items of position k >= 2 skip
+//                    their chunk after a rejection at a position up to k - 2.
+// Sequence-major: each resolver finds its statistics done or nearly so, and
+// the stream of logits runs undisturbed: draws placed among the statistics
+// measured slower at every lag tried (their second read of row j takes slots
+// and bandwidth from the stream), so the second reads all come after it,
+// where the bonus draws, which need none, also run.
+enum ChainOrder : int { kSeqMajor = 0, kPosMajor = 1, kPosMajorGated = 2 };
+
+template <class DT, bool VecOk, int Order>
 __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
     __shared__ __align__(16) float lds[kDrawLds];
     // The statistics items' arguments are loaded with the schedule's, in one
@@ -868,15 +1054,24 @@ __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
     // loads before its first logit load.
     asm volatile("" ::"s"(a.target), "s"(a.draft), "s"(a.partial), "s"(a.c), "s"(a.V), "s"(a.chunk),
                  "s"(a.tag), "s"(a.tag_src));
-    const ChainItem it = chain_fused_item(blockIdx.x, a);
+    const ChainItem it = Order == kSeqMajor ? chain_fused_item(blockIdx.x, a) : chain_ex_item(blockIdx.x, a);
     const int b = static_cast<int>(it.b);
     if (it.kind == kItemStats) {
         int row, ch;
         chain_stats_row(it.p, a, row, ch);
+        if constexpr (Order == kPosMajorGated) {
+            const int pos = row <= a.K ? row : row - a.K - 1;
+            if (pos >= 2 && rows_not_needed(a, b, pos)) return;
+        }
         stats_item<DT, VecOk>(a, it.b, row, ch);
     } else if (it.kind == kItemBonusStats) {
+        // The bonus row matters only when every draft is accepted; after a
+        // rejection already recorded its chunk is not read.
+        if (a.gate_bonus && bonus_not_needed(a, b)) return;
         stats_item<DT, VecOk>(a, it.b, a.K, static_cast<int>(it.p));
-    } else if (it.kind == kItemResolver) {
+    } else if (Order != kSeqMajor && it.kind == kItemPair) {
+        pair_resolver_item<DT>(a, b, static_cast<int>(it.p));
+    } else if (Order == kSeqMajor && it.kind == kItemResolver) {
         resolver_item<DT, true>(a, b, lds);
     } else if (it.kind == kItemDraw) {
         draw_item<DT, VecOk>(a, b, static_cast<int>(it.p), lds);
@@ -885,6 +1080,13 @@ __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
     } else {
         bonus_item<DT, VecOk, true>(a, b, lds);
     }
+}
+
+template <class DT, bool VecOk>
+void launch_fused_order(const ChainArgs &a, dim3 g, hipStream_t s) {
+    if (!a.early_exit) k_chain_fused<DT, VecOk, kSeqMajor><<<g, kWG, 0, s>>>(a);
+    else if (!a.gate_rows) k_chain_fused<DT, VecOk, kPosMajor><<<g, kWG, 0, s>>>(a);
+    else k_chain_fused<DT, VecOk, kPosMajorGated><<<g, kWG, 0, s>>>(a);
 }
 
 }  // namespace
@@ -902,13 +1104,13 @@ hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(chain_fused_grid(a)), blk(kWG);
+    const dim3 g(a.early_exit ? chain_ex_grid(a) : chain_fused_grid(a));
     if (dtype == 1) {
-        if (a.V % Bf16::kVec == 0) k_chain_fused<Bf16, true><<<g, blk, 0, s>>>(a);
-        else k_chain_fused<Bf16, false><<<g, blk, 0, s>>>(a);
+        if (a.V % Bf16::kVec == 0) launch_fused_order<Bf16, true>(a, g, s);
+        else launch_fused_order<Bf16, false>(a, g, s);
     } else {
-        if (a.V % F32::kVec == 0) k_chain_fused<F32, true><<<g, blk, 0, s>>>(a);
-        else k_chain_fused<F32, false><<<g, blk, 0, s>>>(a);
+        if (a.V % F32::kVec == 0) launch_fused_order<F32, true>(a, g, s);
+        else launch_fused_order<F32, false>(a, g, s);
     }
     return hipGetLastError();
 }

@@ -22,6 +22,8 @@ constexpr int kDrawChunkBytes = kStatChunkBytes;
 // top-k merges trail their rows' chunks by about this many workgroups.
 constexpr int kResidentWGs = 2048;
 constexpr int kRecWords = 8;       // words per sequence record (five used)
+// Outcome of one position's accept test (the low half of its tagged word).
+constexpr uint32_t kPairAccept = 0, kPairReject = 1, kPairSkip = 2, kPairFail = 3;
 constexpr int kMaxDrawChunks = kMaxStatChunks;  // draw chunks per row (two per lane of a wavefront)
 // LDS words of a draw workgroup: its sequence's row statistics (ref, z), the
 // vector searched in the crossing chunk (4 words per row, target and draft)
@@ -39,7 +41,7 @@ struct Plan {
     int nchunk = 0;        // chunks per row, first pass
     int chunk2 = 0;        // elements per chunk, residual / bonus pass (chain)
     int nchunk2 = 0;       // chunks per row, residual / bonus pass (chain)
-    size_t off_partial = 0, off_sums = 0, off_rec = 0;
+    size_t off_partial = 0, off_sums = 0, off_rec = 0, off_pairs = 0;
     size_t bytes = 0;      // total workspace
 };
 
@@ -97,6 +99,16 @@ struct ChainArgs {
     // statistics and resolvers end, and where the bonus rows' statistics end.
     uint32_t S, D, blocks_end, bon_end;
     FastDiv fd_nch, fd_D, fd_S1;
+    // Position-major one-launch order (early exit): the items of one position
+    // of every sequence (L = 2 nchunk B), where the blocks of a pair
+    // resolvers' run and a position's items end, and divisions by 2 nchunk
+    // and by B + L.
+    bool early_exit;
+    bool gate_rows;          // position-major statistics skip rows after a rejection
+    bool gate_bonus;         // bonus-row statistics skip rows whose sequence rejected
+    uint32_t L, body_end;
+    FastDiv fd_2nch, fd_LB;
+    uint64_t *pairs;         // [B][K] tagged outcome of each position's accept test
     uint64_t *partial;       // [B][2K+1][nchunk][2] tagged (ref, z); rows 0..K target, K+1.. draft
     uint64_t *sums;          // [B][nchunk2][2] tagged residual and target mass per chunk
     uint64_t *rec;           // [B][kRecWords] tagged record of each resolve: j, row j's (ref, 1/z) x 2

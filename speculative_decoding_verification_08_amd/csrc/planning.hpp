@@ -60,6 +60,8 @@ inline bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dty
         off += align_up(static_cast<size_t>(B) * p.nchunk2 * 16);
         p.off_rec = off;   // one record per sequence
         off += align_up(static_cast<size_t>(B) * kRecWords * 8);
+        p.off_pairs = off;  // one tagged outcome per position
+        off += align_up(static_cast<size_t>(B) * KN * 8);
     } else if (mode == SPEC_MODE_TOPK) {
         // One launch: a workgroup per (row, chunk) and a merge workgroup per
         // row (one wavefront holds the row's chunk maxima, two per lane).
@@ -95,6 +97,20 @@ inline uint32_t chain_schedule(ChainArgs &a) {
     a.fd_S1 = make_fastdiv(static_cast<uint32_t>(S + 1));
     a.blocks_end = static_cast<uint32_t>(S + (B - 1) * (S + 1));
     a.bon_end = static_cast<uint32_t>(a.blocks_end + 1 + B * nch);
+    return static_cast<uint32_t>(total);
+}
+
+// The position-major one-launch schedule (chain_ex_item), for K >= 2: its
+// fields, and its grid size, or 0 if it would not fit a one-dimensional grid.
+inline uint32_t chain_ex_schedule(ChainArgs &a) {
+    const uint64_t B = a.B, K = a.K, nch = a.nchunk, D = a.D, L = 2 * nch * B;
+    if (K < 2) return 0;
+    const uint64_t total = K * L + K * B + B * nch + B * D + 2 * B;
+    if (total > 0x7fffffffull || B + L > 0xffffffffull) return 0;
+    a.L = static_cast<uint32_t>(L);
+    a.body_end = static_cast<uint32_t>(2 * L + (K - 2) * (B + L));
+    a.fd_2nch = make_fastdiv(static_cast<uint32_t>(2 * nch));
+    a.fd_LB = make_fastdiv(static_cast<uint32_t>(B + L));
     return static_cast<uint32_t>(total);
 }
 

@@ -180,6 +180,89 @@ static void check_chain(const ChainShape &c) {
     }
 }
 
+// The position-major one-launch order (early exit), K >= 2.
+static void check_chain_ex(const ChainShape &c) {
+    Plan plan;
+    if (!make_plan(SPEC_MODE_CHAIN, c.B, c.K, c.V, c.dt, plan) || c.B == 0 || c.K < 2) return;
+    ChainArgs a{};
+    a.B = c.B;
+    a.K = c.K;
+    a.V = c.V;
+    a.chunk = plan.chunk;
+    a.nchunk = plan.nchunk;
+    a.nchunk2 = plan.nchunk2;
+    chain_grid_fields(plan, c.K, a);
+    const uint32_t total = chain_ex_schedule(a);
+    if (total == 0) return;  // the sequence-major order runs instead
+    ++g_cases;
+    if (g_mutant == 8) a.fd_LB = make_fastdiv(a.B + a.L + 1);  // blocks one workgroup too long
+    const int64_t B = c.B, K = c.K, R = 2 * K + 1, nch = plan.nchunk, D = a.D;
+    CHECK(total == chain_ex_grid(a), "ex grid %u vs %u", total, chain_ex_grid(a));
+    CHECK(plan.off_pairs >= plan.off_rec + static_cast<size_t>(B) * kRecWords * 8, "pairs overlap records");
+    CHECK(plan.off_pairs + static_cast<size_t>(B * K) * 8 <= plan.bytes, "pairs past the workspace");
+    std::vector<int64_t> st(B * R * nch, -1), pr(B * K, -1), draw(B * D, -1), fin(B, -1), bon(B, -1);
+    for (uint32_t g = 0; g < total; ++g) {
+        const ChainItem it = chain_ex_item(g, a);
+        CHECK(it.b < B, "ex g=%u b=%u", g, it.b);
+        if (it.b >= B) continue;
+        int64_t *slot = nullptr;
+        if (it.kind == kItemStats) {
+            int row = -1, ch = -1;
+            chain_stats_row(it.p, a, row, ch);
+            CHECK(row >= 0 && row < R && row != K && ch >= 0 && ch < nch, "ex g=%u row=%d ch=%d", g, row, ch);
+            if (row >= 0 && row < R && ch >= 0 && ch < nch) slot = &st[(it.b * R + row) * nch + ch];
+        } else if (it.kind == kItemBonusStats) {
+            CHECK(it.p < nch, "ex g=%u bonus chunk %u", g, it.p);
+            if (it.p < nch) slot = &st[(it.b * R + K) * nch + it.p];
+        } else if (it.kind == kItemPair) {
+            CHECK(it.p < K, "ex g=%u position %u", g, it.p);
+            if (it.p < K) slot = &pr[it.b * K + it.p];
+        } else if (it.kind == kItemDraw) {
+            CHECK(it.p < D, "ex g=%u draw chunk %u", g, it.p);
+            if (it.p < D) slot = &draw[it.b * D + it.p];
+        } else if (it.kind == kItemFinisher) {
+            slot = &fin[it.b];
+        } else {
+            CHECK(it.kind == kItemBonus, "ex g=%u kind %d", g, it.kind);
+            slot = &bon[it.b];
+        }
+        CHECK(slot && *slot < 0, "ex g=%u kind=%d b=%u p=%u twice", g, it.kind, it.b, it.p);
+        if (slot) *slot = g;
+    }
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t last_pr = -1, last_draw = -1, last_bonus_row = -1;
+        for (int64_t r = 0; r < R; ++r)
+            for (int64_t ch = 0; ch < nch; ++ch) {
+                const int64_t p = st[(b * R + r) * nch + ch];
+                CHECK(p >= 0, "ex b=%lld row=%lld ch=%lld never run", (long long)b, (long long)r, (long long)ch);
+                if (r == K) last_bonus_row = std::max(last_bonus_row, p);
+            }
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t p = pr[b * K + k];
+            CHECK(p >= 0, "ex b=%lld pair %lld missing", (long long)b, (long long)k);
+            // after the statistics of its two rows and the earlier positions' resolvers
+            for (int64_t ch = 0; ch < nch; ++ch) {
+                CHECK(p > st[(b * R + k) * nch + ch] && p > st[(b * R + K + 1 + k) * nch + ch],
+                      "ex b=%lld pair %lld before its rows", (long long)b, (long long)k);
+            }
+            if (k > 0) CHECK(p > pr[b * K + k - 1], "ex b=%lld pair %lld before pair %lld", (long long)b,
+                             (long long)k, (long long)(k - 1));
+            // position k's outcome is out before position k + 2's rows start
+            if (k + 2 < K)
+                for (int64_t ch = 0; ch < nch; ++ch)
+                    CHECK(p < st[(b * R + k + 2) * nch + ch], "ex b=%lld pair %lld after its gated rows",
+                          (long long)b, (long long)k);
+            last_pr = std::max(last_pr, p);
+        }
+        for (int64_t p = 0; p < D; ++p) {
+            CHECK(draw[b * D + p] > last_pr, "ex b=%lld draw before the record", (long long)b);
+            last_draw = std::max(last_draw, draw[b * D + p]);
+        }
+        CHECK(fin[b] > last_draw && fin[b] > last_pr, "ex b=%lld finisher too early", (long long)b);
+        CHECK(bon[b] > last_pr && bon[b] > last_bonus_row, "ex b=%lld bonus item too early", (long long)b);
+    }
+}
+
 // ------------------------------------------------------------------ greedy chain, static tree
 
 static void check_argmax(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dtype dt) {
@@ -356,13 +439,17 @@ int main(int argc, char **argv) {
         {1, 0, 1, F},          {0, 4, 100, F},       {7, 1, 2048, F},      {7, 1, 2049, F},
         {9, 2, 4096, BF},      {9, 2, 4097, BF},     {128, 1, 4096, F},    {3, 64, 300000, BF},
     };
-    for (const auto &c : chains) check_chain(c);
+    for (const auto &c : chains) {
+        check_chain(c);
+        check_chain_ex(c);
+    }
     for (int i = 0; i < 300; ++i) {
         const int32_t B = 1 + static_cast<int32_t>(rng() % 96), K = static_cast<int32_t>(rng() % 17);
         const spec_dtype dt = (rng() & 1) ? BF : F;
         const int32_t vmax = dt == BF ? (1 << 19) : (1 << 18);
         const int32_t V = 1 + static_cast<int32_t>(rng() % (i < 150 ? 20000 : vmax));
         check_chain({B, K, V, dt});
+        check_chain_ex({B, K, V, dt});
     }
     const int32_t argmax_shapes[][3] = {{64, 5, 32000}, {8, 0, 1}, {1, 64, 128256}, {3, 7, 8193},
                                         {32, 45, 128256}, {5, 1, 4096}, {300, 3, 100}};

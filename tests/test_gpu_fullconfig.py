@@ -40,11 +40,17 @@ def case(msg):
 
 
 def run_chain(sv, d, ws=None):
-    tok, acc, diag = sv.spec_verify_chain(dev(d["target"]), dev(d["draft"]), dev(d["tokens"]),
-                                          dev(d["u_accept"]), dev(d["u_sample"]), d["T"], diag=True,
-                                          workspace_buf=ws)
+    """One chain verify with per-position diagnostics, and the same call
+    without them (for K >= 2 the position-major order that skips rows after a
+    rejection): the two must agree bit for bit."""
+    args = (dev(d["target"]), dev(d["draft"]), dev(d["tokens"]), dev(d["u_accept"]),
+            dev(d["u_sample"]), d["T"])
+    tok, acc, diag = sv.spec_verify_chain(*args, diag=True, workspace_buf=ws)
+    tok2, acc2, _ = sv.spec_verify_chain(*args, workspace_buf=ws)
     torch.cuda.synchronize()
-    return tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy()
+    got = tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy()
+    assert np.array_equal(tok2.cpu().numpy(), got[0]) and np.array_equal(acc2.cpu().numpy(), got[1])
+    return got
 
 
 def chain_case(name, B, K, V, dtype, T, recipe="peaked", sigma=0.7, step=0, target_sd=2.0):
@@ -204,3 +210,21 @@ def test_sample_after_stale_statistics_reports_failure(sv):
     torch.cuda.synchronize()
     assert np.all(acc.cpu().numpy() == -1) and np.all(tok.cpu().numpy() == -1)
     assert sv.workspace_failures(ws) == B
+
+
+# ------------------------------------------------------------------ position-major order
+
+@pytest.mark.parametrize("B,K,V,dtype", [(103, 8, 20000, "f32"), (128, 6, 32768, "bf16"),
+                                         (128, 5, 32768, "bf16"), (1024, 64, 2048, "bf16")])
+def test_chain_position_major_order(sv, B, K, V, dtype):
+    """Shapes whose one-call verify runs position by position (one position's
+    items fill the chip; rows after a rejection are skipped for K >= 6): the
+    tokens equal the sequence-major order's (the call with diagnostics) bit
+    for bit, and the oracle's, at low and high acceptance."""
+    for sigma, step in ((0.7, 0), (2.5, 1)):
+        case(f"chain position-major B={B} K={K} V={V} {dtype} sigma={sigma}")
+        d = chain_case(f"pm{B}_{K}", B, K, V, dtype, 1.0, sigma=sigma, step=step)
+        tok, acc, diag = run_chain(sv, d)
+        n = parity.check_chain(d, tok, acc, diag)
+        assert n["sequences"] == B
+        print("position-major", B, K, V, dtype, sigma, dict(n), "mean accepted", acc.mean())

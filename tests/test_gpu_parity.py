@@ -38,12 +38,18 @@ def case(msg):
     print(f"[case] {msg}", flush=True)
 
 
-def run_chain(sv, d, stream=None):
-    tok, acc, diag = sv.spec_verify_chain(dev(d["target"]), dev(d["draft"]), dev(d["tokens"]),
-                                          dev(d["u_accept"]), dev(d["u_sample"]), d["T"], diag=True,
-                                          stream=stream)
+def run_chain(sv, d, stream=None, ws=None):
+    """One chain verify with per-position diagnostics, and the same call
+    without them (for K >= 2 the position-major order that skips rows after a
+    rejection): the two must agree bit for bit."""
+    args = (dev(d["target"]), dev(d["draft"]), dev(d["tokens"]), dev(d["u_accept"]),
+            dev(d["u_sample"]), d["T"])
+    tok, acc, diag = sv.spec_verify_chain(*args, diag=True, stream=stream, workspace_buf=ws)
+    tok2, acc2, _ = sv.spec_verify_chain(*args, stream=stream, workspace_buf=ws)
     torch.cuda.synchronize()
-    return tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy()
+    got = tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy()
+    assert np.array_equal(tok2.cpu().numpy(), got[0]) and np.array_equal(acc2.cpu().numpy(), got[1])
+    return got
 
 
 def chain_case(name, B, K, V, dtype, T, recipe="normal", sigma=0.5, step=0, target_sd=2.0):
@@ -171,11 +177,7 @@ def test_chain_workspace_reuse_across_shapes(sv):
     for i, (B, K, V, dt) in enumerate(shapes):
         case(f"workspace reuse call {i}: B={B} K={K} V={V} {dt}")
         d = chain_case("reuse", B, K, V, dt, 0.9, recipe="peaked", sigma=0.7, step=i)
-        tok, acc, diag = sv.spec_verify_chain(dev(d["target"]), dev(d["draft"]), dev(d["tokens"]),
-                                              dev(d["u_accept"]), dev(d["u_sample"]), d["T"],
-                                              diag=True, workspace_buf=ws)
-        torch.cuda.synchronize()
-        parity.check_chain(d, tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy())
+        parity.check_chain(d, *run_chain(sv, d, ws=ws))
 
 
 def test_chain_full_size_128k(sv):
@@ -549,11 +551,7 @@ def test_workspace_shared_by_every_entry_point(sv):
     for rep in range(2):
         case(f"shared workspace round {rep}: chain")
         d = chain_case("shared", 6, 4, 30000, "bf16", 1.0, recipe="peaked", sigma=0.7, step=rep)
-        tok, acc, diag = sv.spec_verify_chain(dev(d["target"]), dev(d["draft"]), dev(d["tokens"]),
-                                              dev(d["u_accept"]), dev(d["u_sample"]), d["T"],
-                                              diag=True, workspace_buf=ws)
-        torch.cuda.synchronize()
-        parity.check_chain(d, tok.cpu().numpy(), acc.cpu().numpy(), diag.cpu().numpy())
+        parity.check_chain(d, *run_chain(sv, d, ws=ws))
         case(f"shared workspace round {rep}: greedy")
         g = W.greedy_inputs(W.WORKLOADS["greedy_32k"].with_sizes(B=6, K=4, V=30000), rep)
         tok, acc = sv.spec_verify_greedy(dev(g["target"]), dev(g["tokens"]), workspace_buf=ws)

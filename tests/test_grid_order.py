@@ -21,6 +21,7 @@ MUTANTS = {
     5: "two-phase draw items per sequence off by one",
     6: "compact tree order with rows of Nmax - 1",
     7: "top-k chunks per row off by one",
+    8: "position-major blocks one workgroup too long",
 }
 
 
