@@ -711,16 +711,17 @@ __device__ __forceinline__ uint64_t plain_word(const uint64_t *p) {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Whether a statistics item of position k >= 2 of sequence b may skip its
-// chunk: a published outcome of a position up to k - 2 ended the sequence's
-// accept tests.  Uniform over the workgroup (thread 0 reads, LDS shares).
+// Whether a statistics item of position k >= 1 of sequence b may skip its
+// chunk: an outcome already published for a position below k ended the
+// sequence's accept tests.  Uniform over the workgroup (thread 0 reads, LDS
+// shares).
 __device__ __forceinline__ bool rows_not_needed(const ChainArgs &a, int b, int k) {
     __shared__ int s_skip;
     if (threadIdx.x == 0) {
         const uint32_t tag = a.tag_src ? *a.tag_src : a.tag;
         const uint64_t *pairs = a.pairs + static_cast<int64_t>(b) * a.K;
         bool skip = false;
-        for (int i = 0; i + 2 <= k; ++i) {
+        for (int i = 0; i < k; ++i) {
             const uint64_t v = plain_word(pairs + i);
             skip = skip || (current(v, tag) && static_cast<uint32_t>(v) != kPairAccept);
         }
@@ -1036,8 +1037,8 @@ __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
 // registers it cost the statistics items):
 //   kSeqMajor        chain_fused_item, one resolver per sequence;
 //   kPosMajor        chain_ex_item, one pair resolver per position;
-//   kPosMajorGated   the same, and statistics items of position k >= 2 skip
-//                    their chunk after a rejection at a position up to k - 2.
+//   kPosMajorGated   the same, and statistics items of position k >= 1 skip
+//                    their chunk after a published rejection below k.
 // Sequence-major: each resolver finds its statistics done or nearly so, and
 // the stream of logits runs undisturbed: draws placed among the statistics
 // measured slower at every lag tried (their second read of row j takes slots
@@ -1061,7 +1062,7 @@ __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
         chain_stats_row(it.p, a, row, ch);
         if constexpr (Order == kPosMajorGated) {
             const int pos = row <= a.K ? row : row - a.K - 1;
-            if (pos >= 2 && rows_not_needed(a, b, pos)) return;
+            if (pos >= 1 && rows_not_needed(a, b, pos)) return;
         }
         stats_item<DT, VecOk>(a, it.b, row, ch);
     } else if (it.kind == kItemBonusStats) {

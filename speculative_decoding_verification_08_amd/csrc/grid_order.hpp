@@ -84,53 +84,40 @@ inline uint32_t chain_fused_grid(const ChainArgs &a) {
 inline uint32_t chain_draw_grid(const ChainArgs &a) { return static_cast<uint32_t>(a.B) * (a.D + 3); }
 
 // The position-major one-launch order (k_chain_fused with early exit), for
-// K >= 2.  Level k holds the statistics of target row k and draft row k of
-// every sequence (2 nchunk items per sequence, sequence by sequence); the
-// pair resolvers of position k (one per sequence) run one level later:
-//   [L0][L1][P0][L2][P1] ... [P(K-3)][L(K-1)][P(K-2)][P(K-1)]
-//   [bonus rows][draw items][finishers][bonus items]
+// K >= 2.  Block k holds the statistics of target row k and draft row k of
+// every sequence (2 nchunk items per sequence, sequence by sequence), then
+// the pair resolvers of position k (one per sequence):
+//   [L0][P0][L1][P1] ... [L(K-1)][P(K-1)][bonus rows][draws][finishers][bonus items]
 // A pair resolver waits for its two rows and for the pair resolvers of the
-// earlier positions of its sequence, all of lower index.  Statistics items of
-// level k >= 2 wait for nothing: they skip their chunk when the outcome of a
-// position up to k - 2 of their sequence, already published, ended the
-// sequence's accept tests.  Statistics item index p is that of
+// earlier positions of its sequence, all of lower index.  Statistics items
+// wait for nothing: with row skipping on, an item of position k >= 1 skips
+// its chunk when an outcome already published for a position below k ended
+// its sequence's accept tests.  Statistics item index p is that of
 // chain_stats_row (rows k and K + 1 + k).
 __host__ __device__ __forceinline__ ChainItem chain_ex_item(uint32_t g, const ChainArgs &a) {
     const uint32_t B = a.B, K = a.K, D = a.D, nch = a.nchunk, L = a.L;
-    ChainItem it{kItemStats, 0, 0};
-    uint32_t lev, r;
-    if (g < 2 * L) {
-        lev = g >= L ? 1 : 0;
-        r = g - lev * L;
-    } else if (g < a.body_end) {
-        const uint32_t h = g - 2 * L, blk = fdiv(h, a.fd_LB), q = h - blk * (B + L);
-        if (q < B) return ChainItem{kItemPair, q, blk};
-        lev = blk + 2;
-        r = q - B;
-    } else {
-        uint32_t h = g - a.body_end;
-        if (h < 2 * B) return ChainItem{kItemPair, h < B ? h : h - B, h < B ? K - 2 : K - 1};
-        h -= 2 * B;
-        if (h < B * nch) {
-            const uint32_t b = fdiv(h, a.fd_nch);
-            return ChainItem{kItemBonusStats, b, h - b * nch};
-        }
-        h -= B * nch;
-        if (h < B * D) {
-            const uint32_t b = fdiv(h, a.fd_D);
-            return ChainItem{kItemDraw, b, h - b * D};
-        }
-        h -= B * D;
-        return h < B ? ChainItem{kItemFinisher, h, 0} : ChainItem{kItemBonus, h - B, 0};
+    if (g < a.body_end) {
+        const uint32_t lev = fdiv(g, a.fd_LB), q = g - lev * (L + B);
+        if (q >= L) return ChainItem{kItemPair, q - L, lev};
+        const uint32_t b = fdiv(q, a.fd_2nch), r = q - b * 2 * nch, dr = r >= nch ? 1 : 0;
+        return ChainItem{kItemStats, b, (dr * K + lev) * nch + (r - dr * nch)};
     }
-    const uint32_t b = fdiv(r, a.fd_2nch), q = r - b * 2 * nch, dr = q >= nch ? 1 : 0;
-    it.b = b;
-    it.p = (dr * K + lev) * nch + (q - dr * nch);
-    return it;
+    uint32_t h = g - a.body_end;
+    if (h < B * nch) {
+        const uint32_t b = fdiv(h, a.fd_nch);
+        return ChainItem{kItemBonusStats, b, h - b * nch};
+    }
+    h -= B * nch;
+    if (h < B * D) {
+        const uint32_t b = fdiv(h, a.fd_D);
+        return ChainItem{kItemDraw, b, h - b * D};
+    }
+    h -= B * D;
+    return h < B ? ChainItem{kItemFinisher, h, 0} : ChainItem{kItemBonus, h - B, 0};
 }
 inline uint32_t chain_ex_grid(const ChainArgs &a) {
     const uint32_t B = a.B;
-    return a.body_end + 2 * B + B * (a.nchunk + a.D + 2);
+    return a.body_end + B * (a.nchunk + a.D + 2);
 }
 
 // Row and chunk of statistics item p of a sequence: rows 0..K-1 (target) and

@@ -99,10 +99,10 @@ struct ChainArgs {
     // statistics and resolvers end, and where the bonus rows' statistics end.
     uint32_t S, D, blocks_end, bon_end;
     FastDiv fd_nch, fd_D, fd_S1;
-    // Position-major one-launch order (early exit): the items of one position
-    // of every sequence (L = 2 nchunk B), where the blocks of a pair
-    // resolvers' run and a position's items end, and divisions by 2 nchunk
-    // and by B + L.
+    // Position-major one-launch order (early exit): the statistics items of
+    // one position of every sequence (L = 2 nchunk B), where the blocks of
+    // (position items, pair resolvers) end, and divisions by 2 nchunk and by
+    // L + B.
     bool early_exit;
     bool gate_rows;          // position-major statistics skip rows after a rejection
     bool gate_bonus;         // bonus-row statistics skip rows whose sequence rejected

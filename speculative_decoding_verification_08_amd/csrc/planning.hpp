@@ -108,7 +108,7 @@ inline uint32_t chain_ex_schedule(ChainArgs &a) {
     const uint64_t total = K * L + K * B + B * nch + B * D + 2 * B;
     if (total > 0x7fffffffull || B + L > 0xffffffffull) return 0;
     a.L = static_cast<uint32_t>(L);
-    a.body_end = static_cast<uint32_t>(2 * L + (K - 2) * (B + L));
+    a.body_end = static_cast<uint32_t>(K * (B + L));
     a.fd_2nch = make_fastdiv(static_cast<uint32_t>(2 * nch));
     a.fd_LB = make_fastdiv(static_cast<uint32_t>(B + L));
     return static_cast<uint32_t>(total);

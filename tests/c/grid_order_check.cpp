@@ -247,11 +247,11 @@ static void check_chain_ex(const ChainShape &c) {
             }
             if (k > 0) CHECK(p > pr[b * K + k - 1], "ex b=%lld pair %lld before pair %lld", (long long)b,
                              (long long)k, (long long)(k - 1));
-            // position k's outcome is out before position k + 2's rows start
-            if (k + 2 < K)
+            // position k's outcome comes before position k + 1's rows
+            if (k + 1 < K)
                 for (int64_t ch = 0; ch < nch; ++ch)
-                    CHECK(p < st[(b * R + k + 2) * nch + ch], "ex b=%lld pair %lld after its gated rows",
-                          (long long)b, (long long)k);
+                    CHECK(p < st[(b * R + k + 1) * nch + ch] && p < st[(b * R + K + 2 + k) * nch + ch],
+                          "ex b=%lld pair %lld after its gated rows", (long long)b, (long long)k);
             last_pr = std::max(last_pr, p);
         }
         for (int64_t p = 0; p < D; ++p) {
