@@ -31,11 +31,12 @@
  *    example with hipMemsetAsync); after that it can serve any number of
  *    calls of any entry point and shape without clearing.  Words that
  *    workgroups hand each other carry a per-call tag (from a process-wide
- *    call counter, never 0), so words left by an earlier call of this
- *    library, or zeros, are never taken for fresh ones.  Memory with other
- *    prior contents could hold a word that looks fresh (a small integer in
- *    its upper half), so an unzeroed workspace gives unspecified outputs.
- *    Calls that share a workspace must be ordered on one stream.
+ *    call counter that starts at a random value, never 0), so words left by
+ *    an earlier call of this library, or zeros, are never taken for fresh
+ *    ones.  Memory with other prior contents holds a word that looks fresh
+ *    only by a 2^-31 chance per word, so an unzeroed workspace gives
+ *    unspecified outputs.  Calls that share a workspace must be ordered on
+ *    one stream.
  *  - Graph capture: every entry point can be recorded into a HIP graph.  A
  *    call made while its stream is being captured also records a one-thread
  *    kernel that advances a tag word kept in the first 256 bytes of its
@@ -149,10 +150,20 @@ spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_
  * One kernel launch that computes the same as spec_verify_chain_stats
  * followed by spec_verify_chain_sample, bit for bit.  Its workgroups hand
  * each other words in the workspace and wait for each other (bounded, about
- * 2 s): a sequence's draw waits for its statistics, and the draw workgroups
- * of one sequence for each other.  If a wait ever ran out, the sequence gets
- * out_accepted[b] = -1 and out_tokens[b] all -1.  Sizes whose one-launch grid
- * would exceed 2^31 - 1 workgroups run as the two phases instead.
+ * 2 s): a sequence's accept tests wait for its statistics, its draw for its
+ * accept tests, and its final draw for its chunk masses.  If a wait ever ran
+ * out, the sequence gets out_accepted[b] = -1 and out_tokens[b] all -1, and
+ * the workspace's failure count grows (spec_verify_workspace_failures).
+ * Sizes whose one-launch grid would exceed 2^31 - 1 workgroups run as the two
+ * phases instead.
+ *
+ * Without out_diag, and when one position's work fills the GPU, the launch
+ * streams the batch position by position and publishes each position's
+ * accept outcome as it goes; then the bonus row of a sequence that rejected
+ * a draft, and (for K >= 6) the rows of positions after a sequence's first
+ * rejection, are not read.  The accept rule never consults them, so the
+ * outputs are the same as with every row read.  With out_diag every
+ * position's p, q and ratio are computed, so every row is read.
  */
 spec_status spec_verify_chain(const void *target_logits, const void *draft_logits, spec_dtype dtype,
                               const int32_t *draft_tokens, const float *u_accept,
@@ -178,10 +189,15 @@ spec_status spec_verify_chain_stats(const void *target_logits, const void *draft
  * position, the first rejection j, the residual or bonus draw and the emitted
  * tokens, from the statistics the first phase left in the same workspace.
  * Must follow spec_verify_chain_stats with identical logits, tokens, sizes and
- * temperature on the same stream; sequences whose statistics were not written
- * by that phase get out_accepted = -1.  The draw workgroups of one sequence
- * wait for each other (bounded, about 2 s); if a wait ran out, the sequence
- * gets out_accepted[b] = -1 and out_tokens[b] all -1.
+ * temperature on the same stream, with no other chain call on the workspace
+ * in between: the statistics phase records its tag in the workspace header
+ * and the sample phase reads the statistics under that tag.  Sequences whose
+ * statistics were not written by that phase (no statistics phase, or another
+ * call's) get out_accepted = -1 and out_tokens all -1, and each adds one to
+ * the workspace's failure count; they are never drawn from other statistics.
+ * The draw workgroups of one sequence wait for each other (bounded, about
+ * 2 s); if a wait ran out, the sequence gets the same -1 outputs and is
+ * counted.
  */
 spec_status spec_verify_chain_sample(const void *target_logits, const void *draft_logits,
                                      spec_dtype dtype, const int32_t *draft_tokens,
