@@ -779,7 +779,8 @@ __device__ __forceinline__ bool read_record(const ChainArgs &a, int b, uint32_t 
 // [ch*C2, ch*C2 + C2) of rows j -- the residual max(0, p_j - q_j) and the
 // target p_j -- summed in the order the finisher's scan of the same chunk
 // uses, so the two agree bit for bit.  It waits for nothing but the record
-// and leaves the draw to the sequence's finisher.
+// and leaves the draw to the sequence's finisher, unless the row is a single
+// chunk: then it draws itself.
 template <class DT, bool VecOk>
 __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, float *lds) {
     using CK = Chunk2<DT>;
@@ -799,6 +800,38 @@ __device__ __forceinline__ void draw_item(const ChainArgs &a, int b, int ch, flo
     float lp[NQ], lr[NQ], ex_r[NQ], ex_p[NQ], mr, mp;
     chunk_weights<DT, VecOk, true>(a, w, c0, n, rt, rd, lp, lr);
     round_scan2<NQ>(lr, lp, ex_r, ex_p, mr, mp);
+    if (a.nchunk2 == 1) {
+        // The row is one chunk and this workgroup holds all of it: it draws
+        // here, through the crossing and search a finisher would run on the
+        // same masses (so the same bits), with no hand-over and no reload.
+        __shared__ float s_tau1, s_base1, s_S1;
+        __shared__ int s_resid1;
+        const int lane = tid % kWave;
+        const int32_t my_tok = a.tokens[static_cast<int64_t>(b) * K + min(lane, K - 1)];
+        if (tid < kWave) {
+            const float r0 = lane == 0 ? mr : 0.f, p0 = lane == 0 ? mp : 0.f;
+            const bool resid = wave_last(wave_incl_sum(r0)) > 0.f;
+            float S, tau, base;
+            int cstar;
+            crossing_chunk(resid ? r0 : p0, 0.f, a.u_sample[b], S, tau, cstar, base);
+            if (lane == 0) {
+                s_tau1 = tau;
+                s_base1 = base;
+                s_S1 = S;
+                s_resid1 = resid;
+            }
+        }
+        __syncthreads();
+        const bool resid = s_resid1;
+        float start[NQ], l[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            start[q] = s_base1 + (resid ? ex_r[q] : ex_p[q]);
+            l[q] = resid ? lr[q] : lp[q];
+        }
+        search_emit<DT, true>(a, b, c0, j, w, resid, s_tau1, start, l, rt, rd, s_S1, my_tok, lds);
+        return;
+    }
     if (tid == 0) {
         uint64_t *sums = a.sums + 2 * (static_cast<int64_t>(b) * a.nchunk2 + ch);
         publish_f32(sums, tag, mr);
@@ -833,6 +866,7 @@ __device__ __forceinline__ void finisher_item(const ChainArgs &a, int b, float *
         return;
     }
     if (j < 0 || j >= K) return;  // a failed resolve (reported), or the bonus item's draw
+    if (nc == 1) return;          // a one-chunk row: its draw item drew
     w.resid = true;
     w.trow = (static_cast<int64_t>(b) * (K + 1) + j) * a.V;
     w.drow = (static_cast<int64_t>(b) * K + j) * a.V;
