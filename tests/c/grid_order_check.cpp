@@ -438,6 +438,7 @@ int main(int argc, char **argv) {
         {2, 3, 1 << 19, BF},   {2, 3, 1 << 18, F},   {2, 3, (1 << 19) - 1, BF}, {4096, 4, 32000, BF},
         {1, 0, 1, F},          {0, 4, 100, F},       {7, 1, 2048, F},      {7, 1, 2049, F},
         {9, 2, 4096, BF},      {9, 2, 4097, BF},     {128, 1, 4096, F},    {3, 64, 300000, BF},
+        {8, 3, 1 << 19, BF},   {8, 3, 1 << 18, F},   {1, 64, 1 << 19, BF},
     };
     for (const auto &c : chains) {
         check_chain(c);
@@ -452,7 +453,8 @@ int main(int argc, char **argv) {
         check_chain_ex({B, K, V, dt});
     }
     const int32_t argmax_shapes[][3] = {{64, 5, 32000}, {8, 0, 1}, {1, 64, 128256}, {3, 7, 8193},
-                                        {32, 45, 128256}, {5, 1, 4096}, {300, 3, 100}};
+                                        {32, 45, 128256}, {5, 1, 4096}, {300, 3, 100},
+                                        {1, 1, 1 << 26}, {1, 2, 1 << 26}, {1, 4, 1 << 26}};
     for (const auto &s : argmax_shapes) {
         check_argmax(SPEC_MODE_GREEDY, s[0], s[1], s[2], BF);
         check_argmax(SPEC_MODE_GREEDY, s[0], s[1], s[2], F);

@@ -228,3 +228,47 @@ def test_chain_position_major_order(sv, B, K, V, dtype):
         n = parity.check_chain(d, tok, acc, diag)
         assert n["sequences"] == B
         print("position-major", B, K, V, dtype, sigma, dict(n), "mean accepted", acc.mean())
+
+
+# ------------------------------------------------------------------ documented size limits
+
+@pytest.mark.parametrize("dtype,B,K", [("bf16", 8, 3), ("f32", 8, 3), ("bf16", 1, 64)])
+def test_chain_at_the_vocabulary_limit(sv, dtype, B, K):
+    """The largest vocabulary the chain verify takes in each logit type: 128
+    statistics chunks and 128 draw chunks per row, so the wavefront that
+    gathers a row's chunk masses holds two per lane.  With B = 8 the call
+    without diagnostics runs position by position; with K = 64 the longest
+    draft, sequence by sequence."""
+    V = sv.MAX_CHAIN_V_BF16 if dtype == "bf16" else sv.MAX_CHAIN_V_F32
+    for sigma, step in ((0.7, 0), (2.5, 1)):
+        case(f"chain at the vocabulary limit B={B} K={K} V={V} {dtype} sigma={sigma}")
+        d = chain_case(f"vlimit{K}", B, K, V, dtype, 1.0, sigma=sigma, step=step)
+        tok, acc, diag = run_chain(sv, d)
+        n = parity.check_chain(d, tok, acc, diag)
+        assert n["sequences"] == B
+
+
+@pytest.mark.parametrize("dtype,K", [("bf16", 2), ("f32", 1)])
+def test_greedy_at_the_vocabulary_limit(sv, dtype, K):
+    """Greedy verify at the largest vocabulary it takes (2^26 entries per row,
+    thousands of argmax chunks per row for the resolve to merge)."""
+    case(f"greedy at the vocabulary limit V={sv.MAX_V} {dtype} K={K}")
+    w = W.Workload("glimit", 95, "greedy", B=1, K=K, V=sv.MAX_V, dtype=dtype, target_sd=3.0)
+    d = W.greedy_inputs(w, 0)
+    tok, acc = sv.spec_verify_greedy(dev(d["target"]), dev(d["tokens"]))
+    torch.cuda.synchronize()
+    n = parity.check_greedy(d, tok.cpu().numpy(), acc.cpu().numpy())
+    assert n["sequences"] == 1
+
+
+def test_tree_at_the_vocabulary_limit(sv):
+    """Static-tree greedy verify at the largest vocabulary (four nodes: a root
+    with two children, one of which has a child)."""
+    case(f"tree at the vocabulary limit V={sv.MAX_V} bf16")
+    w = W.Workload("tlimit", 96, "tree", B=1, V=sv.MAX_V, dtype="bf16", recipe="peaked")
+    d = W.tree_inputs(w, 0, parents=[-1, 0, 0, 1], p_match=0.9)
+    tok, path, depth = sv.spec_verify_tree_greedy(dev(d["node_logits"]), dev(d["node_tokens"]),
+                                                  d["parents"])
+    torch.cuda.synchronize()
+    n = parity.check_tree(d, tok.cpu().numpy(), path.cpu().numpy(), depth.cpu().numpy())
+    assert n["sequences"] == 1
