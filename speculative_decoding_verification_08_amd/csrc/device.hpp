@@ -28,8 +28,9 @@ struct F32 {
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// A 16-byte load marked non-temporal: a streamed logit is read once, so it
-// should not displace data that is reused from the caches.
+// A 16-byte load marked non-temporal, for data read once (streamed logits,
+// KV rows on their way to the cache): it should not displace data that is
+// reused from the caches, and it streams faster than a plain load.
 __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));

@@ -53,7 +53,7 @@ __device__ __forceinline__ void argmax_item(const ArgmaxArgs &a, int64_t row, in
     for (; v + (U - 1) * kWG < s.vb; v += U * kWG) {
         uint4 raw[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = vp[v + u * kWG];
+        for (int u = 0; u < U; ++u) raw[u] = load_nt(vp + v + u * kWG);
         // Every load in flight before the first wait: left to itself the
         // scheduler starts on the first vector before issuing the last two,
         // which then leave one memory round trip later.
@@ -76,7 +76,7 @@ __device__ __forceinline__ void argmax_item(const ArgmaxArgs &a, int64_t row, in
     }
     for (; v < s.vb; v += kWG) {
         float x[VEC];
-        unpack<DT>(vp[v], x);
+        unpack<DT>(load_nt(vp + v), x);
 #pragma unroll
         for (int i = 0; i < VEC; ++i)
             if (x[i] > bv) {

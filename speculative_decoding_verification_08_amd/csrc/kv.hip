@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kWG) void k_kv_commit(KvArgs a) {
         const bool live = fu[u] < total, in = r >= 0 && r < a.N;
         bad = bad || (live && !in);
         v[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (live && in) v[u] = src[static_cast<int64_t>(r) * vpr + (fu[u] - (fu[u] / vpr) * vpr)];
+        if (live && in) v[u] = load_nt(src + static_cast<int64_t>(r) * vpr + (fu[u] - (fu[u] / vpr) * vpr));
     }
     // Rows past the first round: check their path entries too.
     constexpr uint32_t kRound = kWG * kUnroll;
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kWG) void k_kv_commit(KvArgs a) {
             if (f < total) {
                 const uint32_t i = f / vpr;
                 const int r = pb ? pb[i] : static_cast<int>(i);
-                w[u] = src[static_cast<int64_t>(r) * vpr + (f - i * vpr)];
+                w[u] = load_nt(src + static_cast<int64_t>(r) * vpr + (f - i * vpr));
             }
         }
 #pragma unroll

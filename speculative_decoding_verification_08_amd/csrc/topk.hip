@@ -266,7 +266,7 @@ __device__ __forceinline__ void topk_chunk(const TopkArgs &a, int64_t row, int c
         uint4 raw[NQ];
         const int last = n / VEC - 1;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) raw[q] = vp[min(tid + q * kWG, last)];
+        for (int q = 0; q < NQ; ++q) raw[q] = load_nt(vp + min(tid + q * kWG, last));
         // Every load in flight before the first wait: one memory round trip.
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
