@@ -11,6 +11,7 @@
 #include <chrono>
 #include <random>
 
+#include "grid_order.hpp"
 #include "plan.hpp"
 #include "planning.hpp"
 #include "kv.hpp"
@@ -340,6 +341,7 @@ spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtyp
     t.node_count = node_count;
     t.B = B;
     t.Nmax = Nmax;
+    t.fd_nmax = make_fastdiv(static_cast<uint32_t>(Nmax));
     t.out_tokens = out_tokens;
     t.out_path = out_path;
     t.out_depth = out_depth;
@@ -368,6 +370,8 @@ spec_status spec_draft_topk(const void *logits, spec_dtype dtype, int32_t rows, 
     const spec_status st = call_tag(workspace, stream, a.tag, a.tag_src);
     if (st != SPEC_OK) return st;
     a.lag = topk_lag(rows, plan.nchunk);
+    a.fd_nch = make_fastdiv(static_cast<uint32_t>(plan.nchunk));
+    a.fd_blk = make_fastdiv(static_cast<uint32_t>(kTopkGroupRows * plan.nchunk + 1));
     a.partial = at<uint64_t>(workspace, plan.off_partial);
     a.hdr = static_cast<uint32_t *>(workspace);
     a.out_idx = out_idx;
@@ -408,6 +412,8 @@ spec_status spec_kv_commit(const void *scratch, void *cache, int32_t planes, int
     a.S = S;
     a.P = P;
     a.vpr = static_cast<int32_t>(vpr);
+    a.fd_planes = make_fastdiv(static_cast<uint32_t>(planes));
+    a.fd_vpr = make_fastdiv(static_cast<uint32_t>(vpr));
     a.path = path;
     a.count = count;
     a.len = cache_len;

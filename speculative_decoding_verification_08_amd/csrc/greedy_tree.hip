@@ -443,14 +443,14 @@ __global__ __launch_bounds__(kWG) void k_tree_dyn(TreeDynArgs a) {
     // `row`, or nothing.
     TreeDynItem it;
     if (B <= static_cast<uint32_t>(kCompactTrees)) {
-        const uint32_t R = g / nch;
+        const uint32_t R = fdiv(g, a.am.fd_nch);
         uint32_t b = 0, v = 0;
         const uint32_t T = B <= static_cast<uint32_t>(kWave) ? locate_row<1>(a, R, b, v)
                                                              : locate_row<kCountsPerLane>(a, R, b, v);
-        it = tree_dyn_compact_item(g, nch, T, b, v, B, static_cast<uint32_t>(a.Nmax));
+        it = tree_dyn_compact_item(g, R, nch, T, b, v, B, static_cast<uint32_t>(a.Nmax));
     } else {
-        it = tree_dyn_full_item(g, nch, static_cast<uint32_t>(a.am.rows), static_cast<uint32_t>(a.Nmax),
-                                a.node_count);
+        it = tree_dyn_full_item(g, nch, a.am.fd_nch, static_cast<uint32_t>(a.am.rows),
+                                static_cast<uint32_t>(a.Nmax), a.fd_nmax, a.node_count);
     }
     if (it.argmax) argmax_item<DT, 4, VecOk>(am, it.row, static_cast<int>(it.ch));
     else if (it.resolve) tree_dyn_resolve_item(a, am, static_cast<int>(it.row));

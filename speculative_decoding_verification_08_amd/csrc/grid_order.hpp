@@ -158,7 +158,10 @@ struct TopkItem {
 // chunks of groups 0..L-1; then for each group q >= L its chunks followed by
 // one merge workgroup for group q - L; then the merges of the last L groups.
 // A merge thus trails its rows' chunks by about L groups of workgroups.
-__host__ __device__ __forceinline__ TopkItem topk_item(int64_t g, int64_t R, int64_t nch, int64_t L) {
+// fd_nch divides by nch, fd_blk by 4 nch + 1; every numerator is an index of
+// a grid of fewer than 2^31 workgroups.
+__host__ __device__ __forceinline__ TopkItem topk_item(int64_t g, int64_t R, int64_t nch, int64_t L,
+                                                       FastDiv fd_nch, FastDiv fd_blk) {
     const int64_t G = (R + kTopkGroupRows - 1) / kTopkGroupRows;
     auto group_chunks = [&](int64_t q) {
         const int64_t end = (q + 1) * kTopkGroupRows;
@@ -168,18 +171,19 @@ __host__ __device__ __forceinline__ TopkItem topk_item(int64_t g, int64_t R, int
     const int64_t full = kTopkGroupRows * nch, head = L < G ? L * full : R * nch;
     TopkItem it{-1, 0, -1};
     if (g < head) {
-        it.row = g / nch;
-        it.ch = g % nch;
+        it.row = fdiv(static_cast<uint32_t>(g), fd_nch);
+        it.ch = g - it.row * nch;
     } else {
         const int64_t h = g - head, nbody = G - L;  // groups with chunks after the head
         // Body blocks: group L + b's chunks, then one merge (group b); the
         // last group may be partial.
-        const int64_t blk = h / (full + 1), off = h % (full + 1);
+        const int64_t blk = fdiv(static_cast<uint32_t>(h), fd_blk), off = h - blk * (full + 1);
         if (blk < nbody - 1 || (blk == nbody - 1 && off <= group_chunks(G - 1))) {
             const int64_t q = L + blk, nc = group_chunks(q);
             if (off < nc) {
-                it.row = q * kTopkGroupRows + off / nch;
-                it.ch = off % nch;
+                const int64_t r = fdiv(static_cast<uint32_t>(off), fd_nch);
+                it.row = q * kTopkGroupRows + r;
+                it.ch = off - r * nch;
             } else {
                 it.mgroup = blk;
             }
@@ -273,13 +277,13 @@ struct TreeDynItem {
     uint32_t ch;
 };
 
-// The compact order, given the batch's real rows T and, for R = g / nch < T,
-// the tree b and node v of real row R.
-__host__ __device__ __forceinline__ TreeDynItem tree_dyn_compact_item(uint32_t g, uint32_t nch,
-                                                                      uint32_t T, uint32_t b,
-                                                                      uint32_t v, uint32_t B,
-                                                                      uint32_t Nmax) {
-    const uint32_t R = g / nch, nam = T * nch;
+// The compact order, given R = g / nch, the batch's real rows T and, for
+// R < T, the tree b and node v of real row R.
+__host__ __device__ __forceinline__ TreeDynItem tree_dyn_compact_item(uint32_t g, uint32_t R,
+                                                                      uint32_t nch, uint32_t T,
+                                                                      uint32_t b, uint32_t v,
+                                                                      uint32_t B, uint32_t Nmax) {
+    const uint32_t nam = T * nch;
     TreeDynItem it;
     it.argmax = g < nam;
     it.resolve = !it.argmax && g < nam + B;
@@ -292,12 +296,13 @@ __host__ __device__ __forceinline__ TreeDynItem tree_dyn_compact_item(uint32_t g
 // slot is padding (count is the slot's tree's node count); then a resolve per
 // tree.
 __host__ __device__ __forceinline__ TreeDynItem tree_dyn_full_item(uint32_t g, uint32_t nch,
-                                                                   uint32_t rows, uint32_t Nmax,
+                                                                   FastDiv fd_nch, uint32_t rows,
+                                                                   uint32_t Nmax, FastDiv fd_nmax,
                                                                    const int32_t *node_count) {
     TreeDynItem it{false, false, 0, 0};
     const uint32_t nam = rows * nch;
     if (g < nam) {
-        const uint32_t slot = g / nch, b = slot / Nmax, v = slot - b * Nmax;
+        const uint32_t slot = fdiv(g, fd_nch), b = fdiv(slot, fd_nmax), v = slot - b * Nmax;
         it.argmax = v < static_cast<uint32_t>(tree_rows(node_count[b], static_cast<int>(Nmax)));
         it.row = slot;
         it.ch = g - slot * nch;

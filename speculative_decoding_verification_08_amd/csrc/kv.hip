@@ -27,16 +27,17 @@ constexpr int kUnroll = 4;  // 16-byte vectors per thread per round
 // their remaining path entries before the vote and copy the rest after it.
 __global__ __launch_bounds__(kWG) void k_kv_commit(KvArgs a) {
     const int tid = threadIdx.x;
-    const int b = static_cast<int>(blockIdx.x / static_cast<uint32_t>(a.planes));
+    const int b = static_cast<int>(fdiv(blockIdx.x, a.fd_planes));
     const int plane = static_cast<int>(blockIdx.x - static_cast<uint32_t>(b) * a.planes);
     const int32_t *pb = a.path ? a.path + static_cast<int64_t>(b) * a.P : nullptr;
     const uint32_t vpr = static_cast<uint32_t>(a.vpr);
-    uint32_t fu[kUnroll];
+    uint32_t fu[kUnroll], iu[kUnroll];
     int ru[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         fu[u] = static_cast<uint32_t>(u * kWG + tid);
-        const uint32_t i = fu[u] / vpr;
+        const uint32_t i = fdiv(fu[u], a.fd_vpr);
+        iu[u] = i;
         ru[u] = static_cast<int>(i);
         if (pb && i < static_cast<uint32_t>(a.P)) ru[u] = pb[i];
     }
@@ -55,11 +56,11 @@ __global__ __launch_bounds__(kWG) void k_kv_commit(KvArgs a) {
         const bool live = fu[u] < total, in = r >= 0 && r < a.N;
         bad = bad || (live && !in);
         v[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (live && in) v[u] = load_nt(src + static_cast<int64_t>(r) * vpr + (fu[u] - (fu[u] / vpr) * vpr));
+        if (live && in) v[u] = load_nt(src + static_cast<int64_t>(r) * vpr + (fu[u] - iu[u] * vpr));
     }
     // Rows past the first round: check their path entries too.
     constexpr uint32_t kRound = kWG * kUnroll;
-    for (uint32_t i = kRound / vpr + tid; pb && static_cast<uint64_t>(i) * vpr < total; i += kWG) {
+    for (uint32_t i = fdiv(kRound, a.fd_vpr) + tid; pb && static_cast<uint64_t>(i) * vpr < total; i += kWG) {
         const int r = pb[i];
         if (r < 0 || r >= a.N) bad = true;
     }
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kWG) void k_kv_commit(KvArgs a) {
             const uint32_t f = f0 + u * kWG + tid;
             w[u] = make_uint4(0u, 0u, 0u, 0u);
             if (f < total) {
-                const uint32_t i = f / vpr;
+                const uint32_t i = fdiv(f, a.fd_vpr);
                 const int r = pb ? pb[i] : static_cast<int>(i);
                 w[u] = load_nt(src + static_cast<int64_t>(r) * vpr + (f - i * vpr));
             }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 namespace sv {
 
 struct KvArgs {
@@ -11,6 +13,7 @@ struct KvArgs {
     uint4 *cache;            // [planes][B][S][vpr]
     int32_t planes, B, N, S, P;
     int32_t vpr;             // 16-byte vectors per row
+    FastDiv fd_planes, fd_vpr;  // division by planes and by vpr
     const int32_t *path;     // nullable [B][P]
     const int32_t *count;    // [B]
     const int32_t *len;      // [B]

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 namespace sv {
 
 constexpr int kMaxK = 64;
@@ -59,26 +61,6 @@ constexpr int kHdrGraphTag = 0;  // the tag word of calls recorded into a graph
 constexpr int kHdrPhaseTag = 1;  // the tag of the statistics the last chain_stats call left
 constexpr int kHdrFailures = 2;  // count of bounded waits that ran out (and stale statistics)
 static_assert(kHdrFailures == 2, "count_failure writes the third header word");
-
-// Division by a divisor fixed for the launch, without a division sequence:
-// q = (mulhi(n, m) + n) >> s, exact for n < 2^31 (Granlund and Montgomery's
-// method with a 33-bit multiplier whose top bit is implicit).
-struct FastDiv {
-    uint32_t m = 0, s = 0;
-};
-inline FastDiv make_fastdiv(uint32_t d) {  // d >= 1
-    FastDiv f;
-    if (d == 0) return f;
-    uint32_t l = 0;
-    while ((1ull << l) < d) ++l;
-    f.s = l;
-    f.m = static_cast<uint32_t>(((1ull << 32) * ((1ull << l) - d)) / d + 1);
-    return f;
-}
-__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-    const uint32_t hi = static_cast<uint32_t>((static_cast<uint64_t>(n) * f.m) >> 32);
-    return (hi + n) >> f.s;  // hi < n for n < 2^31, so the sum does not wrap
-}
 
 // Chain verify, all kernels.
 struct ChainArgs {
@@ -167,6 +149,7 @@ struct TreeDynArgs {
     const int32_t *parents;     // [B][Nmax]
     const int32_t *node_count;  // [B]
     int32_t B, Nmax;
+    FastDiv fd_nmax;            // division by Nmax
     int32_t *out_tokens;        // [B][Nmax]
     int32_t *out_path;          // nullable [B][Nmax]
     int32_t *out_depth;         // [B]

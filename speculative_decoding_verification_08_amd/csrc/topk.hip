@@ -372,7 +372,7 @@ template <class DT, bool VecOk>
 __global__ __launch_bounds__(kWG) void k_topk(TopkArgs a) {
     if (a.tag_src) a.tag = *a.tag_src;  // a graph replay's tag
     const int64_t R = a.rows;
-    const TopkItem it = topk_item(blockIdx.x, R, a.nchunk, a.lag);
+    const TopkItem it = topk_item(blockIdx.x, R, a.nchunk, a.lag, a.fd_nch, a.fd_blk);
     const int64_t row = it.row, ch = it.ch, mgroup = it.mgroup;
     if (mgroup < 0) {
         topk_chunk<DT, VecOk>(a, row, static_cast<int>(ch));

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.hpp"
+
 namespace sv {
 
 // Top-k of rows [rows][V] in one launch: one workgroup per (row, 16 KB chunk)
@@ -17,6 +19,7 @@ struct TopkArgs {
     int64_t rows;
     int32_t V, chunk, nchunk, k;
     int64_t lag;             // groups of four rows between a group's chunks and its merge, 1 <= lag <= groups
+    FastDiv fd_nch, fd_blk;  // division by nchunk and by 4 nchunk + 1 (a body block of the grid)
     uint32_t tag;
     const uint32_t *tag_src; // nullable: read the tag from this device word instead (graph replays)
     uint64_t *partial;       // [rows][nchunk][kMaxTopK][2] tagged (value bits, index)

@@ -346,16 +346,19 @@ static void check_tree_dyn(int32_t B, int32_t Nmax, int32_t V, spec_dtype dt, st
     CHECK(rows == static_cast<uint32_t>(B) * Nmax, "rows");
     const uint32_t n = argmax_grid(rows, nch, B);
     std::vector<int64_t> am(static_cast<size_t>(rows) * nch, -1), res(B, -1);
+    // The divisors as the library makes them for the launch.
+    const FastDiv fd_nch = make_fastdiv(nch), fd_nmax = make_fastdiv(static_cast<uint32_t>(Nmax));
     for (uint32_t g = 0; g < n; ++g) {
         TreeDynItem it;
         if (B <= kCompactTrees) {
-            const uint32_t R = g / nch;
+            const uint32_t R = fdiv(g, fd_nch);
+            CHECK(R == g / nch, "g=%u row %u", g, R);
             uint32_t b = 0, v = 0;
             const uint32_t T = B <= 64 ? locate_row_host<1>(count, B, Nmax, R, b, v)
                                        : locate_row_host<kCountsPerLane>(count, B, Nmax, R, b, v);
-            it = tree_dyn_compact_item(g, nch, T, b, v, B, g_mutant == 6 ? Nmax - 1 : Nmax);
+            it = tree_dyn_compact_item(g, R, nch, T, b, v, B, g_mutant == 6 ? Nmax - 1 : Nmax);
         } else {
-            it = tree_dyn_full_item(g, nch, rows, Nmax, count.data());
+            it = tree_dyn_full_item(g, nch, fd_nch, rows, Nmax, fd_nmax, count.data());
         }
         CHECK(!(it.argmax && it.resolve), "g=%u both", g);
         if (it.argmax) {
@@ -399,8 +402,11 @@ static void check_topk(int32_t rows, int32_t V, int32_t k, spec_dtype dt) {
     CHECK(plan.off_partial + static_cast<size_t>(rows * nch) * kMaxTopK * 16 <= plan.bytes, "topk lists");
     const uint32_t n = topk_grid(rows, nch);
     std::vector<int64_t> chunk(rows * nch, -1), merge(G, -1);
+    const int64_t nch_dec = g_mutant == 7 ? nch + 1 : nch;  // chunks per row, as the decode sees them
+    const FastDiv fd_nch = make_fastdiv(static_cast<uint32_t>(nch_dec)),
+                  fd_blk = make_fastdiv(static_cast<uint32_t>(kTopkGroupRows * nch_dec + 1));
     for (uint32_t g = 0; g < n; ++g) {
-        const TopkItem it = topk_item(g, rows, g_mutant == 7 ? nch + 1 : nch, L);  // chunks per row
+        const TopkItem it = topk_item(g, rows, nch_dec, L, fd_nch, fd_blk);
         if (it.mgroup < 0) {
             CHECK(it.row >= 0 && it.row < rows && it.ch >= 0 && it.ch < nch, "g=%u row %lld ch %lld", g,
                   (long long)it.row, (long long)it.ch);
