@@ -35,8 +35,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "verify steps/s (B×(K+1)×V logits) + achieved HBM GB/s vs peak"
 CHAIN_KERNEL_SRC = [os.path.join(ROOT, "speculative_decoding_verification_08_amd", "csrc", f)
-                    for f in ("chain.hip", "device.hpp", "handover.hpp", "plan.hpp", "grid_order.hpp",
-                              "planning.hpp", "abi.hip")]
+                    for f in ("chain.hip", "device.hpp", "handover.hpp", "plan.hpp", "fastdiv.hpp",
+                              "grid_order.hpp", "planning.hpp", "abi.hip")]
 
 
 def code_tokens(text: str) -> str:
