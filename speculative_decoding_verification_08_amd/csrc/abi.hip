@@ -207,7 +207,7 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
     // delays every gated item by one read, which measured slower for K = 5
     // (64 x 5 x 128256 bf16: 43.0 against 38.7 us) and faster for K = 8
     // (256 x 8 x 151936 fp32: 384 against 436 us).
-    a.early_exit = out_diag == nullptr && 2ll * plan.nchunk * B >= 2048 && chain_ex_schedule(a) != 0;
+    a.early_exit = out_diag == nullptr && 2ll * plan.nchunk * B >= 2048 && chain_pm_schedule(a) != 0;
     a.gate_rows = a.early_exit && K >= 6;
     if (a.early_exit || chain_schedule(a) != 0) return launch_status(launch_chain_fused(a, dtype, stream));
     // Too large for one grid: the two kernels of the phase entry points, the

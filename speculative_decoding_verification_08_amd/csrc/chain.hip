@@ -1069,8 +1069,9 @@ __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
 // kernel, so that each carries only its own decode and item kinds: an unused
 // branch measured 4 us slower on 64 x 5 x 128256 bf16 through the scalar
 // registers it cost the statistics items):
-//   kSeqMajor        chain_fused_item, one resolver per sequence;
-//   kPosMajor        chain_ex_item, one pair resolver per position;
+//   kSeqMajor        chain_fused_item on a 1D grid, one resolver per sequence;
+//   kPosMajor        chain_pm_item on a 3D grid, one pair resolver per
+//                    position of each sequence;
 //   kPosMajorGated   the same, and statistics items of position k >= 1 skip
 //                    their chunk after a published rejection below k.
 // Sequence-major: each resolver finds its statistics done or nearly so, and
@@ -1089,16 +1090,19 @@ __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
     // loads before its first logit load.
     asm volatile("" ::"s"(a.target), "s"(a.draft), "s"(a.partial), "s"(a.c), "s"(a.V), "s"(a.chunk),
                  "s"(a.tag), "s"(a.tag_src));
-    const ChainItem it = Order == kSeqMajor ? chain_fused_item(blockIdx.x, a) : chain_ex_item(blockIdx.x, a);
+    int row = 0, ch = 0;
+    const ChainItem it = Order == kSeqMajor ? chain_fused_item(blockIdx.x, a)
+                                            : chain_pm_item(blockIdx.x, blockIdx.y, blockIdx.z, a, row, ch);
     const int b = static_cast<int>(it.b);
     if (it.kind == kItemStats) {
-        int row, ch;
-        chain_stats_row(it.p, a, row, ch);
+        if constexpr (Order == kSeqMajor) chain_stats_row(it.p, a, row, ch);
         if constexpr (Order == kPosMajorGated) {
-            const int pos = row <= a.K ? row : row - a.K - 1;
+            const int pos = static_cast<int>(blockIdx.z);
             if (pos >= 1 && rows_not_needed(a, b, pos)) return;
         }
         stats_item<DT, VecOk>(a, it.b, row, ch);
+    } else if (Order != kSeqMajor && it.kind == kItemNone) {
+        return;
     } else if (it.kind == kItemBonusStats) {
         // The bonus row matters only when every draft is accepted; after a
         // rejection already recorded its chunk is not read.
@@ -1139,7 +1143,8 @@ hipError_t launch_chain_stats(const ChainArgs &a, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_chain_fused(const ChainArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(a.early_exit ? chain_ex_grid(a) : chain_fused_grid(a));
+    const Grid3 pm = chain_pm_grid(a);
+    const dim3 g = a.early_exit ? dim3(pm.x, pm.y, pm.z) : dim3(chain_fused_grid(a));
     if (dtype == 1) {
         if (a.V % Bf16::kVec == 0) launch_fused_order<Bf16, true>(a, g, s);
         else launch_fused_order<Bf16, false>(a, g, s);

@@ -26,6 +26,7 @@ enum ChainItemKind : int {
     kItemBonusStats = 4,  // statistics of one chunk of the bonus row
     kItemBonus = 5,       // the bonus draw of one sequence (when j = K)
     kItemPair = 6,        // the accept test of one position of one sequence
+    kItemNone = 7,        // an empty slot of a three-dimensional grid
 };
 
 struct ChainItem {
@@ -84,25 +85,34 @@ inline uint32_t chain_fused_grid(const ChainArgs &a) {
 inline uint32_t chain_draw_grid(const ChainArgs &a) { return static_cast<uint32_t>(a.B) * (a.D + 3); }
 
 // The position-major one-launch order (k_chain_fused with early exit), for
-// K >= 2.  Block k holds the statistics of target row k and draft row k of
-// every sequence (2 nchunk items per sequence, sequence by sequence), then
-// the pair resolvers of position k (one per sequence):
-//   [L0][P0][L1][P1] ... [L(K-1)][P(K-1)][bonus rows][draws][finishers][bonus items]
-// A pair resolver waits for its two rows and for the pair resolvers of the
-// earlier positions of its sequence, all of lower index.  Statistics items
-// wait for nothing: with row skipping on, an item of position k >= 1 skips
-// its chunk when an outcome already published for a position below k ended
-// its sequence's accept tests.  Statistics item index p is that of
-// chain_stats_row (rows k and K + 1 + k).
-__host__ __device__ __forceinline__ ChainItem chain_ex_item(uint32_t g, const ChainArgs &a) {
-    const uint32_t B = a.B, K = a.K, D = a.D, nch = a.nchunk, L = a.L;
-    if (g < a.body_end) {
-        const uint32_t lev = fdiv(g, a.fd_LB), q = g - lev * (L + B);
-        if (q >= L) return ChainItem{kItemPair, q - L, lev};
-        const uint32_t b = fdiv(q, a.fd_2nch), r = q - b * 2 * nch, dr = r >= nch ? 1 : 0;
-        return ChainItem{kItemStats, b, (dr * K + lev) * nch + (r - dr * nch)};
+// K >= 2, on a three-dimensional grid of X = 2 nchunk + 1 by B by K + 2
+// workgroups, handed out x fastest, then y, then z (flattened index
+// g = (z B + y) X + x).  Slab z < K is position z: its row y holds the
+// statistics of target row z and draft row z of sequence y (x < 2 nchunk),
+// then that sequence's pair resolver of position z (x = 2 nchunk):
+//   [seq 0: L0 chunks, P0][seq 1: L0 chunks, P0] ... [slab 1] ... [slab K-1][tail]
+// The two last slabs hold the tail in flattened order t = (z - K) B X + y X
+// + x: the bonus rows' statistics, the draws, the finishers and the bonus
+// items, then empty slots.  The item comes from the workgroup's three
+// indices with no division in the slabs of positions (a division ahead of a
+// workgroup's first load delays the stream).  A pair resolver waits for its
+// two rows and for the pair resolvers of the earlier positions of its
+// sequence, all of lower index.  Statistics items wait for nothing: with row
+// skipping on, an item of position k >= 1 skips its chunk when an outcome
+// already published for a position below k ended its sequence's accept
+// tests.  A statistics item also gives its row and chunk; p is its index as
+// chain_stats_row reads it (rows k and K + 1 + k).
+__host__ __device__ __forceinline__ ChainItem chain_pm_item(uint32_t x, uint32_t y, uint32_t z,
+                                                            const ChainArgs &a, int &row, int &ch) {
+    const uint32_t B = a.B, K = a.K, D = a.D, nch = a.nchunk, X = 2 * nch + 1;
+    if (z < K) {
+        if (x == 2 * nch) return ChainItem{kItemPair, y, z};
+        const uint32_t dr = x >= nch ? 1 : 0, c = x - dr * nch;
+        row = static_cast<int>(dr ? K + 1 + z : z);
+        ch = static_cast<int>(c);
+        return ChainItem{kItemStats, y, (dr * K + z) * nch + c};
     }
-    uint32_t h = g - a.body_end;
+    uint32_t h = ((z - K) * B + y) * X + x;
     if (h < B * nch) {
         const uint32_t b = fdiv(h, a.fd_nch);
         return ChainItem{kItemBonusStats, b, h - b * nch};
@@ -113,11 +123,18 @@ __host__ __device__ __forceinline__ ChainItem chain_ex_item(uint32_t g, const Ch
         return ChainItem{kItemDraw, b, h - b * D};
     }
     h -= B * D;
-    return h < B ? ChainItem{kItemFinisher, h, 0} : ChainItem{kItemBonus, h - B, 0};
+    if (h < B) return ChainItem{kItemFinisher, h, 0};
+    if (h < 2 * B) return ChainItem{kItemBonus, h - B, 0};
+    return ChainItem{kItemNone, 0, 0};
 }
-inline uint32_t chain_ex_grid(const ChainArgs &a) {
-    const uint32_t B = a.B;
-    return a.body_end + B * (a.nchunk + a.D + 2);
+
+// Dimensions of the position-major grid (x, y, z).
+struct Grid3 {
+    uint32_t x, y, z;
+};
+inline Grid3 chain_pm_grid(const ChainArgs &a) {
+    return Grid3{2 * static_cast<uint32_t>(a.nchunk) + 1, static_cast<uint32_t>(a.B),
+                 static_cast<uint32_t>(a.K) + 2};
 }
 
 // Row and chunk of statistics item p of a sequence: rows 0..K-1 (target) and

@@ -81,15 +81,10 @@ struct ChainArgs {
     // statistics and resolvers end, and where the bonus rows' statistics end.
     uint32_t S, D, blocks_end, bon_end;
     FastDiv fd_nch, fd_D, fd_S1;
-    // Position-major one-launch order (early exit): the statistics items of
-    // one position of every sequence (L = 2 nchunk B), where the blocks of
-    // (position items, pair resolvers) end, and divisions by 2 nchunk and by
-    // L + B.
+    // Position-major one-launch order (early exit, a three-dimensional grid).
     bool early_exit;
     bool gate_rows;          // position-major statistics skip rows after a rejection
     bool gate_bonus;         // bonus-row statistics skip rows whose sequence rejected
-    uint32_t L, body_end;
-    FastDiv fd_2nch, fd_LB;
     uint64_t *pairs;         // [B][K] tagged outcome of each position's accept test
     uint64_t *partial;       // [B][2K+1][nchunk][2] tagged (ref, z); rows 0..K target, K+1.. draft
     uint64_t *sums;          // [B][nchunk2][2] tagged residual and target mass per chunk

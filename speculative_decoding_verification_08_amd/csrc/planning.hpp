@@ -100,17 +100,16 @@ inline uint32_t chain_schedule(ChainArgs &a) {
     return static_cast<uint32_t>(total);
 }
 
-// The position-major one-launch schedule (chain_ex_item), for K >= 2: its
-// fields, and its grid size, or 0 if it would not fit a one-dimensional grid.
-inline uint32_t chain_ex_schedule(ChainArgs &a) {
-    const uint64_t B = a.B, K = a.K, nch = a.nchunk, D = a.D, L = 2 * nch * B;
-    if (K < 2) return 0;
-    const uint64_t total = K * L + K * B + B * nch + B * D + 2 * B;
-    if (total > 0x7fffffffull || B + L > 0xffffffffull) return 0;
-    a.L = static_cast<uint32_t>(L);
-    a.body_end = static_cast<uint32_t>(K * (B + L));
-    a.fd_2nch = make_fastdiv(static_cast<uint32_t>(2 * nch));
-    a.fd_LB = make_fastdiv(static_cast<uint32_t>(B + L));
+// The position-major grid (chain_pm_grid), if the shape can take it: K >= 2,
+// B within the hardware's y dimension (65535), the tail within its two
+// slabs, and every flattened index below 2^31 (the tail decode divides
+// them).  Returns the number of workgroups, or 0.
+inline uint32_t chain_pm_schedule(const ChainArgs &a) {
+    const uint64_t B = a.B, K = a.K, nch = a.nchunk, D = a.D, X = 2 * nch + 1;
+    if (K < 2 || B > 65535) return 0;
+    if (nch + D + 2 > 2 * X) return 0;
+    const uint64_t total = X * B * (K + 2);
+    if (total > 0x7fffffffull) return 0;
     return static_cast<uint32_t>(total);
 }
 

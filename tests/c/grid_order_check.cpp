@@ -181,7 +181,7 @@ static void check_chain(const ChainShape &c) {
 }
 
 // The position-major one-launch order (early exit), K >= 2.
-static void check_chain_ex(const ChainShape &c) {
+static void check_chain_pm(const ChainShape &c) {
     Plan plan;
     if (!make_plan(SPEC_MODE_CHAIN, c.B, c.K, c.V, c.dt, plan) || c.B == 0 || c.K < 2) return;
     ChainArgs a{};
@@ -192,41 +192,58 @@ static void check_chain_ex(const ChainShape &c) {
     a.nchunk = plan.nchunk;
     a.nchunk2 = plan.nchunk2;
     chain_grid_fields(plan, c.K, a);
-    const uint32_t total = chain_ex_schedule(a);
+    const uint32_t total = chain_pm_schedule(a);
     if (total == 0) return;  // the sequence-major order runs instead
     ++g_cases;
-    if (g_mutant == 8) a.fd_LB = make_fastdiv(a.B + a.L + 1);  // blocks one workgroup too long
+    if (g_mutant == 8) a.fd_nch = make_fastdiv(a.nchunk + 1);  // the bonus rows' decode off by one
     const int64_t B = c.B, K = c.K, R = 2 * K + 1, nch = plan.nchunk, D = a.D;
-    CHECK(total == chain_ex_grid(a), "ex grid %u vs %u", total, chain_ex_grid(a));
+    const Grid3 grid = chain_pm_grid(a);
+    CHECK(static_cast<uint64_t>(grid.x) * grid.y * grid.z == total, "pm grid %u x %u x %u vs %u", grid.x,
+          grid.y, grid.z, total);
     CHECK(plan.off_pairs >= plan.off_rec + static_cast<size_t>(B) * kRecWords * 8, "pairs overlap records");
     CHECK(plan.off_pairs + static_cast<size_t>(B * K) * 8 <= plan.bytes, "pairs past the workspace");
     std::vector<int64_t> st(B * R * nch, -1), pr(B * K, -1), draw(B * D, -1), fin(B, -1), bon(B, -1);
+    // The arguments the decode sees (a planted mistake narrows its rows).
+    ChainArgs dec = a;
+    if (g_mutant == 9 && dec.nchunk > 1) dec.nchunk -= 1;  // slabs decoded one chunk too narrow
+    int64_t last_real = -1, first_none = -1;
     for (uint32_t g = 0; g < total; ++g) {
-        const ChainItem it = chain_ex_item(g, a);
-        CHECK(it.b < B, "ex g=%u b=%u", g, it.b);
+        // The flattened index the hardware hands out: x fastest, then y, then z.
+        const uint32_t x = g % grid.x, y = (g / grid.x) % grid.y, z = g / (grid.x * grid.y);
+        int row = -1, ch = -1;
+        const ChainItem it = chain_pm_item(x, y, z, dec, row, ch);
+        if (it.kind == kItemNone) {
+            CHECK(z >= K, "pm g=%u empty slot among the positions", g);
+            if (first_none < 0) first_none = g;
+            continue;
+        }
+        last_real = g;
+        CHECK(it.b < B, "pm g=%u b=%u", g, it.b);
         if (it.b >= B) continue;
         int64_t *slot = nullptr;
         if (it.kind == kItemStats) {
-            int row = -1, ch = -1;
-            chain_stats_row(it.p, a, row, ch);
-            CHECK(row >= 0 && row < R && row != K && ch >= 0 && ch < nch, "ex g=%u row=%d ch=%d", g, row, ch);
+            int prow = -1, pch = -1;
+            chain_stats_row(it.p, a, prow, pch);
+            CHECK(prow == row && pch == ch, "pm g=%u row %d/%d ch %d/%d", g, row, prow, ch, pch);
+            CHECK(z < K && row >= 0 && row < R && row != K && ch >= 0 && ch < nch, "pm g=%u row=%d ch=%d", g,
+                  row, ch);
             if (row >= 0 && row < R && ch >= 0 && ch < nch) slot = &st[(it.b * R + row) * nch + ch];
         } else if (it.kind == kItemBonusStats) {
-            CHECK(it.p < nch, "ex g=%u bonus chunk %u", g, it.p);
+            CHECK(it.p < nch, "pm g=%u bonus chunk %u", g, it.p);
             if (it.p < nch) slot = &st[(it.b * R + K) * nch + it.p];
         } else if (it.kind == kItemPair) {
-            CHECK(it.p < K, "ex g=%u position %u", g, it.p);
+            CHECK(it.p < K, "pm g=%u position %u", g, it.p);
             if (it.p < K) slot = &pr[it.b * K + it.p];
         } else if (it.kind == kItemDraw) {
-            CHECK(it.p < D, "ex g=%u draw chunk %u", g, it.p);
+            CHECK(it.p < D, "pm g=%u draw chunk %u", g, it.p);
             if (it.p < D) slot = &draw[it.b * D + it.p];
         } else if (it.kind == kItemFinisher) {
             slot = &fin[it.b];
         } else {
-            CHECK(it.kind == kItemBonus, "ex g=%u kind %d", g, it.kind);
+            CHECK(it.kind == kItemBonus, "pm g=%u kind %d", g, it.kind);
             slot = &bon[it.b];
         }
-        CHECK(slot && *slot < 0, "ex g=%u kind=%d b=%u p=%u twice", g, it.kind, it.b, it.p);
+        CHECK(slot && *slot < 0, "pm g=%u kind=%d b=%u p=%u twice", g, it.kind, it.b, it.p);
         if (slot) *slot = g;
     }
     for (int64_t b = 0; b < B; ++b) {
@@ -234,33 +251,35 @@ static void check_chain_ex(const ChainShape &c) {
         for (int64_t r = 0; r < R; ++r)
             for (int64_t ch = 0; ch < nch; ++ch) {
                 const int64_t p = st[(b * R + r) * nch + ch];
-                CHECK(p >= 0, "ex b=%lld row=%lld ch=%lld never run", (long long)b, (long long)r, (long long)ch);
+                CHECK(p >= 0, "pm b=%lld row=%lld ch=%lld never run", (long long)b, (long long)r, (long long)ch);
                 if (r == K) last_bonus_row = std::max(last_bonus_row, p);
             }
         for (int64_t k = 0; k < K; ++k) {
             const int64_t p = pr[b * K + k];
-            CHECK(p >= 0, "ex b=%lld pair %lld missing", (long long)b, (long long)k);
+            CHECK(p >= 0, "pm b=%lld pair %lld missing", (long long)b, (long long)k);
             // after the statistics of its two rows and the earlier positions' resolvers
             for (int64_t ch = 0; ch < nch; ++ch) {
                 CHECK(p > st[(b * R + k) * nch + ch] && p > st[(b * R + K + 1 + k) * nch + ch],
-                      "ex b=%lld pair %lld before its rows", (long long)b, (long long)k);
+                      "pm b=%lld pair %lld before its rows", (long long)b, (long long)k);
             }
-            if (k > 0) CHECK(p > pr[b * K + k - 1], "ex b=%lld pair %lld before pair %lld", (long long)b,
+            if (k > 0) CHECK(p > pr[b * K + k - 1], "pm b=%lld pair %lld before pair %lld", (long long)b,
                              (long long)k, (long long)(k - 1));
             // position k's outcome comes before position k + 1's rows
             if (k + 1 < K)
                 for (int64_t ch = 0; ch < nch; ++ch)
                     CHECK(p < st[(b * R + k + 1) * nch + ch] && p < st[(b * R + K + 2 + k) * nch + ch],
-                          "ex b=%lld pair %lld after its gated rows", (long long)b, (long long)k);
+                          "pm b=%lld pair %lld after its gated rows", (long long)b, (long long)k);
             last_pr = std::max(last_pr, p);
         }
         for (int64_t p = 0; p < D; ++p) {
-            CHECK(draw[b * D + p] > last_pr, "ex b=%lld draw before the record", (long long)b);
+            CHECK(draw[b * D + p] > last_pr, "pm b=%lld draw before the record", (long long)b);
             last_draw = std::max(last_draw, draw[b * D + p]);
         }
-        CHECK(fin[b] > last_draw && fin[b] > last_pr, "ex b=%lld finisher too early", (long long)b);
-        CHECK(bon[b] > last_pr && bon[b] > last_bonus_row, "ex b=%lld bonus item too early", (long long)b);
+        CHECK(fin[b] > last_draw && fin[b] > last_pr, "pm b=%lld finisher too early", (long long)b);
+        CHECK(bon[b] > last_pr && bon[b] > last_bonus_row, "pm b=%lld bonus item too early", (long long)b);
     }
+    CHECK(first_none < 0 || first_none > last_real, "pm empty slot %lld before item %lld", (long long)first_none,
+          (long long)last_real);
 }
 
 // ------------------------------------------------------------------ greedy chain, static tree
@@ -448,7 +467,7 @@ int main(int argc, char **argv) {
     };
     for (const auto &c : chains) {
         check_chain(c);
-        check_chain_ex(c);
+        check_chain_pm(c);
     }
     for (int i = 0; i < 300; ++i) {
         const int32_t B = 1 + static_cast<int32_t>(rng() % 96), K = static_cast<int32_t>(rng() % 17);
@@ -456,7 +475,7 @@ int main(int argc, char **argv) {
         const int32_t vmax = dt == BF ? (1 << 19) : (1 << 18);
         const int32_t V = 1 + static_cast<int32_t>(rng() % (i < 150 ? 20000 : vmax));
         check_chain({B, K, V, dt});
-        check_chain_ex({B, K, V, dt});
+        check_chain_pm({B, K, V, dt});
     }
     const int32_t argmax_shapes[][3] = {{64, 5, 32000}, {8, 0, 1}, {1, 64, 128256}, {3, 7, 8193},
                                         {32, 45, 128256}, {5, 1, 4096}, {300, 3, 100},

@@ -21,7 +21,8 @@ MUTANTS = {
     5: "two-phase draw items per sequence off by one",
     6: "compact tree order with rows of Nmax - 1",
     7: "top-k chunks per row off by one",
-    8: "position-major blocks one workgroup too long",
+    8: "position-major bonus rows decoded with nchunk + 1",
+    9: "position-major slabs decoded one chunk too narrow",
 }
 
 
