@@ -256,6 +256,7 @@ spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
     g.tokens = draft_tokens;
     g.B = B;
     g.K = K;
+    g.fd_per = make_fastdiv(static_cast<uint32_t>(K + 1));
     g.out_tokens = out_tokens;
     g.out_accepted = out_accepted;
     return launch_status(launch_greedy(g, dtype, stream));
@@ -296,6 +297,7 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
     t.am.chunk = plan.chunk;
     t.am.nchunk = plan.nchunk;
     t.am.fd_nch = make_fastdiv(plan.nchunk);
+    t.fd_per = make_fastdiv(static_cast<uint32_t>(N));
     const spec_status st = call_tag(workspace, stream, t.am.tag, t.am.tag_src);
     if (st != SPEC_OK) return st;
     t.am.partial = at<uint64_t>(workspace, plan.off_partial);

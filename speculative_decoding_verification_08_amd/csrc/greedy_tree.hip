@@ -9,11 +9,13 @@
 // +0.0 behave as on the raw logits.  Each publishes its chunk's (value, index)
 // as two tagged words.
 //
-// Resolve items: one workgroup per sequence (or tree), placed after every
-// argmax workgroup of the grid, so it only waits (bounded) for workgroups of
-// lower index.  Each group of 16 lanes merges one row's chunk partials with a
-// DPP tree; the comparison is exact, so the result does not depend on the
-// merge order.
+// Resolve: for the greedy chain and the static tree, the argmax item of the
+// last chunk of a sequence's last row resolves the sequence once its own
+// partial is out; for per-sequence trees, one resolve workgroup per tree
+// placed after every argmax workgroup.  Either way a resolve waits (bounded)
+// only for workgroups of lower index.  Each group of 16 lanes merges one
+// row's chunk partials with a DPP tree; the comparison is exact, so the
+// result does not depend on the merge order.
 #include "device.hpp"
 #include "handover.hpp"
 #include "grid_order.hpp"
@@ -117,6 +119,15 @@ __device__ __forceinline__ bool merge_argmax_rows(const uint64_t *part, int nrow
     __shared__ int s_stale[2][kWaves + 1];
     const int tid = threadIdx.x, lane = tid % kWave, grp = tid / kGroup, gl = tid % kGroup;
     const uint64_t t0 = wall_clock64();
+    // The sequence's last-dispatched chunk usually lands last: waiting for it
+    // first spares the rounds of reading everything again as earlier chunks
+    // come in one after another.
+    if (tid == 0) {
+        const uint64_t *last = part + 2 * (static_cast<int64_t>(nrows - 1) * nch + nch - 1);
+        wait_word(last, tag, t0);
+        wait_word(last + 1, tag, t0);
+    }
+    __syncthreads();
     for (int it = 0;; ++it) {
         const uint64_t *miss = nullptr;
         for (int r0 = 0; r0 < nrows; r0 += kGroups * kPasses) {
@@ -243,10 +254,21 @@ __device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, const Argma
     __shared__ int s_anc[kMaxTreeNodes];
     __shared__ int s_best;
     __shared__ int s_path[kMaxTreeNodes];
+    __shared__ int s_par[kMaxTreeNodes], s_dep[kMaxTreeNodes];
+    __shared__ int32_t s_tok[kMaxTreeNodes];
     static_assert(kMaxTreeNodes == kWG, "one thread per node");
     const int v = threadIdx.x;
     const int N = a.tree.N, D = a.tree.D, nch = am.nchunk;
+    // The tree's shape and the drafted tokens go to LDS while the partials
+    // are awaited: read from the argument block with a per-node index, each
+    // would otherwise be a memory round trip after the last partial lands
+    // (merge_argmax ends with a barrier).
     const int32_t tok = v < N ? a.tokens[static_cast<int64_t>(b) * N + v] : 0;
+    if (v < N) {
+        s_par[v] = a.tree.parent[v];
+        s_dep[v] = a.tree.depth[v];
+        s_tok[v] = tok;
+    }
     const uint64_t *part = am.partial + 2 * static_cast<int64_t>(b) * N * nch;
     if (!merge_argmax(part, N, nch, am.tag, s_a)) {
         if (v <= D) {
@@ -262,7 +284,7 @@ __device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, const Argma
     // match[v], then accepted = all matches on the path to the root, folded
     // by pointer jumping: after the steps of 1, 2, 4, ... <= D every node has
     // folded all of its at most D ancestors.
-    const int par = v < N ? a.tree.parent[v] : -1;
+    const int par = v < N ? s_par[v] : -1;
     if (v < N) {
         s_ok[v] = (v == 0) ? 1 : (tok == s_a[par]);
         s_anc[v] = par;
@@ -286,25 +308,25 @@ __device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, const Argma
         __syncthreads();
     }
     // Deepest accepted node, lowest index among equals.
-    const int key = (v < N && s_ok[v]) ? ((a.tree.depth[v] << 16) | (0xFFFF - v)) : -1;
+    const int key = (v < N && s_ok[v]) ? ((s_dep[v] << 16) | (0xFFFF - v)) : -1;
     const int best_key = max_wg(key);
     if (v == 0) s_best = 0xFFFF - (best_key & 0xFFFF);
     __syncthreads();
     if (v == 0) {
         const int best = s_best;
-        const int d = a.tree.depth[best];
+        const int d = s_dep[best];
         int node = best;
         for (int i = d; i >= 0; --i) {
             s_path[i] = node;
-            node = a.tree.parent[node];
+            node = s_par[node];
         }
     }
     __syncthreads();
     // Thread i writes entry i of the path outputs.
-    const int best = s_best, d = a.tree.depth[best];
+    const int best = s_best, d = s_dep[best];
     if (v <= D) {
         int32_t o = -1;
-        if (v < d) o = a.tokens[static_cast<int64_t>(b) * N + s_path[v + 1]];
+        if (v < d) o = s_tok[s_path[v + 1]];
         else if (v == d) o = s_a[best];
         a.out_tokens[static_cast<int64_t>(b) * (D + 1) + v] = o;
         if (a.out_path) a.out_path[static_cast<int64_t>(b) * (D + 1) + v] = v <= d ? s_path[v] : -1;
@@ -321,12 +343,14 @@ __device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, cons
     __shared__ int32_t s_a[kMaxTreeNodes];
     __shared__ int s_ok[kMaxTreeNodes], s_anc[kMaxTreeNodes], s_dep[kMaxTreeNodes];
     __shared__ int s_par[kMaxTreeNodes], s_path[kMaxTreeNodes];
+    __shared__ int32_t s_tok[kMaxTreeNodes];
     __shared__ int s_best;
     static_assert(kMaxTreeNodes == kWG, "one thread per node");
     const int v = threadIdx.x, Nmax = a.Nmax, nch = am.nchunk;
     const int64_t row0 = static_cast<int64_t>(b) * Nmax;
     const int n = min(max(a.node_count[b], 1), Nmax);
     const int32_t tok = v < n ? a.tokens[row0 + v] : 0;
+    if (v < n) s_tok[v] = tok;  // for the path's tokens, after merge_argmax's barrier
     int par = v < n ? a.parents[row0 + v] : -1;
     const bool valid = v > 0 && v < n && par >= 0 && par < v;
     if (!valid) par = -1;
@@ -385,7 +409,7 @@ __device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, cons
     const int best = s_best, d = s_dep[best];
     if (v < Nmax) {
         int32_t o = -1;
-        if (v < d) o = a.tokens[row0 + s_path[v + 1]];
+        if (v < d) o = s_tok[s_path[v + 1]];
         else if (v == d) o = s_a[best];
         a.out_tokens[row0 + v] = o;
         if (a.out_path) a.out_path[row0 + v] = v <= d ? s_path[v] : -1;
@@ -466,8 +490,10 @@ __global__ __launch_bounds__(kWG) void k_greedy(GreedyArgs a) {
     // second round of argument loads stands before the first logit load.
     asm volatile("" ::"s"(a.am.logits), "s"(a.am.V), "s"(a.am.chunk), "s"(a.am.partial), "s"(a.am.tag));
     const ArgmaxItem it = argmax_item_of(blockIdx.x, a.am.nchunk, a.am.fd_nch, static_cast<uint32_t>(a.am.rows));
-    if (it.argmax) argmax_item<DT, 4, VecOk>(am, it.row, static_cast<int>(it.ch));
-    else greedy_resolve_item(a, am, static_cast<int>(it.row));
+    argmax_item<DT, 4, VecOk>(am, it.row, static_cast<int>(it.ch));
+    uint32_t b;
+    if (argmax_resolves(it.row, it.ch, a.am.nchunk, static_cast<uint32_t>(a.K) + 1, a.fd_per, b))
+        greedy_resolve_item(a, am, static_cast<int>(b));
 }
 
 template <class DT, bool VecOk>
@@ -480,14 +506,16 @@ __global__ __launch_bounds__(kWG) void k_tree(TreeArgs a) {
     // second round of argument loads stands before the first logit load.
     asm volatile("" ::"s"(a.am.logits), "s"(a.am.V), "s"(a.am.chunk), "s"(a.am.partial), "s"(a.am.tag));
     const ArgmaxItem it = argmax_item_of(blockIdx.x, a.am.nchunk, a.am.fd_nch, static_cast<uint32_t>(a.am.rows));
-    if (it.argmax) argmax_item<DT, 4, VecOk>(am, it.row, static_cast<int>(it.ch));
-    else tree_resolve_item(a, am, static_cast<int>(it.row));
+    argmax_item<DT, 4, VecOk>(am, it.row, static_cast<int>(it.ch));
+    uint32_t b;
+    if (argmax_resolves(it.row, it.ch, a.am.nchunk, static_cast<uint32_t>(a.tree.N), a.fd_per, b))
+        tree_resolve_item(a, am, static_cast<int>(b));
 }
 
 }  // namespace
 
 hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(argmax_grid(a.am.rows, a.am.nchunk, a.B)), blk(kWG);
+    const dim3 g(argmax_only_grid(a.am.rows, a.am.nchunk)), blk(kWG);
     const bool vec = a.am.V % (dtype == 1 ? Bf16::kVec : F32::kVec) == 0;
     if (dtype == 1) {
         if (vec) k_greedy<Bf16, true><<<g, blk, 0, s>>>(a);
@@ -500,7 +528,7 @@ hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_tree(const TreeArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(argmax_grid(a.am.rows, a.am.nchunk, a.B)), blk(kWG);
+    const dim3 g(argmax_only_grid(a.am.rows, a.am.nchunk)), blk(kWG);
     const bool vec = a.am.V % (dtype == 1 ? Bf16::kVec : F32::kVec) == 0;
     if (dtype == 1) {
         if (vec) k_tree<Bf16, true><<<g, blk, 0, s>>>(a);

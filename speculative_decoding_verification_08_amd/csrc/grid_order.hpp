@@ -220,8 +220,8 @@ inline uint32_t topk_grid(int64_t rows, int64_t nch) {
 
 // ------------------------------------------------------------------ greedy chain and static tree
 
-// One workgroup per (row, chunk) of the argmax, rows in order, then one
-// resolve per sequence (or tree).
+// One workgroup per (row, chunk) of the argmax, rows in order (then, for the
+// per-sequence trees, one resolve per tree).
 struct ArgmaxItem {
     bool argmax;
     uint32_t row;  // argmax: the row; resolve: the sequence
@@ -236,9 +236,21 @@ __host__ __device__ __forceinline__ ArgmaxItem argmax_item_of(uint32_t g, uint32
     }
     return ArgmaxItem{false, g - nam, 0};
 }
-// Workgroups of the greedy, static-tree and per-sequence-tree launches.
+// Workgroups of the per-sequence-tree launch (argmax items, then a resolve
+// per tree).
 inline uint32_t argmax_grid(int64_t rows, int64_t nch, int64_t B) {
     return static_cast<uint32_t>(rows * nch + B);
+}
+
+// The greedy and static-tree launches have argmax items only: the item of
+// the last chunk of a sequence's last row (per rows a sequence) also
+// resolves the sequence.  Every other item of the sequence has a lower index,
+// so its wait for their words only waits on workgroups handed out before it.
+inline uint32_t argmax_only_grid(int64_t rows, int64_t nch) { return static_cast<uint32_t>(rows * nch); }
+__host__ __device__ __forceinline__ bool argmax_resolves(uint32_t row, uint32_t ch, uint32_t nch,
+                                                         uint32_t per, FastDiv fd_per, uint32_t &b) {
+    b = fdiv(row, fd_per);
+    return ch == nch - 1 && row == b * per + per - 1;
 }
 
 // ------------------------------------------------------------------ per-sequence trees

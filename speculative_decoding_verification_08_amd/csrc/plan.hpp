@@ -112,6 +112,7 @@ struct GreedyArgs {
     ArgmaxArgs am;
     const int32_t *tokens;   // [B][K]
     int32_t B, K;
+    FastDiv fd_per;          // division by K + 1, the rows of a sequence
     int32_t *out_tokens;     // [B][K+1]
     int32_t *out_accepted;   // [B]
 };
@@ -129,6 +130,7 @@ struct TreeArgs {
     ArgmaxArgs am;
     const int32_t *tokens;   // [B][N]
     int32_t B;
+    FastDiv fd_per;          // division by N, the rows of a tree
     int32_t *out_tokens;     // [B][D+1]
     int32_t *out_path;       // nullable [B][D+1]
     int32_t *out_depth;      // [B]

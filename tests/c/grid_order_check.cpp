@@ -293,22 +293,23 @@ static void check_argmax(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_
     CHECK(rows % B == 0, "rows %lld per sequence", (long long)rows);
     CHECK((nch - 1) * plan.chunk < V && nch * plan.chunk >= V, "argmax chunks");
     CHECK(plan.off_partial + static_cast<size_t>(rows * nch) * 16 <= plan.bytes, "argmax partials");
-    const uint32_t n = argmax_grid(rows, nch, B);
+    // Argmax items only; the last chunk of a sequence's last row resolves it.
+    const uint32_t n = argmax_only_grid(rows, nch);
+    const uint32_t per_dec = static_cast<uint32_t>(g_mutant == 10 ? per + 1 : per);  // rows a sequence, as decoded
+    const FastDiv fd_nch = make_fastdiv(static_cast<uint32_t>(nch)), fd_per = make_fastdiv(per_dec);
     std::vector<int64_t> am(rows * nch, -1), res(B, -1);
     for (uint32_t g = 0; g < n; ++g) {
-        const ArgmaxItem it = argmax_item_of(g, static_cast<uint32_t>(nch), make_fastdiv(static_cast<uint32_t>(nch)),
-                                             static_cast<uint32_t>(rows));
-        if (it.argmax) {
-            CHECK(it.row < rows && it.ch < nch, "g=%u", g);
-            if (it.row < rows && it.ch < nch) {
-                CHECK(am[it.row * nch + it.ch] < 0, "g=%u twice", g);
-                am[it.row * nch + it.ch] = g;
-            }
-        } else {
-            CHECK(it.row < static_cast<uint32_t>(B), "g=%u resolve %u", g, it.row);
-            if (it.row < static_cast<uint32_t>(B)) {
-                CHECK(res[it.row] < 0, "g=%u resolve twice", g);
-                res[it.row] = g;
+        const ArgmaxItem it = argmax_item_of(g, static_cast<uint32_t>(nch), fd_nch, static_cast<uint32_t>(rows));
+        CHECK(it.argmax && it.row < rows && it.ch < nch, "g=%u", g);
+        if (!(it.argmax && it.row < rows && it.ch < nch)) continue;
+        CHECK(am[it.row * nch + it.ch] < 0, "g=%u twice", g);
+        am[it.row * nch + it.ch] = g;
+        uint32_t b = 0;
+        if (argmax_resolves(it.row, it.ch, static_cast<uint32_t>(nch), per_dec, fd_per, b)) {
+            CHECK(b < static_cast<uint32_t>(B), "g=%u resolves %u", g, b);
+            if (b < static_cast<uint32_t>(B)) {
+                CHECK(res[b] < 0, "g=%u resolves %u twice", g, b);
+                res[b] = g;
             }
         }
     }
@@ -316,8 +317,8 @@ static void check_argmax(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_
         CHECK(res[b] >= 0, "resolve %lld missing", (long long)b);
         for (int64_t r = b * per; r < (b + 1) * per; ++r)
             for (int64_t ch = 0; ch < nch; ++ch)
-                CHECK(am[r * nch + ch] >= 0 && am[r * nch + ch] < res[b], "row %lld ch %lld", (long long)r,
-                      (long long)ch);
+                CHECK(am[r * nch + ch] >= 0 && am[r * nch + ch] <= res[b], "row %lld ch %lld after its resolve",
+                      (long long)r, (long long)ch);
     }
 }
 

@@ -23,6 +23,7 @@ MUTANTS = {
     7: "top-k chunks per row off by one",
     8: "position-major bonus rows decoded with nchunk + 1",
     9: "position-major slabs decoded one chunk too narrow",
+    10: "argmax resolve on a sequence of one row too many",
 }
 
 
