@@ -272,3 +272,16 @@ def test_tree_at_the_vocabulary_limit(sv):
     torch.cuda.synchronize()
     n = parity.check_tree(d, tok.cpu().numpy(), path.cpu().numpy(), depth.cpu().numpy())
     assert n["sequences"] == 1
+
+
+@pytest.mark.parametrize("B,K,V,dtype", [(8192, 2, 2048, "bf16"), (70000, 2, 64, "f32")])
+def test_chain_position_major_grid_limits(sv, B, K, V, dtype):
+    """The position-major order puts the sequence in the grid's y dimension:
+    8192 sequences run in it; past 65535 the call without diagnostics falls
+    back to the sequence-major order.  Both agree with the call with
+    diagnostics bit for bit, and with the oracle."""
+    case(f"chain position-major grid limits B={B} K={K} V={V} {dtype}")
+    d = chain_case(f"pmlim{B}", B, K, V, dtype, 1.0, sigma=0.7)
+    tok, acc, diag = run_chain(sv, d)
+    n = parity.check_chain(d, tok, acc, diag)
+    assert n["sequences"] == B
