@@ -107,7 +107,7 @@ struct ArgmaxArgs {
 };
 
 // Greedy chain verify in one launch: the argmax workgroups of rows
-// [B][K+1], then one resolve workgroup per sequence.
+// [B][K+1]; the one of a sequence's last chunk also resolves it.
 struct GreedyArgs {
     ArgmaxArgs am;
     const int32_t *tokens;   // [B][K]
@@ -125,7 +125,7 @@ struct TreeShape {
 };
 
 // Greedy static-tree verify in one launch: the argmax workgroups of node rows
-// [B][N], then one resolve workgroup per tree.
+// [B][N]; the one of a tree's last chunk also resolves it.
 struct TreeArgs {
     ArgmaxArgs am;
     const int32_t *tokens;   // [B][N]

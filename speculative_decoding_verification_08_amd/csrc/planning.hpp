@@ -71,7 +71,8 @@ inline bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dty
         if (rows * p.nchunk + (rows + 3) / 4 > 0x7fffffffLL) return false;
         off += align_up(static_cast<size_t>(rows) * p.nchunk * kMaxTopK * 16);
     } else {
-        // One launch: argmax workgroups, then one resolve workgroup per sequence.
+        // One launch: argmax workgroups (and, for per-sequence trees, one
+        // resolve workgroup per tree after them).
         if (rows * p.nchunk + B > 0x7fffffffLL) return false;
         off += align_up(static_cast<size_t>(rows) * p.nchunk * 16);  // two tagged words
     }
