@@ -102,7 +102,8 @@ inline uint32_t chain_schedule(ChainArgs &a) {
 }
 
 // The position-major grid (chain_pm_grid), if the shape can take it: K >= 2,
-// B within the hardware's y dimension (65535), the tail within its two
+// B within the grid's y dimension (gfx950 reports at most 65536; B <= 65535
+// is taken), the tail within its two
 // slabs, and every flattened index below 2^31 (the tail decode divides
 // them).  Returns the number of workgroups, or 0.
 inline uint32_t chain_pm_schedule(const ChainArgs &a) {
