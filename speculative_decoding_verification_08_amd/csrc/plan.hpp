@@ -13,7 +13,7 @@ constexpr int kMaxK = 64;
 constexpr int kMaxTreeNodes = 256;
 constexpr int kChunk2Bytes = 16384;  // bytes of one row per chunk of the residual / bonus pass
 // The chain's statistics items take 8 KB of a row each (two 16-byte vectors
-// per thread); a draw chunk is two statistics chunks.
+// per thread).
 constexpr int kStatVecs = 2;
 constexpr int kStatChunkBytes = kStatVecs * 16 * 256;
 constexpr int kMaxStatChunks = 128;  // statistics chunks per row: V <= 128 x 8 KB of entries
