@@ -217,7 +217,7 @@ spec_status spec_verify_chain_sample(const void *target_logits, const void *draf
  *
  * Returns SPEC_ERR_SCRATCH_LIMIT, before any HIP call, when
  * spec_verify_workspace_bytes(SPEC_MODE_CHAIN, B, K, V, dtype) exceeds that
- * size (B = 256, K = 8, V = 151936 fp32 needs 5.3 MiB), and
+ * size (B = 256, K = 8, V = 151936 fp32 needs 5.6 MiB), and
  * SPEC_ERR_INVALID_ARG for sizes spec_verify_chain rejects.  The first call on
  * a device looks up that device's copy (the current device; `stream` must
  * belong to it); SPEC_ERR_LAUNCH if that fails.

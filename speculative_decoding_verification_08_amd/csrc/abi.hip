@@ -93,6 +93,7 @@ spec_status chain_setup(const void *target, const void *draft, spec_dtype dtype,
     a.sums = at<uint64_t>(ws, plan.off_sums);
     a.rec = at<uint64_t>(ws, plan.off_rec);
     a.pairs = at<uint64_t>(ws, plan.off_pairs);
+    a.gate = at<uint64_t>(ws, plan.off_gate);
     // Skipping bonus-row chunks after a rejection costs each bonus-row item
     // one read of its record first: worth it once the bonus rows are more
     // than a few hundred chunks.
@@ -203,12 +204,16 @@ spec_status spec_verify_chain(const void *target_logits, const void *draft_logit
     // The position-major order when no per-position diagnostics are asked for
     // (they need every position's statistics) and one position's items fill
     // the chip (smaller batches wait on its resolvers' chain instead).  Its
-    // rows after a rejection are skipped only for long drafts: the check
-    // delays every gated item by one read, which measured slower for K = 5
-    // (64 x 5 x 128256 bf16: 43.0 against 38.7 us) and faster for K = 8
-    // (256 x 8 x 151936 fp32: 384 against 436 us).
+    // statistics items skip their rows after a published rejection, at the
+    // price of one read before their loads.  Items of position 1 skip too
+    // when one position's rows take long to stream (64 MB or more), so that
+    // position 0's outcomes come out early in position 1.  Measured, us per
+    // step: 64 x 5 x 128256 bf16 (33 MB a position) 34.0 skipping from
+    // position 2, 34.9 from position 1, 35.5 with no skips; 256 x 8 x 151936
+    // fp32 (311 MB) 272.0 from position 1, 275.8 from position 2, 318.8.
     a.early_exit = out_diag == nullptr && 2ll * plan.nchunk * B >= 2048 && chain_pm_schedule(a) != 0;
-    a.gate_rows = a.early_exit && K >= 6;
+    const int64_t position_bytes = 2ll * B * V * (dtype == SPEC_DTYPE_BF16 ? 2 : 4);
+    a.gate_pos1 = a.early_exit && position_bytes >= (64ll << 20);
     if (a.early_exit || chain_schedule(a) != 0) return launch_status(launch_chain_fused(a, dtype, stream));
     // Too large for one grid: the two kernels of the phase entry points, the
     // draws reading the statistics under this call's own tag.

@@ -619,6 +619,23 @@ __device__ __forceinline__ bool pair_stats(const ChainArgs &a, int b, int k, uin
     return s_ok != 0;
 }
 
+// Word offset of the gate line of (sequence b, position k).
+__device__ __forceinline__ int64_t gate_line(const ChainArgs &a, int b, int k) {
+    return (static_cast<int64_t>(b) * a.K + k) * kGateLineWords;
+}
+
+// The accept tests of sequence b ended at position k (a rejection or a
+// failure): marks the gate lines of positions k+1..K-1, whose rows are then
+// not needed.  Only the position-major orders, which skip rows, mark (a
+// compile-time choice: reading a flag for it made the compiler load the flag
+// at every workgroup's entry, one memory round trip before any load).
+template <bool Gate>
+__device__ __forceinline__ void mark_rows_not_needed(const ChainArgs &a, int b, int k, uint32_t tag) {
+    if constexpr (!Gate) return;
+    uint64_t *g = a.gate + gate_line(a, b, 0);
+    for (int i = k + 1; i < a.K; ++i) publish(g + i * kGateLineWords, tag, 1u);
+}
+
 // Publishes sequence b's record: j, then row j's (ref, 1/z) of the target and
 // the draft (zeros unless 0 <= j < K).
 __device__ __forceinline__ void publish_record(const ChainArgs &a, int b, uint32_t tag, int j, float rt,
@@ -641,7 +658,7 @@ __device__ __forceinline__ void publish_record(const ChainArgs &a, int b, uint32
 // the sequence's record (j = k), and so does the last position when every
 // draft is accepted (j = K).  A word that does not come in time fails the
 // sequence (record j = -1).
-template <class DT>
+template <class DT, bool Gate>
 __device__ __forceinline__ void pair_resolver_item(const ChainArgs &a, int b, int k) {
     __shared__ int s_prev;
     const int K = a.K, V = a.V, tid = threadIdx.x, lane = tid % kWave;
@@ -673,7 +690,10 @@ __device__ __forceinline__ void pair_resolver_item(const ChainArgs &a, int b, in
     if (s_prev != 0) {
         if (s_prev == 2) fail_sequence(a, b);
         if (tid == 0) {
-            if (s_prev == 2) publish_record(a, b, tag, -1, 0.f, 0.f, 0.f, 0.f);
+            if (s_prev == 2) {
+                publish_record(a, b, tag, -1, 0.f, 0.f, 0.f, 0.f);
+                mark_rows_not_needed<Gate>(a, b, k, tag);
+            }
             publish(pairs + k, tag, s_prev == 2 ? kPairFail : kPairSkip);
         }
         return;
@@ -683,6 +703,7 @@ __device__ __forceinline__ void pair_resolver_item(const ChainArgs &a, int b, in
         fail_sequence(a, b);
         if (tid == 0) {
             publish_record(a, b, tag, -1, 0.f, 0.f, 0.f, 0.f);
+            mark_rows_not_needed<Gate>(a, b, k, tag);
             publish(pairs + k, tag, kPairFail);
         }
         return;
@@ -697,8 +718,12 @@ __device__ __forceinline__ void pair_resolver_item(const ChainArgs &a, int b, in
             dg[1] = Q;
             dg[2] = Q > 0.f ? P / Q : (P > 0.f ? INFINITY : 0.f);
         }
-        if (reject) publish_record(a, b, tag, k, rt, 1.f / zt, rd, 1.f / zd);
-        else if (k == K - 1) publish_record(a, b, tag, K, 0.f, 0.f, 0.f, 0.f);
+        if (reject) {
+            mark_rows_not_needed<Gate>(a, b, k, tag);
+            publish_record(a, b, tag, k, rt, 1.f / zt, rd, 1.f / zd);
+        } else if (k == K - 1) {
+            publish_record(a, b, tag, K, 0.f, 0.f, 0.f, 0.f);
+        }
         publish(pairs + k, tag, reject ? kPairReject : kPairAccept);
     }
 }
@@ -711,21 +736,18 @@ __device__ __forceinline__ uint64_t plain_word(const uint64_t *p) {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Whether a statistics item of position k >= 1 of sequence b may skip its
+// Whether a statistics item of position k of sequence b may skip its
 // chunk: an outcome already published for a position below k ended the
-// sequence's accept tests.  Uniform over the workgroup (thread 0 reads, LDS
-// shares).
+// sequence's accept tests, and so marked the gate line of (b, k).  Each
+// (sequence, position) has a line of its own, read only by that position's
+// items: a line an XCD's L2 holds from a read made before the mark was
+// written stays stale there, and would otherwise hide the marks of later
+// positions too.  Uniform over the workgroup (thread 0 reads, LDS shares).
 __device__ __forceinline__ bool rows_not_needed(const ChainArgs &a, int b, int k) {
     __shared__ int s_skip;
     if (threadIdx.x == 0) {
         const uint32_t tag = a.tag_src ? *a.tag_src : a.tag;
-        const uint64_t *pairs = a.pairs + static_cast<int64_t>(b) * a.K;
-        bool skip = false;
-        for (int i = 0; i < k; ++i) {
-            const uint64_t v = plain_word(pairs + i);
-            skip = skip || (current(v, tag) && static_cast<uint32_t>(v) != kPairAccept);
-        }
-        s_skip = skip;
+        s_skip = current(plain_word(a.gate + gate_line(a, b, k)), tag);
     }
     __syncthreads();
     return s_skip != 0;
@@ -1071,15 +1093,18 @@ __global__ __launch_bounds__(kWG) void k_chain_draw(ChainArgs a) {
 // registers it cost the statistics items):
 //   kSeqMajor        chain_fused_item on a 1D grid, one resolver per sequence;
 //   kPosMajor        chain_pm_item on a 3D grid, one pair resolver per
-//                    position of each sequence;
-//   kPosMajorGated   the same, and statistics items of position k >= 1 skip
-//                    their chunk after a published rejection below k.
+//                    position of each sequence; statistics items of position
+//                    k >= 2 skip their chunk after a published rejection
+//                    below k;
+//   kPosMajorGate1   the same, and items of position 1 skip too (positions
+//                    whose rows stream long enough for position 0's
+//                    outcomes to come out early in position 1).
 // Sequence-major: each resolver finds its statistics done or nearly so, and
 // the stream of logits runs undisturbed: draws placed among the statistics
 // measured slower at every lag tried (their second read of row j takes slots
 // and bandwidth from the stream), so the second reads all come after it,
 // where the bonus draws, which need none, also run.
-enum ChainOrder : int { kSeqMajor = 0, kPosMajor = 1, kPosMajorGated = 2 };
+enum ChainOrder : int { kSeqMajor = 0, kPosMajor = 1, kPosMajorGate1 = 2 };
 
 template <class DT, bool VecOk, int Order>
 __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
@@ -1096,9 +1121,9 @@ __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
     const int b = static_cast<int>(it.b);
     if (it.kind == kItemStats) {
         if constexpr (Order == kSeqMajor) chain_stats_row(it.p, a, row, ch);
-        if constexpr (Order == kPosMajorGated) {
+        if constexpr (Order != kSeqMajor) {
             const int pos = static_cast<int>(blockIdx.z);
-            if (pos >= 1 && rows_not_needed(a, b, pos)) return;
+            if (pos >= (Order == kPosMajorGate1 ? 1 : 2) && rows_not_needed(a, b, pos)) return;
         }
         stats_item<DT, VecOk>(a, it.b, row, ch);
     } else if (Order != kSeqMajor && it.kind == kItemNone) {
@@ -1109,7 +1134,7 @@ __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
         if (a.gate_bonus && bonus_not_needed(a, b)) return;
         stats_item<DT, VecOk>(a, it.b, a.K, static_cast<int>(it.p));
     } else if (Order != kSeqMajor && it.kind == kItemPair) {
-        pair_resolver_item<DT>(a, b, static_cast<int>(it.p));
+        pair_resolver_item<DT, Order != kSeqMajor>(a, b, static_cast<int>(it.p));
     } else if (Order == kSeqMajor && it.kind == kItemResolver) {
         resolver_item<DT, true>(a, b, lds);
     } else if (it.kind == kItemDraw) {
@@ -1124,8 +1149,8 @@ __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
 template <class DT, bool VecOk>
 void launch_fused_order(const ChainArgs &a, dim3 g, hipStream_t s) {
     if (!a.early_exit) k_chain_fused<DT, VecOk, kSeqMajor><<<g, kWG, 0, s>>>(a);
-    else if (!a.gate_rows) k_chain_fused<DT, VecOk, kPosMajor><<<g, kWG, 0, s>>>(a);
-    else k_chain_fused<DT, VecOk, kPosMajorGated><<<g, kWG, 0, s>>>(a);
+    else if (!a.gate_pos1) k_chain_fused<DT, VecOk, kPosMajor><<<g, kWG, 0, s>>>(a);
+    else k_chain_fused<DT, VecOk, kPosMajorGate1><<<g, kWG, 0, s>>>(a);
 }
 
 }  // namespace

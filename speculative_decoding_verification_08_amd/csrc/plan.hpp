@@ -24,6 +24,10 @@ constexpr int kDrawChunkBytes = kStatChunkBytes;
 // top-k merges trail their rows' chunks by about this many workgroups.
 constexpr int kResidentWGs = 2048;
 constexpr int kRecWords = 8;       // words per sequence record (five used)
+// The row gate of a (sequence, position) is one tagged word alone on its
+// 128-byte cache line.
+constexpr int kGateLineBytes = 128;
+constexpr int kGateLineWords = kGateLineBytes / 8;
 // Outcome of one position's accept test (the low half of its tagged word).
 constexpr uint32_t kPairAccept = 0, kPairReject = 1, kPairSkip = 2, kPairFail = 3;
 constexpr int kMaxDrawChunks = kMaxStatChunks;  // draw chunks per row (two per lane of a wavefront)
@@ -43,7 +47,7 @@ struct Plan {
     int nchunk = 0;        // chunks per row, first pass
     int chunk2 = 0;        // elements per chunk, residual / bonus pass (chain)
     int nchunk2 = 0;       // chunks per row, residual / bonus pass (chain)
-    size_t off_partial = 0, off_sums = 0, off_rec = 0, off_pairs = 0;
+    size_t off_partial = 0, off_sums = 0, off_rec = 0, off_pairs = 0, off_gate = 0;
     size_t bytes = 0;      // total workspace
 };
 
@@ -83,7 +87,7 @@ struct ChainArgs {
     FastDiv fd_nch, fd_D, fd_S1;
     // Position-major one-launch order (early exit, a three-dimensional grid).
     bool early_exit;
-    bool gate_rows;          // position-major statistics skip rows after a rejection
+    bool gate_pos1;          // position-major statistics of position 1 also skip rows
     bool gate_bonus;         // bonus-row statistics skip rows whose sequence rejected
     uint64_t *pairs;         // [B][K] tagged outcome of each position's accept test
     uint64_t *partial;       // [B][2K+1][nchunk][2] tagged (ref, z); rows 0..K target, K+1.. draft
@@ -92,6 +96,9 @@ struct ChainArgs {
     int32_t *out_tokens;     // [B][K+1]
     int32_t *out_accepted;   // [B]
     float *out_diag;         // nullable [B][K+1][4]
+    // Last: the fields before it keep the offsets of the single batch of
+    // argument loads the statistics items were measured with.
+    uint64_t *gate;          // [B][K] lines: position k's rows of sequence b are not needed
 };
 
 // Row argmax over rows of [rows][V], one workgroup per (row, chunk).

@@ -62,6 +62,8 @@ inline bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dty
         off += align_up(static_cast<size_t>(B) * kRecWords * 8);
         p.off_pairs = off;  // one tagged outcome per position
         off += align_up(static_cast<size_t>(B) * KN * 8);
+        p.off_gate = off;   // one cache line per (sequence, position)
+        off += align_up(static_cast<size_t>(B) * KN * kGateLineBytes);
     } else if (mode == SPEC_MODE_TOPK) {
         // One launch: a workgroup per (row, chunk) and a merge workgroup per
         // row (one wavefront holds the row's chunk maxima, two per lane).

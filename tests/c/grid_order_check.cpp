@@ -201,7 +201,10 @@ static void check_chain_pm(const ChainShape &c) {
     CHECK(static_cast<uint64_t>(grid.x) * grid.y * grid.z == total, "pm grid %u x %u x %u vs %u", grid.x,
           grid.y, grid.z, total);
     CHECK(plan.off_pairs >= plan.off_rec + static_cast<size_t>(B) * kRecWords * 8, "pairs overlap records");
-    CHECK(plan.off_pairs + static_cast<size_t>(B * K) * 8 <= plan.bytes, "pairs past the workspace");
+    CHECK(plan.off_gate >= plan.off_pairs + static_cast<size_t>(B * K) * 8, "gate lines overlap pairs");
+    CHECK(plan.off_gate % kGateLineBytes == 0, "gate lines not line-aligned");
+    CHECK(plan.off_gate + static_cast<size_t>(B * K) * kGateLineBytes <= plan.bytes,
+          "gate lines past the workspace");
     std::vector<int64_t> st(B * R * nch, -1), pr(B * K, -1), draw(B * D, -1), fin(B, -1), bon(B, -1);
     // The arguments the decode sees (a planted mistake narrows its rows).
     ChainArgs dec = a;
