@@ -160,8 +160,9 @@ spec_status spec_verify_workspace_bytes(spec_mode mode, int32_t B, int32_t K_or_
  * Without out_diag, and when one position's work fills the GPU, the launch
  * streams the batch position by position and publishes each position's
  * accept outcome as it goes; then the bonus row of a sequence that rejected
- * a draft, and (for K >= 6) the rows of positions after a sequence's first
- * rejection, are not read.  The accept rule never consults them, so the
+ * a draft, and the rows of positions after a sequence's first rejection
+ * (from position 2 on, or from position 1 when one position's rows are
+ * 64 MB or more), are not read once that rejection is published.  The accept rule never consults them, so the
  * outputs are the same as with every row read.  With out_diag every
  * position's p, q and ratio are computed, so every row is read.
  */

@@ -215,12 +215,15 @@ def test_sample_after_stale_statistics_reports_failure(sv):
 # ------------------------------------------------------------------ position-major order
 
 @pytest.mark.parametrize("B,K,V,dtype", [(103, 8, 20000, "f32"), (128, 6, 32768, "bf16"),
-                                         (128, 5, 32768, "bf16"), (1024, 64, 2048, "bf16")])
+                                         (128, 5, 32768, "bf16"), (1024, 64, 2048, "bf16"),
+                                         (128, 3, 65536, "f32"), (256, 2, 65536, "bf16")])
 def test_chain_position_major_order(sv, B, K, V, dtype):
     """Shapes whose one-call verify runs position by position (one position's
-    items fill the chip; rows after a rejection are skipped for K >= 6): the
-    tokens equal the sequence-major order's (the call with diagnostics) bit
-    for bit, and the oracle's, at low and high acceptance."""
+    items fill the chip; rows after a rejection are skipped from position 2,
+    or from position 1 when a position's rows are 64 MB or more, as in the
+    last two shapes): the tokens equal the sequence-major order's (the call
+    with diagnostics) bit for bit, and the oracle's, at low and high
+    acceptance."""
     for sigma, step in ((0.7, 0), (2.5, 1)):
         case(f"chain position-major B={B} K={K} V={V} {dtype} sigma={sigma}")
         d = chain_case(f"pm{B}_{K}", B, K, V, dtype, 1.0, sigma=sigma, step=step)
