@@ -312,6 +312,22 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
     t.out_tokens = out_tokens;
     t.out_path = out_path;
     t.out_depth = out_depth;
+    // Node-major order, which does not read the rows of nodes that cannot be
+    // accepted, when the batch streams over many generations of workgroups
+    // (so that a node's outcome is out before its children's items start)
+    // and the tree reaches two levels below the root (a level-one node's
+    // items start before the root's outcome is out; from the first node two
+    // levels down, the items read their gate line).
+    t.gate_from = N;
+    for (int v = 1; v < N; ++v)
+        if (t.tree.depth[v] >= 2) {
+            t.gate_from = v;
+            break;
+        }
+    t.node_major = B <= 65535 && t.gate_from < N &&
+                   static_cast<int64_t>(B) * N * plan.nchunk >= kTreeNodeMajorItems;
+    t.node_out = at<uint64_t>(workspace, plan.off_pairs);
+    t.gate = at<uint64_t>(workspace, plan.off_gate);
     return launch_status(launch_tree(t, dtype, stream));
 }
 

@@ -728,14 +728,6 @@ __device__ __forceinline__ void pair_resolver_item(const ChainArgs &a, int b, in
     }
 }
 
-// A hand-over word read through the caches, without waiting: it may be stale
-// (an earlier value of this call's word, or a word of an earlier call), never
-// wrong, and a stale word only costs the skip it would have allowed.  The
-// device-scope read measured no better and delays the item more.
-__device__ __forceinline__ uint64_t plain_word(const uint64_t *p) {
-    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
 // Whether a statistics item of position k of sequence b may skip its
 // chunk: an outcome already published for a position below k ended the
 // sequence's accept tests, and so marked the gate line of (b, k).  Each

@@ -244,6 +244,53 @@ __device__ __forceinline__ void greedy_resolve_item(const GreedyArgs &a, const A
     if (lane == 0) a.out_accepted[b] = j;
 }
 
+// Tree b's outputs after a bounded wait ran out: every entry -1, counted.
+__device__ __forceinline__ void tree_fail(const TreeArgs &a, const ArgmaxArgs &am, int b) {
+    const int v = threadIdx.x, D = a.tree.D;
+    if (v <= D) {
+        a.out_tokens[static_cast<int64_t>(b) * (D + 1) + v] = -1;
+        if (a.out_path) a.out_path[static_cast<int64_t>(b) * (D + 1) + v] = -1;
+    }
+    if (v == 0) {
+        a.out_depth[b] = -1;
+        count_failure(am.hdr);
+    }
+}
+
+// Tree b's outputs from its accepted nodes (s_ok), their argmaxes (s_a, read
+// at accepted nodes only) and its shape in LDS: the deepest accepted node,
+// lowest index among equals, the tokens of the nodes on its path below the
+// root, then its argmax.  Thread i writes entry i.
+__device__ __forceinline__ void tree_emit(const TreeArgs &a, int b, const int *s_ok, const int32_t *s_a,
+                                          const int *s_par, const int *s_dep, const int32_t *s_tok) {
+    __shared__ int s_best;
+    __shared__ int s_path[kMaxTreeNodes];
+    const int v = threadIdx.x, N = a.tree.N, D = a.tree.D;
+    const int key = (v < N && s_ok[v]) ? ((s_dep[v] << 16) | (0xFFFF - v)) : -1;
+    const int best_key = max_wg(key);
+    if (v == 0) s_best = 0xFFFF - (best_key & 0xFFFF);
+    __syncthreads();
+    if (v == 0) {
+        const int best = s_best;
+        const int d = s_dep[best];
+        int node = best;
+        for (int i = d; i >= 0; --i) {
+            s_path[i] = node;
+            node = s_par[node];
+        }
+    }
+    __syncthreads();
+    const int best = s_best, d = s_dep[best];
+    if (v <= D) {
+        int32_t o = -1;
+        if (v < d) o = s_tok[s_path[v + 1]];
+        else if (v == d) o = s_a[best];
+        a.out_tokens[static_cast<int64_t>(b) * (D + 1) + v] = o;
+        if (a.out_path) a.out_path[static_cast<int64_t>(b) * (D + 1) + v] = v <= d ? s_path[v] : -1;
+    }
+    if (v == 0) a.out_depth[b] = d;
+}
+
 // Tree b: node v matches iff its token equals its parent's argmax; a node is
 // accepted iff it and all its ancestors match; the deepest accepted node wins
 // (lowest index among equals); emits the path's tokens, then that node's
@@ -252,8 +299,6 @@ __device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, const Argma
     __shared__ int32_t s_a[kMaxTreeNodes];
     __shared__ int s_ok[kMaxTreeNodes];
     __shared__ int s_anc[kMaxTreeNodes];
-    __shared__ int s_best;
-    __shared__ int s_path[kMaxTreeNodes];
     __shared__ int s_par[kMaxTreeNodes], s_dep[kMaxTreeNodes];
     __shared__ int32_t s_tok[kMaxTreeNodes];
     static_assert(kMaxTreeNodes == kWG, "one thread per node");
@@ -271,14 +316,7 @@ __device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, const Argma
     }
     const uint64_t *part = am.partial + 2 * static_cast<int64_t>(b) * N * nch;
     if (!merge_argmax(part, N, nch, am.tag, s_a)) {
-        if (v <= D) {
-            a.out_tokens[static_cast<int64_t>(b) * (D + 1) + v] = -1;
-            if (a.out_path) a.out_path[static_cast<int64_t>(b) * (D + 1) + v] = -1;
-        }
-        if (v == 0) {
-            a.out_depth[b] = -1;
-            count_failure(am.hdr);
-        }
+        tree_fail(a, am, b);
         return;
     }
     // match[v], then accepted = all matches on the path to the root, folded
@@ -307,31 +345,111 @@ __device__ __forceinline__ void tree_resolve_item(const TreeArgs &a, const Argma
         }
         __syncthreads();
     }
-    // Deepest accepted node, lowest index among equals.
-    const int key = (v < N && s_ok[v]) ? ((s_dep[v] << 16) | (0xFFFF - v)) : -1;
-    const int best_key = max_wg(key);
-    if (v == 0) s_best = 0xFFFF - (best_key & 0xFFFF);
+    tree_emit(a, b, s_ok, s_a, s_par, s_dep, s_tok);
+}
+
+// ------------------------------------------------------------ node-major order
+//
+// A node's row matters only if the node can be accepted: its argmax decides
+// its children's matches and, for the deepest accepted node, the bonus token.
+// In node-major order (nodes in index order, every tree's row of a node
+// together) each node's resolver publishes the node's outcome -- its argmax,
+// or kNodeDead when it cannot be accepted -- and marks the gate lines of the
+// children that cannot be accepted, so that their chunk items, dispatched
+// later, skip their loads.  The outputs are those of the tree-major order.
+
+constexpr uint32_t kNodeDead = 0xffffffffu, kNodeFailed = 0xfffffffeu;
+
+__device__ __forceinline__ int64_t node_gate_line(int64_t b, int N, int v) {
+    return (b * N + v) * kGateLineWords;
+}
+
+// Whether the chunk items of node v of tree b may skip: its gate line is
+// marked (read through the caches: a stale line only costs the skip).
+// Uniform over the workgroup.
+__device__ __forceinline__ bool node_not_needed(const TreeArgs &a, uint32_t tag, int b, int v) {
+    __shared__ int s_skip;
+    if (threadIdx.x == 0) s_skip = current(plain_word(a.gate + node_gate_line(b, a.tree.N, v)), tag);
     __syncthreads();
-    if (v == 0) {
-        const int best = s_best;
-        const int d = s_dep[best];
-        int node = best;
-        for (int i = d; i >= 0; --i) {
-            s_path[i] = node;
-            node = s_par[node];
+    return s_skip != 0;
+}
+
+// Tree b from every node's outcome, by the resolver of its last node (whose
+// own outcome is `last`): a node is accepted iff its outcome is an argmax.
+__device__ __forceinline__ void tree_from_outcomes(const TreeArgs &a, const ArgmaxArgs &am, int b,
+                                                   uint32_t last) {
+    __shared__ int32_t s_a[kMaxTreeNodes], s_tok[kMaxTreeNodes];
+    __shared__ int s_ok[kMaxTreeNodes], s_par[kMaxTreeNodes], s_dep[kMaxTreeNodes];
+    __shared__ int s_fail;
+    const int u = threadIdx.x, N = a.tree.N;
+    if (u == 0) s_fail = 0;
+    if (u < N) {
+        s_par[u] = a.tree.parent[u];
+        s_dep[u] = a.tree.depth[u];
+        s_tok[u] = a.tokens[static_cast<int64_t>(b) * N + u];
+    }
+    __syncthreads();
+    if (u < N) {
+        uint32_t o = last;
+        if (u < N - 1) {
+            const uint64_t *w = a.node_out + static_cast<int64_t>(b) * N + u;
+            wait_word(w, am.tag, wall_clock64());
+            const uint64_t x = fetch(w);
+            o = current(x, am.tag) ? static_cast<uint32_t>(x) : kNodeFailed;
         }
+        if (o == kNodeFailed) s_fail = 1;
+        s_ok[u] = o < kNodeFailed;
+        s_a[u] = static_cast<int32_t>(o);
     }
     __syncthreads();
-    // Thread i writes entry i of the path outputs.
-    const int best = s_best, d = s_dep[best];
-    if (v <= D) {
-        int32_t o = -1;
-        if (v < d) o = s_tok[s_path[v + 1]];
-        else if (v == d) o = s_a[best];
-        a.out_tokens[static_cast<int64_t>(b) * (D + 1) + v] = o;
-        if (a.out_path) a.out_path[static_cast<int64_t>(b) * (D + 1) + v] = v <= d ? s_path[v] : -1;
+    if (s_fail) {
+        tree_fail(a, am, b);
+        return;
     }
-    if (v == 0) a.out_depth[b] = d;
+    tree_emit(a, b, s_ok, s_a, s_par, s_dep, s_tok);
+}
+
+// Resolver of node v of tree b.  It waits (bounded) for its parent's
+// outcome: v can be accepted iff the parent is and v's token is the parent's
+// argmax.  Then it merges v's chunk partials into v's argmax (only if v can
+// be accepted: otherwise its items may have skipped), publishes the outcome,
+// and marks the gate line of each child that cannot be accepted.  A wait that
+// runs out makes the outcome kNodeFailed, and the tree's outputs -1.
+__device__ __forceinline__ void node_resolver_item(const TreeArgs &a, const ArgmaxArgs &am, int b, int v) {
+    __shared__ int32_t s_arg[1];
+    __shared__ uint32_t s_live;
+    const int N = a.tree.N, u = threadIdx.x;
+    const uint32_t tag = am.tag;
+    uint64_t *out = a.node_out + static_cast<int64_t>(b) * N;
+    const int32_t *tk = a.tokens + static_cast<int64_t>(b) * N;
+    // The children and their tokens, read before anything waits.
+    const bool child = u > v && u < N && a.tree.parent[u] == v;
+    const int32_t tok_u = child ? tk[u] : 0;
+    if (u == 0) {
+        uint32_t live = 1;  // 1: can be accepted, 0: cannot, 2: a wait ran out
+        if (v > 0) {
+            const int32_t tok_v = tk[v];
+            const uint64_t *pw = out + a.tree.parent[v];
+            wait_word(pw, tag, wall_clock64());
+            const uint64_t w = fetch(pw);
+            const uint32_t pv = static_cast<uint32_t>(w);
+            live = (!current(w, tag) || pv == kNodeFailed) ? 2u
+                   : (pv == kNodeDead || static_cast<int32_t>(pv) != tok_v) ? 0u
+                                                                          : 1u;
+        }
+        s_live = live;
+    }
+    __syncthreads();
+    const uint32_t live = s_live;
+    uint32_t res = live == 0 ? kNodeDead : kNodeFailed;
+    if (live == 1) {
+        const uint64_t *part = am.partial + 2 * (static_cast<int64_t>(b) * N + v) * am.nchunk;
+        if (merge_argmax(part, 1, am.nchunk, tag, s_arg)) res = static_cast<uint32_t>(s_arg[0]);
+    }
+    if (u == 0) publish(out + v, tag, res);
+    if (child && (res >= kNodeFailed || tok_u != static_cast<int32_t>(res)))
+        publish(a.gate + node_gate_line(b, N, u), tag, 1u);
+    if (v == N - 1) tree_from_outcomes(a, am, b, res);
 }
 
 // Tree b of a batch of per-sequence trees: n = node_count[b] (clamped to
@@ -496,15 +614,32 @@ __global__ __launch_bounds__(kWG) void k_greedy(GreedyArgs a) {
         greedy_resolve_item(a, am, static_cast<int>(b));
 }
 
-template <class DT, bool VecOk>
+template <class DT, bool VecOk, bool NodeMajor>
 __global__ __launch_bounds__(kWG) void k_tree(TreeArgs a) {
+    // The items' arguments in one batch ahead of everything else, so no
+    // second round of argument loads stands before the first logit load.
+    if constexpr (NodeMajor)
+        asm volatile("" ::"s"(a.am.logits), "s"(a.am.V), "s"(a.am.chunk), "s"(a.am.partial),
+                     "s"(a.am.tag), "s"(a.am.tag_src), "s"(a.am.nchunk), "s"(a.tree.N), "s"(a.gate),
+                     "s"(a.gate_from));
     // The argument block stays untouched (writing into it would copy it to
     // scratch); the argmax arguments with the call's tag are a local copy.
     ArgmaxArgs am = a.am;
     if (am.tag_src) am.tag = *am.tag_src;  // a graph replay's tag
-    // The argmax items' arguments in one batch ahead of the decode, so no
-    // second round of argument loads stands before the first logit load.
     asm volatile("" ::"s"(a.am.logits), "s"(a.am.V), "s"(a.am.chunk), "s"(a.am.partial), "s"(a.am.tag));
+    if constexpr (NodeMajor) {
+        // Grid (chunks + 1) x trees x nodes: x < nchunk a chunk item of row
+        // (y, z), x = nchunk the resolver of node z of tree y.
+        const int b = static_cast<int>(blockIdx.y), v = static_cast<int>(blockIdx.z);
+        const int ch = static_cast<int>(blockIdx.x);
+        if (ch < am.nchunk) {
+            if (v >= a.gate_from && node_not_needed(a, am.tag, b, v)) return;
+            argmax_item<DT, 4, VecOk>(am, static_cast<int64_t>(b) * a.tree.N + v, ch);
+        } else {
+            node_resolver_item(a, am, b, v);
+        }
+        return;
+    }
     const ArgmaxItem it = argmax_item_of(blockIdx.x, a.am.nchunk, a.am.fd_nch, static_cast<uint32_t>(a.am.rows));
     argmax_item<DT, 4, VecOk>(am, it.row, static_cast<int>(it.ch));
     uint32_t b;
@@ -527,15 +662,24 @@ hipError_t launch_greedy(const GreedyArgs &a, int dtype, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <class DT, bool VecOk>
+void launch_tree_order(const TreeArgs &a, hipStream_t s) {
+    if (a.node_major) {
+        const Grid3 g = tree_node_major_grid(a.am.nchunk, a.B, a.tree.N);
+        k_tree<DT, VecOk, true><<<dim3(g.x, g.y, g.z), kWG, 0, s>>>(a);
+    } else {
+        k_tree<DT, VecOk, false><<<dim3(argmax_only_grid(a.am.rows, a.am.nchunk)), kWG, 0, s>>>(a);
+    }
+}
+
 hipError_t launch_tree(const TreeArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(argmax_only_grid(a.am.rows, a.am.nchunk)), blk(kWG);
     const bool vec = a.am.V % (dtype == 1 ? Bf16::kVec : F32::kVec) == 0;
     if (dtype == 1) {
-        if (vec) k_tree<Bf16, true><<<g, blk, 0, s>>>(a);
-        else k_tree<Bf16, false><<<g, blk, 0, s>>>(a);
+        if (vec) launch_tree_order<Bf16, true>(a, s);
+        else launch_tree_order<Bf16, false>(a, s);
     } else {
-        if (vec) k_tree<F32, true><<<g, blk, 0, s>>>(a);
-        else k_tree<F32, false><<<g, blk, 0, s>>>(a);
+        if (vec) launch_tree_order<F32, true>(a, s);
+        else launch_tree_order<F32, false>(a, s);
     }
     return hipGetLastError();
 }

@@ -247,6 +247,11 @@ inline uint32_t argmax_grid(int64_t rows, int64_t nch, int64_t B) {
 // resolves the sequence.  Every other item of the sequence has a lower index,
 // so its wait for their words only waits on workgroups handed out before it.
 inline uint32_t argmax_only_grid(int64_t rows, int64_t nch) { return static_cast<uint32_t>(rows * nch); }
+// The static tree's node-major grid: (chunks + 1) x trees x nodes; x = nchunk
+// is the resolver of node z of tree y.
+inline Grid3 tree_node_major_grid(int32_t nch, int32_t B, int32_t N) {
+    return Grid3{static_cast<uint32_t>(nch) + 1, static_cast<uint32_t>(B), static_cast<uint32_t>(N)};
+}
 __host__ __device__ __forceinline__ bool argmax_resolves(uint32_t row, uint32_t ch, uint32_t nch,
                                                          uint32_t per, FastDiv fd_per, uint32_t &b) {
     b = fdiv(row, fd_per);

@@ -36,6 +36,14 @@ __device__ __forceinline__ bool current(uint64_t w, uint32_t tag) {
 __device__ __forceinline__ float word_f32(uint64_t w) {
     return __uint_as_float(static_cast<uint32_t>(w));
 }
+// A hand-over word read through the caches, without waiting: it may be stale
+// (an earlier value of this call's word, or a word of an earlier call), never
+// wrong, and a stale word only costs the skip it would have allowed.  The
+// device-scope read measured no better and delays the item more.
+__device__ __forceinline__ uint64_t plain_word(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Bounded wait (from t0) until one word carries the call's tag.  One lane
 // polls one word with a pause between reads, so waiting workgroups add little
 // traffic beside the streaming ones; the caller then reads everything it

@@ -23,9 +23,12 @@ constexpr int kDrawChunkBytes = kStatChunkBytes;
 // Workgroups of 256 threads the chip holds at once (256 CUs, 8 each): the
 // top-k merges trail their rows' chunks by about this many workgroups.
 constexpr int kResidentWGs = 2048;
+// Chunk items from which a static-tree batch takes the node-major order
+// (about eight generations of resident workgroups).
+constexpr int64_t kTreeNodeMajorItems = 8 * kResidentWGs;
 constexpr int kRecWords = 8;       // words per sequence record (five used)
-// The row gate of a (sequence, position) is one tagged word alone on its
-// 128-byte cache line.
+// The row gate of a (sequence, position), or of a tree node, is one tagged
+// word alone on its 128-byte cache line.
 constexpr int kGateLineBytes = 128;
 constexpr int kGateLineWords = kGateLineBytes / 8;
 // Outcome of one position's accept test (the low half of its tagged word).
@@ -47,7 +50,9 @@ struct Plan {
     int nchunk = 0;        // chunks per row, first pass
     int chunk2 = 0;        // elements per chunk, residual / bonus pass (chain)
     int nchunk2 = 0;       // chunks per row, residual / bonus pass (chain)
-    size_t off_partial = 0, off_sums = 0, off_rec = 0, off_pairs = 0, off_gate = 0;
+    size_t off_partial = 0, off_sums = 0, off_rec = 0;
+    size_t off_pairs = 0;  // chain: an outcome per position; static tree: one per node
+    size_t off_gate = 0;   // gate lines of the same
     size_t bytes = 0;      // total workspace
 };
 
@@ -131,8 +136,10 @@ struct TreeShape {
     int32_t N, D;
 };
 
-// Greedy static-tree verify in one launch: the argmax workgroups of node rows
-// [B][N]; the one of a tree's last chunk also resolves it.
+// Greedy static-tree verify in one launch.  Tree-major: the argmax workgroups
+// of node rows [B][N]; the one of a tree's last chunk also resolves it.
+// Node-major: node by node, every tree's chunk items of the node and then a
+// resolver per tree; a node that cannot be accepted is not read.
 struct TreeArgs {
     ArgmaxArgs am;
     const int32_t *tokens;   // [B][N]
@@ -142,6 +149,11 @@ struct TreeArgs {
     int32_t *out_path;       // nullable [B][D+1]
     int32_t *out_depth;      // [B]
     TreeShape tree;
+    // Node-major order (a 3D grid: chunk and resolver, tree, node).
+    uint64_t *node_out;      // [B][N] tagged outcome of each node: its argmax, or kNodeDead
+    uint64_t *gate;          // [B][N] lines: node v of tree b cannot be accepted
+    int32_t gate_from;       // the first node whose chunk items read their gate line
+    bool node_major;         // the launch's order (read on the host only)
 };
 
 // Greedy verify on per-sequence trees in one launch: the argmax workgroups of

@@ -296,6 +296,16 @@ static void check_argmax(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_
     CHECK(rows % B == 0, "rows %lld per sequence", (long long)rows);
     CHECK((nch - 1) * plan.chunk < V && nch * plan.chunk >= V, "argmax chunks");
     CHECK(plan.off_partial + static_cast<size_t>(rows * nch) * 16 <= plan.bytes, "argmax partials");
+    if (mode == SPEC_MODE_TREE) {
+        // The node-major order: an outcome word per node, then a gate line
+        // per node, and a grid (chunks + 1) x trees x nodes.
+        CHECK(plan.off_pairs >= plan.off_partial + static_cast<size_t>(rows * nch) * 16, "node outcomes overlap");
+        CHECK(plan.off_gate >= plan.off_pairs + static_cast<size_t>(rows) * 8, "node gates overlap");
+        CHECK(plan.off_gate % kGateLineBytes == 0, "node gates not line-aligned");
+        CHECK(plan.off_gate + static_cast<size_t>(rows) * kGateLineBytes <= plan.bytes, "node gates past the workspace");
+        const Grid3 g = tree_node_major_grid(static_cast<int32_t>(nch), B, KN);
+        CHECK(static_cast<int64_t>(g.x) * g.y * g.z == (nch + 1) * rows, "node-major grid");
+    }
     // Argmax items only; the last chunk of a sequence's last row resolves it.
     const uint32_t n = argmax_only_grid(rows, nch);
     const uint32_t per_dec = static_cast<uint32_t>(g_mutant == 10 ? per + 1 : per);  // rows a sequence, as decoded

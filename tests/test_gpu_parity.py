@@ -312,6 +312,29 @@ def test_tree_full_size_128k(sv):
         print("tree_128k mean depth", g[2].mean())
 
 
+@pytest.mark.parametrize("B,V,dtype,shape,p_match", [
+    (40, 65536, "f32", "c5", 0.6), (40, 65536, "f32", "c5", 0.95), (40, 65536, "f32", "c5", 0.1),
+    (128, 8192, "bf16", "random", 0.8), (600, 32000, "bf16", "chain", 0.7)])
+def test_tree_node_major_order(sv, B, V, dtype, shape, p_match):
+    """Batches of at least 16384 chunk items (B x N x chunks) whose tree
+    reaches two levels down stream node by node, and the chunks of nodes that
+    cannot be accepted are not read: the outputs equal the oracle's exactly,
+    whatever was skipped, at low, middling and high match rates."""
+    rng = np.random.default_rng(B + int(100 * p_match))
+    if shape == "c5":
+        parents = None  # branching 4, 2, 2, 1: 45 nodes
+    elif shape == "random":
+        parents = [-1] + [int(rng.integers(max(0, v - 4), v)) for v in range(1, 130)]
+    else:
+        parents = [-1, 0, 1, 2, 3, 4, 5]
+    w = W.Workload("tn", 96, "tree", B=B, V=V, dtype=dtype, branching=(4, 2, 2, 1), recipe="peaked")
+    case(f"tree node-major B={B} V={V} {dtype} {shape} p_match={p_match}")
+    d = W.tree_inputs(w, 0, parents=parents, p_match=p_match)
+    g = run_tree(sv, d)
+    parity.check_tree(d, *g)
+    print("node-major", shape, p_match, "mean depth", g[2].mean())
+
+
 # ------------------------------------------------------------------ per-sequence trees
 
 def run_tree_dyn(sv, d):
