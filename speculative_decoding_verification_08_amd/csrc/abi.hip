@@ -368,6 +368,13 @@ spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtyp
     t.out_tokens = out_tokens;
     t.out_path = out_path;
     t.out_depth = out_depth;
+    // Node-major order (rows of nodes that cannot be accepted are not read)
+    // for batches that stream over many generations of workgroups, as for
+    // the static tree; padding rows cost their items one read of the count.
+    t.node_major = B <= 65535 && Nmax >= 3 &&
+                   static_cast<int64_t>(B) * Nmax * plan.nchunk >= kTreeNodeMajorItems;
+    t.node_out = at<uint64_t>(workspace, plan.off_pairs);
+    t.gate = at<uint64_t>(workspace, plan.off_gate);
     return launch_status(launch_tree_dyn(t, dtype, stream));
 }
 

@@ -452,44 +452,32 @@ __device__ __forceinline__ void node_resolver_item(const TreeArgs &a, const Argm
     if (v == N - 1) tree_from_outcomes(a, am, b, res);
 }
 
-// Tree b of a batch of per-sequence trees: n = node_count[b] (clamped to
-// [1, Nmax]) nodes with parents[b][v] < v; the static tree's rule on that
-// tree.  A node whose parent entry is out of range is unattached: neither it
-// nor its subtree is accepted, and nothing outside the tree is read.  Depths
-// and acceptance are both folded by pointer jumping, ceil(log2 n) steps.
-__device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, const ArgmaxArgs &am, int b) {
-    __shared__ int32_t s_a[kMaxTreeNodes];
-    __shared__ int s_ok[kMaxTreeNodes], s_anc[kMaxTreeNodes], s_dep[kMaxTreeNodes];
-    __shared__ int s_par[kMaxTreeNodes], s_path[kMaxTreeNodes];
-    __shared__ int32_t s_tok[kMaxTreeNodes];
+// Tree b's outputs after a bounded wait ran out: every entry -1, counted.
+__device__ __forceinline__ void tree_dyn_fail(const TreeDynArgs &a, const ArgmaxArgs &am, int b) {
+    const int v = threadIdx.x;
+    const int64_t row0 = static_cast<int64_t>(b) * a.Nmax;
+    if (v < a.Nmax) {
+        a.out_tokens[row0 + v] = -1;
+        if (a.out_path) a.out_path[row0 + v] = -1;
+    }
+    if (v == 0) {
+        a.out_depth[b] = -1;
+        count_failure(am.hdr);
+    }
+}
+
+// Tree b of n nodes from node v's match (s_ok), parent (s_anc, s_par; -1 if
+// unattached), unit depth step (s_dep), argmax (s_a) and token (s_tok), in
+// LDS: acceptance and depth folded over the ancestors by pointer jumping,
+// ceil(log2 n) steps; then the deepest accepted node, lowest index among
+// equals (the root always is), its path's tokens and its argmax.
+__device__ __forceinline__ void tree_dyn_finish(const TreeDynArgs &a, int b, int n, int *s_ok, int *s_anc,
+                                                int *s_dep, const int *s_par, const int32_t *s_a,
+                                                const int32_t *s_tok) {
     __shared__ int s_best;
-    static_assert(kMaxTreeNodes == kWG, "one thread per node");
-    const int v = threadIdx.x, Nmax = a.Nmax, nch = am.nchunk;
+    __shared__ int s_path[kMaxTreeNodes];
+    const int v = threadIdx.x, Nmax = a.Nmax;
     const int64_t row0 = static_cast<int64_t>(b) * Nmax;
-    const int n = min(max(a.node_count[b], 1), Nmax);
-    const int32_t tok = v < n ? a.tokens[row0 + v] : 0;
-    if (v < n) s_tok[v] = tok;  // for the path's tokens, after merge_argmax's barrier
-    int par = v < n ? a.parents[row0 + v] : -1;
-    const bool valid = v > 0 && v < n && par >= 0 && par < v;
-    if (!valid) par = -1;
-    const uint64_t *part = am.partial + 2 * row0 * nch;
-    if (!merge_argmax(part, n, nch, am.tag, s_a)) {
-        if (v < Nmax) {
-            a.out_tokens[row0 + v] = -1;
-            if (a.out_path) a.out_path[row0 + v] = -1;
-        }
-        if (v == 0) {
-            a.out_depth[b] = -1;
-            count_failure(am.hdr);
-        }
-        return;
-    }
-    if (v < n) {
-        s_ok[v] = v == 0 ? 1 : (valid && tok == s_a[max(par, 0)]);
-        s_anc[v] = par;
-        s_dep[v] = v == 0 ? 0 : 1;
-        s_par[v] = par;
-    }
     __syncthreads();
     for (int step = 1; step < n; step <<= 1) {
         int ok = 0, anc = -1, dep = 0;
@@ -511,7 +499,6 @@ __device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, cons
         }
         __syncthreads();
     }
-    // Deepest accepted node, lowest index among equals (the root always is).
     const int key = (v < n && s_ok[v]) ? ((s_dep[v] << 16) | (0xFFFF - v)) : -1;
     const int best_key = max_wg(key);
     if (v == 0) {
@@ -533,6 +520,129 @@ __device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, cons
         if (a.out_path) a.out_path[row0 + v] = v <= d ? s_path[v] : -1;
     }
     if (v == 0) a.out_depth[b] = d;
+}
+
+// Tree b of a batch of per-sequence trees: n = node_count[b] (clamped to
+// [1, Nmax]) nodes with parents[b][v] < v; the static tree's rule on that
+// tree.  A node whose parent entry is out of range is unattached: neither it
+// nor its subtree is accepted, and nothing outside the tree is read.  Depths
+// and acceptance are both folded by pointer jumping, ceil(log2 n) steps.
+__device__ __forceinline__ void tree_dyn_resolve_item(const TreeDynArgs &a, const ArgmaxArgs &am, int b) {
+    __shared__ int32_t s_a[kMaxTreeNodes];
+    __shared__ int s_ok[kMaxTreeNodes], s_anc[kMaxTreeNodes], s_dep[kMaxTreeNodes];
+    __shared__ int s_par[kMaxTreeNodes];
+    __shared__ int32_t s_tok[kMaxTreeNodes];
+    static_assert(kMaxTreeNodes == kWG, "one thread per node");
+    const int v = threadIdx.x, Nmax = a.Nmax, nch = am.nchunk;
+    const int64_t row0 = static_cast<int64_t>(b) * Nmax;
+    const int n = min(max(a.node_count[b], 1), Nmax);
+    const int32_t tok = v < n ? a.tokens[row0 + v] : 0;
+    if (v < n) s_tok[v] = tok;  // for the path's tokens, after merge_argmax's barrier
+    int par = v < n ? a.parents[row0 + v] : -1;
+    const bool valid = v > 0 && v < n && par >= 0 && par < v;
+    if (!valid) par = -1;
+    const uint64_t *part = am.partial + 2 * row0 * nch;
+    if (!merge_argmax(part, n, nch, am.tag, s_a)) {
+        tree_dyn_fail(a, am, b);
+        return;
+    }
+    if (v < n) {
+        s_ok[v] = v == 0 ? 1 : (valid && tok == s_a[max(par, 0)]);
+        s_anc[v] = par;
+        s_dep[v] = v == 0 ? 0 : 1;
+        s_par[v] = par;
+    }
+    tree_dyn_finish(a, b, n, s_ok, s_anc, s_dep, s_par, s_a, s_tok);
+}
+
+// Node-major order for per-sequence trees (as the static tree's, above):
+// chunk items read their tree's node count and their gate line in one round
+// and skip padding rows and nodes that cannot be accepted; a resolver per
+// (tree, node) publishes the node's outcome and marks its children's gate
+// lines; the resolver of a tree's last node resolves the tree.
+__device__ __forceinline__ bool dyn_node_skips(const TreeDynArgs &a, uint32_t tag, int b, int v) {
+    __shared__ int s_skip;
+    if (threadIdx.x == 0) {
+        const int32_t count = a.node_count[b];
+        const uint64_t g = plain_word(a.gate + node_gate_line(b, a.Nmax, v));
+        s_skip = v >= min(max(count, 1), a.Nmax) || current(g, tag);
+    }
+    __syncthreads();
+    return s_skip != 0;
+}
+
+__device__ __forceinline__ void dyn_node_resolver_item(const TreeDynArgs &a, const ArgmaxArgs &am, int b,
+                                                       int v) {
+    __shared__ int32_t s_arg[1];
+    __shared__ uint32_t s_live;
+    __shared__ int32_t s_a[kMaxTreeNodes], s_tok[kMaxTreeNodes];
+    __shared__ int s_ok[kMaxTreeNodes], s_anc[kMaxTreeNodes], s_dep[kMaxTreeNodes], s_par[kMaxTreeNodes];
+    __shared__ int s_fail;
+    const int Nmax = a.Nmax, u = threadIdx.x;
+    const int n = min(max(a.node_count[b], 1), Nmax);
+    if (v >= n) return;  // a padding row
+    const uint32_t tag = am.tag;
+    const int64_t row0 = static_cast<int64_t>(b) * Nmax;
+    uint64_t *out = a.node_out + row0;
+    // The children, their tokens, and (for the last node's tree resolve)
+    // every node's parent and token, read before anything waits.
+    const int par_u = u < n ? a.parents[row0 + u] : -1;
+    const int32_t tok_u = u < n ? a.tokens[row0 + u] : 0;
+    const bool child = u > v && u < n && par_u == v;
+    if (u == 0) {
+        uint32_t live = 1;  // 1: can be accepted, 0: cannot, 2: a wait ran out
+        if (v > 0) {
+            const int p = a.parents[row0 + v];
+            if (p < 0 || p >= v) {
+                live = 0;  // unattached
+            } else {
+                const int32_t tok_v = a.tokens[row0 + v];
+                wait_word(out + p, tag, wall_clock64());
+                const uint64_t w = fetch(out + p);
+                const uint32_t pv = static_cast<uint32_t>(w);
+                live = (!current(w, tag) || pv == kNodeFailed) ? 2u
+                       : (pv == kNodeDead || static_cast<int32_t>(pv) != tok_v) ? 0u
+                                                                              : 1u;
+            }
+        }
+        s_live = live;
+    }
+    __syncthreads();
+    const uint32_t live = s_live;
+    uint32_t res = live == 0 ? kNodeDead : kNodeFailed;
+    if (live == 1) {
+        const uint64_t *part = am.partial + 2 * (row0 + v) * am.nchunk;
+        if (merge_argmax(part, 1, am.nchunk, tag, s_arg)) res = static_cast<uint32_t>(s_arg[0]);
+    }
+    if (u == 0) publish(out + v, tag, res);
+    if (child && (res >= kNodeFailed || tok_u != static_cast<int32_t>(res)))
+        publish(a.gate + node_gate_line(b, Nmax, u), tag, 1u);
+    if (v != n - 1) return;
+    // The tree, from every node's outcome: accepted iff it is an argmax.
+    if (u == 0) s_fail = 0;
+    __syncthreads();
+    if (u < n) {
+        uint32_t o = res;
+        if (u < n - 1) {
+            wait_word(out + u, tag, wall_clock64());
+            const uint64_t x = fetch(out + u);
+            o = current(x, tag) ? static_cast<uint32_t>(x) : kNodeFailed;
+        }
+        if (o == kNodeFailed) s_fail = 1;
+        const int par = (u > 0 && par_u >= 0 && par_u < u) ? par_u : -1;
+        s_ok[u] = o < kNodeFailed;
+        s_a[u] = static_cast<int32_t>(o);
+        s_tok[u] = tok_u;
+        s_anc[u] = par;
+        s_par[u] = par;
+        s_dep[u] = u == 0 ? 0 : 1;
+    }
+    __syncthreads();
+    if (s_fail) {
+        tree_dyn_fail(a, am, b);
+        return;
+    }
+    tree_dyn_finish(a, b, n, s_ok, s_anc, s_dep, s_par, s_a, s_tok);
 }
 
 // Inclusive integer sum over lanes 0..lane of a wavefront (DPP, as the
@@ -574,12 +684,31 @@ __device__ __forceinline__ uint32_t locate_row(const TreeDynArgs &a, uint32_t R,
     return T;
 }
 
-template <class DT, bool VecOk>
+template <class DT, bool VecOk, bool NodeMajor>
 __global__ __launch_bounds__(kWG) void k_tree_dyn(TreeDynArgs a) {
+    // The items' arguments in one batch ahead of everything else, so no
+    // second round of argument loads stands before the first logit load.
+    if constexpr (NodeMajor)
+        asm volatile("" ::"s"(a.am.logits), "s"(a.am.V), "s"(a.am.chunk), "s"(a.am.partial),
+                     "s"(a.am.tag), "s"(a.am.tag_src), "s"(a.am.nchunk), "s"(a.Nmax), "s"(a.node_count),
+                     "s"(a.gate));
     // The argument block stays untouched (writing into it would copy it to
     // scratch); the argmax arguments with the call's tag are a local copy.
     ArgmaxArgs am = a.am;
     if (am.tag_src) am.tag = *am.tag_src;  // a graph replay's tag
+    if constexpr (NodeMajor) {
+        // Grid (chunks + 1) x trees x Nmax: x < nchunk a chunk item of row
+        // (y, z), x = nchunk the resolver of node z of tree y.
+        const int b = static_cast<int>(blockIdx.y), v = static_cast<int>(blockIdx.z);
+        const int ch = static_cast<int>(blockIdx.x);
+        if (ch < am.nchunk) {
+            if (v > 0 && dyn_node_skips(a, am.tag, b, v)) return;
+            argmax_item<DT, 4, VecOk>(am, static_cast<int64_t>(b) * a.Nmax + v, ch);
+        } else {
+            dyn_node_resolver_item(a, am, b, v);
+        }
+        return;
+    }
     const uint32_t nch = a.am.nchunk, g = blockIdx.x, B = static_cast<uint32_t>(a.B);
     // This workgroup's item: an argmax item (row, ch), the resolve of tree
     // `row`, or nothing.
@@ -684,15 +813,24 @@ hipError_t launch_tree(const TreeArgs &a, int dtype, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <class DT, bool VecOk>
+void launch_tree_dyn_order(const TreeDynArgs &a, hipStream_t s) {
+    if (a.node_major) {
+        const Grid3 g = tree_node_major_grid(a.am.nchunk, a.B, a.Nmax);
+        k_tree_dyn<DT, VecOk, true><<<dim3(g.x, g.y, g.z), kWG, 0, s>>>(a);
+    } else {
+        k_tree_dyn<DT, VecOk, false><<<dim3(argmax_grid(a.am.rows, a.am.nchunk, a.B)), kWG, 0, s>>>(a);
+    }
+}
+
 hipError_t launch_tree_dyn(const TreeDynArgs &a, int dtype, hipStream_t s) {
-    const dim3 g(argmax_grid(a.am.rows, a.am.nchunk, a.B)), blk(kWG);
     const bool vec = a.am.V % (dtype == 1 ? Bf16::kVec : F32::kVec) == 0;
     if (dtype == 1) {
-        if (vec) k_tree_dyn<Bf16, true><<<g, blk, 0, s>>>(a);
-        else k_tree_dyn<Bf16, false><<<g, blk, 0, s>>>(a);
+        if (vec) launch_tree_dyn_order<Bf16, true>(a, s);
+        else launch_tree_dyn_order<Bf16, false>(a, s);
     } else {
-        if (vec) k_tree_dyn<F32, true><<<g, blk, 0, s>>>(a);
-        else k_tree_dyn<F32, false><<<g, blk, 0, s>>>(a);
+        if (vec) launch_tree_dyn_order<F32, true>(a, s);
+        else launch_tree_dyn_order<F32, false>(a, s);
     }
     return hipGetLastError();
 }

@@ -156,9 +156,9 @@ struct TreeArgs {
     bool node_major;         // the launch's order (read on the host only)
 };
 
-// Greedy verify on per-sequence trees in one launch: the argmax workgroups of
-// node rows [B][Nmax] (rows past a tree's node count skip), then one resolve
-// workgroup per tree.
+// Greedy verify on per-sequence trees in one launch.  Tree-major: the argmax
+// workgroups of node rows [B][Nmax] (rows past a tree's node count skip),
+// then one resolve workgroup per tree.  Node-major: as the static tree's.
 struct TreeDynArgs {
     ArgmaxArgs am;
     const int32_t *tokens;      // [B][Nmax]
@@ -169,6 +169,10 @@ struct TreeDynArgs {
     int32_t *out_tokens;        // [B][Nmax]
     int32_t *out_path;          // nullable [B][Nmax]
     int32_t *out_depth;         // [B]
+    // Node-major order (a 3D grid: chunk and resolver, tree, node slot).
+    uint64_t *node_out;         // [B][Nmax] tagged outcome of each node: its argmax, or kNodeDead
+    uint64_t *gate;             // [B][Nmax] lines: node v of tree b cannot be accepted
+    bool node_major;            // the launch's order (read on the host only)
 };
 
 // Host launchers (defined next to their kernels).

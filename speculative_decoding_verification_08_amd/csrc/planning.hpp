@@ -77,7 +77,7 @@ inline bool make_plan(spec_mode mode, int32_t B, int32_t KN, int32_t V, spec_dty
         // resolve workgroup per tree after them).
         if (rows * p.nchunk + B > 0x7fffffffLL) return false;
         off += align_up(static_cast<size_t>(rows) * p.nchunk * 16);  // two tagged words
-        if (mode == SPEC_MODE_TREE) {
+        if (mode == SPEC_MODE_TREE || mode == SPEC_MODE_TREE_DYN) {
             p.off_pairs = off;  // the node-major order: one tagged outcome per node
             off += align_up(static_cast<size_t>(rows) * 8);
             p.off_gate = off;   // and one gate line per node

@@ -368,6 +368,14 @@ static void check_tree_dyn(int32_t B, int32_t Nmax, int32_t V, spec_dtype dt, st
     CHECK(make_plan(SPEC_MODE_TREE_DYN, B, Nmax, V, dt, plan), "tree_dyn shape rejected");
     ++g_cases;
     if (B == 0) return;
+    {
+        // The node-major order: an outcome word and a gate line per node slot.
+        const int64_t rows = plan.rows, nch = plan.nchunk;
+        CHECK(plan.off_pairs >= plan.off_partial + static_cast<size_t>(rows * nch) * 16, "node outcomes overlap");
+        CHECK(plan.off_gate >= plan.off_pairs + static_cast<size_t>(rows) * 8, "node gates overlap");
+        CHECK(plan.off_gate % kGateLineBytes == 0, "node gates not line-aligned");
+        CHECK(plan.off_gate + static_cast<size_t>(rows) * kGateLineBytes <= plan.bytes, "node gates past the workspace");
+    }
     // Node counts: in range, or out of range both ways (clamped to [1, Nmax]).
     std::vector<int32_t> count(B);
     for (auto &c : count) {

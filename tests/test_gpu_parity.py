@@ -355,6 +355,40 @@ def test_tree_dyn_random_shapes(sv):
         parity.check_tree_dyn(d, *run_tree_dyn(sv, d))
 
 
+@pytest.mark.parametrize("B,Nmax,V,dtype,p_match", [
+    (32, 64, 65536, "f32", 0.6), (32, 64, 65536, "f32", 0.95), (300, 9, 65536, "bf16", 0.5)])
+def test_tree_dyn_node_major_order(sv, B, Nmax, V, dtype, p_match):
+    """Batches of at least 16384 chunk items (B x Nmax x chunks) stream node
+    by node: padding rows and nodes that cannot be accepted are not read.  Two
+    node counts are out of range (clamped to 1 and to Nmax) and two trees have
+    an unattached node.  Expected: the oracle on the same trees with counts
+    clamped and each unattached node re-attached to the root with a token
+    that matches nothing."""
+    w = W.Workload("tdn", 98, "tree_dyn", B=B, K=Nmax, V=V, dtype=dtype, recipe="peaked")
+    d = W.tree_dyn_inputs(w, 0, p_match=p_match, nmin=1)
+    par, cnt, tok = d["parents"].copy(), d["node_count"].copy(), d["node_tokens"].copy()
+    exp_par, exp_tok = par.copy(), tok.copy()
+    cnt[0], cnt[1] = 0, Nmax + 5
+    for v in range(1, Nmax):  # sequence 1 now has Nmax nodes: padding gets parents in range
+        if v >= d["node_count"][1]:
+            par[1, v] = exp_par[1, v] = v - 1
+    for b in (2, 3):
+        v = int(min(cnt[b], Nmax)) - 1
+        if v >= 1:
+            par[b, v] = v + 3
+            exp_par[b, v] = 0
+            exp_tok[b, v] = -1
+    exp_cnt = np.clip(cnt, 1, Nmax).astype(np.int32)
+    case(f"per-sequence trees node-major B={B} Nmax={Nmax} V={V} {dtype} p_match={p_match}")
+    g = sv.spec_verify_tree_greedy_dyn(dev(d["node_logits"]), dev(tok), dev(par), dev(cnt))
+    torch.cuda.synchronize()
+    g = [x.cpu().numpy() for x in g]
+    o = oracle.verify_tree_greedy_dyn(d["node_logits"], exp_tok, exp_par, exp_cnt)
+    for x, y in zip(g, o):
+        assert np.array_equal(x, y)
+    print("node-major per-sequence", B, Nmax, p_match, "mean depth", g[2].mean())
+
+
 def test_tree_dyn_batch_sizes_around_the_compact_limit(sv):
     """Batches of up to 256 trees take the compact item order (argmax items on
     real rows only), larger ones one item per row slot: both sides of the
