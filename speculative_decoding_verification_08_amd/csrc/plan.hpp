@@ -23,9 +23,12 @@ constexpr int kDrawChunkBytes = kStatChunkBytes;
 // Workgroups of 256 threads the chip holds at once (256 CUs, 8 each): the
 // top-k merges trail their rows' chunks by about this many workgroups.
 constexpr int kResidentWGs = 2048;
-// Chunk items from which a static-tree batch takes the node-major order
-// (about eight generations of resident workgroups).
-constexpr int64_t kTreeNodeMajorItems = 8 * kResidentWGs;
+// Chunk items (trees x node slots x chunks) from which a tree batch takes the
+// node-major order, about five generations of resident workgroups.  Measured
+// on 45-node trees (branching 4, 2, 2, 1) and 64-slot per-sequence trees,
+// V = 128256 bf16, us per call, tree-major against node-major: 5,760 items
+// 19.9 / 24.9, 8,192 items 19.2 / 24.0, 11,520 items 33.8 / 30.0.
+constexpr int64_t kTreeNodeMajorItems = 5 * kResidentWGs;
 constexpr int kRecWords = 8;       // words per sequence record (five used)
 // The row gate of a (sequence, position), or of a tree node, is one tagged
 // word alone on its 128-byte cache line.

@@ -316,7 +316,7 @@ def test_tree_full_size_128k(sv):
     (40, 65536, "f32", "c5", 0.6), (40, 65536, "f32", "c5", 0.95), (40, 65536, "f32", "c5", 0.1),
     (128, 8192, "bf16", "random", 0.8), (600, 32000, "bf16", "chain", 0.7)])
 def test_tree_node_major_order(sv, B, V, dtype, shape, p_match):
-    """Batches of at least 16384 chunk items (B x N x chunks) whose tree
+    """Batches of at least 10240 chunk items (B x N x chunks) whose tree
     reaches two levels down stream node by node, and the chunks of nodes that
     cannot be accepted are not read: the outputs equal the oracle's exactly,
     whatever was skipped, at low, middling and high match rates."""
@@ -358,7 +358,7 @@ def test_tree_dyn_random_shapes(sv):
 @pytest.mark.parametrize("B,Nmax,V,dtype,p_match", [
     (32, 64, 65536, "f32", 0.6), (32, 64, 65536, "f32", 0.95), (300, 9, 65536, "bf16", 0.5)])
 def test_tree_dyn_node_major_order(sv, B, Nmax, V, dtype, p_match):
-    """Batches of at least 16384 chunk items (B x Nmax x chunks) stream node
+    """Batches of at least 10240 chunk items (B x Nmax x chunks) stream node
     by node: padding rows and nodes that cannot be accepted are not read.  Two
     node counts are out of range (clamped to 1 and to Nmax) and two trees have
     an unattached node.  Expected: the oracle on the same trees with counts
