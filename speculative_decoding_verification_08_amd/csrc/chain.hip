@@ -51,46 +51,38 @@ struct NegInf<F32> {
 
 // ------------------------------------------------------------ stats item
 
-// Row r of sequence b (r <= K: target row r; r > K: draft row r - K - 1),
-// chunk ch: a.chunk entries, 8 KB, two 16-byte vectors per thread.  With V a
-// multiple of the vector width every chunk starts on a vector (the vectors
-// past the end of a row's last chunk read as -inf); otherwise the entries are
-// read one by one.  Loads are non-temporal: a logit is streamed once, and its
-// second read by a draw comes from HBM either way.
-template <class DT, bool VecOk>
-__device__ __forceinline__ void stats_item(const ChainArgs &a, int64_t b, int r, int ch) {
+// Loads chunk ch of a row (element offset `trow * V` in `base`): thread t
+// takes vectors t and t + 256 (one non-temporal 16-byte load each, both in
+// flight before any use); returns the chunk's vector count.
+template <class DT>
+__device__ __forceinline__ int load_stat_chunk(const ChainArgs &a, const void *base, int64_t trow, int ch,
+                                               uint4 (&raw)[kStatVecs]) {
+    constexpr int VEC = DT::kVec;
+    const int64_t e0 = static_cast<int64_t>(ch) * a.chunk;
+    const int n = static_cast<int>(min(static_cast<int64_t>(a.chunk), static_cast<int64_t>(a.V) - e0));
+    const uint4 *vp = static_cast<const uint4 *>(base) + (trow * a.V + e0) / VEC;
+    const int nv = n / VEC, last = nv - 1, tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kStatVecs; ++u) raw[u] = load_nt(vp + min(tid + u * kWG, last));
+    return nv;
+}
+
+// The softmax statistics of a loaded chunk, published as its partial: the
+// vectors past the row's end (in its last chunk) read as -inf.
+template <class DT>
+__device__ __forceinline__ void reduce_stat_chunk(const ChainArgs &a, int64_t row, int ch,
+                                                  uint4 (&raw)[kStatVecs], int nv) {
     constexpr int VEC = DT::kVec, U = kStatVecs, N = U * VEC;
     constexpr uint32_t kInf = NegInf<DT>::kBits;
-    const int K = a.K, V = a.V, R = 2 * K + 1;
-    const int64_t row = b * R + r;
-    const void *base = r <= K ? a.target : a.draft;
-    const int64_t trow = r <= K ? b * (K + 1) + r : b * K + (r - K - 1);
-    const int64_t e0 = static_cast<int64_t>(ch) * a.chunk;
-    const int n = static_cast<int>(min(static_cast<int64_t>(a.chunk), static_cast<int64_t>(V) - e0));
     const int tid = threadIdx.x;
-    float x[N];
-    if constexpr (VecOk) {
-        const uint4 *vp = static_cast<const uint4 *>(base) + (trow * V + e0) / VEC;
-        const int nv = n / VEC, last = nv - 1;
-        uint4 raw[U];
+    if (nv < U * kWG) {  // the row's last chunk
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = load_nt(vp + min(tid + u * kWG, last));
-        if (nv < U * kWG) {  // the row's last chunk
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (tid + u * kWG > last) raw[u] = make_uint4(kInf, kInf, kInf, kInf);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) unpack<DT>(raw[u], x + u * VEC);
-    } else {
-        const int64_t g0 = trow * V + e0;
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int e = tid + i * kWG;
-            const float v = load_one<DT>(base, g0 + min(e, n - 1));
-            x[i] = e < n ? v : -INFINITY;
-        }
+        for (int u = 0; u < U; ++u)
+            if (tid + u * kWG > nv - 1) raw[u] = make_uint4(kInf, kInf, kInf, kInf);
     }
+    float x[N];
+#pragma unroll
+    for (int u = 0; u < U; ++u) unpack<DT>(raw[u], x + u * VEC);
     float ref = -INFINITY, z = 0.f;
     mz_chunk_wg<N>(x, a.c, ref, z);
     if (tid == 0) {
@@ -99,6 +91,67 @@ __device__ __forceinline__ void stats_item(const ChainArgs &a, int64_t b, int r,
         publish_f32(w, tag, ref);
         publish_f32(w + 1, tag, z);
     }
+}
+
+// Statistics item: softmax statistics (ref, z) of one chunk of row r of
+// sequence b (r <= K: target row r; r > K: draft row r - K - 1), published as
+// tagged words; chunk ch: a.chunk entries, 8 KB, two 16-byte vectors per
+// thread.  With V a
+// multiple of the vector width every chunk starts on a vector (the vectors
+// past the end of a row's last chunk read as -inf); otherwise the entries are
+// read one by one.  Loads are non-temporal: a logit is streamed once, and its
+// second read by a draw comes from HBM either way.
+template <class DT, bool VecOk>
+__device__ __forceinline__ void stats_item(const ChainArgs &a, int64_t b, int r, int ch) {
+    const int K = a.K, R = 2 * K + 1;
+    const int64_t row = b * R + r;
+    const void *base = r <= K ? a.target : a.draft;
+    const int64_t trow = r <= K ? b * (K + 1) + r : b * K + (r - K - 1);
+    if constexpr (VecOk) {
+        uint4 raw[kStatVecs];
+        const int nv = load_stat_chunk<DT>(a, base, trow, ch, raw);
+        reduce_stat_chunk<DT>(a, row, ch, raw, nv);
+    } else {
+        constexpr int N = kStatVecs * DT::kVec;
+        const int64_t e0 = static_cast<int64_t>(ch) * a.chunk;
+        const int n = static_cast<int>(min(static_cast<int64_t>(a.chunk), static_cast<int64_t>(a.V) - e0));
+        const int64_t g0 = trow * a.V + e0;
+        float x[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int e = threadIdx.x + i * kWG;
+            const float v = load_one<DT>(base, g0 + min(e, n - 1));
+            x[i] = e < n ? v : -INFINITY;
+        }
+        float ref = -INFINITY, z = 0.f;
+        mz_chunk_wg<N>(x, a.c, ref, z);
+        if (threadIdx.x == 0) {
+            const uint32_t tag = a.tag_src ? *a.tag_src : a.tag;  // a graph replay's tag
+            uint64_t *w = a.partial + 2 * (row * a.nchunk + ch);
+            publish_f32(w, tag, ref);
+            publish_f32(w + 1, tag, z);
+        }
+    }
+}
+
+// Two adjacent chunks ch, ch + 1 of row r in one workgroup (both chunks'
+// loads in flight together; ch + 1 only if the row has it), each reduced and
+// published exactly as a statistics item does it.  V a multiple of the
+// vector width.
+template <class DT>
+__device__ __forceinline__ void stats_pair(const ChainArgs &a, int64_t b, int r, int ch) {
+    const int K = a.K, R = 2 * K + 1;
+    const int64_t row = b * R + r;
+    const void *base = r <= K ? a.target : a.draft;
+    const int64_t trow = r <= K ? b * (K + 1) + r : b * K + (r - K - 1);
+    const bool two = ch + 1 < a.nchunk;
+    uint4 raw0[kStatVecs], raw1[kStatVecs];
+    const int nv0 = load_stat_chunk<DT>(a, base, trow, ch, raw0);
+    const int nv1 = two ? load_stat_chunk<DT>(a, base, trow, ch + 1, raw1) : 0;
+    reduce_stat_chunk<DT>(a, row, ch, raw0, nv0);
+    if (!two) return;
+    __syncthreads();  // the reduction's LDS words are reused
+    reduce_stat_chunk<DT>(a, row, ch + 1, raw1, nv1);
 }
 
 // ------------------------------------------------------------ draw weights
@@ -1115,7 +1168,19 @@ __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
         if constexpr (Order == kSeqMajor) chain_stats_row(it.p, a, row, ch);
         if constexpr (Order != kSeqMajor) {
             const int pos = static_cast<int>(blockIdx.z);
-            if (pos >= (Order == kPosMajorGate1 ? 1 : 2) && rows_not_needed(a, b, pos)) return;
+            if (pos >= (Order == kPosMajorGate1 ? 1 : 2)) {
+                if constexpr (VecOk) {
+                    // In a gated position the item of an even chunk streams
+                    // that chunk and the next after one gate read; the odd
+                    // chunk's item returns at once.  Half the gate reads, and
+                    // a skipped row costs half the workgroup lives.
+                    if (ch & 1) return;
+                    if (rows_not_needed(a, b, pos)) return;
+                    stats_pair<DT>(a, it.b, row, ch);
+                    return;
+                }
+                if (rows_not_needed(a, b, pos)) return;
+            }
         }
         stats_item<DT, VecOk>(a, it.b, row, ch);
     } else if (Order != kSeqMajor && it.kind == kItemNone) {
