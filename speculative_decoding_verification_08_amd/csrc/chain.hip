@@ -134,24 +134,26 @@ __device__ __forceinline__ void stats_item(const ChainArgs &a, int64_t b, int r,
     }
 }
 
-// Two adjacent chunks ch, ch + 1 of row r in one workgroup (both chunks'
-// loads in flight together; ch + 1 only if the row has it), each reduced and
-// published exactly as a statistics item does it.  V a multiple of the
-// vector width.
-template <class DT>
-__device__ __forceinline__ void stats_pair(const ChainArgs &a, int64_t b, int r, int ch) {
+// Chunks ch .. ch + G - 1 of row r (those the row has) in one workgroup, all
+// their loads in flight together, each chunk reduced and published exactly
+// as a statistics item does it.  V a multiple of the vector width.
+template <class DT, int G>
+__device__ __forceinline__ void stats_group(const ChainArgs &a, int64_t b, int r, int ch) {
     const int K = a.K, R = 2 * K + 1;
     const int64_t row = b * R + r;
     const void *base = r <= K ? a.target : a.draft;
     const int64_t trow = r <= K ? b * (K + 1) + r : b * K + (r - K - 1);
-    const bool two = ch + 1 < a.nchunk;
-    uint4 raw0[kStatVecs], raw1[kStatVecs];
-    const int nv0 = load_stat_chunk<DT>(a, base, trow, ch, raw0);
-    const int nv1 = two ? load_stat_chunk<DT>(a, base, trow, ch + 1, raw1) : 0;
-    reduce_stat_chunk<DT>(a, row, ch, raw0, nv0);
-    if (!two) return;
-    __syncthreads();  // the reduction's LDS words are reused
-    reduce_stat_chunk<DT>(a, row, ch + 1, raw1, nv1);
+    const int m = min(G, a.nchunk - ch);
+    uint4 raw[G][kStatVecs];
+    int nv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) nv[g] = g < m ? load_stat_chunk<DT>(a, base, trow, ch + g, raw[g]) : 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (g >= m) return;
+        if (g > 0) __syncthreads();  // the reduction's LDS words are reused
+        reduce_stat_chunk<DT>(a, row, ch + g, raw[g], nv[g]);
+    }
 }
 
 // ------------------------------------------------------------ draw weights
@@ -1170,13 +1172,18 @@ __global__ __launch_bounds__(kWG, 8) void k_chain_fused(ChainArgs a) {
             const int pos = static_cast<int>(blockIdx.z);
             if (pos >= (Order == kPosMajorGate1 ? 1 : 2)) {
                 if constexpr (VecOk) {
-                    // In a gated position the item of an even chunk streams
-                    // that chunk and the next after one gate read; the odd
-                    // chunk's item returns at once.  Half the gate reads, and
-                    // a skipped row costs half the workgroup lives.
-                    if (ch & 1) return;
+                    // In a gated position the item of chunk ch, ch a multiple
+                    // of G, streams chunks ch .. ch + G - 1 after one gate
+                    // read; the other items return at once.  1/G of the gate
+                    // reads, and a skipped row costs 1/G of the workgroup
+                    // lives.  G = 2 for short positions, 4 for long ones
+                    // (64 x 5 x 128256 bf16: 33.5 us with pairs, 35.7 with
+                    // fours; 256 x 8 x 151936 fp32: 253 us with pairs, 243
+                    // with fours).
+                    constexpr int G = Order == kPosMajorGate1 ? 4 : 2;
+                    if (ch % G != 0) return;
                     if (rows_not_needed(a, b, pos)) return;
-                    stats_pair<DT>(a, it.b, row, ch);
+                    stats_group<DT, G>(a, it.b, row, ch);
                     return;
                 }
                 if (rows_not_needed(a, b, pos)) return;
