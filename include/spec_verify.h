@@ -278,7 +278,10 @@ spec_status spec_verify_greedy(const void *target_logits, spec_dtype dtype,
  *
  * One kernel launch.  Each tree's resolve waits (bounded, about 2 s) for the
  * argmax workgroups of its node rows; if a wait ever ran out, the tree gets
- * out_depth[b] = -1 and out_tokens[b], out_path[b] all -1.
+ * out_depth[b] = -1 and out_tokens[b], out_path[b] all -1.  Large batches
+ * (B x N x 16 KB chunks of at least 10240) run node by node, and the row of
+ * a node that can no longer be accepted (an ancestor did not match) is not
+ * read; the outputs are those of reading every row.
  */
 spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
                                     const int32_t *node_tokens, const int32_t *parents,
@@ -311,7 +314,9 @@ spec_status spec_verify_tree_greedy(const void *node_logits, spec_dtype dtype,
  * range is never accepted (nor is its subtree); no entry outside the arrays
  * is read.  One kernel launch; each tree's resolve waits (bounded, about 2 s)
  * for the argmax workgroups of its node rows; if a wait ever ran out, the tree
- * gets out_depth[b] = -1 and out_tokens[b], out_path[b] all -1.
+ * gets out_depth[b] = -1 and out_tokens[b], out_path[b] all -1.  Large
+ * batches run node by node, as for spec_verify_tree_greedy, and do not read
+ * the rows of nodes that can no longer be accepted.
  */
 spec_status spec_verify_tree_greedy_dyn(const void *node_logits, spec_dtype dtype,
                                         const int32_t *node_tokens, const int32_t *parents,

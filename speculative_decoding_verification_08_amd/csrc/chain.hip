@@ -1,17 +1,20 @@
 // Chain verify at T > 0 on gfx950.
 //
-// Statistics items stream every logit of the step once.  One workgroup takes
-// one 8 KB vocabulary chunk of one row (target rows 0..K and draft rows
-// 0..K-1 of a sequence), folds it into softmax statistics (ref, z) and
-// publishes them.  This is the HBM-bound work that carries the bytes; no
-// statistics workgroup waits for another.
+// Statistics items stream the logits of the step, each at most once.  One
+// workgroup takes one 8 KB vocabulary chunk of one row (target rows 0..K and
+// draft rows 0..K-1 of a sequence), folds it into softmax statistics (ref, z)
+// and publishes them; in the position-major order a row whose position comes
+// after its sequence's first rejection is skipped, and there one workgroup
+// takes two or four adjacent chunks after reading its row's gate word.  This
+// is the HBM-bound work that carries the bytes; no statistics workgroup
+// waits for another.
 //
 // A resolver per sequence merges the statistics of the rows the accept tests
 // read, evaluates the accept test of every drafted token (u < p(x)/q(x),
 // French lesson "Décodage spéculatif et Eagle", section "La règle de
 // l'exactitude"; forum post "Speculative Decoding: от идеи до SOTA", §3),
 // finds the first rejection j and publishes a record: j and row j's
-// normalisers.  After a rejection, draw items (one per 16 KB chunk of row j)
+// normalisers.  After a rejection, draw items (one per 8 KB chunk of rows j)
 // publish the chunk's mass of the residual max(0, p_j - q_j) (the residual of
 // the same passages) and of p_j; the sequence's finisher finds the chunk
 // whose running mass first exceeds u * S, reads it again and draws the token.
