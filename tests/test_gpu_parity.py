@@ -1025,3 +1025,88 @@ def test_graph_capture_tagged_entry_points(sv):
         step()
         torch.cuda.synchronize()
         check(inputs)
+
+
+def test_graph_capture_skipping_orders(sv):
+    """The orders that skip rows, captured into one HIP graph: the chain's
+    position-major order (gate words per position, chunks paired in the gated
+    positions) and the node-major static and per-sequence trees (node outcomes
+    and gate words).  Every replay carries its own tag, so three replays with
+    new inputs, with eager calls on the same workspaces in between, all match
+    the oracle."""
+    wc = W.Workload("gs", 101, "chain", B=128, K=5, V=32768, dtype="bf16", T=1.0, recipe="peaked", sigma=0.7)
+    wt = W.Workload("gst", 102, "tree", B=16, V=128256, dtype="bf16", branching=(4, 2, 2, 1), recipe="peaked")
+    wd = W.Workload("gsd", 103, "tree_dyn", B=20, K=32, V=65536, dtype="f32", recipe="peaked")
+
+    def gen(step):
+        return (W.chain_inputs(wc, step), W.tree_inputs(wt, step, p_match=0.6),
+                W.tree_dyn_inputs(wd, step, p_match=0.7, nmin=1))
+
+    def to_t(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16) \
+            if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a))
+
+    c0, t0, d0 = gen(0)
+    ci = {k: dev(c0[k]) for k in ("target", "draft", "tokens", "u_accept", "u_sample")}
+    ti = {k: dev(t0[k]) for k in ("node_logits", "node_tokens")}
+    di = {k: dev(d0[k]) for k in ("node_logits", "node_tokens", "parents", "node_count")}
+    parents = t0["parents"]
+    ws_c = sv.workspace(sv.SPEC_MODE_CHAIN, wc.B, wc.K, wc.V, sv.SPEC_DTYPE_BF16, DEV)
+    ws_t = sv.workspace(sv.SPEC_MODE_TREE, wt.B, len(parents), wt.V, sv.SPEC_DTYPE_BF16, DEV)
+    ws_d = sv.workspace(sv.SPEC_MODE_TREE_DYN, wd.B, wd.K, wd.V, sv.SPEC_DTYPE_F32, DEV)
+    oc = (torch.empty((wc.B, wc.K + 1), dtype=torch.int32, device=DEV),
+          torch.empty(wc.B, dtype=torch.int32, device=DEV))
+    D = sv.tree_max_depth(parents)
+    ot = (torch.empty((wt.B, D + 1), dtype=torch.int32, device=DEV), torch.empty((wt.B, D + 1), dtype=torch.int32, device=DEV),
+          torch.empty(wt.B, dtype=torch.int32, device=DEV))
+    od = (torch.empty((wd.B, wd.K), dtype=torch.int32, device=DEV), torch.empty((wd.B, wd.K), dtype=torch.int32, device=DEV),
+          torch.empty(wd.B, dtype=torch.int32, device=DEV))
+
+    def step(stream=None):
+        sv.spec_verify_chain(ci["target"], ci["draft"], ci["tokens"], ci["u_accept"], ci["u_sample"], 1.0,
+                             out_tokens=oc[0], out_accepted=oc[1], workspace_buf=ws_c, stream=stream)
+        sv.spec_verify_tree_greedy(ti["node_logits"], ti["node_tokens"], parents, out_tokens=ot[0], out_path=ot[1],
+                                   out_depth=ot[2], workspace_buf=ws_t, stream=stream)
+        sv.spec_verify_tree_greedy_dyn(di["node_logits"], di["node_tokens"], di["parents"], di["node_count"],
+                                       out_tokens=od[0], out_path=od[1], out_depth=od[2], workspace_buf=ws_d,
+                                       stream=stream)
+
+    def load(inputs):
+        c, t, d = inputs
+        for name in ci:
+            ci[name].copy_(to_t(c[name]))
+        for name in ti:
+            ti[name].copy_(to_t(t[name]))
+        for name in di:
+            di[name].copy_(to_t(d[name]))
+
+    def check(inputs):
+        c, t, d = inputs
+        parity.check_chain(c, oc[0].cpu().numpy(), oc[1].cpu().numpy(), None)
+        parity.check_tree(t, *[o.cpu().numpy() for o in ot])
+        parity.check_tree_dyn(d, *[o.cpu().numpy() for o in od])
+
+    case("graph capture of the skipping orders: warm-up and capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    check((c0, t0, d0))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        case(f"graph capture of the skipping orders: replay {rep}")
+        inputs = gen(rep + 1)
+        load(inputs)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        check(inputs)
+        inputs = gen(rep + 10)
+        load(inputs)
+        step()
+        torch.cuda.synchronize()
+        check(inputs)
